@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for the selective state space hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library never
+imports, links or calls it, and the two share no code.
+
+The arithmetic lives in ``mss_oracle.c`` (plain C, double precision, the
+sequential recurrence exactly as the pages state it; see that file's header for
+the passages and the readings taken).  This module only marshals numpy arrays
+into it.  Inputs are widened exactly to fp64 by the caller (bf16 and fp32
+values are representable in fp64).
+
+Pins: every routine here is checked in ``tests/test_oracle_pins.py`` against
+closed forms, library routines and brute force (time-invariant case equals a
+causal convolution / first-order IIR filter, brute-force materialised matrix,
+zero-input decay, chunk-split composition, scan equals repeated state updates,
+SSD equals the Mamba-1 scan with scalar-per-head A and its matrix form, special
+cases of D and the gate, linearity, causality).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_liboracle.so")
+_SRC_PATH = os.path.join(_HERE, "mss_oracle.c")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_lib = None
+
+
+def build_command() -> list[str]:
+    """gcc command that builds the oracle's shared library (no fast-math)."""
+    return ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-pthread",
+            "-o", _LIB_PATH, _SRC_PATH, "-lm"]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"oracle library missing: {_LIB_PATH}; run __graft_entry__.build()")
+        lib = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.c_long
+        lib.oracle_selective_scan.argtypes = [_dp] * 10 + [L, L, L, L, ctypes.c_int]
+        lib.oracle_selective_scan.restype = None
+        lib.oracle_state_update.argtypes = [_dp] * 9 + [L, L, L, ctypes.c_int]
+        lib.oracle_state_update.restype = None
+        lib.oracle_ssd.argtypes = [_dp] * 11 + [L] * 7 + [ctypes.c_int]
+        lib.oracle_ssd.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"oracle: expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def default_threads() -> int:
+    return max(1, min(64, os.cpu_count() or 1))
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, threads=None):
+    """Plain sequential selective scan in fp64.
+
+    u, delta, z: [b, d, L]; B, C: [b, N, L]; A: [d, N]; D: [d]; h0: [b, d, N].
+    Returns (y [b, d, L], h_last [b, d, N]), both fp64.
+    """
+    u = _f64(u)
+    b, d, L = u.shape
+    N = np.shape(A)[1]
+    delta = _f64(delta, (b, d, L))
+    A = _f64(A, (d, N))
+    B = _f64(B, (b, N, L))
+    C = _f64(C, (b, N, L))
+    D = _f64(D, (d,))
+    z = _f64(z, (b, d, L))
+    h0 = _f64(h0, (b, d, N))
+    y = np.empty((b, d, L), dtype=np.float64)
+    h_last = np.empty((b, d, N), dtype=np.float64)
+    _load().oracle_selective_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(h0), _ptr(y), _ptr(h_last), b, d, N, L,
+                                  threads or default_threads())
+    return y, h_last
+
+
+def state_update(h, u, delta, A, B, C, D=None, z=None, threads=None):
+    """One recurrent step in fp64.  h: [b, d, N] (not modified; a new array is
+    returned); u, delta, z: [b, d]; B, C: [b, N]; A: [d, N]; D: [d].
+    Returns (h_new, y)."""
+    h = np.array(h, dtype=np.float64, order="C", copy=True)
+    b, d, N = h.shape
+    u = _f64(u, (b, d))
+    delta = _f64(delta, (b, d))
+    A = _f64(A, (d, N))
+    B = _f64(B, (b, N))
+    C = _f64(C, (b, N))
+    D = _f64(D, (d,))
+    z = _f64(z, (b, d))
+    y = np.empty((b, d), dtype=np.float64)
+    _load().oracle_state_update(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(z), _ptr(y), b, d, N, threads or default_threads())
+    return h, y
+
+
+def ssd(x, delta, A, B, C, D=None, z=None, h0=None, chunk=None, threads=None):
+    """Mamba-2 layer as its plain recurrence in fp64.
+
+    x, z: [b, L, H, P]; delta: [b, L, H]; A, D: [H]; B, C: [b, L, G, N];
+    h0: [b, H, P, N].  Returns (y [b, L, H, P], chunk_states or None, h_last).
+    chunk_states [b, nchunks, H, P, N] is the state after the last step of each
+    chunk of ``chunk`` steps (only when ``chunk`` is given).
+    """
+    x = _f64(x)
+    b, L, H, P = x.shape
+    G, N = np.shape(B)[2], np.shape(B)[3]
+    delta = _f64(delta, (b, L, H))
+    A = _f64(A, (H,))
+    B = _f64(B, (b, L, G, N))
+    C = _f64(C, (b, L, G, N))
+    D = _f64(D, (H,))
+    z = _f64(z, (b, L, H, P))
+    h0 = _f64(h0, (b, H, P, N))
+    if H % G:
+        raise ValueError("nheads must be a multiple of ngroups")
+    y = np.empty((b, L, H, P), dtype=np.float64)
+    h_last = np.empty((b, H, P, N), dtype=np.float64)
+    cs = None
+    q = chunk if chunk else L
+    if chunk:
+        cs = np.empty((b, (L + chunk - 1) // chunk, H, P, N), dtype=np.float64)
+    _load().oracle_ssd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                       _ptr(y), _ptr(cs), _ptr(h_last), b, L, H, P, G, N, q,
+                       threads or default_threads())
+    return y, cs, h_last

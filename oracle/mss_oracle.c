@@ -1,0 +1,229 @@
+/*
+ * fp64 CPU oracle for the selective state space hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * definition that the HIP library is checked against.  Only the tests, the
+ * package smoke check and the benchmark's CPU-baseline leg may load it; the
+ * library never does, and this file shares no code with it.
+ *
+ * Every routine runs the sequential recurrence exactly as the pages state it,
+ * one independent unit (a (batch, channel) pair, or a (batch, head) pair for
+ * SSD) at a time, in double precision.  Threads only split the independent
+ * units; nothing is blocked, fused or reordered inside a unit.
+ *
+ * Sources (page title, then section / equation):
+ *  - "Mamba (deep learning)" (wiki article), state-space paragraph:
+ *    discretisation of the continuous model gives the decay Abar = exp(Delta*A).
+ *  - "Mamba-1/2/3 visual guide" (blog.yecov.com), section 1, SSM equation:
+ *    h_t = Abar_t h_{t-1} + Bbar_t x_t,  y_t = C_t h_t.
+ *  - same blog, section 2, selectivity table: Delta, B, C depend on the
+ *    current input (they vary with t); block diagram: the SSM output is
+ *    multiplied elementwise by a gate branch.
+ *  - same blog, section 2 figure "train/prefill -> parallel scan, one-token
+ *    generation -> recurrent update, same model": the decode step is one
+ *    step of the same recurrence.
+ *  - same blog, section 3 comparison table: Mamba-2 restricts A to a scalar
+ *    times identity per head; chunk figure: chunks pass the state.
+ * Readings where the pages are silent (they leave Bbar undefined, and say
+ * nothing of D or of the gate's form):
+ *  - Bbar_t x_t = delta_t * B_t * u_t (Euler-style input term);
+ *  - y_t reads the state after the update at step t (so it includes u_t);
+ *  - out = (C_t . h_t + D * u_t) * silu(z_t), silu(z) = z / (1 + exp(-z));
+ *    D null -> no skip term, z null -> no gate;
+ *  - the initial state is h0 when given, else zero.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* ------------------------------------------------------------------------ */
+/* Selective scan.                                                           */
+/* u, delta, z, y: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen];      */
+/* A: [dim, dstate]; D: [dim]; h0, h_last: [batch, dim, dstate].             */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *h0;
+  double *y, *h_last;
+  long batch, dim, dstate, seqlen;
+  long unit_begin, unit_end;
+} scan_job;
+
+static void scan_unit(const scan_job* j, long b, long d) {
+  const long N = j->dstate, L = j->seqlen;
+  double* h = (double*)malloc(sizeof(double) * (size_t)N);
+  for (long n = 0; n < N; ++n) h[n] = j->h0 ? j->h0[(b * j->dim + d) * N + n] : 0.0;
+  const double* u = j->u + (b * j->dim + d) * L;
+  const double* dl = j->delta + (b * j->dim + d) * L;
+  const double* z = j->z ? j->z + (b * j->dim + d) * L : NULL;
+  double* y = j->y + (b * j->dim + d) * L;
+  const double* Bb = j->B + b * N * L;
+  const double* Cb = j->C + b * N * L;
+  const double Dd = j->D ? j->D[d] : 0.0;
+  for (long t = 0; t < L; ++t) {
+    double acc = 0.0;
+    for (long n = 0; n < N; ++n) {
+      double abar = exp(dl[t] * j->A[d * N + n]);          /* Abar_t = exp(delta_t A) */
+      h[n] = abar * h[n] + dl[t] * Bb[n * L + t] * u[t];   /* + Bbar_t u_t            */
+      acc += Cb[n * L + t] * h[n];                         /* C_t . h_t               */
+    }
+    double out = acc + Dd * u[t];
+    y[t] = z ? out * silu(z[t]) : out;
+  }
+  if (j->h_last)
+    for (long n = 0; n < N; ++n) j->h_last[(b * j->dim + d) * N + n] = h[n];
+  free(h);
+}
+
+static void* scan_worker(void* arg) {
+  const scan_job* j = (const scan_job*)arg;
+  for (long k = j->unit_begin; k < j->unit_end; ++k) scan_unit(j, k / j->dim, k % j->dim);
+  return NULL;
+}
+
+void oracle_selective_scan(const double* u, const double* delta, const double* A, const double* B,
+                           const double* C, const double* D, const double* z, const double* h0,
+                           double* y, double* h_last, long batch, long dim, long dstate, long seqlen,
+                           int nthreads) {
+  long units = batch * dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  scan_job* jobs = (scan_job*)calloc((size_t)nthreads, sizeof(scan_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    scan_job j = {u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen,
+                  units * i / nthreads, units * (i + 1) / nthreads};
+    jobs[i] = j;
+    pthread_create(&th[i], NULL, scan_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One-token state update (generation): one step of the same recurrence,     */
+/* with the state read and written in place.                                 */
+/* h: [batch, dim, dstate]; u, delta, z, y: [batch, dim]; B, C: [batch, dstate] */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  double* h;
+  const double *u, *delta, *A, *B, *C, *D, *z;
+  double* y;
+  long batch, dim, dstate;
+  long unit_begin, unit_end;
+} update_job;
+
+static void* update_worker(void* arg) {
+  const update_job* j = (const update_job*)arg;
+  const long N = j->dstate;
+  for (long bd = j->unit_begin; bd < j->unit_end; ++bd) {
+    const long b = bd / j->dim, d = bd % j->dim;
+    double acc = 0.0;
+    for (long n = 0; n < N; ++n) {
+      double abar = exp(j->delta[bd] * j->A[d * N + n]);
+      j->h[bd * N + n] = abar * j->h[bd * N + n] + j->delta[bd] * j->B[b * N + n] * j->u[bd];
+      acc += j->C[b * N + n] * j->h[bd * N + n];
+    }
+    double out = acc + (j->D ? j->D[d] : 0.0) * j->u[bd];
+    j->y[bd] = j->z ? out * silu(j->z[bd]) : out;
+  }
+  return NULL;
+}
+
+void oracle_state_update(double* h, const double* u, const double* delta, const double* A,
+                         const double* B, const double* C, const double* D, const double* z,
+                         double* y, long batch, long dim, long dstate, int nthreads) {
+  long units = batch * dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  update_job* jobs = (update_job*)calloc((size_t)nthreads, sizeof(update_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    update_job j = {h, u, delta, A, B, C, D, z, y, batch, dim, dstate,
+                    units * i / nthreads, units * (i + 1) / nthreads};
+    jobs[i] = j;
+    pthread_create(&th[i], NULL, update_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mamba-2 (SSD) layer, computed as its plain recurrence: per head the decay */
+/* is one scalar exp(delta * A_h) applied to the whole P x N state; heads of */
+/* one group share B and C.  No chunking: the chunk size only decides at     */
+/* which steps the state is recorded in chunk_states.                        */
+/* x, z, y: [batch, seqlen, nheads, headdim]; delta: [batch, seqlen, nheads];*/
+/* A, D: [nheads]; B, C: [batch, seqlen, ngroups, dstate];                   */
+/* h0, h_last: [batch, nheads, headdim, dstate];                             */
+/* chunk_states: [batch, nchunks, nheads, headdim, dstate], the state after  */
+/* the last step of each chunk.                                              */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const double *x, *delta, *A, *B, *C, *D, *z, *h0;
+  double *y, *chunk_states, *h_last;
+  long batch, seqlen, nheads, headdim, ngroups, dstate, chunk;
+  long unit_begin, unit_end;
+} ssd_job;
+
+static void ssd_unit(const ssd_job* j, long b, long hd) {
+  const long L = j->seqlen, H = j->nheads, P = j->headdim, G = j->ngroups, N = j->dstate;
+  const long g = hd / (H / G);
+  const long nchunks = (L + j->chunk - 1) / j->chunk;
+  double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));
+  for (long i = 0; i < P * N; ++i) S[i] = j->h0 ? j->h0[(b * H + hd) * P * N + i] : 0.0;
+  for (long t = 0; t < L; ++t) {
+    const double dlt = j->delta[(b * L + t) * H + hd];
+    const double abar = exp(dlt * j->A[hd]);
+    const double* Bt = j->B + ((b * L + t) * G + g) * N;
+    const double* Ct = j->C + ((b * L + t) * G + g) * N;
+    const double* xt = j->x + ((b * L + t) * H + hd) * P;
+    double* yt = j->y + ((b * L + t) * H + hd) * P;
+    for (long p = 0; p < P; ++p) {
+      double acc = 0.0;
+      for (long n = 0; n < N; ++n) {
+        S[p * N + n] = abar * S[p * N + n] + dlt * Bt[n] * xt[p];
+        acc += Ct[n] * S[p * N + n];
+      }
+      double out = acc + (j->D ? j->D[hd] : 0.0) * xt[p];
+      yt[p] = j->z ? out * silu(j->z[((b * L + t) * H + hd) * P + p]) : out;
+    }
+    if (j->chunk_states && ((t + 1) % j->chunk == 0 || t == L - 1)) {
+      long c = t / j->chunk;
+      memcpy(j->chunk_states + (((b * nchunks + c) * H + hd) * P * N), S, sizeof(double) * (size_t)(P * N));
+    }
+  }
+  if (j->h_last) memcpy(j->h_last + (b * H + hd) * P * N, S, sizeof(double) * (size_t)(P * N));
+  free(S);
+}
+
+static void* ssd_worker(void* arg) {
+  const ssd_job* j = (const ssd_job*)arg;
+  for (long k = j->unit_begin; k < j->unit_end; ++k) ssd_unit(j, k / j->nheads, k % j->nheads);
+  return NULL;
+}
+
+void oracle_ssd(const double* x, const double* delta, const double* A, const double* B,
+                const double* C, const double* D, const double* z, const double* h0, double* y,
+                double* chunk_states, double* h_last, long batch, long seqlen, long nheads,
+                long headdim, long ngroups, long dstate, long chunk, int nthreads) {
+  long units = batch * nheads;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  ssd_job* jobs = (ssd_job*)calloc((size_t)nthreads, sizeof(ssd_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    ssd_job j = {x, delta, A, B, C, D, z, h0, y, chunk_states, h_last, batch, seqlen, nheads,
+                 headdim, ngroups, dstate, chunk, units * i / nthreads, units * (i + 1) / nthreads};
+    jobs[i] = j;
+    pthread_create(&th[i], NULL, ssd_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+}

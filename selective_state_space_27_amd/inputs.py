@@ -1,0 +1,241 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module is shared by the HIP path's tests/bench and by the fp64 oracle's
+callers.  It holds input *preparation* only (random draws, the delta recipe,
+bf16 rounding); none of the scan's own arithmetic lives here.
+
+Workloads (shapes follow the Mamba pages: Mamba-1 blocks with d_state 16,
+Mamba-2 blocks with d_state 128 and headdim 64, "Mamba State-Space Models"
+skills page, usage section; the five workload shapes themselves are this
+library's benchmark presets):
+
+  scan_tiny     b=1  d_inner=16    N=16  L=64     fp32
+  scan_130m     b=8  d_inner=1536  N=16  L=2048   fp32
+  scan_2p8b     b=4  d_inner=5120  N=16  L=8192   bf16 I/O, fp32 A/D/state
+  decode_2p8b   b=256 d_inner=5120 N=16  one token per step, 1000 steps
+  ssd_2p8b      b=2  H=80 P=64 N=128 L=16384 chunk 256
+
+Every tensor comes from its own numpy PCG64 stream seeded by
+SeedSequence([seed, tensor_id(, step)]), so the order in which tensors are
+drawn cannot change their values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+# Tensor ids for the per-tensor child streams.
+TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X = range(1, 11)
+
+SEED_BASE = 27000
+
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    seqlen: int
+    io: str          # "fp32" or "bf16" (u, delta, B, C, z, y)
+    seed: int
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    steps: int
+    io: str          # dtype of u, delta, B, C, z, y; state h is always fp32
+    seed: int
+
+
+@dataclasses.dataclass(frozen=True)
+class SSDConfig:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    chunk: int
+    seed: int
+
+
+SCAN_TINY = ScanConfig("scan_tiny", 1, 16, 16, 64, "fp32", SEED_BASE + 0)
+SCAN_130M = ScanConfig("scan_130m", 8, 1536, 16, 2048, "fp32", SEED_BASE + 1)
+SCAN_2P8B = ScanConfig("scan_2p8b", 4, 5120, 16, 8192, "bf16", SEED_BASE + 2)
+DECODE_2P8B = DecodeConfig("decode_2p8b", 256, 5120, 16, 1000, "bf16", SEED_BASE + 3)
+SSD_2P8B = SSDConfig("ssd_2p8b", 2, 16384, 80, 64, 1, 128, 256, SEED_BASE + 4)
+
+# Distinct per-step input sets drawn for the 1000-step decode workload; step s
+# uses set s % DECODE_POOL (input recipe).
+DECODE_POOL = 16
+
+
+def rng(seed: int, tid: int, step: int | None = None) -> np.random.Generator:
+    key = [int(seed), int(tid)] + ([int(step)] if step is not None else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
+
+
+# ----------------------------------------------------------------- bf16 -----
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round fp32 values to bf16 with round-to-nearest-even; returns uint16 bits.
+
+    NaN stays NaN (quiet); infinities and signed zeros are preserved."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    bits = a.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = (bits + 0x7FFF + lsb) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = ((bits[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# ---------------------------------------------------------------- delta -----
+def softplus(x: np.ndarray) -> np.ndarray:
+    """Stable softplus in fp64: max(x,0) + log1p(exp(-|x|))."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def inv_softplus(y: np.ndarray) -> np.ndarray:
+    """Inverse of softplus for y > 0: y + log(-expm1(-y))."""
+    y = np.asarray(y, dtype=np.float64)
+    return y + np.log(-np.expm1(-y))
+
+
+def draw_dt(seed: int, count: int, lo: float = 1e-3, hi: float = 1e-1) -> np.ndarray:
+    """dt log-uniform on [lo, hi], one per channel (or per head)."""
+    g = rng(seed, TID_DT)
+    return np.exp(g.uniform(np.log(lo), np.log(hi), size=count))
+
+
+def make_delta(dt: np.ndarray, noise: np.ndarray, axis_shape) -> np.ndarray:
+    """delta = softplus(0.5*noise + inv_softplus(dt)), computed in fp64.
+
+    ``dt`` is broadcast against ``noise`` via ``axis_shape`` (a reshape of dt)."""
+    return softplus(0.5 * noise.astype(np.float64) + inv_softplus(dt).reshape(axis_shape))
+
+
+def _normal(seed, tid, shape, step=None) -> np.ndarray:
+    return rng(seed, tid, step).standard_normal(size=shape, dtype=np.float32)
+
+
+def _io(a: np.ndarray, io: str) -> np.ndarray:
+    """fp32 array -> storage array for the I/O dtype (fp32 or uint16 bf16 bits)."""
+    if io == "fp32":
+        return np.ascontiguousarray(a, dtype=np.float32)
+    if io == "bf16":
+        return f32_to_bf16_bits(a)
+    raise ValueError(io)
+
+
+def to_f64(a: np.ndarray, io: str) -> np.ndarray:
+    """Exact widening of a storage array to fp64 (bf16 bits or fp32)."""
+    if io == "bf16" or a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+# ------------------------------------------------------------ scan inputs ---
+def scan_inputs(cfg: ScanConfig, with_h0: bool = False) -> dict:
+    """Inputs of the selective scan in storage form.
+
+    u, delta, z: [b, d, l]; B, C: [b, n, l]  (I/O dtype)
+    A: [d, n] fp32 = -(n+1) (S4D-real); D: [d] fp32; h0: [b, d, n] fp32 (optional)
+    """
+    b, d, n, L, s = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, cfg.seed
+    dt = draw_dt(s, d)
+    noise = _normal(s, TID_DNOISE, (b, d, L))
+    delta = make_delta(dt, noise, (1, d, 1)).astype(np.float32)
+    del noise
+    out = {
+        "u": _io(_normal(s, TID_U, (b, d, L)), cfg.io),
+        "delta": _io(delta, cfg.io),
+        "A": np.ascontiguousarray(np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (d, n))),
+        "B": _io(_normal(s, TID_B, (b, n, L)), cfg.io),
+        "C": _io(_normal(s, TID_C, (b, n, L)), cfg.io),
+        "D": _normal(s, TID_D, (d,)),
+        "z": _io(_normal(s, TID_Z, (b, d, L)), cfg.io),
+        "h0": (0.1 * _normal(s, TID_H0, (b, d, n))).astype(np.float32) if with_h0 else None,
+        "io": cfg.io,
+    }
+    del delta
+    return out
+
+
+# ---------------------------------------------------------- decode inputs ---
+def decode_state0(cfg: DecodeConfig) -> np.ndarray:
+    """Initial fp32 state h[b, d, n] ~ 0.1 * N(0, 1)."""
+    return (0.1 * _normal(cfg.seed, TID_H0, (cfg.batch, cfg.dim, cfg.dstate))).astype(np.float32)
+
+
+def decode_static(cfg: DecodeConfig) -> dict:
+    """Per-layer parameters of the decode workload: A [d, n], D [d], dt [d]."""
+    d, n = cfg.dim, cfg.dstate
+    return {
+        "A": np.ascontiguousarray(np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (d, n))),
+        "D": _normal(cfg.seed, TID_D, (d,)),
+        "dt": draw_dt(cfg.seed, d),
+    }
+
+
+def decode_step_inputs(cfg: DecodeConfig, step: int, dt: np.ndarray) -> dict:
+    """Fresh token inputs for one generation step (u, delta, z: [b, d]; B, C: [b, n])."""
+    b, d, n, s = cfg.batch, cfg.dim, cfg.dstate, cfg.seed
+    noise = _normal(s, TID_DNOISE, (b, d), step)
+    delta = make_delta(dt, noise, (1, d)).astype(np.float32)
+    return {
+        "u": _io(_normal(s, TID_U, (b, d), step), cfg.io),
+        "delta": _io(delta, cfg.io),
+        "B": _io(_normal(s, TID_B, (b, n), step), cfg.io),
+        "C": _io(_normal(s, TID_C, (b, n), step), cfg.io),
+        "z": _io(_normal(s, TID_Z, (b, d), step), cfg.io),
+        "io": cfg.io,
+    }
+
+
+# ------------------------------------------------------------- SSD inputs ---
+def ssd_inputs(cfg: SSDConfig, with_h0: bool = False) -> dict:
+    """Inputs of the SSD chunked layer.
+
+    x: [b, l, h, p] bf16; B, C: [b, l, g, n] bf16; delta: [b, l, h] fp32;
+    A: [h] fp32 = -exp(U(0, ln 16)); h0: [b, h, p, n] fp32 (optional).
+    """
+    b, L, H, P, G, N, s = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.seed
+    dt = draw_dt(s, H)
+    noise = _normal(s, TID_DNOISE, (b, L, H))
+    delta = make_delta(dt, noise, (1, 1, H)).astype(np.float32)
+    A = (-np.exp(rng(s, TID_A).uniform(0.0, np.log(16.0), size=H))).astype(np.float32)
+    return {
+        "x": f32_to_bf16_bits(_normal(s, TID_X, (b, L, H, P))),
+        "delta": delta,
+        "A": A,
+        "B": f32_to_bf16_bits(_normal(s, TID_B, (b, L, G, N))),
+        "C": f32_to_bf16_bits(_normal(s, TID_C, (b, L, G, N))),
+        "h0": (0.1 * _normal(s, TID_H0, (b, H, P, N))).astype(np.float32) if with_h0 else None,
+    }
+
+
+def small_scan_config(batch, dim, dstate, seqlen, io="fp32", seed=SEED_BASE + 100) -> ScanConfig:
+    return ScanConfig(f"scan_b{batch}_d{dim}_n{dstate}_l{seqlen}_{io}", batch, dim, dstate, seqlen, io, seed)
+
+
+def small_ssd_config(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, seed=SEED_BASE + 200) -> SSDConfig:
+    return SSDConfig(f"ssd_b{batch}_l{seqlen}_h{nheads}_p{headdim}_g{ngroups}_n{dstate}_q{chunk}",
+                     batch, seqlen, nheads, headdim, ngroups, dstate, chunk, seed)

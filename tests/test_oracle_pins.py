@@ -1,0 +1,366 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+No test here compares the oracle with a retyped copy of its own recurrence.
+Each check goes through a different route: hand-derived values, a textbook
+library routine (numpy convolution, scipy's IIR filter), a closed form, a
+brute-force materialised matrix, or an invariant of the method.
+
+Passages (page title, section):
+  "Mamba (deep learning)", state-space paragraph: Abar = exp(Delta*A); a
+    time-invariant model is one long convolution.
+  "Mamba-1/2/3 visual guide" (blog.yecov.com), section 1 SSM equation
+    (recurrence and readout); section 2 selectivity table (Delta, B, C vary
+    with the input), block diagram (gate), figure "parallel scan vs recurrent
+    update: same model"; section 3 (scalar-times-identity A per head, chunks
+    pass the state, matrix view).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import scipy.special
+import torch
+
+import oracle
+from selective_state_space_27_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")
+
+
+def silu(z):
+    return z * scipy.special.expit(z)
+
+
+def rand_scan(b, d, n, L, seed=5, gate=True, dmin=1e-3, dmax=2e-1):
+    g = np.random.default_rng(seed)
+    A = -np.exp(g.uniform(-1.0, 1.5, size=(d, n)))
+    return dict(
+        u=g.standard_normal((b, d, L)),
+        delta=np.exp(g.uniform(np.log(dmin), np.log(dmax), size=(b, d, L))),
+        A=A,
+        B=g.standard_normal((b, n, L)),
+        C=g.standard_normal((b, n, L)),
+        D=g.standard_normal(d),
+        z=g.standard_normal((b, d, L)) if gate else None,
+    )
+
+
+# --------------------------------------------------------------- golden -----
+def test_hand_derived_scan():
+    gd = json.load(open(GOLDEN))
+    for key in ("scan_n1", "scan_n2_time_varying"):
+        c = gd[key]
+        y, h = oracle.selective_scan(c["u"], c["delta"], c["A"], c["B"], c["C"], c["D"], None)
+        np.testing.assert_allclose(y, c["y"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(h, c["h_last"], rtol=0, atol=1e-14)
+
+
+def test_hand_derived_state_update():
+    c = json.load(open(GOLDEN))["state_update_n2"]
+    h, y = oracle.state_update(c["h"], c["u"], c["delta"], c["A"], c["B"], c["C"], c["D"], None)
+    np.testing.assert_allclose(h, c["h_new"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(y, c["y"], rtol=0, atol=1e-14)
+
+
+def test_hand_derived_ssd():
+    c = json.load(open(GOLDEN))["ssd_p2_n1"]
+    y, cs, _ = oracle.ssd(c["x"], c["delta"], c["A"], c["B"], c["C"], chunk=c["chunk"])
+    np.testing.assert_allclose(y, c["y"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(cs, c["chunk_states"], rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------- P1: LTI == convolution ---
+@pytest.mark.parametrize("gate", [False, True])
+def test_lti_equals_causal_convolution(gate):
+    """Constant delta (per channel) and constant B, C: y = K * u + D u with
+    K_k = sum_n C_n exp(k delta A_n) delta B_n ("Mamba (deep learning)",
+    state-space paragraph).  Checked with numpy.convolve and, per state, with
+    scipy.signal.lfilter as the first-order IIR filter h_t = a h_{t-1} + b u_t."""
+    b, d, n, L = 2, 3, 4, 300
+    g = np.random.default_rng(11)
+    u = g.standard_normal((b, d, L))
+    dl = np.exp(g.uniform(np.log(1e-3), np.log(0.3), size=(b, d)))
+    A = -np.exp(g.uniform(-1, 1.5, size=(d, n)))
+    Bc = g.standard_normal((b, n))
+    Cc = g.standard_normal((b, n))
+    D = g.standard_normal(d)
+    z = g.standard_normal((b, d, L)) if gate else None
+    delta = np.repeat(dl[:, :, None], L, axis=2)
+    B = np.repeat(Bc[:, :, None], L, axis=2)
+    C = np.repeat(Cc[:, :, None], L, axis=2)
+    y, _ = oracle.selective_scan(u, delta, A, B, C, D, z)
+    k = np.arange(L)
+    for bi in range(b):
+        for di in range(d):
+            a = np.exp(dl[bi, di] * A[di])                      # per state decay
+            K = (Cc[bi][None, :] * a[None, :] ** k[:, None] * dl[bi, di] * Bc[bi][None, :]).sum(1)
+            ref = np.convolve(u[bi, di], K)[:L] + D[di] * u[bi, di]
+            iir = sum(Cc[bi, m] * scipy.signal.lfilter([dl[bi, di] * Bc[bi, m]], [1.0, -a[m]], u[bi, di])
+                      for m in range(n)) + D[di] * u[bi, di]
+            if gate:
+                ref = ref * silu(z[bi, di])
+                iir = iir * silu(z[bi, di])
+            scale = np.abs(ref).max()
+            assert np.abs(y[bi, di] - ref).max() <= 1e-12 * scale
+            assert np.abs(y[bi, di] - iir).max() <= 1e-12 * scale
+
+
+# ------------------------------------------------- P2: brute-force matrix ---
+def brute_force_scan(u, delta, A, B, C, D, z, h0=None):
+    """y[t] = sum_{s<=t} M[t,s] u[s] + D u[t] (+ initial-state term), gated,
+    with M[t,s] = sum_n C_n(t) prod_{k=s+1..t} exp(delta_k A_n) delta_s B_n(s);
+    every product is formed explicitly (no recurrence)."""
+    b, d, L = u.shape
+    N = A.shape[1]
+    y = np.zeros((b, d, L))
+    for bi in range(b):
+        for di in range(d):
+            M = np.zeros((L, L))
+            init = np.zeros(L)
+            for t in range(L):
+                for s in range(t + 1):
+                    acc = 0.0
+                    for m in range(N):
+                        p = 1.0
+                        for kk in range(s + 1, t + 1):
+                            p *= np.exp(delta[bi, di, kk] * A[di, m])
+                        acc += C[bi, m, t] * p * delta[bi, di, s] * B[bi, m, s]
+                    M[t, s] = acc
+                if h0 is not None:
+                    for m in range(N):
+                        p = 1.0
+                        for kk in range(0, t + 1):
+                            p *= np.exp(delta[bi, di, kk] * A[di, m])
+                        init[t] += C[bi, m, t] * p * h0[bi, di, m]
+            out = M @ u[bi, di] + (D[di] if D is not None else 0.0) * u[bi, di] + init
+            y[bi, di] = out * silu(z[bi, di]) if z is not None else out
+    return y
+
+
+def test_brute_force_matrix_tiny_workload():
+    """The tiny fp32 workload (b=1, d=16, N=16, L=64) itself, reduced to 4
+    channels to keep the explicit products quick."""
+    x = I.scan_inputs(I.SCAN_TINY)
+    sel = slice(0, 4)
+    u = I.to_f64(x["u"], "fp32")[:, sel]
+    dl = I.to_f64(x["delta"], "fp32")[:, sel]
+    A = x["A"].astype(np.float64)[sel]
+    B, C = x["B"].astype(np.float64), x["C"].astype(np.float64)
+    D = x["D"].astype(np.float64)[sel]
+    z = I.to_f64(x["z"], "fp32")[:, sel]
+    y, _ = oracle.selective_scan(u, dl, A, B, C, D, z)
+    ref = brute_force_scan(u, dl, A, B, C, D, z)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_brute_force_matrix_with_h0_and_time_varying_decay():
+    p = rand_scan(1, 2, 3, 20, seed=3, dmax=0.8)
+    h0 = np.random.default_rng(4).standard_normal((1, 2, 3))
+    y, _ = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], h0)
+    ref = brute_force_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], h0)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+# ------------------------------------------------- P3: zero input decays ----
+def test_zero_input_decays_in_closed_form():
+    b, d, n, L = 2, 3, 5, 50
+    p = rand_scan(b, d, n, L, seed=7, dmax=0.5)
+    h0 = np.random.default_rng(8).standard_normal((b, d, n))
+    u0 = np.zeros((b, d, L))
+    y, h = oracle.selective_scan(u0, p["delta"], p["A"], p["B"], p["C"], p["D"], None, h0)
+    cum = np.cumsum(p["delta"], axis=2)                                # [b, d, L]
+    expect_h = np.exp(p["A"][None] * cum[:, :, -1:]) * h0              # exp(A sum delta) h0
+    np.testing.assert_allclose(h, expect_h, rtol=1e-13, atol=0)
+    expect_y = np.einsum("bnt,bdnt->bdt", p["C"], np.exp(p["A"][None, :, :, None] * cum[:, :, None, :]) * h0[..., None])
+    np.testing.assert_allclose(y, expect_y, rtol=1e-12, atol=1e-14)
+    assert np.all(np.abs(h) <= np.abs(h0))                             # A < 0, delta > 0
+    y2, h2 = oracle.selective_scan(u0, p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], None)
+    assert np.all(y2 == 0.0) and np.all(h2 == 0.0)
+
+
+# ------------------------------------------ P4: chunk-split composition ----
+@pytest.mark.parametrize("L1", [1, 17, 64, 99])
+def test_chunk_split_composition(L1):
+    p = rand_scan(2, 3, 4, 100, seed=9)
+    y, h = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"])
+    a = {k: (v[..., :L1] if k in ("u", "delta", "B", "C", "z") else v) for k, v in p.items()}
+    c = {k: (v[..., L1:] if k in ("u", "delta", "B", "C", "z") else v) for k, v in p.items()}
+    y1, h1 = oracle.selective_scan(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"])
+    y2, h2 = oracle.selective_scan(c["u"], c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"], h1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=2), y, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(h2, h, rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------- P5: scan == L state updates ------
+def test_scan_equals_repeated_state_update():
+    b, d, n, L = 2, 3, 4, 40
+    p = rand_scan(b, d, n, L, seed=13)
+    h0 = np.random.default_rng(14).standard_normal((b, d, n))
+    y, hl = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], h0)
+    h = h0.copy()
+    ys = []
+    for t in range(L):
+        h, yt = oracle.state_update(h, p["u"][..., t], p["delta"][..., t], p["A"], p["B"][..., t],
+                                    p["C"][..., t], p["D"], p["z"][..., t])
+        ys.append(yt)
+    np.testing.assert_allclose(np.stack(ys, axis=2), y, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(h, hl, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------- P6: SSD == Mamba-1 special case ------
+def rand_ssd(b, L, H, P, G, N, seed=21, gate=False, with_d=False):
+    g = np.random.default_rng(seed)
+    return dict(
+        x=g.standard_normal((b, L, H, P)),
+        delta=np.exp(g.uniform(np.log(1e-3), np.log(0.3), size=(b, L, H))),
+        A=-np.exp(g.uniform(0, np.log(16), size=H)),
+        B=g.standard_normal((b, L, G, N)),
+        C=g.standard_normal((b, L, G, N)),
+        D=g.standard_normal(H) if with_d else None,
+        z=g.standard_normal((b, L, H, P)) if gate else None,
+    )
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_equals_mamba1_scan_special_case(G):
+    """Mamba-2 restricts A to a scalar per head ("Mamba-1/2/3 visual guide",
+    section 3 table): the SSD layer is the Mamba-1 scan with channel d = (h, p),
+    A[d, n] = A_h, delta[b, d, l] = delta[b, l, h] and B, C of the head's group."""
+    b, L, H, P, N = 2, 37, 4, 3, 5
+    s = rand_ssd(b, L, H, P, G, N, gate=True, with_d=True)
+    h0 = np.random.default_rng(22).standard_normal((b, H, P, N))
+    y, _, hl = oracle.ssd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], h0)
+    hpg = H // G
+    for bi in range(b):
+        for g in range(G):
+            heads = range(g * hpg, (g + 1) * hpg)
+            u = np.concatenate([s["x"][bi, :, h, :].T for h in heads])[None]            # [1, hpg*P, L]
+            dl = np.concatenate([np.repeat(s["delta"][bi, :, h][None], P, 0) for h in heads])[None]
+            A = np.concatenate([np.full((P, N), s["A"][h]) for h in heads])
+            Dv = np.concatenate([np.full(P, s["D"][h]) for h in heads])
+            z = np.concatenate([s["z"][bi, :, h, :].T for h in heads])[None]
+            B = s["B"][bi, :, g, :].T[None]
+            C = s["C"][bi, :, g, :].T[None]
+            h0m = np.concatenate([h0[bi, h] for h in heads])[None]
+            ym, hm = oracle.selective_scan(u, dl, A, B, C, Dv, z, h0m)
+            for j, h in enumerate(heads):
+                np.testing.assert_allclose(y[bi, :, h, :], ym[0, j * P:(j + 1) * P].T, rtol=1e-13, atol=1e-13)
+                np.testing.assert_allclose(hl[bi, h], hm[0, j * P:(j + 1) * P], rtol=1e-13, atol=1e-13)
+
+
+def test_ssd_matrix_form():
+    """Matrix view of the same model ("Mamba-1/2/3 visual guide", section 3;
+    "Mamba (deep learning)", duality paragraph):
+    y = (Lmask o C B^T)(delta x) with Lmask[t,s] = exp(A sum_{k=s+1..t} delta_k)."""
+    b, L, H, P, N = 1, 48, 2, 4, 6
+    s = rand_ssd(b, L, H, P, 1, N, seed=31)
+    y, _, _ = oracle.ssd(s["x"], s["delta"], s["A"], s["B"], s["C"])
+    for h in range(H):
+        cs = np.cumsum(s["delta"][0, :, h])
+        seg = cs[:, None] - cs[None, :]
+        Lm = np.where(np.tri(L, dtype=bool), np.exp(s["A"][h] * np.where(np.tri(L, dtype=bool), seg, 0.0)), 0.0)
+        G = s["C"][0, :, 0, :] @ s["B"][0, :, 0, :].T
+        ref = (Lm * G) @ (s["delta"][0, :, h][:, None] * s["x"][0, :, h, :])
+        np.testing.assert_allclose(y[0, :, h, :], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk,L", [(8, 32), (8, 29), (16, 5)])
+def test_ssd_chunk_states_are_prefix_states(chunk, L):
+    """The state recorded after chunk c is the final state of the same layer
+    run on the first min((c+1)Q, L) steps (chunks pass the state)."""
+    s = rand_ssd(1, L, 2, 3, 1, 4, seed=41)
+    _, cs, hl = oracle.ssd(s["x"], s["delta"], s["A"], s["B"], s["C"], chunk=chunk)
+    nch = (L + chunk - 1) // chunk
+    assert cs.shape[1] == nch
+    for c in range(nch):
+        e = min((c + 1) * chunk, L)
+        _, _, hp = oracle.ssd(s["x"][:, :e], s["delta"][:, :e], s["A"], s["B"][:, :e], s["C"][:, :e])
+        np.testing.assert_allclose(cs[:, c], hp, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(cs[:, -1], hl, rtol=0, atol=0)
+
+
+# ------------------------------------------------- P7: special cases --------
+def test_c_zero_gives_skip_times_gate():
+    p = rand_scan(2, 3, 4, 30, seed=51)
+    y, _ = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], np.zeros_like(p["C"]), p["D"], p["z"])
+    np.testing.assert_allclose(y, p["D"][None, :, None] * p["u"] * silu(p["z"]), rtol=1e-14, atol=0)
+
+
+def test_gate_is_elementwise_silu():
+    p = rand_scan(2, 3, 4, 30, seed=52)
+    y_g, _ = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"])
+    y_u, _ = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], None)
+    np.testing.assert_allclose(y_g, y_u * silu(p["z"]), rtol=1e-14, atol=1e-300)
+    y0, _ = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], np.zeros_like(p["z"]))
+    assert np.all(y0 == 0.0)                                    # silu(0) = 0
+
+
+def test_vanishing_delta_leaves_only_skip():
+    p = rand_scan(1, 2, 3, 20, seed=53)
+    y, h = oracle.selective_scan(p["u"], np.full_like(p["delta"], 1e-30), p["A"], p["B"], p["C"], p["D"], p["z"])
+    ref = p["D"][None, :, None] * p["u"] * silu(p["z"])
+    np.testing.assert_allclose(y, ref, rtol=1e-15, atol=1e-300)   # state term ~1e-30
+    assert np.abs(h).max() < 1e-27
+
+
+# ---------------------------------------------------- P8: linearity ---------
+def test_linearity_in_u_and_h0():
+    p = rand_scan(2, 3, 4, 25, seed=61, gate=False)
+    g = np.random.default_rng(62)
+    u2 = g.standard_normal(p["u"].shape)
+    h01, h02 = g.standard_normal((2, 3, 4)), g.standard_normal((2, 3, 4))
+    al, be = 0.7, -1.9
+    run = lambda u, h0: oracle.selective_scan(u, p["delta"], p["A"], p["B"], p["C"], p["D"], None, h0)
+    y1, s1 = run(p["u"], h01)
+    y2, s2 = run(u2, h02)
+    y3, s3 = run(al * p["u"] + be * u2, al * h01 + be * h02)
+    np.testing.assert_allclose(y3, al * y1 + be * y2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s3, al * s1 + be * s2, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------- P9: causality ---------
+def test_causality():
+    p = rand_scan(1, 4, 4, 60, seed=71)
+    y, _ = oracle.selective_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"])
+    for t0 in (0, 1, 30, 59):
+        u = p["u"].copy()
+        u[:, :, t0] += 3.0
+        y2, _ = oracle.selective_scan(u, p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"])
+        assert np.array_equal(y2[:, :, :t0], y[:, :, :t0])
+        assert not np.array_equal(y2[:, :, t0], y[:, :, t0])
+
+
+# -------------------------------------------- P10: input generator ----------
+def test_delta_recipe_roundtrip():
+    dt = I.draw_dt(123, 1000)
+    assert dt.min() >= 1e-3 and dt.max() <= 1e-1
+    got = I.make_delta(dt, np.zeros((2, 1000)), (1, 1000))
+    np.testing.assert_allclose(got, np.broadcast_to(dt, (2, 1000)), rtol=1e-14, atol=0)
+    x = np.linspace(-30, 30, 101)
+    np.testing.assert_allclose(I.softplus(x), np.log1p(np.exp(x)), rtol=1e-14, atol=1e-300)
+
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(5)
+    vals = np.concatenate([g.standard_normal(100000).astype(np.float32) * 10 ** g.uniform(-5, 5, 100000).astype(np.float32),
+                           np.array([0.0, -0.0, np.inf, -np.inf, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8,
+                                     3.3895314e38, 1e-40, -1e-40], dtype=np.float32)])
+    ours = I.f32_to_bf16_bits(vals)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = I.bf16_bits_to_f32(ours)
+    np.testing.assert_array_equal(torch.from_numpy(back).numpy(), torch.from_numpy(vals).to(torch.bfloat16).float().numpy())
+
+
+def test_generator_deterministic_and_order_independent():
+    a = I.scan_inputs(I.SCAN_TINY)
+    c = I.rng(I.SCAN_TINY.seed, I.TID_C).standard_normal(size=(1, 16, 64), dtype=np.float32)
+    b = I.scan_inputs(I.SCAN_TINY)
+    for k in ("u", "delta", "A", "B", "C", "D", "z"):
+        assert np.array_equal(a[k], b[k])
+    assert np.array_equal(a["C"], c)            # C's stream does not depend on draw order
+    assert not np.array_equal(a["B"], a["C"])
+    assert np.all(a["A"] == -(np.arange(16) + 1.0)[None])
+    assert a["delta"].min() > 0
