@@ -69,7 +69,15 @@ def _ptr(a):
 
 
 def default_threads() -> int:
-    return max(1, min(64, os.cpu_count() or 1))
+    """Threads the oracle uses: the CPUs this process may run on, at most 16."""
+    env = os.environ.get("MSS_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, threads=None):

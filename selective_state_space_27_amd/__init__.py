@@ -1,0 +1,250 @@
+"""Python binding of libmambascan (the MI355X selective state space hot path).
+
+The functions here only marshal arguments into the C ABI declared in
+``include/mambascan.h``: they check device/dtype/contiguity, allocate the
+output and workspace tensors with PyTorch (device memory only) and pass raw
+device pointers and the current HIP stream.  Every arithmetic step runs in the
+library's HIP kernels.  There is no CPU fallback: if the library is missing
+or a GPU is absent, the calls raise.
+
+Operations (see the header for the exact definitions and layouts):
+  selective_scan_fwd  Mamba-1 selective scan over a whole sequence
+  state_update        one recurrent generation step, state updated in place
+  ssd_chunk_fwd       Mamba-2 SSD layer, chunked, dense products on MFMA
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmambascan.so")
+
+MSS_OK = 0
+MSS_FP32 = 0
+MSS_BF16 = 1
+MSS_FLAG_DECAY_GENERAL = 0x1
+
+STATUS_NAMES = {0: "MSS_OK", 1: "MSS_ERR_NULL", 2: "MSS_ERR_SHAPE", 3: "MSS_ERR_DTYPE", 4: "MSS_ERR_ALIGN",
+                5: "MSS_ERR_UNSUPPORTED", 6: "MSS_ERR_WORKSPACE", 7: "MSS_ERR_ALIAS", 8: "MSS_ERR_HIP"}
+
+# Every symbol the header declares.
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_state_update",
+           "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_status_string", "mss_last_hip_error",
+           "mss_abi_version")
+
+
+class MambaScanError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{what}: {lib().mss_status_string(status).decode()}"
+        if status == 8:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmambascan with argument types set (loads on first use)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmambascan not built: {LIB_PATH} is missing "
+                           "(run `python -m selective_state_space_27_amd.build`)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp, i64, u32, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    L.mss_selective_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, i64, i64, i64, i64, ctypes.c_int,
+                                         u32, vp, sz, vp]
+    L.mss_selective_scan_fwd.restype = ctypes.c_int
+    L.mss_selective_scan_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
+    L.mss_selective_scan_workspace_size.restype = sz
+    L.mss_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ctypes.c_int, u32, vp]
+    L.mss_state_update.restype = ctypes.c_int
+    L.mss_ssd_chunk_fwd.argtypes = [vp, fp, fp, vp, vp, fp, vp, fp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
+                                    ctypes.c_int, u32, vp, sz, vp]
+    L.mss_ssd_chunk_fwd.restype = ctypes.c_int
+    L.mss_ssd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    L.mss_ssd_workspace_size.restype = sz
+    L.mss_status_string.argtypes = [ctypes.c_int]
+    L.mss_status_string.restype = ctypes.c_char_p
+    L.mss_last_hip_error.argtypes = []
+    L.mss_last_hip_error.restype = ctypes.c_int
+    L.mss_abi_version.argtypes = []
+    L.mss_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().mss_abi_version()
+
+
+# --------------------------------------------------------------- helpers ----
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _io_code(dtype) -> int:
+    if dtype == torch.float32:
+        return MSS_FP32
+    if dtype == torch.bfloat16:
+        return MSS_BF16
+    raise TypeError(f"unsupported I/O dtype {dtype} (float32 or bfloat16)")
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(status: int, what: str):
+    if status != MSS_OK:
+        raise MambaScanError(status, what, lib().mss_last_hip_error())
+
+
+def _device_of(t: torch.Tensor) -> torch.device:
+    if t.device.type != "cuda":
+        raise ValueError("libmambascan works on GPU tensors only (no CPU path)")
+    return t.device
+
+
+# ------------------------------------------------------------ selective scan
+def selective_scan_workspace_size(batch, dim, dstate, seqlen, dtype=torch.bfloat16, flags=0) -> int:
+    return lib().mss_selective_scan_workspace_size(batch, dim, dstate, seqlen, _io_code(dtype), flags)
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, *, return_last_state=False,
+                       force_general_decay=False, out=None, h_last=None, workspace=None, stream=None):
+    """Selective scan over the whole sequence.
+
+    u, delta, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16, all the same);
+    A: [d, N] float32; D: [d] float32; h0: [b, d, N] float32.
+    Returns y [b, d, L] (same dtype as u), and h_last [b, d, N] float32 when
+    ``return_last_state``.
+    """
+    dev = _device_of(u)
+    b, d, L = u.shape
+    N = A.shape[1]
+    io = u.dtype
+    _check(u, "u", (b, d, L), io, dev)
+    _check(delta, "delta", (b, d, L), io, dev)
+    _check(A, "A", (d, N), torch.float32, dev)
+    _check(B, "B", (b, N, L), io, dev)
+    _check(C, "C", (b, N, L), io, dev)
+    _check(D, "D", (d,), torch.float32, dev)
+    _check(z, "z", (b, d, L), io, dev)
+    _check(h0, "h0", (b, d, N), torch.float32, dev)
+    flags = MSS_FLAG_DECAY_GENERAL if force_general_decay else 0
+    code = _io_code(io)
+    if out is None:
+        out = torch.empty((b, d, L), dtype=io, device=dev)
+    _check(out, "out", (b, d, L), io, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((b, d, N), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", (b, d, N), torch.float32, dev)
+    need = lib().mss_selective_scan_workspace_size(b, d, N, L, code, flags)
+    if need == 0:
+        _raise(5, "selective_scan_fwd")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().mss_selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(out), _ptr(h_last), b, d, N, L, code, flags, _ptr(workspace),
+                                      workspace.numel(), _stream(stream))
+    _raise(st, "mss_selective_scan_fwd")
+    return (out, h_last) if return_last_state else out
+
+
+# -------------------------------------------------------------- state update
+def state_update(h, u, delta, A, B, C, D=None, z=None, *, out=None, stream=None):
+    """One generation step; ``h`` [b, d, N] float32 is updated in place.
+
+    u, delta, z: [b, d]; B, C: [b, N] (float32 or bfloat16); A: [d, N];
+    D: [d].  Returns y [b, d] in the I/O dtype."""
+    dev = _device_of(h)
+    b, d, N = h.shape
+    io = u.dtype
+    _check(h, "h", (b, d, N), torch.float32, dev)
+    _check(u, "u", (b, d), io, dev)
+    _check(delta, "delta", (b, d), io, dev)
+    _check(A, "A", (d, N), torch.float32, dev)
+    _check(B, "B", (b, N), io, dev)
+    _check(C, "C", (b, N), io, dev)
+    _check(D, "D", (d,), torch.float32, dev)
+    _check(z, "z", (b, d), io, dev)
+    if out is None:
+        out = torch.empty((b, d), dtype=io, device=dev)
+    _check(out, "out", (b, d), io, dev)
+    st = lib().mss_state_update(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(out), b, d, N, _io_code(io), 0, _stream(stream))
+    _raise(st, "mss_state_update")
+    return out
+
+
+# ----------------------------------------------------------------------- SSD
+def ssd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16) -> int:
+    return lib().mss_ssd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, _io_code(dtype))
+
+
+def ssd_chunk_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk=256, return_chunk_states=False,
+                  return_last_state=False, out=None, workspace=None, stream=None):
+    """Mamba-2 SSD layer.
+
+    x, z: [b, L, H, P] bfloat16; delta: [b, L, H] float32; A, D: [H] float32;
+    B, C: [b, L, G, N] bfloat16; h0: [b, H, P, N] float32.
+    Returns y [b, L, H, P] float32, plus chunk_states [b, nchunks, H, P, N]
+    and/or h_last [b, H, P, N] when requested (in that order)."""
+    dev = _device_of(x)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = x.dtype
+    _check(x, "x", (b, L, H, P), io, dev)
+    _check(delta, "delta", (b, L, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(B, "B", (b, L, G, N), io, dev)
+    _check(C, "C", (b, L, G, N), io, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(z, "z", (b, L, H, P), io, dev)
+    _check(h0, "h0", (b, H, P, N), torch.float32, dev)
+    code = _io_code(io)
+    nch = (L + chunk - 1) // chunk
+    if out is None:
+        out = torch.empty((b, L, H, P), dtype=torch.float32, device=dev)
+    _check(out, "out", (b, L, H, P), torch.float32, dev)
+    cs = torch.empty((b, nch, H, P, N), dtype=torch.float32, device=dev) if return_chunk_states else None
+    hl = torch.empty((b, H, P, N), dtype=torch.float32, device=dev) if return_last_state else None
+    need = lib().mss_ssd_workspace_size(b, L, H, P, G, N, chunk, code)
+    if need == 0:
+        _raise(5, "ssd_chunk_fwd")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().mss_ssd_chunk_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                 _ptr(out), _ptr(cs), _ptr(hl), b, L, H, P, G, N, chunk, code, 0, _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _raise(st, "mss_ssd_chunk_fwd")
+    res = [out]
+    if return_chunk_states:
+        res.append(cs)
+    if return_last_state:
+        res.append(hl)
+    return res[0] if len(res) == 1 else tuple(res)

@@ -1,0 +1,251 @@
+// C-ABI entry points of libmambascan: host-side validation, then launch.
+// Everything here runs on the host before any HIP call; on any error nothing
+// is enqueued and no output is touched.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mambascan.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(mss_dtype t) { return t == MSS_BF16 ? 2 : 4; }
+
+bool dtype_ok(mss_dtype t) { return t == MSS_FP32 || t == MSS_BF16; }
+
+// An output range must not overlap any of the listed (non-null) input ranges.
+bool output_clear(const void* out, size_t out_bytes, const void* const* ins, const size_t* in_bytes, int n) {
+  if (out == nullptr) return true;
+  const Range o = range_of(out, out_bytes);
+  for (int i = 0; i < n; ++i)
+    if (ins[i] != nullptr && overlaps(o, range_of(ins[i], in_bytes[i]))) return false;
+  return true;
+}
+
+mss_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MSS_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MSS_ERR_HIP;
+}
+
+constexpr int64_t kMaxIndex = INT32_MAX;
+
+}  // namespace
+
+extern "C" {
+
+const char* mss_status_string(mss_status s) {
+  switch (s) {
+    case MSS_OK: return "MSS_OK";
+    case MSS_ERR_NULL: return "MSS_ERR_NULL: a required pointer is NULL";
+    case MSS_ERR_SHAPE: return "MSS_ERR_SHAPE: a size is not positive or is too large";
+    case MSS_ERR_DTYPE: return "MSS_ERR_DTYPE: unknown dtype";
+    case MSS_ERR_ALIGN: return "MSS_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case MSS_ERR_UNSUPPORTED: return "MSS_ERR_UNSUPPORTED: shape or option not implemented";
+    case MSS_ERR_WORKSPACE: return "MSS_ERR_WORKSPACE: workspace missing or too small";
+    case MSS_ERR_ALIAS: return "MSS_ERR_ALIAS: an output overlaps an input";
+    case MSS_ERR_HIP: return "MSS_ERR_HIP: a HIP call failed";
+  }
+  return "unknown mss_status";
+}
+
+int mss_last_hip_error(void) { return g_last_hip_error; }
+
+int mss_abi_version(void) { return MSS_ABI_VERSION; }
+
+// ------------------------------------------------------------ selective scan
+static mss_status scan_check_shape(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype t) {
+  if (!dtype_ok(t)) return MSS_ERR_DTYPE;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return MSS_ERR_SHAPE;
+  if (batch > 65535 || seqlen > kMaxIndex || dim * seqlen > kMaxIndex || dim * dstate > kMaxIndex ||
+      batch * dim > kMaxIndex)
+    return MSS_ERR_SHAPE;
+  if (dstate > 64) return MSS_ERR_UNSUPPORTED;
+  return MSS_OK;
+}
+
+size_t mss_selective_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                         mss_dtype io_dtype, uint32_t flags) {
+  (void)flags;
+  if (scan_check_shape(batch, dim, dstate, seqlen, io_dtype) != MSS_OK) return 0;
+  return mss::scan_workspace_bytes(batch, dim, dstate, seqlen);
+}
+
+mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* h0, void* y, float* h_last,
+                                  int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype io_dtype,
+                                  uint32_t flags, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!u || !delta || !A || !B || !C || !y) return MSS_ERR_NULL;
+  mss_status st = scan_check_shape(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MSS_OK) return st;
+  if (flags & ~MSS_FLAG_DECAY_GENERAL) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {u, delta, A, B, C, D, z, h0, y, h_last, workspace};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t need = mss::scan_workspace_bytes(batch, dim, dstate, seqlen);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+
+  const size_t es = elem_size(io_dtype);
+  const size_t nbdl = (size_t)batch * dim * seqlen;
+  const size_t nbnl = (size_t)batch * dstate * seqlen;
+  const size_t nstate = (size_t)batch * dim * dstate * sizeof(float);
+  const void* ins[] = {u, delta, A, B, C, D, z, h0, workspace};
+  const size_t in_bytes[] = {nbdl * es, nbdl * es, (size_t)dim * dstate * 4, nbnl * es, nbnl * es,
+                             (size_t)dim * 4, nbdl * es, nstate, need};
+  if (!output_clear(y, nbdl * es, ins, in_bytes, 9)) return MSS_ERR_ALIAS;
+  if (!output_clear(h_last, nstate, ins, in_bytes, 9)) return MSS_ERR_ALIAS;
+  if (h_last && overlaps(range_of(y, nbdl * es), range_of(h_last, nstate))) return MSS_ERR_ALIAS;
+
+  mss::ScanParams p;
+  p.u = u;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.h0 = h0;
+  p.y = y;
+  p.h_last = h_last;
+  p.batch = batch;
+  p.dim = dim;
+  p.dstate = dstate;
+  p.seqlen = seqlen;
+  p.bf16 = io_dtype == MSS_BF16;
+  p.force_general = (flags & MSS_FLAG_DECAY_GENERAL) != 0;
+  p.workspace = workspace;
+  return hip_status(mss::launch_scan(p, static_cast<hipStream_t>(hip_stream)));
+}
+
+// -------------------------------------------------------------- state update
+mss_status mss_state_update(float* h, const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, void* y, int64_t batch, int64_t dim,
+                            int64_t dstate, mss_dtype io_dtype, uint32_t flags, void* hip_stream) {
+  if (!h || !u || !delta || !A || !B || !C || !y) return MSS_ERR_NULL;
+  if (!dtype_ok(io_dtype)) return MSS_ERR_DTYPE;
+  if (batch <= 0 || dim <= 0 || dstate <= 0) return MSS_ERR_SHAPE;
+  if (batch * dim * dstate > kMaxIndex * 4LL || batch * dim * 4 > kMaxIndex * 64LL) return MSS_ERR_SHAPE;
+  if (dstate > 64) return MSS_ERR_UNSUPPORTED;
+  if (flags != 0) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {h, u, delta, A, B, C, D, z, y};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t es = elem_size(io_dtype);
+  const size_t nbd = (size_t)batch * dim;
+  const size_t nstate = nbd * dstate * sizeof(float);
+  const void* ins[] = {u, delta, A, B, C, D, z};
+  const size_t in_bytes[] = {nbd * es, nbd * es, (size_t)dim * dstate * 4, (size_t)batch * dstate * es,
+                             (size_t)batch * dstate * es, (size_t)dim * 4, nbd * es};
+  if (!output_clear(h, nstate, ins, in_bytes, 7)) return MSS_ERR_ALIAS;
+  if (!output_clear(y, nbd * es, ins, in_bytes, 7)) return MSS_ERR_ALIAS;
+  if (overlaps(range_of(y, nbd * es), range_of(h, nstate))) return MSS_ERR_ALIAS;
+
+  mss::UpdateParams p;
+  p.h = h;
+  p.u = u;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.y = y;
+  p.batch = batch;
+  p.dim = dim;
+  p.dstate = dstate;
+  p.bf16 = io_dtype == MSS_BF16;
+  return hip_status(mss::launch_state_update(p, static_cast<hipStream_t>(hip_stream)));
+}
+
+// ----------------------------------------------------------------------- SSD
+static mss_status ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                  int64_t ngroups, int64_t dstate, int64_t chunk, mss_dtype t) {
+  if (!dtype_ok(t)) return MSS_ERR_DTYPE;
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || chunk <= 0)
+    return MSS_ERR_SHAPE;
+  if (seqlen * nheads * headdim > kMaxIndex || batch > 65535 || nheads > 65535) return MSS_ERR_SHAPE;
+  if (t != MSS_BF16) return MSS_ERR_UNSUPPORTED;
+  if (headdim != 64 || dstate != 128 || !(chunk == 64 || chunk == 128 || chunk == 256)) return MSS_ERR_UNSUPPORTED;
+  if (nheads % ngroups != 0) return MSS_ERR_UNSUPPORTED;
+  return MSS_OK;
+}
+
+size_t mss_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                              int64_t dstate, int64_t chunk, mss_dtype in_dtype) {
+  if (ssd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, in_dtype) != MSS_OK) return 0;
+  return mss::ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk);
+}
+
+mss_status mss_ssd_chunk_fwd(const void* x, const float* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* h0, float* y, float* chunk_states,
+                             float* h_last, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t ngroups, int64_t dstate, int64_t chunk, mss_dtype in_dtype, uint32_t flags,
+                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!x || !delta || !A || !B || !C || !y) return MSS_ERR_NULL;
+  mss_status st = ssd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, in_dtype);
+  if (st != MSS_OK) return st;
+  if (flags != 0) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {x, delta, A, B, C, D, z, h0, y, chunk_states, h_last, workspace};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t need = mss::ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, chunk);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+
+  const size_t es = elem_size(in_dtype);
+  const size_t nx = (size_t)batch * seqlen * nheads * headdim;
+  const size_t nbc = (size_t)batch * seqlen * ngroups * dstate;
+  const size_t nstate = (size_t)batch * nheads * headdim * dstate * sizeof(float);
+  const size_t nchunks = (size_t)((seqlen + chunk - 1) / chunk);
+  const void* ins[] = {x, delta, A, B, C, D, z, h0, workspace};
+  const size_t in_bytes[] = {nx * es, (size_t)batch * seqlen * nheads * 4, (size_t)nheads * 4, nbc * es,
+                             nbc * es, (size_t)nheads * 4, nx * es, nstate, need};
+  const void* outs[] = {y, chunk_states, h_last};
+  const size_t out_bytes[] = {nx * 4, nstate * nchunks, nstate};
+  for (int i = 0; i < 3; ++i) {
+    if (!output_clear(outs[i], out_bytes[i], ins, in_bytes, 9)) return MSS_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[i] && outs[j] && overlaps(range_of(outs[i], out_bytes[i]), range_of(outs[j], out_bytes[j])))
+        return MSS_ERR_ALIAS;
+  }
+
+  mss::SSDParams p;
+  p.x = x;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.h0 = h0;
+  p.y = y;
+  p.chunk_states = chunk_states;
+  p.h_last = h_last;
+  p.batch = batch;
+  p.seqlen = seqlen;
+  p.nheads = nheads;
+  p.headdim = headdim;
+  p.ngroups = ngroups;
+  p.dstate = dstate;
+  p.chunk = chunk;
+  p.workspace = workspace;
+  return hip_status(mss::launch_ssd(p, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

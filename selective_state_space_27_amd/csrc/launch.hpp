@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel files.
+// Arguments have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mss {
+
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;   // nullable
+  const void* z;    // nullable
+  const float* h0;  // nullable
+  void* y;
+  float* h_last;    // nullable
+  int64_t batch, dim, dstate, seqlen;
+  bool bf16;
+  bool force_general;
+  void* workspace;
+};
+
+size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
+hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
+
+struct UpdateParams {
+  float* h;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;  // nullable
+  const void* z;   // nullable
+  void* y;
+  int64_t batch, dim, dstate;
+  bool bf16;
+};
+
+hipError_t launch_state_update(const UpdateParams& p, hipStream_t stream);
+
+struct SSDParams {
+  const void* x;
+  const float* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* h0;       // nullable
+  float* y;
+  float* chunk_states;   // nullable
+  float* h_last;         // nullable
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate, chunk;
+  void* workspace;
+};
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                           int64_t ngroups, int64_t dstate, int64_t chunk);
+hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
+
+}  // namespace mss

@@ -1,0 +1,176 @@
+"""GPU parity of mss_selective_scan_fwd against the fp64 oracle.
+
+Tolerance: max |g - r| / max(|r|, rms(r)) <= 1e-4 for fp32 I/O and 2e-2 for
+bf16 I/O (bf16 outputs are rounded to nearest even; the oracle's are not).
+The oracle receives exactly the inputs the GPU receives (bf16 widened
+exactly).  Full-size workloads are compared on sampled channels, which the
+oracle computes independently (channels do not interact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_27_amd as mss
+from selective_state_space_27_amd import inputs as I
+from gpu_util import assert_close, dev, host64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, force_general=False, with_h0=False, drop=()):
+    io = x["io"]
+    g = {k: (None if k in drop else dev(x[k])) for k in ("u", "delta", "A", "B", "C", "D", "z")}
+    h0 = dev(x["h0"]) if with_h0 and x.get("h0") is not None else None
+    y, hl = mss.selective_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], h0,
+                                   return_last_state=True, force_general_decay=force_general)
+    torch.cuda.synchronize()
+    return y, hl
+
+
+def run_oracle(x, chans=None, with_h0=False, drop=()):
+    io = x["io"]
+    u, dl, z = I.to_f64(x["u"], io), I.to_f64(x["delta"], io), I.to_f64(x["z"], io)
+    A, B, C, D = x["A"].astype(np.float64), I.to_f64(x["B"], io), I.to_f64(x["C"], io), x["D"].astype(np.float64)
+    h0 = x["h0"].astype(np.float64) if with_h0 and x.get("h0") is not None else None
+    if "D" in drop:
+        D = None
+    if "z" in drop:
+        z = None
+    if chans is None:
+        return oracle.selective_scan(u, dl, A, B, C, D, z, h0)
+    ys, hs = [], []
+    for b, d in chans:   # one channel at a time: [1, 1, L]
+        y, h = oracle.selective_scan(u[b:b + 1, d:d + 1], dl[b:b + 1, d:d + 1], A[d:d + 1], B[b:b + 1], C[b:b + 1],
+                                     None if D is None else D[d:d + 1], None if z is None else z[b:b + 1, d:d + 1],
+                                     None if h0 is None else h0[b:b + 1, d:d + 1])
+        ys.append(y[0, 0])
+        hs.append(h[0, 0])
+    return np.stack(ys), np.stack(hs)
+
+
+@pytest.mark.parametrize("force_general", [False, True])
+def test_scan_tiny_workload(force_general):
+    x = I.scan_inputs(I.SCAN_TINY)
+    y, hl = run_gpu(x, force_general)
+    ry, rh = run_oracle(x)
+    print(f"tiny: y err {assert_close(host64(y), ry, 'fp32', 'y'):.2e}  h err {assert_close(host64(hl), rh, 'fp32', 'h_last'):.2e}")
+
+
+SHAPES = [
+    # b, d, N, L, io
+    (1, 16, 16, 64, "fp32"),
+    (2, 100, 16, 77, "fp32"),      # ragged channels and L (odd L: element loads)
+    (2, 130, 4, 50, "bf16"),
+    (1, 64, 1, 33, "fp32"),
+    (2, 70, 64, 40, "fp32"),
+    (1, 65, 64, 31, "bf16"),
+    (3, 64, 12, 100, "bf16"),
+    (1, 192, 16, 1, "fp32"),       # single step
+    (2, 64, 16, 15, "bf16"),       # shorter than one tile
+    (2, 64, 16, 300, "bf16"),      # several tiles and a ragged tail
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}d{}n{}l{}{}".format(*s))
+@pytest.mark.parametrize("force_general", [False, True])
+def test_scan_shapes_with_h0(shape, force_general):
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    y, hl = run_gpu(x, force_general, with_h0=True)
+    ry, rh = run_oracle(x, with_h0=True)
+    assert_close(host64(y), ry, io, "y")
+    assert_close(host64(hl), rh, "fp32" if io == "fp32" else "bf16", "h_last")
+
+
+@pytest.mark.parametrize("drop", [("D",), ("z",), ("D", "z")])
+def test_scan_optional_inputs(drop):
+    x = I.scan_inputs(I.small_scan_config(2, 96, 16, 70, "fp32"))
+    y, hl = run_gpu(x, drop=drop)
+    ry, rh = run_oracle(x, drop=drop)
+    assert_close(host64(y), ry, "fp32", "y")
+    assert_close(host64(hl), rh, "fp32", "h_last")
+
+
+def test_scan_general_a_matrix():
+    """A without the S4D-real structure takes the per-state exp path."""
+    x = I.scan_inputs(I.small_scan_config(2, 128, 16, 90, "fp32"))
+    g = np.random.default_rng(3)
+    x["A"] = (-np.exp(g.uniform(-1, 2, size=x["A"].shape))).astype(np.float32)
+    x["A"][:64] = -(np.arange(16, dtype=np.float32) + 1)    # first block S4D, second general
+    y, hl = run_gpu(x)
+    ry, rh = run_oracle(x)
+    assert_close(host64(y), ry, "fp32", "y")
+    assert_close(host64(hl), rh, "fp32", "h_last")
+
+
+def test_scan_130m_workload_full():
+    """b=8, d_inner=1536, N=16, L=2048, fp32: every output against the oracle."""
+    x = I.scan_inputs(I.SCAN_130M)
+    y, hl = run_gpu(x)
+    ry, rh = run_oracle(x)
+    e1 = assert_close(host64(y), ry, "fp32", "y")
+    e2 = assert_close(host64(hl), rh, "fp32", "h_last")
+    print(f"scan_130m: y err {e1:.2e}  h_last err {e2:.2e}")
+
+
+def test_scan_2p8b_workload_sampled():
+    """b=4, d_inner=5120, N=16, L=8192, bf16 I/O: the full launch, checked on
+    256 sampled channels (each computed by the oracle on its own)."""
+    x = I.scan_inputs(I.SCAN_2P8B)
+    y, hl = run_gpu(x)
+    g = np.random.default_rng(2024)
+    chans = [(int(b), int(d)) for b, d in zip(g.integers(0, 4, 256), g.integers(0, 5120, 256))]
+    chans += [(0, 0), (3, 5119), (1, 63), (2, 64)]
+    ry, rh = run_oracle(x, chans)
+    yg, hg = host64(y), host64(hl)
+    gy = np.stack([yg[b, d] for b, d in chans])
+    gh = np.stack([hg[b, d] for b, d in chans])
+    e1 = assert_close(gy, ry, "bf16", "y")
+    e2 = assert_close(gh, rh, "bf16", "h_last")
+    print(f"scan_2p8b sampled: y err {e1:.2e}  h_last err {e2:.2e}")
+    # Also the fp32-level accuracy of the state (not rounded to bf16 anywhere).
+    assert rel_err(gh, rh) < 1e-4
+
+
+def test_scan_deterministic_and_split_composition():
+    """Bitwise run-to-run determinism; and scan(L) == scan(L1) then
+    scan(L - L1, h0=h_last) bitwise (same arithmetic in the same order)."""
+    x = I.scan_inputs(I.small_scan_config(2, 128, 16, 200, "bf16"))
+    y1, h1 = run_gpu(x)
+    y2, h2 = run_gpu(x)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    for L1 in (64, 37):
+        a = dict(x)
+        c = dict(x)
+        for k in ("u", "delta", "B", "C", "z"):
+            a[k] = np.ascontiguousarray(x[k][..., :L1])
+            c[k] = np.ascontiguousarray(x[k][..., L1:])
+        ya, ha = run_gpu(a)
+        g = {k: dev(c[k]) for k in ("u", "delta", "A", "B", "C", "D", "z")}
+        yc, hc = mss.selective_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], ha,
+                                        return_last_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat([ya, yc], dim=2), y1), L1
+        assert torch.equal(hc, h1), L1
+
+
+def test_scan_causality_and_nan_propagation():
+    x = I.scan_inputs(I.small_scan_config(1, 64, 16, 96, "fp32"))
+    y, _ = run_gpu(x)
+    for t0 in (0, 17, 95):
+        x2 = dict(x)
+        x2["u"] = x["u"].copy()
+        x2["u"][0, 5, t0] += 2.0
+        y2, _ = run_gpu(x2)
+        assert torch.equal(y2[..., :t0], y[..., :t0])
+        assert not torch.equal(y2[0, 5, t0], y[0, 5, t0])
+    x3 = dict(x)
+    x3["u"] = x["u"].copy()
+    x3["u"][0, 9, 40] = np.nan
+    y3, h3 = run_gpu(x3)
+    y3 = y3.cpu()
+    assert torch.isnan(y3[0, 9, 40:]).all() and not torch.isnan(y3[0, 9, :40]).any()
+    others = torch.cat([y3[0, :9], y3[0, 10:]])
+    assert not torch.isnan(others).any()
+    assert torch.isnan(h3[0, 9]).all()
