@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the selective state space hot path on one MI355X.
+
+Default workload (the headline): the Mamba-2.8b-shaped selective scan,
+batch 4 x d_inner 5120 x d_state 16 x L 8192, bf16 u/delta/B/C/z/y, fp32 A/D
+and state.  One step = one mss_selective_scan_fwd call over the whole batch
+(all of its kernels), inputs resident in HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+prints ONE JSON line: state updates/s (B*L*D*N per second), the roofline of
+the dominant kernel (algorithmic bytes / event-timed launch duration against
+8 TB/s HBM3E) and the fp64 CPU oracle's throughput on a bounded sample of the
+same workload, timed on this host's cores.
+
+Other workloads (for the record in the design doc, not the headline):
+  scan_130m    b8 x d1536 x N16 x L2048, fp32 I/O
+  decode_2p8b  b256 x d5120 x N16 one-token steps, bf16 I/O; one step = 1000 tokens
+  ssd_2p8b     b2 x L16384 x H80 x P64 x N128, chunk 256 (Mamba-2 SSD)
+  copy         a plain 1 GiB device copy (calibrates the HBM byte counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+METRIC = "state updates/s (B*L*D*N) + % HBM roofline, Mamba-2.8b-shaped scan"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="scan_2p8b",
+                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "copy"])
+    ap.add_argument("--force-general-decay", action="store_true",
+                    help="scan: per-state exp decay even where A has the S4D-real structure")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------- byte counts ----
+def scan_bytes(b, d, n, L, es):
+    """Algorithmic bytes: u, delta, z read and y written once ([b,d,L]), B and C
+    read once ([b,n,L]), A [d,n] and D [d] fp32 read once."""
+    return 4 * b * d * L * es + 2 * b * n * L * es + d * n * 4 + d * 4
+
+
+def decode_step_bytes(b, d, n, es):
+    """Per token step: state read + written (fp32), u/delta/z/y, B/C, A, D."""
+    return 2 * b * d * n * 4 + 4 * b * d * es + 2 * b * n * es + d * n * 4 + d * 4
+
+
+def ssd_bytes(b, L, H, P, G, N, es):
+    """x and B, C read once (bf16), delta (fp32), A, y written once (fp32)."""
+    return b * L * H * P * es + 2 * b * L * G * N * es + b * L * H * 4 + H * 4 + b * L * H * P * 4
+
+
+# ------------------------------------------------------- traffic record -----
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "selective_state_space_27_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, files):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash(files):
+        return None
+    return float(m_val.group(1))
+
+
+# ------------------------------------------------------------ workloads -----
+def to_dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def time_region(torch, fn, steps, warmup):
+    """Event-timed region on the current stream (the library launches there)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def bench_scan(args, torch, mss, I, cfg):
+    x = I.scan_inputs(cfg)
+    g = {k: to_dev(torch, x[k]) for k in ("u", "delta", "A", "B", "C", "D", "z")}
+    io_dt = g["u"].dtype
+    b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    ws = torch.empty(mss.selective_scan_workspace_size(b, d, n, L, io_dt), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(g["u"])
+
+    def step():
+        mss.selective_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], out=out, workspace=ws,
+                               force_general_decay=args.force_general_decay)
+
+    ms = time_region(torch, step, args.steps, args.warmup)
+    updates = b * d * n * L
+    es = 2 if cfg.io == "bf16" else 4
+    nbytes = scan_bytes(b, d, n, L, es)
+    res = {
+        "metric": METRIC, "value": updates / (ms * 1e-3), "unit": "state updates/s", "ms_per_step": ms,
+        "dtype": "f32",
+        "config": {"workload": f"{cfg.name}: selective scan b={b} d_inner={d} d_state={n} L={L}, "
+                               f"{cfg.io} u/delta/B/C/z/y, fp32 A/D/state",
+                   "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io_dtype": cfg.io,
+                   "decay": "per-state exp (forced)" if args.force_general_decay else
+                            "power chain (S4D-real structure detected on device)"},
+    }
+    files = ["scan.hip", "common.hpp"]
+    kernel = "scan_kernel (+ bc_transpose_kernel, s4d_check_kernel in the same timed call)"
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = list(range(min(2, b)))          # bounded sample: the first two batch rows, every channel, full L
+        f64 = lambda k: I.to_f64(x[k][rows], cfg.io)
+        args64 = (f64("u"), f64("delta"), x["A"].astype(np.float64), f64("B"), f64("C"), x["D"].astype(np.float64),
+                  f64("z"))
+        th = cpu_threads()
+        t = time.perf_counter()
+        oracle.selective_scan(*args64, threads=th)
+        dt = time.perf_counter() - t
+        cpu = {"value": len(rows) * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"batch rows {rows} of {b} (all {d} channels, full L={L}); {dt:.2f} s wall, fp64 C oracle"}
+    return res, nbytes, ms, kernel, files, cpu
+
+
+def bench_decode(args, torch, mss, I):
+    cfg = I.DECODE_2P8B
+    st = I.decode_static(cfg)
+    pool = [I.decode_step_inputs(cfg, s, st["dt"]) for s in range(I.DECODE_POOL)]
+    dpool = [{k: to_dev(torch, p[k]) for k in ("u", "delta", "B", "C", "z")} for p in pool]
+    h = to_dev(torch, I.decode_state0(cfg))
+    A, D = to_dev(torch, st["A"]), to_dev(torch, st["D"])
+    y = torch.empty((cfg.batch, cfg.dim), dtype=torch.bfloat16, device="cuda:0")
+
+    def step():  # 1000 consecutive generation steps
+        for s in range(cfg.steps):
+            p = dpool[s % I.DECODE_POOL]
+            mss.state_update(h, p["u"], p["delta"], A, p["B"], p["C"], D, p["z"], out=y)
+
+    steps = max(1, args.steps // 10)
+    ms = time_region(torch, step, steps, max(1, args.warmup // 5))
+    b, d, n = cfg.batch, cfg.dim, cfg.dstate
+    updates = b * d * n * cfg.steps
+    res = {"metric": "state updates/s (B*D*N per token step), one-token generation", "value": updates / (ms * 1e-3),
+           "unit": "state updates/s", "ms_per_step": ms, "dtype": "f32",
+           "config": {"workload": f"{cfg.name}: state update b={b} d_inner={d} d_state={n}, 1000 consecutive tokens, "
+                                  "bf16 u/delta/B/C/z/y, fp32 state in place", "batch": b, "d_inner": d, "d_state": n,
+                      "tokens_per_step": cfg.steps}}
+    nbytes = decode_step_bytes(b, d, n, 2)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        h64 = I.decode_state0(cfg).astype(np.float64)[:32]
+        th = cpu_threads()
+        t = time.perf_counter()
+        for s in range(20):
+            p = pool[s % I.DECODE_POOL]
+            h64, _ = oracle.state_update(h64, I.to_f64(p["u"][:32], "bf16"), I.to_f64(p["delta"][:32], "bf16"), st["A"],
+                                         I.to_f64(p["B"][:32], "bf16"), I.to_f64(p["C"][:32], "bf16"), st["D"],
+                                         I.to_f64(p["z"][:32], "bf16"), threads=th)
+        dt = time.perf_counter() - t
+        cpu = {"value": 32 * d * n * 20 / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"batch rows 0-31 of {b}, 20 token steps; {dt:.2f} s wall"}
+    # per-launch figures: one launch = one token step
+    return res, nbytes, ms / cfg.steps, "state_update_kernel", ["state_update.hip", "common.hpp"], cpu
+
+
+def bench_ssd(args, torch, mss, I):
+    cfg = I.SSD_2P8B
+    x = I.ssd_inputs(cfg)
+    g = {k: to_dev(torch, x[k]) for k in ("x", "delta", "A", "B", "C")}
+    b, L, H, P, G, N, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.chunk
+    ws = torch.empty(mss.ssd_workspace_size(b, L, H, P, G, N, Q), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty((b, L, H, P), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        mss.ssd_chunk_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], chunk=Q, out=out, workspace=ws)
+
+    ms = time_region(torch, step, args.steps, args.warmup)
+    updates = b * L * H * P * N
+    res = {"metric": "state updates/s (B*L*H*P*N), Mamba-2 SSD layer", "value": updates / (ms * 1e-3),
+           "unit": "state updates/s", "ms_per_step": ms, "dtype": "bf16 MFMA operands, f32 accumulate",
+           "config": {"workload": f"{cfg.name}: SSD b={b} L={L} H={H} P={P} G={G} N={N} chunk={Q}, bf16 x/B/C, "
+                                  "fp32 delta/y/states", "batch": b, "seqlen": L, "nheads": H, "headdim": P,
+                      "d_state": N, "chunk": Q}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        Ls = 2048
+        th = cpu_threads()
+        args64 = (I.to_f64(x["x"][:1, :Ls], "bf16"), x["delta"][:1, :Ls].astype(np.float64), x["A"],
+                  I.to_f64(x["B"][:1, :Ls], "bf16"), I.to_f64(x["C"][:1, :Ls], "bf16"))
+        t = time.perf_counter()
+        oracle.ssd(*args64, threads=th)
+        dt = time.perf_counter() - t
+        cpu = {"value": Ls * H * P * N / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"batch row 0, first {Ls} of {L} steps, all heads; {dt:.2f} s wall"}
+    return res, ssd_bytes(b, L, H, P, G, N, 2), ms, "ssd kernels", ["ssd.hip", "common.hpp"], cpu
+
+
+def bench_copy(args, torch):
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    c = torch.empty_like(a)
+    ms = time_region(torch, lambda: c.copy_(a), args.steps, args.warmup)
+    res = {"metric": "device copy GB/s (read + write)", "value": 2 * n * 4 / (ms * 1e-3) / 1e9, "unit": "GB/s",
+           "ms_per_step": ms, "dtype": "f32", "config": {"workload": "copy: 1 GiB fp32 device-to-device"}}
+    return res, 2 * n * 4, ms, "copy", [], None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the hot path shards over batch and channels with no communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, ROOT)
+    import selective_state_space_27_amd as mss
+    from selective_state_space_27_amd import inputs as I
+
+    if args.workload == "scan_2p8b":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_2P8B)
+    elif args.workload == "scan_130m":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_130M)
+    elif args.workload == "decode_2p8b":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_decode(args, torch, mss, I)
+    elif args.workload == "ssd_2p8b":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_ssd(args, torch, mss, I)
+    else:
+        res, nbytes, launch_ms, kernel, files, cpu = bench_copy(args, torch)
+
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(args.workload, files) if files else None
+    line = {
+        "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic (seeded generator, workload shapes)",
+        "config": res["config"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

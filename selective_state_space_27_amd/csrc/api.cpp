@@ -74,7 +74,7 @@ int mss_abi_version(void) { return MSS_ABI_VERSION; }
 static mss_status scan_check_shape(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype t) {
   if (!dtype_ok(t)) return MSS_ERR_DTYPE;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return MSS_ERR_SHAPE;
-  if (batch > 65535 || seqlen > kMaxIndex || dim * seqlen > kMaxIndex || dim * dstate > kMaxIndex ||
+  if (batch > 65535 || seqlen >= (1LL << 24) || dim * seqlen > kMaxIndex || dim * dstate > kMaxIndex ||
       batch * dim > kMaxIndex)
     return MSS_ERR_SHAPE;
   if (dstate > 64) return MSS_ERR_UNSUPPORTED;

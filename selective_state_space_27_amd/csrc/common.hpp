@@ -39,3 +39,50 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float silu(float z) { return z * rcp_fast(1.0f + exp2_fast(-z * kLog2e)); }
 
 }  // namespace mss
+
+namespace mss {
+
+// Raw buffer descriptors: an access whose byte offset is at or beyond
+// `bytes` reads 0 and a store there is dropped, so tails and inactive lanes
+// need no branches (branch-free loads keep the in-order vmcnt bookkeeping
+// precise, which lets loads issued several tiles ahead stay in flight).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every descriptor used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t buf_load_u32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 buf_load_u32x2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_load_u32x4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u32(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u16(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u32x2(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+
+// Broadcast lane P of each row of 16 lanes to the whole row (DPP row_newbcast).
+// Used as the first operand of a multiply, the move folds into v_mul_f32_dpp.
+template <int P>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + P, 0xf, 0xf, false));
+}
+
+}  // namespace mss

@@ -16,19 +16,25 @@
 // processed in tiles of 16 steps with one barrier per tile:
 //   prologue (all 512 threads, one (channel, 2 steps) item each): widen u and
 //     delta, x = delta*u and the decay table for the tile into LDS;
-//   core (each wave, its SPW states, 16 sequential steps): B and C of the step
-//     come in through SGPRs from a pre-transposed fp32 copy; partial readouts
-//     go to LDS;
+//   core (each wave, its SPW states, 16 sequential steps): B and C are shared
+//     by every channel, so each lane loads a few of them (fp32, pre-arranged
+//     by bc_transpose_kernel) and the multiplies take them from lane p of the
+//     row with a DPP row broadcast (v_mul_f32_dpp row_newbcast:p); partial
+//     readouts go to LDS;
 //   epilogue (all threads, same items as the prologue): sum the 8 partial
 //     readouts in a fixed order, add D*u, gate with silu(z), store y.
 // The prologue of tile k+1 and the epilogue of tile k run in the same loop
-// iteration as the core of tile k; global loads are issued three tiles ahead.
+// iteration as the core of tile k.  Streams are read with branch-free buffer
+// loads issued three tiles ahead (B/C two tiles ahead) into fixed register
+// slots: the loop is unrolled by three so nothing in flight is ever copied,
+// which keeps the in-order vmcnt waits from draining the prefetch.
 //
 // Decay.  Where every channel of the block has A[d,n] == (n+1)*A[d,0] (the
 // S4D-real structure, checked on the device), the prologue computes one
 // r = exp2(delta*A[d,0]*log2 e) per (d,l) and the start power r^(g*SPW+1) of
 // each wave's states; the waves continue the power chain with multiplies.
 // Elsewhere each wave evaluates exp2(delta*A[d,n]*log2 e) per state.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -54,75 +60,123 @@ struct ScanArgs {
   const float* h0;
   void* y;
   float* h_last;
-  const float* bc;     // [batch][8][lpad][2*SPW]: B then C of each wave's states, fp32
+  const float* bc;     // B and C per wave and tile, fp32, in the layout bc_index() describes
   const int* s4d_ok;   // [nblocks]
-  int batch, dim, dstate, seqlen, lpad;
+  float* carry;        // [streams][8 waves][SPW][64 lanes] state handed between workgroups
+  int* flags;          // [streams] carry ready; [streams] = spin-limit error; [streams + 1] = ticket
+  int* ticket;
+  int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
   int force_general;
 };
 
-// Raw (undecoded) loads of two consecutive steps of one row.
-template <bool BF16>
-struct Raw;
-template <>
-struct Raw<true> {
-  uint32_t w;
-};
-template <>
-struct Raw<false> {
-  float2 w;
+constexpr int kMaxSpins = 1 << 22;
+
+// B/C values a wave needs per 4-step block: 4 steps x (SPW B values, SPW C
+// values) = 8*SPW, spread over NV VGPRs of 16 row positions each.
+template <int SPW>
+struct BCShape {
+  static constexpr int kPerBlk = 8 * SPW;
+  static constexpr int kNV = kPerBlk <= 16 ? 1 : kPerBlk / 16;
+  static constexpr int kPerTile = kNV * 16 * kBlk;  // floats per (batch, wave, tile)
 };
 
-template <bool BF16, bool VEC>
-__device__ __forceinline__ Raw<BF16> load_raw(const void* base, size_t row, int t, int L, bool ok) {
-  Raw<BF16> r;
-  if constexpr (BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + row;
-    if (VEC) {
-      r.w = (ok && t < L) ? *reinterpret_cast<const uint32_t*>(p + t) : 0u;  // L even: t+1 < L too
-    } else {
-      uint32_t lo = (ok && t < L) ? p[t] : 0u;
-      uint32_t hi = (ok && t + 1 < L) ? p[t + 1] : 0u;
-      r.w = lo | (hi << 16);
-    }
-  } else {
-    const float* p = static_cast<const float*>(base) + row;
-    if (VEC) {
-      r.w = (ok && t < L) ? *reinterpret_cast<const float2*>(p + t) : make_float2(0.f, 0.f);
-    } else {
-      r.w.x = (ok && t < L) ? p[t] : 0.f;
-      r.w.y = (ok && t + 1 < L) ? p[t + 1] : 0.f;
-    }
-  }
-  return r;
+// Workspace B/C layout: [batch][wave g][tile][v][row position p][blk].  Lane
+// with row position p loads the float4 over blk, so for block `blk` value i =
+// v*16 + p (step i / (2*SPW), quantity i % (2*SPW): B of states g*SPW.., then
+// C) sits in component blk of VGPR v at row position p.
+template <int SPW>
+__device__ __forceinline__ size_t bc_index(int b, int g, int tile, int ntiles, int v, int p, int blk) {
+  using S = BCShape<SPW>;
+  return ((((size_t)b * kWaves + g) * ntiles + tile) * S::kNV + v) * 64 + p * 4 + blk;
 }
 
-__device__ __forceinline__ float2 decode(const Raw<true>& r) { return make_float2(bf16_lo(r.w), bf16_hi(r.w)); }
-__device__ __forceinline__ float2 decode(const Raw<false>& r) { return r.w; }
+__device__ __forceinline__ float row_bcast_rt(float v, int p) {
+  switch (p) {
+    case 0: return row_bcast<0>(v);
+    case 1: return row_bcast<1>(v);
+    case 2: return row_bcast<2>(v);
+    case 3: return row_bcast<3>(v);
+    case 4: return row_bcast<4>(v);
+    case 5: return row_bcast<5>(v);
+    case 6: return row_bcast<6>(v);
+    case 7: return row_bcast<7>(v);
+    case 8: return row_bcast<8>(v);
+    case 9: return row_bcast<9>(v);
+    case 10: return row_bcast<10>(v);
+    case 11: return row_bcast<11>(v);
+    case 12: return row_bcast<12>(v);
+    case 13: return row_bcast<13>(v);
+    case 14: return row_bcast<14>(v);
+    default: return row_bcast<15>(v);
+  }
+}
 
+// Raw (undecoded) words of four consecutive steps of one row.
 template <bool BF16>
-__device__ __forceinline__ void store_pair(void* base, size_t row, int t, int L, bool ok, float v0, float v1) {
-  if (!ok || t >= L) return;
-  if constexpr (BF16) {
-    uint16_t* p = static_cast<uint16_t*>(base) + row;
-    if (t + 1 < L && ((row + t) & 1) == 0) {
-      *reinterpret_cast<uint32_t*>(p + t) = pack_bf16x2(v0, v1);
+struct Raw4;
+template <>
+struct Raw4<true> {
+  u32x2 w;
+};
+template <>
+struct Raw4<false> {
+  u32x4 w;
+};
+
+// Branch-free load of steps t..t+3 of this lane's row; out-of-range steps read 0.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ Raw4<BF16> load_raw4(rsrc_t r, uint32_t lane_off, int t, int L, bool ok) {
+  constexpr uint32_t es = BF16 ? 2 : 4;
+  Raw4<BF16> res;
+  if constexpr (VEC) {  // L % 4 == 0: the four steps are all in range or all out
+    const uint32_t o = (ok && t < L) ? lane_off + (uint32_t)t * es : kOffNone;
+    if constexpr (BF16) res.w = buf_load_u32x2(r, o);
+    else res.w = buf_load_u32x4(r, o);
+  } else {
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (ok && t + i < L) ? lane_off + (uint32_t)(t + i) * es : kOffNone;
+    if constexpr (BF16) {
+      res.w.x = (uint32_t)buf_load_u16(r, o[0]) | ((uint32_t)buf_load_u16(r, o[1]) << 16);
+      res.w.y = (uint32_t)buf_load_u16(r, o[2]) | ((uint32_t)buf_load_u16(r, o[3]) << 16);
     } else {
-      p[t] = f32_to_bf16(v0);
-      if (t + 1 < L) p[t + 1] = f32_to_bf16(v1);
+      res.w.x = buf_load_u32(r, o[0]);
+      res.w.y = buf_load_u32(r, o[1]);
+      res.w.z = buf_load_u32(r, o[2]);
+      res.w.w = buf_load_u32(r, o[3]);
+    }
+  }
+  return res;
+}
+
+__device__ __forceinline__ f32x4 decode4(const Raw4<true>& r) {
+  return f32x4{bf16_lo(r.w.x), bf16_hi(r.w.x), bf16_lo(r.w.y), bf16_hi(r.w.y)};
+}
+__device__ __forceinline__ f32x4 decode4(const Raw4<false>& r) { return __builtin_bit_cast(f32x4, r.w); }
+
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void store4(rsrc_t r, uint32_t lane_off, int t, int L, bool ok, f32x4 v) {
+  constexpr uint32_t es = BF16 ? 2 : 4;
+  if constexpr (VEC) {
+    const uint32_t o = (ok && t < L) ? lane_off + (uint32_t)t * es : kOffNone;
+    if constexpr (BF16) {
+      buf_store_u32x2(r, o, u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)});
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)o, 0, 0);
     }
   } else {
-    float* p = static_cast<float*>(base) + row;
-    if (t + 1 < L && ((row + t) & 1) == 0) {
-      *reinterpret_cast<float2*>(p + t) = make_float2(v0, v1);
-    } else {
-      p[t] = v0;
-      if (t + 1 < L) p[t + 1] = v1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = (ok && t + i < L) ? lane_off + (uint32_t)(t + i) * es : kOffNone;
+      if constexpr (BF16) buf_store_u16(r, o, f32_to_bf16(v[i]));
+      else buf_store_u32(r, o, __float_as_uint(v[i]));
     }
   }
 }
 
 // LDS: per buffer, kQMax quantities x kBlk x 64 lanes x float4 (4 steps), and
-// 8 waves x kBlk x 64 lanes x float4 of partial readouts.
+// 8 waves x kBlk x 64 lanes x float4 of partial readouts.  Every access is a
+// whole float4 of one lane, consecutive lanes at consecutive 16-byte slots.
 constexpr int kQFloats = kQMax * kBlk * kLanes * 4;
 constexpr int kPFloats = kWaves * kBlk * kLanes * 4;
 
@@ -130,220 +184,319 @@ __device__ __forceinline__ int q_off(int q, int blk, int lane) { return ((q * kB
 
 template <bool BF16, int SPW, bool VEC>
 __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
+  using S = BCShape<SPW>;
+  constexpr int NV = S::kNV;
+  constexpr uint32_t es = BF16 ? 2 : 4;
   __shared__ __attribute__((aligned(16))) float qbuf[2][kQFloats];
   __shared__ __attribute__((aligned(16))) float pbuf[2][kPFloats];
+  __shared__ int sh_ticket;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave id, uniform
-  const int blk_id = blockIdx.x;
-  const int b = blockIdx.y;
-  const int c = blk_id * kLanes + lane;  // channel of this lane
-  const bool cok = c < a.dim;
   const int L = a.seqlen, N = a.dstate;
-  const size_t row = ((size_t)b * a.dim + (cok ? c : 0)) * (size_t)L;
-  const bool s4d = !a.force_general && a.s4d_ok[blk_id] != 0;
-
-  // Per-lane constants.
-  const float a20 = cok ? a.A[(size_t)c * N] * kLog2e : 0.f;
-  const float dskip = (a.D != nullptr && cok) ? a.D[c] : 0.f;
-  float A2[SPW];
+  const bool has_z = a.z != nullptr;
+  // Waves 0-3 prepare tiles (prologue), waves 4-7 finish them (epilogue); each
+  // thread owns one channel and the 4 steps of block `role_blk` of every tile.
+  const bool is_pro = w < kBlk;
+  const int role_blk = is_pro ? w : w - kBlk;
+  const int e = is_pro ? 0 : 1;
+  const int p16 = lane & 15;
+  const int ntiles = a.ntiles;
+  const uint32_t lane_off = (uint32_t)lane * (uint32_t)L * es;
   float h[SPW];
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int n = w * SPW + j;
-    A2[j] = (cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
-    h[j] = (a.h0 != nullptr && cok && n < N) ? a.h0[((size_t)b * a.dim + c) * N + n] : 0.f;
-  }
 
-  const int ntiles = (L + kTile - 1) / kTile;
-  // Item of this thread in prologue/epilogue: channel `c`, steps t0 + 2w, t0 + 2w + 1.
-  const int tt = 2 * w;
-
-  Raw<BF16> ru[kPrefetch], rd[kPrefetch], rz[kPrefetch];
-#pragma unroll
-  for (int k = 0; k < kPrefetch; ++k) {
-    const int t = k * kTile + tt;
-    ru[k] = load_raw<BF16, VEC>(a.u, row, t, L, cok);
-    rd[k] = load_raw<BF16, VEC>(a.delta, row, t, L, cok);
-    if (a.z) rz[k] = load_raw<BF16, VEC>(a.z, row, t, L, cok);
-  }
-
-  float2 u_keep = make_float2(0.f, 0.f), z_keep = make_float2(0.f, 0.f);
-
-  // Prologue of one tile from the oldest prefetched raw values into qbuf[buf].
-  auto prologue = [&](int buf) {
-    const float2 uu = decode(ru[0]);
-    const float2 dd = decode(rd[0]);
-    float* q = qbuf[buf];
-    const int blk = tt >> 2, sub = tt & 3;
-    const float2 x = make_float2(dd.x * uu.x, dd.y * uu.y);
-    *reinterpret_cast<float2*>(&q[q_off(0, blk, lane) + sub]) = x;
-    if (s4d) {
-      const float2 r = make_float2(exp2_fast(dd.x * a20), exp2_fast(dd.y * a20));
-      *reinterpret_cast<float2*>(&q[q_off(1, blk, lane) + sub]) = r;
-      float2 step = r;  // r^SPW
-#pragma unroll
-      for (int j = 1; j < SPW; ++j) step = make_float2(step.x * r.x, step.y * r.y);
-      float2 s = r;     // r^(g*SPW + 1)
-#pragma unroll
-      for (int g = 0; g < kWaves; ++g) {
-        *reinterpret_cast<float2*>(&q[q_off(2 + g, blk, lane) + sub]) = s;
-        s = make_float2(s.x * step.x, s.y * step.y);
-      }
-    } else {
-      *reinterpret_cast<float2*>(&q[q_off(1, blk, lane) + sub]) = dd;
-    }
-    u_keep = uu;
-    if (a.z) z_keep = decode(rz[0]);
-  };
-
-  // Rotate the prefetch ring and issue the loads for tile `tile`.
-  auto advance = [&](int tile) {
-#pragma unroll
-    for (int k = 0; k + 1 < kPrefetch; ++k) {
-      ru[k] = ru[k + 1];
-      rd[k] = rd[k + 1];
-      if (a.z) rz[k] = rz[k + 1];
-    }
-    const int t = tile * kTile + tt;
-    ru[kPrefetch - 1] = load_raw<BF16, VEC>(a.u, row, t, L, cok);
-    rd[kPrefetch - 1] = load_raw<BF16, VEC>(a.delta, row, t, L, cok);
-    if (a.z) rz[kPrefetch - 1] = load_raw<BF16, VEC>(a.z, row, t, L, cok);
-  };
-
-  const float* bc_wave = a.bc + ((size_t)b * kWaves + w) * (size_t)a.lpad * (2 * SPW);
-
-  // Core: this wave's SPW states over the 16 steps of one tile.  B and C of
-  // four steps (4 * 2 * SPW floats) are fetched with wide scalar loads.
-  auto core_tile = [&](auto guard_tag, int buf, int t0) {
-    constexpr bool GUARD = decltype(guard_tag)::value;
-    const float* q = qbuf[buf];
-    float* pp = pbuf[buf];
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    typedef const __attribute__((address_space(4))) f4* cf4_ptr;
-    cf4_ptr bcs = (cf4_ptr)(bc_wave + (size_t)t0 * (2 * SPW));
-#pragma unroll
-    for (int blk = 0; blk < kBlk; ++blk) {
-      f4 bcv[2 * SPW];  // 4 steps x (B[SPW], C[SPW])
-#pragma unroll
-      for (int i = 0; i < 2 * SPW; ++i) bcv[i] = bcs[blk * 2 * SPW + i];
-      const float* bcf = reinterpret_cast<const float*>(bcv);
-      const float4 xv = *reinterpret_cast<const float4*>(&q[q_off(0, blk, lane)]);
-      const float4 rv = *reinterpret_cast<const float4*>(&q[q_off(1, blk, lane)]);
-      float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s4d) sv = *reinterpret_cast<const float4*>(&q[q_off(2 + w, blk, lane)]);
-      float part[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float x = (&xv.x)[kk];
-        const float r = (&rv.x)[kk];  // r (S4D) or delta (general)
-        const float* bt = bcf + kk * 2 * SPW;
-        float p = 0.f;
-        if (!GUARD || t0 + blk * 4 + kk < L) {
-          if (s4d) {
-            float dec = (&sv.x)[kk];
-#pragma unroll
-            for (int j = 0; j < SPW; ++j) {
-              if (j > 0) dec *= r;
-              h[j] = __builtin_fmaf(dec, h[j], x * bt[j]);
-              p = __builtin_fmaf(bt[SPW + j], h[j], p);
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < SPW; ++j) {
-              const float dec = exp2_fast(r * A2[j]);
-              h[j] = __builtin_fmaf(dec, h[j], x * bt[j]);
-              p = __builtin_fmaf(bt[SPW + j], h[j], p);
-            }
-          }
-        }
-        part[kk] = p;
-      }
-      *reinterpret_cast<float4*>(&pp[q_off(w, blk, lane)]) = make_float4(part[0], part[1], part[2], part[3]);
-    }
-  };
-
-  prologue(0);
-  float2 u_cur = u_keep, z_cur = z_keep;
-  advance(kPrefetch);
+  // Logical workgroup id in start order (a ticket), so the workgroup a carry
+  // is waited for has always started before the one that waits.
+  if (threadIdx.x == 0) sh_ticket = atomicAdd(a.ticket, 1);
   __syncthreads();
+  const int wg_id = sh_ticket;
 
-  for (int k = 0; k < ntiles; ++k) {
-    const int buf = k & 1;
-    const int t0 = k * kTile;
-    if (k + 1 < ntiles) {
-      prologue(buf ^ 1);
-      advance(k + 1 + kPrefetch);
-    }
+  // One piece of work: stream s (batch row, 64-channel block), tiles [tb, te).
+  auto run_piece = [&](int s, int tb, int te, bool carry_in, bool carry_out) {
+    const int b = s / a.nblocks, cb = s % a.nblocks;
+    const int c = cb * kLanes + lane;  // channel of this lane
+    const bool cok = c < a.dim;
+    const bool s4d = !a.force_general && a.s4d_ok[cb] != 0;
 
-    // ---- core: this wave's states over the 16 steps of tile k ----
-    if (t0 + kTile <= L)
-      core_tile(std::false_type{}, buf, t0);
-    else
-      core_tile(std::true_type{}, buf, t0);
-    __syncthreads();
+    // Descriptors over this block's rows [b, cb*64 .. +nch, 0..L).
+    const int nch = min(kLanes, a.dim - cb * kLanes);
+    const size_t base_el = ((size_t)b * a.dim + (size_t)cb * kLanes) * (size_t)L;
+    const uint32_t rows_bytes = (uint32_t)nch * (uint32_t)L * es;
+    const rsrc_t ru_d = make_rsrc(static_cast<const char*>(a.u) + base_el * es, rows_bytes);
+    const rsrc_t rd_d = make_rsrc(static_cast<const char*>(a.delta) + base_el * es, rows_bytes);
+    const rsrc_t rz_d =
+        make_rsrc(has_z ? static_cast<const char*>(a.z) + base_el * es : nullptr, has_z ? rows_bytes : 0u);
+    const rsrc_t ry_d = make_rsrc(static_cast<char*>(a.y) + base_el * es, rows_bytes);
+    const rsrc_t r2_d = is_pro ? rd_d : rz_d;  // second stream of this wave: delta or z
+    const rsrc_t rbc = make_rsrc(a.bc + bc_index<SPW>(b, w, 0, ntiles, 0, 0, 0),
+                                 (uint32_t)ntiles * S::kPerTile * (uint32_t)sizeof(float));
 
-    // ---- epilogue of tile k: items (c, t0 + tt, t0 + tt + 1) ----
-    {
-      const float* pp = pbuf[buf];
-      const int blk = tt >> 2, sub = tt & 3;
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int g = 0; g < kWaves; ++g) {
-        const float2 v = *reinterpret_cast<const float2*>(&pp[q_off(g, blk, lane) + sub]);
-        s0 += v.x;
-        s1 += v.y;
-      }
-      float o0 = __builtin_fmaf(dskip, u_cur.x, s0);
-      float o1 = __builtin_fmaf(dskip, u_cur.y, s1);
-      if (a.z) {
-        o0 *= silu(z_cur.x);
-        o1 *= silu(z_cur.y);
-      }
-      store_pair<BF16>(a.y, row, t0 + tt, L, cok, o0, o1);
-    }
-    u_cur = u_keep;
-    z_cur = z_keep;
-  }
-
-  if (a.h_last != nullptr && cok) {
+    // Per-lane constants.
+    const float a20 = cok ? a.A[(size_t)c * N] * kLog2e : 0.f;
+    const float dskip = (a.D != nullptr && cok) ? a.D[c] : 0.f;
+    float A2[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int n = w * SPW + j;
-      if (n < N) a.h_last[((size_t)b * a.dim + c) * N + n] = h[j];
+      A2[j] = (cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
     }
+
+    // Initial state: the carry published by the workgroup that ran the first
+    // part of this stream, else h0 (or zero).
+    float* carry = a.carry + ((size_t)s * kWaves + w) * SPW * kLanes;
+    if (carry_in) {
+      if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(a.flags + s, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          __builtin_amdgcn_s_sleep(4);
+          if (++spins > kMaxSpins) {  // never expected; keeps every wait finite
+            __hip_atomic_store(a.flags + a.batch * a.nblocks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+        h[j] = __hip_atomic_load(carry + j * kLanes + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int n = w * SPW + j;
+        h[j] = (a.h0 != nullptr && cok && n < N) ? a.h0[((size_t)b * a.dim + c) * N + n] : 0.f;
+      }
+    }
+
+    auto load_bc = [&](int tile, int te_, f32x4* dst) {
+      const uint32_t tile_ok = tile < te_ ? 1u : 0u;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t off = tile_ok ? (uint32_t)(((size_t)tile * NV + v) * 64 + p16 * 4) * 4u : kOffNone;
+        dst[v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
+      }
+    };
+
+    auto run = [&](auto s4d_tag, int tb, int te) {
+      constexpr bool S4D = decltype(s4d_tag)::value;
+      // Prefetch rings, three slots per stream.  Prologue waves keep tile t in
+      // slot t % 3, epilogue waves in slot (t + 1) % 3 (e = 1 below): then in
+      // every step all waves consume and refill the same compile-time slot, and
+      // the tile loop (unrolled by 3) never copies a register whose load is in
+      // flight nor branches around a load.  Stream 1 is u for every wave, stream
+      // 2 is delta (prologue waves) or z (epilogue waves).
+      Raw4<BF16> r1[kPrefetch], r2[kPrefetch];
+      f32x4 bcr[kPrefetch][NV];
+      auto load_tile = [&](int tile, int slot) {
+        const int t = tile * kTile + role_blk * 4;
+        const bool ok = cok && tile >= tb && tile < te;
+        r1[slot] = load_raw4<BF16, VEC>(ru_d, lane_off, t, L, ok);
+        r2[slot] = load_raw4<BF16, VEC>(r2_d, lane_off, t, L, ok);
+      };
+#pragma unroll
+      for (int sl = 0; sl < kPrefetch; ++sl) load_tile(tb + sl - e, sl);
+      load_bc(tb, te, bcr[0]);
+      load_bc(tb + 1, te, bcr[1]);
+
+      // Prologue (waves 0-3) of one tile from ring slot `slot` into qbuf[buf].
+      auto prologue = [&](int buf, int slot) {
+        const f32x4 uu = decode4(r1[slot]);
+        const f32x4 dd = decode4(r2[slot]);
+        float* q = qbuf[buf];
+        *reinterpret_cast<f32x4*>(&q[q_off(0, role_blk, lane)]) = dd * uu;
+        if constexpr (S4D) {
+          f32x4 r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
+          *reinterpret_cast<f32x4*>(&q[q_off(1, role_blk, lane)]) = r;
+          f32x4 step = r;  // r^SPW
+#pragma unroll
+          for (int j = 1; j < SPW; ++j) step = step * r;
+          f32x4 sp = r;    // r^(wave*SPW + 1)
+#pragma unroll
+          for (int wv = 0; wv < kWaves; ++wv) {
+            *reinterpret_cast<f32x4*>(&q[q_off(2 + wv, role_blk, lane)]) = sp;
+            sp = sp * step;
+          }
+        } else {
+          *reinterpret_cast<f32x4*>(&q[q_off(1, role_blk, lane)]) = dd;
+        }
+      };
+
+      // Epilogue (waves 4-7) of tile k: channel c, steps t0 + 4*role_blk .. +3.
+      auto epilogue = [&](int buf, int slot, int t0) {
+        const float* pp = pbuf[buf];
+        f32x4 acc = *reinterpret_cast<const f32x4*>(&pp[q_off(0, role_blk, lane)]);
+#pragma unroll
+        for (int wv = 1; wv < kWaves; ++wv) acc += *reinterpret_cast<const f32x4*>(&pp[q_off(wv, role_blk, lane)]);
+        const f32x4 uu = decode4(r1[slot]);
+        const f32x4 zz = decode4(r2[slot]);
+        f32x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = __builtin_fmaf(dskip, uu[i], acc[i]);
+          out[i] = has_z ? o * silu(zz[i]) : o;
+        }
+        store4<BF16, VEC>(ry_d, lane_off, t0 + role_blk * 4, L, cok, out);
+      };
+
+      // Core: this wave's SPW states over the 16 steps of one tile.
+      auto core_tile = [&](auto guard_tag, int buf, int t0, const f32x4* bc_cur) {
+        constexpr bool GUARD = decltype(guard_tag)::value;
+        const float* q = qbuf[buf];
+        float* pp = pbuf[buf];
+        f32x4 xv[kBlk], rv[kBlk], sv[kBlk];
+#pragma unroll
+        for (int blk = 0; blk < kBlk; ++blk) {
+          xv[blk] = *reinterpret_cast<const f32x4*>(&q[q_off(0, blk, lane)]);
+          rv[blk] = *reinterpret_cast<const f32x4*>(&q[q_off(1, blk, lane)]);
+          if constexpr (S4D) sv[blk] = *reinterpret_cast<const f32x4*>(&q[q_off(2 + w, blk, lane)]);
+          else sv[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int blk = 0; blk < kBlk; ++blk) {
+          f32x4 part;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const float x = xv[blk][kk];
+            const float r = rv[blk][kk];  // r (S4D) or delta (general)
+            float p = 0.f;
+            if (!GUARD || t0 + blk * 4 + kk < L) {
+              float dec = sv[blk][kk];
+#pragma unroll
+              for (int j = 0; j < SPW; ++j) {
+                const int ib = kk * 2 * SPW + j;  // B of state j at step kk
+                const int ic = ib + SPW;          // C of state j at step kk
+                if constexpr (S4D) {
+                  if (j > 0) dec *= r;
+                } else {
+                  dec = exp2_fast(r * A2[j]);
+                }
+                const float bx = row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x;
+                h[j] = __builtin_fmaf(dec, h[j], bx);
+                const float ch = row_bcast_rt(bc_cur[ic / 16][blk], ic % 16) * h[j];
+                p = (j == 0) ? ch : p + ch;
+              }
+            }
+            part[kk] = p;
+          }
+          *reinterpret_cast<f32x4*>(&pp[q_off(w, blk, lane)]) = part;
+        }
+      };
+
+      if (is_pro) prologue(tb & 1, 0);
+      load_tile(tb + kPrefetch - e, 0);
+      __syncthreads();
+
+      // One tile: S = k % 3 is a compile-time ring slot.  The prologue of tile
+      // k+1 and the epilogue of tile k both read slot S+1, which is then refilled
+      // with tile k+4 (prologue waves) or k+3 (epilogue waves).
+      auto tile_step = [&](auto slot_tag, int k) {
+        constexpr int S = decltype(slot_tag)::value;
+        constexpr int S1 = (S + 1) % kPrefetch, S2 = (S + 2) % kPrefetch;
+        const int buf = k & 1;
+        const int t0 = k * kTile;
+        // Past the last tile these loads read zeros (out-of-range offsets) and the
+        // prologue fills an LDS buffer nobody reads; running them unconditionally
+        // keeps the loop body free of branches around loads.
+        load_bc(k + 2, te, bcr[S2]);
+        if (is_pro) prologue(buf ^ 1, S1);
+        if (t0 + kTile <= L)
+          core_tile(std::false_type{}, buf, t0, bcr[S]);
+        else
+          core_tile(std::true_type{}, buf, t0, bcr[S]);
+        __syncthreads();
+        if (!is_pro) epilogue(buf, S1, t0);
+        load_tile(k + 1 + kPrefetch - e, S1);
+      };
+
+      int k = tb;
+      for (; k + kPrefetch <= te; k += kPrefetch) {
+        tile_step(std::integral_constant<int, 0>{}, k);
+        tile_step(std::integral_constant<int, 1>{}, k + 1);
+        tile_step(std::integral_constant<int, 2>{}, k + 2);
+      }
+      if (k < te) tile_step(std::integral_constant<int, 0>{}, k);
+      if (k + 1 < te) tile_step(std::integral_constant<int, 1>{}, k + 1);
+    };
+
+    if (s4d)
+      run(std::true_type{}, tb, te);
+    else
+      run(std::false_type{}, tb, te);
+
+    if (carry_out) {  // publish the state after tile te-1 for the next workgroup
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) carry[j * kLanes + lane] = h[j];
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(a.flags + s, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (te == ntiles && a.h_last != nullptr && cok) {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int n = w * SPW + j;
+        if (n < N) a.h_last[((size_t)b * a.dim + c) * N + n] = h[j];
+      }
+    }
+  };
+
+  // Balanced split: workgroup g owns tiles [g*W/G, (g+1)*W/G) of the
+  // concatenation of all streams (W = streams * ntiles, G = workgroups).  With
+  // at least as many streams as workgroups every range spans a stream end, so
+  // it consists of: the tail of its first stream (which continues the state
+  // the previous workgroup reached), whole streams, and the head of its last
+  // stream (whose end state the next workgroup continues from).  The head is
+  // run first and its state published at once; the tail is run last.
+  const int64_t nstreams = (int64_t)a.batch * a.nblocks;
+  const int64_t wtot = nstreams * ntiles;
+  const int64_t r0 = (int64_t)wg_id * wtot / a.nwg, r1 = (int64_t)(wg_id + 1) * wtot / a.nwg;
+  const int s_first = (int)(r0 / ntiles), s_last = (int)((r1 - 1) / ntiles);
+  const int off_first = (int)(r0 - (int64_t)s_first * ntiles);
+  const int end_last = (int)(r1 - (int64_t)s_last * ntiles);
+  if (s_first == s_last) {
+    run_piece(s_first, off_first, end_last, off_first > 0, end_last < ntiles);
+  } else {
+    run_piece(s_last, 0, end_last, false, end_last < ntiles);
+    for (int s = s_first + 1; s < s_last; ++s) run_piece(s, 0, ntiles, false, false);
+    run_piece(s_first, off_first, ntiles, off_first > 0, false);
   }
 }
 
-// B, C [batch, N, L] (bf16 or fp32) -> fp32 [batch][8][lpad][2*SPW] with zero
-// padding for n >= N and l >= L.  One thread per (b, wave group, l).
+// B, C [batch, N, L] (bf16 or fp32) -> fp32 workspace in the bc_index layout,
+// zero for n >= N, l >= L and unused row positions.  One thread per float.
+// The same launch clears the carry flags, the error word and the ticket.
 template <bool BF16, int SPW>
 __global__ void bc_transpose_kernel(const void* __restrict__ B, const void* __restrict__ C,
-                                    float* __restrict__ out, int batch, int N, int L, int lpad) {
+                                    float* __restrict__ out, int batch, int N, int L, int ntiles,
+                                    int* __restrict__ flags, int nflags) {
+  using S = BCShape<SPW>;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t total = (size_t)batch * kWaves * lpad;
+  for (size_t i = idx; i < (size_t)nflags; i += (size_t)gridDim.x * blockDim.x) flags[i] = 0;
+  const size_t total = (size_t)batch * kWaves * ntiles * S::kPerTile;
   if (idx >= total) return;
-  const int l = (int)(idx % lpad);
-  const int g = (int)((idx / lpad) % kWaves);
-  const int b = (int)(idx / ((size_t)lpad * kWaves));
-  float* o = out + idx * (2 * SPW);
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int n = g * SPW + j;
-    float bv = 0.f, cv = 0.f;
+  const int blk = (int)(idx % 4);
+  const int p = (int)((idx / 4) % 16);
+  size_t rest = idx / 64;
+  const int v = (int)(rest % S::kNV);
+  rest /= S::kNV;
+  const int tile = (int)(rest % ntiles);
+  rest /= ntiles;
+  const int g = (int)(rest % kWaves);
+  const int b = (int)(rest / kWaves);
+  const int i = v * 16 + p;
+  float val = 0.f;
+  if (i < S::kPerBlk) {
+    const int kk = i / (2 * SPW), qn = i % (2 * SPW);
+    const int l = tile * kTile + blk * 4 + kk;
+    const bool isC = qn >= SPW;
+    const int n = g * SPW + (isC ? qn - SPW : qn);
     if (n < N && l < L) {
       const size_t off = ((size_t)b * N + n) * L + l;
-      if (BF16) {
-        bv = bf16_to_f32(static_cast<const uint16_t*>(B)[off]);
-        cv = bf16_to_f32(static_cast<const uint16_t*>(C)[off]);
-      } else {
-        bv = static_cast<const float*>(B)[off];
-        cv = static_cast<const float*>(C)[off];
-      }
+      const void* src = isC ? C : B;
+      val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(src)[off]) : static_cast<const float*>(src)[off];
     }
-    o[j] = bv;
-    o[SPW + j] = cv;
   }
+  out[idx] = val;
 }
 
 // s4d_ok[blk] = 1 when A[d,n] == (n+1)*A[d,0] (exactly, in fp32) for every
@@ -360,22 +513,38 @@ __global__ void s4d_check_kernel(const float* __restrict__ A, int* __restrict__ 
 }
 
 int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : 8; }
-int64_t padded_len(int64_t L) { return (L + kTile - 1) / kTile * kTile; }
+int64_t num_tiles(int64_t L) { return (L + kTile - 1) / kTile; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t carry_floats(int spw, int64_t batch, int64_t dim) {
+  return (size_t)batch * ((dim + kLanes - 1) / kLanes) * kWaves * spw * kLanes;
+}
+size_t flag_ints(int64_t batch, int64_t dim) { return (size_t)batch * ((dim + kLanes - 1) / kLanes) + 2; }
+size_t bc_floats(int spw, int64_t batch, int64_t L) {
+  const int per_tile = spw == 1 ? BCShape<1>::kPerTile : spw == 2 ? BCShape<2>::kPerTile
+                     : spw == 4 ? BCShape<4>::kPerTile : BCShape<8>::kPerTile;
+  return (size_t)batch * kWaves * num_tiles(L) * per_tile;
+}
 
 template <bool BF16, int SPW>
 hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
-  const int64_t lpad = padded_len(p.seqlen);
+  const int64_t ntiles = num_tiles(p.seqlen);
   const int nblocks = (int)((p.dim + kLanes - 1) / kLanes);
   char* ws = static_cast<char*>(p.workspace);
   float* bc = reinterpret_cast<float*>(ws);
-  int* ok = reinterpret_cast<int*>(ws + align256((size_t)p.batch * kWaves * lpad * 2 * SPW * sizeof(float)));
+  const size_t nbc = bc_floats(SPW, p.batch, p.seqlen);
+  size_t off = align256(nbc * sizeof(float));
+  int* ok = reinterpret_cast<int*>(ws + off);
+  off += align256((size_t)nblocks * sizeof(int));
+  float* carry = reinterpret_cast<float*>(ws + off);
+  off += align256(carry_floats(SPW, p.batch, p.dim) * sizeof(float));
+  int* flags = reinterpret_cast<int*>(ws + off);
+  const int64_t nstreams = p.batch * nblocks;
 
   {
-    const size_t total = (size_t)p.batch * kWaves * lpad;
-    const unsigned grid = (unsigned)((total + 255) / 256);
+    const unsigned grid = (unsigned)((nbc + 255) / 256);
     hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(grid), dim3(256), 0, stream, p.B, p.C, bc,
-                       (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)lpad);
+                       (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles, flags,
+                       (int)flag_ints(p.batch, p.dim));
   }
   hipLaunchKernelGGL(s4d_check_kernel, dim3(nblocks), dim3(kLanes), 0, stream, p.A, ok, (int)p.dim,
                      (int)p.dstate);
@@ -395,10 +564,21 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.dim = (int)p.dim;
   a.dstate = (int)p.dstate;
   a.seqlen = (int)p.seqlen;
-  a.lpad = (int)lpad;
+  a.ntiles = (int)ntiles;
+  a.carry = carry;
+  a.flags = flags;
+  a.ticket = flags + nstreams + 1;
+  a.nblocks = nblocks;
+  // One workgroup per compute unit at most (the kernel's LDS allows one), so
+  // the balanced split below covers the chip in a single wave of workgroups.
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  a.nwg = (int)std::min<int64_t>(nstreams, std::max(cus, 1));
   a.force_general = p.force_general ? 1 : 0;
-  const dim3 grid(nblocks, (unsigned)p.batch);
-  if (p.seqlen % 2 == 0)
+  const dim3 grid((unsigned)a.nwg);
+  if (p.seqlen % 4 == 0)
     hipLaunchKernelGGL((scan_kernel<BF16, SPW, true>), grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((scan_kernel<BF16, SPW, false>), grid, dim3(kThreads), 0, stream, a);
@@ -418,10 +598,10 @@ hipError_t launch_dtype(const ScanParams& p, hipStream_t stream) {
 }  // namespace
 
 size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
-  const int spw = states_per_wave(dstate);
-  const int64_t lpad = padded_len(seqlen);
   const int64_t nblocks = (dim + kLanes - 1) / kLanes;
-  return align256((size_t)batch * kWaves * lpad * 2 * spw * sizeof(float)) + align256((size_t)nblocks * sizeof(int));
+  const int spw = states_per_wave(dstate);
+  return align256(bc_floats(spw, batch, seqlen) * sizeof(float)) + align256((size_t)nblocks * sizeof(int)) +
+         align256(carry_floats(spw, batch, dim) * sizeof(float)) + align256(flag_ints(batch, dim) * sizeof(int));
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {

@@ -83,6 +83,22 @@ def test_scan_shapes_with_h0(shape, force_general):
     assert_close(host64(hl), rh, "fp32" if io == "fp32" else "bf16", "h_last")
 
 
+@pytest.mark.parametrize("shape", [(2, 12800, 16, 45, "bf16"), (1, 16448, 16, 64, "fp32"), (3, 8200, 4, 37, "fp32")],
+                         ids=lambda s: "b{}d{}n{}l{}{}".format(*s))
+def test_scan_more_blocks_than_cus(shape):
+    """More 64-channel blocks than compute units: the work is split evenly
+    over one workgroup per CU, so sequences are cut mid-way and the state is
+    handed from one workgroup to the next (ragged L, h0 and h_last included)."""
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    y, hl = run_gpu(x, with_h0=True)
+    ry, rh = run_oracle(x, with_h0=True)
+    assert_close(host64(y), ry, io, "y")
+    assert_close(host64(hl), rh, "fp32" if io == "fp32" else "bf16", "h_last")
+    y2, h2 = run_gpu(x, with_h0=True)
+    assert torch.equal(y, y2) and torch.equal(hl, h2)
+
+
 @pytest.mark.parametrize("drop", [("D",), ("z",), ("D", "z")])
 def test_scan_optional_inputs(drop):
     x = I.scan_inputs(I.small_scan_config(2, 96, 16, 70, "fp32"))
