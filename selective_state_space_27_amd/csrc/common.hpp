@@ -80,9 +80,25 @@ __device__ __forceinline__ void buf_store_u32x2(rsrc_t r, uint32_t off, u32x2 v)
 
 // Broadcast lane P of each row of 16 lanes to the whole row (DPP row_newbcast).
 // Used as the first operand of a multiply, the move folds into v_mul_f32_dpp.
+// Every lane has a valid source, so bound_ctrl is set: the move then needs no
+// zeroed destination register when it cannot be folded.
 template <int P>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + P, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + P, 0xf, 0xf, true));
+}
+
+
+// acc + (lane P of each 16-lane row of v, broadcast) * h as one
+// v_fmac_f32_dpp, which the compiler does not form from a DPP move and a
+// multiply-add.  The broadcast operand v is only ever a register filled by a
+// buffer load, never one written by a VALU instruction just before (that
+// would need wait states the compiler does not insert around inline assembly).
+template <int P>
+__device__ __forceinline__ float fmac_row_bcast(float acc, float v, float h) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(acc)
+      : "v"(v), "v"(h), "i"(P));
+  return acc;
 }
 
 }  // namespace mss

@@ -9,25 +9,24 @@
 // stays in registers (section 2 figure: many steps combined on-chip, only the
 // outputs written back).
 //
-// Mapping on CDNA4.  One workgroup = 8 wave64s = one block of 64 channels of
-// one batch row.  Lanes are channels; the d_state states are split across the
-// 8 waves (SPW = ceil(N/8) states per wave), so 8 waves (2 per SIMD) share one
-// channel block and each wave's sequential chain is 1/8 of the work.  Time is
-// processed in tiles of 16 steps with one barrier per tile:
-//   prologue (all 512 threads, one (channel, 2 steps) item each): widen u and
-//     delta, x = delta*u and the decay table for the tile into LDS;
-//   core (each wave, its SPW states, 16 sequential steps): B and C are shared
-//     by every channel, so each lane loads a few of them (fp32, pre-arranged
-//     by bc_transpose_kernel) and the multiplies take them from lane p of the
-//     row with a DPP row broadcast (v_mul_f32_dpp row_newbcast:p); partial
-//     readouts go to LDS;
-//   epilogue (all threads, same items as the prologue): sum the 8 partial
-//     readouts in a fixed order, add D*u, gate with silu(z), store y.
-// The prologue of tile k+1 and the epilogue of tile k run in the same loop
-// iteration as the core of tile k.  Streams are read with branch-free buffer
-// loads issued three tiles ahead (B/C two tiles ahead) into fixed register
-// slots: the loop is unrolled by three so nothing in flight is ever copied,
-// which keeps the in-order vmcnt waits from draining the prefetch.
+// Mapping on CDNA4.  One workgroup = 16 wave64s working on one block of 64
+// channels of one batch row, time in tiles of 16 steps, one barrier per tile:
+//   8 core waves: lanes are channels; the d_state states are split across the
+//     waves (SPW = ceil(N/8) each), so every wave's sequential chain is 1/8 of
+//     the work.  B and C are shared by every channel: each lane loads a few
+//     (fp32, pre-arranged by bc_transpose_kernel) and the multiplies take them
+//     from lane p of the row with a DPP row broadcast (v_mul_f32_dpp /
+//     v_fmac_f32_dpp row_newbcast:p).  Partial readouts go to LDS.
+//   4 prologue waves: for tile k+1, x = delta*u and the decay data into LDS.
+//   4 epilogue waves: for tile k-1, the 8 partial readouts summed in a fixed
+//     order, plus D*u, gated by silu(z), stored.
+// Prologue and epilogue threads own one channel and 4 steps of a tile, so the
+// four lanes of a channel read or write its 16-step row segment in one
+// instruction.  Streams are read with branch-free buffer loads issued three
+// tiles ahead into fixed register slots: the loops are unrolled by three so
+// nothing in flight is ever copied, which keeps the in-order vmcnt waits from
+// draining the prefetch.  Four waves per SIMD give the issue slack a single
+// wave (one VALU instruction per 8 cycles at most) does not have.
 //
 // Decay.  Where every channel of the block has A[d,n] == (n+1)*A[d,0] (the
 // S4D-real structure, checked on the device), the prologue computes one
@@ -43,9 +42,10 @@
 namespace mss {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;    // core waves: the d_state states split across them
+constexpr int kIoWaves = 4;  // prologue waves, and as many epilogue waves
 constexpr int kLanes = 64;
-constexpr int kThreads = kWaves * kLanes;
+constexpr int kThreads = (kWaves + 2 * kIoWaves) * kLanes;
 constexpr int kTile = 16;          // time steps per tile
 constexpr int kBlk = kTile / 4;    // float4 blocks per tile
 constexpr int kQMax = 2 + kWaves;  // LDS quantities per (d,l): x, r, 8 start powers
@@ -88,6 +88,27 @@ template <int SPW>
 __device__ __forceinline__ size_t bc_index(int b, int g, int tile, int ntiles, int v, int p, int blk) {
   using S = BCShape<SPW>;
   return ((((size_t)b * kWaves + g) * ntiles + tile) * S::kNV + v) * 64 + p * 4 + blk;
+}
+
+__device__ __forceinline__ float fmac_row_bcast_rt(float acc, float v, float h, int p) {
+  switch (p) {
+    case 0: return fmac_row_bcast<0>(acc, v, h);
+    case 1: return fmac_row_bcast<1>(acc, v, h);
+    case 2: return fmac_row_bcast<2>(acc, v, h);
+    case 3: return fmac_row_bcast<3>(acc, v, h);
+    case 4: return fmac_row_bcast<4>(acc, v, h);
+    case 5: return fmac_row_bcast<5>(acc, v, h);
+    case 6: return fmac_row_bcast<6>(acc, v, h);
+    case 7: return fmac_row_bcast<7>(acc, v, h);
+    case 8: return fmac_row_bcast<8>(acc, v, h);
+    case 9: return fmac_row_bcast<9>(acc, v, h);
+    case 10: return fmac_row_bcast<10>(acc, v, h);
+    case 11: return fmac_row_bcast<11>(acc, v, h);
+    case 12: return fmac_row_bcast<12>(acc, v, h);
+    case 13: return fmac_row_bcast<13>(acc, v, h);
+    case 14: return fmac_row_bcast<14>(acc, v, h);
+    default: return fmac_row_bcast<15>(acc, v, h);
+  }
 }
 
 __device__ __forceinline__ float row_bcast_rt(float v, int p) {
@@ -174,13 +195,17 @@ __device__ __forceinline__ void store4(rsrc_t r, uint32_t lane_off, int t, int L
   }
 }
 
-// LDS: per buffer, kQMax quantities x kBlk x 64 lanes x float4 (4 steps), and
-// 8 waves x kBlk x 64 lanes x float4 of partial readouts.  Every access is a
-// whole float4 of one lane, consecutive lanes at consecutive 16-byte slots.
-constexpr int kQFloats = kQMax * kBlk * kLanes * 4;
-constexpr int kPFloats = kWaves * kBlk * kLanes * 4;
+// LDS: per buffer, kQMax quantities x kBlk x channels x float4 (4 steps), and
+// 8 waves x kBlk x channels x float4 of partial readouts.  The channel
+// dimension is padded to kRowPad slots: the core accesses (lane = channel,
+// one 4-step block) stay contiguous, and the prologue/epilogue accesses (four
+// lanes per channel, one per block; the block stride is 64 bytes modulo 256)
+// fall on 16 distinct 16-byte bank groups per 16 lanes.
+constexpr int kRowPad = kLanes + 4;
+constexpr int kQFloats = kQMax * kBlk * kRowPad * 4;
+constexpr int kPFloats = kWaves * kBlk * kRowPad * 4;
 
-__device__ __forceinline__ int q_off(int q, int blk, int lane) { return ((q * kBlk + blk) * kLanes + lane) * 4; }
+__device__ __forceinline__ int q_off(int q, int blk, int ch) { return ((q * kBlk + blk) * kRowPad + ch) * 4; }
 
 template <bool BF16, int SPW, bool VEC>
 __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
@@ -193,16 +218,21 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave id, uniform
+  const bool is_core = w < kWaves;
+  const bool is_pro = !is_core && w < kWaves + kIoWaves;
+  const int wc = is_core ? w : 0;  // core wave index (states wc*SPW ..)
   const int L = a.seqlen, N = a.dstate;
   const bool has_z = a.z != nullptr;
-  // Waves 0-3 prepare tiles (prologue), waves 4-7 finish them (epilogue); each
-  // thread owns one channel and the 4 steps of block `role_blk` of every tile.
-  const bool is_pro = w < kBlk;
-  const int role_blk = is_pro ? w : w - kBlk;
-  const int e = is_pro ? 0 : 1;
+  // Prologue and epilogue waves: a thread owns channel io_ch of the block and
+  // the 4-step block io_blk of every tile, so four consecutive lanes cover one
+  // channel's 16 steps and each global access instruction moves 16 whole row
+  // segments.
+  const int io = is_core ? 0 : (w - kWaves) % kIoWaves;
+  const int io_ch = io * 16 + (lane >> 2);
+  const int io_blk = lane & 3;
   const int p16 = lane & 15;
   const int ntiles = a.ntiles;
-  const uint32_t lane_off = (uint32_t)lane * (uint32_t)L * es;
+  const uint32_t io_off = (uint32_t)io_ch * (uint32_t)L * es;
   float h[SPW];
 
   // Logical workgroup id in start order (a ticket), so the workgroup a carry
@@ -212,10 +242,12 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   const int wg_id = sh_ticket;
 
   // One piece of work: stream s (batch row, 64-channel block), tiles [tb, te).
-  auto run_piece = [&](int s, int tb, int te, bool carry_in, bool carry_out) {
+  auto run_piece = [&](int s, int tb, int te, bool carry_in, bool carry_out) __attribute__((always_inline)) {
     const int b = s / a.nblocks, cb = s % a.nblocks;
-    const int c = cb * kLanes + lane;  // channel of this lane
+    const int c = cb * kLanes + lane;     // channel of this lane in the core
     const bool cok = c < a.dim;
+    const int c_io = cb * kLanes + io_ch;  // channel of this thread's I/O items
+    const bool iok = c_io < a.dim;
     const bool s4d = !a.force_general && a.s4d_ok[cb] != 0;
 
     // Descriptors over this block's rows [b, cb*64 .. +nch, 0..L).
@@ -227,23 +259,23 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     const rsrc_t rz_d =
         make_rsrc(has_z ? static_cast<const char*>(a.z) + base_el * es : nullptr, has_z ? rows_bytes : 0u);
     const rsrc_t ry_d = make_rsrc(static_cast<char*>(a.y) + base_el * es, rows_bytes);
-    const rsrc_t r2_d = is_pro ? rd_d : rz_d;  // second stream of this wave: delta or z
-    const rsrc_t rbc = make_rsrc(a.bc + bc_index<SPW>(b, w, 0, ntiles, 0, 0, 0),
+    const rsrc_t rbc = make_rsrc(a.bc + bc_index<SPW>(b, wc, 0, ntiles, 0, 0, 0),
                                  (uint32_t)ntiles * S::kPerTile * (uint32_t)sizeof(float));
 
-    // Per-lane constants.
-    const float a20 = cok ? a.A[(size_t)c * N] * kLog2e : 0.f;
-    const float dskip = (a.D != nullptr && cok) ? a.D[c] : 0.f;
+    // Per-thread constants: the prologue channel's A[., 0], the epilogue
+    // channel's D, the core channel's A row for this wave's states.
+    const float a20 = (is_pro && iok) ? a.A[(size_t)c_io * N] * kLog2e : 0.f;
+    const float dskip = (!is_core && !is_pro && a.D != nullptr && iok) ? a.D[c_io] : 0.f;
     float A2[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-      const int n = w * SPW + j;
-      A2[j] = (cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
+      const int n = wc * SPW + j;
+      A2[j] = (is_core && cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
     }
 
     // Initial state: the carry published by the workgroup that ran the first
     // part of this stream, else h0 (or zero).
-    float* carry = a.carry + ((size_t)s * kWaves + w) * SPW * kLanes;
+    float* carry = a.carry + ((size_t)s * kWaves + wc) * SPW * kLanes;
     if (carry_in) {
       if (threadIdx.x == 0) {
         int spins = 0;
@@ -256,112 +288,67 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         }
       }
       __syncthreads();
+      if (is_core) {
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-        h[j] = __hip_atomic_load(carry + j * kLanes + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+        for (int j = 0; j < SPW; ++j)
+          h[j] = __hip_atomic_load(carry + j * kLanes + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (is_core) {
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
-        const int n = w * SPW + j;
+        const int n = wc * SPW + j;
         h[j] = (a.h0 != nullptr && cok && n < N) ? a.h0[((size_t)b * a.dim + c) * N + n] : 0.f;
       }
     }
 
-    auto load_bc = [&](int tile, int te_, f32x4* dst) {
-      const uint32_t tile_ok = tile < te_ ? 1u : 0u;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const uint32_t off = tile_ok ? (uint32_t)(((size_t)tile * NV + v) * 64 + p16 * 4) * 4u : kOffNone;
-        dst[v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
-      }
-    };
-
-    auto run = [&](auto s4d_tag, int tb, int te) {
+    // ---- core waves: this wave's SPW states of the block's 64 channels ----
+    auto core_run = [&](auto s4d_tag) __attribute__((always_inline)) {
       constexpr bool S4D = decltype(s4d_tag)::value;
-      // Prefetch rings, three slots per stream.  Prologue waves keep tile t in
-      // slot t % 3, epilogue waves in slot (t + 1) % 3 (e = 1 below): then in
-      // every step all waves consume and refill the same compile-time slot, and
-      // the tile loop (unrolled by 3) never copies a register whose load is in
-      // flight nor branches around a load.  Stream 1 is u for every wave, stream
-      // 2 is delta (prologue waves) or z (epilogue waves).
-      Raw4<BF16> r1[kPrefetch], r2[kPrefetch];
+      // B/C ring, three slots (tile t in slot (t - tb) % 3), two tiles ahead.
       f32x4 bcr[kPrefetch][NV];
-      auto load_tile = [&](int tile, int slot) {
-        const int t = tile * kTile + role_blk * 4;
-        const bool ok = cok && tile >= tb && tile < te;
-        r1[slot] = load_raw4<BF16, VEC>(ru_d, lane_off, t, L, ok);
-        r2[slot] = load_raw4<BF16, VEC>(r2_d, lane_off, t, L, ok);
-      };
+      auto load_bc = [&](int tile, f32x4* dst) {
+        const uint32_t tile_ok = tile < te ? 1u : 0u;
 #pragma unroll
-      for (int sl = 0; sl < kPrefetch; ++sl) load_tile(tb + sl - e, sl);
-      load_bc(tb, te, bcr[0]);
-      load_bc(tb + 1, te, bcr[1]);
-
-      // Prologue (waves 0-3) of one tile from ring slot `slot` into qbuf[buf].
-      auto prologue = [&](int buf, int slot) {
-        const f32x4 uu = decode4(r1[slot]);
-        const f32x4 dd = decode4(r2[slot]);
-        float* q = qbuf[buf];
-        *reinterpret_cast<f32x4*>(&q[q_off(0, role_blk, lane)]) = dd * uu;
-        if constexpr (S4D) {
-          f32x4 r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
-          *reinterpret_cast<f32x4*>(&q[q_off(1, role_blk, lane)]) = r;
-          f32x4 step = r;  // r^SPW
-#pragma unroll
-          for (int j = 1; j < SPW; ++j) step = step * r;
-          f32x4 sp = r;    // r^(wave*SPW + 1)
-#pragma unroll
-          for (int wv = 0; wv < kWaves; ++wv) {
-            *reinterpret_cast<f32x4*>(&q[q_off(2 + wv, role_blk, lane)]) = sp;
-            sp = sp * step;
-          }
-        } else {
-          *reinterpret_cast<f32x4*>(&q[q_off(1, role_blk, lane)]) = dd;
+        for (int v = 0; v < NV; ++v) {
+          const uint32_t off = tile_ok ? (uint32_t)(((size_t)tile * NV + v) * 64 + p16 * 4) * 4u : kOffNone;
+          dst[v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
         }
       };
+      load_bc(tb, bcr[0]);
+      load_bc(tb + 1, bcr[1]);
 
-      // Epilogue (waves 4-7) of tile k: channel c, steps t0 + 4*role_blk .. +3.
-      auto epilogue = [&](int buf, int slot, int t0) {
-        const float* pp = pbuf[buf];
-        f32x4 acc = *reinterpret_cast<const f32x4*>(&pp[q_off(0, role_blk, lane)]);
-#pragma unroll
-        for (int wv = 1; wv < kWaves; ++wv) acc += *reinterpret_cast<const f32x4*>(&pp[q_off(wv, role_blk, lane)]);
-        const f32x4 uu = decode4(r1[slot]);
-        const f32x4 zz = decode4(r2[slot]);
-        f32x4 out;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float o = __builtin_fmaf(dskip, uu[i], acc[i]);
-          out[i] = has_z ? o * silu(zz[i]) : o;
-        }
-        store4<BF16, VEC>(ry_d, lane_off, t0 + role_blk * 4, L, cok, out);
-      };
-
-      // Core: this wave's SPW states over the 16 steps of one tile.
+      // One tile: x, the decay (S4D: r) and the start power of the four
+      // blocks come from qbuf (read all up front when the registers allow);
+      // partial readouts go to pbuf.
+      constexpr int kAhead = SPW <= 4 ? kBlk : 1;
       auto core_tile = [&](auto guard_tag, int buf, int t0, const f32x4* bc_cur) {
         constexpr bool GUARD = decltype(guard_tag)::value;
         const float* q = qbuf[buf];
         float* pp = pbuf[buf];
-        f32x4 xv[kBlk], rv[kBlk], sv[kBlk];
+        f32x4 xvs[kAhead], rvs[kAhead], svs[kAhead];
+        auto read_blk = [&](int blk, int i) {
+          xvs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(0, blk, lane)]);
+          rvs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(1, blk, lane)]);
+          if constexpr (S4D) svs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(2 + wc, blk, lane)]);
+          else svs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        };
+        if constexpr (kAhead == kBlk) {
 #pragma unroll
-        for (int blk = 0; blk < kBlk; ++blk) {
-          xv[blk] = *reinterpret_cast<const f32x4*>(&q[q_off(0, blk, lane)]);
-          rv[blk] = *reinterpret_cast<const f32x4*>(&q[q_off(1, blk, lane)]);
-          if constexpr (S4D) sv[blk] = *reinterpret_cast<const f32x4*>(&q[q_off(2 + w, blk, lane)]);
-          else sv[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int blk = 0; blk < kBlk; ++blk) read_blk(blk, blk);
         }
 #pragma unroll
         for (int blk = 0; blk < kBlk; ++blk) {
+          if constexpr (kAhead == 1) read_blk(blk, 0);
+          const int i = kAhead == kBlk ? blk : 0;
+          const f32x4 xv = xvs[i], rv = rvs[i], sv = svs[i];
           f32x4 part;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            const float x = xv[blk][kk];
-            const float r = rv[blk][kk];  // r (S4D) or delta (general)
+            const float x = xv[kk];
+            const float r = rv[kk];  // r (S4D) or delta (general)
             float p = 0.f;
             if (!GUARD || t0 + blk * 4 + kk < L) {
-              float dec = sv[blk][kk];
+              float dec = sv[kk];
 #pragma unroll
               for (int j = 0; j < SPW; ++j) {
                 const int ib = kk * 2 * SPW + j;  // B of state j at step kk
@@ -373,68 +360,179 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
                 }
                 const float bx = row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x;
                 h[j] = __builtin_fmaf(dec, h[j], bx);
-                const float ch = row_bcast_rt(bc_cur[ic / 16][blk], ic % 16) * h[j];
-                p = (j == 0) ? ch : p + ch;
+                if (j == 0)
+                  p = row_bcast_rt(bc_cur[ic / 16][blk], ic % 16) * h[j];
+                else
+                  p = fmac_row_bcast_rt(p, bc_cur[ic / 16][blk], h[j], ic % 16);
               }
             }
             part[kk] = p;
           }
-          *reinterpret_cast<f32x4*>(&pp[q_off(w, blk, lane)]) = part;
+          *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
         }
       };
 
-      if (is_pro) prologue(tb & 1, 0);
-      load_tile(tb + kPrefetch - e, 0);
-      __syncthreads();
-
-      // One tile: S = k % 3 is a compile-time ring slot.  The prologue of tile
-      // k+1 and the epilogue of tile k both read slot S+1, which is then refilled
-      // with tile k+4 (prologue waves) or k+3 (epilogue waves).
-      auto tile_step = [&](auto slot_tag, int k) {
-        constexpr int S = decltype(slot_tag)::value;
-        constexpr int S1 = (S + 1) % kPrefetch, S2 = (S + 2) % kPrefetch;
-        const int buf = k & 1;
+      __syncthreads();  // the prologue of tile tb is in qbuf
+      auto step = [&](auto slot_tag, int k) {
+        constexpr int Sl = decltype(slot_tag)::value;
+        constexpr int S2 = (Sl + 2) % kPrefetch;
         const int t0 = k * kTile;
-        // Past the last tile these loads read zeros (out-of-range offsets) and the
-        // prologue fills an LDS buffer nobody reads; running them unconditionally
-        // keeps the loop body free of branches around loads.
-        load_bc(k + 2, te, bcr[S2]);
-        if (is_pro) prologue(buf ^ 1, S1);
+        load_bc(k + 2, bcr[S2]);  // past the last tile: reads zeros, unused
         if (t0 + kTile <= L)
-          core_tile(std::false_type{}, buf, t0, bcr[S]);
+          core_tile(std::false_type{}, k & 1, t0, bcr[Sl]);
         else
-          core_tile(std::true_type{}, buf, t0, bcr[S]);
+          core_tile(std::true_type{}, k & 1, t0, bcr[Sl]);
         __syncthreads();
-        if (!is_pro) epilogue(buf, S1, t0);
-        load_tile(k + 1 + kPrefetch - e, S1);
       };
-
       int k = tb;
       for (; k + kPrefetch <= te; k += kPrefetch) {
-        tile_step(std::integral_constant<int, 0>{}, k);
-        tile_step(std::integral_constant<int, 1>{}, k + 1);
-        tile_step(std::integral_constant<int, 2>{}, k + 2);
+        step(std::integral_constant<int, 0>{}, k);
+        step(std::integral_constant<int, 1>{}, k + 1);
+        step(std::integral_constant<int, 2>{}, k + 2);
       }
-      if (k < te) tile_step(std::integral_constant<int, 0>{}, k);
-      if (k + 1 < te) tile_step(std::integral_constant<int, 1>{}, k + 1);
+      if (k < te) step(std::integral_constant<int, 0>{}, k);
+      if (k + 1 < te) step(std::integral_constant<int, 1>{}, k + 1);
     };
 
-    if (s4d)
-      run(std::true_type{}, tb, te);
-    else
-      run(std::false_type{}, tb, te);
+    // ---- prologue waves prepare tile k+1 and epilogue waves finish tile k-1
+    // while the core runs tile k ----
+    auto io_run = [&](auto s4d_tag, auto pro_tag) __attribute__((always_inline)) {
+      constexpr bool S4D = decltype(s4d_tag)::value;
+      constexpr bool PRO = decltype(pro_tag)::value;
+      // Rings of three slots: (u, delta) for the prologue hold tile t in slot
+      // (t - tb) % 3 and are loaded three steps ahead; (u, z) for the
+      // epilogue hold tile t in slot (t - tb + 2) % 3, also three steps ahead.
+      // In every step both rings consume and refill the same compile-time
+      // slot, and the loop (unrolled by 3) never copies a register whose load
+      // is in flight nor branches around a load.
+      Raw4<BF16> pu[kPrefetch], pd[kPrefetch], eu[kPrefetch], ez[kPrefetch];
+      auto load_pro = [&](int tile, int slot) {
+        const int t = tile * kTile + io_blk * 4;
+        const bool ok = iok && tile >= tb && tile < te;
+        pu[slot] = load_raw4<BF16, VEC>(ru_d, io_off, t, L, ok);
+        pd[slot] = load_raw4<BF16, VEC>(rd_d, io_off, t, L, ok);
+      };
+      auto load_epi = [&](int tile, int slot) {
+        const int t = tile * kTile + io_blk * 4;
+        const bool ok = iok && tile >= tb && tile < te;
+        eu[slot] = load_raw4<BF16, VEC>(ru_d, io_off, t, L, ok);
+        ez[slot] = load_raw4<BF16, VEC>(rz_d, io_off, t, L, ok);
+      };
+
+      // Prologue of one tile from ring slot `slot` into qbuf[buf]: x = delta*u,
+      // then r = exp2(delta*A0*log2 e) and the start powers r^(w*SPW+1) (S4D)
+      // or delta itself (general decay).
+      auto prologue = [&](int buf, int slot) {
+        const f32x4 uu = decode4(pu[slot]);
+        const f32x4 dd = decode4(pd[slot]);
+        float* q = qbuf[buf];
+        *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
+        if constexpr (S4D) {
+          f32x4 r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
+          *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = r;
+          f32x4 stp = r;  // r^SPW
+#pragma unroll
+          for (int j = 1; j < SPW; ++j) stp = stp * r;
+          f32x4 sp = r;   // r^(wave*SPW + 1)
+#pragma unroll
+          for (int wv = 0; wv < kWaves; ++wv) {
+            *reinterpret_cast<f32x4*>(&q[q_off(2 + wv, io_blk, io_ch)]) = sp;
+            sp = sp * stp;
+          }
+        } else {
+          *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = dd;
+        }
+      };
+
+      // Epilogue of tile `tile`: the 8 partial readouts from pbuf[buf] summed in
+      // a fixed order, plus D*u, gated by silu(z); stores only inside the piece.
+      auto epilogue = [&](int buf, int slot, int tile) {
+        const float* pp = pbuf[buf];
+        f32x4 acc = *reinterpret_cast<const f32x4*>(&pp[q_off(0, io_blk, io_ch)]);
+#pragma unroll
+        for (int wv = 1; wv < kWaves; ++wv) acc += *reinterpret_cast<const f32x4*>(&pp[q_off(wv, io_blk, io_ch)]);
+        const f32x4 uu = decode4(eu[slot]);
+        const f32x4 zz = decode4(ez[slot]);
+        f32x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = __builtin_fmaf(dskip, uu[i], acc[i]);
+          out[i] = has_z ? o * silu(zz[i]) : o;
+        }
+        const bool ok = iok && tile >= tb && tile < te;
+        store4<BF16, VEC>(ry_d, io_off, tile * kTile + io_blk * 4, L, ok, out);
+      };
+
+      if constexpr (PRO) {
+#pragma unroll
+        for (int sl = 0; sl < kPrefetch; ++sl) load_pro(tb + sl, sl);
+        prologue(tb & 1, 0);
+        load_pro(tb + kPrefetch, 0);
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < kPrefetch; ++sl) load_epi(tb + sl - 2, sl);
+        load_epi(tb + 1, 0);
+      }
+      __syncthreads();  // the prologue of tile tb is in qbuf
+
+      auto step = [&](auto slot_tag, int k) {
+        constexpr int Sl = decltype(slot_tag)::value;
+        constexpr int S1 = (Sl + 1) % kPrefetch;
+        const int buf = k & 1;
+        if constexpr (PRO) {
+          prologue(buf ^ 1, S1);  // tile k+1 into the buffer the core is not reading
+          __syncthreads();
+          load_pro(k + 1 + kPrefetch, S1);
+        } else {
+          epilogue(buf ^ 1, S1, k - 1);  // tile k-1: partials complete since the last barrier
+          __syncthreads();
+          load_epi(k + 2, S1);
+        }
+      };
+      int k = tb;
+      for (; k + kPrefetch <= te; k += kPrefetch) {
+        step(std::integral_constant<int, 0>{}, k);
+        step(std::integral_constant<int, 1>{}, k + 1);
+        step(std::integral_constant<int, 2>{}, k + 2);
+      }
+      if (k < te) step(std::integral_constant<int, 0>{}, k);
+      if (k + 1 < te) step(std::integral_constant<int, 1>{}, k + 1);
+      // The last tile's partial readouts are complete after the last barrier;
+      // its epilogue ring slot is (te - tb + 1) % 3.
+      if constexpr (!PRO) {
+        const int ph = (te - tb) % kPrefetch;
+        const int lb = (te - 1) & 1;
+        if (ph == 0) epilogue(lb, 1, te - 1);
+        else if (ph == 1) epilogue(lb, 2, te - 1);
+        else epilogue(lb, 0, te - 1);
+      }
+    };
+
+    if (is_core) {
+      if (s4d) core_run(std::true_type{});
+      else core_run(std::false_type{});
+    } else if (is_pro) {
+      if (s4d) io_run(std::true_type{}, std::true_type{});
+      else io_run(std::false_type{}, std::true_type{});
+    } else {
+      io_run(std::false_type{}, std::false_type{});  // the epilogue is the same for both decays
+    }
 
     if (carry_out) {  // publish the state after tile te-1 for the next workgroup
+      if (is_core) {
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) carry[j * kLanes + lane] = h[j];
+        for (int j = 0; j < SPW; ++j) carry[j * kLanes + lane] = h[j];
+      }
       __threadfence();
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_store(a.flags + s, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (te == ntiles && a.h_last != nullptr && cok) {
+    if (is_core && te == ntiles && a.h_last != nullptr && cok) {
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
-        const int n = w * SPW + j;
+        const int n = wc * SPW + j;
         if (n < N) a.h_last[((size_t)b * a.dim + c) * N + n] = h[j];
       }
     }
@@ -453,12 +551,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   const int s_first = (int)(r0 / ntiles), s_last = (int)((r1 - 1) / ntiles);
   const int off_first = (int)(r0 - (int64_t)s_first * ntiles);
   const int end_last = (int)(r1 - (int64_t)s_last * ntiles);
-  if (s_first == s_last) {
-    run_piece(s_first, off_first, end_last, off_first > 0, end_last < ntiles);
-  } else {
-    run_piece(s_last, 0, end_last, false, end_last < ntiles);
-    for (int s = s_first + 1; s < s_last; ++s) run_piece(s, 0, ntiles, false, false);
-    run_piece(s_first, off_first, ntiles, off_first > 0, false);
+  // Pieces in run order (one call site keeps a single inlined copy of the loops).
+  const int npieces = s_last - s_first + 1;
+  for (int i = 0; i < npieces; ++i) {
+    int s, tb, te;
+    if (npieces == 1) {
+      s = s_first, tb = off_first, te = end_last;
+    } else if (i == 0) {
+      s = s_last, tb = 0, te = end_last;         // head of the last stream
+    } else if (i == npieces - 1) {
+      s = s_first, tb = off_first, te = ntiles;  // tail of the first stream
+    } else {
+      s = s_first + i, tb = 0, te = ntiles;      // whole streams
+    }
+    run_piece(s, tb, te, tb > 0, te < ntiles);
   }
 }
 
