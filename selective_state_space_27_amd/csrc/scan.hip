@@ -319,10 +319,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
       // One tile: x, the decay (S4D: r) and the start power of the four
       // blocks come from qbuf (read all up front when the registers allow);
-      // partial readouts go to pbuf.
+      // partial readouts go to pbuf.  Steps at or past L need no guard: their
+      // delta, u and B read as zero, so the decay is exp2(0) = 1 and the input
+      // term 0, and the update leaves h unchanged.
       constexpr int kAhead = SPW <= 4 ? kBlk : 1;
-      auto core_tile = [&](auto guard_tag, int buf, int t0, const f32x4* bc_cur) {
-        constexpr bool GUARD = decltype(guard_tag)::value;
+      auto core_tile = [&](int buf, const f32x4* bc_cur) {
         const float* q = qbuf[buf];
         float* pp = pbuf[buf];
         f32x4 xvs[kAhead], rvs[kAhead], svs[kAhead];
@@ -347,24 +348,22 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
             const float x = xv[kk];
             const float r = rv[kk];  // r (S4D) or delta (general)
             float p = 0.f;
-            if (!GUARD || t0 + blk * 4 + kk < L) {
-              float dec = sv[kk];
+            float dec = sv[kk];
 #pragma unroll
-              for (int j = 0; j < SPW; ++j) {
-                const int ib = kk * 2 * SPW + j;  // B of state j at step kk
-                const int ic = ib + SPW;          // C of state j at step kk
-                if constexpr (S4D) {
-                  if (j > 0) dec *= r;
-                } else {
-                  dec = exp2_fast(r * A2[j]);
-                }
-                const float bx = row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x;
-                h[j] = __builtin_fmaf(dec, h[j], bx);
-                if (j == 0)
-                  p = row_bcast_rt(bc_cur[ic / 16][blk], ic % 16) * h[j];
-                else
-                  p = fmac_row_bcast_rt(p, bc_cur[ic / 16][blk], h[j], ic % 16);
+            for (int j = 0; j < SPW; ++j) {
+              const int ib = kk * 2 * SPW + j;  // B of state j at step kk
+              const int ic = ib + SPW;          // C of state j at step kk
+              if constexpr (S4D) {
+                if (j > 0) dec *= r;
+              } else {
+                dec = exp2_fast(r * A2[j]);
               }
+              const float bx = row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x;
+              h[j] = __builtin_fmaf(dec, h[j], bx);
+              if (j == 0)
+                p = row_bcast_rt(bc_cur[ic / 16][blk], ic % 16) * h[j];
+              else
+                p = fmac_row_bcast_rt(p, bc_cur[ic / 16][blk], h[j], ic % 16);
             }
             part[kk] = p;
           }
@@ -376,12 +375,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       auto step = [&](auto slot_tag, int k) {
         constexpr int Sl = decltype(slot_tag)::value;
         constexpr int S2 = (Sl + 2) % kPrefetch;
-        const int t0 = k * kTile;
         load_bc(k + 2, bcr[S2]);  // past the last tile: reads zeros, unused
-        if (t0 + kTile <= L)
-          core_tile(std::false_type{}, k & 1, t0, bcr[Sl]);
-        else
-          core_tile(std::true_type{}, k & 1, t0, bcr[Sl]);
+        core_tile(k & 1, bcr[Sl]);
         __syncthreads();
       };
       int k = tb;
@@ -422,9 +417,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       // Prologue of one tile from ring slot `slot` into qbuf[buf]: x = delta*u,
       // then r = exp2(delta*A0*log2 e) and the start powers r^(w*SPW+1) (S4D)
       // or delta itself (general decay).
-      auto prologue = [&](int buf, int slot) {
+      auto prologue = [&](int buf, int slot, auto&& refill) {
         const f32x4 uu = decode4(pu[slot]);
         const f32x4 dd = decode4(pd[slot]);
+        refill();  // the slot's registers are free: issue its next load now
         float* q = qbuf[buf];
         *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
         if constexpr (S4D) {
@@ -448,18 +444,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
       // Epilogue of tile `tile`: the 8 partial readouts from pbuf[buf] summed in
       // a fixed order, plus D*u, gated by silu(z); stores only inside the piece.
-      auto epilogue = [&](int buf, int slot, int tile) {
+      auto epilogue = [&](int buf, int slot, int tile, auto&& refill) {
+        const f32x4 uu = decode4(eu[slot]);
+        const f32x4 zz = decode4(ez[slot]);
+        refill();  // the slot's registers are free: issue its next load now
         const float* pp = pbuf[buf];
         f32x4 acc = *reinterpret_cast<const f32x4*>(&pp[q_off(0, io_blk, io_ch)]);
 #pragma unroll
         for (int wv = 1; wv < kWaves; ++wv) acc += *reinterpret_cast<const f32x4*>(&pp[q_off(wv, io_blk, io_ch)]);
-        const f32x4 uu = decode4(eu[slot]);
-        const f32x4 zz = decode4(ez[slot]);
         f32x4 out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float o = __builtin_fmaf(dskip, uu[i], acc[i]);
-          out[i] = has_z ? o * silu(zz[i]) : o;
+          const float g = silu(zz[i]);  // z reads as 0 when absent; the select drops it
+          out[i] = o * (has_z ? g : 1.0f);
         }
         const bool ok = iok && tile >= tb && tile < te;
         store4<BF16, VEC>(ry_d, io_off, tile * kTile + io_blk * 4, L, ok, out);
@@ -468,11 +466,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       if constexpr (PRO) {
 #pragma unroll
         for (int sl = 0; sl < kPrefetch; ++sl) load_pro(tb + sl, sl);
-        prologue(tb & 1, 0);
-        load_pro(tb + kPrefetch, 0);
+        prologue(tb & 1, 0, [&] { load_pro(tb + kPrefetch, 0); });
       } else {
-#pragma unroll
-        for (int sl = 0; sl < kPrefetch; ++sl) load_epi(tb + sl - 2, sl);
+        load_epi(tb - 1, 1);  // (no such tile: zeros, stores masked)
+        load_epi(tb, 2);
         load_epi(tb + 1, 0);
       }
       __syncthreads();  // the prologue of tile tb is in qbuf
@@ -481,15 +478,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         constexpr int Sl = decltype(slot_tag)::value;
         constexpr int S1 = (Sl + 1) % kPrefetch;
         const int buf = k & 1;
-        if constexpr (PRO) {
-          prologue(buf ^ 1, S1);  // tile k+1 into the buffer the core is not reading
-          __syncthreads();
-          load_pro(k + 1 + kPrefetch, S1);
-        } else {
-          epilogue(buf ^ 1, S1, k - 1);  // tile k-1: partials complete since the last barrier
-          __syncthreads();
-          load_epi(k + 2, S1);
-        }
+        if constexpr (PRO)  // tile k+1 into the buffer the core is not reading
+          prologue(buf ^ 1, S1, [&] { load_pro(k + 1 + kPrefetch, S1); });
+        else  // tile k-1: its partial readouts are complete since the last barrier
+          epilogue(buf ^ 1, S1, k - 1, [&] { load_epi(k + 2, S1); });
+        __syncthreads();
       };
       int k = tb;
       for (; k + kPrefetch <= te; k += kPrefetch) {
@@ -504,9 +497,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       if constexpr (!PRO) {
         const int ph = (te - tb) % kPrefetch;
         const int lb = (te - 1) & 1;
-        if (ph == 0) epilogue(lb, 1, te - 1);
-        else if (ph == 1) epilogue(lb, 2, te - 1);
-        else epilogue(lb, 0, te - 1);
+        auto none = [] {};
+        if (ph == 0) epilogue(lb, 1, te - 1, none);
+        else if (ph == 1) epilogue(lb, 2, te - 1, none);
+        else epilogue(lb, 0, te - 1, none);
       }
     };
 
