@@ -13,21 +13,27 @@
 //   S_out = exp(s_last) S_in + sum_j exp(s_last - s_j) delta_j x_j B_j^T
 // which is the recurrence above summed over the block (exact up to rounding).
 //
-// Two kernels:
-//   ssd_state_kernel: one workgroup per (batch, head) walks the chunks in
-//     order with the 64 x 128 state in MFMA accumulators (fp32) and writes the
-//     state entering every chunk to the workspace (and, on request, the state
-//     after every chunk and the final state).
+// Two kernels, both on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+//   ssd_state_kernel: one workgroup per (batch, head, 32-wide headdim tile),
+//     one 32 x 32 tile of S^T per wave kept in MFMA accumulators, walks the
+//     sequence in 64-step blocks (the next block's loads in flight while the
+//     current one is used) and writes the state entering every chunk to the
+//     workspace (and, on request, the state after every chunk and the final
+//     state).
 //   ssd_scan_kernel: one workgroup per (batch, chunk, head) starts from the
-//     state entering its chunk and walks the chunk in 64-step blocks: C B^T,
-//     the decay-masked diagonal block times x, exp(s) C S^T, all on
-//     v_mfma_f32_32x32x16_bf16 with fp32 accumulation, then the block's state
-//     update, kept in accumulators.  Every operand that is not an exact bf16
-//     input (the state in C S^T, the decay-weighted diagonal block, x scaled
-//     by the decay weights) enters as a bf16 hi/lo pair (two products), so it
-//     keeps ~16 bits of mantissa; accumulation is fp32 throughout.
-// Operands that the matrix cores read along time (x and B for the state
-// update, x for the diagonal block) are staged transposed in LDS.
+//     state entering its chunk and walks the chunk in 64-step blocks.  Each
+//     wave owns one 32 x 32 output tile and holds S^T for its headdim tile in
+//     accumulators; C S^T, G^T = B C^T, the decay-masked diagonal block times
+//     x and the state update all run on the matrix cores.  Accumulator tiles
+//     become MFMA operands in registers: a K slice of 16 rows is gathered by
+//     swapping lane halves of register pairs (v_permlane32_swap), so neither
+//     the state nor G passes through LDS.
+// Every operand that is not an exact bf16 input (the state in C S^T, the
+// decay-weighted diagonal block, x scaled by the decay weights) enters as a
+// bf16 hi/lo pair (two products), keeping ~16 bits of mantissa.  Operands the
+// matrix cores read along time (x and B) are staged transposed in LDS.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,30 +42,62 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kP = 64;      // headdim
 constexpr int kN = 128;     // dstate
-constexpr int kSub = 64;    // steps per block inside the scan kernel
+constexpr int kSub = 64;    // steps per block
 constexpr int kT = 256;     // threads per workgroup (4 waves)
 constexpr int kPadH = 8;    // bf16 row padding (16 bytes)
+constexpr int kTRow = kSub + kPadH;  // row length of the time-contiguous (transposed) stagings
 
+// Element (row, step j) of a time-contiguous staging [rows][kTRow]: the eight
+// 16-byte blocks of a row are permuted by (row >> 4) so that the staging
+// writes (two steps of many rows per instruction) spread over all LDS banks,
+// while a 16-byte operand read (8 consecutive steps of one row) stays whole.
+__device__ __forceinline__ int tsw(int row, int j) {
+  return row * kTRow + ((((j >> 3) ^ (row >> 4)) & 7) << 3) + (j & 7);
+}
+
+// D += A B with A 32x16 (lane l: row l%32, k = 8(l/32)+t), B 16x32 (lane l:
+// k = 8(l/32)+t, column l%32), t the bf16 index in the 8-vector.
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
 
-// Row (within a 32x32 tile) of accumulator register r of lane l.
+// Row (within a 32x32 tile) of accumulator register r of lane l; the column is l%32.
 __device__ __forceinline__ int acc_row(int r, int l) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
 
+// Rows 16S..16S+15 of an accumulator tile in operand form: lane l gets rows
+// 16S + 8(l/32) + t, t = 0..7, of column l%32.  Registers 8S+q hold rows
+// 16S+q (lanes 0-31) and 16S+4+q (lanes 32-63), registers 8S+4+q rows 16S+8+q
+// and 16S+12+q; swapping the upper half of the first with the lower half of
+// the second puts every row where the operand layout wants it.
+template <int S>
+__device__ __forceinline__ void acc_kslice(const f32x16& acc, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[8 * S + q]),
+                                                    __float_as_uint(acc[8 * S + 4 + q]), false, false);
+    v[q] = __uint_as_float(r[0]);
+    v[4 + q] = __uint_as_float(r[1]);
+  }
+}
 
 // fp32 pair -> (hi, lo) bf16 pairs with hi + lo = value to ~16 mantissa bits.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16x2(a, b);
   lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
 }
-__device__ __forceinline__ float lo16(uint32_t w) { return bf16_lo(w); }
-__device__ __forceinline__ float hi16(uint32_t w) { return bf16_hi(w); }
+__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t h, l;
+    split2(v[2 * q], v[2 * q + 1], h, l);
+    hi[q] = h;
+    lo[q] = l;
+  }
+}
 
 struct SSDArgs {
   const uint16_t* x;   // [b, L, H, P] bf16
@@ -77,60 +115,58 @@ struct SSDArgs {
   int batch, L, H, G, Q, nchunks;
 };
 
-// Inclusive prefix sum of delta over steps [l0, l0 + n) of head h, computed by
-// wave 0 (n <= 64) into cum[]; also stores the deltas.  Out-of-range steps
-// count as zero.  Fixed shuffle order: deterministic.
-__device__ __forceinline__ void block_cumsum64(const SSDArgs& a, int b, int h, int l0, float* dl, float* cum) {
+// Wave 0: delta of the block's steps (d, zero past L), inclusive prefix sums
+// in a fixed shuffle order, and e_i = exp(s_i), w_j = delta_j exp(s_last -
+// s_j), decay = exp(s_last) with s = A * prefix.  Any of the outputs may be null.
+__device__ __forceinline__ void block_weights(float d, float a2, float* s_dl, float* s_cum, float* s_e, float* s_w,
+                                              float* s_decay) {
   const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
-    const int l = l0 + lane;
-    float d = (l < a.L) ? a.delta[((size_t)b * a.L + l) * a.H + h] : 0.f;
-    float s = d;
+  float s = d;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float t = __shfl_up(s, o, 64);
-      if (lane >= o) s += t;
-    }
-    dl[lane] = d;
-    cum[lane] = s;
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(s, o, 64);
+    if (lane >= o) s += t;
   }
+  const float last = __shfl(s, 63, 64);
+  if (s_dl) s_dl[lane] = d;
+  if (s_cum) s_cum[lane] = s;
+  if (s_e) s_e[lane] = exp2_fast(a2 * s);
+  s_w[lane] = d * exp2_fast(a2 * (last - s));
+  if (lane == 0) *s_decay = exp2_fast(a2 * last);
 }
 
-// Stages x^T (bf16, [P][kSub + pad]) for steps [l0, l0 + 64) of head h.
-// One thread per (step pair, 8 headdim values): two 16-byte row loads, eight
-// packed (step, step+1) words written along time.
-__device__ __forceinline__ void stage_xT(const SSDArgs& a, int b, int h, int l0, uint16_t (*xT)[kSub + kPadH]) {
-  const int t = threadIdx.x;
-  const int pg = t & 7, jp = t >> 3;  // 8 groups of 8 headdim values, 32 step pairs
-  const int j = 2 * jp;
-  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * kP, (uint32_t)((size_t)a.L * a.H * kP * 2));
-  const uint32_t o0 = (l0 + j < a.L) ? (uint32_t)((((size_t)(l0 + j) * a.H + h) * kP + pg * 8) * 2) : kOffNone;
-  const uint32_t o1 = (l0 + j + 1 < a.L) ? (uint32_t)((((size_t)(l0 + j + 1) * a.H + h) * kP + pg * 8) * 2) : kOffNone;
-  const u32x4 r0 = buf_load_u32x4(rx, o0);
-  const u32x4 r1 = buf_load_u32x4(rx, o1);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t w0 = r0[k], w1 = r1[k];
-    *reinterpret_cast<uint32_t*>(&xT[pg * 8 + 2 * k][j]) = (w0 & 0xffffu) | (w1 << 16);
-    *reinterpret_cast<uint32_t*>(&xT[pg * 8 + 2 * k + 1][j]) = (w0 >> 16) | (w1 & 0xffff0000u);
-  }
+__device__ __forceinline__ float load_delta(const SSDArgs& a, int b, int h, int l0) {
+  const int l = l0 + (threadIdx.x & 63);
+  return (l < a.L) ? a.delta[((size_t)b * a.L + l) * a.H + h] : 0.f;
 }
 
-// Stages B (or C) of group g for steps [l0, l0 + 64): row-major copy
-// rm[step][N + pad] and/or transposed copy tr[N][kSub + pad].
-template <bool ROWMAJOR, bool TRANSPOSED>
-__device__ __forceinline__ void stage_bc(const SSDArgs& a, const uint16_t* src, int b, int g, int l0,
-                                         uint16_t (*rm)[kN + kPadH], uint16_t (*tr)[kSub + kPadH]) {
+// B or C rows of group g for steps (l0 + j, l0 + j + 1), 8 states from ng*8:
+// two 16-byte loads per unit, 2 units per thread.  Steps past L read zero.
+struct BCRegs {
+  u32x4 r[2][2];
+};
+__device__ __forceinline__ void load_bc_rows(const SSDArgs& a, const uint16_t* src, int b, int g, int l0, BCRegs& o) {
   const rsrc_t rs = make_rsrc(src + (size_t)b * a.L * a.G * kN, (uint32_t)((size_t)a.L * a.G * kN * 2));
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int u = threadIdx.x + kT * it;    // 512 units: 32 step pairs x 16 groups of 8 states
-    const int ng = u & 15, jp = u >> 4;
-    const int j = 2 * jp;
-    const uint32_t o0 = (l0 + j < a.L) ? (uint32_t)((((size_t)(l0 + j) * a.G + g) * kN + ng * 8) * 2) : kOffNone;
-    const uint32_t o1 = (l0 + j + 1 < a.L) ? (uint32_t)((((size_t)(l0 + j + 1) * a.G + g) * kN + ng * 8) * 2) : kOffNone;
-    const u32x4 r0 = buf_load_u32x4(rs, o0);
-    const u32x4 r1 = buf_load_u32x4(rs, o1);
+    const int u = threadIdx.x + kT * it;  // 512 units: 32 step pairs x 16 groups of 8 states
+    const int ng = u & 15, j = 2 * (u >> 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int l = l0 + j + e;
+      const uint32_t off = (l < a.L) ? (uint32_t)((((size_t)l * a.G + g) * kN + ng * 8) * 2) : kOffNone;
+      o.r[it][e] = buf_load_u32x4(rs, off);
+    }
+  }
+}
+// Row-major copy rm[step][N + pad] and/or time-contiguous copy tr (tsw layout, N rows).
+template <bool ROWMAJOR, bool TRANSPOSED>
+__device__ __forceinline__ void store_bc_rows(const BCRegs& o, uint16_t (*rm)[kN + kPadH], uint16_t* tr) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int u = threadIdx.x + kT * it;
+    const int ng = u & 15, j = 2 * (u >> 4);
+    const u32x4 r0 = o.r[it][0], r1 = o.r[it][1];
     if constexpr (ROWMAJOR) {
       *reinterpret_cast<u32x4*>(&rm[j][ng * 8]) = r0;
       *reinterpret_cast<u32x4*>(&rm[j + 1][ng * 8]) = r1;
@@ -139,243 +175,359 @@ __device__ __forceinline__ void stage_bc(const SSDArgs& a, const uint16_t* src, 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t w0 = r0[k], w1 = r1[k];
-        *reinterpret_cast<uint32_t*>(&tr[ng * 8 + 2 * k][j]) = (w0 & 0xffffu) | (w1 << 16);
-        *reinterpret_cast<uint32_t*>(&tr[ng * 8 + 2 * k + 1][j]) = (w0 >> 16) | (w1 & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&tr[tsw(ng * 8 + 2 * k, j)]) = (w0 & 0xffffu) | (w1 << 16);
+        *reinterpret_cast<uint32_t*>(&tr[tsw(ng * 8 + 2 * k + 1, j)]) = (w0 >> 16) | (w1 & 0xffff0000u);
       }
     }
   }
 }
 
-// State update over one staged 64-step block, for this wave's two state tiles
-// (headdim tile pt, state tiles nt0, nt0+1):
-//   S <- decay * S + sum_j w_j x_j B_j^T,  w_j = delta_j exp(s_last - s_j)
-// A operand: x^T rows scaled by w_j, as a bf16 hi/lo pair (two products);
-// B operand: B^T (exact bf16 inputs).
-__device__ __forceinline__ void state_update_block(f32x16* acc, float decay, const float* w,
-                                                   const uint16_t (*xT)[kSub + kPadH],
-                                                   const uint16_t (*BT)[kSub + kPadH], int pt, int nt0) {
+// One 32x32 tile of S^T (rows n = nt*32.., columns p = pt*32..) from/to a
+// [P][N] fp32 state: each lane moves 4 consecutive n of its column at a time.
+__device__ __forceinline__ void load_stateT(f32x16& acc, const float* S, int nt, int pt) {
   const int lane = threadIdx.x & 63;
+  const int p = pt * 32 + (lane & 31);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) acc[t] *= decay;
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int n = nt * 32 + 8 * g4 + 4 * (lane >> 5);
+    const f32x4 v = S ? *reinterpret_cast<const f32x4*>(&S[(size_t)p * kN + n]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < kSub / 16; ++kk) {
-    const int j0 = kk * 16 + 8 * (lane >> 5);
-    const u32x4 xr = *reinterpret_cast<const u32x4*>(&xT[pt * 32 + (lane & 31)][j0]);
-    u32x4 ah, al;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t hh, ll;
-      split2(lo16(xr[q]) * w[j0 + 2 * q], hi16(xr[q]) * w[j0 + 2 * q + 1], hh, ll);
-      ah[q] = hh;
-      al[q] = ll;
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(&BT[(nt0 + t) * 32 + (lane & 31)][j0]);
-      acc[t] = mfma(ah, bv, acc[t]);
-      acc[t] = mfma(al, bv, acc[t]);
-    }
+    for (int q = 0; q < 4; ++q) acc[4 * g4 + q] = v[q];
   }
 }
-
-// Per-block decay quantities from the prefix sums (wave 0): e_i = exp(s_i),
-// w_j = delta_j exp(s_last - s_j), and the block decay exp(s_last).
-__device__ __forceinline__ void block_weights(float a2, const float* dl, const float* cum, float* e, float* w,
-                                              float* decay) {
-  if (threadIdx.x < 64) {
-    const int i = threadIdx.x;
-    const float last = cum[63];
-    e[i] = exp2_fast(a2 * cum[i]);
-    w[i] = dl[i] * exp2_fast(a2 * (last - cum[i]));
-    if (i == 0) *decay = exp2_fast(a2 * last);
+__device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt, int pt) {
+  const int lane = threadIdx.x & 63;
+  const int p = pt * 32 + (lane & 31);
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int n = nt * 32 + 8 * g4 + 4 * (lane >> 5);
+    *reinterpret_cast<f32x4*>(&S[(size_t)p * kN + n]) =
+        f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
   }
-}
-
-// Loads/stores one wave's two 32x32 state tiles (headdim tile pt, state tiles
-// nt0, nt0+1) of a [P][N] fp32 state.
-__device__ __forceinline__ void load_state(f32x16* acc, const float* S, int pt, int nt0) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      acc[t][r] = S ? S[(pt * 32 + acc_row(r, lane)) * kN + (nt0 + t) * 32 + (lane & 31)] : 0.f;
-}
-__device__ __forceinline__ void store_state(const f32x16* acc, float* S, int pt, int nt0) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[(pt * 32 + acc_row(r, lane)) * kN + (nt0 + t) * 32 + (lane & 31)] = acc[t][r];
 }
 
 // ---------------------------------------------------------------------------
-// Chunk states.  grid (H, batch), 256 threads.
+// Chunk states.  grid (2H, batch), 256 threads: workgroup (b, h, pt) owns
+// headdim tile pt; wave w owns the S^T tile of state rows w*32.. .
 __global__ void __launch_bounds__(kT) ssd_state_kernel(SSDArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xT[kP][kSub + kPadH];
-  __shared__ __attribute__((aligned(16))) uint16_t BT[kN][kSub + kPadH];
-  __shared__ float s_dl[kSub], s_cum[kSub], s_e[kSub], s_w[kSub];
+  __shared__ __attribute__((aligned(16))) uint16_t xT[32 * kTRow];  // tsw layout, this tile's headdim rows
+  __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];  // tsw layout, state rows
+  __shared__ __attribute__((aligned(16))) float s_w[kSub];
   __shared__ float s_decay;
 
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int pt = blockIdx.x & 1, h = blockIdx.x >> 1, b = blockIdx.y;
   const int g = h / (a.H / a.G);
-  const int w = threadIdx.x >> 6;
-  const int pt = w & 1, nt0 = 2 * (w >> 1);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lc = lane & 31, hf = lane >> 5;
   const float a2 = a.A[h] * kLog2e;
   const size_t state_stride = (size_t)kP * kN;
 
-  f32x16 acc[2];
-  load_state(acc, a.h0 ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, pt, nt0);
+  // x staging: thread -> (step pair j, 4 headdim values pq*4..) of this tile.
+  const int pq = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
+  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * kP, (uint32_t)((size_t)a.L * a.H * kP * 2));
+  auto load_x = [&](int l0, u32x2* xr) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int l = l0 + jx + e;
+      const uint32_t off = (l < a.L) ? (uint32_t)((((size_t)l * a.H + h) * kP + pt * 32 + pq * 4) * 2) : kOffNone;
+      xr[e] = buf_load_u32x2(rx, off);
+    }
+  };
+  auto store_x = [&](const u32x2* xr) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t w0 = xr[0][k], w1 = xr[1][k];
+      *reinterpret_cast<uint32_t*>(&xT[tsw(pq * 4 + 2 * k, jx)]) = (w0 & 0xffffu) | (w1 << 16);
+      *reinterpret_cast<uint32_t*>(&xT[tsw(pq * 4 + 2 * k + 1, jx)]) = (w0 >> 16) | (w1 & 0xffff0000u);
+    }
+  };
+
+  f32x16 st;
+  load_stateT(st, a.h0 ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, w, pt);
+
+  // Three blocks of loads in flight (ring of register slots, tile loop
+  // unrolled by 3 so the slot index is a compile-time constant).
+  struct Slot {
+    u32x2 xr[2];
+    BCRegs br;
+    float d;
+  };
+  Slot ring[3];
+  auto load_slot = [&](int blk, Slot& sl) {
+    const int l0 = blk * kSub;  // past L: zeros
+    load_x(l0, sl.xr);
+    load_bc_rows(a, a.B, b, g, l0, sl.br);
+    sl.d = load_delta(a, b, h, l0);
+  };
+  load_slot(0, ring[0]);
+  load_slot(1, ring[1]);
+  load_slot(2, ring[2]);
 
   const int sub_per_chunk = a.Q / kSub;
   const int nsub = (a.L + kSub - 1) / kSub;
-  for (int sb = 0; sb < nsub; ++sb) {
-    const int l0 = sb * kSub;
+  auto step = [&](auto slot_tag, int sb) {
+    constexpr int S = decltype(slot_tag)::value;
     const int c = sb / sub_per_chunk;
     if (sb % sub_per_chunk == 0)  // state entering chunk c
-      store_state(acc, a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, pt, nt0);
-    block_cumsum64(a, b, h, l0, s_dl, s_cum);
-    stage_xT(a, b, h, l0, xT);
-    stage_bc<false, true>(a, a.B, b, g, l0, nullptr, BT);
+      store_stateT(st, a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, w, pt);
+    store_x(ring[S].xr);
+    store_bc_rows<false, true>(ring[S].br, nullptr, BT);
+    if (w == 0) block_weights(ring[S].d, a2, nullptr, nullptr, nullptr, s_w, &s_decay);
+    load_slot(sb + 3, ring[S]);
     __syncthreads();
-    block_weights(a2, s_dl, s_cum, s_e, s_w, &s_decay);
-    __syncthreads();
-    state_update_block(acc, s_decay, s_w, xT, BT, pt, nt0);
+
+    st *= s_decay;
+#pragma unroll
+    for (int kk = 0; kk < kSub / 16; ++kk) {
+      const int j0 = kk * 16 + 8 * hf;
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(&xT[tsw(lc, j0)]);
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_w[j0]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_w[j0 + 4]);
+      const float v[8] = {bf16_lo(xv[0]) * w0[0], bf16_hi(xv[0]) * w0[1], bf16_lo(xv[1]) * w0[2],
+                          bf16_hi(xv[1]) * w0[3], bf16_lo(xv[2]) * w1[0], bf16_hi(xv[2]) * w1[1],
+                          bf16_lo(xv[3]) * w1[2], bf16_hi(xv[3]) * w1[3]};
+      u32x4 bh, bl;
+      split8(v, bh, bl);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[tsw(w * 32 + lc, j0)]);
+      st = mfma(av, bh, st);
+      st = mfma(av, bl, st);
+    }
     const bool chunk_end = (sb % sub_per_chunk == sub_per_chunk - 1) || sb == nsub - 1;
     if (chunk_end && a.chunk_states)
-      store_state(acc, a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, pt, nt0);
+      store_stateT(st, a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, w, pt);
     __syncthreads();
+  };
+  int sb = 0;
+  for (; sb + 3 <= nsub; sb += 3) {
+    step(std::integral_constant<int, 0>{}, sb);
+    step(std::integral_constant<int, 1>{}, sb + 1);
+    step(std::integral_constant<int, 2>{}, sb + 2);
   }
-  if (a.h_last) store_state(acc, a.h_last + ((size_t)b * a.H + h) * state_stride, pt, nt0);
+  if (sb < nsub) step(std::integral_constant<int, 0>{}, sb);
+  if (sb + 1 < nsub) step(std::integral_constant<int, 1>{}, sb + 1);
+  if (a.h_last) store_stateT(st, a.h_last + ((size_t)b * a.H + h) * state_stride, w, pt);
 }
 
 // ---------------------------------------------------------------------------
-// Chunk outputs.  grid (nchunks, H, batch), 256 threads; wave w owns output
-// tile (row tile w>>1, headdim tile w&1) and state tiles (w&1, 2*(w>>1)+{0,1}).
-__global__ void __launch_bounds__(kT) ssd_scan_kernel(SSDArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xT[kP][kSub + kPadH];
-  __shared__ __attribute__((aligned(16))) uint16_t BT[kN][kSub + kPadH];
+// Chunk outputs.  grid (nchunks, H, batch), 256 threads.  Wave w = (rt, pt)
+// with rt = w>>1, pt = w&1 owns output tile (row tile rt, headdim tile pt) and
+// the two S^T tiles (state rows 64*rt .. +64, headdim tile pt).  C S^T is
+// split by state rows: each wave forms it over its own two state tiles for
+// both row tiles and hands the other row tile's partial sum to its partner
+// wave (1-rt, pt) through LDS.
+template <int RT>
+__device__ __forceinline__ void diag_block(f32x16& yacc, const uint16_t (*Cs)[kN + kPadH],
+                                           const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_cum,
+                                           const float* s_dl, float a2, int pt) {
+  const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
+  const int i = RT * 32 + lc;
+  const float ci = s_cum[i];
+#pragma unroll
+  for (int jt = 0; jt <= RT; ++jt) {
+    // G^T tile (rows j of tile jt, columns i of tile RT) = B C^T.
+    f32x16 gacc = {};
+#pragma unroll
+    for (int kk = 0; kk < kN / 16; ++kk) {
+      const u32x4 bop = *reinterpret_cast<const u32x4*>(&Bs[jt * 32 + lc][kk * 16 + 8 * hf]);
+      const u32x4 cop = *reinterpret_cast<const u32x4*>(&Cs[RT * 32 + lc][kk * 16 + 8 * hf]);
+      gacc = mfma(bop, cop, gacc);
+    }
+    // M = mask o G o exp(s_i - s_j) delta_j as the A operand (rows i, k = j).
+    auto slice = [&](auto s_tag) {
+      constexpr int S = decltype(s_tag)::value;
+      float gv[8];
+      acc_kslice<S>(gacc, gv);
+      const int j0 = jt * 32 + 16 * S + 8 * hf;
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_cum[j0]);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_cum[j0 + 4]);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_dl[j0]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_dl[j0 + 4]);
+      const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      const float dj[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      float m[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float dec = exp2_fast(fminf(a2 * (ci - cj[t]), 0.f));
+        const float v = gv[t] * dec * dj[t];
+        m[t] = (jt < RT || j0 + t <= i) ? v : 0.f;
+      }
+      u32x4 mh, ml;
+      split8(m, mh, ml);
+      const u32x4 xb = *reinterpret_cast<const u32x4*>(&xT[tsw(pt * 32 + lc, j0)]);
+      yacc = mfma(mh, xb, yacc);
+      yacc = mfma(ml, xb, yacc);
+    };
+    slice(std::integral_constant<int, 0>{});
+    slice(std::integral_constant<int, 1>{});
+  }
+}
+
+__global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xT[kP * kTRow];  // tsw layout, headdim rows
+  __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];  // tsw layout, state rows
   __shared__ __attribute__((aligned(16))) uint16_t Cs[kSub][kN + kPadH];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kSub][kN + kPadH];
-  __shared__ __attribute__((aligned(16))) uint16_t Shi[kP][kN + kPadH];
-  __shared__ __attribute__((aligned(16))) uint16_t Slo[kP][kN + kPadH];
-  __shared__ __attribute__((aligned(16))) float Gb[kSub][kSub + 4];
-  __shared__ float s_dl[kSub], s_cum[kSub], s_e[kSub], s_w[kSub];
+  __shared__ __attribute__((aligned(16))) float xbuf[4][16][64];  // partial C S^T handed to the partner wave
+  __shared__ __attribute__((aligned(16))) float s_dl[kSub];
+  __shared__ __attribute__((aligned(16))) float s_cum[kSub];
+  __shared__ __attribute__((aligned(16))) float s_e[kSub];
+  __shared__ __attribute__((aligned(16))) float s_w[kSub];
   __shared__ float s_decay;
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (a.H / a.G);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rt = w >> 1, pt = w & 1;        // output tile
-  const int spt = w & 1, snt0 = 2 * (w >> 1);  // state tiles
+  const int lc = lane & 31, hf = lane >> 5;
+  const int rt = w >> 1, pt = w & 1;
+  const int partner = w ^ 2;
   const float a2 = a.A[h] * kLog2e;
   const float dh = a.D ? a.D[h] : 0.f;
   const size_t state_stride = (size_t)kP * kN;
+  const int p = pt * 32 + lc;  // headdim of this lane's output column
 
+  // x staging: thread -> (step pair j, 8 headdim values pg*8..).
+  const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
+  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * kP, (uint32_t)((size_t)a.L * a.H * kP * 2));
+  auto load_x = [&](int l0, u32x4* xr) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int l = l0 + jx + e;
+      const uint32_t off = (l < a.L) ? (uint32_t)((((size_t)l * a.H + h) * kP + pg * 8) * 2) : kOffNone;
+      xr[e] = buf_load_u32x4(rx, off);
+    }
+  };
+  auto store_x = [&](const u32x4* xr) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w0 = xr[0][k], w1 = xr[1][k];
+      *reinterpret_cast<uint32_t*>(&xT[tsw(pg * 8 + 2 * k, jx)]) = (w0 & 0xffffu) | (w1 << 16);
+      *reinterpret_cast<uint32_t*>(&xT[tsw(pg * 8 + 2 * k + 1, jx)]) = (w0 >> 16) | (w1 & 0xffff0000u);
+    }
+  };
+
+  // This wave's two S^T tiles: state rows (2*rt + t)*32.., headdim tile pt.
   f32x16 st[2];
-  load_state(st, a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, spt, snt0);
+  const float* sin = a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) load_stateT(st[t], sin, 2 * rt + t, pt);
+
+  // Output of the previous block, finished at the start of the next one (the
+  // partner's partial C S^T is in xbuf then): accumulator, exp(s_i) and x of
+  // this lane's 16 rows.
+  f32x16 yprev = {};
+  float eprev[16], xprev[16];
+  int lprev = -1;  // first step of the block yprev belongs to
+  auto finish = [&]() {
+    if (lprev < 0) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = rt * 32 + acc_row(r, lane);
+      const int l = lprev + i;
+      float v = __builtin_fmaf(eprev[r], xbuf[partner][r][lane], yprev[r]);
+      v = __builtin_fmaf(dh, xprev[r], v);
+      if (l < a.L && l < (c + 1) * a.Q) {
+        const size_t off = (((size_t)b * a.L + l) * a.H + h) * kP + p;
+        if (a.z) v *= silu(bf16_to_f32(a.z[off]));
+        a.y[off] = v;
+      }
+    }
+  };
 
   const int lbeg = c * a.Q;
   const int lend = min(a.L, lbeg + a.Q);
+  u32x4 xr[2];
+  BCRegs br, cr;
+  float d;
+  load_x(lbeg, xr);
+  load_bc_rows(a, a.B, b, g, lbeg, br);
+  load_bc_rows(a, a.C, b, g, lbeg, cr);
+  d = load_delta(a, b, h, lbeg);  // every wave loads it (no branch around loads); wave 0 uses it
   for (int l0 = lbeg; l0 < lend; l0 += kSub) {
-    // Stage the block and the current state (hi/lo bf16 split of fp32).
-    block_cumsum64(a, b, h, l0, s_dl, s_cum);
-    stage_xT(a, b, h, l0, xT);
-    stage_bc<true, true>(a, a.B, b, g, l0, Bs, BT);
-    stage_bc<true, false>(a, a.C, b, g, l0, Cs, nullptr);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = spt * 32 + acc_row(r, lane), n = (snt0 + t) * 32 + (lane & 31);
-        const float v = st[t][r];
-        const uint16_t hv = f32_to_bf16(v);
-        Shi[p][n] = hv;
-        Slo[p][n] = f32_to_bf16(v - bf16_to_f32(hv));
-      }
+    finish();  // the previous block (its xbuf entries were written before the last barrier)
+    store_x(xr);
+    store_bc_rows<true, true>(br, Bs, BT);
+    store_bc_rows<true, false>(cr, Cs, nullptr);
+    if (w == 0) block_weights(d, a2, s_dl, s_cum, s_e, s_w, &s_decay);
+    // Next block's loads in flight while this one is used (the block after
+    // the chunk's last is read and ignored; past L reads zero).
+    load_x(l0 + kSub, xr);
+    load_bc_rows(a, a.B, b, g, l0 + kSub, br);
+    load_bc_rows(a, a.C, b, g, l0 + kSub, cr);
+    d = load_delta(a, b, h, l0 + kSub);
     __syncthreads();
-    block_weights(a2, s_dl, s_cum, s_e, s_w, &s_decay);
 
-    // G = C B^T for this wave's 32x32 tile (row tile rt, column tile pt).
-    {
-      f32x16 gacc = {};
+    // C S^T over this wave's state rows for both row tiles, the state as hi + lo.
+    f32x16 yown = {}, yoth = {};
 #pragma unroll
-      for (int kk = 0; kk < kN / 16; ++kk) {
-        const int k0 = kk * 16 + 8 * (lane >> 5);
-        const u32x4 av = *reinterpret_cast<const u32x4*>(&Cs[rt * 32 + (lane & 31)][k0]);
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(&Bs[pt * 32 + (lane & 31)][k0]);
-        gacc = mfma(av, bv, gacc);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Gb[rt * 32 + acc_row(r, lane)][pt * 32 + (lane & 31)] = gacc[r];
+    for (int t = 0; t < 2; ++t) {
+      auto slice = [&](auto s_tag) {
+        constexpr int S = decltype(s_tag)::value;
+        float v[8];
+        acc_kslice<S>(st[t], v);
+        u32x4 bh, bl;
+        split8(v, bh, bl);
+        const int k0 = (2 * rt + t) * 32 + 16 * S + 8 * hf;
+        const u32x4 c_own = *reinterpret_cast<const u32x4*>(&Cs[rt * 32 + lc][k0]);
+        const u32x4 c_oth = *reinterpret_cast<const u32x4*>(&Cs[(1 - rt) * 32 + lc][k0]);
+        yown = mfma(c_own, bh, yown);
+        yown = mfma(c_own, bl, yown);
+        yoth = mfma(c_oth, bh, yoth);
+        yoth = mfma(c_oth, bl, yoth);
+      };
+      slice(std::integral_constant<int, 0>{});
+      slice(std::integral_constant<int, 1>{});
     }
-
-    // Off-diagonal part: exp(s_i) * C_i S^T, state as hi + lo.
-    f32x16 yacc = {};
 #pragma unroll
-    for (int kk = 0; kk < kN / 16; ++kk) {
-      const int k0 = kk * 16 + 8 * (lane >> 5);
-      const u32x4 av = *reinterpret_cast<const u32x4*>(&Cs[rt * 32 + (lane & 31)][k0]);
-      const u32x4 bh = *reinterpret_cast<const u32x4*>(&Shi[pt * 32 + (lane & 31)][k0]);
-      const u32x4 bl = *reinterpret_cast<const u32x4*>(&Slo[pt * 32 + (lane & 31)][k0]);
-      yacc = mfma(av, bh, yacc);
-      yacc = mfma(av, bl, yacc);
+    for (int r = 0; r < 16; ++r) xbuf[w][r][lane] = yoth[r];
+
+    // Own tile: exp(s_i) (own part of C S^T) + diagonal block.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = rt * 32 + acc_row(r, lane);
+      eprev[r] = s_e[i];
+      yown[r] *= eprev[r];
     }
-    __syncthreads();  // G tiles and block weights complete
+    if (rt == 0)
+      diag_block<0>(yown, Cs, Bs, xT, s_cum, s_dl, a2, pt);
+    else
+      diag_block<1>(yown, Cs, Bs, xT, s_cum, s_dl, a2, pt);
+    yprev = yown;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) yacc[r] *= s_e[rt * 32 + acc_row(r, lane)];
-
-    // Diagonal block: M = mask o G o exp(s_i - s_j) delta_j, times x.
-    {
-      const int i = rt * 32 + (lane & 31);
-      const float ci = s_cum[i];
-      for (int kk = 0; kk < 2 * (rt + 1); ++kk) {
-        const int j0 = kk * 16 + 8 * (lane >> 5);
-        const float4 g0 = *reinterpret_cast<const float4*>(&Gb[i][j0]);
-        const float4 g1 = *reinterpret_cast<const float4*>(&Gb[i][j0 + 4]);
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        float m[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int j = j0 + q;
-          const float dec = exp2_fast(fminf(a2 * (ci - s_cum[j]), 0.f));
-          m[q] = (j <= i) ? gv[q] * dec * s_dl[j] : 0.f;
-        }
-        u32x4 ah, al;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t hh, ll;
-          split2(m[2 * q], m[2 * q + 1], hh, ll);
-          ah[q] = hh;
-          al[q] = ll;
-        }
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(&xT[pt * 32 + (lane & 31)][j0]);
-        yacc = mfma(ah, bv, yacc);
-        yacc = mfma(al, bv, yacc);
-      }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int i0 = rt * 32 + 8 * g4 + 4 * hf;
+      const u32x2 xx = *reinterpret_cast<const u32x2*>(&xT[tsw(p, i0)]);
+      xprev[4 * g4] = bf16_lo(xx[0]);
+      xprev[4 * g4 + 1] = bf16_hi(xx[0]);
+      xprev[4 * g4 + 2] = bf16_lo(xx[1]);
+      xprev[4 * g4 + 3] = bf16_hi(xx[1]);
     }
+    lprev = l0;
 
-    // Skip term, gate, store: element (row i, headdim p).
-    {
-      const int p = pt * 32 + (lane & 31);
+    // State after the block: S^T <- decay S^T + B^T (w o x).
+    const float decay = s_decay;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = rt * 32 + acc_row(r, lane);
-        const int l = l0 + i;
-        if (l < lend) {
-          float v = yacc[r];
-          const size_t off = (((size_t)b * a.L + l) * a.H + h) * kP + p;
-          if (a.D) v = __builtin_fmaf(dh, bf16_to_f32(xT[p][i]), v);
-          if (a.z) v *= silu(bf16_to_f32(a.z[off]));
-          a.y[off] = v;
-        }
+    for (int t = 0; t < 2; ++t) st[t] *= decay;
+#pragma unroll
+    for (int kk = 0; kk < kSub / 16; ++kk) {
+      const int j0 = kk * 16 + 8 * hf;
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(&xT[tsw(p, j0)]);
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_w[j0]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_w[j0 + 4]);
+      const float v[8] = {bf16_lo(xv[0]) * w0[0], bf16_hi(xv[0]) * w0[1], bf16_lo(xv[1]) * w0[2],
+                          bf16_hi(xv[1]) * w0[3], bf16_lo(xv[2]) * w1[0], bf16_hi(xv[2]) * w1[1],
+                          bf16_lo(xv[3]) * w1[2], bf16_hi(xv[3]) * w1[3]};
+      u32x4 bh, bl;
+      split8(v, bh, bl);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[tsw((2 * rt + t) * 32 + lc, j0)]);
+        st[t] = mfma(av, bh, st[t]);
+        st[t] = mfma(av, bl, st[t]);
       }
     }
-
-    // State after the block.
-    state_update_block(st, s_decay, s_w, xT, BT, spt, snt0);
     __syncthreads();
   }
+  finish();
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -409,7 +561,7 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.G = (int)p.ngroups;
   a.Q = (int)p.chunk;
   a.nchunks = (int)((p.seqlen + p.chunk - 1) / p.chunk);
-  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)a.H, (unsigned)a.batch), dim3(kT), 0, stream, a);
+  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch), dim3(kT), 0, stream, a);
   hipLaunchKernelGGL(ssd_scan_kernel, dim3((unsigned)a.nchunks, (unsigned)a.H, (unsigned)a.batch), dim3(kT), 0,
                      stream, a);
   return hipGetLastError();
