@@ -115,24 +115,41 @@ struct SSDArgs {
   int batch, L, H, G, Q, nchunks;
 };
 
+// x plus lane (lane - S) of its 16-lane row (0 for the first S lanes of a row).
+template <int S>
+__device__ __forceinline__ float add_row_shr(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + S, 0xf, 0xf,
+                                                                   false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave in a fixed order: scans
+// inside each 16-lane row (DPP row_shr 1, 2, 4, 8), then row 0's total is
+// added to row 1 and row 2's to row 3 (row_bcast:15), then the total of rows
+// 0-1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x = add_row_shr<1>(x);
+  x = add_row_shr<2>(x);
+  x = add_row_shr<4>(x);
+  x = add_row_shr<8>(x);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
 // Wave 0: delta of the block's steps (d, zero past L), inclusive prefix sums
-// in a fixed shuffle order, and e_i = exp(s_i), w_j = delta_j exp(s_last -
-// s_j), decay = exp(s_last) with s = A * prefix.  Any of the outputs may be null.
-__device__ __forceinline__ void block_weights(float d, float a2, float* s_dl, float* s_cum, float* s_e, float* s_w,
+// and, with s = A * prefix (kept as ls = s * log2 e): e_i = exp(s_i),
+// w_j = delta_j exp(s_last - s_j), decay = exp(s_last).  Any of the outputs
+// but s_w may be null.
+__device__ __forceinline__ void block_weights(float d, float a2, float* s_dl, float* s_ls, float* s_e, float* s_w,
                                               float* s_decay) {
   const int lane = threadIdx.x & 63;
-  float s = d;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(s, o, 64);
-    if (lane >= o) s += t;
-  }
-  const float last = __shfl(s, 63, 64);
+  const float ls = a2 * wave_prefix_sum(d);
+  const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
   if (s_dl) s_dl[lane] = d;
-  if (s_cum) s_cum[lane] = s;
-  if (s_e) s_e[lane] = exp2_fast(a2 * s);
-  s_w[lane] = d * exp2_fast(a2 * (last - s));
-  if (lane == 0) *s_decay = exp2_fast(a2 * last);
+  if (s_ls) s_ls[lane] = ls;
+  if (s_e) s_e[lane] = exp2_fast(ls);
+  s_w[lane] = d * exp2_fast(last - ls);
+  if (lane == 0) *s_decay = exp2_fast(last);
 }
 
 __device__ __forceinline__ float load_delta(const SSDArgs& a, int b, int h, int l0) {
@@ -317,11 +334,11 @@ __global__ void __launch_bounds__(kT) ssd_state_kernel(SSDArgs a) {
 // wave (1-rt, pt) through LDS.
 template <int RT>
 __device__ __forceinline__ void diag_block(f32x16& yacc, const uint16_t (*Cs)[kN + kPadH],
-                                           const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_cum,
-                                           const float* s_dl, float a2, int pt) {
+                                           const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_ls,
+                                           const float* s_dl, int pt) {
   const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int i = RT * 32 + lc;
-  const float ci = s_cum[i];
+  const float lsi = s_ls[i];
 #pragma unroll
   for (int jt = 0; jt <= RT; ++jt) {
     // G^T tile (rows j of tile jt, columns i of tile RT) = B C^T.
@@ -338,8 +355,8 @@ __device__ __forceinline__ void diag_block(f32x16& yacc, const uint16_t (*Cs)[kN
       float gv[8];
       acc_kslice<S>(gacc, gv);
       const int j0 = jt * 32 + 16 * S + 8 * hf;
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_cum[j0]);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_cum[j0 + 4]);
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_ls[j0]);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_ls[j0 + 4]);
       const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_dl[j0]);
       const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_dl[j0 + 4]);
       const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
@@ -347,7 +364,7 @@ __device__ __forceinline__ void diag_block(f32x16& yacc, const uint16_t (*Cs)[kN
       float m[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float dec = exp2_fast(fminf(a2 * (ci - cj[t]), 0.f));
+        const float dec = exp2_fast(fminf(lsi - cj[t], 0.f));
         const float v = gv[t] * dec * dj[t];
         m[t] = (jt < RT || j0 + t <= i) ? v : 0.f;
       }
@@ -362,6 +379,7 @@ __device__ __forceinline__ void diag_block(f32x16& yacc, const uint16_t (*Cs)[kN
   }
 }
 
+template <bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xT[kP * kTRow];  // tsw layout, headdim rows
   __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];  // tsw layout, state rows
@@ -369,7 +387,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kSub][kN + kPadH];
   __shared__ __attribute__((aligned(16))) float xbuf[4][16][64];  // partial C S^T handed to the partner wave
   __shared__ __attribute__((aligned(16))) float s_dl[kSub];
-  __shared__ __attribute__((aligned(16))) float s_cum[kSub];
+  __shared__ __attribute__((aligned(16))) float s_ls[kSub];
   __shared__ __attribute__((aligned(16))) float s_e[kSub];
   __shared__ __attribute__((aligned(16))) float s_w[kSub];
   __shared__ float s_decay;
@@ -414,27 +432,39 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   // Output of the previous block, finished at the start of the next one (the
   // partner's partial C S^T is in xbuf then): accumulator, exp(s_i) and x of
   // this lane's 16 rows.
+  const int lbeg = c * a.Q;
+  const int lend = min(a.L, lbeg + a.Q);
   f32x16 yprev = {};
   float eprev[16], xprev[16];
   int lprev = -1;  // first step of the block yprev belongs to
+  // y and z rows of this batch entry and head: element (step l, headdim p) at
+  // l*H*P + p; steps outside the chunk are dropped (store) or read as 0 (z).
+  const uint32_t row = (uint32_t)(a.H * kP);
+  const size_t bh_el = (size_t)b * a.L * a.H * kP + (size_t)h * kP;
+  const rsrc_t ry = make_rsrc(a.y + bh_el, (uint32_t)(((size_t)a.L * a.H - h) * kP * 4));
+  const rsrc_t rz = make_rsrc(a.z ? a.z + bh_el : nullptr, a.z ? (uint32_t)(((size_t)a.L * a.H - h) * kP * 2) : 0u);
   auto finish = [&]() {
     if (lprev < 0) return;
+    float zv[16];
+    if constexpr (HAS_Z) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int l = lprev + rt * 32 + acc_row(r, lane);
+        const uint32_t zo = (l < lend) ? ((uint32_t)l * row + (uint32_t)p) * 2u : kOffNone;
+        zv[r] = bf16_to_f32(buf_load_u16(rz, zo));
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = rt * 32 + acc_row(r, lane);
-      const int l = lprev + i;
+      const int l = lprev + rt * 32 + acc_row(r, lane);
       float v = __builtin_fmaf(eprev[r], xbuf[partner][r][lane], yprev[r]);
-      v = __builtin_fmaf(dh, xprev[r], v);
-      if (l < a.L && l < (c + 1) * a.Q) {
-        const size_t off = (((size_t)b * a.L + l) * a.H + h) * kP + p;
-        if (a.z) v *= silu(bf16_to_f32(a.z[off]));
-        a.y[off] = v;
-      }
+      if constexpr (HAS_D) v = __builtin_fmaf(dh, xprev[r], v);
+      if constexpr (HAS_Z) v *= silu(zv[r]);
+      const uint32_t yo = (l < lend) ? ((uint32_t)l * row + (uint32_t)p) * 4u : kOffNone;
+      buf_store_u32(ry, yo, __float_as_uint(v));
     }
   };
 
-  const int lbeg = c * a.Q;
-  const int lend = min(a.L, lbeg + a.Q);
   u32x4 xr[2];
   BCRegs br, cr;
   float d;
@@ -447,7 +477,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     store_x(xr);
     store_bc_rows<true, true>(br, Bs, BT);
     store_bc_rows<true, false>(cr, Cs, nullptr);
-    if (w == 0) block_weights(d, a2, s_dl, s_cum, s_e, s_w, &s_decay);
+    if (w == 0) block_weights(d, a2, s_dl, s_ls, s_e, s_w, &s_decay);
     // Next block's loads in flight while this one is used (the block after
     // the chunk's last is read and ignored; past L reads zero).
     load_x(l0 + kSub, xr);
@@ -488,18 +518,20 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       yown[r] *= eprev[r];
     }
     if (rt == 0)
-      diag_block<0>(yown, Cs, Bs, xT, s_cum, s_dl, a2, pt);
+      diag_block<0>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
     else
-      diag_block<1>(yown, Cs, Bs, xT, s_cum, s_dl, a2, pt);
+      diag_block<1>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
     yprev = yown;
+    if constexpr (HAS_D) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int i0 = rt * 32 + 8 * g4 + 4 * hf;
-      const u32x2 xx = *reinterpret_cast<const u32x2*>(&xT[tsw(p, i0)]);
-      xprev[4 * g4] = bf16_lo(xx[0]);
-      xprev[4 * g4 + 1] = bf16_hi(xx[0]);
-      xprev[4 * g4 + 2] = bf16_lo(xx[1]);
-      xprev[4 * g4 + 3] = bf16_hi(xx[1]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int i0 = rt * 32 + 8 * g4 + 4 * hf;
+        const u32x2 xx = *reinterpret_cast<const u32x2*>(&xT[tsw(p, i0)]);
+        xprev[4 * g4] = bf16_lo(xx[0]);
+        xprev[4 * g4 + 1] = bf16_hi(xx[0]);
+        xprev[4 * g4 + 2] = bf16_lo(xx[1]);
+        xprev[4 * g4 + 3] = bf16_hi(xx[1]);
+      }
     }
     lprev = l0;
 
@@ -562,8 +594,15 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.Q = (int)p.chunk;
   a.nchunks = (int)((p.seqlen + p.chunk - 1) / p.chunk);
   hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch), dim3(kT), 0, stream, a);
-  hipLaunchKernelGGL(ssd_scan_kernel, dim3((unsigned)a.nchunks, (unsigned)a.H, (unsigned)a.batch), dim3(kT), 0,
-                     stream, a);
+  const dim3 grid((unsigned)a.nchunks, (unsigned)a.H, (unsigned)a.batch);
+  if (a.z && a.D)
+    hipLaunchKernelGGL((ssd_scan_kernel<true, true>), grid, dim3(kT), 0, stream, a);
+  else if (a.z)
+    hipLaunchKernelGGL((ssd_scan_kernel<true, false>), grid, dim3(kT), 0, stream, a);
+  else if (a.D)
+    hipLaunchKernelGGL((ssd_scan_kernel<false, true>), grid, dim3(kT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((ssd_scan_kernel<false, false>), grid, dim3(kT), 0, stream, a);
   return hipGetLastError();
 }
 
