@@ -145,7 +145,9 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
 /*          state after the last step of each chunk, nchunks = ceil(L/chunk). */
 /* D, z, h0, chunk_states and h_last may be NULL.                           */
 /* Supported: in_dtype MSS_BF16; headdim 64; dstate 128; chunk 64, 128 or   */
-/* 256; nheads % ngroups == 0.  seqlen need not be a multiple of chunk.      */
+/* 256; nheads % ngroups == 0; seqlen*nheads*headdim and                  */
+/* seqlen*ngroups*dstate below 2^30 (else MSS_ERR_SHAPE).  seqlen need not  */
+/* be a multiple of chunk.                                                  */
 /* `flags` must be 0.  Outputs must not overlap inputs or each other.        */
 /* ------------------------------------------------------------------------ */
 mss_status mss_ssd_chunk_fwd(const void* x, const float* delta, const float* A, const void* B,

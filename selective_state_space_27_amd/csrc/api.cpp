@@ -180,7 +180,10 @@ static mss_status ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads,
   if (!dtype_ok(t)) return MSS_ERR_DTYPE;
   if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || chunk <= 0)
     return MSS_ERR_SHAPE;
-  if (seqlen * nheads * headdim > kMaxIndex || batch > 65535 || nheads > 65535) return MSS_ERR_SHAPE;
+  // Byte offsets inside one batch entry of y (fp32) and of B, C must fit 32 bits.
+  if (seqlen * nheads * headdim >= (int64_t{1} << 30) || seqlen * ngroups * dstate >= (int64_t{1} << 30) ||
+      batch > 65535 || nheads > 65535)
+    return MSS_ERR_SHAPE;
   if (t != MSS_BF16) return MSS_ERR_UNSUPPORTED;
   if (headdim != 64 || dstate != 128 || !(chunk == 64 || chunk == 128 || chunk == 256)) return MSS_ERR_UNSUPPORTED;
   if (nheads % ngroups != 0) return MSS_ERR_UNSUPPORTED;

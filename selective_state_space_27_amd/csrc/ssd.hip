@@ -112,7 +112,9 @@ struct SSDArgs {
   float* chunk_states; // [b, nchunks, H, P, N] or null
   float* h_last;       // [b, H, P, N] or null
   float* s_in;         // workspace [b, nchunks, H, P, N]: state entering each chunk
-  int batch, L, H, G, Q, nchunks;
+  float* dlT;          // workspace [b, H, Lp]: delta, head-major (0 past L)
+  float* lsT;          // workspace [b, H, Lp]: A log2(e) times the prefix sum of delta inside each 64-step block
+  int batch, L, H, G, Q, nchunks, Lp;
 };
 
 // x plus lane (lane - S) of its 16-lane row (0 for the first S lanes of a row).
@@ -136,25 +138,29 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
   return x;
 }
 
-// Wave 0: delta of the block's steps (d, zero past L), inclusive prefix sums
-// and, with s = A * prefix (kept as ls = s * log2 e): e_i = exp(s_i),
-// w_j = delta_j exp(s_last - s_j), decay = exp(s_last).  Any of the outputs
-// but s_w may be null.
-__device__ __forceinline__ void block_weights(float d, float a2, float* s_dl, float* s_ls, float* s_e, float* s_w,
-                                              float* s_decay) {
-  const int lane = threadIdx.x & 63;
-  const float ls = a2 * wave_prefix_sum(d);
-  const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
-  if (s_dl) s_dl[lane] = d;
-  if (s_ls) s_ls[lane] = ls;
-  if (s_e) s_e[lane] = exp2_fast(ls);
-  s_w[lane] = d * exp2_fast(last - ls);
-  if (lane == 0) *s_decay = exp2_fast(last);
-}
-
-__device__ __forceinline__ float load_delta(const SSDArgs& a, int b, int h, int l0) {
-  const int l = l0 + (threadIdx.x & 63);
-  return (l < a.L) ? a.delta[((size_t)b * a.L + l) * a.H + h] : 0.f;
+// Head-major delta rows and their scaled prefix sums, per (64-step block,
+// 64-head tile, batch): ls_i = A log2(e) sum_{j<=i} delta_j inside the block,
+// so that inside a block exp(s_i - s_j) = exp2(ls_i - ls_j), the decay over a
+// whole block is exp2(ls_63) and steps past L (delta 0) leave ls unchanged.
+__global__ void __launch_bounds__(256) ssd_cumsum_kernel(SSDArgs a) {
+  __shared__ float tile[kSub][65];
+  const int l0 = blockIdx.x * kSub, h0 = blockIdx.y * 64, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kSub / 4; ++i) {
+    const int j = w + 4 * i, l = l0 + j, hh = h0 + lane;
+    tile[j][lane] = (l < a.L && hh < a.H) ? a.delta[((size_t)b * a.L + l) * a.H + hh] : 0.f;
+  }
+  __syncthreads();
+  for (int k = 0; k < 16; ++k) {
+    const int h = h0 + w * 16 + k;
+    if (h >= a.H) break;
+    const float d = tile[lane][w * 16 + k];
+    const float ls = a.A[h] * kLog2e * wave_prefix_sum(d);
+    const size_t o = ((size_t)b * a.H + h) * a.Lp + l0 + lane;
+    a.dlT[o] = d;
+    a.lsT[o] = ls;
+  }
 }
 
 // B or C rows of group g for steps (l0 + j, l0 + j + 1), 8 states from ng*8:
@@ -224,105 +230,158 @@ __device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt
 }
 
 // ---------------------------------------------------------------------------
-// Chunk states.  grid (2H, batch), 256 threads: workgroup (b, h, pt) owns
-// headdim tile pt; wave w owns the S^T tile of state rows w*32.. .
-__global__ void __launch_bounds__(kT) ssd_state_kernel(SSDArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xT[32 * kTRow];  // tsw layout, this tile's headdim rows
-  __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];  // tsw layout, state rows
-  __shared__ __attribute__((aligned(16))) float s_w[kSub];
-  __shared__ float s_decay;
+// Chunk states.  grid (2H, batch), 512 threads: workgroup (b, h, pt) owns
+// headdim tile pt.  Wave w owns S^T rows (w&3)*32.. over half of every block's
+// steps (k-half w>>2): the state is the sum of the two halves' partial states,
+// which decay alike, so they are only added where a state is written out.
+// Each thread forms the decay weights of its own steps from the head-major
+// delta rows; the weighted x (w_j x_j) is staged once per block as bf16 hi/lo
+// pairs.  Stagings are double-buffered: one barrier per block.
+constexpr int kTS = 512;
 
-  const int pt = blockIdx.x & 1, h = blockIdx.x >> 1, b = blockIdx.y;
+__global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xh[2][32 * kTRow];  // tsw layout: hi part of w o x, headdim rows
+  __shared__ __attribute__((aligned(16))) uint16_t xl[2][32 * kTRow];  // lo part
+  __shared__ __attribute__((aligned(16))) uint16_t BT[2][kN * kTRow];  // tsw layout, state rows
+  __shared__ __attribute__((aligned(16))) float xsum[4][16][64];        // k-half 1 partial states, for output
+
+  // Both headdim tiles of a head on one XCD (workgroups are dealt to the XCDs
+  // round-robin), so that each x row is fetched from HBM once.
+  const int i = blockIdx.x;
+  const bool pair = (a.H & 7) == 0;
+  const int pt = pair ? (i >> 3) & 1 : i & 1;
+  const int h = pair ? ((i >> 4) << 3) | (i & 7) : i >> 1;
+  const int b = blockIdx.y;
   const int g = h / (a.H / a.G);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lc = lane & 31, hf = lane >> 5;
-  const float a2 = a.A[h] * kLog2e;
+  const int nt = w & 3, kh = w >> 2;
   const size_t state_stride = (size_t)kP * kN;
 
-  // x staging: thread -> (step pair j, 4 headdim values pq*4..) of this tile.
-  const int pq = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
-  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * kP, (uint32_t)((size_t)a.L * a.H * kP * 2));
-  auto load_x = [&](int l0, u32x2* xr) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int l = l0 + jx + e;
-      const uint32_t off = (l < a.L) ? (uint32_t)((((size_t)l * a.H + h) * kP + pt * 32 + pq * 4) * 2) : kOffNone;
-      xr[e] = buf_load_u32x2(rx, off);
-    }
-  };
-  auto store_x = [&](const u32x2* xr) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t w0 = xr[0][k], w1 = xr[1][k];
-      *reinterpret_cast<uint32_t*>(&xT[tsw(pq * 4 + 2 * k, jx)]) = (w0 & 0xffffu) | (w1 << 16);
-      *reinterpret_cast<uint32_t*>(&xT[tsw(pq * 4 + 2 * k + 1, jx)]) = (w0 >> 16) | (w1 & 0xffff0000u);
-    }
-  };
+  // Staging map: thread -> step pair (jx, jx+1); headdim values pq*2, pq*2+1
+  // of x, states ng*8 .. ng*8+7 of B.
+  const int pq = threadIdx.x & 15, ng = pq, jx = 2 * (threadIdx.x >> 4);
+  // Each block's loads go through descriptors based at the block's first
+  // step, so the per-lane offsets are fixed; rows past L (or past the padded
+  // delta rows) lie beyond the descriptor and read 0.  Byte offsets inside
+  // one batch entry fit 32 bits (checked by the caller).
+  const uint32_t x_row = (uint32_t)(a.H * kP * 2), b_row = (uint32_t)(a.G * kN * 2);
+  const uint32_t xo0 = (uint32_t)jx * x_row + (uint32_t)((h * kP + pt * 32 + pq * 2) * 2), xo1 = xo0 + x_row;
+  const uint32_t bo0 = (uint32_t)jx * b_row + (uint32_t)((g * kN + ng * 8) * 2), bo1 = bo0 + b_row;
+  const uint32_t dlo = (uint32_t)jx * 4u;
+  const size_t row_bh = ((size_t)b * a.H + h) * a.Lp;
+  typedef __attribute__((address_space(4))) const float scalar_float;  // uniform loads through the scalar cache
 
-  f32x16 st;
-  load_stateT(st, a.h0 ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, w, pt);
-
-  // Three blocks of loads in flight (ring of register slots, tile loop
-  // unrolled by 3 so the slot index is a compile-time constant).
+  // Loads of one block, kept three blocks ahead.
   struct Slot {
-    u32x2 xr[2];
-    BCRegs br;
-    float d;
+    uint32_t xr[2];
+    u32x4 br[2];
+    u32x2 dl, ls;
+    float last;
   };
-  Slot ring[3];
   auto load_slot = [&](int blk, Slot& sl) {
-    const int l0 = blk * kSub;  // past L: zeros
-    load_x(l0, sl.xr);
-    load_bc_rows(a, a.B, b, g, l0, sl.br);
-    sl.d = load_delta(a, b, h, l0);
+    const int l0 = blk * kSub;
+    const uint32_t left = (uint32_t)max(a.L - l0, 0), left_p = (uint32_t)max(a.Lp - l0, 0);
+    const rsrc_t rx = make_rsrc(a.x + ((size_t)b * a.L + l0) * a.H * kP, left * x_row);
+    const rsrc_t rb = make_rsrc(a.B + ((size_t)b * a.L + l0) * a.G * kN, left * b_row);
+    const rsrc_t rd = make_rsrc(a.dlT + row_bh + l0, left_p * 4u);
+    const rsrc_t rl = make_rsrc(a.lsT + row_bh + l0, left_p * 4u);
+    sl.xr[0] = buf_load_u32(rx, xo0);
+    sl.xr[1] = buf_load_u32(rx, xo1);
+    sl.br[0] = buf_load_u32x4(rb, bo0);
+    sl.br[1] = buf_load_u32x4(rb, bo1);
+    sl.dl = buf_load_u32x2(rd, dlo);
+    sl.ls = buf_load_u32x2(rl, dlo);
+    // Prefix sum at the block's last step (blocks past the end read the last block's).
+    sl.last = ((scalar_float*)(a.lsT + row_bh))[min(l0, a.Lp - kSub) + kSub - 1];
   };
-  load_slot(0, ring[0]);
-  load_slot(1, ring[1]);
-  load_slot(2, ring[2]);
+  // w o x for steps (jx, jx+1) of headdim rows pq*2, pq*2+1 as hi/lo pairs,
+  // w_j = delta_j exp(s_last - s_j); B transposed to state rows.
+  auto stage = [&](const Slot& sl, int buf) {
+    const float w0 = __uint_as_float(sl.dl[0]) * exp2_fast(sl.last - __uint_as_float(sl.ls[0]));
+    const float w1 = __uint_as_float(sl.dl[1]) * exp2_fast(sl.last - __uint_as_float(sl.ls[1]));
+    uint32_t hi, lo;
+    split2(bf16_lo(sl.xr[0]) * w0, bf16_lo(sl.xr[1]) * w1, hi, lo);
+    *reinterpret_cast<uint32_t*>(&xh[buf][tsw(pq * 2, jx)]) = hi;
+    *reinterpret_cast<uint32_t*>(&xl[buf][tsw(pq * 2, jx)]) = lo;
+    split2(bf16_hi(sl.xr[0]) * w0, bf16_hi(sl.xr[1]) * w1, hi, lo);
+    *reinterpret_cast<uint32_t*>(&xh[buf][tsw(pq * 2 + 1, jx)]) = hi;
+    *reinterpret_cast<uint32_t*>(&xl[buf][tsw(pq * 2 + 1, jx)]) = lo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t v0 = sl.br[0][k], v1 = sl.br[1][k];
+      *reinterpret_cast<uint32_t*>(&BT[buf][tsw(ng * 8 + 2 * k, jx)]) = (v0 & 0xffffu) | (v1 << 16);
+      *reinterpret_cast<uint32_t*>(&BT[buf][tsw(ng * 8 + 2 * k + 1, jx)]) = (v0 >> 16) | (v1 & 0xffff0000u);
+    }
+  };
+
+  // The state is the sum of both k-halves' partials: k-half 0 starts from h0.
+  f32x16 st;
+  load_stateT(st, (a.h0 && kh == 0) ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, nt, pt);
+  // Writes the full state tile: k-half 1 hands its partial over through LDS.
+  auto write_state = [&](float* S) {
+    if (kh == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xsum[nt][r][lane] = st[r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      f32x16 t = st;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] += xsum[nt][r][lane];
+      store_stateT(t, S, nt, pt);
+    }
+    __syncthreads();
+  };
 
   const int sub_per_chunk = a.Q / kSub;
   const int nsub = (a.L + kSub - 1) / kSub;
-  auto step = [&](auto slot_tag, int sb) {
-    constexpr int S = decltype(slot_tag)::value;
-    const int c = sb / sub_per_chunk;
-    if (sb % sub_per_chunk == 0)  // state entering chunk c
-      store_stateT(st, a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, w, pt);
-    store_x(ring[S].xr);
-    store_bc_rows<false, true>(ring[S].br, nullptr, BT);
-    if (w == 0) block_weights(ring[S].d, a2, nullptr, nullptr, nullptr, s_w, &s_decay);
-    load_slot(sb + 3, ring[S]);
-    __syncthreads();
+  // Software pipeline: iteration sb runs block sb's products from staging
+  // buffer sb&1 while it stages block sb+1 into the other buffer (whose last
+  // readers finished before the previous barrier), one barrier per block.
+  // Ring slot (sb+1)%3 holds block sb+1, loaded three iterations earlier.
+  Slot ring[3];
+  load_slot(0, ring[0]);
+  load_slot(1, ring[1]);
+  load_slot(2, ring[2]);
+  stage(ring[0], 0);
+  float decay = exp2_fast(ring[0].last);  // exp(s_last) of the block being multiplied
+  load_slot(3, ring[0]);
+  __syncthreads();
 
-    st *= s_decay;
+  auto step = [&](auto slot_tag, int sb) {
+    constexpr int S1 = decltype(slot_tag)::value;  // (sb + 1) % 3
+    const int c = sb / sub_per_chunk;
+    const int buf = sb & 1;
+    if (sb % sub_per_chunk == 0)  // state entering chunk c
+      write_state(a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
+    st *= decay;
 #pragma unroll
-    for (int kk = 0; kk < kSub / 16; ++kk) {
-      const int j0 = kk * 16 + 8 * hf;
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(&xT[tsw(lc, j0)]);
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_w[j0]);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_w[j0 + 4]);
-      const float v[8] = {bf16_lo(xv[0]) * w0[0], bf16_hi(xv[0]) * w0[1], bf16_lo(xv[1]) * w0[2],
-                          bf16_hi(xv[1]) * w0[3], bf16_lo(xv[2]) * w1[0], bf16_hi(xv[2]) * w1[1],
-                          bf16_lo(xv[3]) * w1[2], bf16_hi(xv[3]) * w1[3]};
-      u32x4 bh, bl;
-      split8(v, bh, bl);
-      const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[tsw(w * 32 + lc, j0)]);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int j0 = (kh * 2 + kk) * 16 + 8 * hf;
+      const u32x4 bh = *reinterpret_cast<const u32x4*>(&xh[buf][tsw(lc, j0)]);
+      const u32x4 bl = *reinterpret_cast<const u32x4*>(&xl[buf][tsw(lc, j0)]);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[buf][tsw(nt * 32 + lc, j0)]);
       st = mfma(av, bh, st);
       st = mfma(av, bl, st);
     }
+    stage(ring[S1], buf ^ 1);
+    decay = exp2_fast(ring[S1].last);
+    load_slot(sb + 4, ring[S1]);
     const bool chunk_end = (sb % sub_per_chunk == sub_per_chunk - 1) || sb == nsub - 1;
     if (chunk_end && a.chunk_states)
-      store_stateT(st, a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride, w, pt);
+      write_state(a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
     __syncthreads();
   };
   int sb = 0;
   for (; sb + 3 <= nsub; sb += 3) {
-    step(std::integral_constant<int, 0>{}, sb);
-    step(std::integral_constant<int, 1>{}, sb + 1);
-    step(std::integral_constant<int, 2>{}, sb + 2);
+    step(std::integral_constant<int, 1>{}, sb);
+    step(std::integral_constant<int, 2>{}, sb + 1);
+    step(std::integral_constant<int, 0>{}, sb + 2);
   }
-  if (sb < nsub) step(std::integral_constant<int, 0>{}, sb);
-  if (sb + 1 < nsub) step(std::integral_constant<int, 1>{}, sb + 1);
-  if (a.h_last) store_stateT(st, a.h_last + ((size_t)b * a.H + h) * state_stride, w, pt);
+  if (sb < nsub) step(std::integral_constant<int, 1>{}, sb);
+  if (sb + 1 < nsub) step(std::integral_constant<int, 2>{}, sb + 1);
+  if (a.h_last) write_state(a.h_last + ((size_t)b * a.H + h) * state_stride);
 }
 
 // ---------------------------------------------------------------------------
@@ -398,7 +457,6 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const int lc = lane & 31, hf = lane >> 5;
   const int rt = w >> 1, pt = w & 1;
   const int partner = w ^ 2;
-  const float a2 = a.A[h] * kLog2e;
   const float dh = a.D ? a.D[h] : 0.f;
   const size_t state_stride = (size_t)kP * kN;
   const int p = pt * 32 + lc;  // headdim of this lane's output column
@@ -465,25 +523,42 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     }
   };
 
+  // Head-major delta and its block prefix sums: lane j holds step l0 + j.
+  const size_t row_bh = ((size_t)b * a.H + h) * a.Lp;
+  const rsrc_t rd = make_rsrc(a.dlT + row_bh, (uint32_t)a.Lp * 4u);
+  const rsrc_t rl = make_rsrc(a.lsT + row_bh, (uint32_t)a.Lp * 4u);
+  auto load_dls = [&](int l0, float& d, float& ls) {
+    d = __uint_as_float(buf_load_u32(rd, (uint32_t)(l0 + lane) * 4u));
+    ls = __uint_as_float(buf_load_u32(rl, (uint32_t)(l0 + lane) * 4u));
+  };
+
   u32x4 xr[2];
   BCRegs br, cr;
-  float d;
+  float d, ls;
   load_x(lbeg, xr);
   load_bc_rows(a, a.B, b, g, lbeg, br);
   load_bc_rows(a, a.C, b, g, lbeg, cr);
-  d = load_delta(a, b, h, lbeg);  // every wave loads it (no branch around loads); wave 0 uses it
+  load_dls(lbeg, d, ls);  // every wave loads them (no branch around loads); wave 0 uses them
   for (int l0 = lbeg; l0 < lend; l0 += kSub) {
     finish();  // the previous block (its xbuf entries were written before the last barrier)
     store_x(xr);
     store_bc_rows<true, true>(br, Bs, BT);
     store_bc_rows<true, false>(cr, Cs, nullptr);
-    if (w == 0) block_weights(d, a2, s_dl, s_ls, s_e, s_w, &s_decay);
+    if (w == 0) {
+      // e_i = exp(s_i), w_j = delta_j exp(s_last - s_j), decay = exp(s_last).
+      const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
+      s_dl[lane] = d;
+      s_ls[lane] = ls;
+      s_e[lane] = exp2_fast(ls);
+      s_w[lane] = d * exp2_fast(last - ls);
+      if (lane == 0) s_decay = exp2_fast(last);
+    }
     // Next block's loads in flight while this one is used (the block after
     // the chunk's last is read and ignored; past L reads zero).
     load_x(l0 + kSub, xr);
     load_bc_rows(a, a.B, b, g, l0 + kSub, br);
     load_bc_rows(a, a.C, b, g, l0 + kSub, cr);
-    d = load_delta(a, b, h, l0 + kSub);
+    load_dls(l0 + kSub, d, ls);
     __syncthreads();
 
     // C S^T over this wave's state rows for both row tiles, the state as hi + lo.
@@ -570,7 +645,9 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_
                            int64_t dstate, int64_t chunk) {
   (void)ngroups;
   const int64_t nchunks = (seqlen + chunk - 1) / chunk;
-  return align256((size_t)batch * nchunks * nheads * headdim * dstate * sizeof(float));
+  const int64_t lp = (seqlen + kSub - 1) / kSub * kSub;
+  return align256((size_t)batch * nchunks * nheads * headdim * dstate * sizeof(float)) +
+         2 * align256((size_t)batch * nheads * lp * sizeof(float));
 }
 
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
@@ -593,7 +670,16 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.G = (int)p.ngroups;
   a.Q = (int)p.chunk;
   a.nchunks = (int)((p.seqlen + p.chunk - 1) / p.chunk);
-  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch), dim3(kT), 0, stream, a);
+  const int nsub = (a.L + kSub - 1) / kSub;
+  a.Lp = nsub * kSub;
+  char* ws = static_cast<char*>(p.workspace);
+  ws += align256((size_t)a.batch * a.nchunks * a.H * kP * kN * sizeof(float));
+  a.dlT = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)a.batch * a.H * a.Lp * sizeof(float));
+  a.lsT = reinterpret_cast<float*>(ws);
+  hipLaunchKernelGGL(ssd_cumsum_kernel, dim3((unsigned)nsub, (unsigned)((a.H + 63) / 64), (unsigned)a.batch), dim3(256),
+                     0, stream, a);
+  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch), dim3(kTS), 0, stream, a);
   const dim3 grid((unsigned)a.nchunks, (unsigned)a.H, (unsigned)a.batch);
   if (a.z && a.D)
     hipLaunchKernelGGL((ssd_scan_kernel<true, true>), grid, dim3(kT), 0, stream, a);
