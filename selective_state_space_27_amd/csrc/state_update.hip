@@ -9,10 +9,12 @@
 // The step is a pure stream over the fp32 state (read once, written once), so
 // the kernel is laid out for HBM: 4 consecutive lanes own one channel's state
 // row, each lane a contiguous slice of SPL states, so one wave instruction
-// touches one contiguous span of the state (1 KB for N = 16).  The partial
-// readouts of the 4 lanes are combined with a fixed butterfly (bitwise
-// deterministic).  Decays use one hardware exp per state: the step is bound by
-// the state stream, not by arithmetic.
+// touches one contiguous span of the state (1 KB for N = 16).  Each thread
+// handles kRows channel rows 16 channels apart and issues every load of all
+// of them before any arithmetic, so a wave keeps kRows such spans in flight
+// (the step is bound by how many state bytes are in flight, not by
+// arithmetic).  The partial readouts of the 4 lanes are combined with a fixed
+// butterfly (bitwise deterministic).  Decays use one hardware exp per state.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,6 +22,8 @@ namespace mss {
 namespace {
 
 constexpr int kLanesPerChannel = 4;
+constexpr int kRows = 4;
+constexpr int kThreadsSU = 256;
 
 template <bool BF16>
 __device__ __forceinline__ float load_io(const void* p, size_t i) {
@@ -27,87 +31,123 @@ __device__ __forceinline__ float load_io(const void* p, size_t i) {
   else return static_cast<const float*>(p)[i];
 }
 
+// SPL consecutive B (or C) values from n0 of batch row b.
 template <bool BF16, int SPL>
-__global__ void __launch_bounds__(256) state_update_kernel(float* __restrict__ h, const void* __restrict__ u,
-                                                           const void* __restrict__ delta, const float* __restrict__ A,
-                                                           const void* __restrict__ B, const void* __restrict__ C,
-                                                           const float* __restrict__ D, const void* __restrict__ z,
-                                                           void* __restrict__ y, int batch, int dim, int N) {
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t bd = gid / kLanesPerChannel;       // (b, d) pair
-  const int q = (int)(gid % kLanesPerChannel);    // slice of the state row
-  const bool active = bd < (size_t)batch * dim;
-  const size_t bds = active ? bd : 0;
-  const int b = (int)(bds / dim);
-  const int d = (int)(bds % dim);
-  const int n0 = q * SPL;
-
-  const float uu = load_io<BF16>(u, bds);
-  const float dl = load_io<BF16>(delta, bds);
-  const float du = dl * uu;
-
-  float hv[SPL], av[SPL], bv[SPL], cv[SPL];
-  float* hrow = h + bds * N;
-  const float* arow = A + (size_t)d * N;
-  const bool full = (N == kLanesPerChannel * SPL);
-  if (full && SPL % 4 == 0) {
-#pragma unroll
-    for (int j = 0; j < SPL; j += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(hrow + n0 + j);
-      const float4 s = *reinterpret_cast<const float4*>(arow + n0 + j);
-      hv[j] = t.x; hv[j + 1] = t.y; hv[j + 2] = t.z; hv[j + 3] = t.w;
-      av[j] = s.x; av[j + 1] = s.y; av[j + 2] = s.z; av[j + 3] = s.w;
+__device__ __forceinline__ void load_vec(const void* p, size_t off, int n0, int N, bool fast, float* v) {
+  if constexpr (SPL == 4) {
+    if (fast) {
+      if constexpr (BF16) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + off);
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+      } else {
+        const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + off);
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+      }
+      return;
     }
-  } else {
+  }
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) v[j] = (n0 + j < N) ? load_io<BF16>(p, off + j) : 0.f;
+}
+
+template <bool BF16, int SPL>
+__global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restrict__ h, const void* __restrict__ u,
+                                                                 const void* __restrict__ delta,
+                                                                 const float* __restrict__ A,
+                                                                 const void* __restrict__ B,
+                                                                 const void* __restrict__ C,
+                                                                 const float* __restrict__ D,
+                                                                 const void* __restrict__ z, void* __restrict__ y,
+                                                                 int batch, int dim, int N) {
+  const size_t gid = (size_t)blockIdx.x * kThreadsSU + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int q = lane % kLanesPerChannel;  // slice of the state row
+  const int n0 = q * SPL;
+  // A wave covers 16 consecutive channels per row set and kRows row sets.
+  const size_t row0 = (gid >> 6) * (16 * kRows) + (size_t)(lane / kLanesPerChannel);
+  const size_t nrows = (size_t)batch * dim;
+  // Vector loads need whole aligned slices: N a multiple of 4 lanes * SPL.
+  const bool full = (N == kLanesPerChannel * SPL) && (SPL % 4 == 0);
+  const bool bc_fast = full && ((N * (BF16 ? 2 : 4)) % 8 == 0);
+
+  float hv[kRows][SPL], av[kRows][SPL], bv[kRows][SPL], cv[kRows][SPL];
+  float uu[kRows], dl[kRows], zz[kRows], dd[kRows];
+  bool act[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const size_t bd = row0 + (size_t)k * 16;
+    act[k] = bd < nrows;
+    const size_t bds = act[k] ? bd : 0;
+    const int b = (int)(bds / dim);
+    const int d = (int)(bds % dim);
+    const float* hrow = h + bds * N;
+    const float* arow = A + (size_t)d * N;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < SPL; j += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(hrow + n0 + j);
+        const float4 s = *reinterpret_cast<const float4*>(arow + n0 + j);
+        hv[k][j] = t.x; hv[k][j + 1] = t.y; hv[k][j + 2] = t.z; hv[k][j + 3] = t.w;
+        av[k][j] = s.x; av[k][j + 1] = s.y; av[k][j + 2] = s.z; av[k][j + 3] = s.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const bool ok = n0 + j < N;
+        hv[k][j] = ok ? hrow[n0 + j] : 0.f;
+        av[k][j] = ok ? arow[n0 + j] : 0.f;
+      }
+    }
+    load_vec<BF16, SPL>(B, (size_t)b * N + n0, n0, N, bc_fast, bv[k]);
+    load_vec<BF16, SPL>(C, (size_t)b * N + n0, n0, N, bc_fast, cv[k]);
+    uu[k] = load_io<BF16>(u, bds);
+    dl[k] = load_io<BF16>(delta, bds);
+    zz[k] = z != nullptr ? load_io<BF16>(z, bds) : 0.f;
+    dd[k] = D != nullptr ? D[d] : 0.f;
+  }
+
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const float du = dl[k] * uu[k];
+    float p = 0.f;
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
-      const bool ok = n0 + j < N;
-      hv[j] = ok ? hrow[n0 + j] : 0.f;
-      av[j] = ok ? arow[n0 + j] : 0.f;
+      const float dec = exp2_fast(dl[k] * av[k][j] * kLog2e);
+      hv[k][j] = __builtin_fmaf(dec, hv[k][j], du * bv[k][j]);
+      p = __builtin_fmaf(cv[k][j], hv[k][j], p);
     }
-  }
+    // Fixed-order butterfly over the 4 lanes of the channel.
+    p += __shfl_xor(p, 1, kLanesPerChannel);
+    p += __shfl_xor(p, 2, kLanesPerChannel);
+    if (!act[k]) continue;
+    const size_t bd = row0 + (size_t)k * 16;
+    float* hrow = h + bd * N;
+    if (full) {
 #pragma unroll
-  for (int j = 0; j < SPL; ++j) {
-    const bool ok = n0 + j < N;
-    bv[j] = ok ? load_io<BF16>(B, (size_t)b * N + n0 + j) : 0.f;
-    cv[j] = ok ? load_io<BF16>(C, (size_t)b * N + n0 + j) : 0.f;
-  }
-
-  float p = 0.f;
+      for (int j = 0; j < SPL; j += 4)
+        *reinterpret_cast<float4*>(hrow + n0 + j) =
+            make_float4(hv[k][j], hv[k][j + 1], hv[k][j + 2], hv[k][j + 3]);
+    } else {
 #pragma unroll
-  for (int j = 0; j < SPL; ++j) {
-    const float dec = exp2_fast(dl * av[j] * kLog2e);
-    hv[j] = __builtin_fmaf(dec, hv[j], du * bv[j]);
-    p = __builtin_fmaf(cv[j], hv[j], p);
-  }
-  // Fixed-order butterfly over the 4 lanes of the channel.
-  p += __shfl_xor(p, 1, kLanesPerChannel);
-  p += __shfl_xor(p, 2, kLanesPerChannel);
-
-  if (!active) return;
-  if (full && SPL % 4 == 0) {
-#pragma unroll
-    for (int j = 0; j < SPL; j += 4)
-      *reinterpret_cast<float4*>(hrow + n0 + j) = make_float4(hv[j], hv[j + 1], hv[j + 2], hv[j + 3]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < SPL; ++j)
-      if (n0 + j < N) hrow[n0 + j] = hv[j];
-  }
-  if (q == 0) {
-    float out = __builtin_fmaf(D != nullptr ? D[d] : 0.f, uu, p);
-    if (z != nullptr) out *= silu(load_io<BF16>(z, bds));
-    if constexpr (BF16) static_cast<uint16_t*>(y)[bds] = f32_to_bf16(out);
-    else static_cast<float*>(y)[bds] = out;
+      for (int j = 0; j < SPL; ++j)
+        if (n0 + j < N) hrow[n0 + j] = hv[k][j];
+    }
+    if (q == 0) {
+      float out = __builtin_fmaf(dd[k], uu[k], p);
+      if (z != nullptr) out *= silu(zz[k]);
+      if constexpr (BF16) static_cast<uint16_t*>(y)[bd] = f32_to_bf16(out);
+      else static_cast<float*>(y)[bd] = out;
+    }
   }
 }
 
 template <bool BF16, int SPL>
 hipError_t launch_typed(const UpdateParams& p, hipStream_t stream) {
-  const size_t threads = (size_t)p.batch * p.dim * kLanesPerChannel;
-  const unsigned grid = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((state_update_kernel<BF16, SPL>), dim3(grid), dim3(256), 0, stream, p.h, p.u, p.delta, p.A,
-                     p.B, p.C, p.D, p.z, p.y, (int)p.batch, (int)p.dim, (int)p.dstate);
+  const size_t rows = (size_t)p.batch * p.dim;
+  const size_t waves = (rows + 16 * kRows - 1) / (16 * kRows);
+  const unsigned grid = (unsigned)((waves * 64 + kThreadsSU - 1) / kThreadsSU);
+  hipLaunchKernelGGL((state_update_kernel<BF16, SPL>), dim3(grid), dim3(kThreadsSU), 0, stream, p.h, p.u, p.delta,
+                     p.A, p.B, p.C, p.D, p.z, p.y, (int)p.batch, (int)p.dim, (int)p.dstate);
   return hipGetLastError();
 }
 
