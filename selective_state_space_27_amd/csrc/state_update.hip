@@ -13,7 +13,8 @@
 // handles kRows channel rows 16 channels apart and issues every load of all
 // of them before any arithmetic, so a wave keeps kRows such spans in flight
 // (the step is bound by how many state bytes are in flight, not by
-// arithmetic).  The partial readouts of the 4 lanes are combined with a fixed
+// arithmetic; two rows measured best, more rows cost occupancy).  The new
+// state is written with non-temporal stores.  The partial readouts of the 4 lanes are combined with a fixed
 // butterfly (bitwise deterministic).  Decays use one hardware exp per state.
 #include "common.hpp"
 #include "launch.hpp"
@@ -22,7 +23,7 @@ namespace mss {
 namespace {
 
 constexpr int kLanesPerChannel = 4;
-constexpr int kRows = 4;
+constexpr int kRows = 2;
 constexpr int kThreadsSU = 256;
 
 template <bool BF16>
@@ -125,8 +126,8 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
     if (full) {
 #pragma unroll
       for (int j = 0; j < SPL; j += 4)
-        *reinterpret_cast<float4*>(hrow + n0 + j) =
-            make_float4(hv[k][j], hv[k][j + 1], hv[k][j + 2], hv[k][j + 3]);
+        __builtin_nontemporal_store(f32x4{hv[k][j], hv[k][j + 1], hv[k][j + 2], hv[k][j + 3]},
+                                    reinterpret_cast<f32x4*>(hrow + n0 + j));
     } else {
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
