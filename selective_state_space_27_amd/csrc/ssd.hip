@@ -205,7 +205,7 @@ __device__ __forceinline__ void store_bc_rows(const BCRegs& o, uint16_t (*rm)[kN
   }
 }
 
-// One 32x32 tile of S^T (rows n = nt*32.., columns p = pt*32..) from/to a
+// One 32x32 tile of S^T (rows n = nt*32.., columns p = pt*32..) from a
 // [P][N] fp32 state: each lane moves 4 consecutive n of its column at a time.
 __device__ __forceinline__ void load_stateT(f32x16& acc, const float* S, int nt, int pt) {
   const int lane = threadIdx.x & 63;
@@ -216,16 +216,6 @@ __device__ __forceinline__ void load_stateT(f32x16& acc, const float* S, int nt,
     const f32x4 v = S ? *reinterpret_cast<const f32x4*>(&S[(size_t)p * kN + n]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[4 * g4 + q] = v[q];
-  }
-}
-__device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt, int pt) {
-  const int lane = threadIdx.x & 63;
-  const int p = pt * 32 + (lane & 31);
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    const int n = nt * 32 + 8 * g4 + 4 * (lane >> 5);
-    *reinterpret_cast<f32x4*>(&S[(size_t)p * kN + n]) =
-        f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
   }
 }
 
@@ -243,7 +233,11 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xh[2][32 * kTRow];  // tsw layout: hi part of w o x, headdim rows
   __shared__ __attribute__((aligned(16))) uint16_t xl[2][32 * kTRow];  // lo part
   __shared__ __attribute__((aligned(16))) uint16_t BT[2][kN * kTRow];  // tsw layout, state rows
-  __shared__ __attribute__((aligned(16))) float xsum[4][16][64];        // k-half 1 partial states, for output
+  // The 32 x 128 state slice [p][n] of this headdim tile on its way out (rows
+  // padded to 132 floats: a b128 access of 16 lanes of one n and 16 rows p
+  // covers 16 distinct bank groups).
+  constexpr int kSRow = kN + 4;
+  __shared__ __attribute__((aligned(16))) float sout[32 * kSRow];
 
   // Both headdim tiles of a head on one XCD (workgroups are dealt to the XCDs
   // round-robin), so that each x row is fetched from HBM once.
@@ -318,18 +312,35 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   // The state is the sum of both k-halves' partials: k-half 0 starts from h0.
   f32x16 st;
   load_stateT(st, (a.h0 && kh == 0) ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, nt, pt);
-  // Writes the full state tile: k-half 1 hands its partial over through LDS.
+  // Writes the full state slice (rows pt*32.., all n) of a [P][N] state: k-half
+  // 1 puts its partial in LDS, k-half 0 adds its own, then the workgroup
+  // copies the 16 KB slice out with whole-row stores.
   auto write_state = [&](float* S) {
+    const int sp = lc;  // headdim row of this lane's accumulator column
     if (kh == 1) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xsum[nt][r][lane] = st[r];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int n = nt * 32 + 8 * g4 + 4 * hf;
+        *reinterpret_cast<f32x4*>(&sout[sp * kSRow + n]) =
+            f32x4{st[4 * g4], st[4 * g4 + 1], st[4 * g4 + 2], st[4 * g4 + 3]};
+      }
     }
     __syncthreads();
     if (kh == 0) {
-      f32x16 t = st;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] += xsum[nt][r][lane];
-      store_stateT(t, S, nt, pt);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int n = nt * 32 + 8 * g4 + 4 * hf;
+        f32x4* q = reinterpret_cast<f32x4*>(&sout[sp * kSRow + n]);
+        *q = *q + f32x4{st[4 * g4], st[4 * g4 + 1], st[4 * g4 + 2], st[4 * g4 + 3]};
+      }
+    }
+    __syncthreads();
+    float* dst = S + (size_t)pt * 32 * kN;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = (threadIdx.x + it * kTS) * 4;  // element of the 32 x 128 slice
+      const int row = e / kN, col = e % kN;
+      *reinterpret_cast<f32x4*>(&dst[e]) = *reinterpret_cast<const f32x4*>(&sout[row * kSRow + col]);
     }
     __syncthreads();
   };
