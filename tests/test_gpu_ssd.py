@@ -50,6 +50,10 @@ CASES = [
     (2, 300, 4, 2, 128, True, False, True),     # ragged L, two groups
     (1, 77, 3, 1, 64, False, True, False),      # shorter than two blocks, ragged
     (2, 512, 8, 1, 256, False, False, True),
+    (1, 1, 2, 1, 64, True, True, True),         # a single step
+    (1, 64, 3, 1, 64, False, False, True),      # exactly one block and one chunk
+    (2, 65, 16, 4, 256, True, False, False),    # one step past a block; 8-head pairs, four groups
+    (1, 200, 8, 8, 128, False, True, True),     # one head per group
 ]
 
 
