@@ -401,52 +401,54 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
 // the two S^T tiles (state rows 64*rt .. +64, headdim tile pt).  C S^T is
 // split by state rows: each wave forms it over its own two state tiles for
 // both row tiles and hands the other row tile's partial sum to its partner
-// wave (1-rt, pt) through LDS.
-template <int RT>
-__device__ __forceinline__ void diag_block(f32x16& yacc, const uint16_t (*Cs)[kN + kPadH],
-                                           const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_ls,
-                                           const float* s_dl, int pt) {
+// wave (1-rt, pt) through LDS, already scaled by exp(s_i).  Of the masked
+// decay block's three 32x32 tiles (0,0), (1,0), (1,1), the full tile (1,0) is
+// split by k-slice between the two row tiles, so that every wave forms three
+// slices; the rows-0 wave hands its slice's product over with the C S^T part.
+// Part of the masked decay block: the G^T tile (rows j of tile JT, columns i
+// of tile RT) = B C^T on the matrix cores, then k-slices [S0, S1) of
+// M = mask o G o exp(s_i - s_j) delta_j as the A operand (rows i, k = j),
+// times x (headdim tile pt) accumulated into yacc.
+template <int RT, int JT, int S0, int S1>
+__device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN + kPadH],
+                                          const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_ls,
+                                          const float* s_dl, int pt) {
   const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int i = RT * 32 + lc;
   const float lsi = s_ls[i];
+  f32x16 gacc = {};
 #pragma unroll
-  for (int jt = 0; jt <= RT; ++jt) {
-    // G^T tile (rows j of tile jt, columns i of tile RT) = B C^T.
-    f32x16 gacc = {};
-#pragma unroll
-    for (int kk = 0; kk < kN / 16; ++kk) {
-      const u32x4 bop = *reinterpret_cast<const u32x4*>(&Bs[jt * 32 + lc][kk * 16 + 8 * hf]);
-      const u32x4 cop = *reinterpret_cast<const u32x4*>(&Cs[RT * 32 + lc][kk * 16 + 8 * hf]);
-      gacc = mfma(bop, cop, gacc);
-    }
-    // M = mask o G o exp(s_i - s_j) delta_j as the A operand (rows i, k = j).
-    auto slice = [&](auto s_tag) {
-      constexpr int S = decltype(s_tag)::value;
-      float gv[8];
-      acc_kslice<S>(gacc, gv);
-      const int j0 = jt * 32 + 16 * S + 8 * hf;
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_ls[j0]);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_ls[j0 + 4]);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_dl[j0]);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_dl[j0 + 4]);
-      const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-      const float dj[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      float m[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float dec = exp2_fast(fminf(lsi - cj[t], 0.f));
-        const float v = gv[t] * dec * dj[t];
-        m[t] = (jt < RT || j0 + t <= i) ? v : 0.f;
-      }
-      u32x4 mh, ml;
-      split8(m, mh, ml);
-      const u32x4 xb = *reinterpret_cast<const u32x4*>(&xT[tsw(pt * 32 + lc, j0)]);
-      yacc = mfma(mh, xb, yacc);
-      yacc = mfma(ml, xb, yacc);
-    };
-    slice(std::integral_constant<int, 0>{});
-    slice(std::integral_constant<int, 1>{});
+  for (int kk = 0; kk < kN / 16; ++kk) {
+    const u32x4 bop = *reinterpret_cast<const u32x4*>(&Bs[JT * 32 + lc][kk * 16 + 8 * hf]);
+    const u32x4 cop = *reinterpret_cast<const u32x4*>(&Cs[RT * 32 + lc][kk * 16 + 8 * hf]);
+    gacc = mfma(bop, cop, gacc);
   }
+  auto slice = [&](auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
+    float gv[8];
+    acc_kslice<S>(gacc, gv);
+    const int j0 = JT * 32 + 16 * S + 8 * hf;
+    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_ls[j0]);
+    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_ls[j0 + 4]);
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_dl[j0]);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_dl[j0 + 4]);
+    const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float dj[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    float m[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float dec = exp2_fast(fminf(lsi - cj[t], 0.f));
+      const float v = gv[t] * dec * dj[t];
+      m[t] = (JT < RT || j0 + t <= i) ? v : 0.f;
+    }
+    u32x4 mh, ml;
+    split8(m, mh, ml);
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(&xT[tsw(pt * 32 + lc, j0)]);
+    yacc = mfma(mh, xb, yacc);
+    yacc = mfma(ml, xb, yacc);
+  };
+  if constexpr (S0 <= 0 && S1 > 0) slice(std::integral_constant<int, 0>{});
+  if constexpr (S0 <= 1 && S1 > 1) slice(std::integral_constant<int, 1>{});
 }
 
 template <bool HAS_Z, bool HAS_D>
@@ -499,12 +501,11 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   for (int t = 0; t < 2; ++t) load_stateT(st[t], sin, 2 * rt + t, pt);
 
   // Output of the previous block, finished at the start of the next one (the
-  // partner's partial C S^T is in xbuf then): accumulator, exp(s_i) and x of
-  // this lane's 16 rows.
+  // partner's part is in xbuf then): accumulator and x of this lane's 16 rows.
   const int lbeg = c * a.Q;
   const int lend = min(a.L, lbeg + a.Q);
   f32x16 yprev = {};
-  float eprev[16], xprev[16];
+  float xprev[16];
   int lprev = -1;  // first step of the block yprev belongs to
   // y and z rows of this batch entry and head: element (step l, headdim p) at
   // l*H*P + p; steps outside the chunk are dropped (store) or read as 0 (z).
@@ -526,7 +527,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int l = lprev + rt * 32 + acc_row(r, lane);
-      float v = __builtin_fmaf(eprev[r], xbuf[partner][r][lane], yprev[r]);
+      float v = xbuf[partner][r][lane] + yprev[r];
       if constexpr (HAS_D) v = __builtin_fmaf(dh, xprev[r], v);
       if constexpr (HAS_Z) v *= silu(zv[r]);
       const uint32_t yo = (l < lend) ? ((uint32_t)l * row + (uint32_t)p) * 4u : kOffNone;
@@ -593,20 +594,22 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       slice(std::integral_constant<int, 0>{});
       slice(std::integral_constant<int, 1>{});
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xbuf[w][r][lane] = yoth[r];
 
-    // Own tile: exp(s_i) (own part of C S^T) + diagonal block.
+    // exp(s_i) on both row tiles' C S^T parts, then the masked decay block.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = rt * 32 + acc_row(r, lane);
-      eprev[r] = s_e[i];
-      yown[r] *= eprev[r];
+      yown[r] *= s_e[rt * 32 + acc_row(r, lane)];
+      yoth[r] *= s_e[(1 - rt) * 32 + acc_row(r, lane)];
     }
-    if (rt == 0)
-      diag_block<0>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
-    else
-      diag_block<1>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
+    if (rt == 0) {
+      diag_part<0, 0, 0, 2>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
+      diag_part<1, 0, 0, 1>(yoth, Cs, Bs, xT, s_ls, s_dl, pt);
+    } else {
+      diag_part<1, 1, 0, 2>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
+      diag_part<1, 0, 1, 2>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xbuf[w][r][lane] = yoth[r];
     yprev = yown;
     if constexpr (HAS_D) {
 #pragma unroll
