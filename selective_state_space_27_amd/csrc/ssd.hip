@@ -266,32 +266,39 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const size_t row_bh = ((size_t)b * a.H + h) * a.Lp;
   typedef __attribute__((address_space(4))) const float scalar_float;  // uniform loads through the scalar cache
 
-  // Loads of one block, kept three blocks ahead.
-  struct Slot {
+  // Loads of one block: x and the delta rows (from HBM) four blocks ahead of
+  // their staging, B (shared by every head, so mostly an L2 hit) two ahead.
+  struct XSlot {
     uint32_t xr[2];
-    u32x4 br[2];
     u32x2 dl, ls;
     float last;
   };
-  auto load_slot = [&](int blk, Slot& sl) {
+  struct BSlot {
+    u32x4 br[2];
+  };
+  auto load_x = [&](int blk, XSlot& sl) {
     const int l0 = blk * kSub;
     const uint32_t left = (uint32_t)max(a.L - l0, 0), left_p = (uint32_t)max(a.Lp - l0, 0);
     const rsrc_t rx = make_rsrc(a.x + ((size_t)b * a.L + l0) * a.H * kP, left * x_row);
-    const rsrc_t rb = make_rsrc(a.B + ((size_t)b * a.L + l0) * a.G * kN, left * b_row);
     const rsrc_t rd = make_rsrc(a.dlT + row_bh + l0, left_p * 4u);
     const rsrc_t rl = make_rsrc(a.lsT + row_bh + l0, left_p * 4u);
     sl.xr[0] = buf_load_u32(rx, xo0);
     sl.xr[1] = buf_load_u32(rx, xo1);
-    sl.br[0] = buf_load_u32x4(rb, bo0);
-    sl.br[1] = buf_load_u32x4(rb, bo1);
     sl.dl = buf_load_u32x2(rd, dlo);
     sl.ls = buf_load_u32x2(rl, dlo);
     // Prefix sum at the block's last step (blocks past the end read the last block's).
     sl.last = ((scalar_float*)(a.lsT + row_bh))[min(l0, a.Lp - kSub) + kSub - 1];
   };
+  auto load_b = [&](int blk, BSlot& sl) {
+    const int l0 = blk * kSub;
+    const uint32_t left = (uint32_t)max(a.L - l0, 0);
+    const rsrc_t rb = make_rsrc(a.B + ((size_t)b * a.L + l0) * a.G * kN, left * b_row);
+    sl.br[0] = buf_load_u32x4(rb, bo0);
+    sl.br[1] = buf_load_u32x4(rb, bo1);
+  };
   // w o x for steps (jx, jx+1) of headdim rows pq*2, pq*2+1 as hi/lo pairs,
   // w_j = delta_j exp(s_last - s_j); B transposed to state rows.
-  auto stage = [&](const Slot& sl, int buf) {
+  auto stage = [&](const XSlot& sl, const BSlot& sb_, int buf) {
     const float w0 = __uint_as_float(sl.dl[0]) * exp2_fast(sl.last - __uint_as_float(sl.ls[0]));
     const float w1 = __uint_as_float(sl.dl[1]) * exp2_fast(sl.last - __uint_as_float(sl.ls[1]));
     uint32_t hi, lo;
@@ -303,7 +310,7 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     *reinterpret_cast<uint32_t*>(&xl[buf][tsw(pq * 2 + 1, jx)]) = lo;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t v0 = sl.br[0][k], v1 = sl.br[1][k];
+      const uint32_t v0 = sb_.br[0][k], v1 = sb_.br[1][k];
       *reinterpret_cast<uint32_t*>(&BT[buf][tsw(ng * 8 + 2 * k, jx)]) = (v0 & 0xffffu) | (v1 << 16);
       *reinterpret_cast<uint32_t*>(&BT[buf][tsw(ng * 8 + 2 * k + 1, jx)]) = (v0 >> 16) | (v1 & 0xffff0000u);
     }
@@ -350,18 +357,23 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   // Software pipeline: iteration sb runs block sb's products from staging
   // buffer sb&1 while it stages block sb+1 into the other buffer (whose last
   // readers finished before the previous barrier), one barrier per block.
-  // Ring slot (sb+1)%3 holds block sb+1, loaded three iterations earlier.
-  Slot ring[3];
-  load_slot(0, ring[0]);
-  load_slot(1, ring[1]);
-  load_slot(2, ring[2]);
-  stage(ring[0], 0);
-  float decay = exp2_fast(ring[0].last);  // exp(s_last) of the block being multiplied
-  load_slot(3, ring[0]);
+  // Block sb+1 sits in x slot (sb+1)%4 and B slot (sb+1)%2 (loop unrolled by
+  // four so the slots are compile-time constants).
+  XSlot xring[4];
+  BSlot bring[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) load_x(k, xring[k]);
+  load_b(0, bring[0]);
+  load_b(1, bring[1]);
+  stage(xring[0], bring[0], 0);
+  float decay = exp2_fast(xring[0].last);  // exp(s_last) of the block being multiplied
+  load_x(4, xring[0]);
+  load_b(2, bring[0]);
   __syncthreads();
 
-  auto step = [&](auto slot_tag, int sb) {
-    constexpr int S1 = decltype(slot_tag)::value;  // (sb + 1) % 3
+  auto step = [&](auto x_tag, auto b_tag, int sb) {
+    constexpr int SX = decltype(x_tag)::value;  // (sb + 1) % 4
+    constexpr int SB = decltype(b_tag)::value;  // (sb + 1) % 2
     const int c = sb / sub_per_chunk;
     const int buf = sb & 1;
     if (sb % sub_per_chunk == 0)  // state entering chunk c
@@ -376,22 +388,29 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
       st = mfma(av, bh, st);
       st = mfma(av, bl, st);
     }
-    stage(ring[S1], buf ^ 1);
-    decay = exp2_fast(ring[S1].last);
-    load_slot(sb + 4, ring[S1]);
+    stage(xring[SX], bring[SB], buf ^ 1);
+    decay = exp2_fast(xring[SX].last);
+    load_x(sb + 5, xring[SX]);
+    load_b(sb + 3, bring[SB]);
     const bool chunk_end = (sb % sub_per_chunk == sub_per_chunk - 1) || sb == nsub - 1;
     if (chunk_end && a.chunk_states)
       write_state(a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
     __syncthreads();
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   int sb = 0;
-  for (; sb + 3 <= nsub; sb += 3) {
-    step(std::integral_constant<int, 1>{}, sb);
-    step(std::integral_constant<int, 2>{}, sb + 1);
-    step(std::integral_constant<int, 0>{}, sb + 2);
+  for (; sb + 4 <= nsub; sb += 4) {
+    step(I1{}, I1{}, sb);
+    step(I2{}, I0{}, sb + 1);
+    step(I3{}, I1{}, sb + 2);
+    step(I0{}, I0{}, sb + 3);
   }
-  if (sb < nsub) step(std::integral_constant<int, 1>{}, sb);
-  if (sb + 1 < nsub) step(std::integral_constant<int, 2>{}, sb + 1);
+  if (sb < nsub) step(I1{}, I1{}, sb);
+  if (sb + 1 < nsub) step(I2{}, I0{}, sb + 1);
+  if (sb + 2 < nsub) step(I3{}, I1{}, sb + 2);
   if (a.h_last) write_state(a.h_last + ((size_t)b * a.H + h) * state_stride);
 }
 
