@@ -427,14 +427,19 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
 // Part of the masked decay block: the G^T tile (rows j of tile JT, columns i
 // of tile RT) = B C^T on the matrix cores, then k-slices [S0, S1) of
 // M = mask o G o exp(s_i - s_j) delta_j as the A operand (rows i, k = j),
-// times x (headdim tile pt) accumulated into yacc.
-template <int RT, int JT, int S0, int S1>
+// times x (headdim tile pt) accumulated into yacc.  Masked elements (j > i)
+// are dropped by a select, so whatever their exponent gives is harmless.
+// FACTORED: the block's prefix sums fall (A <= 0) by less than 200 (log2
+// units), and exp(s_i - s_j) delta_j is taken as ei[i] * fd[j] with
+// ei = exp2(ls - mid), fd = delta exp2(mid - ls) (each factor within 2^100,
+// the unmasked products at most delta); otherwise one exp2 per element.
+template <int RT, int JT, int S0, int S1, bool FACTORED>
 __device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN + kPadH],
                                           const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_ls,
-                                          const float* s_dl, int pt) {
+                                          const float* s_dl, const float* s_ei, const float* s_fd, int pt) {
   const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int i = RT * 32 + lc;
-  const float lsi = s_ls[i];
+  const float rowv = FACTORED ? s_ei[i] : s_ls[i];  // ei[i], or ls_i
   f32x16 gacc = {};
 #pragma unroll
   for (int kk = 0; kk < kN / 16; ++kk) {
@@ -447,18 +452,29 @@ __device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN 
     float gv[8];
     acc_kslice<S>(gacc, gv);
     const int j0 = JT * 32 + 16 * S + 8 * hf;
-    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_ls[j0]);
-    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_ls[j0 + 4]);
-    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_dl[j0]);
-    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_dl[j0 + 4]);
-    const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    const float dj[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
     float m[8];
+    if constexpr (FACTORED) {
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(&s_fd[j0]);
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(&s_fd[j0 + 4]);
+      const float fj[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float dec = exp2_fast(fminf(lsi - cj[t], 0.f));
-      const float v = gv[t] * dec * dj[t];
-      m[t] = (JT < RT || j0 + t <= i) ? v : 0.f;
+      for (int t = 0; t < 8; ++t) {
+        const float v = gv[t] * rowv * fj[t];
+        m[t] = (JT < RT || j0 + t <= i) ? v : 0.f;
+      }
+    } else {
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_ls[j0]);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(&s_ls[j0 + 4]);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_dl[j0]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_dl[j0 + 4]);
+      const float cj[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      const float dj[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float dec = exp2_fast(rowv - cj[t]);
+        const float v = gv[t] * dec * dj[t];
+        m[t] = (JT < RT || j0 + t <= i) ? v : 0.f;
+      }
     }
     u32x4 mh, ml;
     split8(m, mh, ml);
@@ -481,7 +497,10 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ __attribute__((aligned(16))) float s_ls[kSub];
   __shared__ __attribute__((aligned(16))) float s_e[kSub];
   __shared__ __attribute__((aligned(16))) float s_w[kSub];
+  __shared__ __attribute__((aligned(16))) float s_ei[kSub];  // exp2(ls - mid) (factored decay block)
+  __shared__ __attribute__((aligned(16))) float s_fd[kSub];  // delta exp2(mid - ls)
   __shared__ float s_decay;
+  __shared__ int s_factored;
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (a.H / a.G);
@@ -583,6 +602,13 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       s_e[lane] = exp2_fast(ls);
       s_w[lane] = d * exp2_fast(last - ls);
       if (lane == 0) s_decay = exp2_fast(last);
+      // Factors of exp(s_i - s_j) about the block's middle prefix sum, used
+      // when the prefix sums fall (A <= 0) by less than 200 over the block.
+      const float first = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 0));
+      const float mid = 0.5f * (first + last);
+      s_ei[lane] = exp2_fast(ls - mid);
+      s_fd[lane] = d * exp2_fast(mid - ls);
+      if (lane == 0) s_factored = (first - last >= 0.f && first - last < 200.f) ? 1 : 0;
     }
     // Next block's loads in flight while this one is used (the block after
     // the chunk's last is read and ignored; past L reads zero).
@@ -620,13 +646,20 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       yown[r] *= s_e[rt * 32 + acc_row(r, lane)];
       yoth[r] *= s_e[(1 - rt) * 32 + acc_row(r, lane)];
     }
-    if (rt == 0) {
-      diag_part<0, 0, 0, 2>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
-      diag_part<1, 0, 0, 1>(yoth, Cs, Bs, xT, s_ls, s_dl, pt);
-    } else {
-      diag_part<1, 1, 0, 2>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
-      diag_part<1, 0, 1, 2>(yown, Cs, Bs, xT, s_ls, s_dl, pt);
-    }
+    auto diag = [&](auto factored_tag) {
+      constexpr bool F = decltype(factored_tag)::value;
+      if (rt == 0) {
+        diag_part<0, 0, 0, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
+        diag_part<1, 0, 0, 1, F>(yoth, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
+      } else {
+        diag_part<1, 1, 0, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
+        diag_part<1, 0, 1, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
+      }
+    };
+    if (__builtin_amdgcn_readfirstlane(s_factored))
+      diag(std::true_type{});
+    else
+      diag(std::false_type{});
 #pragma unroll
     for (int r = 0; r < 16; ++r) xbuf[w][r][lane] = yoth[r];
     yprev = yown;
