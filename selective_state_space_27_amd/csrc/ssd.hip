@@ -610,11 +610,6 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       s_fd[lane] = d * exp2_fast(mid - ls);
       if (lane == 0) s_factored = (first - last >= 0.f && first - last < 200.f) ? 1 : 0;
     }
-    // Next block's loads in flight while this one is used (the block after
-    // the chunk's last is read and ignored; past L reads zero).
-    load_x(l0 + kSub, xr);
-    load_bc_rows(a, a.B, b, g, l0 + kSub, br);
-    load_bc_rows(a, a.C, b, g, l0 + kSub, cr);
     load_dls(l0 + kSub, d, ls);
     __syncthreads();
 
@@ -662,6 +657,12 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       diag(std::false_type{});
 #pragma unroll
     for (int r = 0; r < 16; ++r) xbuf[w][r][lane] = yoth[r];
+    // The next block's loads, issued once the products that need the most
+    // registers are done (the block after the chunk's last is read and
+    // ignored; past L reads zero).
+    load_x(l0 + kSub, xr);
+    load_bc_rows(a, a.B, b, g, l0 + kSub, br);
+    load_bc_rows(a, a.C, b, g, l0 + kSub, cr);
     yprev = yown;
     if constexpr (HAS_D) {
 #pragma unroll
