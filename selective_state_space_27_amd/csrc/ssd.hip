@@ -13,13 +13,17 @@
 //   S_out = exp(s_last) S_in + sum_j exp(s_last - s_j) delta_j x_j B_j^T
 // which is the recurrence above summed over the block (exact up to rounding).
 //
-// Two kernels, both on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+// Three kernels; the two big ones on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation:
+//   ssd_cumsum_kernel: delta transposed to head-major rows and its prefix
+//     sums inside every 64-step block, scaled by A log2(e), into the
+//     workspace (the decay factors of both other kernels come from these).
 //   ssd_state_kernel: one workgroup per (batch, head, 32-wide headdim tile),
-//     one 32 x 32 tile of S^T per wave kept in MFMA accumulators, walks the
-//     sequence in 64-step blocks (the next block's loads in flight while the
-//     current one is used) and writes the state entering every chunk to the
-//     workspace (and, on request, the state after every chunk and the final
-//     state).
+//     eight waves (four 32-row tiles of S^T, each over half of every block's
+//     steps, the halves added where a state is written), walks the sequence
+//     in 64-step blocks with the next block staged while the current one is
+//     multiplied, and writes the state entering every chunk to the workspace
+//     (and, on request, the state after every chunk and the final state).
 //   ssd_scan_kernel: one workgroup per (batch, chunk, head) starts from the
 //     state entering its chunk and walks the chunk in 64-step blocks.  Each
 //     wave owns one 32 x 32 output tile and holds S^T for its headdim tile in
