@@ -146,7 +146,7 @@ def bench_scan(args, torch, mss, I, cfg):
                             "power chain (S4D-real structure detected on device)"},
     }
     files = ["scan.hip", "common.hpp"]
-    kernel = "scan_kernel (+ bc_transpose_kernel, s4d_check_kernel in the same timed call)"
+    kernel = "scan_kernel (+ bc_transpose_kernel in the same timed call)"
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

@@ -564,14 +564,30 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
 // B, C [batch, N, L] (bf16 or fp32) -> fp32 workspace in the bc_index layout,
 // zero for n >= N, l >= L and unused row positions.  One thread per float.
-// The same launch clears the carry flags, the error word and the ticket.
+// The same launch clears the carry flags, the error word and the ticket, and
+// its first waves check the decay structure: s4d_ok[blk] = 1 when
+// A[d,n] == (n+1)*A[d,0] (exactly, in fp32) for every channel d of the
+// 64-channel block blk (wave blk checks block blk).
 template <bool BF16, int SPW>
-__global__ void bc_transpose_kernel(const void* __restrict__ B, const void* __restrict__ C,
-                                    float* __restrict__ out, int batch, int N, int L, int ntiles,
-                                    int* __restrict__ flags, int nflags) {
+__global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restrict__ B, const void* __restrict__ C,
+                                                           float* __restrict__ out, int batch, int N, int L,
+                                                           int ntiles, int* __restrict__ flags, int nflags,
+                                                           const float* __restrict__ A, int* __restrict__ ok_out,
+                                                           int dim, int nblocks) {
   using S = BCShape<SPW>;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (size_t i = idx; i < (size_t)nflags; i += (size_t)gridDim.x * blockDim.x) flags[i] = 0;
+  const size_t wave = idx / kLanes;  // whole waves: the block size is a multiple of 64
+  if (wave < (size_t)nblocks) {
+    const int c = (int)wave * kLanes + (int)(idx % kLanes);
+    bool ok = true;
+    if (c < dim) {
+      const float a0 = A[(size_t)c * N];
+      for (int n = 1; n < N; ++n) ok = ok && (A[(size_t)c * N + n] == (float)(n + 1) * a0);
+    }
+    const bool all = __all(ok);
+    if (idx % kLanes == 0) ok_out[wave] = all ? 1 : 0;
+  }
   const size_t total = (size_t)batch * kWaves * ntiles * S::kPerTile;
   if (idx >= total) return;
   const int blk = (int)(idx % 4);
@@ -597,19 +613,6 @@ __global__ void bc_transpose_kernel(const void* __restrict__ B, const void* __re
     }
   }
   out[idx] = val;
-}
-
-// s4d_ok[blk] = 1 when A[d,n] == (n+1)*A[d,0] (exactly, in fp32) for every
-// channel d of the 64-channel block.  One wave per block.
-__global__ void s4d_check_kernel(const float* __restrict__ A, int* __restrict__ ok_out, int dim, int N) {
-  const int c = blockIdx.x * kLanes + threadIdx.x;
-  bool ok = true;
-  if (c < dim) {
-    const float a0 = A[(size_t)c * N];
-    for (int n = 1; n < N; ++n) ok = ok && (A[(size_t)c * N + n] == (float)(n + 1) * a0);
-  }
-  const bool all = __all(ok);
-  if (threadIdx.x == 0) ok_out[blockIdx.x] = all ? 1 : 0;
 }
 
 int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : 8; }
@@ -641,13 +644,13 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   const int64_t nstreams = p.batch * nblocks;
 
   {
-    const unsigned grid = (unsigned)((nbc + 255) / 256);
+    // Enough threads for every B/C float and one wave per channel block.
+    const size_t threads = std::max<size_t>(nbc, (size_t)nblocks * kLanes);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(grid), dim3(256), 0, stream, p.B, p.C, bc,
                        (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles, flags,
-                       (int)flag_ints(p.batch, p.dim));
+                       (int)flag_ints(p.batch, p.dim), p.A, ok, (int)p.dim, nblocks);
   }
-  hipLaunchKernelGGL(s4d_check_kernel, dim3(nblocks), dim3(kLanes), 0, stream, p.A, ok, (int)p.dim,
-                     (int)p.dstate);
 
   ScanArgs a;
   a.u = p.u;
