@@ -17,7 +17,15 @@ Other workloads (for the record in the design doc, not the headline):
   scan_130m    b8 x d1536 x N16 x L2048, fp32 I/O
   decode_2p8b  b256 x d5120 x N16 one-token steps, bf16 I/O; one step = 1000 tokens
   ssd_2p8b     b2 x L16384 x H80 x P64 x N128, chunk 256 (Mamba-2 SSD)
+  scan_m2shape the Mamba-1 scan on ssd_2p8b's shape: b2 x d5120 (80 heads of
+               64 channels) x N128 x L16384, A and delta shared within a head
   copy         a plain 1 GiB device copy (calibrates the HBM byte counters)
+
+--seqlen L and --batch B (scan and SSD workloads) time the same workload at
+another sequence length or batch: the preset's inputs are drawn as usual and
+repeated (or cut) along L or the batch on the device.  Such lines carry no
+traffic figure (the counters were taken at the preset shape) and no CPU
+baseline.
 """
 from __future__ import annotations
 
@@ -42,7 +50,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scan_2p8b",
-                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "copy"])
+                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "scan_m2shape", "copy"])
+    ap.add_argument("--seqlen", type=int, default=0,
+                    help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="scan/SSD workloads: batch (inputs repeated along the batch); 0 = the preset's")
     ap.add_argument("--force-general-decay", action="store_true",
                     help="scan: per-state exp decay even where A has the S4D-real structure")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -120,11 +132,23 @@ def cpu_threads():
     return max(1, min(16, n))
 
 
+def along_l(torch, t, L, dim):
+    """Device tensor repeated (or cut) to length L along dimension `dim`."""
+    reps = [1] * t.dim()
+    reps[dim] = -(-L // t.shape[dim])
+    return t.repeat(*reps).narrow(dim, 0, L).contiguous()
+
+
 def bench_scan(args, torch, mss, I, cfg):
     x = I.scan_inputs(cfg)
     g = {k: to_dev(torch, x[k]) for k in ("u", "delta", "A", "B", "C", "D", "z")}
     io_dt = g["u"].dtype
     b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    if args.seqlen or args.batch:
+        L, b = args.seqlen or L, args.batch or b
+        for k in ("u", "delta", "B", "C", "z"):
+            g[k] = along_l(torch, along_l(torch, g[k], L, 2), b, 0)
+        torch.cuda.synchronize()
     ws = torch.empty(mss.selective_scan_workspace_size(b, d, n, L, io_dt), dtype=torch.uint8, device="cuda:0")
     out = torch.empty_like(g["u"])
 
@@ -137,18 +161,23 @@ def bench_scan(args, torch, mss, I, cfg):
     es = 2 if cfg.io == "bf16" else 4
     nbytes = scan_bytes(b, d, n, L, es)
     res = {
-        "metric": METRIC, "value": updates / (ms * 1e-3), "unit": "state updates/s", "ms_per_step": ms,
+        "metric": METRIC if cfg is I.SCAN_2P8B else "state updates/s (B*L*D*N), selective scan",
+        "value": updates / (ms * 1e-3), "unit": "state updates/s", "ms_per_step": ms,
         "dtype": "f32",
         "config": {"workload": f"{cfg.name}: selective scan b={b} d_inner={d} d_state={n} L={L}, "
                                f"{cfg.io} u/delta/B/C/z/y, fp32 A/D/state",
                    "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io_dtype": cfg.io,
                    "decay": "per-state exp (forced)" if args.force_general_decay else
+                            "one decay per (d, l) for all states (A equal over n, detected on device)"
+                            if cfg.a_form == "head" else
                             "power chain (S4D-real structure detected on device)"},
     }
+    if args.seqlen or args.batch:
+        res["config"]["inputs"] = f"the preset's b={cfg.batch} L={cfg.seqlen} draw repeated or cut along b and L"
     files = ["scan.hip", "common.hpp"]
     kernel = "scan_kernel (+ bc_transpose_kernel in the same timed call)"
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (args.seqlen or args.batch):
         import oracle
         rows = list(range(min(2, b)))          # bounded sample: the first two batch rows, every channel, full L
         f64 = lambda k: I.to_f64(x[k][rows], cfg.io)
@@ -210,6 +239,11 @@ def bench_ssd(args, torch, mss, I):
     x = I.ssd_inputs(cfg)
     g = {k: to_dev(torch, x[k]) for k in ("x", "delta", "A", "B", "C")}
     b, L, H, P, G, N, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.chunk
+    if args.seqlen or args.batch:
+        L, b = args.seqlen or L, args.batch or b
+        for k in ("x", "delta", "B", "C"):
+            g[k] = along_l(torch, along_l(torch, g[k], L, 1), b, 0)
+        torch.cuda.synchronize()
     ws = torch.empty(mss.ssd_workspace_size(b, L, H, P, G, N, Q), dtype=torch.uint8, device="cuda:0")
     out = torch.empty((b, L, H, P), dtype=torch.float32, device="cuda:0")
 
@@ -223,8 +257,10 @@ def bench_ssd(args, torch, mss, I):
            "config": {"workload": f"{cfg.name}: SSD b={b} L={L} H={H} P={P} G={G} N={N} chunk={Q}, bf16 x/B/C, "
                                   "fp32 delta/y/states", "batch": b, "seqlen": L, "nheads": H, "headdim": P,
                       "d_state": N, "chunk": Q}}
+    if args.seqlen or args.batch:
+        res["config"]["inputs"] = f"the preset's b={cfg.batch} L={cfg.seqlen} draw repeated or cut along b and L"
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (args.seqlen or args.batch):
         import oracle
         Ls = 2048
         th = cpu_threads()
@@ -254,6 +290,10 @@ def main():
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
               "the hot path shards over batch and channels with no communication, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
+    if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and args.workload in ("decode_2p8b", "copy")):
+        print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
+              file=sys.stderr)
+        sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -270,11 +310,13 @@ def main():
         res, nbytes, launch_ms, kernel, files, cpu = bench_decode(args, torch, mss, I)
     elif args.workload == "ssd_2p8b":
         res, nbytes, launch_ms, kernel, files, cpu = bench_ssd(args, torch, mss, I)
+    elif args.workload == "scan_m2shape":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_M2)
     else:
         res, nbytes, launch_ms, kernel, files, cpu = bench_copy(args, torch)
 
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.workload, files) if files else None
+    traffic = recorded_traffic(args.workload, files) if files and not (args.seqlen or args.batch) else None
     line = {
         "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",

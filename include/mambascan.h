@@ -58,9 +58,11 @@ typedef enum { MSS_FP32 = 0, MSS_BF16 = 1 } mss_dtype;
 
 /* Force the per-state exp(delta*A[d,n]) decay path of the selective scan.
  * Without this flag the scan checks on the device, per block of 64 channels,
- * whether A[d,n] == (n+1)*A[d,0] holds exactly for every channel in the block
- * (the S4D-real structure); where it does, it computes the same decays as
- * r^(n+1) with r = exp(delta*A[d,0]) (equal in exact arithmetic).          */
+ * whether A[d,n] == A[d,0] holds exactly for every channel in the block (A
+ * constant over the states, the Mamba-2 form), else whether
+ * A[d,n] == (n+1)*A[d,0] does (the S4D-real structure); where one holds it
+ * computes the same decays from r = exp(delta*A[d,0]) alone, as r or as
+ * r^(n+1) (equal in exact arithmetic).                                     */
 #define MSS_FLAG_DECAY_GENERAL 0x1u
 
 /* ------------------------------------------------------------------------ */
@@ -86,7 +88,8 @@ typedef enum { MSS_FP32 = 0, MSS_BF16 = 1 } mss_dtype;
 /*   A              : [dim, dstate] fp32;  D : [dim] fp32 (NULL = no skip)  */
 /*   h0, h_last     : [batch, dim, dstate] fp32 (each may be NULL)          */
 /* delta is used as given (no softplus or bias inside).                     */
-/* Supported: 1 <= dstate <= 64; seqlen <= 2^31-1; dim*seqlen < 2^31.        */
+/* Supported: 1 <= dstate <= 128; seqlen < 2^24; dim*seqlen < 2^31;        */
+/* batch <= 65535.                                                          */
 /* Outputs y and h_last must not overlap any input or each other.           */
 /* ------------------------------------------------------------------------ */
 mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B,

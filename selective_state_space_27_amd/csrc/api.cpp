@@ -77,7 +77,7 @@ static mss_status scan_check_shape(int64_t batch, int64_t dim, int64_t dstate, i
   if (batch > 65535 || seqlen >= (1LL << 24) || dim * seqlen > kMaxIndex || dim * dstate > kMaxIndex ||
       batch * dim > kMaxIndex)
     return MSS_ERR_SHAPE;
-  if (dstate > 64) return MSS_ERR_UNSUPPORTED;
+  if (dstate > 128) return MSS_ERR_UNSUPPORTED;
   return MSS_OK;
 }
 

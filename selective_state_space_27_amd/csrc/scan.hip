@@ -28,11 +28,14 @@
 // draining the prefetch.  Four waves per SIMD give the issue slack a single
 // wave (one VALU instruction per 8 cycles at most) does not have.
 //
-// Decay.  Where every channel of the block has A[d,n] == (n+1)*A[d,0] (the
-// S4D-real structure, checked on the device), the prologue computes one
-// r = exp2(delta*A[d,0]*log2 e) per (d,l) and the start power r^(g*SPW+1) of
-// each wave's states; the waves continue the power chain with multiplies.
-// Elsewhere each wave evaluates exp2(delta*A[d,n]*log2 e) per state.
+// Decay, chosen per block of 64 channels from A (checked on the device):
+//   S4D-real (A[d,n] == (n+1)*A[d,0] in every channel): the prologue computes
+//     one r = exp2(delta*A[d,0]*log2 e) per (d,l) and the start power
+//     r^(g*SPW+1) of each wave's states; the waves continue the power chain
+//     with multiplies.
+//   scalar (A[d,n] == A[d,0] in every channel, the Mamba-2 form of A): every
+//     state decays by the same r, computed once per (d,l) by the prologue.
+//   general: each wave evaluates exp2(delta*A[d,n]*log2 e) per state.
 #include <algorithm>
 #include <type_traits>
 
@@ -61,7 +64,7 @@ struct ScanArgs {
   void* y;
   float* h_last;
   const float* bc;     // B and C per wave and tile, fp32, in the layout bc_index() describes
-  const int* s4d_ok;   // [nblocks]
+  const int* decay_mode;  // [nblocks]: kDecayGeneral, kDecayS4D or kDecayScalar
   float* carry;        // [streams][8 waves][SPW][64 lanes] state handed between workgroups
   int* flags;          // [streams] carry ready; [streams] = spin-limit error; [streams + 1] = ticket
   int* ticket;
@@ -71,6 +74,11 @@ struct ScanArgs {
 
 constexpr int kMaxSpins = 1 << 22;
 
+// Decay modes of a 64-channel block.
+constexpr int kDecayGeneral = 0;  // exp2(delta*A[d,n]*log2 e) per state
+constexpr int kDecayS4D = 1;      // A[d,n] == (n+1)*A[d,0]: powers of one r per (d,l)
+constexpr int kDecayScalar = 2;   // A[d,n] == A[d,0]: one r per (d,l) for every state
+
 // B/C values a wave needs per 4-step block: 4 steps x (SPW B values, SPW C
 // values) = 8*SPW, spread over NV VGPRs of 16 row positions each.
 template <int SPW>
@@ -78,12 +86,17 @@ struct BCShape {
   static constexpr int kPerBlk = 8 * SPW;
   static constexpr int kNV = kPerBlk <= 16 ? 1 : kPerBlk / 16;
   static constexpr int kPerTile = kNV * 16 * kBlk;  // floats per (batch, wave, tile)
+  static constexpr bool kBlockLayout = kNV >= 8;    // see bc_index
 };
 
-// Workspace B/C layout: [batch][wave g][tile][v][row position p][blk].  Lane
-// with row position p loads the float4 over blk, so for block `blk` value i =
-// v*16 + p (step i / (2*SPW), quantity i % (2*SPW): B of states g*SPW.., then
-// C) sits in component blk of VGPR v at row position p.
+// Workspace B/C layout, per [batch][wave g][tile]: value i = v*16 + p of
+// block blk (step i / (2*SPW), quantity i % (2*SPW): B of states g*SPW..,
+// then C) belongs to row position p, and
+//   tile layout  [v][p][blk]:        lane p loads the float4 over blk, so the
+//                                    value sits in component blk of VGPR v;
+//   block layout [blk][v/4][p][v%4]: lane p loads, per block, the float4 over
+//                                    v%4, so it sits in component v%4 of
+//                                    VGPR v/4 of that block's load.
 template <int SPW>
 __device__ __forceinline__ size_t bc_index(int b, int g, int tile, int ntiles, int v, int p, int blk) {
   using S = BCShape<SPW>;
@@ -248,7 +261,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     const bool cok = c < a.dim;
     const int c_io = cb * kLanes + io_ch;  // channel of this thread's I/O items
     const bool iok = c_io < a.dim;
-    const bool s4d = !a.force_general && a.s4d_ok[cb] != 0;
+    const int mode = a.force_general ? kDecayGeneral : a.decay_mode[cb];
 
     // Descriptors over this block's rows [b, cb*64 .. +nch, 0..L).
     const int nch = min(kLanes, a.dim - cb * kLanes);
@@ -275,11 +288,19 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
     // Initial state: the carry published by the workgroup that ran the first
     // part of this stream, else h0 (or zero).
+    //
+    // The hand-off uses relaxed agent-scope atomics only: on this multi-die
+    // part they are coherent loads and stores past the per-die L2, whereas
+    // acquire/release at agent scope would also write back or invalidate the
+    // whole L2 of the die (on every poll of the flag), stalling every other
+    // workgroup there.  Order comes from the producer waiting for its carry
+    // stores to complete before it sets the flag, and from the consumer
+    // issuing its carry loads only after it has seen the flag.
     float* carry = a.carry + ((size_t)s * kWaves + wc) * SPW * kLanes;
     if (carry_in) {
       if (threadIdx.x == 0) {
         int spins = 0;
-        while (__hip_atomic_load(a.flags + s, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        while (__hip_atomic_load(a.flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
           __builtin_amdgcn_s_sleep(4);
           if (++spins > kMaxSpins) {  // never expected; keeps every wait finite
             __hip_atomic_store(a.flags + a.batch * a.nblocks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -302,10 +323,19 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     }
 
     // ---- core waves: this wave's SPW states of the block's 64 channels ----
-    auto core_run = [&](auto s4d_tag) __attribute__((always_inline)) {
-      constexpr bool S4D = decltype(s4d_tag)::value;
-      // B/C ring, three slots (tile t in slot (t - tb) % 3), two tiles ahead.
-      f32x4 bcr[kPrefetch][NV];
+    auto core_run = [&](auto mode_tag) __attribute__((always_inline)) {
+      constexpr int M = decltype(mode_tag)::value;
+      constexpr bool S4D = M == kDecayS4D;
+      // B/C registers.  Tile layout (SPW <= 8): a ring of three tiles (tile t
+      // in slot (t - tb) % 3) loaded two tiles ahead, value i of block blk in
+      // component blk of bct[slot][i / 16].  Block layout (SPW == 16, whose
+      // per-tile share would not fit): a ring of four 4-step blocks (block blk
+      // of any tile in slot blk) loaded three blocks ahead, value i in
+      // component (i / 16) % 4 of bcb[blk][i / 64].
+      constexpr bool kBlkBC = S::kBlockLayout;
+      constexpr int kRing = kBlkBC ? 1 : kPrefetch;
+      f32x4 bct[kRing][NV];
+      f32x4 bcb[kBlk][kBlkBC ? NV / 4 : 1];
       auto load_bc = [&](int tile, f32x4* dst) {
         const uint32_t tile_ok = tile < te ? 1u : 0u;
 #pragma unroll
@@ -314,8 +344,23 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           dst[v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
         }
       };
-      load_bc(tb, bcr[0]);
-      load_bc(tb + 1, bcr[1]);
+      auto load_bc_blk = [&](int tile, int blk, f32x4* dst) {
+        const uint32_t tile_ok = tile < te ? 1u : 0u;
+#pragma unroll
+        for (int vq = 0; vq < NV / 4; ++vq) {
+          const uint32_t off =
+              tile_ok ? (uint32_t)((((size_t)tile * kBlk + blk) * (NV / 4) + vq) * 64 + p16 * 4) * 4u : kOffNone;
+          dst[vq] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
+        }
+      };
+      if constexpr (kBlkBC) {
+        load_bc_blk(tb, 0, bcb[0]);
+        load_bc_blk(tb, 1, bcb[1]);
+        load_bc_blk(tb, 2, bcb[2]);
+      } else {
+        load_bc(tb, bct[0]);
+        load_bc(tb + 1, bct[1]);
+      }
 
       // One tile: x, the decay (S4D: r) and the start power of the four
       // blocks come from qbuf (read all up front when the registers allow);
@@ -323,7 +368,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       // delta, u and B read as zero, so the decay is exp2(0) = 1 and the input
       // term 0, and the update leaves h unchanged.
       constexpr int kAhead = SPW <= 4 ? kBlk : 1;
-      auto core_tile = [&](int buf, const f32x4* bc_cur) {
+      auto core_tile = [&](int buf, int k, const f32x4* bc_cur) {
         const float* q = qbuf[buf];
         float* pp = pbuf[buf];
         f32x4 xvs[kAhead], rvs[kAhead], svs[kAhead];
@@ -339,6 +384,16 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         }
 #pragma unroll
         for (int blk = 0; blk < kBlk; ++blk) {
+          if constexpr (kBlkBC) {  // block blk + 3: this tile's last block, or the next tile's
+            constexpr int kNext = 3;
+            const int nb = (blk + kNext) % kBlk;
+            load_bc_blk(blk + kNext < kBlk ? k : k + 1, nb, bcb[nb]);
+          }
+          // B/C value i of this block (a register and its row position).
+          auto bcv = [&](int i) -> float {
+            if constexpr (kBlkBC) return bcb[blk][(i / 16) / 4][(i / 16) % 4];
+            else return bc_cur[i / 16][blk];
+          };
           if constexpr (kAhead == 1) read_blk(blk, 0);
           const int i = kAhead == kBlk ? blk : 0;
           const f32x4 xv = xvs[i], rv = rvs[i], sv = svs[i];
@@ -346,7 +401,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const float x = xv[kk];
-            const float r = rv[kk];  // r (S4D) or delta (general)
+            const float r = rv[kk];  // r (S4D, scalar) or delta (general)
             float p = 0.f;
             float dec = sv[kk];
 #pragma unroll
@@ -355,15 +410,17 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
               const int ic = ib + SPW;          // C of state j at step kk
               if constexpr (S4D) {
                 if (j > 0) dec *= r;
+              } else if constexpr (M == kDecayScalar) {
+                dec = r;
               } else {
                 dec = exp2_fast(r * A2[j]);
               }
-              const float bx = row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x;
+              const float bx = row_bcast_rt(bcv(ib), ib % 16) * x;
               h[j] = __builtin_fmaf(dec, h[j], bx);
               if (j == 0)
-                p = row_bcast_rt(bc_cur[ic / 16][blk], ic % 16) * h[j];
+                p = row_bcast_rt(bcv(ic), ic % 16) * h[j];
               else
-                p = fmac_row_bcast_rt(p, bc_cur[ic / 16][blk], h[j], ic % 16);
+                p = fmac_row_bcast_rt(p, bcv(ic), h[j], ic % 16);
             }
             part[kk] = p;
           }
@@ -372,27 +429,34 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       };
 
       __syncthreads();  // the prologue of tile tb is in qbuf
-      auto step = [&](auto slot_tag, int k) {
-        constexpr int Sl = decltype(slot_tag)::value;
-        constexpr int S2 = (Sl + 2) % kPrefetch;
-        load_bc(k + 2, bcr[S2]);  // past the last tile: reads zeros, unused
-        core_tile(k & 1, bcr[Sl]);
-        __syncthreads();
-      };
-      int k = tb;
-      for (; k + kPrefetch <= te; k += kPrefetch) {
-        step(std::integral_constant<int, 0>{}, k);
-        step(std::integral_constant<int, 1>{}, k + 1);
-        step(std::integral_constant<int, 2>{}, k + 2);
+      if constexpr (kBlkBC) {
+        for (int k = tb; k < te; ++k) {
+          core_tile(k & 1, k, nullptr);
+          __syncthreads();
+        }
+      } else {
+        auto step = [&](auto slot_tag, int k) {
+          constexpr int Sl = decltype(slot_tag)::value;
+          constexpr int S2 = (Sl + 2) % kPrefetch;
+          load_bc(k + 2, bct[S2]);  // past the last tile: reads zeros, unused
+          core_tile(k & 1, k, bct[Sl]);
+          __syncthreads();
+        };
+        int k = tb;
+        for (; k + kPrefetch <= te; k += kPrefetch) {
+          step(std::integral_constant<int, 0>{}, k);
+          step(std::integral_constant<int, 1>{}, k + 1);
+          step(std::integral_constant<int, 2>{}, k + 2);
+        }
+        if (k < te) step(std::integral_constant<int, 0>{}, k);
+        if (k + 1 < te) step(std::integral_constant<int, 1>{}, k + 1);
       }
-      if (k < te) step(std::integral_constant<int, 0>{}, k);
-      if (k + 1 < te) step(std::integral_constant<int, 1>{}, k + 1);
     };
 
     // ---- prologue waves prepare tile k+1 and epilogue waves finish tile k-1
     // while the core runs tile k ----
-    auto io_run = [&](auto s4d_tag, auto pro_tag) __attribute__((always_inline)) {
-      constexpr bool S4D = decltype(s4d_tag)::value;
+    auto io_run = [&](auto mode_tag, auto pro_tag) __attribute__((always_inline)) {
+      constexpr int M = decltype(mode_tag)::value;
       constexpr bool PRO = decltype(pro_tag)::value;
       // Rings of three slots: (u, delta) for the prologue hold tile t in slot
       // (t - tb) % 3 and are loaded three steps ahead; (u, z) for the
@@ -415,15 +479,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       };
 
       // Prologue of one tile from ring slot `slot` into qbuf[buf]: x = delta*u,
-      // then r = exp2(delta*A0*log2 e) and the start powers r^(w*SPW+1) (S4D)
-      // or delta itself (general decay).
+      // then r = exp2(delta*A0*log2 e) and the start powers r^(w*SPW+1) (S4D),
+      // r alone (scalar) or delta itself (general decay).
       auto prologue = [&](int buf, int slot, auto&& refill) {
         const f32x4 uu = decode4(pu[slot]);
         const f32x4 dd = decode4(pd[slot]);
         refill();  // the slot's registers are free: issue its next load now
         float* q = qbuf[buf];
         *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
-        if constexpr (S4D) {
+        if constexpr (M == kDecayScalar) {
+          f32x4 r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
+          *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = r;
+        } else if constexpr (M == kDecayS4D) {
           f32x4 r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
@@ -504,24 +573,30 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       }
     };
 
+    using G = std::integral_constant<int, kDecayGeneral>;
+    using S4 = std::integral_constant<int, kDecayS4D>;
+    using SC = std::integral_constant<int, kDecayScalar>;
     if (is_core) {
-      if (s4d) core_run(std::true_type{});
-      else core_run(std::false_type{});
+      if (mode == kDecayS4D) core_run(S4{});
+      else if (mode == kDecayScalar) core_run(SC{});
+      else core_run(G{});
     } else if (is_pro) {
-      if (s4d) io_run(std::true_type{}, std::true_type{});
-      else io_run(std::false_type{}, std::true_type{});
+      if (mode == kDecayS4D) io_run(S4{}, std::true_type{});
+      else if (mode == kDecayScalar) io_run(SC{}, std::true_type{});
+      else io_run(G{}, std::true_type{});
     } else {
-      io_run(std::false_type{}, std::false_type{});  // the epilogue is the same for both decays
+      io_run(G{}, std::false_type{});  // the epilogue is the same for every decay
     }
 
     if (carry_out) {  // publish the state after tile te-1 for the next workgroup
       if (is_core) {
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) carry[j * kLanes + lane] = h[j];
+        for (int j = 0; j < SPW; ++j)
+          __hip_atomic_store(carry + j * kLanes + lane, h[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the carry stores have completed
       }
-      __threadfence();
       __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_store(a.flags + s, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) __hip_atomic_store(a.flags + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (is_core && te == ntiles && a.h_last != nullptr && cok) {
 #pragma unroll
@@ -565,14 +640,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 // B, C [batch, N, L] (bf16 or fp32) -> fp32 workspace in the bc_index layout,
 // zero for n >= N, l >= L and unused row positions.  One thread per float.
 // The same launch clears the carry flags, the error word and the ticket, and
-// its first waves check the decay structure: s4d_ok[blk] = 1 when
-// A[d,n] == (n+1)*A[d,0] (exactly, in fp32) for every channel d of the
-// 64-channel block blk (wave blk checks block blk).
+// its first waves pick each 64-channel block's decay mode (wave blk checks
+// block blk, comparing exactly in fp32): kDecayScalar when A[d,n] == A[d,0]
+// for every channel d of the block, else kDecayS4D when A[d,n] == (n+1)*A[d,0]
+// for every channel, else kDecayGeneral.
 template <bool BF16, int SPW>
 __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restrict__ B, const void* __restrict__ C,
                                                            float* __restrict__ out, int batch, int N, int L,
                                                            int ntiles, int* __restrict__ flags, int nflags,
-                                                           const float* __restrict__ A, int* __restrict__ ok_out,
+                                                           const float* __restrict__ A, int* __restrict__ mode_out,
                                                            int dim, int nblocks) {
   using S = BCShape<SPW>;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -580,21 +656,35 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
   const size_t wave = idx / kLanes;  // whole waves: the block size is a multiple of 64
   if (wave < (size_t)nblocks) {
     const int c = (int)wave * kLanes + (int)(idx % kLanes);
-    bool ok = true;
+    bool s4d = true, scalar = true;
     if (c < dim) {
       const float a0 = A[(size_t)c * N];
-      for (int n = 1; n < N; ++n) ok = ok && (A[(size_t)c * N + n] == (float)(n + 1) * a0);
+      for (int n = 1; n < N; ++n) {
+        const float an = A[(size_t)c * N + n];
+        s4d = s4d && (an == (float)(n + 1) * a0);
+        scalar = scalar && (an == a0);
+      }
     }
-    const bool all = __all(ok);
-    if (idx % kLanes == 0) ok_out[wave] = all ? 1 : 0;
+    const bool all_scalar = __all(scalar), all_s4d = __all(s4d);
+    if (idx % kLanes == 0) mode_out[wave] = all_scalar ? kDecayScalar : all_s4d ? kDecayS4D : kDecayGeneral;
   }
   const size_t total = (size_t)batch * kWaves * ntiles * S::kPerTile;
   if (idx >= total) return;
-  const int blk = (int)(idx % 4);
-  const int p = (int)((idx / 4) % 16);
-  size_t rest = idx / 64;
-  const int v = (int)(rest % S::kNV);
-  rest /= S::kNV;
+  int blk, p, v;
+  size_t rest;
+  if constexpr (S::kBlockLayout) {
+    p = (int)((idx / 4) % 16);
+    v = (int)((idx / 64) % (S::kNV / 4)) * 4 + (int)(idx % 4);
+    rest = idx / (64 * (S::kNV / 4));
+    blk = (int)(rest % kBlk);
+    rest /= kBlk;
+  } else {
+    blk = (int)(idx % 4);
+    p = (int)((idx / 4) % 16);
+    rest = idx / 64;
+    v = (int)(rest % S::kNV);
+    rest /= S::kNV;
+  }
   const int tile = (int)(rest % ntiles);
   rest /= ntiles;
   const int g = (int)(rest % kWaves);
@@ -615,7 +705,7 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
   out[idx] = val;
 }
 
-int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : 8; }
+int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : N <= 64 ? 8 : 16; }
 int64_t num_tiles(int64_t L) { return (L + kTile - 1) / kTile; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carry_floats(int spw, int64_t batch, int64_t dim) {
@@ -624,7 +714,8 @@ size_t carry_floats(int spw, int64_t batch, int64_t dim) {
 size_t flag_ints(int64_t batch, int64_t dim) { return (size_t)batch * ((dim + kLanes - 1) / kLanes) + 2; }
 size_t bc_floats(int spw, int64_t batch, int64_t L) {
   const int per_tile = spw == 1 ? BCShape<1>::kPerTile : spw == 2 ? BCShape<2>::kPerTile
-                     : spw == 4 ? BCShape<4>::kPerTile : BCShape<8>::kPerTile;
+                     : spw == 4 ? BCShape<4>::kPerTile : spw == 8 ? BCShape<8>::kPerTile
+                     : BCShape<16>::kPerTile;
   return (size_t)batch * kWaves * num_tiles(L) * per_tile;
 }
 
@@ -636,7 +727,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   float* bc = reinterpret_cast<float*>(ws);
   const size_t nbc = bc_floats(SPW, p.batch, p.seqlen);
   size_t off = align256(nbc * sizeof(float));
-  int* ok = reinterpret_cast<int*>(ws + off);
+  int* mode = reinterpret_cast<int*>(ws + off);
   off += align256((size_t)nblocks * sizeof(int));
   float* carry = reinterpret_cast<float*>(ws + off);
   off += align256(carry_floats(SPW, p.batch, p.dim) * sizeof(float));
@@ -649,7 +740,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
     const unsigned grid = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(grid), dim3(256), 0, stream, p.B, p.C, bc,
                        (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles, flags,
-                       (int)flag_ints(p.batch, p.dim), p.A, ok, (int)p.dim, nblocks);
+                       (int)flag_ints(p.batch, p.dim), p.A, mode, (int)p.dim, nblocks);
   }
 
   ScanArgs a;
@@ -662,7 +753,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.y = p.y;
   a.h_last = p.h_last;
   a.bc = bc;
-  a.s4d_ok = ok;
+  a.decay_mode = mode;
   a.batch = (int)p.batch;
   a.dim = (int)p.dim;
   a.dstate = (int)p.dstate;
@@ -694,7 +785,8 @@ hipError_t launch_dtype(const ScanParams& p, hipStream_t stream) {
     case 1: return launch_typed<BF16, 1>(p, stream);
     case 2: return launch_typed<BF16, 2>(p, stream);
     case 4: return launch_typed<BF16, 4>(p, stream);
-    default: return launch_typed<BF16, 8>(p, stream);
+    case 8: return launch_typed<BF16, 8>(p, stream);
+    default: return launch_typed<BF16, 16>(p, stream);
   }
 }
 

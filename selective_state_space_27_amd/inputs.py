@@ -14,6 +14,8 @@ library's benchmark presets):
   scan_2p8b     b=4  d_inner=5120  N=16  L=8192   bf16 I/O, fp32 A/D/state
   decode_2p8b   b=256 d_inner=5120 N=16  one token per step, 1000 steps
   ssd_2p8b      b=2  H=80 P=64 N=128 L=16384 chunk 256
+  scan_m2shape  b=2  d_inner=5120 (80 heads of 64) N=128 L=16384, bf16 I/O,
+                A and delta shared within a head (the Mamba-2 form)
 
 Every tensor comes from its own numpy PCG64 stream seeded by
 SeedSequence([seed, tensor_id(, step)]), so the order in which tensors are
@@ -39,6 +41,12 @@ class ScanConfig:
     seqlen: int
     io: str          # "fp32" or "bf16" (u, delta, B, C, z, y)
     seed: int
+    # "s4d": A[d, n] = -(n+1) (the Mamba-1 S4D-real form), delta per channel.
+    # "head": Mamba-2 form run through the Mamba-1 scan: channels in heads of
+    #   `head` (a head's A[d, n] = A_h for every n, A_h = -exp(U(0, ln 16)) as
+    #   in the SSD inputs, and one delta per (b, head, l) shared by its channels).
+    a_form: str = "s4d"
+    head: int = 64
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,6 +78,9 @@ SCAN_130M = ScanConfig("scan_130m", 8, 1536, 16, 2048, "fp32", SEED_BASE + 1)
 SCAN_2P8B = ScanConfig("scan_2p8b", 4, 5120, 16, 8192, "bf16", SEED_BASE + 2)
 DECODE_2P8B = DecodeConfig("decode_2p8b", 256, 5120, 16, 1000, "bf16", SEED_BASE + 3)
 SSD_2P8B = SSDConfig("ssd_2p8b", 2, 16384, 80, 64, 1, 128, 256, SEED_BASE + 4)
+# The Mamba-1 scan on the SSD workload's shape (d_inner = 80 heads x 64, N=128,
+# the same b and L): the two kernels compared on one layer shape.
+SCAN_M2 = ScanConfig("scan_m2shape", 2, 5120, 128, 16384, "bf16", SEED_BASE + 5, a_form="head")
 
 # Distinct per-step input sets drawn for the 1000-step decode workload; step s
 # uses set s % DECODE_POOL (input recipe).
@@ -157,17 +168,28 @@ def scan_inputs(cfg: ScanConfig, with_h0: bool = False) -> dict:
     """Inputs of the selective scan in storage form.
 
     u, delta, z: [b, d, l]; B, C: [b, n, l]  (I/O dtype)
-    A: [d, n] fp32 = -(n+1) (S4D-real); D: [d] fp32; h0: [b, d, n] fp32 (optional)
+    A: [d, n] fp32 = -(n+1) (S4D-real; a_form "head": A_h per head of channels);
+    D: [d] fp32; h0: [b, d, n] fp32 (optional)
     """
     b, d, n, L, s = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, cfg.seed
-    dt = draw_dt(s, d)
-    noise = _normal(s, TID_DNOISE, (b, d, L))
-    delta = make_delta(dt, noise, (1, d, 1)).astype(np.float32)
+    if cfg.a_form == "head":
+        nh = -(-d // cfg.head)
+        dt = draw_dt(s, nh)
+        noise = _normal(s, TID_DNOISE, (b, nh, L))
+        delta = make_delta(dt, noise, (1, nh, 1)).astype(np.float32)
+        delta = np.ascontiguousarray(np.repeat(delta, cfg.head, axis=1)[:, :d])
+        a_h = (-np.exp(rng(s, TID_A).uniform(0.0, np.log(16.0), size=nh))).astype(np.float32)
+        A = np.ascontiguousarray(np.broadcast_to(np.repeat(a_h, cfg.head)[:d, None], (d, n)))
+    else:
+        dt = draw_dt(s, d)
+        noise = _normal(s, TID_DNOISE, (b, d, L))
+        delta = make_delta(dt, noise, (1, d, 1)).astype(np.float32)
+        A = np.ascontiguousarray(np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (d, n)))
     del noise
     out = {
         "u": _io(_normal(s, TID_U, (b, d, L)), cfg.io),
         "delta": _io(delta, cfg.io),
-        "A": np.ascontiguousarray(np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (d, n))),
+        "A": A,
         "B": _io(_normal(s, TID_B, (b, n, L)), cfg.io),
         "C": _io(_normal(s, TID_C, (b, n, L)), cfg.io),
         "D": _normal(s, TID_D, (d,)),
@@ -232,8 +254,10 @@ def ssd_inputs(cfg: SSDConfig, with_h0: bool = False) -> dict:
     }
 
 
-def small_scan_config(batch, dim, dstate, seqlen, io="fp32", seed=SEED_BASE + 100) -> ScanConfig:
-    return ScanConfig(f"scan_b{batch}_d{dim}_n{dstate}_l{seqlen}_{io}", batch, dim, dstate, seqlen, io, seed)
+def small_scan_config(batch, dim, dstate, seqlen, io="fp32", seed=SEED_BASE + 100, a_form="s4d",
+                      head=64) -> ScanConfig:
+    return ScanConfig(f"scan_b{batch}_d{dim}_n{dstate}_l{seqlen}_{io}_{a_form}", batch, dim, dstate, seqlen, io, seed,
+                      a_form, head)
 
 
 def small_ssd_config(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, seed=SEED_BASE + 200) -> SSDConfig:

@@ -71,7 +71,7 @@ def test_scan_validation_errors():
     assert scan_call(shape=(2, 64, 16, 0)) == SHAPE
     assert scan_call(shape=(2, 1 << 20, 16, 1 << 12)) == SHAPE
     assert scan_call(io=7) == DTYPE
-    assert scan_call(shape=(2, 64, 65, 128)) == UNSUP
+    assert scan_call(shape=(2, 64, 129, 128)) == UNSUP
     assert scan_call(flags=0x80) == UNSUP
     assert scan_call(z=P(6, 2)) == ALIGN
     assert scan_call(h_last=P(9, 4)) == ALIGN
@@ -85,7 +85,7 @@ def test_scan_validation_errors():
 def test_scan_workspace_query():
     lib = mss.lib()
     assert lib.mss_selective_scan_workspace_size(4, 5120, 16, 8192, BF16, 0) > 0
-    assert lib.mss_selective_scan_workspace_size(4, 5120, 65, 8192, BF16, 0) == 0
+    assert lib.mss_selective_scan_workspace_size(4, 5120, 129, 8192, BF16, 0) == 0
     assert lib.mss_selective_scan_workspace_size(0, 5120, 16, 8192, BF16, 0) == 0
     assert lib.mss_selective_scan_workspace_size(1, 16, 16, 64, 3, 0) == 0
 

@@ -69,6 +69,9 @@ SHAPES = [
     (1, 192, 16, 1, "fp32"),       # single step
     (2, 64, 16, 15, "bf16"),       # shorter than one tile
     (2, 64, 16, 300, "bf16"),      # several tiles and a ragged tail
+    (1, 70, 128, 40, "fp32"),      # d_state 128: B/C loaded per 4-step block
+    (2, 64, 100, 50, "bf16"),      # d_state 100: states past N padded with zeros
+    (1, 130, 128, 33, "bf16"),
 ]
 
 
@@ -118,6 +121,56 @@ def test_scan_general_a_matrix():
     ry, rh = run_oracle(x)
     assert_close(host64(y), ry, "fp32", "y")
     assert_close(host64(hl), rh, "fp32", "h_last")
+
+
+@pytest.mark.parametrize("shape", [(2, 200, 16, 90, "fp32"), (1, 192, 128, 70, "bf16"), (2, 130, 128, 37, "fp32"),
+                                   (1, 64, 1, 20, "fp32")],
+                         ids=lambda s: "b{}d{}n{}l{}{}".format(*s))
+def test_scan_decay_mode_per_block(shape):
+    """Each 64-channel block takes its own decay path from A: A[d, n] equal
+    over n (the Mamba-2 form, heads of 32 channels here), the S4D-real form,
+    or neither; forcing the per-state path must agree."""
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io, a_form="head", head=32), with_h0=True)
+    x["A"] = x["A"].copy()
+    if d > 64:
+        x["A"][64:128] = -0.5 * (np.arange(n, dtype=np.float32) + 1)       # S4D-real, A[d,0] = -0.5
+    if d > 128:
+        g = np.random.default_rng(5)
+        x["A"][128:192] = -np.exp(g.uniform(-1.0, 1.5, size=x["A"][128:192].shape)).astype(np.float32)
+    ry, rh = run_oracle(x, with_h0=True)
+    hio = "fp32" if io == "fp32" else "bf16"
+    for force in (False, True):
+        y, hl = run_gpu(x, force, with_h0=True)
+        assert_close(host64(y), ry, io, f"y force_general={force}")
+        assert_close(host64(hl), rh, hio, f"h_last force_general={force}")
+
+
+def test_scan_dstate128_more_blocks_than_cus():
+    """d_state 128 with the sequence cut between workgroups (257 blocks)."""
+    x = I.scan_inputs(I.small_scan_config(1, 16448, 128, 21, "bf16", a_form="head"), with_h0=True)
+    y, hl = run_gpu(x, with_h0=True)
+    ry, rh = run_oracle(x, with_h0=True)
+    assert_close(host64(y), ry, "bf16", "y")
+    assert_close(host64(hl), rh, "bf16", "h_last")
+
+
+def test_scan_m2shape_workload_sampled():
+    """The Mamba-1 scan on the SSD layer's shape (b=2, d_inner=5120 in 80
+    heads, N=128, L=16384, bf16 I/O, A and delta shared within a head): the
+    full launch, checked on 96 sampled channels."""
+    x = I.scan_inputs(I.SCAN_M2)
+    y, hl = run_gpu(x)
+    g = np.random.default_rng(77)
+    chans = [(int(b), int(d)) for b, d in zip(g.integers(0, 2, 96), g.integers(0, 5120, 96))]
+    chans += [(0, 0), (1, 5119), (0, 64)]
+    ry, rh = run_oracle(x, chans)
+    yg, hg = host64(y), host64(hl)
+    e1 = assert_close(np.stack([yg[b, d] for b, d in chans]), ry, "bf16", "y")
+    gh = np.stack([hg[b, d] for b, d in chans])
+    e2 = assert_close(gh, rh, "bf16", "h_last")
+    assert rel_err(gh, rh) < 1e-4
+    print(f"scan_m2shape sampled: y err {e1:.2e}  h_last err {e2:.2e}")
 
 
 def test_scan_130m_workload_full():
