@@ -124,6 +124,20 @@ def time_region(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
+CPU_MIN_S = 10.0  # the oracle leg repeats its sample until at least this much wall time has passed
+
+
+def repeat_timed(fn, min_s=CPU_MIN_S, max_reps=100000):
+    """Calls fn until at least min_s seconds have passed; returns (calls, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or reps >= max_reps:
+            return reps, dt
+
+
 def cpu_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -179,16 +193,14 @@ def bench_scan(args, torch, mss, I, cfg):
     cpu = None
     if not args.no_cpu_baseline and not (args.seqlen or args.batch):
         import oracle
-        rows = list(range(min(2, b)))          # bounded sample: the first two batch rows, every channel, full L
-        f64 = lambda k: I.to_f64(x[k][rows], cfg.io)
+        f64 = lambda k: I.to_f64(x[k], cfg.io)  # the whole workload, repeated for at least CPU_MIN_S
         args64 = (f64("u"), f64("delta"), x["A"].astype(np.float64), f64("B"), f64("C"), x["D"].astype(np.float64),
                   f64("z"))
         th = cpu_threads()
-        t = time.perf_counter()
-        oracle.selective_scan(*args64, threads=th)
-        dt = time.perf_counter() - t
-        cpu = {"value": len(rows) * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"batch rows {rows} of {b} (all {d} channels, full L={L}); {dt:.2f} s wall, fp64 C oracle"}
+        reps, dt = repeat_timed(lambda: oracle.selective_scan(*args64, threads=th))
+        cpu = {"value": reps * b * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"the whole workload (b={b}, d={d}, N={n}, L={L}) {reps} times; {dt:.2f} s wall, "
+                         "fp64 C oracle"}
     return res, nbytes, ms, kernel, files, cpu
 
 
@@ -219,17 +231,19 @@ def bench_decode(args, torch, mss, I):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        h64 = I.decode_state0(cfg).astype(np.float64)[:32]
+        p64 = [{k: I.to_f64(p[k], "bf16") for k in ("u", "delta", "B", "C", "z")} for p in pool]
+        state = {"h": I.decode_state0(cfg).astype(np.float64), "s": 0}
         th = cpu_threads()
-        t = time.perf_counter()
-        for s in range(20):
-            p = pool[s % I.DECODE_POOL]
-            h64, _ = oracle.state_update(h64, I.to_f64(p["u"][:32], "bf16"), I.to_f64(p["delta"][:32], "bf16"), st["A"],
-                                         I.to_f64(p["B"][:32], "bf16"), I.to_f64(p["C"][:32], "bf16"), st["D"],
-                                         I.to_f64(p["z"][:32], "bf16"), threads=th)
-        dt = time.perf_counter() - t
-        cpu = {"value": 32 * d * n * 20 / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"batch rows 0-31 of {b}, 20 token steps; {dt:.2f} s wall"}
+
+        def token_step():  # consecutive token steps over the whole batch, inputs cycling through the pool
+            p = p64[state["s"] % I.DECODE_POOL]
+            state["h"], _ = oracle.state_update(state["h"], p["u"], p["delta"], st["A"], p["B"], p["C"], st["D"],
+                                                p["z"], threads=th)
+            state["s"] += 1
+
+        reps, dt = repeat_timed(token_step)
+        cpu = {"value": b * d * n * reps / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"all {b} batch rows, {reps} consecutive token steps; {dt:.2f} s wall"}
     # per-launch figures: one launch = one token step
     return res, nbytes, ms / cfg.steps, "state_update_kernel", ["state_update.hip", "common.hpp"], cpu
 
@@ -262,15 +276,12 @@ def bench_ssd(args, torch, mss, I):
     cpu = None
     if not args.no_cpu_baseline and not (args.seqlen or args.batch):
         import oracle
-        Ls = 2048
         th = cpu_threads()
-        args64 = (I.to_f64(x["x"][:1, :Ls], "bf16"), x["delta"][:1, :Ls].astype(np.float64), x["A"],
-                  I.to_f64(x["B"][:1, :Ls], "bf16"), I.to_f64(x["C"][:1, :Ls], "bf16"))
-        t = time.perf_counter()
-        oracle.ssd(*args64, threads=th)
-        dt = time.perf_counter() - t
-        cpu = {"value": Ls * H * P * N / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"batch row 0, first {Ls} of {L} steps, all heads; {dt:.2f} s wall"}
+        args64 = (I.to_f64(x["x"], "bf16"), x["delta"].astype(np.float64), x["A"], I.to_f64(x["B"], "bf16"),
+                  I.to_f64(x["C"], "bf16"))
+        reps, dt = repeat_timed(lambda: oracle.ssd(*args64, threads=th))
+        cpu = {"value": reps * b * L * H * P * N / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"the whole workload (b={b}, L={L}, all heads) {reps} times; {dt:.2f} s wall"}
     return res, ssd_bytes(b, L, H, P, G, N, 2), ms, "ssd kernels", ["ssd.hip", "common.hpp"], cpu
 
 
