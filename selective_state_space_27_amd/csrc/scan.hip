@@ -65,14 +65,32 @@ struct ScanArgs {
   float* h_last;
   const float* bc;     // B and C per wave and tile, fp32, in the layout bc_index() describes
   const int* decay_mode;  // [nblocks]: kDecayGeneral, kDecayS4D or kDecayScalar
-  float* carry;        // [streams][8 waves][SPW][64 lanes] state handed between workgroups
-  int* flags;          // [streams] carry ready; [streams] = spin-limit error; [streams + 1] = ticket
+  float* carry;        // [kMaxWG boundaries][8 waves][SPW][64 lanes] state at the end of workgroup g's range
+  float* hloc;         // same layout: zero-start end state of the piece ending at boundary g (split pass)
+  float* dsum;         // [kMaxWG][64 channels][4]: partial sums of delta over that piece (split pass)
+  int* flags;          // [kMaxWG] carry ready; [kMaxWG] = spin-limit error; [kMaxWG + 1] = ticket
   int* ticket;
   int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
   int force_general;
+  int pass;            // kPassSingle, kPassLocal or kPassFinal
 };
 
 constexpr int kMaxSpins = 1 << 22;
+
+// Workgroups per launch at most (carry slots are per workgroup boundary).
+constexpr int kMaxWG = 512;
+
+// Passes.  Single: one launch, each carry handed to the next workgroup through
+// a flag.  When there are too few sequences to fill the chip, sequences are
+// cut into more pieces than workgroups could hand on in turn, and three
+// launches replace the single one: Local (every piece that ends mid-sequence
+// runs from a zero state; its end state and the sum of delta over it are
+// kept), carry_combine_kernel (chains those along each sequence into the
+// exact start state of every piece), Final (every piece runs from its start
+// state, all at once).
+constexpr int kPassSingle = 0;
+constexpr int kPassLocal = 1;
+constexpr int kPassFinal = 2;
 
 // Decay modes of a 64-channel block.
 constexpr int kDecayGeneral = 0;  // exp2(delta*A[d,n]*log2 e) per state
@@ -220,7 +238,7 @@ constexpr int kPFloats = kWaves * kBlk * kRowPad * 4;
 
 __device__ __forceinline__ int q_off(int q, int blk, int ch) { return ((q * kBlk + blk) * kRowPad + ch) * 4; }
 
-template <bool BF16, int SPW, bool VEC>
+template <bool BF16, int SPW, bool VEC, bool LOCAL>
 __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   using S = BCShape<SPW>;
   constexpr int NV = S::kNV;
@@ -249,12 +267,17 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   float h[SPW];
 
   // Logical workgroup id in start order (a ticket), so the workgroup a carry
-  // is waited for has always started before the one that waits.
-  if (threadIdx.x == 0) sh_ticket = atomicAdd(a.ticket, 1);
-  __syncthreads();
-  const int wg_id = sh_ticket;
+  // is waited for has always started before the one that waits.  The split
+  // passes never wait and use the launch index.
+  if (a.pass == kPassSingle) {
+    if (threadIdx.x == 0) sh_ticket = atomicAdd(a.ticket, 1);
+    __syncthreads();
+  }
+  const int wg_id = a.pass == kPassSingle ? sh_ticket : (int)blockIdx.x;
 
   // One piece of work: stream s (batch row, 64-channel block), tiles [tb, te).
+  // The carry into it is slot wg_id - 1 (the end of the previous workgroup's
+  // range), the carry out of it slot wg_id.
   auto run_piece = [&](int s, int tb, int te, bool carry_in, bool carry_out) __attribute__((always_inline)) {
     const int b = s / a.nblocks, cb = s % a.nblocks;
     const int c = cb * kLanes + lane;     // channel of this lane in the core
@@ -286,8 +309,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       A2[j] = (is_core && cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
     }
 
-    // Initial state: the carry published by the workgroup that ran the first
-    // part of this stream, else h0 (or zero).
+    // Initial state: zero in the local pass; for a piece that continues a
+    // sequence, the carry at the end of the previous workgroup's range
+    // (published by that workgroup, or chained by carry_combine_kernel before
+    // the final pass); else h0 (or zero).
     //
     // The hand-off uses relaxed agent-scope atomics only: on this multi-die
     // part they are coherent loads and stores past the per-die L2, whereas
@@ -296,14 +321,19 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     // workgroup there.  Order comes from the producer waiting for its carry
     // stores to complete before it sets the flag, and from the consumer
     // issuing its carry loads only after it has seen the flag.
-    float* carry = a.carry + ((size_t)s * kWaves + wc) * SPW * kLanes;
-    if (carry_in) {
-      if (threadIdx.x == 0) {
+    const size_t slot_in = ((size_t)(wg_id - 1) * kWaves + wc) * SPW * kLanes;
+    const size_t slot_out = ((size_t)wg_id * kWaves + wc) * SPW * kLanes;
+    if (LOCAL) {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) h[j] = 0.f;
+    } else if (carry_in) {
+      float* carry = a.carry + slot_in;
+      if (a.pass == kPassSingle && threadIdx.x == 0) {
         int spins = 0;
-        while (__hip_atomic_load(a.flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        while (__hip_atomic_load(a.flags + wg_id - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
           __builtin_amdgcn_s_sleep(4);
           if (++spins > kMaxSpins) {  // never expected; keeps every wait finite
-            __hip_atomic_store(a.flags + a.batch * a.nblocks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.flags + kMaxWG, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
         }
@@ -417,14 +447,20 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
               }
               const float bx = row_bcast_rt(bcv(ib), ib % 16) * x;
               h[j] = __builtin_fmaf(dec, h[j], bx);
-              if (j == 0)
-                p = row_bcast_rt(bcv(ic), ic % 16) * h[j];
-              else
-                p = fmac_row_bcast_rt(p, bcv(ic), h[j], ic % 16);
+              // Without the readout nothing but the end state uses h, and the
+              // optimiser then restructures the tile into far more live
+              // values than registers; an empty asm per step keeps each h.
+              if constexpr (LOCAL) asm volatile("" : "+v"(h[j]));
+              if constexpr (!LOCAL) {  // the local pass needs the end state only
+                if (j == 0)
+                  p = row_bcast_rt(bcv(ic), ic % 16) * h[j];
+                else
+                  p = fmac_row_bcast_rt(p, bcv(ic), h[j], ic % 16);
+              }
             }
             part[kk] = p;
           }
-          *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
+          if constexpr (!LOCAL) *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
         }
       };
 
@@ -458,6 +494,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     auto io_run = [&](auto mode_tag, auto pro_tag) __attribute__((always_inline)) {
       constexpr int M = decltype(mode_tag)::value;
       constexpr bool PRO = decltype(pro_tag)::value;
+      if constexpr (LOCAL && !PRO) {  // no outputs in the local pass: keep the barrier count only
+        for (int k = tb; k <= te; ++k) __syncthreads();
+        return;
+      }
+      float dacc = 0.f;  // local pass: sum of delta over this thread's steps of the piece
       // Rings of three slots: (u, delta) for the prologue hold tile t in slot
       // (t - tb) % 3 and are loaded three steps ahead; (u, z) for the
       // epilogue hold tile t in slot (t - tb + 2) % 3, also three steps ahead.
@@ -484,6 +525,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       auto prologue = [&](int buf, int slot, auto&& refill) {
         const f32x4 uu = decode4(pu[slot]);
         const f32x4 dd = decode4(pd[slot]);
+        if constexpr (LOCAL) dacc += (dd[0] + dd[1]) + (dd[2] + dd[3]);  // zero past the piece and past L
         refill();  // the slot's registers are free: issue its next load now
         float* q = qbuf[buf];
         *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
@@ -561,6 +603,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       }
       if (k < te) step(std::integral_constant<int, 0>{}, k);
       if (k + 1 < te) step(std::integral_constant<int, 1>{}, k + 1);
+      if constexpr (LOCAL && PRO) a.dsum[((size_t)wg_id * kLanes + io_ch) * 4 + io_blk] = dacc;
       // The last tile's partial readouts are complete after the last barrier;
       // its epilogue ring slot is (te - tb + 1) % 3.
       if constexpr (!PRO) {
@@ -588,17 +631,23 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       io_run(G{}, std::false_type{});  // the epilogue is the same for every decay
     }
 
-    if (carry_out) {  // publish the state after tile te-1 for the next workgroup
+    if (LOCAL) {  // the zero-start end state, for carry_combine_kernel (a later launch)
       if (is_core) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) a.hloc[slot_out + j * kLanes + lane] = h[j];
+      }
+    } else if (carry_out && a.pass == kPassSingle) {  // publish the state after tile te-1
+      if (is_core) {
+        float* carry = a.carry + slot_out;
 #pragma unroll
         for (int j = 0; j < SPW; ++j)
           __hip_atomic_store(carry + j * kLanes + lane, h[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the carry stores have completed
       }
       __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_store(a.flags + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) __hip_atomic_store(a.flags + wg_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (is_core && te == ntiles && a.h_last != nullptr && cok) {
+    if (!LOCAL && is_core && te == ntiles && a.h_last != nullptr && cok) {
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
         const int n = wc * SPW + j;
@@ -608,12 +657,14 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   };
 
   // Balanced split: workgroup g owns tiles [g*W/G, (g+1)*W/G) of the
-  // concatenation of all streams (W = streams * ntiles, G = workgroups).  With
-  // at least as many streams as workgroups every range spans a stream end, so
-  // it consists of: the tail of its first stream (which continues the state
-  // the previous workgroup reached), whole streams, and the head of its last
-  // stream (whose end state the next workgroup continues from).  The head is
-  // run first and its state published at once; the tail is run last.
+  // concatenation of all streams (W = streams * ntiles, G = workgroups).  In
+  // the single pass there are at least as many streams as workgroups, so every
+  // range spans a stream end and consists of: the tail of its first stream
+  // (which continues the state the previous workgroup reached), whole streams,
+  // and the head of its last stream (whose end state the next workgroup
+  // continues from).  The head is run first and its state published at once;
+  // the tail is run last.  In the split passes a range may also lie inside one
+  // stream; the local pass runs only the piece that ends mid-stream.
   const int64_t nstreams = (int64_t)a.batch * a.nblocks;
   const int64_t wtot = nstreams * ntiles;
   const int64_t r0 = (int64_t)wg_id * wtot / a.nwg, r1 = (int64_t)(wg_id + 1) * wtot / a.nwg;
@@ -633,7 +684,45 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     } else {
       s = s_first + i, tb = 0, te = ntiles;      // whole streams
     }
+    if (LOCAL && te == ntiles) continue;
     run_piece(s, tb, te, tb > 0, te < ntiles);
+  }
+}
+
+// Split passes, between the local and the final pass: for every stream, walk
+// its piece boundaries in order and chain h <- exp(A*sum(delta)) * h + hloc
+// (the piece's decay over all its steps times the state entering it, plus its
+// zero-start end state), starting from h0 (or zero); the result is the exact
+// start state of the next piece, written to its carry slot.  One thread per
+// (stream, state, channel).
+template <int SPW>
+__global__ void __launch_bounds__(256) carry_combine_kernel(const float* __restrict__ hloc,
+                                                            const float* __restrict__ dsum,
+                                                            const float* __restrict__ A, const float* __restrict__ h0,
+                                                            float* __restrict__ carry, int batch, int dim, int N,
+                                                            int ntiles, int nblocks, int nwg) {
+  const int64_t nstreams = (int64_t)batch * nblocks;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int Np = kWaves * SPW;  // states padded to the wave split
+  if (idx >= nstreams * Np * kLanes) return;
+  const int c = (int)(idx % kLanes);
+  const int n = (int)((idx / kLanes) % Np);
+  const int64_t s = idx / ((int64_t)kLanes * Np);
+  const int b = (int)(s / nblocks), cg = (int)(s % nblocks) * kLanes + c;
+  const bool ok = cg < dim && n < N;
+  const float a2 = ok ? A[(size_t)cg * N + n] * kLog2e : 0.f;
+  float h = (ok && h0 != nullptr) ? h0[((size_t)b * dim + cg) * N + n] : 0.f;
+  const int64_t wtot = nstreams * ntiles, s0 = s * ntiles, s1 = s0 + ntiles;
+  const int w = n / SPW, j = n % SPW;
+  for (int g = (int)max<int64_t>(0, s0 * nwg / wtot - 1); g < nwg - 1; ++g) {
+    const int64_t r1 = (int64_t)(g + 1) * wtot / nwg;  // end of workgroup g's range
+    if (r1 <= s0) continue;
+    if (r1 >= s1) break;
+    const float* ds = dsum + ((size_t)g * kLanes + c) * 4;
+    const float sd = (ds[0] + ds[1]) + (ds[2] + ds[3]);
+    const size_t k = (((size_t)g * kWaves + w) * SPW + j) * kLanes + c;
+    h = __builtin_fmaf(exp2f(a2 * sd), h, hloc[k]);
+    carry[k] = h;
   }
 }
 
@@ -708,10 +797,13 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
 int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : N <= 64 ? 8 : 16; }
 int64_t num_tiles(int64_t L) { return (L + kTile - 1) / kTile; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-size_t carry_floats(int spw, int64_t batch, int64_t dim) {
-  return (size_t)batch * ((dim + kLanes - 1) / kLanes) * kWaves * spw * kLanes;
-}
-size_t flag_ints(int64_t batch, int64_t dim) { return (size_t)batch * ((dim + kLanes - 1) / kLanes) + 2; }
+size_t carry_floats(int spw) { return (size_t)kMaxWG * kWaves * spw * kLanes; }  // also the hloc size
+size_t dsum_floats() { return (size_t)kMaxWG * kLanes * 4; }
+size_t flag_ints() { return (size_t)kMaxWG + 2; }
+
+// Sequences are cut into pieces for the split passes when there are at most
+// half as many streams as workgroups and each piece still has this many tiles.
+constexpr int kMinPieceTiles = 8;
 size_t bc_floats(int spw, int64_t batch, int64_t L) {
   const int per_tile = spw == 1 ? BCShape<1>::kPerTile : spw == 2 ? BCShape<2>::kPerTile
                      : spw == 4 ? BCShape<4>::kPerTile : spw == 8 ? BCShape<8>::kPerTile
@@ -730,7 +822,11 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   int* mode = reinterpret_cast<int*>(ws + off);
   off += align256((size_t)nblocks * sizeof(int));
   float* carry = reinterpret_cast<float*>(ws + off);
-  off += align256(carry_floats(SPW, p.batch, p.dim) * sizeof(float));
+  off += align256(carry_floats(SPW) * sizeof(float));
+  float* hloc = reinterpret_cast<float*>(ws + off);
+  off += align256(carry_floats(SPW) * sizeof(float));
+  float* dsum = reinterpret_cast<float*>(ws + off);
+  off += align256(dsum_floats() * sizeof(float));
   int* flags = reinterpret_cast<int*>(ws + off);
   const int64_t nstreams = p.batch * nblocks;
 
@@ -739,8 +835,8 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
     const size_t threads = std::max<size_t>(nbc, (size_t)nblocks * kLanes);
     const unsigned grid = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(grid), dim3(256), 0, stream, p.B, p.C, bc,
-                       (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles, flags,
-                       (int)flag_ints(p.batch, p.dim), p.A, mode, (int)p.dim, nblocks);
+                       (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles, flags, (int)flag_ints(), p.A, mode,
+                       (int)p.dim, nblocks);
   }
 
   ScanArgs a;
@@ -760,22 +856,42 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.seqlen = (int)p.seqlen;
   a.ntiles = (int)ntiles;
   a.carry = carry;
+  a.hloc = hloc;
+  a.dsum = dsum;
   a.flags = flags;
-  a.ticket = flags + nstreams + 1;
+  a.ticket = flags + kMaxWG + 1;
   a.nblocks = nblocks;
+  a.force_general = p.force_general ? 1 : 0;
   // One workgroup per compute unit at most (the kernel's LDS allows one), so
-  // the balanced split below covers the chip in a single wave of workgroups.
+  // the balanced split covers the chip in a single wave of workgroups.
   int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  a.nwg = (int)std::min<int64_t>(nstreams, std::max(cus, 1));
-  a.force_general = p.force_general ? 1 : 0;
+  const int cap = std::min(std::max(cus, 1), kMaxWG);
+  const bool split = nstreams * 2 <= cap && nstreams * ntiles >= (int64_t)cap * kMinPieceTiles;
+  a.nwg = split ? cap : (int)std::min<int64_t>(nstreams, cap);
   const dim3 grid((unsigned)a.nwg);
-  if (p.seqlen % 4 == 0)
-    hipLaunchKernelGGL((scan_kernel<BF16, SPW, true>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((scan_kernel<BF16, SPW, false>), grid, dim3(kThreads), 0, stream, a);
+  auto run = [&](auto local_tag) {
+    constexpr bool LOCAL = decltype(local_tag)::value;
+    if (p.seqlen % 4 == 0)
+      hipLaunchKernelGGL((scan_kernel<BF16, SPW, true, LOCAL>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((scan_kernel<BF16, SPW, false, LOCAL>), grid, dim3(kThreads), 0, stream, a);
+  };
+  if (!split) {
+    a.pass = kPassSingle;
+    run(std::false_type{});
+  } else {
+    a.pass = kPassLocal;
+    run(std::true_type{});
+    const int64_t threads = nstreams * kWaves * SPW * kLanes;
+    hipLaunchKernelGGL((carry_combine_kernel<SPW>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       hloc, dsum, p.A, p.h0, carry, (int)p.batch, (int)p.dim, (int)p.dstate, (int)ntiles, nblocks,
+                       a.nwg);
+    a.pass = kPassFinal;
+    run(std::false_type{});
+  }
   return hipGetLastError();
 }
 
@@ -796,7 +912,8 @@ size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t 
   const int64_t nblocks = (dim + kLanes - 1) / kLanes;
   const int spw = states_per_wave(dstate);
   return align256(bc_floats(spw, batch, seqlen) * sizeof(float)) + align256((size_t)nblocks * sizeof(int)) +
-         align256(carry_floats(spw, batch, dim) * sizeof(float)) + align256(flag_ints(batch, dim) * sizeof(int));
+         2 * align256(carry_floats(spw) * sizeof(float)) + align256(dsum_floats() * sizeof(float)) +
+         align256(flag_ints() * sizeof(int));
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {

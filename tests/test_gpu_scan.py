@@ -173,6 +173,52 @@ def test_scan_m2shape_workload_sampled():
     print(f"scan_m2shape sampled: y err {e1:.2e}  h_last err {e2:.2e}")
 
 
+# Few sequences, long L: on a 256-CU part the scan cuts every sequence into
+# pieces on all CUs (streams * 2 <= CUs and >= 8 tiles per piece) and runs the
+# local pass, the carry chain and the final pass.
+SPLIT_SHAPES = [
+    # b, d, N, L, io, A form
+    (1, 128, 16, 16384, "fp32", "s4d"),    # 2 streams over 256 workgroups: chains of 127 boundaries
+    (2, 100, 16, 20001, "fp32", "s4d"),    # ragged channels and L (element loads)
+    (1, 192, 128, 16384, "bf16", "head"),  # d_state 128, one decay for all states
+    (1, 5120, 16, 4096, "bf16", "s4d"),    # the 2.8b layer at batch 1
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "b{}d{}n{}l{}{}_{}".format(*s))
+def test_scan_split_along_l(shape):
+    b, d, n, L, io, form = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io, a_form=form), with_h0=True)
+    ry, rh = run_oracle(x, with_h0=True)
+    hio = "fp32" if io == "fp32" else "bf16"
+    y, hl = run_gpu(x, with_h0=True)
+    e1 = assert_close(host64(y), ry, io, "y")
+    e2 = assert_close(host64(hl), rh, hio, "h_last")
+    y2, h2 = run_gpu(x, with_h0=True)
+    assert torch.equal(y, y2) and torch.equal(hl, h2)  # deterministic
+    yg, hg = run_gpu(x, force_general=True, with_h0=True)
+    assert_close(host64(yg), ry, io, "y (per-state exp)")
+    assert_close(host64(hg), rh, hio, "h_last (per-state exp)")
+    print(f"split {shape}: y err {e1:.2e}  h_last err {e2:.2e}")
+
+
+def test_scan_split_general_a_and_long_sequence_sampled():
+    """b=1, d_inner=5120, L=65536, bf16: a long single-sequence prefill, with
+    one 64-channel block on a general A; checked on sampled channels."""
+    x = I.scan_inputs(I.small_scan_config(1, 5120, 16, 65536, "bf16"))
+    g = np.random.default_rng(11)
+    x["A"] = x["A"].copy()
+    x["A"][640:704] = -np.exp(g.uniform(-1.0, 1.5, size=(64, 16))).astype(np.float32)
+    y, hl = run_gpu(x)
+    chans = [(0, int(c)) for c in g.integers(0, 5120, 48)] + [(0, 0), (0, 640), (0, 703), (0, 5119)]
+    ry, rh = run_oracle(x, chans)
+    yg, hg = host64(y), host64(hl)
+    assert_close(np.stack([yg[b, c] for b, c in chans]), ry, "bf16", "y")
+    gh = np.stack([hg[b, c] for b, c in chans])
+    assert_close(gh, rh, "bf16", "h_last")
+    assert rel_err(gh, rh) < 1e-4
+
+
 def test_scan_130m_workload_full():
     """b=8, d_inner=1536, N=16, L=2048, fp32: every output against the oracle."""
     x = I.scan_inputs(I.SCAN_130M)
