@@ -16,6 +16,8 @@ causal convolution / first-order IIR filter, brute-force materialised matrix,
 zero-input decay, chunk-split composition, scan equals repeated state updates,
 SSD equals the Mamba-1 scan with scalar-per-head A and its matrix form, special
 cases of D and the gate, linearity, causality).
+The backward is pinned by central finite differences of the forward, a
+different computation.
 """
 from __future__ import annotations
 
@@ -51,6 +53,8 @@ def _load():
         lib.oracle_state_update.restype = None
         lib.oracle_ssd.argtypes = [_dp] * 11 + [L] * 7 + [ctypes.c_int]
         lib.oracle_ssd.restype = None
+        lib.oracle_selective_scan_bwd.argtypes = [_dp] * 18 + [L, L, L, L, ctypes.c_int]
+        lib.oracle_selective_scan_bwd.restype = None
         _lib = lib
     return _lib
 
@@ -102,6 +106,34 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, threads=None):
                                   _ptr(h0), _ptr(y), _ptr(h_last), b, d, N, L,
                                   threads or default_threads())
     return y, h_last
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, threads=None):
+    """Gradient of a loss through the selective scan, in fp64 (mss_oracle.c,
+    oracle_selective_scan_bwd): given dy = dloss/dy [b, d, L] and optionally
+    dh_last = dloss/dh_last [b, d, N], returns a dict with du, ddelta [b, d, L],
+    dA [d, N], dB, dC [b, N, L], dD [d] (None without D), dz [b, d, L] (None
+    without z) and dh0 [b, d, N] (the gradient of the initial state)."""
+    u = _f64(u)
+    b, d, L = u.shape
+    N = np.shape(A)[1]
+    delta = _f64(delta, (b, d, L))
+    A = _f64(A, (d, N))
+    B = _f64(B, (b, N, L))
+    C = _f64(C, (b, N, L))
+    D = _f64(D, (d,))
+    z = _f64(z, (b, d, L))
+    h0 = _f64(h0, (b, d, N))
+    dy = _f64(dy, (b, d, L))
+    dh_last = _f64(dh_last, (b, d, N))
+    g = {"du": np.empty((b, d, L)), "ddelta": np.empty((b, d, L)), "dA": np.empty((d, N)),
+         "dB": np.empty((b, N, L)), "dC": np.empty((b, N, L)), "dD": np.empty(d) if D is not None else None,
+         "dz": np.empty((b, d, L)) if z is not None else None, "dh0": np.empty((b, d, N))}
+    _load().oracle_selective_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                      _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                                      b, d, N, L, threads or default_threads())
+    return g
 
 
 def state_update(h, u, delta, A, B, C, D=None, z=None, threads=None):

@@ -105,6 +105,140 @@ void oracle_selective_scan(const double* u, const double* delta, const double* A
 }
 
 /* ------------------------------------------------------------------------ */
+/* Selective scan, backward: the gradient of a scalar loss with respect to   */
+/* every input of the forward above, given dy = dloss/dy (and dh_last =      */
+/* dloss/dh_last, or zero).  Training runs the same model over whole         */
+/* sequences ("Mamba (deep learning)", paragraph on how it generates and     */
+/* trains; visual guide section 2 figure: training/prefill use the parallel  */
+/* scan); the gradient is the derivative of the forward as defined, written  */
+/* out by the chain rule in reverse time, with the forward states kept.      */
+/* For each (b, d), with dh the gradient of the state after step t:          */
+/*   dout_t = dy_t * silu(z_t);  dz_t = dy_t * out_t * silu'(z_t)            */
+/*   dh    += C_t dout_t               (then dC_t += dout_t h_t)             */
+/*   h_t = a_t h_{t-1} + delta_t B_t u_t,  a_t = exp(delta_t A):             */
+/*   dA += dh h_{t-1} a_t delta_t;  ddelta_t += dh (h_{t-1} a_t A + B_t u_t) */
+/*   du_t += dh delta_t B_t (+ D dout_t);  dB_t += dh delta_t u_t            */
+/*   dh    <- a_t dh                   (the gradient of h_{t-1})             */
+/* and dh0 is dh after step 0.  dB, dC sum over d; dA, dD over b and t.      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *h0, *dy, *dh_last;
+  double *du, *ddelta, *dz, *dh0;
+  double *dA, *dB, *dC, *dD;  /* this thread's partial sums (zeroed by the caller) */
+  long batch, dim, dstate, seqlen;
+  long unit_begin, unit_end;
+} bwd_job;
+
+static void bwd_unit(const bwd_job* j, long b, long d) {
+  const long N = j->dstate, L = j->seqlen;
+  const size_t row = (size_t)(b * j->dim + d);
+  const double* u = j->u + row * L;
+  const double* dl = j->delta + row * L;
+  const double* z = j->z ? j->z + row * L : NULL;
+  const double* dy = j->dy + row * L;
+  const double* Bb = j->B + b * N * L;
+  const double* Cb = j->C + b * N * L;
+  const double* Ad = j->A + d * N;
+  const double Dd = j->D ? j->D[d] : 0.0;
+  /* forward, keeping every state (hs[t*N + n] = h after step t) and out_t */
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(L * N));
+  double* out = (double*)malloc(sizeof(double) * (size_t)L);
+  double* h0 = (double*)malloc(sizeof(double) * (size_t)N);
+  double* dh = (double*)malloc(sizeof(double) * (size_t)N);
+  for (long n = 0; n < N; ++n) h0[n] = j->h0 ? j->h0[row * N + n] : 0.0;
+  for (long t = 0; t < L; ++t) {
+    double acc = 0.0;
+    for (long n = 0; n < N; ++n) {
+      const double hp = t > 0 ? hs[(t - 1) * N + n] : h0[n];
+      const double h = exp(dl[t] * Ad[n]) * hp + dl[t] * Bb[n * L + t] * u[t];
+      hs[t * N + n] = h;
+      acc += Cb[n * L + t] * h;
+    }
+    out[t] = acc + Dd * u[t];
+  }
+  /* reverse */
+  for (long n = 0; n < N; ++n) dh[n] = j->dh_last ? j->dh_last[row * N + n] : 0.0;
+  for (long t = L - 1; t >= 0; --t) {
+    double dout = dy[t];
+    if (z) {
+      const double sg = 1.0 / (1.0 + exp(-z[t]));
+      dout = dy[t] * z[t] * sg;                                    /* dy * silu(z)        */
+      j->dz[row * L + t] = dy[t] * out[t] * sg * (1.0 + z[t] * (1.0 - sg)); /* silu'(z)  */
+    }
+    double du = Dd * dout, dd = 0.0;
+    if (j->D) j->dD[d] += dout * u[t];
+    for (long n = 0; n < N; ++n) {
+      const double h = hs[t * N + n];
+      const double hp = t > 0 ? hs[(t - 1) * N + n] : h0[n];
+      const double a = exp(dl[t] * Ad[n]);
+      dh[n] += Cb[n * L + t] * dout;
+      j->dC[(b * N + n) * L + t] += dout * h;
+      j->dA[d * N + n] += dh[n] * hp * a * dl[t];
+      dd += dh[n] * (hp * a * Ad[n] + Bb[n * L + t] * u[t]);
+      du += dh[n] * dl[t] * Bb[n * L + t];
+      j->dB[(b * N + n) * L + t] += dh[n] * dl[t] * u[t];
+      dh[n] *= a;
+    }
+    j->du[row * L + t] = du;
+    j->ddelta[row * L + t] = dd;
+  }
+  if (j->dh0)
+    for (long n = 0; n < N; ++n) j->dh0[row * N + n] = dh[n];
+  free(hs);
+  free(out);
+  free(h0);
+  free(dh);
+}
+
+static void* bwd_worker(void* arg) {
+  const bwd_job* j = (const bwd_job*)arg;
+  for (long k = j->unit_begin; k < j->unit_end; ++k) bwd_unit(j, k / j->dim, k % j->dim);
+  return NULL;
+}
+
+/* dA [dim, dstate], dB, dC [batch, dstate, seqlen], dD [dim] are written   */
+/* (not accumulated); dz is written only when z is given, dh0 when non-null. */
+void oracle_selective_scan_bwd(const double* u, const double* delta, const double* A, const double* B,
+                               const double* C, const double* D, const double* z, const double* h0,
+                               const double* dy, const double* dh_last, double* du, double* ddelta,
+                               double* dA, double* dB, double* dC, double* dD, double* dz, double* dh0,
+                               long batch, long dim, long dstate, long seqlen, int nthreads) {
+  long units = batch * dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  const size_t nA = (size_t)(dim * dstate), nBC = (size_t)(batch * dstate * seqlen), nD = (size_t)dim;
+  const size_t per = nA + 2 * nBC + nD;
+  double* part = (double*)calloc((size_t)nthreads * per, sizeof(double));
+  bwd_job* jobs = (bwd_job*)calloc((size_t)nthreads, sizeof(bwd_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    double* p = part + (size_t)i * per;
+    bwd_job j = {u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dz, dh0,
+                 p, p + nA, p + nA + nBC, p + nA + 2 * nBC, batch, dim, dstate, seqlen,
+                 units * i / nthreads, units * (i + 1) / nthreads};
+    jobs[i] = j;
+    pthread_create(&th[i], NULL, bwd_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  /* partial sums added in thread order */
+  memset(dA, 0, nA * sizeof(double));
+  memset(dB, 0, nBC * sizeof(double));
+  memset(dC, 0, nBC * sizeof(double));
+  if (dD) memset(dD, 0, nD * sizeof(double));
+  for (int i = 0; i < nthreads; ++i) {
+    const double* p = part + (size_t)i * per;
+    for (size_t k = 0; k < nA; ++k) dA[k] += p[k];
+    for (size_t k = 0; k < nBC; ++k) dB[k] += p[nA + k];
+    for (size_t k = 0; k < nBC; ++k) dC[k] += p[nA + nBC + k];
+    if (dD)
+      for (size_t k = 0; k < nD; ++k) dD[k] += p[nA + 2 * nBC + k];
+  }
+  free(th);
+  free(jobs);
+  free(part);
+}
+
+/* ------------------------------------------------------------------------ */
 /* One-token state update (generation): one step of the same recurrence,     */
 /* with the state read and written in place.                                 */
 /* h: [batch, dim, dstate]; u, delta, z, y: [batch, dim]; B, C: [batch, dstate] */

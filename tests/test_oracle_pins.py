@@ -364,3 +364,77 @@ def test_generator_deterministic_and_order_independent():
     assert not np.array_equal(a["B"], a["C"])
     assert np.all(a["A"] == -(np.arange(16) + 1.0)[None])
     assert a["delta"].min() > 0
+
+
+# ------------------------------------------------------------ backward ------
+def _fd_grads(args, dy, dh_last, eps=1e-6):
+    """Central finite differences of loss = sum(y * dy) + sum(h_last * dh_last)
+    through the forward oracle, for every element of every given input."""
+    def loss(a):
+        y, hl = oracle.selective_scan(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"],
+                                      threads=1)
+        return float((y * dy).sum() + (0.0 if dh_last is None else (hl * dh_last).sum()))
+    out = {}
+    for k, v in args.items():
+        if v is None:
+            continue
+        fd = np.zeros_like(v)
+        for i in np.ndindex(v.shape):
+            a = dict(args)
+            vp = v.copy()
+            vp[i] += eps
+            a[k] = vp
+            lp = loss(a)
+            vm = v.copy()
+            vm[i] -= eps
+            a[k] = vm
+            fd[i] = (lp - loss(a)) / (2 * eps)
+        out[k] = fd
+    return out
+
+
+@pytest.mark.parametrize("full", [True, False], ids=["D_z_h0_dhlast", "bare"])
+def test_backward_equals_finite_differences(full):
+    """Every gradient of the backward oracle against central differences of the
+    forward oracle (a dropped term, a wrong sign or a transposed index in the
+    chain rule fails this)."""
+    g = np.random.default_rng(17 if full else 18)
+    b, d, N, L = 2, 3, 4, 6
+    args = {"u": g.normal(size=(b, d, L)), "delta": np.exp(g.uniform(-3, -0.5, size=(b, d, L))),
+            "A": -np.exp(g.uniform(-1, 1, size=(d, N))), "B": g.normal(size=(b, N, L)),
+            "C": g.normal(size=(b, N, L)),
+            "D": g.normal(size=d) if full else None, "z": g.normal(size=(b, d, L)) if full else None,
+            "h0": g.normal(size=(b, d, N)) if full else None}
+    dy = g.normal(size=(b, d, L))
+    dh_last = g.normal(size=(b, d, N)) if full else None
+    gr = oracle.selective_scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                                   args["h0"], dy, dh_last, threads=2)
+    fd = _fd_grads(args, dy, dh_last)
+    names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    for k, v in fd.items():
+        err = np.max(np.abs(gr[names[k]] - v)) / np.max(np.abs(v))
+        assert err < 1e-7, (k, err)
+    if not full:
+        assert gr["dD"] is None and gr["dz"] is None
+        # without h0 the initial state is zero; its gradient is still defined
+        assert np.all(np.isfinite(gr["dh0"]))
+
+
+def test_backward_of_lti_is_reversed_convolution():
+    """With constant delta, B, C (a time-invariant filter with kernel
+    k_s = sum_n C_n B_n delta exp(delta A_n s)), du is the reversed (anti-causal)
+    correlation of dy with k: du_t = sum_{s>=0} k_s dy_{t+s}."""
+    g = np.random.default_rng(21)
+    d, N, L = 2, 3, 40
+    dl = 0.3
+    A = -np.exp(g.uniform(-1, 1, size=(d, N)))
+    Bv, Cv = g.normal(size=N), g.normal(size=N)
+    u = g.normal(size=(1, d, L))
+    dy = g.normal(size=(1, d, L))
+    gr = oracle.selective_scan_bwd(u, np.full((1, d, L), dl), A, np.broadcast_to(Bv[None, :, None], (1, N, L)),
+                                   np.broadcast_to(Cv[None, :, None], (1, N, L)), dy=dy, threads=1)
+    s = np.arange(L)
+    for c in range(d):
+        k = (Cv[:, None] * Bv[:, None] * dl * np.exp(dl * A[c][:, None] * s[None])).sum(0)
+        want = np.array([np.dot(k[:L - t], dy[0, c, t:]) for t in range(L)])
+        np.testing.assert_allclose(gr["du"][0, c], want, rtol=1e-11, atol=1e-12)
