@@ -105,6 +105,52 @@ size_t mss_selective_scan_workspace_size(int64_t batch, int64_t dim, int64_t dst
                                          int64_t seqlen, mss_dtype io_dtype, uint32_t flags);
 
 /* ------------------------------------------------------------------------ */
+/* Selective scan, backward (training).                                      */
+/*                                                                          */
+/* The gradient of a scalar loss through mss_selective_scan_fwd, given       */
+/* dy = dloss/dy and optionally dh_last = dloss/dh_last.  Training runs the  */
+/* layer over whole sequences ("Mamba (deep learning)", paragraph on how the */
+/* model trains and generates; "Mamba-1/2/3 visual guide", section 2 figure: */
+/* training and prefill use the parallel scan); the gradient is the chain    */
+/* rule through the forward recurrence in reverse time.  Per (b, d), with dh */
+/* the gradient of the state after step t and a = exp(delta*A):             */
+/*   dout = dy*silu(z), dz = dy*out*silu'(z)   (out = C.h + D*u)            */
+/*   dh += C*dout;  dC += dout*h;  dA += dh*h_prev*a*delta                   */
+/*   ddelta = sum_n dh*(h_prev*a*A + B*u);  du = sum_n dh*delta*B + D*dout   */
+/*   dB += dh*delta*u;  dh *= a   (then the previous step); dh0 = final dh   */
+/* dB and dC are summed over the channels, dA over batch and time, dD over   */
+/* batch and time.  The states are recomputed (a forward pass writes the     */
+/* state entering every 16-step tile into the workspace), not taken from the */
+/* caller.                                                                   */
+/*                                                                          */
+/* Inputs: as mss_selective_scan_fwd (u, delta, A, B, C, D, z, h0 with the   */
+/* same layouts and dtypes), dy [batch, dim, seqlen] io_dtype, dh_last       */
+/* [batch, dim, dstate] fp32 (NULL = zero).                                  */
+/* Outputs (written, not accumulated): du, ddelta [batch, dim, seqlen] and   */
+/* dB, dC [batch, dstate, seqlen] in io_dtype; dA [dim, dstate] fp32;        */
+/* dD [dim] fp32 (NULL = not computed; with D NULL it is the gradient at     */
+/* D = 0); dz [batch, dim, seqlen] io_dtype, given exactly when z is (else    */
+/* MSS_ERR_NULL); dh0 [batch, dim, dstate] fp32 (NULL = not computed; the     */
+/* gradient of the initial state, h0 or zero).                              */
+/* Supported: 1 <= dstate <= 16 (else MSS_ERR_UNSUPPORTED), the scan's other */
+/* limits.  flags: 0 or MSS_FLAG_DECAY_GENERAL (as in the forward).  Outputs */
+/* must not overlap any input or each other.  The workspace (size from       */
+/* mss_selective_scan_bwd_workspace_size) need not be zeroed.                */
+/* ------------------------------------------------------------------------ */
+mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                                  const void* C, const float* D, const void* z, const float* h0,
+                                  const void* dy, const float* dh_last, void* du, void* ddelta,
+                                  float* dA, void* dB, void* dC, float* dD, void* dz, float* dh0,
+                                  int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                  mss_dtype io_dtype, uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace mss_selective_scan_bwd needs (0 when the shape  */
+/* is unsupported).                                                          */
+size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                             int64_t seqlen, mss_dtype io_dtype, uint32_t flags);
+
+/* ------------------------------------------------------------------------ */
 /* Single-token state update (generation step).                             */
 /*                                                                          */
 /* One step of the same recurrence, with the state carried between calls     */

@@ -31,7 +31,8 @@ STATUS_NAMES = {0: "MSS_OK", 1: "MSS_ERR_NULL", 2: "MSS_ERR_SHAPE", 3: "MSS_ERR_
                 5: "MSS_ERR_UNSUPPORTED", 6: "MSS_ERR_WORKSPACE", 7: "MSS_ERR_ALIAS", 8: "MSS_ERR_HIP"}
 
 # Every symbol the header declares.
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_state_update",
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_selective_scan_bwd",
+           "mss_selective_scan_bwd_workspace_size", "mss_state_update",
            "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_status_string", "mss_last_hip_error",
            "mss_abi_version")
 
@@ -64,6 +65,11 @@ def lib() -> ctypes.CDLL:
     L.mss_selective_scan_fwd.restype = ctypes.c_int
     L.mss_selective_scan_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
     L.mss_selective_scan_workspace_size.restype = sz
+    L.mss_selective_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, vp, vp, fp, vp, vp, fp, vp, fp,
+                                         i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.mss_selective_scan_bwd.restype = ctypes.c_int
+    L.mss_selective_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
+    L.mss_selective_scan_bwd_workspace_size.restype = sz
     L.mss_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ctypes.c_int, u32, vp]
     L.mss_state_update.restype = ctypes.c_int
     L.mss_ssd_chunk_fwd.argtypes = [vp, fp, fp, vp, vp, fp, vp, fp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
@@ -173,6 +179,47 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, *, return_las
                                       workspace.numel(), _stream(stream))
     _raise(st, "mss_selective_scan_fwd")
     return (out, h_last) if return_last_state else out
+
+
+def selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, dtype=torch.bfloat16, flags=0) -> int:
+    return lib().mss_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, _io_code(dtype), flags)
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dD=True,
+                       want_dh0=False, force_general_decay=False, workspace=None, stream=None) -> dict:
+    """Gradient of a loss through selective_scan_fwd (same inputs), given
+    dy = dloss/dy [b, d, L] and optionally dh_last = dloss/dh_last [b, d, N]
+    float32.  Returns a dict: du, ddelta, dz (None without z) [b, d, L] and dB,
+    dC [b, N, L] in the I/O dtype; dA [d, N], dD [d] (None unless want_dD) and
+    dh0 [b, d, N] (None unless want_dh0) in float32.  d_state <= 16."""
+    dev = _device_of(u)
+    b, d, L = u.shape
+    N = A.shape[1]
+    io = u.dtype
+    for t, name, shape, dt in ((u, "u", (b, d, L), io), (delta, "delta", (b, d, L), io), (A, "A", (d, N), torch.float32),
+                               (B, "B", (b, N, L), io), (C, "C", (b, N, L), io), (D, "D", (d,), torch.float32),
+                               (z, "z", (b, d, L), io), (h0, "h0", (b, d, N), torch.float32), (dy, "dy", (b, d, L), io),
+                               (dh_last, "dh_last", (b, d, N), torch.float32)):
+        _check(t, name, shape, dt, dev)
+    flags = MSS_FLAG_DECAY_GENERAL if force_general_decay else 0
+    code = _io_code(io)
+    g = {"du": torch.empty((b, d, L), dtype=io, device=dev), "ddelta": torch.empty((b, d, L), dtype=io, device=dev),
+         "dA": torch.empty((d, N), dtype=torch.float32, device=dev),
+         "dB": torch.empty((b, N, L), dtype=io, device=dev), "dC": torch.empty((b, N, L), dtype=io, device=dev),
+         "dD": torch.empty((d,), dtype=torch.float32, device=dev) if want_dD else None,
+         "dz": torch.empty((b, d, L), dtype=io, device=dev) if z is not None else None,
+         "dh0": torch.empty((b, d, N), dtype=torch.float32, device=dev) if want_dh0 else None}
+    need = lib().mss_selective_scan_bwd_workspace_size(b, d, N, L, code, flags)
+    if need == 0:
+        _raise(5, "selective_scan_bwd")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().mss_selective_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                      _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                                      b, d, N, L, code, flags, _ptr(workspace), workspace.numel(), _stream(stream))
+    _raise(st, "mss_selective_scan_bwd")
+    return g
 
 
 # -------------------------------------------------------------- state update

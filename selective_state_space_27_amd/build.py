@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmambascan.so")
-SOURCES = ["scan.hip", "state_update.hip", "ssd.hip", "api.cpp"]
+SOURCES = ["scan.hip", "scan_bwd.hip", "state_update.hip", "ssd.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

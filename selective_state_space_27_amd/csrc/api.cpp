@@ -134,6 +134,79 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
   return hip_status(mss::launch_scan(p, static_cast<hipStream_t>(hip_stream)));
 }
 
+// --------------------------------------------------- selective scan backward
+size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                             mss_dtype io_dtype, uint32_t flags) {
+  (void)flags;
+  if (scan_check_shape(batch, dim, dstate, seqlen, io_dtype) != MSS_OK || dstate > 16) return 0;
+  return mss::scan_bwd_workspace_bytes(batch, dim, dstate, seqlen);
+}
+
+mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* h0, const void* dy,
+                                  const float* dh_last, void* du, void* ddelta, float* dA, void* dB, void* dC,
+                                  float* dD, void* dz, float* dh0, int64_t batch, int64_t dim, int64_t dstate,
+                                  int64_t seqlen, mss_dtype io_dtype, uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return MSS_ERR_NULL;
+  if ((z == nullptr) != (dz == nullptr)) return MSS_ERR_NULL;
+  mss_status st = scan_check_shape(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MSS_OK) return st;
+  if (dstate > 16) return MSS_ERR_UNSUPPORTED;
+  if (flags & ~MSS_FLAG_DECAY_GENERAL) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t need = mss::scan_bwd_workspace_bytes(batch, dim, dstate, seqlen);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+
+  const size_t es = elem_size(io_dtype);
+  const size_t nbdl = (size_t)batch * dim * seqlen * es;
+  const size_t nbnl = (size_t)batch * dstate * seqlen * es;
+  const size_t nA = (size_t)dim * dstate * 4, nD = (size_t)dim * 4;
+  const size_t nstate = (size_t)batch * dim * dstate * sizeof(float);
+  const void* ins[] = {u, delta, A, B, C, D, z, h0, dy, dh_last, workspace};
+  const size_t in_bytes[] = {nbdl, nbdl, nA, nbnl, nbnl, nD, nbdl, nstate, nbdl, nstate, need};
+  void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, dh0};
+  const size_t out_bytes[] = {nbdl, nbdl, nA, nbnl, nbnl, nD, nbdl, nstate};
+  for (int i = 0; i < 8; ++i) {
+    if (!output_clear(outs[i], out_bytes[i], ins, in_bytes, 11)) return MSS_ERR_ALIAS;
+    for (int j = i + 1; j < 8; ++j)
+      if (outs[i] && outs[j] && overlaps(range_of(outs[i], out_bytes[i]), range_of(outs[j], out_bytes[j])))
+        return MSS_ERR_ALIAS;
+  }
+
+  mss::ScanBwdParams p;
+  p.fwd.u = u;
+  p.fwd.delta = delta;
+  p.fwd.A = A;
+  p.fwd.B = B;
+  p.fwd.C = C;
+  p.fwd.D = D;
+  p.fwd.z = z;
+  p.fwd.h0 = h0;
+  p.fwd.y = nullptr;
+  p.fwd.h_last = nullptr;
+  p.fwd.batch = batch;
+  p.fwd.dim = dim;
+  p.fwd.dstate = dstate;
+  p.fwd.seqlen = seqlen;
+  p.fwd.bf16 = io_dtype == MSS_BF16;
+  p.fwd.force_general = (flags & MSS_FLAG_DECAY_GENERAL) != 0;
+  p.fwd.workspace = workspace;
+  p.dy = dy;
+  p.dh_last = dh_last;
+  p.du = du;
+  p.ddelta = ddelta;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = dD;
+  p.dz = dz;
+  p.dh0 = dh0;
+  return hip_status(mss::launch_scan_bwd(p, static_cast<hipStream_t>(hip_stream)));
+}
+
 // -------------------------------------------------------------- state update
 mss_status mss_state_update(float* h, const void* u, const void* delta, const float* A, const void* B,
                             const void* C, const float* D, const void* z, void* y, int64_t batch, int64_t dim,

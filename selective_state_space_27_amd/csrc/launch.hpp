@@ -23,10 +23,30 @@ struct ScanParams {
   bool bf16;
   bool force_general;
   void* workspace;
+  float* ckpt = nullptr;  // backward only: states entering every tile, [b*nblocks][ntiles][8][SPW][64]
 };
 
 size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
+
+// Backward of the selective scan: fwd holds the forward's inputs, shape and
+// workspace (y, h_last and ckpt unused); dstate <= 16.
+struct ScanBwdParams {
+  ScanParams fwd;
+  const void* dy;
+  const float* dh_last;  // nullable
+  void* du;
+  void* ddelta;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;             // nullable
+  void* dz;              // non-null exactly when fwd.z is
+  float* dh0;            // nullable
+};
+
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
+hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t stream);
 
 struct UpdateParams {
   float* h;

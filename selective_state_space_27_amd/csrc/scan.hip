@@ -41,16 +41,13 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "scan_layout.hpp"
 
 namespace mss {
 namespace {
 
-constexpr int kWaves = 8;    // core waves: the d_state states split across them
 constexpr int kIoWaves = 4;  // prologue waves, and as many epilogue waves
-constexpr int kLanes = 64;
 constexpr int kThreads = (kWaves + 2 * kIoWaves) * kLanes;
-constexpr int kTile = 16;          // time steps per tile
-constexpr int kBlk = kTile / 4;    // float4 blocks per tile
 constexpr int kQMax = 2 + kWaves;  // LDS quantities per (d,l): x, r, 8 start powers
 constexpr int kPrefetch = 3;       // tiles of global loads in flight
 
@@ -68,6 +65,7 @@ struct ScanArgs {
   float* carry;        // [kMaxWG boundaries][8 waves][SPW][64 lanes] state at the end of workgroup g's range
   float* hloc;         // same layout: zero-start end state of the piece ending at boundary g (split pass)
   float* dsum;         // [kMaxWG][64 channels][4]: partial sums of delta over that piece (split pass)
+  float* ckpt;         // state-only kernels outside the local pass: [streams][ntiles][8][SPW][64] (nullable)
   int* flags;          // [kMaxWG] carry ready; [kMaxWG] = spin-limit error; [kMaxWG + 1] = ticket
   int* ticket;
   int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
@@ -97,134 +95,8 @@ constexpr int kDecayGeneral = 0;  // exp2(delta*A[d,n]*log2 e) per state
 constexpr int kDecayS4D = 1;      // A[d,n] == (n+1)*A[d,0]: powers of one r per (d,l)
 constexpr int kDecayScalar = 2;   // A[d,n] == A[d,0]: one r per (d,l) for every state
 
-// B/C values a wave needs per 4-step block: 4 steps x (SPW B values, SPW C
-// values) = 8*SPW, spread over NV VGPRs of 16 row positions each.
-template <int SPW>
-struct BCShape {
-  static constexpr int kPerBlk = 8 * SPW;
-  static constexpr int kNV = kPerBlk <= 16 ? 1 : kPerBlk / 16;
-  static constexpr int kPerTile = kNV * 16 * kBlk;  // floats per (batch, wave, tile)
-  static constexpr bool kBlockLayout = kNV >= 8;    // see bc_index
-};
 
-// Workspace B/C layout, per [batch][wave g][tile]: value i = v*16 + p of
-// block blk (step i / (2*SPW), quantity i % (2*SPW): B of states g*SPW..,
-// then C) belongs to row position p, and
-//   tile layout  [v][p][blk]:        lane p loads the float4 over blk, so the
-//                                    value sits in component blk of VGPR v;
-//   block layout [blk][v/4][p][v%4]: lane p loads, per block, the float4 over
-//                                    v%4, so it sits in component v%4 of
-//                                    VGPR v/4 of that block's load.
-template <int SPW>
-__device__ __forceinline__ size_t bc_index(int b, int g, int tile, int ntiles, int v, int p, int blk) {
-  using S = BCShape<SPW>;
-  return ((((size_t)b * kWaves + g) * ntiles + tile) * S::kNV + v) * 64 + p * 4 + blk;
-}
 
-__device__ __forceinline__ float fmac_row_bcast_rt(float acc, float v, float h, int p) {
-  switch (p) {
-    case 0: return fmac_row_bcast<0>(acc, v, h);
-    case 1: return fmac_row_bcast<1>(acc, v, h);
-    case 2: return fmac_row_bcast<2>(acc, v, h);
-    case 3: return fmac_row_bcast<3>(acc, v, h);
-    case 4: return fmac_row_bcast<4>(acc, v, h);
-    case 5: return fmac_row_bcast<5>(acc, v, h);
-    case 6: return fmac_row_bcast<6>(acc, v, h);
-    case 7: return fmac_row_bcast<7>(acc, v, h);
-    case 8: return fmac_row_bcast<8>(acc, v, h);
-    case 9: return fmac_row_bcast<9>(acc, v, h);
-    case 10: return fmac_row_bcast<10>(acc, v, h);
-    case 11: return fmac_row_bcast<11>(acc, v, h);
-    case 12: return fmac_row_bcast<12>(acc, v, h);
-    case 13: return fmac_row_bcast<13>(acc, v, h);
-    case 14: return fmac_row_bcast<14>(acc, v, h);
-    default: return fmac_row_bcast<15>(acc, v, h);
-  }
-}
-
-__device__ __forceinline__ float row_bcast_rt(float v, int p) {
-  switch (p) {
-    case 0: return row_bcast<0>(v);
-    case 1: return row_bcast<1>(v);
-    case 2: return row_bcast<2>(v);
-    case 3: return row_bcast<3>(v);
-    case 4: return row_bcast<4>(v);
-    case 5: return row_bcast<5>(v);
-    case 6: return row_bcast<6>(v);
-    case 7: return row_bcast<7>(v);
-    case 8: return row_bcast<8>(v);
-    case 9: return row_bcast<9>(v);
-    case 10: return row_bcast<10>(v);
-    case 11: return row_bcast<11>(v);
-    case 12: return row_bcast<12>(v);
-    case 13: return row_bcast<13>(v);
-    case 14: return row_bcast<14>(v);
-    default: return row_bcast<15>(v);
-  }
-}
-
-// Raw (undecoded) words of four consecutive steps of one row.
-template <bool BF16>
-struct Raw4;
-template <>
-struct Raw4<true> {
-  u32x2 w;
-};
-template <>
-struct Raw4<false> {
-  u32x4 w;
-};
-
-// Branch-free load of steps t..t+3 of this lane's row; out-of-range steps read 0.
-template <bool BF16, bool VEC>
-__device__ __forceinline__ Raw4<BF16> load_raw4(rsrc_t r, uint32_t lane_off, int t, int L, bool ok) {
-  constexpr uint32_t es = BF16 ? 2 : 4;
-  Raw4<BF16> res;
-  if constexpr (VEC) {  // L % 4 == 0: the four steps are all in range or all out
-    const uint32_t o = (ok && t < L) ? lane_off + (uint32_t)t * es : kOffNone;
-    if constexpr (BF16) res.w = buf_load_u32x2(r, o);
-    else res.w = buf_load_u32x4(r, o);
-  } else {
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (ok && t + i < L) ? lane_off + (uint32_t)(t + i) * es : kOffNone;
-    if constexpr (BF16) {
-      res.w.x = (uint32_t)buf_load_u16(r, o[0]) | ((uint32_t)buf_load_u16(r, o[1]) << 16);
-      res.w.y = (uint32_t)buf_load_u16(r, o[2]) | ((uint32_t)buf_load_u16(r, o[3]) << 16);
-    } else {
-      res.w.x = buf_load_u32(r, o[0]);
-      res.w.y = buf_load_u32(r, o[1]);
-      res.w.z = buf_load_u32(r, o[2]);
-      res.w.w = buf_load_u32(r, o[3]);
-    }
-  }
-  return res;
-}
-
-__device__ __forceinline__ f32x4 decode4(const Raw4<true>& r) {
-  return f32x4{bf16_lo(r.w.x), bf16_hi(r.w.x), bf16_lo(r.w.y), bf16_hi(r.w.y)};
-}
-__device__ __forceinline__ f32x4 decode4(const Raw4<false>& r) { return __builtin_bit_cast(f32x4, r.w); }
-
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void store4(rsrc_t r, uint32_t lane_off, int t, int L, bool ok, f32x4 v) {
-  constexpr uint32_t es = BF16 ? 2 : 4;
-  if constexpr (VEC) {
-    const uint32_t o = (ok && t < L) ? lane_off + (uint32_t)t * es : kOffNone;
-    if constexpr (BF16) {
-      buf_store_u32x2(r, o, u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)});
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)o, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t o = (ok && t + i < L) ? lane_off + (uint32_t)(t + i) * es : kOffNone;
-      if constexpr (BF16) buf_store_u16(r, o, f32_to_bf16(v[i]));
-      else buf_store_u32(r, o, __float_as_uint(v[i]));
-    }
-  }
-}
 
 // LDS: per buffer, kQMax quantities x kBlk x channels x float4 (4 steps), and
 // 8 waves x kBlk x channels x float4 of partial readouts.  The channel
@@ -238,7 +110,7 @@ constexpr int kPFloats = kWaves * kBlk * kRowPad * 4;
 
 __device__ __forceinline__ int q_off(int q, int blk, int ch) { return ((q * kBlk + blk) * kRowPad + ch) * 4; }
 
-template <bool BF16, int SPW, bool VEC, bool LOCAL>
+template <bool BF16, int SPW, bool VEC, bool STATE>
 __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   using S = BCShape<SPW>;
   constexpr int NV = S::kNV;
@@ -323,7 +195,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     // issuing its carry loads only after it has seen the flag.
     const size_t slot_in = ((size_t)(wg_id - 1) * kWaves + wc) * SPW * kLanes;
     const size_t slot_out = ((size_t)wg_id * kWaves + wc) * SPW * kLanes;
-    if (LOCAL) {
+    if (STATE && a.pass == kPassLocal) {
 #pragma unroll
       for (int j = 0; j < SPW; ++j) h[j] = 0.f;
     } else if (carry_in) {
@@ -450,8 +322,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
               // Without the readout nothing but the end state uses h, and the
               // optimiser then restructures the tile into far more live
               // values than registers; an empty asm per step keeps each h.
-              if constexpr (LOCAL) asm volatile("" : "+v"(h[j]));
-              if constexpr (!LOCAL) {  // the local pass needs the end state only
+              if constexpr (STATE) asm volatile("" : "+v"(h[j]));
+              if constexpr (!STATE) {  // the state-only passes need no readout
                 if (j == 0)
                   p = row_bcast_rt(bcv(ic), ic % 16) * h[j];
                 else
@@ -460,13 +332,24 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
             }
             part[kk] = p;
           }
-          if constexpr (!LOCAL) *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
+          if constexpr (!STATE) *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
         }
       };
 
       __syncthreads();  // the prologue of tile tb is in qbuf
+      // Checkpoint pass: the state entering every tile, for the backward.
+      auto checkpoint = [&](int k) {
+        if constexpr (STATE) {
+          if (a.ckpt != nullptr && a.pass != kPassLocal) {
+            float* cp = a.ckpt + ((((size_t)s * ntiles + k) * kWaves + wc) * SPW) * kLanes + lane;
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) cp[j * kLanes] = h[j];
+          }
+        }
+      };
       if constexpr (kBlkBC) {
         for (int k = tb; k < te; ++k) {
+          checkpoint(k);
           core_tile(k & 1, k, nullptr);
           __syncthreads();
         }
@@ -475,6 +358,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           constexpr int Sl = decltype(slot_tag)::value;
           constexpr int S2 = (Sl + 2) % kPrefetch;
           load_bc(k + 2, bct[S2]);  // past the last tile: reads zeros, unused
+          checkpoint(k);
           core_tile(k & 1, k, bct[Sl]);
           __syncthreads();
         };
@@ -494,7 +378,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     auto io_run = [&](auto mode_tag, auto pro_tag) __attribute__((always_inline)) {
       constexpr int M = decltype(mode_tag)::value;
       constexpr bool PRO = decltype(pro_tag)::value;
-      if constexpr (LOCAL && !PRO) {  // no outputs in the local pass: keep the barrier count only
+      if constexpr (STATE && !PRO) {  // no outputs in the state-only passes: keep the barrier count only
         for (int k = tb; k <= te; ++k) __syncthreads();
         return;
       }
@@ -525,7 +409,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       auto prologue = [&](int buf, int slot, auto&& refill) {
         const f32x4 uu = decode4(pu[slot]);
         const f32x4 dd = decode4(pd[slot]);
-        if constexpr (LOCAL) dacc += (dd[0] + dd[1]) + (dd[2] + dd[3]);  // zero past the piece and past L
+        if constexpr (STATE) dacc += (dd[0] + dd[1]) + (dd[2] + dd[3]);  // zero past the piece and past L
         refill();  // the slot's registers are free: issue its next load now
         float* q = qbuf[buf];
         *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
@@ -603,7 +487,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       }
       if (k < te) step(std::integral_constant<int, 0>{}, k);
       if (k + 1 < te) step(std::integral_constant<int, 1>{}, k + 1);
-      if constexpr (LOCAL && PRO) a.dsum[((size_t)wg_id * kLanes + io_ch) * 4 + io_blk] = dacc;
+      if constexpr (STATE && PRO) {
+        if (a.pass == kPassLocal) a.dsum[((size_t)wg_id * kLanes + io_ch) * 4 + io_blk] = dacc;
+      }
       // The last tile's partial readouts are complete after the last barrier;
       // its epilogue ring slot is (te - tb + 1) % 3.
       if constexpr (!PRO) {
@@ -631,7 +517,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       io_run(G{}, std::false_type{});  // the epilogue is the same for every decay
     }
 
-    if (LOCAL) {  // the zero-start end state, for carry_combine_kernel (a later launch)
+    if (STATE && a.pass == kPassLocal) {  // the zero-start end state, for carry_combine_kernel (a later launch)
       if (is_core) {
 #pragma unroll
         for (int j = 0; j < SPW; ++j) a.hloc[slot_out + j * kLanes + lane] = h[j];
@@ -647,7 +533,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_store(a.flags + wg_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!LOCAL && is_core && te == ntiles && a.h_last != nullptr && cok) {
+    if (!STATE && is_core && te == ntiles && a.h_last != nullptr && cok) {
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
         const int n = wc * SPW + j;
@@ -684,7 +570,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     } else {
       s = s_first + i, tb = 0, te = ntiles;      // whole streams
     }
-    if (LOCAL && te == ntiles) continue;
+    if (STATE && a.pass == kPassLocal && te == ntiles) continue;
     run_piece(s, tb, te, tb > 0, te < ntiles);
   }
 }
@@ -794,9 +680,6 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
   out[idx] = val;
 }
 
-int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : N <= 64 ? 8 : 16; }
-int64_t num_tiles(int64_t L) { return (L + kTile - 1) / kTile; }
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carry_floats(int spw) { return (size_t)kMaxWG * kWaves * spw * kLanes; }  // also the hloc size
 size_t dsum_floats() { return (size_t)kMaxWG * kLanes * 4; }
 size_t flag_ints() { return (size_t)kMaxWG + 2; }
@@ -804,12 +687,6 @@ size_t flag_ints() { return (size_t)kMaxWG + 2; }
 // Sequences are cut into pieces for the split passes when there are at most
 // half as many streams as workgroups and each piece still has this many tiles.
 constexpr int kMinPieceTiles = 8;
-size_t bc_floats(int spw, int64_t batch, int64_t L) {
-  const int per_tile = spw == 1 ? BCShape<1>::kPerTile : spw == 2 ? BCShape<2>::kPerTile
-                     : spw == 4 ? BCShape<4>::kPerTile : spw == 8 ? BCShape<8>::kPerTile
-                     : BCShape<16>::kPerTile;
-  return (size_t)batch * kWaves * num_tiles(L) * per_tile;
-}
 
 template <bool BF16, int SPW>
 hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
@@ -858,6 +735,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.carry = carry;
   a.hloc = hloc;
   a.dsum = dsum;
+  a.ckpt = p.ckpt;
   a.flags = flags;
   a.ticket = flags + kMaxWG + 1;
   a.nblocks = nblocks;
@@ -872,16 +750,18 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   const bool split = nstreams * 2 <= cap && nstreams * ntiles >= (int64_t)cap * kMinPieceTiles;
   a.nwg = split ? cap : (int)std::min<int64_t>(nstreams, cap);
   const dim3 grid((unsigned)a.nwg);
-  auto run = [&](auto local_tag) {
-    constexpr bool LOCAL = decltype(local_tag)::value;
+  // With a checkpoint buffer (for the backward) every pass runs state-only.
+  auto run = [&](auto state_tag) {
+    constexpr bool STATE = decltype(state_tag)::value;
     if (p.seqlen % 4 == 0)
-      hipLaunchKernelGGL((scan_kernel<BF16, SPW, true, LOCAL>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((scan_kernel<BF16, SPW, true, STATE>), grid, dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((scan_kernel<BF16, SPW, false, LOCAL>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((scan_kernel<BF16, SPW, false, STATE>), grid, dim3(kThreads), 0, stream, a);
   };
   if (!split) {
     a.pass = kPassSingle;
-    run(std::false_type{});
+    if (p.ckpt != nullptr) run(std::true_type{});
+    else run(std::false_type{});
   } else {
     a.pass = kPassLocal;
     run(std::true_type{});
@@ -890,7 +770,8 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
                        hloc, dsum, p.A, p.h0, carry, (int)p.batch, (int)p.dim, (int)p.dstate, (int)ntiles, nblocks,
                        a.nwg);
     a.pass = kPassFinal;
-    run(std::false_type{});
+    if (p.ckpt != nullptr) run(std::true_type{});
+    else run(std::false_type{});
   }
   return hipGetLastError();
 }

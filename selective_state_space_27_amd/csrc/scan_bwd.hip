@@ -1,0 +1,428 @@
+// Selective scan backward (Mamba-1 selective SSM layer) for gfx950.
+//
+// What is computed: the gradient of a scalar loss through the forward of
+// include/mambascan.h, given dy = dloss/dy and optionally dloss/dh_last.
+// Training runs the same layer over whole sequences ("Mamba (deep
+// learning)", paragraph on how the model trains and generates; "Mamba-1/2/3
+// visual guide" section 2 figure: training and prefill use the parallel
+// scan); the gradient is the chain rule applied to the forward recurrence in
+// reverse time.  Per (b, d), with dh the gradient of the state after step t
+// and a_t = exp(delta_t A):
+//   dout = dy*silu(z);  dz = dy*out*silu'(z)          (out = C.h + D*u)
+//   dh  += C_t*dout;    dC_t += dout*h_t              (summed over d)
+//   dA  += dh*h_{t-1}*a_t*delta_t                     (summed over b and t)
+//   ddelta_t = sum_n dh*(h_{t-1}*a_t*A + B_t*u_t)
+//   du_t     = sum_n dh*delta_t*B_t + D*dout;  dB_t += dh*delta_t*u_t
+//   dh  *= a_t                                        (gradient of h_{t-1})
+// and dh0 is dh after step 0.
+//
+// Mapping on CDNA4 (three launches):
+//  1. The forward's state-only kernel (scan.hip) writes the state entering
+//     every 16-step tile; it reuses the forward's balanced split, carries and
+//     split passes, and the fp32 B/C workspace of bc_transpose_kernel.
+//  2. scan_bwd_kernel: one workgroup of 8 waves per stream (batch row,
+//     64-channel block), tiles in reverse.  Lanes are channels and the states
+//     are split over the waves as in the forward.  Per tile every wave
+//     recomputes its states' 16 steps from the checkpoint into registers, then
+//     runs the gradient backwards in 4-step blocks.  Sums over states (for du,
+//     ddelta, dz) go through LDS to the threads that own the channel's row
+//     segment; sums over the 64 channels (dB, dC) are taken in LDS and written
+//     per stream.  Global loads of the next tile but one are issued into fixed
+//     register slots while the current tile runs (the tile loop is unrolled by
+//     two).
+//  3. bwd_reduce_kernel: dB, dC summed over the channel blocks and dA, dD over
+//     the batch rows, each in a fixed order (deterministic).
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "scan_layout.hpp"
+
+namespace mss {
+namespace {
+
+constexpr int kBwdThreads = kWaves * kLanes;  // 512
+constexpr int kInPad = kLanes + 4;            // LDS row stride of the per-tile inputs
+
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const float* D;
+  const void* z;
+  const void* dy;
+  const float* dh_last;
+  const float* bc;     // forward B/C workspace (bc_index layout)
+  const float* ckpt;   // [streams][ntiles][8][SPW][64] state entering each tile
+  void* du;
+  void* ddelta;
+  void* dz;
+  float* dh0;
+  float* dbc;          // [streams][2][8*SPW][L]: dB (0) and dC (1) summed over the stream's channels
+  float* dA_part;      // [streams][8*SPW][64]
+  float* dD_part;      // [streams][64][4]
+  int batch, dim, dstate, seqlen, ntiles, nblocks;
+};
+
+__device__ __forceinline__ float dsilu(float z) {  // d/dz of z*sigmoid(z)
+  const float sg = rcp_fast(1.0f + exp2_fast(-z * kLog2e));
+  return sg * (1.0f + z * (1.0f - sg));
+}
+
+template <bool BF16, int SPW, bool VEC>
+__global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
+  using S = BCShape<SPW>;
+  constexpr int NV = S::kNV;
+  constexpr int Np = kWaves * SPW;  // states padded to the wave split
+  constexpr uint32_t es = BF16 ? 2 : 4;
+  static_assert(!S::kBlockLayout, "the backward uses the tile B/C layout");
+  // Per tile: x, delta, u, dout by [step][channel]; per 4-step block: per-wave
+  // sums over its states by [wave][step][quantity][channel] and per-lane terms
+  // of dB, dC by [wave][state][step][quantity][channel].
+  __shared__ __attribute__((aligned(16))) float s_in[4][kTile][kInPad];
+  __shared__ __attribute__((aligned(16))) float s_part[kWaves][4][3][kLanes];
+  __shared__ __attribute__((aligned(16))) float s_dbc[kWaves][SPW][4][2][kLanes];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = a.seqlen, N = a.dstate, ntiles = a.ntiles;
+  const int s = blockIdx.x;  // stream: batch row b, channel block cb
+  const int b = s / a.nblocks, cb = s % a.nblocks;
+  const int c = cb * kLanes + lane;
+  const bool cok = c < a.dim;
+  const bool has_z = a.z != nullptr;
+
+  // I/O role: group 0 (waves 0-3) streams u and delta and writes du, ddelta;
+  // group 1 (waves 4-7) streams z and dy and writes dz.  A thread owns channel
+  // io_ch of the block and 4-step block io_blk of every tile.
+  const int grp = w >> 2;
+  const int io_ch = (threadIdx.x & 255) >> 2, io_blk = threadIdx.x & 3;
+  const int c_io = cb * kLanes + io_ch;
+  const bool iok = c_io < a.dim;
+  const int nch = min(kLanes, a.dim - cb * kLanes);
+  const size_t base_el = ((size_t)b * a.dim + (size_t)cb * kLanes) * (size_t)L;
+  const uint32_t rows_bytes = (uint32_t)nch * (uint32_t)L * es;
+  const uint32_t io_off = (uint32_t)io_ch * (uint32_t)L * es;
+  auto rsrc_of = [&](const void* p) {
+    return make_rsrc(p != nullptr ? static_cast<const char*>(p) + base_el * es : nullptr, p != nullptr ? rows_bytes : 0u);
+  };
+  const rsrc_t r_in0 = rsrc_of(grp == 0 ? a.u : a.z);
+  const rsrc_t r_in1 = rsrc_of(grp == 0 ? a.delta : a.dy);
+  const rsrc_t r_out0 = rsrc_of(grp == 0 ? a.du : (has_z ? a.dz : nullptr));
+  const rsrc_t r_out1 = rsrc_of(grp == 0 ? a.ddelta : nullptr);
+  const float dskip = (a.D != nullptr && iok) ? a.D[c_io] : 0.f;
+
+  // Core constants of this lane's channel and this wave's states.
+  float Aj[SPW], A2[SPW], dh[SPW], dA[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int n = w * SPW + j;
+    const bool ok = cok && n < N;
+    Aj[j] = ok ? a.A[(size_t)c * N + n] : 0.f;
+    A2[j] = Aj[j] * kLog2e;
+    dh[j] = (ok && a.dh_last != nullptr) ? a.dh_last[((size_t)b * a.dim + c) * N + n] : 0.f;
+    dA[j] = 0.f;
+  }
+  float dD = 0.f;
+
+  const rsrc_t rbc = make_rsrc(a.bc + bc_index<SPW>(b, w, 0, ntiles, 0, 0, 0),
+                               (uint32_t)ntiles * S::kPerTile * (uint32_t)sizeof(float));
+  const float* ckpt = a.ckpt + (((size_t)s * ntiles) * kWaves + w) * SPW * kLanes + lane;
+
+  // Register slots of the prefetch (tile k in slot k & 1 relative to the top).
+  Raw4<BF16> in0[2], in1[2];
+  f32x4 bct[2][NV];
+  float hck[2][SPW];
+  auto load = [&](int k, int sl) {
+    const bool tok = k >= 0;
+    const int t = k * kTile + io_blk * 4;
+    in0[sl] = load_raw4<BF16, VEC>(r_in0, io_off, t, L, iok && tok);
+    in1[sl] = load_raw4<BF16, VEC>(r_in1, io_off, t, L, iok && tok);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const uint32_t off = tok ? (uint32_t)(((size_t)k * NV + v) * 64 + (lane & 15) * 4) * 4u : kOffNone;
+      bct[sl][v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
+    }
+    const int kc = tok ? k : 0;  // (a tile before the first is never used)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) hck[sl][j] = ckpt[((size_t)kc * kWaves * SPW + j) * kLanes];
+  };
+
+  auto tile = [&](int k, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int Sl = decltype(slot_tag)::value;
+    const int t0 = k * kTile;
+    // ---- inputs of the tile into LDS ----
+    const f32x4 v0 = decode4(in0[Sl]);  // u (group 0) or z (group 1)
+    const f32x4 v1 = decode4(in1[Sl]);  // delta or dy
+    f32x4 bc_cur[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) bc_cur[v] = bct[Sl][v];
+    float hs[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) hs[j] = hck[Sl][j];
+    load(k - 2, Sl);  // the slot is free: the tile after next (in reverse)
+    if (grp == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_in[0][io_blk * 4 + i][io_ch] = v1[i] * v0[i];
+        s_in[1][io_blk * 4 + i][io_ch] = v1[i];
+        s_in[2][io_blk * 4 + i][io_ch] = v0[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_in[3][io_blk * 4 + i][io_ch] = has_z ? v1[i] * silu(v0[i]) : v1[i];
+    }
+    __syncthreads();
+
+    // ---- states of the 16 steps, from the checkpoint ----
+    float h[kTile][SPW];
+#pragma unroll
+    for (int t = 0; t < kTile; ++t) {
+      const int blk = t / 4, kk = t % 4;
+      const float x = s_in[0][t][lane], dl = s_in[1][t][lane];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int ib = kk * 2 * SPW + j;
+        const float hp = t > 0 ? h[t - 1][j] : hs[j];
+        h[t][j] = __builtin_fmaf(exp2_fast(dl * A2[j]), hp, row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x);
+      }
+    }
+
+    // ---- gradient, 4-step blocks in reverse ----
+#pragma unroll
+    for (int blk = kBlk - 1; blk >= 0; --blk) {
+#pragma unroll
+      for (int kk = 3; kk >= 0; --kk) {
+        const int t = blk * 4 + kk;
+        const float x = s_in[0][t][lane], dl = s_in[1][t][lane], dout = s_in[3][t][lane];
+        float sg = 0.f, s1 = 0.f, outp = 0.f;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          const int ib = kk * 2 * SPW + j;  // B of state j at step kk
+          const int ic = ib + SPW;          // C of state j at step kk
+          dh[j] = fmac_row_bcast_rt(dh[j], bc_cur[ic / 16][blk], dout, ic % 16);
+          const float hp = t > 0 ? h[t - 1][j] : hs[j];
+          const float dec = exp2_fast(dl * A2[j]);
+          const float ga = dh[j] * hp * dec;
+          dA[j] = __builtin_fmaf(ga, dl, dA[j]);
+          sg = __builtin_fmaf(ga, Aj[j], sg);
+          s1 = fmac_row_bcast_rt(s1, bc_cur[ib / 16][blk], dh[j], ib % 16);
+          outp = fmac_row_bcast_rt(outp, bc_cur[ic / 16][blk], h[t][j], ic % 16);
+          s_dbc[w][j][kk][0][lane] = dh[j] * x;
+          s_dbc[w][j][kk][1][lane] = dout * h[t][j];
+          dh[j] *= dec;
+        }
+        s_part[w][kk][0][lane] = sg;
+        s_part[w][kk][1][lane] = s1;
+        s_part[w][kk][2][lane] = outp;
+      }
+      __syncthreads();
+
+      // dB, dC of the block: 2 x Np x 4 columns of 64 channel terms, each summed
+      // by kTpc consecutive threads (a fixed order).
+      {
+        constexpr int kCols = 2 * Np * 4;
+        constexpr int kTpc = kBwdThreads / kCols;  // 4 (SPW 2) or 8 (SPW 1)
+        constexpr int kLpt = kLanes / kTpc;
+        const int col = threadIdx.x / kTpc, part = threadIdx.x % kTpc;
+        const int kk = col % 4, n = (col / 4) % Np, q = col / (4 * Np);
+        const float* src = &s_dbc[n / SPW][n % SPW][kk][q][part * kLpt];
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < kLpt; i += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
+          acc += (v[0] + v[1]) + (v[2] + v[3]);
+        }
+#pragma unroll
+        for (int m = 1; m < kTpc; m <<= 1) acc += __shfl_xor(acc, m);
+        const int t = t0 + blk * 4 + kk;
+        if (part == 0 && t < L) a.dbc[(((size_t)s * 2 + q) * Np + n) * (size_t)L + t] = acc;
+      }
+
+      // du, ddelta (group 0) and dz (group 1) of this block's steps.
+      if (io_blk == blk) {
+        f32x4 o0, o1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = blk * 4 + i;
+          const float dout = s_in[3][t][io_ch];
+          if (grp == 0) {
+            float sgs = 0.f, s1s = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) {
+              sgs += s_part[wv][i][0][io_ch];
+              s1s += s_part[wv][i][1][io_ch];
+            }
+            o0[i] = __builtin_fmaf(s1s, v1[i], dskip * dout);  // du = sum dh B delta + D dout
+            o1[i] = __builtin_fmaf(s1s, v0[i], sgs);            // ddelta = sum dh (B u + h a A)
+            dD = __builtin_fmaf(dout, v0[i], dD);
+          } else {
+            float outs = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) outs += s_part[wv][i][2][io_ch];
+            const float out = __builtin_fmaf(dskip, s_in[2][t][io_ch], outs);
+            o0[i] = has_z ? v1[i] * out * dsilu(v0[i]) : 0.f;
+            o1[i] = 0.f;
+          }
+        }
+        const int t = t0 + blk * 4;
+        store4<BF16, VEC>(r_out0, io_off, t, L, iok, o0);  // (no dz stream without z: size 0)
+        if (grp == 0) store4<BF16, VEC>(r_out1, io_off, t, L, iok, o1);
+      }
+      __syncthreads();
+    }
+  };
+
+  load(ntiles - 1, 0);
+  load(ntiles - 2, 1);
+  int k = ntiles - 1;
+  for (; k >= 1; k -= 2) {
+    tile(k, std::integral_constant<int, 0>{});
+    tile(k - 1, std::integral_constant<int, 1>{});
+  }
+  if (k == 0) tile(0, std::integral_constant<int, 0>{});
+
+  // Per-stream partial sums and the gradient of the initial state.
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int n = w * SPW + j;
+    a.dA_part[((size_t)s * Np + n) * kLanes + lane] = dA[j];
+    if (a.dh0 != nullptr && cok && n < N) a.dh0[((size_t)b * a.dim + c) * N + n] = dh[j];
+  }
+  if (grp == 0) a.dD_part[((size_t)s * kLanes + io_ch) * 4 + io_blk] = dD;
+}
+
+// dB, dC [b, N, L] = sums of the per-stream partials over the channel blocks;
+// dA [d, N] and dD [d] = sums over the batch rows; fixed order.  One thread per
+// output element; index ranges: dB, then dC, then dA, then dD.
+template <bool BF16, int SPW>
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict__ dbc, const float* __restrict__ dA_part,
+                                                         const float* __restrict__ dD_part, void* dB, void* dC,
+                                                         float* __restrict__ dA, float* __restrict__ dD, int batch,
+                                                         int dim, int N, int L, int nblocks) {
+  constexpr int Np = kWaves * SPW;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nbc = (int64_t)batch * N * L;
+  if (idx < 2 * nbc) {
+    const int q = (int)(idx / nbc);
+    const int64_t r = idx % nbc;
+    const int t = (int)(r % L);
+    const int n = (int)((r / L) % N);
+    const int b = (int)(r / ((int64_t)L * N));
+    float acc = 0.f;
+    for (int cb = 0; cb < nblocks; ++cb)
+      acc += dbc[((((size_t)b * nblocks + cb) * 2 + q) * Np + n) * (size_t)L + t];
+    void* out = q == 0 ? dB : dC;
+    if (BF16) static_cast<uint16_t*>(out)[r] = f32_to_bf16(acc);
+    else static_cast<float*>(out)[r] = acc;
+    return;
+  }
+  int64_t r = idx - 2 * nbc;
+  if (r < (int64_t)dim * N) {
+    const int d = (int)(r / N), n = (int)(r % N);
+    float acc = 0.f;
+    for (int b = 0; b < batch; ++b)
+      acc += dA_part[(((size_t)b * nblocks + d / kLanes) * Np + n) * kLanes + d % kLanes];
+    dA[r] = acc;
+    return;
+  }
+  r -= (int64_t)dim * N;
+  if (dD != nullptr && r < dim) {
+    const int d = (int)r;
+    float acc = 0.f;
+    for (int b = 0; b < batch; ++b) {
+      const float* p = dD_part + (((size_t)b * nblocks + d / kLanes) * kLanes + d % kLanes) * 4;
+      acc += (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    dD[d] = acc;
+  }
+}
+
+struct BwdLayout {
+  size_t fwd, ckpt, dbc, dA, dD, total;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  const int spw = states_per_wave(dstate);
+  const int64_t nstreams = batch * ((dim + kLanes - 1) / kLanes);
+  const int64_t np = (int64_t)kWaves * spw;
+  BwdLayout l;
+  l.fwd = align256(scan_workspace_bytes(batch, dim, dstate, seqlen));
+  l.ckpt = align256((size_t)nstreams * num_tiles(seqlen) * np * kLanes * sizeof(float));
+  l.dbc = align256((size_t)nstreams * 2 * np * seqlen * sizeof(float));
+  l.dA = align256((size_t)nstreams * np * kLanes * sizeof(float));
+  l.dD = align256((size_t)nstreams * kLanes * 4 * sizeof(float));
+  l.total = l.fwd + l.ckpt + l.dbc + l.dA + l.dD;
+  return l;
+}
+
+template <bool BF16, int SPW>
+hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
+  const BwdLayout l = bwd_layout(p.fwd.batch, p.fwd.dim, p.fwd.dstate, p.fwd.seqlen);
+  char* ws = static_cast<char*>(p.fwd.workspace);
+  float* ckpt = reinterpret_cast<float*>(ws + l.fwd);
+  float* dbc = reinterpret_cast<float*>(ws + l.fwd + l.ckpt);
+  float* dA_part = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc);
+  float* dD_part = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc + l.dA);
+
+  // 1. forward, state only: the checkpoints (and the B/C workspace at its start)
+  ScanParams f = p.fwd;
+  f.y = nullptr;
+  f.h_last = nullptr;
+  f.ckpt = ckpt;
+  hipError_t err = launch_scan(f, stream);
+  if (err != hipSuccess) return err;
+
+  // 2. backward, one workgroup per stream
+  const int nblocks = (int)((p.fwd.dim + kLanes - 1) / kLanes);
+  const int64_t nstreams = p.fwd.batch * nblocks;
+  BwdArgs a;
+  a.u = p.fwd.u;
+  a.delta = p.fwd.delta;
+  a.A = p.fwd.A;
+  a.D = p.fwd.D;
+  a.z = p.fwd.z;
+  a.dy = p.dy;
+  a.dh_last = p.dh_last;
+  a.bc = reinterpret_cast<const float*>(ws);
+  a.ckpt = ckpt;
+  a.du = p.du;
+  a.ddelta = p.ddelta;
+  a.dz = p.dz;
+  a.dh0 = p.dh0;
+  a.dbc = dbc;
+  a.dA_part = dA_part;
+  a.dD_part = dD_part;
+  a.batch = (int)p.fwd.batch;
+  a.dim = (int)p.fwd.dim;
+  a.dstate = (int)p.fwd.dstate;
+  a.seqlen = (int)p.fwd.seqlen;
+  a.ntiles = (int)num_tiles(p.fwd.seqlen);
+  a.nblocks = nblocks;
+  if (p.fwd.seqlen % 4 == 0)
+    hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, true>), dim3((unsigned)nstreams), dim3(kBwdThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, false>), dim3((unsigned)nstreams), dim3(kBwdThreads), 0, stream, a);
+
+  // 3. fixed-order sums
+  const int64_t total = 2 * p.fwd.batch * p.fwd.dstate * p.fwd.seqlen + p.fwd.dim * p.fwd.dstate + p.fwd.dim;
+  hipLaunchKernelGGL((bwd_reduce_kernel<BF16, SPW>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, dbc,
+                     dA_part, dD_part, p.dB, p.dC, p.dA, p.dD, (int)p.fwd.batch, (int)p.fwd.dim, (int)p.fwd.dstate,
+                     (int)p.fwd.seqlen, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  return bwd_layout(batch, dim, dstate, seqlen).total;
+}
+
+hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t stream) {
+  const int spw = states_per_wave(p.fwd.dstate);
+  if (p.fwd.bf16) return spw == 1 ? launch_bwd_typed<true, 1>(p, stream) : launch_bwd_typed<true, 2>(p, stream);
+  return spw == 1 ? launch_bwd_typed<false, 1>(p, stream) : launch_bwd_typed<false, 2>(p, stream);
+}
+
+}  // namespace mss

@@ -82,6 +82,43 @@ def test_scan_validation_errors():
     assert scan_call(h_last=P(10)) == ALIAS           # h_last on the workspace
 
 
+def bwd_call(**kw):
+    b, d, n, L = kw.pop("shape", (2, 64, 16, 128))
+    io = kw.pop("io", BF16)
+    ws_bytes = kw.pop("ws_bytes", mss.lib().mss_selective_scan_bwd_workspace_size(b, d, n, L, io, 0) or 1 << 20)
+    args = dict(u=P(0), delta=P(1), A=P(2), B=P(3), C=P(4), D=P(5), z=P(6), h0=P(7), dy=P(8), dh_last=P(9),
+                du=P(10), ddelta=P(11), dA=P(12), dB=P(13), dC=P(14), dD=P(15), dz=P(16), dh0=P(17), ws=P(18),
+                flags=0)
+    args.update(kw)
+    return mss.lib().mss_selective_scan_bwd(*(args[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "h0", "dy",
+                                                                "dh_last", "du", "ddelta", "dA", "dB", "dC", "dD",
+                                                                "dz", "dh0")),
+                                            b, d, n, L, io, args["flags"], args["ws"], ws_bytes, None)
+
+
+def test_scan_bwd_validation_enqueues_nothing():
+    """Every error is found on the host (fake device pointers, no GPU)."""
+    assert bwd_call(u=None) == NULL
+    assert bwd_call(dy=None) == NULL
+    assert bwd_call(dB=None) == NULL
+    assert bwd_call(dz=None) == NULL                  # z given without dz
+    assert bwd_call(z=None) == NULL                   # dz given without z
+    assert bwd_call(shape=(2, 64, 17, 128)) == UNSUP  # d_state above 16
+    assert bwd_call(shape=(2, 64, 16, 0)) == SHAPE
+    assert bwd_call(io=7) == DTYPE
+    assert bwd_call(flags=0x80) == UNSUP
+    assert bwd_call(dA=P(12, 4)) == ALIGN
+    assert bwd_call(ws=None) == WS
+    assert bwd_call(ws_bytes=16) == WS
+    assert bwd_call(du=P(0, 256)) == ALIAS            # du inside u
+    assert bwd_call(ddelta=P(10, 64)) == ALIAS        # two outputs overlap
+    assert bwd_call(dh0=P(18)) == ALIAS               # output on the workspace
+    lib = mss.lib()
+    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 16, 8192, BF16, 0) > \
+        lib.mss_selective_scan_workspace_size(4, 5120, 16, 8192, BF16, 0)
+    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 32, 8192, BF16, 0) == 0
+
+
 def test_scan_workspace_query():
     lib = mss.lib()
     assert lib.mss_selective_scan_workspace_size(4, 5120, 16, 8192, BF16, 0) > 0

@@ -1,0 +1,157 @@
+"""GPU parity of mss_selective_scan_bwd against the fp64 oracle backward.
+
+The oracle's backward is pinned to central finite differences of its forward
+(tests/test_oracle_pins.py).  Tolerance as for the forward: max |g - r| /
+max(|r|, rms(r)) <= 1e-4 for fp32 I/O and 2e-2 for bf16 I/O (bf16 gradients
+are rounded to nearest even).  dA and dD are always fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_27_amd as mss
+from selective_state_space_27_amd import inputs as I
+from gpu_util import assert_close, dev, host64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def grads_inputs(x, seed=99, with_dh_last=True):
+    """dy (I/O dtype) and dh_last (fp32) for a loss through the scan."""
+    b, d, L = x["u"].shape
+    N = x["A"].shape[1]
+    g = np.random.default_rng(seed)
+    dy = g.standard_normal((b, d, L)).astype(np.float32)
+    dy = I.f32_to_bf16_bits(dy) if x["io"] == "bf16" else dy
+    dhl = (0.5 * g.standard_normal((b, d, N))).astype(np.float32) if with_dh_last else None
+    return dy, dhl
+
+
+def run_gpu_bwd(x, dy, dhl, drop=(), with_h0=True, force_general=False):
+    g = {k: (None if k in drop else dev(x[k])) for k in ("u", "delta", "A", "B", "C", "D", "z")}
+    h0 = dev(x["h0"]) if with_h0 and x.get("h0") is not None else None
+    r = mss.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], h0, dy=dev(dy),
+                               dh_last=dev(dhl), want_dD=True, want_dh0=True, force_general_decay=force_general)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else host64(v)) for k, v in r.items()}
+
+
+def run_oracle_bwd(x, dy, dhl, drop=(), with_h0=True, rows=None, chans=None):
+    io = x["io"]
+    sel = lambda a: a if rows is None else a[rows]
+    u, dl, z = (sel(I.to_f64(x[k], io)) for k in ("u", "delta", "z"))
+    B, C = sel(I.to_f64(x["B"], io)), sel(I.to_f64(x["C"], io))
+    A, D = x["A"].astype(np.float64), x["D"].astype(np.float64)
+    h0 = sel(x["h0"].astype(np.float64)) if with_h0 and x.get("h0") is not None else None
+    dy64 = sel(I.to_f64(dy, io))
+    dhl64 = None if dhl is None else sel(dhl.astype(np.float64))
+    if "D" in drop:
+        D = None
+    if "z" in drop:
+        z = None
+    if chans is not None:  # a subset of channels (per-channel outputs and dA, dD only)
+        u, dl, dy64 = u[:, chans], dl[:, chans], dy64[:, chans]
+        z = None if z is None else z[:, chans]
+        A, D = A[chans], None if D is None else D[chans]
+        h0 = None if h0 is None else h0[:, chans]
+        dhl64 = None if dhl64 is None else dhl64[:, chans]
+    return oracle.selective_scan_bwd(u, dl, A, B, C, D, z, h0, dy64, dhl64)
+
+
+def check(got, ref, io, keys=("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0")):
+    errs = {}
+    for k in keys:
+        if ref.get(k) is None:
+            assert got.get(k) is None or k == "dD", k
+            continue
+        tol_io = "fp32" if k in ("dA", "dD", "dh0") and io == "fp32" else io
+        if k in ("dA", "dD", "dh0") and io == "bf16":
+            tol_io = "bf16"  # computed from bf16-rounded inputs in fp32; compared at the bf16 bar
+        errs[k] = assert_close(got[k], ref[k], tol_io, k)
+    return errs
+
+
+SHAPES = [
+    # b, d, N, L, io
+    (1, 16, 16, 64, "fp32"),
+    (2, 100, 16, 77, "fp32"),      # ragged channels and L (element loads)
+    (2, 130, 4, 50, "bf16"),
+    (1, 64, 1, 33, "fp32"),        # one state per wave pair (SPW 1)
+    (3, 64, 12, 100, "bf16"),      # states padded to the wave split
+    (1, 192, 16, 1, "fp32"),       # single step
+    (2, 64, 16, 15, "bf16"),       # shorter than one tile
+    (2, 64, 16, 300, "bf16"),      # several tiles and a ragged tail
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}d{}n{}l{}{}".format(*s))
+def test_scan_bwd_shapes(shape):
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    dy, dhl = grads_inputs(x)
+    got = run_gpu_bwd(x, dy, dhl)
+    errs = check(got, run_oracle_bwd(x, dy, dhl), io)
+    print(shape, {k: f"{v:.1e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("drop", [("D",), ("z",), ("D", "z")])
+def test_scan_bwd_optional_inputs(drop):
+    x = I.scan_inputs(I.small_scan_config(2, 96, 16, 70, "fp32"))
+    dy, _ = grads_inputs(x, with_dh_last=False)
+    got = run_gpu_bwd(x, dy, None, drop=drop, with_h0=False)
+    ref = run_oracle_bwd(x, dy, None, drop=drop, with_h0=False)
+    if "D" in drop:  # the gradient at D = 0 is still returned when asked for
+        ref_d = run_oracle_bwd(dict(x, D=np.zeros_like(x["D"])), dy, None, drop=tuple(k for k in drop if k != "D"),
+                               with_h0=False)
+        ref["dD"] = ref_d["dD"]
+    check(got, ref, "fp32")
+
+
+@pytest.mark.parametrize("force_general", [False, True])
+def test_scan_bwd_general_a(force_general):
+    x = I.scan_inputs(I.small_scan_config(2, 128, 16, 90, "fp32"), with_h0=True)
+    g = np.random.default_rng(3)
+    x["A"] = (-np.exp(g.uniform(-1, 2, size=x["A"].shape))).astype(np.float32)
+    x["A"][:64] = -(np.arange(16, dtype=np.float32) + 1)
+    dy, dhl = grads_inputs(x)
+    check(run_gpu_bwd(x, dy, dhl, force_general=force_general), run_oracle_bwd(x, dy, dhl), "fp32")
+
+
+@pytest.mark.parametrize("shape", [(2, 12800, 16, 45, "bf16"), (1, 128, 16, 16384, "fp32")],
+                         ids=["carry_handoff", "split_passes"])
+def test_scan_bwd_checkpoint_paths(shape):
+    """The checkpoint forward with more streams than CUs (carries handed between
+    workgroups) and with few long sequences (split passes)."""
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    dy, dhl = grads_inputs(x)
+    errs = check(run_gpu_bwd(x, dy, dhl), run_oracle_bwd(x, dy, dhl), io)
+    print(shape, {k: f"{v:.1e}" for k, v in errs.items()})
+
+
+def test_scan_bwd_deterministic():
+    x = I.scan_inputs(I.small_scan_config(2, 256, 16, 200, "bf16"), with_h0=True)
+    dy, dhl = grads_inputs(x)
+    a = run_gpu_bwd(x, dy, dhl)
+    c = run_gpu_bwd(x, dy, dhl)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], c[k]), k
+
+
+def test_scan_bwd_2p8b_workload():
+    """b=4, d_inner=5120, N=16, L=8192, bf16: the full backward launch; batch
+    row 0 checked in full against the oracle (dB, dC of that row, du, ddelta,
+    dz, dh0), dA and dD on sampled channels over all rows."""
+    x = I.scan_inputs(I.SCAN_2P8B, with_h0=True)
+    dy, dhl = grads_inputs(x)
+    got = run_gpu_bwd(x, dy, dhl)
+    ref = run_oracle_bwd(x, dy, dhl, rows=[0])
+    row0 = {k: (None if v is None or k in ("dA", "dD") else v[:1]) for k, v in got.items()}
+    errs = check(row0, ref, "bf16", keys=("du", "ddelta", "dB", "dC", "dz", "dh0"))
+    chans = [0, 63, 64, 777, 2500, 5119]
+    refc = run_oracle_bwd(x, dy, dhl, chans=chans)
+    errs.update(check({"dA": got["dA"][chans], "dD": got["dD"][chans]}, refc, "bf16", keys=("dA", "dD")))
+    print("scan_2p8b bwd:", {k: f"{v:.1e}" for k, v in errs.items()})
+    assert rel_err(got["dh0"][:1], ref["dh0"]) < 1e-2
