@@ -19,6 +19,8 @@ Other workloads (for the record in the design doc, not the headline):
   ssd_2p8b     b2 x L16384 x H80 x P64 x N128, chunk 256 (Mamba-2 SSD)
   scan_m2shape the Mamba-1 scan on ssd_2p8b's shape: b2 x d5120 (80 heads of
                64 channels) x N128 x L16384, A and delta shared within a head
+  scan_2p8b_bwd  the backward (gradients of u, delta, A, B, C, D, z) of the
+               headline scan, one mss_selective_scan_bwd call per step
   copy         a plain 1 GiB device copy (calibrates the HBM byte counters)
 
 --seqlen L and --batch B (scan and SSD workloads) time the same workload at
@@ -50,7 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scan_2p8b",
-                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "scan_m2shape", "copy"])
+                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "scan_m2shape", "scan_2p8b_bwd",
+                             "copy"])
     ap.add_argument("--seqlen", type=int, default=0,
                     help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
     ap.add_argument("--batch", type=int, default=0,
@@ -66,6 +69,13 @@ def scan_bytes(b, d, n, L, es):
     """Algorithmic bytes: u, delta, z read and y written once ([b,d,L]), B and C
     read once ([b,n,L]), A [d,n] and D [d] fp32 read once."""
     return 4 * b * d * L * es + 2 * b * n * L * es + d * n * 4 + d * 4
+
+
+def scan_bwd_bytes(b, d, n, L, es):
+    """Algorithmic bytes of the backward: u, delta, z, dy read and du, ddelta,
+    dz written once ([b,d,L]); B, C read and dB, dC written once ([b,N,L]); A,
+    D read and dA, dD written once (fp32)."""
+    return 7 * b * d * L * es + 4 * b * n * L * es + 2 * (d * n * 4 + d * 4)
 
 
 def decode_step_bytes(b, d, n, es):
@@ -188,7 +198,7 @@ def bench_scan(args, torch, mss, I, cfg):
     }
     if args.seqlen or args.batch:
         res["config"]["inputs"] = f"the preset's b={cfg.batch} L={cfg.seqlen} draw repeated or cut along b and L"
-    files = ["scan.hip", "common.hpp"]
+    files = ["scan.hip", "scan_layout.hpp", "common.hpp"]
     kernel = "scan_kernel (+ bc_transpose_kernel in the same timed call)"
     cpu = None
     if not args.no_cpu_baseline and not (args.seqlen or args.batch):
@@ -202,6 +212,44 @@ def bench_scan(args, torch, mss, I, cfg):
                "sample": f"the whole workload (b={b}, d={d}, N={n}, L={L}) {reps} times; {dt:.2f} s wall, "
                          "fp64 C oracle"}
     return res, nbytes, ms, kernel, files, cpu
+
+
+def bench_scan_bwd(args, torch, mss, I, cfg):
+    x = I.scan_inputs(cfg)
+    g = {k: to_dev(torch, x[k]) for k in ("u", "delta", "A", "B", "C", "D", "z")}
+    dy_host = I.scan_grad_output(cfg)
+    dy = to_dev(torch, dy_host)
+    io_dt = g["u"].dtype
+    b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    ws = torch.empty(mss.selective_scan_bwd_workspace_size(b, d, n, L, io_dt), dtype=torch.uint8, device="cuda:0")
+    out = mss.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], dy=dy, workspace=ws)
+
+    def step():
+        mss.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], dy=dy, out=out,
+                               workspace=ws)
+
+    ms = time_region(torch, step, args.steps, args.warmup)
+    es = 2 if cfg.io == "bf16" else 4
+    res = {"metric": "state updates/s (B*L*D*N), selective scan backward", "value": b * d * n * L / (ms * 1e-3),
+           "unit": "state updates/s", "ms_per_step": ms, "dtype": "f32",
+           "config": {"workload": f"{cfg.name}_bwd: selective scan backward b={b} d_inner={d} d_state={n} L={L}, "
+                                  f"{cfg.io} u/delta/B/C/z/dy and gradients, fp32 A/D/dA/dD/state",
+                      "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io_dtype": cfg.io,
+                      "gradients": "du, ddelta, dA, dB, dC, dD, dz"}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        f64 = lambda k: I.to_f64(x[k][:1], cfg.io)  # bounded sample: batch row 0, every channel, full L
+        args64 = (f64("u"), f64("delta"), x["A"].astype(np.float64), f64("B"), f64("C"), x["D"].astype(np.float64),
+                  f64("z"), None, I.to_f64(dy_host[:1], cfg.io))
+        th = cpu_threads()
+        reps, dt = repeat_timed(lambda: oracle.selective_scan_bwd(*args64, threads=th))
+        cpu = {"value": reps * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"batch row 0 of {b} (all {d} channels, full L={L}) {reps} times; {dt:.2f} s wall, "
+                         "fp64 C oracle backward"}
+    files = ["scan.hip", "scan_bwd.hip", "scan_layout.hpp", "common.hpp"]
+    kernel = "scan_bwd_kernel (+ checkpoint forward and bwd_reduce_kernel in the same timed call)"
+    return res, scan_bwd_bytes(b, d, n, L, es), ms, kernel, files, cpu
 
 
 def bench_decode(args, torch, mss, I):
@@ -301,7 +349,8 @@ def main():
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
               "the hot path shards over batch and channels with no communication, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
-    if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and args.workload in ("decode_2p8b", "copy")):
+    if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and
+                                             args.workload in ("decode_2p8b", "copy", "scan_2p8b_bwd")):
         print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
               file=sys.stderr)
         sys.exit(2)
@@ -323,6 +372,8 @@ def main():
         res, nbytes, launch_ms, kernel, files, cpu = bench_ssd(args, torch, mss, I)
     elif args.workload == "scan_m2shape":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_M2)
+    elif args.workload == "scan_2p8b_bwd":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_bwd(args, torch, mss, I, I.SCAN_2P8B)
     else:
         res, nbytes, launch_ms, kernel, files, cpu = bench_copy(args, torch)
 

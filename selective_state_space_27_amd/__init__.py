@@ -186,12 +186,14 @@ def selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, dtype=torch.bf
 
 
 def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dD=True,
-                       want_dh0=False, force_general_decay=False, workspace=None, stream=None) -> dict:
+                       want_dh0=False, force_general_decay=False, out=None, workspace=None, stream=None) -> dict:
     """Gradient of a loss through selective_scan_fwd (same inputs), given
     dy = dloss/dy [b, d, L] and optionally dh_last = dloss/dh_last [b, d, N]
     float32.  Returns a dict: du, ddelta, dz (None without z) [b, d, L] and dB,
     dC [b, N, L] in the I/O dtype; dA [d, N], dD [d] (None unless want_dD) and
-    dh0 [b, d, N] (None unless want_dh0) in float32.  d_state <= 16."""
+    dh0 [b, d, N] (None unless want_dh0) in float32.  d_state <= 16.  ``out``:
+    a dict from an earlier call with the same shapes whose tensors are
+    written again (nothing is allocated for them)."""
     dev = _device_of(u)
     b, d, L = u.shape
     N = A.shape[1]
@@ -203,12 +205,19 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
         _check(t, name, shape, dt, dev)
     flags = MSS_FLAG_DECAY_GENERAL if force_general_decay else 0
     code = _io_code(io)
-    g = {"du": torch.empty((b, d, L), dtype=io, device=dev), "ddelta": torch.empty((b, d, L), dtype=io, device=dev),
+    g = out if out is not None else {
+         "du": torch.empty((b, d, L), dtype=io, device=dev), "ddelta": torch.empty((b, d, L), dtype=io, device=dev),
          "dA": torch.empty((d, N), dtype=torch.float32, device=dev),
          "dB": torch.empty((b, N, L), dtype=io, device=dev), "dC": torch.empty((b, N, L), dtype=io, device=dev),
          "dD": torch.empty((d,), dtype=torch.float32, device=dev) if want_dD else None,
          "dz": torch.empty((b, d, L), dtype=io, device=dev) if z is not None else None,
          "dh0": torch.empty((b, d, N), dtype=torch.float32, device=dev) if want_dh0 else None}
+    for k, shape, dt in (("du", (b, d, L), io), ("ddelta", (b, d, L), io), ("dA", (d, N), torch.float32),
+                         ("dB", (b, N, L), io), ("dC", (b, N, L), io), ("dD", (d,), torch.float32),
+                         ("dz", (b, d, L), io), ("dh0", (b, d, N), torch.float32)):
+        _check(g.get(k), k, shape, dt, dev)
+    if (z is None) != (g.get("dz") is None):
+        raise ValueError("dz is returned exactly when z is given")
     need = lib().mss_selective_scan_bwd_workspace_size(b, d, N, L, code, flags)
     if need == 0:
         _raise(5, "selective_scan_bwd")
@@ -216,7 +225,8 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib().mss_selective_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                       _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
-                                      _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                                      _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+                                      _ptr(g.get("dh0")),
                                       b, d, N, L, code, flags, _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(st, "mss_selective_scan_bwd")
     return g

@@ -77,12 +77,14 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   constexpr int Np = kWaves * SPW;  // states padded to the wave split
   constexpr uint32_t es = BF16 ? 2 : 4;
   static_assert(!S::kBlockLayout, "the backward uses the tile B/C layout");
-  // Per tile: x, delta, u, dout by [step][channel]; per 4-step block: per-wave
-  // sums over its states by [wave][step][quantity][channel] and per-lane terms
-  // of dB, dC by [wave][state][step][quantity][channel].
-  __shared__ __attribute__((aligned(16))) float s_in[4][kTile][kInPad];
+  // Per tile: x, delta, u, dout, dy*silu'(z) by [step][channel] (once a
+  // block's gradients are known, x, dout and dy*silu'(z) of its steps are
+  // replaced by du, ddelta and dz); per 4-step block: per-wave sums over its
+  // states by [wave][step][quantity][channel] and per-lane terms of dB, dC by
+  // [wave][state][step][quantity][channel].  Rows padded to 68 floats.
+  __shared__ __attribute__((aligned(16))) float s_in[5][kTile][kInPad];
   __shared__ __attribute__((aligned(16))) float s_part[kWaves][4][3][kLanes];
-  __shared__ __attribute__((aligned(16))) float s_dbc[kWaves][SPW][4][2][kLanes];
+  __shared__ __attribute__((aligned(16))) float s_dbc[kWaves][SPW][4][2][kInPad];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -111,7 +113,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   const rsrc_t r_in1 = rsrc_of(grp == 0 ? a.delta : a.dy);
   const rsrc_t r_out0 = rsrc_of(grp == 0 ? a.du : (has_z ? a.dz : nullptr));
   const rsrc_t r_out1 = rsrc_of(grp == 0 ? a.ddelta : nullptr);
-  const float dskip = (a.D != nullptr && iok) ? a.D[c_io] : 0.f;
+  const float dskip = (a.D != nullptr && cok) ? a.D[c] : 0.f;  // of the lane's channel
 
   // Core constants of this lane's channel and this wave's states.
   float Aj[SPW], A2[SPW], dh[SPW], dA[SPW];
@@ -171,7 +173,10 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_in[3][io_blk * 4 + i][io_ch] = has_z ? v1[i] * silu(v0[i]) : v1[i];
+      for (int i = 0; i < 4; ++i) {
+        s_in[3][io_blk * 4 + i][io_ch] = has_z ? v1[i] * silu(v0[i]) : v1[i];
+        s_in[4][io_blk * 4 + i][io_ch] = has_z ? v1[i] * dsilu(v0[i]) : 0.f;
+      }
     }
     __syncthreads();
 
@@ -240,38 +245,44 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
         if (part == 0 && t < L) a.dbc[(((size_t)s * 2 + q) * Np + n) * (size_t)L + t] = acc;
       }
 
-      // du, ddelta (group 0) and dz (group 1) of this block's steps.
-      if (io_blk == blk) {
-        f32x4 o0, o1;
+      // du, ddelta (group 0) and dz (group 1) of this block: thread (channel
+      // lane, step w & 3) of its group sums the 8 waves' partials; the results
+      // replace inputs nobody reads any more (x, dout, dy*silu'(z)).
+      {
+        const int t = blk * 4 + (w & 3);
+        if (grp == 0) {
+          float sgs = 0.f, s1s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = blk * 4 + i;
-          const float dout = s_in[3][t][io_ch];
-          if (grp == 0) {
-            float sgs = 0.f, s1s = 0.f;
-#pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) {
-              sgs += s_part[wv][i][0][io_ch];
-              s1s += s_part[wv][i][1][io_ch];
-            }
-            o0[i] = __builtin_fmaf(s1s, v1[i], dskip * dout);  // du = sum dh B delta + D dout
-            o1[i] = __builtin_fmaf(s1s, v0[i], sgs);            // ddelta = sum dh (B u + h a A)
-            dD = __builtin_fmaf(dout, v0[i], dD);
-          } else {
-            float outs = 0.f;
-#pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) outs += s_part[wv][i][2][io_ch];
-            const float out = __builtin_fmaf(dskip, s_in[2][t][io_ch], outs);
-            o0[i] = has_z ? v1[i] * out * dsilu(v0[i]) : 0.f;
-            o1[i] = 0.f;
+          for (int wv = 0; wv < kWaves; ++wv) {
+            sgs += s_part[wv][w & 3][0][lane];
+            s1s += s_part[wv][w & 3][1][lane];
           }
+          const float dout = s_in[3][t][lane], uu = s_in[2][t][lane];
+          s_in[0][t][lane] = __builtin_fmaf(s1s, s_in[1][t][lane], dskip * dout);  // du = sum dh B delta + D dout
+          s_in[3][t][lane] = __builtin_fmaf(s1s, uu, sgs);                         // ddelta = sum dh (B u + h a A)
+          dD = __builtin_fmaf(dout, uu, dD);
+        } else {
+          float outs = 0.f;
+#pragma unroll
+          for (int wv = 0; wv < kWaves; ++wv) outs += s_part[wv][w & 3][2][lane];
+          s_in[4][t][lane] *= __builtin_fmaf(dskip, s_in[2][t][lane], outs);  // dz = dy silu'(z) out
         }
-        const int t = t0 + blk * 4;
-        store4<BF16, VEC>(r_out0, io_off, t, L, iok, o0);  // (no dz stream without z: size 0)
-        if (grp == 0) store4<BF16, VEC>(r_out1, io_off, t, L, iok, o1);
       }
       __syncthreads();
     }
+
+    // Gradients of the tile's row segments: du, ddelta (group 0), dz (group 1).
+    {
+      f32x4 o0, o1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o0[i] = s_in[grp == 0 ? 0 : 4][io_blk * 4 + i][io_ch];
+        o1[i] = s_in[3][io_blk * 4 + i][io_ch];
+      }
+      store4<BF16, VEC>(r_out0, io_off, t0 + io_blk * 4, L, iok, o0);  // (no dz stream without z: size 0)
+      if (grp == 0) store4<BF16, VEC>(r_out1, io_off, t0 + io_blk * 4, L, iok, o1);
+    }
+    __syncthreads();  // the next tile overwrites s_in
   };
 
   load(ntiles - 1, 0);
@@ -290,7 +301,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
     a.dA_part[((size_t)s * Np + n) * kLanes + lane] = dA[j];
     if (a.dh0 != nullptr && cok && n < N) a.dh0[((size_t)b * a.dim + c) * N + n] = dh[j];
   }
-  if (grp == 0) a.dD_part[((size_t)s * kLanes + io_ch) * 4 + io_blk] = dD;
+  if (grp == 0) a.dD_part[((size_t)s * kLanes + lane) * 4 + (w & 3)] = dD;
 }
 
 // dB, dC [b, N, L] = sums of the per-stream partials over the channel blocks;

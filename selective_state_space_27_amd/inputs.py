@@ -27,7 +27,7 @@ import dataclasses
 import numpy as np
 
 # Tensor ids for the per-tensor child streams.
-TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X = range(1, 11)
+TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X, TID_DY = range(1, 12)
 
 SEED_BASE = 27000
 
@@ -199,6 +199,11 @@ def scan_inputs(cfg: ScanConfig, with_h0: bool = False) -> dict:
     }
     del delta
     return out
+
+
+def scan_grad_output(cfg: ScanConfig) -> np.ndarray:
+    """dy = dloss/dy [b, d, l] ~ N(0, 1) in the I/O dtype, for the backward."""
+    return _io(_normal(cfg.seed, TID_DY, (cfg.batch, cfg.dim, cfg.seqlen)), cfg.io)
 
 
 # ---------------------------------------------------------- decode inputs ---
