@@ -20,9 +20,12 @@
 //  1. The forward's state-only kernel (scan.hip) writes the state entering
 //     every 16-step tile; it reuses the forward's balanced split, carries and
 //     split passes, and the fp32 B/C workspace of bc_transpose_kernel.
-//  2. scan_bwd_kernel: one workgroup of 8 waves per stream (batch row,
-//     64-channel block), tiles in reverse.  Lanes are channels and the states
-//     are split over the waves as in the forward.  Per tile every wave
+//  2. scan_bwd_kernel: one workgroup of 8 waves per CU; the streams (batch
+//     row, 64-channel block) are split over them as in the forward's balanced
+//     split, each piece run in reverse, the gradient of the state handed from
+//     the workgroup holding a stream's end to the one holding its start
+//     (relaxed agent-scope atomics, as in the forward).  Lanes are channels and
+//     the states are split over the waves as in the forward.  Per tile every wave
 //     recomputes its states' 16 steps from the checkpoint into registers, then
 //     runs the gradient backwards in 4-step blocks.  Sums over states (for du,
 //     ddelta, dz) go through LDS to the threads that own the channel's row
@@ -60,10 +63,16 @@ struct BwdArgs {
   void* dz;
   float* dh0;
   float* dbc;          // [streams][2][8*SPW][L]: dB (0) and dC (1) summed over the stream's channels
-  float* dA_part;      // [streams][8*SPW][64]
-  float* dD_part;      // [streams][64][4]
-  int batch, dim, dstate, seqlen, ntiles, nblocks;
+  float* dA_part;      // [streams][2 pieces][8*SPW][64]
+  float* dD_part;      // [streams][2 pieces][64][4]
+  float* carry;        // [kMaxBwdWG][8][SPW][64]: dh entering the first tile of range g
+  int* flags;          // [kMaxBwdWG] carry ready; [kMaxBwdWG] spin-limit error; [kMaxBwdWG + 1] ticket
+  int* ticket;
+  int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
 };
+
+constexpr int kMaxBwdWG = 512;        // workgroups per launch at most
+constexpr int kBwdMaxSpins = 1 << 22;
 
 __device__ __forceinline__ float dsilu(float z) {  // d/dz of z*sigmoid(z)
   const float sg = rcp_fast(1.0f + exp2_fast(-z * kLog2e));
@@ -89,17 +98,28 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int L = a.seqlen, N = a.dstate, ntiles = a.ntiles;
-  const int s = blockIdx.x;  // stream: batch row b, channel block cb
+  const bool has_z = a.z != nullptr;
+  const int grp = w >> 2;
+  const int io_ch = (threadIdx.x & 255) >> 2, io_blk = threadIdx.x & 3;
+
+  // Logical range index in reverse start order (a ticket): a workgroup waits
+  // only for the one holding the next range, which has always started first.
+  __shared__ int sh_ticket;
+  if (threadIdx.x == 0) sh_ticket = atomicAdd(a.ticket, 1);
+  __syncthreads();
+  const int g = a.nwg - 1 - sh_ticket;
+
+  // One piece: stream s (batch row, 64-channel block), tiles [tb, te) in
+  // reverse.  dh enters at te from dh_last (te == ntiles) or from the next
+  // workgroup's carry slot g + 1, and leaves at tb to slot g when tb > 0.
+  auto run_piece = [&](int s, int tb, int te) __attribute__((always_inline)) {
   const int b = s / a.nblocks, cb = s % a.nblocks;
   const int c = cb * kLanes + lane;
   const bool cok = c < a.dim;
-  const bool has_z = a.z != nullptr;
 
   // I/O role: group 0 (waves 0-3) streams u and delta and writes du, ddelta;
   // group 1 (waves 4-7) streams z and dy and writes dz.  A thread owns channel
   // io_ch of the block and 4-step block io_blk of every tile.
-  const int grp = w >> 2;
-  const int io_ch = (threadIdx.x & 255) >> 2, io_blk = threadIdx.x & 3;
   const int c_io = cb * kLanes + io_ch;
   const bool iok = c_io < a.dim;
   const int nch = min(kLanes, a.dim - cb * kLanes);
@@ -123,10 +143,27 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
     const bool ok = cok && n < N;
     Aj[j] = ok ? a.A[(size_t)c * N + n] : 0.f;
     A2[j] = Aj[j] * kLog2e;
-    dh[j] = (ok && a.dh_last != nullptr) ? a.dh_last[((size_t)b * a.dim + c) * N + n] : 0.f;
+    dh[j] = (te == ntiles && ok && a.dh_last != nullptr) ? a.dh_last[((size_t)b * a.dim + c) * N + n] : 0.f;
     dA[j] = 0.f;
   }
   float dD = 0.f;
+  if (te < ntiles) {  // the gradient entering at te, from the workgroup holding [te, ...)
+    float* carry = a.carry + ((size_t)(g + 1) * kWaves + w) * SPW * kLanes;
+    if (threadIdx.x == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(a.flags + g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        __builtin_amdgcn_s_sleep(4);
+        if (++spins > kBwdMaxSpins) {  // never expected; keeps every wait finite
+          __hip_atomic_store(a.flags + kMaxBwdWG, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      dh[j] = __hip_atomic_load(carry + j * kLanes + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   const rsrc_t rbc = make_rsrc(a.bc + bc_index<SPW>(b, w, 0, ntiles, 0, 0, 0),
                                (uint32_t)ntiles * S::kPerTile * (uint32_t)sizeof(float));
@@ -137,7 +174,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   f32x4 bct[2][NV];
   float hck[2][SPW];
   auto load = [&](int k, int sl) {
-    const bool tok = k >= 0;
+    const bool tok = k >= tb;
     const int t = k * kTile + io_blk * 4;
     in0[sl] = load_raw4<BF16, VEC>(r_in0, io_off, t, L, iok && tok);
     in1[sl] = load_raw4<BF16, VEC>(r_in1, io_off, t, L, iok && tok);
@@ -146,7 +183,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
       const uint32_t off = tok ? (uint32_t)(((size_t)k * NV + v) * 64 + (lane & 15) * 4) * 4u : kOffNone;
       bct[sl][v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
     }
-    const int kc = tok ? k : 0;  // (a tile before the first is never used)
+    const int kc = tok ? k : tb;  // (a tile before the piece is never used)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) hck[sl][j] = ckpt[((size_t)kc * kWaves * SPW + j) * kLanes];
   };
@@ -285,23 +322,73 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
     __syncthreads();  // the next tile overwrites s_in
   };
 
-  load(ntiles - 1, 0);
-  load(ntiles - 2, 1);
-  int k = ntiles - 1;
-  for (; k >= 1; k -= 2) {
+  load(te - 1, 0);
+  load(te - 2, 1);
+  int k = te - 1;
+  for (; k >= tb + 1; k -= 2) {
     tile(k, std::integral_constant<int, 0>{});
     tile(k - 1, std::integral_constant<int, 1>{});
   }
-  if (k == 0) tile(0, std::integral_constant<int, 0>{});
+  if (k == tb) tile(tb, std::integral_constant<int, 0>{});
 
-  // Per-stream partial sums and the gradient of the initial state.
+  if (tb > 0) {  // publish the gradient entering tile tb for the workgroup holding [.., tb)
+    float* carry = a.carry + ((size_t)g * kWaves + w) * SPW * kLanes;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      __hip_atomic_store(carry + j * kLanes + lane, dh[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the carry stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(a.flags + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Partial sums of the piece (slot 0: the piece starting at tile 0, slot 1:
+  // the piece ending the stream; a whole stream zeroes slot 1) and the
+  // gradient of the initial state.
+  const int slot = tb == 0 ? 0 : 1;
+  const bool whole = tb == 0 && te == ntiles;
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int n = w * SPW + j;
-    a.dA_part[((size_t)s * Np + n) * kLanes + lane] = dA[j];
-    if (a.dh0 != nullptr && cok && n < N) a.dh0[((size_t)b * a.dim + c) * N + n] = dh[j];
+    a.dA_part[(((size_t)s * 2 + slot) * Np + n) * kLanes + lane] = dA[j];
+    if (whole) a.dA_part[(((size_t)s * 2 + 1) * Np + n) * kLanes + lane] = 0.f;
+    if (tb == 0 && a.dh0 != nullptr && cok && n < N) a.dh0[((size_t)b * a.dim + c) * N + n] = dh[j];
   }
-  if (grp == 0) a.dD_part[((size_t)s * kLanes + lane) * 4 + (w & 3)] = dD;
+  if (grp == 0) {
+    a.dD_part[(((size_t)s * 2 + slot) * kLanes + lane) * 4 + (w & 3)] = dD;
+    if (whole) a.dD_part[(((size_t)s * 2 + 1) * kLanes + lane) * 4 + (w & 3)] = 0.f;
+  }
+  };
+
+  // Balanced split as in the forward: range g holds tiles [g W/G, (g+1) W/G)
+  // of the concatenated streams (at least as many streams as workgroups, so a
+  // stream is cut at most once).  Run order: the end of its first stream
+  // (needs nothing, publishes at once), whole streams, then the start of its
+  // last stream (waits for range g + 1).
+  const int64_t nstreams = (int64_t)a.batch * a.nblocks;
+  const int64_t wtot = nstreams * ntiles;
+  const int64_t r0 = (int64_t)g * wtot / a.nwg, r1 = (int64_t)(g + 1) * wtot / a.nwg;
+  const int s_first = (int)(r0 / ntiles), s_last = (int)((r1 - 1) / ntiles);
+  const int off_first = (int)(r0 - (int64_t)s_first * ntiles);
+  const int end_last = (int)(r1 - (int64_t)s_last * ntiles);
+  const int npieces = s_last - s_first + 1;
+  for (int i = 0; i < npieces; ++i) {
+    int s, tb, te;
+    if (npieces == 1) {
+      s = s_first, tb = off_first, te = end_last;
+    } else if (i == 0) {
+      s = s_first, tb = off_first, te = ntiles;  // end of the first stream
+    } else if (i == npieces - 1) {
+      s = s_last, tb = 0, te = end_last;         // start of the last stream
+    } else {
+      s = s_first + i, tb = 0, te = ntiles;      // whole streams
+    }
+    run_piece(s, tb, te);
+  }
+}
+
+// Clears the backward's carry flags, error word and ticket.
+__global__ void __launch_bounds__(256) bwd_clear_kernel(int* flags, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) flags[i] = 0;
 }
 
 // dB, dC [b, N, L] = sums of the per-stream partials over the channel blocks;
@@ -334,7 +421,8 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
     const int d = (int)(r / N), n = (int)(r % N);
     float acc = 0.f;
     for (int b = 0; b < batch; ++b)
-      acc += dA_part[(((size_t)b * nblocks + d / kLanes) * Np + n) * kLanes + d % kLanes];
+      for (int sl = 0; sl < 2; ++sl)
+        acc += dA_part[((((size_t)b * nblocks + d / kLanes) * 2 + sl) * Np + n) * kLanes + d % kLanes];
     dA[r] = acc;
     return;
   }
@@ -342,16 +430,17 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
   if (dD != nullptr && r < dim) {
     const int d = (int)r;
     float acc = 0.f;
-    for (int b = 0; b < batch; ++b) {
-      const float* p = dD_part + (((size_t)b * nblocks + d / kLanes) * kLanes + d % kLanes) * 4;
-      acc += (p[0] + p[1]) + (p[2] + p[3]);
-    }
+    for (int b = 0; b < batch; ++b)
+      for (int sl = 0; sl < 2; ++sl) {
+        const float* p = dD_part + ((((size_t)b * nblocks + d / kLanes) * 2 + sl) * kLanes + d % kLanes) * 4;
+        acc += (p[0] + p[1]) + (p[2] + p[3]);
+      }
     dD[d] = acc;
   }
 }
 
 struct BwdLayout {
-  size_t fwd, ckpt, dbc, dA, dD, total;
+  size_t fwd, ckpt, dbc, dA, dD, carry, flags, total;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -362,9 +451,11 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen)
   l.fwd = align256(scan_workspace_bytes(batch, dim, dstate, seqlen));
   l.ckpt = align256((size_t)nstreams * num_tiles(seqlen) * np * kLanes * sizeof(float));
   l.dbc = align256((size_t)nstreams * 2 * np * seqlen * sizeof(float));
-  l.dA = align256((size_t)nstreams * np * kLanes * sizeof(float));
-  l.dD = align256((size_t)nstreams * kLanes * 4 * sizeof(float));
-  l.total = l.fwd + l.ckpt + l.dbc + l.dA + l.dD;
+  l.dA = align256((size_t)nstreams * 2 * np * kLanes * sizeof(float));
+  l.dD = align256((size_t)nstreams * 2 * kLanes * 4 * sizeof(float));
+  l.carry = align256((size_t)kMaxBwdWG * np * kLanes * sizeof(float));
+  l.flags = align256((size_t)(kMaxBwdWG + 2) * sizeof(int));
+  l.total = l.fwd + l.ckpt + l.dbc + l.dA + l.dD + l.carry + l.flags;
   return l;
 }
 
@@ -376,6 +467,8 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   float* dbc = reinterpret_cast<float*>(ws + l.fwd + l.ckpt);
   float* dA_part = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc);
   float* dD_part = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc + l.dA);
+  float* carry = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc + l.dA + l.dD);
+  int* flags = reinterpret_cast<int*>(ws + l.fwd + l.ckpt + l.dbc + l.dA + l.dD + l.carry);
 
   // 1. forward, state only: the checkpoints (and the B/C workspace at its start)
   ScanParams f = p.fwd;
@@ -385,9 +478,15 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   hipError_t err = launch_scan(f, stream);
   if (err != hipSuccess) return err;
 
-  // 2. backward, one workgroup per stream
+  // 2. backward: the streams' tiles split evenly over one workgroup per CU
   const int nblocks = (int)((p.fwd.dim + kLanes - 1) / kLanes);
   const int64_t nstreams = p.fwd.batch * nblocks;
+  int dev = 0, cus = 0;
+  err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const int nwg = (int)std::min<int64_t>(nstreams, std::min(std::max(cus, 1), kMaxBwdWG));
+  hipLaunchKernelGGL(bwd_clear_kernel, dim3(1), dim3(256), 0, stream, flags, kMaxBwdWG + 2);
   BwdArgs a;
   a.u = p.fwd.u;
   a.delta = p.fwd.delta;
@@ -405,6 +504,10 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   a.dbc = dbc;
   a.dA_part = dA_part;
   a.dD_part = dD_part;
+  a.carry = carry;
+  a.flags = flags;
+  a.ticket = flags + kMaxBwdWG + 1;
+  a.nwg = nwg;
   a.batch = (int)p.fwd.batch;
   a.dim = (int)p.fwd.dim;
   a.dstate = (int)p.fwd.dstate;
@@ -412,9 +515,9 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   a.ntiles = (int)num_tiles(p.fwd.seqlen);
   a.nblocks = nblocks;
   if (p.fwd.seqlen % 4 == 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, true>), dim3((unsigned)nstreams), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, true>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, false>), dim3((unsigned)nstreams), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, false>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
 
   // 3. fixed-order sums
   const int64_t total = 2 * p.fwd.batch * p.fwd.dstate * p.fwd.seqlen + p.fwd.dim * p.fwd.dstate + p.fwd.dim;
