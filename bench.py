@@ -221,6 +221,12 @@ def bench_scan_bwd(args, torch, mss, I, cfg):
     dy = to_dev(torch, dy_host)
     io_dt = g["u"].dtype
     b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    if args.seqlen or args.batch:
+        L, b = args.seqlen or L, args.batch or b
+        for k in ("u", "delta", "B", "C", "z"):
+            g[k] = along_l(torch, along_l(torch, g[k], L, 2), b, 0)
+        dy = along_l(torch, along_l(torch, dy, L, 2), b, 0)
+        torch.cuda.synchronize()
     ws = torch.empty(mss.selective_scan_bwd_workspace_size(b, d, n, L, io_dt), dtype=torch.uint8, device="cuda:0")
     out = mss.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], dy=dy, workspace=ws)
 
@@ -236,8 +242,10 @@ def bench_scan_bwd(args, torch, mss, I, cfg):
                                   f"{cfg.io} u/delta/B/C/z/dy and gradients, fp32 A/D/dA/dD/state",
                       "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io_dtype": cfg.io,
                       "gradients": "du, ddelta, dA, dB, dC, dD, dz"}}
+    if args.seqlen or args.batch:
+        res["config"]["inputs"] = f"the preset's b={cfg.batch} L={cfg.seqlen} draw repeated or cut along b and L"
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (args.seqlen or args.batch):
         import oracle
         f64 = lambda k: I.to_f64(x[k][:1], cfg.io)  # bounded sample: batch row 0, every channel, full L
         args64 = (f64("u"), f64("delta"), x["A"].astype(np.float64), f64("B"), f64("C"), x["D"].astype(np.float64),
@@ -350,7 +358,7 @@ def main():
               "the hot path shards over batch and channels with no communication, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
     if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and
-                                             args.workload in ("decode_2p8b", "copy", "scan_2p8b_bwd")):
+                                             args.workload in ("decode_2p8b", "copy")):
         print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
               file=sys.stderr)
         sys.exit(2)

@@ -69,10 +69,15 @@ struct BwdArgs {
   int* flags;          // [kMaxBwdWG] carry ready; [kMaxBwdWG] spin-limit error; [kMaxBwdWG + 1] ticket
   int* ticket;
   int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
+  float* hloc;         // split passes: [kMaxBwdWG][8][SPW][64] zero-end gradient at the start of range g's first piece
+  float* dsum;         // split passes: [kMaxBwdWG][64][4] partial sums of delta over that piece
+  int split;           // carries precomputed by the local pass and the chain (no waits, no publishing);
+                       // dA, dD partials per (workgroup, piece) instead of per (stream, part)
 };
 
 constexpr int kMaxBwdWG = 512;        // workgroups per launch at most
 constexpr int kBwdMaxSpins = 1 << 22;
+constexpr int kBwdMinPieceTiles = 8;  // split passes only while pieces keep this many tiles
 
 __device__ __forceinline__ float dsilu(float z) {  // d/dz of z*sigmoid(z)
   const float sg = rcp_fast(1.0f + exp2_fast(-z * kLog2e));
@@ -109,10 +114,26 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   __syncthreads();
   const int g = a.nwg - 1 - sh_ticket;
 
+  // Balanced split as in the forward: range g holds tiles [g W/G, (g+1) W/G)
+  // of the concatenated streams.  In the single pass (at least as many
+  // streams as workgroups) a stream is cut at most once; in the split passes
+  // (fewer streams than workgroups) a range holds at most two pieces.  Run order: the
+  // end of its first stream (needs nothing in the single pass, publishes at
+  // once), whole streams, then the start of its last stream (waits for range
+  // g + 1 in the single pass).
+  const int64_t nstreams = (int64_t)a.batch * a.nblocks;
+  const int64_t wtot = nstreams * ntiles;
+  const int64_t r0 = (int64_t)g * wtot / a.nwg, r1 = (int64_t)(g + 1) * wtot / a.nwg;
+  const int s_first = (int)(r0 / ntiles), s_last = (int)((r1 - 1) / ntiles);
+  const int off_first = (int)(r0 - (int64_t)s_first * ntiles);
+  const int end_last = (int)(r1 - (int64_t)s_last * ntiles);
+  const int npieces = s_last - s_first + 1;
+  const int npieces_g = npieces;
+
   // One piece: stream s (batch row, 64-channel block), tiles [tb, te) in
   // reverse.  dh enters at te from dh_last (te == ntiles) or from the next
   // workgroup's carry slot g + 1, and leaves at tb to slot g when tb > 0.
-  auto run_piece = [&](int s, int tb, int te) __attribute__((always_inline)) {
+  auto run_piece = [&](int s, int tb, int te, int piece) __attribute__((always_inline)) {
   const int b = s / a.nblocks, cb = s % a.nblocks;
   const int c = cb * kLanes + lane;
   const bool cok = c < a.dim;
@@ -149,7 +170,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   float dD = 0.f;
   if (te < ntiles) {  // the gradient entering at te, from the workgroup holding [te, ...)
     float* carry = a.carry + ((size_t)(g + 1) * kWaves + w) * SPW * kLanes;
-    if (threadIdx.x == 0) {
+    if (!a.split && threadIdx.x == 0) {
       int spins = 0;
       while (__hip_atomic_load(a.flags + g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
         __builtin_amdgcn_s_sleep(4);
@@ -331,7 +352,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
   }
   if (k == tb) tile(tb, std::integral_constant<int, 0>{});
 
-  if (tb > 0) {  // publish the gradient entering tile tb for the workgroup holding [.., tb)
+  if (!a.split && tb > 0) {  // publish the gradient entering tile tb for the workgroup holding [.., tb)
     float* carry = a.carry + ((size_t)g * kWaves + w) * SPW * kLanes;
 #pragma unroll
     for (int j = 0; j < SPW; ++j)
@@ -341,36 +362,27 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
     if (threadIdx.x == 0) __hip_atomic_store(a.flags + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // Partial sums of the piece (slot 0: the piece starting at tile 0, slot 1:
-  // the piece ending the stream; a whole stream zeroes slot 1) and the
-  // gradient of the initial state.
-  const int slot = tb == 0 ? 0 : 1;
-  const bool whole = tb == 0 && te == ntiles;
+  // Partial sums of the piece and the gradient of the initial state.  Slots:
+  // per (stream, part) in the single pass (part 0: the piece starting at tile
+  // 0, part 1: the piece ending the stream; a whole stream zeroes part 1);
+  // per (workgroup, piece) in the split passes (a range holds at most two
+  // pieces there; a lone piece zeroes the second slot).
+  const int slot = a.split ? g * 2 + piece : s * 2 + (tb == 0 ? 0 : 1);
+  const int zslot = a.split ? g * 2 + 1 : s * 2 + 1;
+  const bool whole = a.split ? npieces_g == 1 : (tb == 0 && te == ntiles);
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int n = w * SPW + j;
-    a.dA_part[(((size_t)s * 2 + slot) * Np + n) * kLanes + lane] = dA[j];
-    if (whole) a.dA_part[(((size_t)s * 2 + 1) * Np + n) * kLanes + lane] = 0.f;
+    a.dA_part[((size_t)slot * Np + n) * kLanes + lane] = dA[j];
+    if (whole) a.dA_part[((size_t)zslot * Np + n) * kLanes + lane] = 0.f;
     if (tb == 0 && a.dh0 != nullptr && cok && n < N) a.dh0[((size_t)b * a.dim + c) * N + n] = dh[j];
   }
   if (grp == 0) {
-    a.dD_part[(((size_t)s * 2 + slot) * kLanes + lane) * 4 + (w & 3)] = dD;
-    if (whole) a.dD_part[(((size_t)s * 2 + 1) * kLanes + lane) * 4 + (w & 3)] = 0.f;
+    a.dD_part[((size_t)slot * kLanes + lane) * 4 + (w & 3)] = dD;
+    if (whole) a.dD_part[((size_t)zslot * kLanes + lane) * 4 + (w & 3)] = 0.f;
   }
   };
 
-  // Balanced split as in the forward: range g holds tiles [g W/G, (g+1) W/G)
-  // of the concatenated streams (at least as many streams as workgroups, so a
-  // stream is cut at most once).  Run order: the end of its first stream
-  // (needs nothing, publishes at once), whole streams, then the start of its
-  // last stream (waits for range g + 1).
-  const int64_t nstreams = (int64_t)a.batch * a.nblocks;
-  const int64_t wtot = nstreams * ntiles;
-  const int64_t r0 = (int64_t)g * wtot / a.nwg, r1 = (int64_t)(g + 1) * wtot / a.nwg;
-  const int s_first = (int)(r0 / ntiles), s_last = (int)((r1 - 1) / ntiles);
-  const int off_first = (int)(r0 - (int64_t)s_first * ntiles);
-  const int end_last = (int)(r1 - (int64_t)s_last * ntiles);
-  const int npieces = s_last - s_first + 1;
   for (int i = 0; i < npieces; ++i) {
     int s, tb, te;
     if (npieces == 1) {
@@ -382,7 +394,147 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
     } else {
       s = s_first + i, tb = 0, te = ntiles;      // whole streams
     }
-    run_piece(s, tb, te);
+    run_piece(s, tb, te, i);
+  }
+}
+
+// Split passes, local part: for range g whose first piece starts inside a
+// stream, the gradient of the state at that start when the gradient entering
+// at the piece's end is zero (only dh += C dout, dh *= a: no states needed),
+// and the sum of delta over the piece.  Same thread roles and register
+// prefetch as scan_bwd_kernel; two barriers per tile.
+template <bool BF16, int SPW, bool VEC>
+__global__ void __launch_bounds__(kBwdThreads) scan_bwd_local_kernel(BwdArgs a) {
+  using S = BCShape<SPW>;
+  constexpr int NV = S::kNV;
+  constexpr uint32_t es = BF16 ? 2 : 4;
+  __shared__ __attribute__((aligned(16))) float s_dl[kTile][kInPad];
+  __shared__ __attribute__((aligned(16))) float s_do[kTile][kInPad];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = a.seqlen, N = a.dstate, ntiles = a.ntiles;
+  const int grp = w >> 2;
+  const int io_ch = (threadIdx.x & 255) >> 2, io_blk = threadIdx.x & 3;
+  const int g = blockIdx.x;
+  const int64_t nstreams = (int64_t)a.batch * a.nblocks;
+  const int64_t wtot = nstreams * ntiles;
+  const int64_t r0 = (int64_t)g * wtot / a.nwg, r1 = (int64_t)(g + 1) * wtot / a.nwg;
+  const int s = (int)(r0 / ntiles), s_last = (int)((r1 - 1) / ntiles);
+  const int tb = (int)(r0 - (int64_t)s * ntiles);
+  if (tb == 0) return;  // the range starts a stream: nothing enters from its left (uniform)
+  const int te = s_last == s ? (int)(r1 - (int64_t)s_last * ntiles) : ntiles;
+
+  const int b = s / a.nblocks, cb = s % a.nblocks;
+  const int c = cb * kLanes + lane;
+  const bool cok = c < a.dim;
+  const int c_io = cb * kLanes + io_ch;
+  const bool iok = c_io < a.dim;
+  const bool has_z = a.z != nullptr;
+  const int nch = min(kLanes, a.dim - cb * kLanes);
+  const size_t base_el = ((size_t)b * a.dim + (size_t)cb * kLanes) * (size_t)L;
+  const uint32_t rows_bytes = (uint32_t)nch * (uint32_t)L * es;
+  const uint32_t io_off = (uint32_t)io_ch * (uint32_t)L * es;
+  auto rsrc_of = [&](const void* p) {
+    return make_rsrc(p != nullptr ? static_cast<const char*>(p) + base_el * es : nullptr, p != nullptr ? rows_bytes : 0u);
+  };
+  const rsrc_t r_in0 = rsrc_of(grp == 0 ? a.delta : a.z);
+  const rsrc_t r_in1 = rsrc_of(grp == 0 ? nullptr : a.dy);
+  float A2[SPW], dh[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int n = w * SPW + j;
+    A2[j] = (cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
+    dh[j] = 0.f;
+  }
+  float dacc = 0.f;
+  const rsrc_t rbc = make_rsrc(a.bc + bc_index<SPW>(b, w, 0, ntiles, 0, 0, 0),
+                               (uint32_t)ntiles * S::kPerTile * (uint32_t)sizeof(float));
+  Raw4<BF16> in0[2], in1[2];
+  f32x4 bct[2][NV];
+  auto load = [&](int k, int sl) {
+    const bool tok = k >= tb;
+    const int t = k * kTile + io_blk * 4;
+    in0[sl] = load_raw4<BF16, VEC>(r_in0, io_off, t, L, iok && tok);
+    in1[sl] = load_raw4<BF16, VEC>(r_in1, io_off, t, L, iok && tok);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const uint32_t off = tok ? (uint32_t)(((size_t)k * NV + v) * 64 + (lane & 15) * 4) * 4u : kOffNone;
+      bct[sl][v] = __builtin_bit_cast(f32x4, buf_load_u32x4(rbc, off));
+    }
+  };
+  auto tile = [&](int k, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int Sl = decltype(slot_tag)::value;
+    const f32x4 v0 = decode4(in0[Sl]);  // delta (group 0) or z (group 1)
+    const f32x4 v1 = decode4(in1[Sl]);  // (unused) or dy
+    f32x4 bc_cur[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) bc_cur[v] = bct[Sl][v];
+    load(k - 2, Sl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (grp == 0) s_dl[io_blk * 4 + i][io_ch] = v0[i];
+      else s_do[io_blk * 4 + i][io_ch] = has_z ? v1[i] * silu(v0[i]) : v1[i];
+    }
+    if (grp == 0) dacc += (v0[0] + v0[1]) + (v0[2] + v0[3]);  // zero past L
+    __syncthreads();
+#pragma unroll
+    for (int t = kTile - 1; t >= 0; --t) {
+      const int blk = t / 4, kk = t % 4;
+      const float dout = s_do[t][lane], dl = s_dl[t][lane];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int ic = kk * 2 * SPW + j + SPW;  // C of state j at step kk
+        dh[j] = fmac_row_bcast_rt(dh[j], bc_cur[ic / 16][blk], dout, ic % 16);
+        dh[j] *= exp2_fast(dl * A2[j]);
+      }
+    }
+    __syncthreads();
+  };
+  load(te - 1, 0);
+  load(te - 2, 1);
+  int k = te - 1;
+  for (; k >= tb + 1; k -= 2) {
+    tile(k, std::integral_constant<int, 0>{});
+    tile(k - 1, std::integral_constant<int, 1>{});
+  }
+  if (k == tb) tile(tb, std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) a.hloc[(((size_t)g * kWaves + w) * SPW + j) * kLanes + lane] = dh[j];
+  if (grp == 0) a.dsum[((size_t)g * kLanes + io_ch) * 4 + io_blk] = dacc;
+}
+
+// Split passes, chain: for every stream walk its piece starts from right to
+// left, g <- hloc + exp2(A log2e sum delta) * g starting from dh_last (or
+// zero): the exact gradient at each piece start, written to the carry slot the
+// workgroup holding the piece to its left reads.  One thread per (stream,
+// state, channel).
+template <int SPW>
+__global__ void __launch_bounds__(256) bwd_combine_kernel(const float* __restrict__ hloc,
+                                                          const float* __restrict__ dsum, const float* __restrict__ A,
+                                                          const float* __restrict__ dh_last, float* __restrict__ carry,
+                                                          int batch, int dim, int N, int ntiles, int nblocks, int nwg) {
+  const int64_t nstreams = (int64_t)batch * nblocks;
+  const int Np = kWaves * SPW;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= nstreams * Np * kLanes) return;
+  const int c = (int)(idx % kLanes);
+  const int n = (int)((idx / kLanes) % Np);
+  const int64_t s = idx / ((int64_t)kLanes * Np);
+  const int b = (int)(s / nblocks), cg = (int)(s % nblocks) * kLanes + c;
+  const bool ok = cg < dim && n < N;
+  const float a2 = ok ? A[(size_t)cg * N + n] * kLog2e : 0.f;
+  float gr = (ok && dh_last != nullptr) ? dh_last[((size_t)b * dim + cg) * N + n] : 0.f;
+  const int64_t wtot = nstreams * ntiles, s0 = s * ntiles, s1 = s0 + ntiles;
+  const int w = n / SPW, j = n % SPW;
+  for (int gg = (int)min<int64_t>(nwg - 1, s1 * nwg / wtot + 1); gg >= 1; --gg) {
+    const int64_t r0 = (int64_t)gg * wtot / nwg;  // start of range gg
+    if (r0 >= s1) continue;
+    if (r0 <= s0) break;
+    const float* ds = dsum + ((size_t)gg * kLanes + c) * 4;
+    const float sd = (ds[0] + ds[1]) + (ds[2] + ds[3]);
+    const size_t k = (((size_t)gg * kWaves + w) * SPW + j) * kLanes + c;
+    gr = __builtin_fmaf(exp2f(a2 * sd), gr, hloc[k]);
+    carry[k] = gr;
   }
 }
 
@@ -391,14 +543,35 @@ __global__ void __launch_bounds__(256) bwd_clear_kernel(int* flags, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) flags[i] = 0;
 }
 
+// Partial-sum slots holding stream s's pieces: (s, part 0..1) in the single
+// pass; in the split passes (range g, piece 0 or 1) for every range that
+// covers s, piece 0 when s is the range's first stream.  Calls f(slot).
+template <typename F>
+__device__ __forceinline__ void for_stream_slots(int64_t s, int split, int64_t nstreams, int ntiles, int nwg, F&& f) {
+  if (!split) {
+    f(s * 2);
+    f(s * 2 + 1);
+    return;
+  }
+  const int64_t wtot = nstreams * ntiles, s0 = s * ntiles, s1 = s0 + ntiles;
+  for (int64_t gg = max<int64_t>(0, s0 * nwg / wtot - 1); gg < nwg; ++gg) {
+    const int64_t r0 = gg * wtot / nwg, r1 = (gg + 1) * wtot / nwg;
+    if (r1 <= s0) continue;
+    if (r0 >= s1) break;
+    f(gg * 2 + (r0 / ntiles == s ? 0 : 1));
+  }
+}
+
 // dB, dC [b, N, L] = sums of the per-stream partials over the channel blocks;
-// dA [d, N] and dD [d] = sums over the batch rows; fixed order.  One thread per
-// output element; index ranges: dB, then dC, then dA, then dD.
+// dA [d, N] and dD [d] = sums over the batch rows and stream pieces; fixed
+// order.  One thread per output element; index ranges: dB, then dC, then dA,
+// then dD.
 template <bool BF16, int SPW>
 __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict__ dbc, const float* __restrict__ dA_part,
                                                          const float* __restrict__ dD_part, void* dB, void* dC,
                                                          float* __restrict__ dA, float* __restrict__ dD, int batch,
-                                                         int dim, int N, int L, int nblocks) {
+                                                         int dim, int N, int L, int nblocks, int ntiles, int nwg,
+                                                         int split) {
   constexpr int Np = kWaves * SPW;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nbc = (int64_t)batch * N * L;
@@ -420,9 +593,11 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
   if (r < (int64_t)dim * N) {
     const int d = (int)(r / N), n = (int)(r % N);
     float acc = 0.f;
+    const int64_t nstreams = (int64_t)batch * nblocks;
     for (int b = 0; b < batch; ++b)
-      for (int sl = 0; sl < 2; ++sl)
-        acc += dA_part[((((size_t)b * nblocks + d / kLanes) * 2 + sl) * Np + n) * kLanes + d % kLanes];
+      for_stream_slots((int64_t)b * nblocks + d / kLanes, split, nstreams, ntiles, nwg, [&](int64_t sl) {
+        acc += dA_part[((size_t)sl * Np + n) * kLanes + d % kLanes];
+      });
     dA[r] = acc;
     return;
   }
@@ -430,17 +605,18 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
   if (dD != nullptr && r < dim) {
     const int d = (int)r;
     float acc = 0.f;
+    const int64_t nstreams = (int64_t)batch * nblocks;
     for (int b = 0; b < batch; ++b)
-      for (int sl = 0; sl < 2; ++sl) {
-        const float* p = dD_part + ((((size_t)b * nblocks + d / kLanes) * 2 + sl) * kLanes + d % kLanes) * 4;
+      for_stream_slots((int64_t)b * nblocks + d / kLanes, split, nstreams, ntiles, nwg, [&](int64_t sl) {
+        const float* p = dD_part + ((size_t)sl * kLanes + d % kLanes) * 4;
         acc += (p[0] + p[1]) + (p[2] + p[3]);
-      }
+      });
     dD[d] = acc;
   }
 }
 
 struct BwdLayout {
-  size_t fwd, ckpt, dbc, dA, dD, carry, flags, total;
+  size_t fwd, ckpt, dbc, dA, dD, carry, hloc, dsum, flags, total;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -451,11 +627,14 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen)
   l.fwd = align256(scan_workspace_bytes(batch, dim, dstate, seqlen));
   l.ckpt = align256((size_t)nstreams * num_tiles(seqlen) * np * kLanes * sizeof(float));
   l.dbc = align256((size_t)nstreams * 2 * np * seqlen * sizeof(float));
-  l.dA = align256((size_t)nstreams * 2 * np * kLanes * sizeof(float));
-  l.dD = align256((size_t)nstreams * 2 * kLanes * 4 * sizeof(float));
+  const int64_t slots = 2 * std::max<int64_t>(nstreams, kMaxBwdWG);  // per (stream, part) or (range, piece)
+  l.dA = align256((size_t)slots * np * kLanes * sizeof(float));
+  l.dD = align256((size_t)slots * kLanes * 4 * sizeof(float));
   l.carry = align256((size_t)kMaxBwdWG * np * kLanes * sizeof(float));
+  l.hloc = l.carry;
+  l.dsum = align256((size_t)kMaxBwdWG * kLanes * 4 * sizeof(float));
   l.flags = align256((size_t)(kMaxBwdWG + 2) * sizeof(int));
-  l.total = l.fwd + l.ckpt + l.dbc + l.dA + l.dD + l.carry + l.flags;
+  l.total = l.fwd + l.ckpt + l.dbc + l.dA + l.dD + l.carry + l.hloc + l.dsum + l.flags;
   return l;
 }
 
@@ -467,8 +646,11 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   float* dbc = reinterpret_cast<float*>(ws + l.fwd + l.ckpt);
   float* dA_part = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc);
   float* dD_part = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc + l.dA);
-  float* carry = reinterpret_cast<float*>(ws + l.fwd + l.ckpt + l.dbc + l.dA + l.dD);
-  int* flags = reinterpret_cast<int*>(ws + l.fwd + l.ckpt + l.dbc + l.dA + l.dD + l.carry);
+  char* tail = ws + l.fwd + l.ckpt + l.dbc + l.dA + l.dD;
+  float* carry = reinterpret_cast<float*>(tail);
+  float* hloc = reinterpret_cast<float*>(tail + l.carry);
+  float* dsum = reinterpret_cast<float*>(tail + l.carry + l.hloc);
+  int* flags = reinterpret_cast<int*>(tail + l.carry + l.hloc + l.dsum);
 
   // 1. forward, state only: the checkpoints (and the B/C workspace at its start)
   ScanParams f = p.fwd;
@@ -485,7 +667,14 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  const int nwg = (int)std::min<int64_t>(nstreams, std::min(std::max(cus, 1), kMaxBwdWG));
+  const int cap = std::min(std::max(cus, 1), kMaxBwdWG);
+  const int64_t ntiles = num_tiles(p.fwd.seqlen);
+  // Fewer streams than ~4/5 of the workgroups: cut them over all CUs (local
+  // pass, chain, final pass).  The local pass (the adjoint alone) costs a
+  // fraction of the final one, so this pays from there on; with fewer streams
+  // than workgroups a range holds at most two pieces.
+  const bool split = nstreams * 5 < (int64_t)cap * 4 && nstreams * ntiles >= (int64_t)cap * kBwdMinPieceTiles;
+  const int nwg = split ? cap : (int)std::min<int64_t>(nstreams, cap);
   hipLaunchKernelGGL(bwd_clear_kernel, dim3(1), dim3(256), 0, stream, flags, kMaxBwdWG + 2);
   BwdArgs a;
   a.u = p.fwd.u;
@@ -505,6 +694,9 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   a.dA_part = dA_part;
   a.dD_part = dD_part;
   a.carry = carry;
+  a.hloc = hloc;
+  a.dsum = dsum;
+  a.split = split ? 1 : 0;
   a.flags = flags;
   a.ticket = flags + kMaxBwdWG + 1;
   a.nwg = nwg;
@@ -514,6 +706,16 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   a.seqlen = (int)p.fwd.seqlen;
   a.ntiles = (int)num_tiles(p.fwd.seqlen);
   a.nblocks = nblocks;
+  if (split) {
+    if (p.fwd.seqlen % 4 == 0)
+      hipLaunchKernelGGL((scan_bwd_local_kernel<BF16, SPW, true>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((scan_bwd_local_kernel<BF16, SPW, false>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
+    const int64_t threads = nstreams * kWaves * SPW * kLanes;
+    hipLaunchKernelGGL((bwd_combine_kernel<SPW>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, hloc,
+                       dsum, p.fwd.A, p.dh_last, carry, (int)p.fwd.batch, (int)p.fwd.dim, (int)p.fwd.dstate,
+                       (int)ntiles, nblocks, nwg);
+  }
   if (p.fwd.seqlen % 4 == 0)
     hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, true>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
   else
@@ -523,7 +725,7 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   const int64_t total = 2 * p.fwd.batch * p.fwd.dstate * p.fwd.seqlen + p.fwd.dim * p.fwd.dstate + p.fwd.dim;
   hipLaunchKernelGGL((bwd_reduce_kernel<BF16, SPW>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, dbc,
                      dA_part, dD_part, p.dB, p.dC, p.dA, p.dD, (int)p.fwd.batch, (int)p.fwd.dim, (int)p.fwd.dstate,
-                     (int)p.fwd.seqlen, nblocks);
+                     (int)p.fwd.seqlen, nblocks, (int)ntiles, nwg, split ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -118,11 +118,16 @@ def test_scan_bwd_general_a(force_general):
     check(run_gpu_bwd(x, dy, dhl, force_general=force_general), run_oracle_bwd(x, dy, dhl), "fp32")
 
 
-@pytest.mark.parametrize("shape", [(2, 12800, 16, 45, "bf16"), (1, 128, 16, 16384, "fp32")],
-                         ids=["carry_handoff", "split_passes"])
+@pytest.mark.parametrize("shape", [(2, 12800, 16, 45, "bf16"), (1, 128, 16, 16384, "fp32"),
+                                   (1, 5120, 16, 4096, "bf16"), (2, 100, 16, 20001, "fp32"),
+                                   (1, 64, 4, 9000, "fp32"), (2, 10240, 16, 257, "bf16")],
+                         ids=["carry_handoff", "split_passes", "split_b1_layer", "split_ragged", "split_spw1",
+                              "split_two_pieces_per_range"])
 def test_scan_bwd_checkpoint_paths(shape):
-    """The checkpoint forward with more streams than CUs (carries handed between
-    workgroups) and with few long sequences (split passes)."""
+    """More streams than CUs (the backward's gradient and the forward's state
+    handed between workgroups), and few long sequences (both cut over all CUs:
+    the forward's split passes, and the backward's local adjoint pass, chain
+    and final pass with per-workgroup partial sums)."""
     b, d, n, L, io = shape
     x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
     dy, dhl = grads_inputs(x)
