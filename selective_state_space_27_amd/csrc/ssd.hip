@@ -268,10 +268,12 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const uint32_t bo0 = (uint32_t)jx * b_row + (uint32_t)((g * kN + ng * 8) * 2), bo1 = bo0 + b_row;
   const uint32_t dlo = (uint32_t)jx * 4u;
   const size_t row_bh = ((size_t)b * a.H + h) * a.Lp;
-  typedef __attribute__((address_space(4))) const float scalar_float;  // uniform loads through the scalar cache
 
   // Loads of one block: x and the delta rows (from HBM) four blocks ahead of
   // their staging, B (shared by every head, so mostly an L2 hit) two ahead.
+  // All of them are vector loads, waited for through vmcnt in issue order: a
+  // scalar-cache load would share lgkmcnt with the LDS traffic, and the
+  // lgkmcnt(0) in front of every barrier would wait for it right away.
   struct XSlot {
     uint32_t xr[2];
     u32x2 dl, ls;
@@ -290,8 +292,10 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     sl.xr[1] = buf_load_u32(rx, xo1);
     sl.dl = buf_load_u32x2(rd, dlo);
     sl.ls = buf_load_u32x2(rl, dlo);
-    // Prefix sum at the block's last step (blocks past the end read the last block's).
-    sl.last = ((scalar_float*)(a.lsT + row_bh))[min(l0, a.Lp - kSub) + kSub - 1];
+    // Prefix sum at the block's last step, the same address in every lane
+    // (blocks past the padded rows read 0; they are staged as zeros and their
+    // decay is never applied).
+    sl.last = __uint_as_float(buf_load_u32(rl, (uint32_t)(kSub - 1) * 4u));
   };
   auto load_b = [&](int blk, BSlot& sl) {
     const int l0 = blk * kSub;
@@ -371,8 +375,8 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   load_b(1, bring[1]);
   stage(xring[0], bring[0], 0);
   float decay = exp2_fast(xring[0].last);  // exp(s_last) of the block being multiplied
-  load_x(4, xring[0]);
   load_b(2, bring[0]);
+  load_x(4, xring[0]);
   __syncthreads();
 
   auto step = [&](auto x_tag, auto b_tag, int sb) {
@@ -394,8 +398,14 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     }
     stage(xring[SX], bring[SB], buf ^ 1);
     decay = exp2_fast(xring[SX].last);
-    load_x(sb + 5, xring[SX]);
+    // Every read of the two slots happens before their next loads are issued,
+    // so the loads can land in the same registers: otherwise the unrolled
+    // loop ends in register copies that wait for loads still in flight.
+    asm volatile("" ::"v"(decay) : "memory");
+    // B first: loads return in issue order, so the wait for this B two steps
+    // from now covers only the x loads issued before it (three steps old).
     load_b(sb + 3, bring[SB]);
+    load_x(sb + 5, xring[SX]);
     const bool chunk_end = (sb % sub_per_chunk == sub_per_chunk - 1) || sb == nsub - 1;
     if (chunk_end && a.chunk_states)
       write_state(a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
