@@ -36,6 +36,7 @@
 // decay-weighted diagonal block, x scaled by the decay weights) enters as a
 // bf16 hi/lo pair (two products), keeping ~16 bits of mantissa.  Operands the
 // matrix cores read along time (x and B) are staged transposed in LDS.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -115,11 +116,17 @@ struct SSDArgs {
   float* y;            // [b, L, H, P]
   float* chunk_states; // [b, nchunks, H, P, N] or null
   float* h_last;       // [b, H, P, N] or null
-  float* s_in;         // workspace [b, nchunks, H, P, N]: state entering each chunk
+  float* s_in;         // workspace [b, nchunks, H, P, N]: state entering each chunk, from its piece's start
   float* dlT;          // workspace [b, H, Lp]: delta, head-major (0 past L)
   float* lsT;          // workspace [b, H, Lp]: A log2(e) times the prefix sum of delta inside each 64-step block
+  float* pend;         // workspace [b, H, npieces, P, N]: state at the end of each piece, from the piece's start
+  float* pstart;       // workspace [b, H, npieces, P, N]: exact state entering each piece (pieces 1..)
+  float* cdec;         // workspace [b, H, nchunks]: A log2(e) sum of delta from the chunk's piece's start to the chunk
+  float* pdec;         // workspace [b, H, npieces]: the same over each whole piece
   int batch, L, H, G, Q, nchunks, Lp;
+  int npieces, cpp;    // the sequence is cut into npieces pieces of cpp chunks (the last may be shorter)
 };
+
 
 // x plus lane (lane - S) of its 16-lane row (0 for the first S lanes of a row).
 template <int S>
@@ -223,9 +230,25 @@ __device__ __forceinline__ void load_stateT(f32x16& acc, const float* S, int nt,
   }
 }
 
+// The inverse: a 32x32 tile of S^T written back to a [P][N] fp32 state.
+__device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt, int pt) {
+  const int lane = threadIdx.x & 63;
+  const int p = pt * 32 + (lane & 31);
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int n = nt * 32 + 8 * g4 + 4 * (lane >> 5);
+    *reinterpret_cast<f32x4*>(&S[(size_t)p * kN + n]) =
+        f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Chunk states.  grid (2H, batch), 512 threads: workgroup (b, h, pt) owns
-// headdim tile pt.  Wave w owns S^T rows (w&3)*32.. over half of every block's
+// Chunk states.  grid (2H, batch, npieces), 512 threads: workgroup (b, h, pt,
+// piece) owns headdim tile pt over the chunks of one piece of the sequence and
+// runs them from a zero state (piece 0 from h0); ssd_chain_kernel then makes
+// the exact state entering each piece, which the scan kernel adds, decayed,
+// to the state entering each of its chunks.  Cutting the sequence keeps every
+// CU equally busy (2H x batch streams alone would leave some CUs with two).  Wave w owns S^T rows (w&3)*32.. over half of every block's
 // steps (k-half w>>2): the state is the sum of the two halves' partial states,
 // which decay alike, so they are only added where a state is written out.
 // Each thread forms the decay weights of its own steps from the head-major
@@ -250,11 +273,18 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const int pt = pair ? (i >> 3) & 1 : i & 1;
   const int h = pair ? ((i >> 4) << 3) | (i & 7) : i >> 1;
   const int b = blockIdx.y;
+  const int piece = blockIdx.z;
   const int g = h / (a.H / a.G);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lc = lane & 31, hf = lane >> 5;
   const int nt = w & 3, kh = w >> 2;
   const size_t state_stride = (size_t)kP * kN;
+  // This piece's chunks [c0, c1) and 64-step blocks [sb0, sb1).
+  const int sub_per_chunk = a.Q / kSub;
+  const int nsub = (a.L + kSub - 1) / kSub;
+  const int c0 = piece * a.cpp;
+  const int sb0 = c0 * sub_per_chunk;
+  const int sb1 = min(nsub, min(a.nchunks, c0 + a.cpp) * sub_per_chunk);
 
   // Staging map: thread -> step pair (jx, jx+1); headdim values pq*2, pq*2+1
   // of x, states ng*8 .. ng*8+7 of B.
@@ -324,9 +354,10 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     }
   };
 
-  // The state is the sum of both k-halves' partials: k-half 0 starts from h0.
+  // The state is the sum of both k-halves' partials: k-half 0 of piece 0
+  // starts from h0, everything else from zero.
   f32x16 st;
-  load_stateT(st, (a.h0 && kh == 0) ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, nt, pt);
+  load_stateT(st, (a.h0 && kh == 0 && piece == 0) ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, nt, pt);
   // Writes the full state slice (rows pt*32.., all n) of a [P][N] state: k-half
   // 1 puts its partial in LDS, k-half 0 adds its own, then the workgroup
   // copies the 16 KB slice out with whole-row stores.
@@ -360,33 +391,44 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     __syncthreads();
   };
 
-  const int sub_per_chunk = a.Q / kSub;
-  const int nsub = (a.L + kSub - 1) / kSub;
-  // Software pipeline: iteration sb runs block sb's products from staging
-  // buffer sb&1 while it stages block sb+1 into the other buffer (whose last
-  // readers finished before the previous barrier), one barrier per block.
-  // Block sb+1 sits in x slot (sb+1)%4 and B slot (sb+1)%2 (loop unrolled by
-  // four so the slots are compile-time constants).
+  // Software pipeline: iteration rel runs block sb0+rel's products from
+  // staging buffer rel&1 while it stages the next block into the other buffer
+  // (whose last readers finished before the previous barrier), one barrier
+  // per block.  The next block sits in x slot (rel+1)%4 and B slot (rel+1)%2
+  // (loop unrolled by four so the slots are compile-time constants).  Loads
+  // that run past the piece read the next piece's steps (or zeros past the
+  // end) and are never multiplied.
   XSlot xring[4];
   BSlot bring[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) load_x(k, xring[k]);
-  load_b(0, bring[0]);
-  load_b(1, bring[1]);
+  for (int k = 0; k < 4; ++k) load_x(sb0 + k, xring[k]);
+  load_b(sb0, bring[0]);
+  load_b(sb0 + 1, bring[1]);
   stage(xring[0], bring[0], 0);
-  float decay = exp2_fast(xring[0].last);  // exp(s_last) of the block being multiplied
-  load_b(2, bring[0]);
-  load_x(4, xring[0]);
+  float lcur = xring[0].last;  // s_last (log2 units) of the block being multiplied
+  float lsum = 0.f;            // the same summed over the piece's earlier blocks
+  // Chunk and piece decays for the scan and chain kernels (uniform values;
+  // one thread of one headdim tile writes them).
+  const bool dec_writer = threadIdx.x == 0 && pt == 0;
+  float* const cdec_row = a.cdec + ((size_t)b * a.H + h) * a.nchunks;
+  load_b(sb0 + 2, bring[0]);
+  load_x(sb0 + 4, xring[0]);
   __syncthreads();
 
-  auto step = [&](auto x_tag, auto b_tag, int sb) {
-    constexpr int SX = decltype(x_tag)::value;  // (sb + 1) % 4
-    constexpr int SB = decltype(b_tag)::value;  // (sb + 1) % 2
+  auto step = [&](auto x_tag, auto b_tag, int rel) {
+    constexpr int SX = decltype(x_tag)::value;  // (rel + 1) % 4
+    constexpr int SB = decltype(b_tag)::value;  // (rel + 1) % 2
+    const int sb = sb0 + rel;
     const int c = sb / sub_per_chunk;
-    const int buf = sb & 1;
-    if (sb % sub_per_chunk == 0)  // state entering chunk c
-      write_state(a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
-    st *= decay;
+    const int buf = rel & 1;
+    // State entering chunk c (a later piece's first chunk enters with zero,
+    // which the scan kernel knows without reading it).
+    if (rel % sub_per_chunk == 0) {
+      if (rel > 0 || piece == 0) write_state(a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
+      if (dec_writer) cdec_row[c] = lsum;
+    }
+    st *= exp2_fast(lcur);
+    lsum += lcur;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int j0 = (kh * 2 + kk) * 16 + 8 * hf;
@@ -397,35 +439,56 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
       st = mfma(av, bl, st);
     }
     stage(xring[SX], bring[SB], buf ^ 1);
-    decay = exp2_fast(xring[SX].last);
+    lcur = xring[SX].last;
     // Every read of the two slots happens before their next loads are issued,
     // so the loads can land in the same registers: otherwise the unrolled
     // loop ends in register copies that wait for loads still in flight.
-    asm volatile("" ::"v"(decay) : "memory");
+    asm volatile("" ::"v"(lcur) : "memory");
     // B first: loads return in issue order, so the wait for this B two steps
     // from now covers only the x loads issued before it (three steps old).
     load_b(sb + 3, bring[SB]);
     load_x(sb + 5, xring[SX]);
-    const bool chunk_end = (sb % sub_per_chunk == sub_per_chunk - 1) || sb == nsub - 1;
-    if (chunk_end && a.chunk_states)
-      write_state(a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  int sb = 0;
-  for (; sb + 4 <= nsub; sb += 4) {
-    step(I1{}, I1{}, sb);
-    step(I2{}, I0{}, sb + 1);
-    step(I3{}, I1{}, sb + 2);
-    step(I0{}, I0{}, sb + 3);
+  const int nrel = sb1 - sb0;
+  int rel = 0;
+  for (; rel + 4 <= nrel; rel += 4) {
+    step(I1{}, I1{}, rel);
+    step(I2{}, I0{}, rel + 1);
+    step(I3{}, I1{}, rel + 2);
+    step(I0{}, I0{}, rel + 3);
   }
-  if (sb < nsub) step(I1{}, I1{}, sb);
-  if (sb + 1 < nsub) step(I2{}, I0{}, sb + 1);
-  if (sb + 2 < nsub) step(I3{}, I1{}, sb + 2);
-  if (a.h_last) write_state(a.h_last + ((size_t)b * a.H + h) * state_stride);
+  if (rel < nrel) step(I1{}, I1{}, rel);
+  if (rel + 1 < nrel) step(I2{}, I0{}, rel + 1);
+  if (rel + 2 < nrel) step(I3{}, I1{}, rel + 2);
+  // The piece's end state (from its start) for the chain; the last piece's is
+  // not needed (the scan kernel of the last chunk writes the final state).
+  if (piece < a.npieces - 1)
+    write_state(a.pend + (((size_t)b * a.H + h) * a.npieces + piece) * state_stride);
+  if (dec_writer) a.pdec[((size_t)b * a.H + h) * a.npieces + piece] = lsum;
+}
+
+// The exact state entering every piece after the first:
+// S(k+1) = exp(A sum of delta over piece k) S(k) + pend(k), S(1) = pend(0)
+// (piece 0 ran from h0).  grid (8 slices of the state, H, batch), 256
+// threads, 4 state elements per thread.
+constexpr int kMaxPieces = 64;
+__global__ void __launch_bounds__(256) ssd_chain_kernel(SSDArgs a) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const size_t state_stride = (size_t)kP * kN;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const size_t base = ((size_t)b * a.H + h) * a.npieces * state_stride + e;
+  const float* pdec = a.pdec + ((size_t)b * a.H + h) * a.npieces;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 1; k < a.npieces; ++k) {
+    const f32x4 pe = *reinterpret_cast<const f32x4*>(&a.pend[base + (size_t)(k - 1) * state_stride]);
+    s = s * exp2_fast(pdec[k - 1]) + pe;
+    *reinterpret_cast<f32x4*>(&a.pstart[base + (size_t)k * state_stride]) = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -516,7 +579,19 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ float s_decay;
   __shared__ int s_factored;
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin; XCD x takes a contiguous
+  // run of (chunk, batch, head) items in chunk-major order, so the B and C
+  // rows of a chunk and the entering state of a piece are read into one L2.
+  int c, h, b;
+  {
+    const int nwg = a.nchunks * a.batch * a.H;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int q = nwg >> 3, r = nwg & 7;
+    const int t = x * q + min(x, r) + j;
+    c = t / (a.batch * a.H);
+    b = (t / a.H) % a.batch;
+    h = t % a.H;
+  }
   const int g = h / (a.H / a.G);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lc = lane & 31, hf = lane >> 5;
@@ -547,10 +622,25 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   };
 
   // This wave's two S^T tiles: state rows (2*rt + t)*32.., headdim tile pt.
+  // The state entering the chunk is the one from its piece's start plus the
+  // exact state entering the piece decayed over the chunks between (the first
+  // chunk of a later piece enters with zero from its piece's start).
   f32x16 st[2];
+  const int piece = c / a.cpp;
+  const bool piece_head = piece > 0 && c % a.cpp == 0;
   const float* sin = a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) load_stateT(st[t], sin, 2 * rt + t, pt);
+  for (int t = 0; t < 2; ++t) load_stateT(st[t], piece_head ? nullptr : sin, 2 * rt + t, pt);
+  if (piece > 0) {
+    const float e = exp2_fast(a.cdec[((size_t)b * a.H + h) * a.nchunks + c]);
+    const float* ps = a.pstart + (((size_t)b * a.H + h) * a.npieces + piece) * state_stride;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16 v;
+      load_stateT(v, ps, 2 * rt + t, pt);
+      st[t] += e * v;
+    }
+  }
 
   // Output of the previous block, finished at the start of the next one (the
   // partner's part is in xbuf then): accumulator and x of this lane's 16 rows.
@@ -716,19 +806,45 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     __syncthreads();
   }
   finish();
+  // The state after the chunk (exact: the chunk started from the exact state).
+  if (a.chunk_states) {
+    float* cs = a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) store_stateT(st[t], cs, 2 * rt + t, pt);
+  }
+  if (a.h_last && c == a.nchunks - 1) {
+    float* hl = a.h_last + ((size_t)b * a.H + h) * state_stride;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) store_stateT(st[t], hl, 2 * rt + t, pt);
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Pieces per sequence: about ten state-kernel workgroups per CU over all
+// pieces (2H x batch streams), at most kMaxPieces and one per chunk; pieces
+// hold whole chunks, cpp each.
+void ssd_pieces(int64_t batch, int64_t nheads, int64_t nchunks, int& npieces, int& cpp) {
+  const int64_t streams = 2 * nheads * batch;
+  int64_t np = (2560 + streams - 1) / streams;
+  np = std::max<int64_t>(1, std::min<int64_t>({np, (int64_t)kMaxPieces, nchunks}));
+  cpp = (int)((nchunks + np - 1) / np);
+  npieces = (int)((nchunks + cpp - 1) / cpp);
+}
+
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                            int64_t dstate, int64_t chunk) {
   (void)ngroups;
   const int64_t nchunks = (seqlen + chunk - 1) / chunk;
   const int64_t lp = (seqlen + kSub - 1) / kSub * kSub;
-  return align256((size_t)batch * nchunks * nheads * headdim * dstate * sizeof(float)) +
-         2 * align256((size_t)batch * nheads * lp * sizeof(float));
+  int np, cpp;
+  ssd_pieces(batch, nheads, nchunks, np, cpp);
+  const size_t state = (size_t)headdim * dstate * sizeof(float);
+  return align256((size_t)batch * nchunks * nheads * state) + 2 * align256((size_t)batch * nheads * lp * sizeof(float)) +
+         2 * align256((size_t)batch * nheads * np * state) + align256((size_t)batch * nheads * nchunks * sizeof(float)) +
+         align256((size_t)batch * nheads * np * sizeof(float));
 }
 
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
@@ -758,10 +874,24 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.dlT = reinterpret_cast<float*>(ws);
   ws += align256((size_t)a.batch * a.H * a.Lp * sizeof(float));
   a.lsT = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)a.batch * a.H * a.Lp * sizeof(float));
+  ssd_pieces(a.batch, a.H, a.nchunks, a.npieces, a.cpp);
+  const size_t piece_states = (size_t)a.batch * a.H * a.npieces * kP * kN * sizeof(float);
+  a.pend = reinterpret_cast<float*>(ws);
+  ws += align256(piece_states);
+  a.pstart = reinterpret_cast<float*>(ws);
+  ws += align256(piece_states);
+  a.cdec = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)a.batch * a.H * a.nchunks * sizeof(float));
+  a.pdec = reinterpret_cast<float*>(ws);
   hipLaunchKernelGGL(ssd_cumsum_kernel, dim3((unsigned)nsub, (unsigned)((a.H + 63) / 64), (unsigned)a.batch), dim3(256),
                      0, stream, a);
-  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch), dim3(kTS), 0, stream, a);
-  const dim3 grid((unsigned)a.nchunks, (unsigned)a.H, (unsigned)a.batch);
+  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch, (unsigned)a.npieces), dim3(kTS), 0,
+                     stream, a);
+  if (a.npieces > 1)
+    hipLaunchKernelGGL(ssd_chain_kernel, dim3((unsigned)(kP * kN / 1024), (unsigned)a.H, (unsigned)a.batch), dim3(256),
+                       0, stream, a);
+  const dim3 grid((unsigned)a.nchunks * (unsigned)a.H * (unsigned)a.batch);
   if (a.z && a.D)
     hipLaunchKernelGGL((ssd_scan_kernel<true, true>), grid, dim3(kT), 0, stream, a);
   else if (a.z)

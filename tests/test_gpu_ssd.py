@@ -125,3 +125,26 @@ def test_ssd_2p8b_workload_sampled_heads():
     e2 = assert_close(host64(cs)[:, :, heads], rcs, "bf16", "chunk_states")
     e3 = assert_close(host64(hl)[:, heads], rhl, "bf16", "h_last")
     print(f"ssd_2p8b sampled heads: y {e1:.2e} chunk_states {e2:.2e} h_last {e3:.2e}")
+
+
+@pytest.mark.parametrize("case", [
+    # b, L, H, chunk, D, z, h0, heads checked (None: all)
+    (1, 5000, 80, 64, True, True, True, [0, 5, 41, 79]),   # 16 pieces of 5 chunks, ragged L
+    (2, 3000, 40, 128, False, False, True, [0, 13, 39]),   # 12 pieces of 2 chunks, ragged last chunk
+    (1, 16384, 2, 64, False, False, True, None),           # 64 pieces of 4 chunks
+])
+def test_ssd_sequence_cut_into_pieces(case):
+    """With many heads the state pass cuts every sequence into pieces of
+    whole chunks that run from zero; the exact state entering each piece is
+    chained afterwards and added, decayed, to every chunk's entering state.
+    Checked where pieces hold several chunks and L is ragged."""
+    b, L, H, Q, d, z, h0, heads = case
+    cfg, x = gen(b, L, H, 1, Q, seed=21, with_d=d, with_z=z, with_h0=h0)
+    y, cs, hl = run_gpu(x, Q)
+    sel = slice(None) if heads is None else np.array(heads)
+    ry, rcs, rhl = run_oracle(x, Q, None if heads is None else sel)
+    e1 = assert_close(host64(y)[:, :, sel], ry, "bf16", "y")
+    e2 = assert_close(host64(cs)[:, :, sel], rcs, "bf16", "chunk_states")
+    e3 = assert_close(host64(hl)[:, sel], rhl, "bf16", "h_last")
+    print(f"{case}: y {e1:.2e} chunk_states {e2:.2e} h_last {e3:.2e}")
+    assert e1 < 5e-3 and e2 < 5e-3
