@@ -90,15 +90,32 @@ __device__ __forceinline__ void acc_kslice(const f32x16& acc, float* v) {
 }
 
 // fp32 pair -> (hi, lo) bf16 pairs with hi + lo = value to ~16 mantissa bits.
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = pack_bf16x2(a, b);
-  lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
+// The residuals value - hi come from v_dot2_f32_bf16 of the packed hi pair
+// with (-1, 0) or (0, -1), plus the value: one instruction each instead of
+// unpacking hi and subtracting, and exact (the products are exact and the
+// residual of a round-to-nearest is representable).  The two masks live in
+// registers: folded into an inline constant, (-1, 0) is read as (0, -1).
+struct Dot2Masks {
+  bf16x2_t lo, hi;
+};
+__device__ __forceinline__ Dot2Masks dot2_masks() {
+  uint32_t lo = 0x0000bf80u, hi = 0xbf800000u;
+  asm volatile("" : "+v"(lo));
+  asm volatile("" : "+v"(hi));
+  return {__builtin_bit_cast(bf16x2_t, lo), __builtin_bit_cast(bf16x2_t, hi)};
 }
-__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
+__device__ __forceinline__ float dot2_bf16(uint32_t h, bf16x2_t m, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h), m, c, false);
+}
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo, const Dot2Masks& m) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(dot2_bf16(hi, m.lo, a), dot2_bf16(hi, m.hi, b));
+}
+__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo, const Dot2Masks& m) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t h, l;
-    split2(v[2 * q], v[2 * q + 1], h, l);
+    split2(v[2 * q], v[2 * q + 1], h, l, m);
     hi[q] = h;
     lo[q] = l;
   }
@@ -279,6 +296,7 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const int lc = lane & 31, hf = lane >> 5;
   const int nt = w & 3, kh = w >> 2;
   const size_t state_stride = (size_t)kP * kN;
+  const Dot2Masks dm = dot2_masks();
   // This piece's chunks [c0, c1) and 64-step blocks [sb0, sb1).
   const int sub_per_chunk = a.Q / kSub;
   const int nsub = (a.L + kSub - 1) / kSub;
@@ -340,10 +358,10 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     const float w0 = __uint_as_float(sl.dl[0]) * exp2_fast(sl.last - __uint_as_float(sl.ls[0]));
     const float w1 = __uint_as_float(sl.dl[1]) * exp2_fast(sl.last - __uint_as_float(sl.ls[1]));
     uint32_t hi, lo;
-    split2(bf16_lo(sl.xr[0]) * w0, bf16_lo(sl.xr[1]) * w1, hi, lo);
+    split2(bf16_lo(sl.xr[0]) * w0, bf16_lo(sl.xr[1]) * w1, hi, lo, dm);
     *reinterpret_cast<uint32_t*>(&xh[buf][tsw(pq * 2, jx)]) = hi;
     *reinterpret_cast<uint32_t*>(&xl[buf][tsw(pq * 2, jx)]) = lo;
-    split2(bf16_hi(sl.xr[0]) * w0, bf16_hi(sl.xr[1]) * w1, hi, lo);
+    split2(bf16_hi(sl.xr[0]) * w0, bf16_hi(sl.xr[1]) * w1, hi, lo, dm);
     *reinterpret_cast<uint32_t*>(&xh[buf][tsw(pq * 2 + 1, jx)]) = hi;
     *reinterpret_cast<uint32_t*>(&xl[buf][tsw(pq * 2 + 1, jx)]) = lo;
 #pragma unroll
@@ -513,7 +531,8 @@ __global__ void __launch_bounds__(256) ssd_chain_kernel(SSDArgs a) {
 template <int RT, int JT, int S0, int S1, bool FACTORED>
 __device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN + kPadH],
                                           const uint16_t (*Bs)[kN + kPadH], const uint16_t* xT, const float* s_ls,
-                                          const float* s_dl, const float* s_ei, const float* s_fd, int pt) {
+                                          const float* s_dl, const float* s_ei, const float* s_fd, int pt,
+                                          const Dot2Masks& dm) {
   const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int i = RT * 32 + lc;
   const float rowv = FACTORED ? s_ei[i] : s_ls[i];  // ei[i], or ls_i
@@ -554,7 +573,7 @@ __device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN 
       }
     }
     u32x4 mh, ml;
-    split8(m, mh, ml);
+    split8(m, mh, ml, dm);
     const u32x4 xb = *reinterpret_cast<const u32x4*>(&xT[tsw(pt * 32 + lc, j0)]);
     yacc = mfma(mh, xb, yacc);
     yacc = mfma(ml, xb, yacc);
@@ -596,6 +615,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lc = lane & 31, hf = lane >> 5;
   const int rt = w >> 1, pt = w & 1;
+  const Dot2Masks dm = dot2_masks();
   const int partner = w ^ 2;
   const float dh = a.D ? a.D[h] : 0.f;
   const size_t state_stride = (size_t)kP * kN;
@@ -726,7 +746,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
         float v[8];
         acc_kslice<S>(st[t], v);
         u32x4 bh, bl;
-        split8(v, bh, bl);
+        split8(v, bh, bl, dm);
         const int k0 = (2 * rt + t) * 32 + 16 * S + 8 * hf;
         const u32x4 c_own = *reinterpret_cast<const u32x4*>(&Cs[rt * 32 + lc][k0]);
         const u32x4 c_oth = *reinterpret_cast<const u32x4*>(&Cs[(1 - rt) * 32 + lc][k0]);
@@ -748,11 +768,11 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     auto diag = [&](auto factored_tag) {
       constexpr bool F = decltype(factored_tag)::value;
       if (rt == 0) {
-        diag_part<0, 0, 0, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
-        diag_part<1, 0, 0, 1, F>(yoth, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
+        diag_part<0, 0, 0, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt, dm);
+        diag_part<1, 0, 0, 1, F>(yoth, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt, dm);
       } else {
-        diag_part<1, 1, 0, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
-        diag_part<1, 0, 1, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt);
+        diag_part<1, 1, 0, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt, dm);
+        diag_part<1, 0, 1, 2, F>(yown, Cs, Bs, xT, s_ls, s_dl, s_ei, s_fd, pt, dm);
       }
     };
     if (__builtin_amdgcn_readfirstlane(s_factored))
@@ -795,7 +815,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
                           bf16_hi(xv[1]) * w0[3], bf16_lo(xv[2]) * w1[0], bf16_hi(xv[2]) * w1[1],
                           bf16_lo(xv[3]) * w1[2], bf16_hi(xv[3]) * w1[3]};
       u32x4 bh, bl;
-      split8(v, bh, bl);
+      split8(v, bh, bl, dm);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[tsw((2 * rt + t) * 32 + lc, j0)]);
