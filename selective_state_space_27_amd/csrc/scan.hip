@@ -16,10 +16,12 @@
 //     the work.  B and C are shared by every channel: each lane loads a few
 //     (fp32, pre-arranged by bc_transpose_kernel) and the multiplies take them
 //     from lane p of the row with a DPP row broadcast (v_mul_f32_dpp /
-//     v_fmac_f32_dpp row_newbcast:p).  Partial readouts go to LDS.
-//   4 prologue waves: for tile k+1, x = delta*u and the decay data into LDS.
+//     v_fmac_f32_dpp row_newbcast:p).  Partial readouts go to LDS; wave 0's
+//     includes the skip term D*u.
+//   4 prologue waves: for tile k+1, x = delta*u, D*u and the decay data into
+//     LDS.
 //   4 epilogue waves: for tile k-1, the 8 partial readouts summed in a fixed
-//     order, plus D*u, gated by silu(z), stored.
+//     order, gated by silu(z), stored (u is read once, by the prologue).
 // Prologue and epilogue threads own one channel and 4 steps of a tile, so the
 // four lanes of a channel read or write its 16-step row segment in one
 // instruction.  Streams are read with branch-free buffer loads issued three
@@ -48,7 +50,10 @@ namespace {
 
 constexpr int kIoWaves = 4;  // prologue waves, and as many epilogue waves
 constexpr int kThreads = (kWaves + 2 * kIoWaves) * kLanes;
-constexpr int kQMax = 2 + kWaves;  // LDS quantities per (d,l): x, r, 8 start powers
+// LDS quantities per (d,l): x = delta*u, r (or delta), D*u, and the start
+// powers of core waves 1..7 (wave 0's is r itself).
+constexpr int kQMax = 2 + kWaves;
+constexpr int kQDu = 2;  // slot of D*u
 constexpr int kPrefetch = 3;       // tiles of global loads in flight
 
 struct ScanArgs {
@@ -173,7 +178,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     // Per-thread constants: the prologue channel's A[., 0], the epilogue
     // channel's D, the core channel's A row for this wave's states.
     const float a20 = (is_pro && iok) ? a.A[(size_t)c_io * N] * kLog2e : 0.f;
-    const float dskip = (!is_core && !is_pro && a.D != nullptr && iok) ? a.D[c_io] : 0.f;
+    const float dskip = (is_pro && a.D != nullptr && iok) ? a.D[c_io] : 0.f;
     float A2[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -266,10 +271,11 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
       // One tile: x, the decay (S4D: r) and the start power of the four
       // blocks come from qbuf (read all up front when the registers allow);
-      // partial readouts go to pbuf.  Steps at or past L need no guard: their
+      // partial readouts go to pbuf, wave 0's starting from D*u.  Steps at or past L need no guard: their
       // delta, u and B read as zero, so the decay is exp2(0) = 1 and the input
       // term 0, and the update leaves h unchanged.
       constexpr int kAhead = SPW <= 4 ? kBlk : 1;
+      const int sp_slot = wc == 0 ? 1 : 2 + wc;  // start power r^(wc*SPW+1): r itself for wave 0
       auto core_tile = [&](int buf, int k, const f32x4* bc_cur) {
         const float* q = qbuf[buf];
         float* pp = pbuf[buf];
@@ -277,7 +283,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         auto read_blk = [&](int blk, int i) {
           xvs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(0, blk, lane)]);
           rvs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(1, blk, lane)]);
-          if constexpr (S4D) svs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(2 + wc, blk, lane)]);
+          if constexpr (S4D) svs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(sp_slot, blk, lane)]);
           else svs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         };
         if constexpr (kAhead == kBlk) {
@@ -299,6 +305,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           if constexpr (kAhead == 1) read_blk(blk, 0);
           const int i = kAhead == kBlk ? blk : 0;
           const f32x4 xv = xvs[i], rv = rvs[i], sv = svs[i];
+          f32x4 duv = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (!STATE) {
+            if (wc == 0) duv = *reinterpret_cast<const f32x4*>(&q[q_off(kQDu, blk, lane)]);
+          }
           f32x4 part;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
@@ -325,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
               if constexpr (STATE) asm volatile("" : "+v"(h[j]));
               if constexpr (!STATE) {  // the state-only passes need no readout
                 if (j == 0)
-                  p = row_bcast_rt(bcv(ic), ic % 16) * h[j];
+                  p = fmac_row_bcast_rt(duv[kk], bcv(ic), h[j], ic % 16);
                 else
                   p = fmac_row_bcast_rt(p, bcv(ic), h[j], ic % 16);
               }
@@ -384,12 +394,12 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       }
       float dacc = 0.f;  // local pass: sum of delta over this thread's steps of the piece
       // Rings of three slots: (u, delta) for the prologue hold tile t in slot
-      // (t - tb) % 3 and are loaded three steps ahead; (u, z) for the
-      // epilogue hold tile t in slot (t - tb + 2) % 3, also three steps ahead.
+      // (t - tb) % 3 and are loaded three steps ahead; z for the epilogue
+      // holds tile t in slot (t - tb + 2) % 3, also three steps ahead.
       // In every step both rings consume and refill the same compile-time
       // slot, and the loop (unrolled by 3) never copies a register whose load
       // is in flight nor branches around a load.
-      Raw4<BF16> pu[kPrefetch], pd[kPrefetch], eu[kPrefetch], ez[kPrefetch];
+      Raw4<BF16> pu[kPrefetch], pd[kPrefetch], ez[kPrefetch];
       auto load_pro = [&](int tile, int slot) {
         const int t = tile * kTile + io_blk * 4;
         const bool ok = iok && tile >= tb && tile < te;
@@ -399,7 +409,6 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       auto load_epi = [&](int tile, int slot) {
         const int t = tile * kTile + io_blk * 4;
         const bool ok = iok && tile >= tb && tile < te;
-        eu[slot] = load_raw4<BF16, VEC>(ru_d, io_off, t, L, ok);
         ez[slot] = load_raw4<BF16, VEC>(rz_d, io_off, t, L, ok);
       };
 
@@ -413,6 +422,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         refill();  // the slot's registers are free: issue its next load now
         float* q = qbuf[buf];
         *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
+        if constexpr (!STATE) *reinterpret_cast<f32x4*>(&q[q_off(kQDu, io_blk, io_ch)]) = dskip * uu;
         if constexpr (M == kDecayScalar) {
           f32x4 r;
 #pragma unroll
@@ -426,21 +436,21 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           f32x4 stp = r;  // r^SPW
 #pragma unroll
           for (int j = 1; j < SPW; ++j) stp = stp * r;
-          f32x4 sp = r;   // r^(wave*SPW + 1)
+          f32x4 sp = r;   // r^(wave*SPW + 1), slot 2 + wave (wave 0 uses r)
 #pragma unroll
-          for (int wv = 0; wv < kWaves; ++wv) {
-            *reinterpret_cast<f32x4*>(&q[q_off(2 + wv, io_blk, io_ch)]) = sp;
+          for (int wv = 1; wv < kWaves; ++wv) {
             sp = sp * stp;
+            *reinterpret_cast<f32x4*>(&q[q_off(2 + wv, io_blk, io_ch)]) = sp;
           }
         } else {
           *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = dd;
         }
       };
 
-      // Epilogue of tile `tile`: the 8 partial readouts from pbuf[buf] summed in
-      // a fixed order, plus D*u, gated by silu(z); stores only inside the piece.
+      // Epilogue of tile `tile`: the 8 partial readouts from pbuf[buf] (D*u
+      // is in wave 0's) summed in a fixed order, gated by silu(z); stores only
+      // inside the piece.
       auto epilogue = [&](int buf, int slot, int tile, auto&& refill) {
-        const f32x4 uu = decode4(eu[slot]);
         const f32x4 zz = decode4(ez[slot]);
         refill();  // the slot's registers are free: issue its next load now
         const float* pp = pbuf[buf];
@@ -450,9 +460,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         f32x4 out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float o = __builtin_fmaf(dskip, uu[i], acc[i]);
           const float g = silu(zz[i]);  // z reads as 0 when absent; the select drops it
-          out[i] = o * (has_z ? g : 1.0f);
+          out[i] = acc[i] * (has_z ? g : 1.0f);
         }
         const bool ok = iok && tile >= tb && tile < te;
         store4<BF16, VEC>(ry_d, io_off, tile * kTile + io_blk * 4, L, ok, out);
