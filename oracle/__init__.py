@@ -15,7 +15,8 @@ closed forms, library routines and brute force (time-invariant case equals a
 causal convolution / first-order IIR filter, brute-force materialised matrix,
 zero-input decay, chunk-split composition, scan equals repeated state updates,
 SSD equals the Mamba-1 scan with scalar-per-head A and its matrix form, special
-cases of D and the gate, linearity, causality).
+cases of D and the gate, linearity, causality; the scan prologue against a
+library convolution and softplus's closed forms).
 The backward is pinned by central finite differences of the forward, a
 different computation.
 """
@@ -55,6 +56,8 @@ def _load():
         lib.oracle_ssd.restype = None
         lib.oracle_selective_scan_bwd.argtypes = [_dp] * 18 + [L, L, L, L, ctypes.c_int]
         lib.oracle_selective_scan_bwd.restype = None
+        lib.oracle_scan_prologue.argtypes = [_dp] * 7 + [L, L, L, ctypes.c_int, ctypes.c_int]
+        lib.oracle_scan_prologue.restype = None
         _lib = lib
     return _lib
 
@@ -106,6 +109,31 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, threads=None):
                                   _ptr(h0), _ptr(y), _ptr(h_last), b, d, N, L,
                                   threads or default_threads())
     return y, h_last
+
+
+def scan_prologue(x, conv_w, conv_b=None, delta_raw=None, delta_bias=None, conv_silu=False, softplus=True):
+    """u and delta from the short causal convolution of x and the raw delta
+    (see ``oracle_scan_prologue`` for the passages and readings).  x,
+    delta_raw: [b, d, L]; conv_w: [d, 4]; conv_b, delta_bias: [d]."""
+    x = _f64(x)
+    b, d, L = x.shape
+    w = _f64(conv_w, (d, 4))
+    cb = None if conv_b is None else _f64(conv_b, (d,))
+    dr = _f64(delta_raw, (b, d, L))
+    db = None if delta_bias is None else _f64(delta_bias, (d,))
+    u = np.empty((b, d, L))
+    dl = np.empty((b, d, L))
+    _load().oracle_scan_prologue(_ptr(x), _ptr(w), _ptr(cb), _ptr(dr), _ptr(db), _ptr(u), _ptr(dl), b, d, L,
+                                 int(bool(conv_silu)), int(bool(softplus)))
+    return u, dl
+
+
+def selective_scan_fused(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None, h0=None,
+                         conv_silu=False, softplus=True, threads=None):
+    """The scan fed by its prologue: u, delta = scan_prologue(...), then
+    selective_scan(u, delta, ...).  Returns (y, h_last)."""
+    u, dl = scan_prologue(x, conv_w, conv_b, delta_raw, delta_bias, conv_silu, softplus)
+    return selective_scan(u, dl, A, B, C, D, z, h0, threads=threads)
 
 
 def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, threads=None):

@@ -361,3 +361,44 @@ void oracle_ssd(const double* x, const double* delta, const double* A, const dou
   free(th);
   free(jobs);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Scan prologue: the short causal convolution that feeds u, and delta from */
+/* its raw value.                                                            */
+/* x, delta_raw, u, delta: [batch, dim, seqlen]; conv_w: [dim, 4] (tap 3     */
+/* multiplies the current step); conv_b, delta_bias: [dim] or NULL.          */
+/*                                                                           */
+/* Sources: "Mamba (deep learning)", paragraph on the block (an input        */
+/* projection, a short convolution, the selective state space layer and a    */
+/* gate); "Mamba State-Space Models", usage example (d_conv = 4, the         */
+/* convolution's kernel size).  Readings where the pages are silent: the     */
+/* convolution is depthwise (one 4-tap filter per channel) and causal, with  */
+/* zeros before the first step, plus a per-channel bias; its output is used  */
+/* as is, or through silu when conv_silu is set; delta is                    */
+/* softplus(delta_raw + bias) when softplus is set (the form of the          */
+/* workload's delta), else delta_raw + bias.  softplus(v) = log(1 + exp(v)). */
+/* ------------------------------------------------------------------------ */
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+
+void oracle_scan_prologue(const double* x, const double* conv_w, const double* conv_b, const double* delta_raw,
+                          const double* delta_bias, double* u, double* delta, long batch, long dim, long seqlen,
+                          int conv_silu, int use_softplus) {
+  for (long b = 0; b < batch; ++b) {
+    for (long d = 0; d < dim; ++d) {
+      const double* xr = x + (b * dim + d) * seqlen;
+      const double* dr = delta_raw + (b * dim + d) * seqlen;
+      double* ur = u + (b * dim + d) * seqlen;
+      double* dlr = delta + (b * dim + d) * seqlen;
+      for (long t = 0; t < seqlen; ++t) {
+        double acc = conv_b ? conv_b[d] : 0.0;
+        for (long k = 0; k < 4; ++k) {
+          const long s = t - 3 + k; /* tap k reads step t - 3 + k */
+          if (s >= 0) acc += conv_w[d * 4 + k] * xr[s];
+        }
+        ur[t] = conv_silu ? silu(acc) : acc;
+        const double v = dr[t] + (delta_bias ? delta_bias[d] : 0.0);
+        dlr[t] = use_softplus ? softplus(v) : v;
+      }
+    }
+  }
+}

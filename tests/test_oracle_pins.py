@@ -438,3 +438,90 @@ def test_backward_of_lti_is_reversed_convolution():
         k = (Cv[:, None] * Bv[:, None] * dl * np.exp(dl * A[c][:, None] * s[None])).sum(0)
         want = np.array([np.dot(k[:L - t], dy[0, c, t:]) for t in range(L)])
         np.testing.assert_allclose(gr["du"][0, c], want, rtol=1e-11, atol=1e-12)
+
+
+# --- scan prologue: short causal convolution and softplus ------------------
+
+def _prologue_inputs(b=2, d=5, L=37, seed=41):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((b, d, L))
+    w = g.standard_normal((d, 4))
+    cb = g.standard_normal(d)
+    dr = g.uniform(-8.0, 3.0, size=(b, d, L))
+    db = g.uniform(-1.0, 1.0, size=d)
+    return x, w, cb, dr, db
+
+
+def test_prologue_conv_equals_library_convolution():
+    """u[t] = sum_k w[k] x[t-3+k] + bias, zeros before the first step: the
+    first L outputs of numpy's full convolution with the reversed taps."""
+    x, w, cb, dr, db = _prologue_inputs()
+    u, _ = oracle.scan_prologue(x, w, cb, dr, db, conv_silu=False, softplus=False)
+    b, d, L = x.shape
+    for bi in range(b):
+        for di in range(d):
+            ref = np.convolve(x[bi, di], w[di][::-1])[:L] + cb[di]
+            np.testing.assert_allclose(u[bi, di], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_prologue_identity_tap_and_causality():
+    x, w, cb, dr, db = _prologue_inputs(L=20)
+    d = x.shape[1]
+    ident = np.zeros((d, 4))
+    ident[:, 3] = 1.0
+    u, dl = oracle.scan_prologue(x, ident, None, dr, None, conv_silu=False, softplus=False)
+    assert np.array_equal(u, x) and np.array_equal(dl, dr)
+    # Changing x at step s moves u only at steps s .. s+3.
+    u0, _ = oracle.scan_prologue(x, w, cb, dr, db, softplus=False)
+    x2 = x.copy()
+    x2[:, :, 9] += 1.0
+    u1, _ = oracle.scan_prologue(x2, w, cb, dr, db, softplus=False)
+    changed = np.nonzero(np.any(u0 != u1, axis=(0, 1)))[0]
+    assert list(changed) == [9, 10, 11, 12]
+
+
+def test_prologue_silu_option():
+    x, w, cb, dr, db = _prologue_inputs()
+    u_lin, _ = oracle.scan_prologue(x, w, cb, dr, db, conv_silu=False, softplus=False)
+    u_silu, _ = oracle.scan_prologue(x, w, cb, dr, db, conv_silu=True, softplus=False)
+    np.testing.assert_allclose(u_silu, u_lin * scipy.special.expit(u_lin), rtol=1e-13, atol=1e-15)
+
+
+def test_softplus_closed_forms():
+    """softplus(0) = ln 2; softplus(v) - softplus(-v) = v; it inverts the
+    workload's inverse-softplus bias: softplus(log(expm1(dt))) = dt; and it
+    equals log(1 + exp(v)) through numpy's logaddexp."""
+    v = np.concatenate([[0.0], np.linspace(-30, 30, 61), [-700.0, 700.0]])
+    x = np.zeros((1, 1, v.size))
+    w = np.zeros((1, 4))
+    _, sp = oracle.scan_prologue(x, w, None, v[None, None, :], None, softplus=True)
+    _, sm = oracle.scan_prologue(x, w, None, -v[None, None, :], None, softplus=True)
+    sp, sm = sp[0, 0], sm[0, 0]
+    assert abs(sp[0] - np.log(2.0)) < 1e-15
+    np.testing.assert_allclose(sp - sm, v, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(sp, np.logaddexp(0.0, v), rtol=1e-13, atol=0)
+    dt = np.exp(np.random.default_rng(5).uniform(np.log(1e-3), np.log(1e-1), 50))
+    _, back = oracle.scan_prologue(np.zeros((1, 1, 50)), w, None, np.log(np.expm1(dt))[None, None, :], None)
+    np.testing.assert_allclose(back[0, 0], dt, rtol=1e-12)
+
+
+def test_fused_scan_equals_scan_of_prologue_by_library_routes():
+    """The fused oracle equals the plain scan fed with u from numpy's
+    convolution (+ silu via expit) and delta from logaddexp."""
+    x, w, cb, dr, db = _prologue_inputs(b=2, d=4, L=30)
+    b, d, L = x.shape
+    N = 8
+    g = np.random.default_rng(3)
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (d, 1))
+    B = g.standard_normal((b, N, L))
+    C = g.standard_normal((b, N, L))
+    D = g.standard_normal(d)
+    z = g.standard_normal((b, d, L))
+    h0 = g.standard_normal((b, d, N))
+    lin = np.stack([np.stack([np.convolve(x[i, j], w[j][::-1])[:L] + cb[j] for j in range(d)]) for i in range(b)])
+    u = lin * scipy.special.expit(lin)
+    delta = np.logaddexp(0.0, dr + db[None, :, None])
+    y_ref, h_ref = oracle.selective_scan(u, delta, A, B, C, D, z, h0)
+    y, h = oracle.selective_scan_fused(x, w, cb, dr, db, A, B, C, D, z, h0, conv_silu=True, softplus=True)
+    np.testing.assert_allclose(y, y_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(h, h_ref, rtol=1e-11, atol=1e-12)
