@@ -104,6 +104,45 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
 size_t mss_selective_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                          int64_t seqlen, mss_dtype io_dtype, uint32_t flags);
 
+/* Flags of mss_selective_scan_fwd_fused (with MSS_FLAG_DECAY_GENERAL).     */
+#define MSS_FLAG_CONV_SILU 0x2u      /* u = silu(convolution) instead of u = convolution */
+#define MSS_FLAG_DELTA_SOFTPLUS 0x4u /* delta = softplus(delta_raw + bias) instead of delta_raw + bias */
+
+/* ------------------------------------------------------------------------ */
+/* Selective scan fed by its prologue, in one pass.                          */
+/*                                                                          */
+/* The block around the layer has an input projection, a short convolution, */
+/* the selective state space layer and a gate ("Mamba (deep learning)",      */
+/* paragraph on the block); the convolution's kernel size is 4 ("Mamba       */
+/* State-Space Models", usage example, d_conv).  This entry point computes   */
+/* the layer's u from the convolution and delta from its raw value inside    */
+/* the scan, so neither is written to or read from memory:                   */
+/*   c[b,d,l] = conv_b[d] + sum_{k=0..3} conv_w[d,k] * x[b,d,l-3+k]          */
+/*              (x = 0 before the first step: causal, one filter per channel) */
+/*   u[b,d,l] = c  (or silu(c) = c/(1+exp(-c)) with MSS_FLAG_CONV_SILU)      */
+/*   v        = delta_raw[b,d,l] + delta_bias[d]                             */
+/*   delta[b,d,l] = v  (or softplus(v) = log(1+exp(v)) with                  */
+/*              MSS_FLAG_DELTA_SOFTPLUS)                                     */
+/* then exactly mss_selective_scan_fwd(u, delta, A, B, C, D, z, h0, ...).    */
+/* The pages name the convolution but not its activation, nor any transform */
+/* of delta: both are options (softplus is the form of the workload's       */
+/* delta).                                                                   */
+/*                                                                          */
+/* Layouts: x, delta_raw : [batch, dim, seqlen] io_dtype;  conv_w : [dim, 4] */
+/*   fp32 (tap 3 multiplies the current step);  conv_b, delta_bias : [dim]   */
+/*   fp32 (each may be NULL = 0);  everything else as in                      */
+/*   mss_selective_scan_fwd.  Limits, workspace (the size                    */
+/*   mss_selective_scan_workspace_size returns), stream and errors as there; */
+/*   y and h_last must not overlap any input or each other.                  */
+/* ------------------------------------------------------------------------ */
+mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, const float* conv_b,
+                                        const void* delta_raw, const float* delta_bias, const float* A,
+                                        const void* B, const void* C, const float* D, const void* z,
+                                        const float* h0, void* y, float* h_last, int64_t batch,
+                                        int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype io_dtype,
+                                        uint32_t flags, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Selective scan, backward (training).                                      */
 /*                                                                          */

@@ -9,6 +9,9 @@ or a GPU is absent, the calls raise.
 
 Operations (see the header for the exact definitions and layouts):
   selective_scan_fwd  Mamba-1 selective scan over a whole sequence
+  selective_scan_fwd_fused  the same, fed by its prologue (short causal
+                      convolution for u, delta from its raw value) in one pass
+  selective_scan_bwd  its gradient
   state_update        one recurrent generation step, state updated in place
   ssd_chunk_fwd       Mamba-2 SSD layer, chunked, dense products on MFMA
 """
@@ -26,12 +29,15 @@ MSS_OK = 0
 MSS_FP32 = 0
 MSS_BF16 = 1
 MSS_FLAG_DECAY_GENERAL = 0x1
+MSS_FLAG_CONV_SILU = 0x2
+MSS_FLAG_DELTA_SOFTPLUS = 0x4
 
 STATUS_NAMES = {0: "MSS_OK", 1: "MSS_ERR_NULL", 2: "MSS_ERR_SHAPE", 3: "MSS_ERR_DTYPE", 4: "MSS_ERR_ALIGN",
                 5: "MSS_ERR_UNSUPPORTED", 6: "MSS_ERR_WORKSPACE", 7: "MSS_ERR_ALIAS", 8: "MSS_ERR_HIP"}
 
 # Every symbol the header declares.
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_selective_scan_bwd",
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_selective_scan_fwd_fused",
+           "mss_selective_scan_bwd",
            "mss_selective_scan_bwd_workspace_size", "mss_state_update",
            "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_status_string", "mss_last_hip_error",
            "mss_abi_version")
@@ -65,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.mss_selective_scan_fwd.restype = ctypes.c_int
     L.mss_selective_scan_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
     L.mss_selective_scan_workspace_size.restype = sz
+    L.mss_selective_scan_fwd_fused.argtypes = [vp, fp, fp, vp, fp, fp, vp, vp, fp, vp, fp, vp, fp, i64, i64, i64,
+                                               i64, ctypes.c_int, u32, vp, sz, vp]
+    L.mss_selective_scan_fwd_fused.restype = ctypes.c_int
     L.mss_selective_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, vp, vp, fp, vp, vp, fp, vp, fp,
                                          i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
     L.mss_selective_scan_bwd.restype = ctypes.c_int
@@ -178,6 +187,54 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, *, return_las
                                       _ptr(out), _ptr(h_last), b, d, N, L, code, flags, _ptr(workspace),
                                       workspace.numel(), _stream(stream))
     _raise(st, "mss_selective_scan_fwd")
+    return (out, h_last) if return_last_state else out
+
+
+def selective_scan_fwd_fused(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None, h0=None, *,
+                             conv_silu=False, softplus=True, return_last_state=False, force_general_decay=False,
+                             out=None, h_last=None, workspace=None, stream=None):
+    """Selective scan whose u and delta are formed inside the kernel:
+    u = conv_b + causal 4-tap depthwise convolution of x with conv_w (tap 3 on
+    the current step), through silu if ``conv_silu``; delta = delta_raw +
+    delta_bias, through softplus if ``softplus``.
+
+    x, delta_raw, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16, all the
+    same); conv_w: [d, 4] float32; conv_b, delta_bias: [d] float32 or None;
+    A, D, h0 as in selective_scan_fwd.  Returns y (and h_last) like it."""
+    dev = _device_of(x)
+    b, d, L = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    _check(x, "x", (b, d, L), io, dev)
+    _check(conv_w, "conv_w", (d, 4), torch.float32, dev)
+    _check(conv_b, "conv_b", (d,), torch.float32, dev)
+    _check(delta_raw, "delta_raw", (b, d, L), io, dev)
+    _check(delta_bias, "delta_bias", (d,), torch.float32, dev)
+    _check(A, "A", (d, N), torch.float32, dev)
+    _check(B, "B", (b, N, L), io, dev)
+    _check(C, "C", (b, N, L), io, dev)
+    _check(D, "D", (d,), torch.float32, dev)
+    _check(z, "z", (b, d, L), io, dev)
+    _check(h0, "h0", (b, d, N), torch.float32, dev)
+    flags = ((MSS_FLAG_DECAY_GENERAL if force_general_decay else 0) | (MSS_FLAG_CONV_SILU if conv_silu else 0) |
+             (MSS_FLAG_DELTA_SOFTPLUS if softplus else 0))
+    code = _io_code(io)
+    if out is None:
+        out = torch.empty((b, d, L), dtype=io, device=dev)
+    _check(out, "out", (b, d, L), io, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((b, d, N), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", (b, d, N), torch.float32, dev)
+    need = lib().mss_selective_scan_workspace_size(b, d, N, L, code, flags)
+    if need == 0:
+        _raise(5, "selective_scan_fwd_fused")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().mss_selective_scan_fwd_fused(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(delta_raw), _ptr(delta_bias),
+                                            _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(out),
+                                            _ptr(h_last), b, d, N, L, code, flags, _ptr(workspace), workspace.numel(),
+                                            _stream(stream))
+    _raise(st, "mss_selective_scan_fwd_fused")
     return (out, h_last) if return_last_state else out
 
 

@@ -134,6 +134,61 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
   return hip_status(mss::launch_scan(p, static_cast<hipStream_t>(hip_stream)));
 }
 
+mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, const float* conv_b,
+                                        const void* delta_raw, const float* delta_bias, const float* A,
+                                        const void* B, const void* C, const float* D, const void* z,
+                                        const float* h0, void* y, float* h_last, int64_t batch, int64_t dim,
+                                        int64_t dstate, int64_t seqlen, mss_dtype io_dtype, uint32_t flags,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!x || !conv_w || !delta_raw || !A || !B || !C || !y) return MSS_ERR_NULL;
+  mss_status st = scan_check_shape(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MSS_OK) return st;
+  if (flags & ~(MSS_FLAG_DECAY_GENERAL | MSS_FLAG_CONV_SILU | MSS_FLAG_DELTA_SOFTPLUS)) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D, z, h0, y, h_last, workspace};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t need = mss::scan_workspace_bytes(batch, dim, dstate, seqlen);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+
+  const size_t es = elem_size(io_dtype);
+  const size_t nbdl = (size_t)batch * dim * seqlen;
+  const size_t nbnl = (size_t)batch * dstate * seqlen;
+  const size_t nstate = (size_t)batch * dim * dstate * sizeof(float);
+  const void* ins[] = {x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D, z, h0, workspace};
+  const size_t in_bytes[] = {nbdl * es, (size_t)dim * 16, (size_t)dim * 4, nbdl * es, (size_t)dim * 4,
+                             (size_t)dim * dstate * 4, nbnl * es, nbnl * es, (size_t)dim * 4, nbdl * es, nstate,
+                             need};
+  if (!output_clear(y, nbdl * es, ins, in_bytes, 12)) return MSS_ERR_ALIAS;
+  if (!output_clear(h_last, nstate, ins, in_bytes, 12)) return MSS_ERR_ALIAS;
+  if (h_last && overlaps(range_of(y, nbdl * es), range_of(h_last, nstate))) return MSS_ERR_ALIAS;
+
+  mss::ScanParams p;
+  p.u = x;
+  p.delta = delta_raw;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.h0 = h0;
+  p.y = y;
+  p.h_last = h_last;
+  p.batch = batch;
+  p.dim = dim;
+  p.dstate = dstate;
+  p.seqlen = seqlen;
+  p.bf16 = io_dtype == MSS_BF16;
+  p.force_general = (flags & MSS_FLAG_DECAY_GENERAL) != 0;
+  p.workspace = workspace;
+  p.fused = true;
+  p.conv_w = conv_w;
+  p.conv_b = conv_b;
+  p.delta_bias = delta_bias;
+  p.conv_silu = (flags & MSS_FLAG_CONV_SILU) != 0;
+  p.delta_softplus = (flags & MSS_FLAG_DELTA_SOFTPLUS) != 0;
+  return hip_status(mss::launch_scan(p, static_cast<hipStream_t>(hip_stream)));
+}
+
 // --------------------------------------------------- selective scan backward
 size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                              mss_dtype io_dtype, uint32_t flags) {

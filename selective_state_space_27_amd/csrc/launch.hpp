@@ -24,6 +24,14 @@ struct ScanParams {
   bool force_general;
   void* workspace;
   float* ckpt = nullptr;  // backward only: states entering every tile, [b*nblocks][ntiles][8][SPW][64]
+  // Fused prologue (u = x and delta = delta_raw above): u from the causal
+  // 4-tap convolution of x, delta from delta_raw plus bias, optionally softplus.
+  bool fused = false;
+  const float* conv_w = nullptr;      // [dim][4]
+  const float* conv_b = nullptr;      // [dim], nullable
+  const float* delta_bias = nullptr;  // [dim], nullable
+  bool conv_silu = false;
+  bool delta_softplus = false;
 };
 
 size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);

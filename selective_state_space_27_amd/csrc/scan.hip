@@ -76,7 +76,31 @@ struct ScanArgs {
   int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
   int force_general;
   int pass;            // kPassSingle, kPassLocal or kPassFinal
+  // Fused prologue: u and delta above are x and the raw delta; the prologue
+  // waves form u = (silu of) the causal 4-tap convolution of x and
+  // delta = (softplus of) delta_raw + bias.
+  const float* conv_w;      // [dim][4]
+  const float* conv_b;      // [dim] or null
+  const float* delta_bias;  // [dim] or null
+  int fused, conv_silu, delta_softplus;
 };
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(exp(-|v|)), with log1p(e)
+// taken as log(w) * e / (w - 1), w = 1 + e rounded (exact for the rounding of
+// w; e itself when w rounds to 1).
+__device__ __forceinline__ float softplus_f(float v) {
+  const float e = exp2_fast(-fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float l = (w == 1.0f) ? e : __builtin_amdgcn_logf(w) * kLn2 * (e * rcp_fast(w - 1.0f));
+  return fmaxf(v, 0.f) + l;
+}
+
+// The value of lane q-1 of this lane's quad (lane 0 of a quad gets lane 3's).
+__device__ __forceinline__ float quad_prev(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x93, 0xf, 0xf, false));
+}
 
 constexpr int kMaxSpins = 1 << 22;
 
@@ -115,7 +139,7 @@ constexpr int kPFloats = kWaves * kBlk * kRowPad * 4;
 
 __device__ __forceinline__ int q_off(int q, int blk, int ch) { return ((q * kBlk + blk) * kRowPad + ch) * 4; }
 
-template <bool BF16, int SPW, bool VEC, bool STATE>
+template <bool BF16, int SPW, bool VEC, bool STATE, bool FUSED>
 __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   using S = BCShape<SPW>;
   constexpr int NV = S::kNV;
@@ -179,6 +203,14 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
     // channel's D, the core channel's A row for this wave's states.
     const float a20 = (is_pro && iok) ? a.A[(size_t)c_io * N] * kLog2e : 0.f;
     const float dskip = (is_pro && a.D != nullptr && iok) ? a.D[c_io] : 0.f;
+    // Fused prologue: this prologue channel's taps and biases.
+    f32x4 cw = {0.f, 0.f, 0.f, 0.f};
+    float cbias = 0.f, dbias = 0.f;
+    if (FUSED && is_pro && iok) {
+      cw = *reinterpret_cast<const f32x4*>(a.conv_w + (size_t)c_io * 4);
+      cbias = a.conv_b != nullptr ? a.conv_b[c_io] : 0.f;
+      dbias = a.delta_bias != nullptr ? a.delta_bias[c_io] : 0.f;
+    }
     float A2[SPW];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -412,12 +444,55 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         ez[slot] = load_raw4<BF16, VEC>(rz_d, io_off, t, L, ok);
       };
 
+      // Fused prologue: the convolution reads the three steps before this
+      // thread's 4-step block from lane q-1 of its quad (the same channel's
+      // previous block); block 0 keeps them from lane 3 of the previous tile
+      // (hx), or, at the start of a piece, loads them (zeros before step 0).
+      float hx1 = 0.f, hx2 = 0.f, hx3 = 0.f;
+      if constexpr (PRO && FUSED) {
+        if (tb > 0) {
+          const f32x4 v = decode4(load_raw4<BF16, VEC>(ru_d, io_off, tb * kTile - 4, L, iok));
+          hx1 = v[1], hx2 = v[2], hx3 = v[3];
+        }
+      }
+      auto fuse = [&](f32x4& uu, f32x4& dd, int tile) {
+        const float p1 = quad_prev(uu[1]), p2 = quad_prev(uu[2]), p3 = quad_prev(uu[3]);
+        const bool first = io_blk == 0;
+        const float x1 = first ? hx1 : p1, x2 = first ? hx2 : p2, x3 = first ? hx3 : p3;
+        hx1 = p1, hx2 = p2, hx3 = p3;  // lane 3's last steps, for block 0 of the next tile
+        const float xs[7] = {x1, x2, x3, uu[0], uu[1], uu[2], uu[3]};
+        f32x4 c, v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float acc = cbias;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(cw[k], xs[i + k], acc);  // tap k: step t - 3 + k
+          c[i] = a.conv_silu ? silu(acc) : acc;
+          const float vi = dd[i] + dbias;
+          v[i] = a.delta_softplus ? softplus_f(vi) : vi;
+        }
+        // Steps past the piece (the tile after its last, prepared but never
+        // run, whose delta would still enter the local pass's sum of delta)
+        // and at or past L must leave the state alone: delta 0, u 0.
+        if (tile >= te || (tile + 1) * kTile > L) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool in = tile < te && tile * kTile + io_blk * 4 + i < L;
+            c[i] = in ? c[i] : 0.f;
+            v[i] = in ? v[i] : 0.f;
+          }
+        }
+        uu = c;
+        dd = v;
+      };
+
       // Prologue of one tile from ring slot `slot` into qbuf[buf]: x = delta*u,
       // then r = exp2(delta*A0*log2 e) and the start powers r^(w*SPW+1) (S4D),
       // r alone (scalar) or delta itself (general decay).
-      auto prologue = [&](int buf, int slot, auto&& refill) {
-        const f32x4 uu = decode4(pu[slot]);
-        const f32x4 dd = decode4(pd[slot]);
+      auto prologue = [&](int buf, int slot, int tile, auto&& refill) {
+        f32x4 uu = decode4(pu[slot]);
+        f32x4 dd = decode4(pd[slot]);
+        if constexpr (FUSED) fuse(uu, dd, tile);
         if constexpr (STATE) dacc += (dd[0] + dd[1]) + (dd[2] + dd[3]);  // zero past the piece and past L
         refill();  // the slot's registers are free: issue its next load now
         float* q = qbuf[buf];
@@ -470,7 +545,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       if constexpr (PRO) {
 #pragma unroll
         for (int sl = 0; sl < kPrefetch; ++sl) load_pro(tb + sl, sl);
-        prologue(tb & 1, 0, [&] { load_pro(tb + kPrefetch, 0); });
+        prologue(tb & 1, 0, tb, [&] { load_pro(tb + kPrefetch, 0); });
       } else {
         load_epi(tb - 1, 1);  // (no such tile: zeros, stores masked)
         load_epi(tb, 2);
@@ -483,7 +558,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         constexpr int S1 = (Sl + 1) % kPrefetch;
         const int buf = k & 1;
         if constexpr (PRO)  // tile k+1 into the buffer the core is not reading
-          prologue(buf ^ 1, S1, [&] { load_pro(k + 1 + kPrefetch, S1); });
+          prologue(buf ^ 1, S1, k + 1, [&] { load_pro(k + 1 + kPrefetch, S1); });
         else  // tile k-1: its partial readouts are complete since the last barrier
           epilogue(buf ^ 1, S1, k - 1, [&] { load_epi(k + 2, S1); });
         __syncthreads();
@@ -749,6 +824,12 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.ticket = flags + kMaxWG + 1;
   a.nblocks = nblocks;
   a.force_general = p.force_general ? 1 : 0;
+  a.fused = p.fused ? 1 : 0;
+  a.conv_w = p.conv_w;
+  a.conv_b = p.conv_b;
+  a.delta_bias = p.delta_bias;
+  a.conv_silu = p.conv_silu ? 1 : 0;
+  a.delta_softplus = p.delta_softplus ? 1 : 0;
   // One workgroup per compute unit at most (the kernel's LDS allows one), so
   // the balanced split covers the chip in a single wave of workgroups.
   int dev = 0, cus = 0;
@@ -762,10 +843,14 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   // With a checkpoint buffer (for the backward) every pass runs state-only.
   auto run = [&](auto state_tag) {
     constexpr bool STATE = decltype(state_tag)::value;
-    if (p.seqlen % 4 == 0)
-      hipLaunchKernelGGL((scan_kernel<BF16, SPW, true, STATE>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((scan_kernel<BF16, SPW, false, STATE>), grid, dim3(kThreads), 0, stream, a);
+    const bool vec = p.seqlen % 4 == 0;
+    if (p.fused) {
+      if (vec) hipLaunchKernelGGL((scan_kernel<BF16, SPW, true, STATE, true>), grid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((scan_kernel<BF16, SPW, false, STATE, true>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((scan_kernel<BF16, SPW, true, STATE, false>), grid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((scan_kernel<BF16, SPW, false, STATE, false>), grid, dim3(kThreads), 0, stream, a);
+    }
   };
   if (!split) {
     a.pass = kPassSingle;

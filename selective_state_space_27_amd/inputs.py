@@ -27,7 +27,7 @@ import dataclasses
 import numpy as np
 
 # Tensor ids for the per-tensor child streams.
-TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X, TID_DY = range(1, 12)
+TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X, TID_DY, TID_CONVW, TID_CONVB = range(1, 14)
 
 SEED_BASE = 27000
 
@@ -199,6 +199,34 @@ def scan_inputs(cfg: ScanConfig, with_h0: bool = False) -> dict:
     }
     del delta
     return out
+
+
+def scan_fused_inputs(cfg: ScanConfig, with_h0: bool = False) -> dict:
+    """Inputs of the scan fed by its prologue, in storage form: the raw
+    values whose short causal convolution and softplus give u and delta.
+
+    x, delta_raw, z: [b, d, l] and B, C: [b, n, l] (I/O dtype); conv_w: [d, 4]
+    ~ N(0, 0.5^2) and conv_b: [d] ~ N(0, 0.1^2) fp32; delta_raw = 0.5 N(0, 1)
+    and delta_bias = inv_softplus(dt) per channel (dt log-uniform in
+    [1e-3, 1e-1]), the workload's delta recipe before its softplus; A, D, h0
+    as in scan_inputs (S4D-real A).
+    """
+    b, d, n, L, s = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, cfg.seed
+    dt = draw_dt(s, d)
+    return {
+        "x": _io(_normal(s, TID_U, (b, d, L)), cfg.io),
+        "conv_w": (0.5 * _normal(s, TID_CONVW, (d, 4))).astype(np.float32),
+        "conv_b": (0.1 * _normal(s, TID_CONVB, (d,))).astype(np.float32),
+        "delta_raw": _io((0.5 * _normal(s, TID_DNOISE, (b, d, L))).astype(np.float32), cfg.io),
+        "delta_bias": inv_softplus(dt).astype(np.float32),
+        "A": np.ascontiguousarray(np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (d, n))),
+        "B": _io(_normal(s, TID_B, (b, n, L)), cfg.io),
+        "C": _io(_normal(s, TID_C, (b, n, L)), cfg.io),
+        "D": _normal(s, TID_D, (d,)),
+        "z": _io(_normal(s, TID_Z, (b, d, L)), cfg.io),
+        "h0": (0.1 * _normal(s, TID_H0, (b, d, n))).astype(np.float32) if with_h0 else None,
+        "io": cfg.io,
+    }
 
 
 def scan_grad_output(cfg: ScanConfig) -> np.ndarray:

@@ -82,6 +82,40 @@ def test_scan_validation_errors():
     assert scan_call(h_last=P(10)) == ALIAS           # h_last on the workspace
 
 
+def fused_call(**kw):
+    b, d, n, L = kw.pop("shape", (2, 64, 16, 128))
+    io = kw.pop("io", BF16)
+    ws_bytes = kw.pop("ws_bytes", mss.lib().mss_selective_scan_workspace_size(b, d, n, L, io, 0) or 1 << 20)
+    args = dict(x=P(0), conv_w=P(11), conv_b=P(12), delta_raw=P(1), delta_bias=P(13), A=P(2), B=P(3), C=P(4),
+                D=P(5), z=P(6), h0=P(7), y=P(8), h_last=P(9), ws=P(10), flags=mss.MSS_FLAG_DELTA_SOFTPLUS)
+    args.update(kw)
+    return mss.lib().mss_selective_scan_fwd_fused(args["x"], args["conv_w"], args["conv_b"], args["delta_raw"],
+                                                  args["delta_bias"], args["A"], args["B"], args["C"], args["D"],
+                                                  args["z"], args["h0"], args["y"], args["h_last"], b, d, n, L, io,
+                                                  args["flags"], args["ws"], ws_bytes, None)
+
+
+def test_fused_scan_validation_errors():
+    """Every error of the fused entry point comes back from the host checks
+    (fake device pointers: nothing may be enqueued)."""
+    assert fused_call(x=None) == NULL
+    assert fused_call(conv_w=None) == NULL
+    assert fused_call(delta_raw=None) == NULL
+    assert fused_call(y=None) == NULL
+    assert fused_call(shape=(2, 64, 16, 0)) == SHAPE
+    assert fused_call(io=7) == DTYPE
+    assert fused_call(shape=(2, 64, 129, 128)) == UNSUP
+    assert fused_call(flags=0x80) == UNSUP
+    assert fused_call(conv_w=P(11, 4)) == ALIGN
+    assert fused_call(delta_bias=P(13, 8)) == ALIGN
+    assert fused_call(ws=None) == WS
+    assert fused_call(ws_bytes=16) == WS
+    assert fused_call(y=P(0, 256)) == ALIAS           # y inside x
+    assert fused_call(y=P(11)) == ALIAS               # y on the taps
+    assert fused_call(h_last=P(13)) == ALIAS          # h_last on the delta bias
+    assert fused_call(h_last=P(8, 4096)) == ALIAS     # h_last inside y
+
+
 def bwd_call(**kw):
     b, d, n, L = kw.pop("shape", (2, 64, 16, 128))
     io = kw.pop("io", BF16)
