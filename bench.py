@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scan_2p8b",
                     choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "scan_m2shape", "scan_2p8b_bwd",
-                             "copy"])
+                             "scan_2p8b_fused", "copy"])
     ap.add_argument("--seqlen", type=int, default=0,
                     help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
     ap.add_argument("--batch", type=int, default=0,
@@ -69,6 +69,12 @@ def scan_bytes(b, d, n, L, es):
     """Algorithmic bytes: u, delta, z read and y written once ([b,d,L]), B and C
     read once ([b,n,L]), A [d,n] and D [d] fp32 read once."""
     return 4 * b * d * L * es + 2 * b * n * L * es + d * n * 4 + d * 4
+
+
+def scan_fused_bytes(b, d, n, L, es):
+    """The scan's bytes with x and the raw delta in place of u and delta, plus
+    the taps [d,4] and the two biases [d] (fp32) read once."""
+    return scan_bytes(b, d, n, L, es) + d * 4 * 4 + 2 * d * 4
 
 
 def scan_bwd_bytes(b, d, n, L, es):
@@ -212,6 +218,45 @@ def bench_scan(args, torch, mss, I, cfg):
                "sample": f"the whole workload (b={b}, d={d}, N={n}, L={L}) {reps} times; {dt:.2f} s wall, "
                          "fp64 C oracle"}
     return res, nbytes, ms, kernel, files, cpu
+
+
+def bench_scan_fused(args, torch, mss, I, cfg):
+    x = I.scan_fused_inputs(cfg)
+    keys = ("x", "conv_w", "conv_b", "delta_raw", "delta_bias", "A", "B", "C", "D", "z")
+    g = {k: to_dev(torch, x[k]) for k in keys}
+    io_dt = g["x"].dtype
+    b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    ws = torch.empty(mss.selective_scan_workspace_size(b, d, n, L, io_dt), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(g["x"])
+
+    def step():
+        mss.selective_scan_fwd_fused(*(g[k] for k in keys), conv_silu=True, softplus=True, out=out, workspace=ws)
+
+    ms = time_region(torch, step, args.steps, args.warmup)
+    es = 2 if cfg.io == "bf16" else 4
+    res = {
+        "metric": "state updates/s (B*L*D*N), selective scan fed by its prologue",
+        "value": b * d * n * L / (ms * 1e-3), "unit": "state updates/s", "ms_per_step": ms, "dtype": "f32",
+        "config": {"workload": f"{cfg.name}_fused: selective scan b={b} d_inner={d} d_state={n} L={L} whose u is "
+                               "silu(causal 4-tap conv of x + bias) and delta softplus(delta_raw + bias), formed in "
+                               f"the kernel; {cfg.io} x/delta_raw/B/C/z/y, fp32 taps/biases/A/D/state",
+                   "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io_dtype": cfg.io},
+    }
+    files = ["scan.hip", "scan_layout.hpp", "common.hpp"]
+    kernel = "scan_kernel with the fused prologue (+ bc_transpose_kernel in the same timed call)"
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        f64 = lambda k: I.to_f64(x[k], cfg.io)
+        th = cpu_threads()
+        call = lambda: oracle.selective_scan_fused(f64("x"), x["conv_w"], x["conv_b"], f64("delta_raw"),
+                                                   x["delta_bias"], x["A"], f64("B"), f64("C"), x["D"], f64("z"),
+                                                   conv_silu=True, softplus=True, threads=th)
+        reps, dt = repeat_timed(call)
+        cpu = {"value": reps * b * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
+               "sample": f"the whole workload (b={b}, d={d}, N={n}, L={L}) {reps} times; {dt:.2f} s wall, "
+                         "fp64 C oracle (prologue single-threaded, scan on the threads)"}
+    return res, scan_fused_bytes(b, d, n, L, es), ms, kernel, files, cpu
 
 
 def bench_scan_bwd(args, torch, mss, I, cfg):
@@ -358,7 +403,7 @@ def main():
               "the hot path shards over batch and channels with no communication, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
     if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and
-                                             args.workload in ("decode_2p8b", "copy")):
+                                             args.workload in ("decode_2p8b", "copy", "scan_2p8b_fused")):
         print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
               file=sys.stderr)
         sys.exit(2)
@@ -382,6 +427,8 @@ def main():
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_M2)
     elif args.workload == "scan_2p8b_bwd":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan_bwd(args, torch, mss, I, I.SCAN_2P8B)
+    elif args.workload == "scan_2p8b_fused":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_fused(args, torch, mss, I, I.SCAN_2P8B)
     else:
         res, nbytes, launch_ms, kernel, files, cpu = bench_copy(args, torch)
 
