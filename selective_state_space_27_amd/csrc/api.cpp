@@ -308,8 +308,10 @@ static mss_status ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads,
   if (!dtype_ok(t)) return MSS_ERR_DTYPE;
   if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || chunk <= 0)
     return MSS_ERR_SHAPE;
-  // Byte offsets inside one batch entry of y (fp32) and of B, C must fit 32 bits.
-  if (seqlen * nheads * headdim >= (int64_t{1} << 30) || seqlen * ngroups * dstate >= (int64_t{1} << 30) ||
+  // Byte offsets inside one batch entry of y (fp32) and of B, C must fit 32
+  // bits, with every descriptor at most 2^32 - 256 bytes (the kernels' "no
+  // element" offset lies past it).
+  if (seqlen * nheads * headdim > (int64_t{1} << 30) - 64 || seqlen * ngroups * dstate >= (int64_t{1} << 30) ||
       batch > 65535 || nheads > 65535)
     return MSS_ERR_SHAPE;
   if (t != MSS_BF16) return MSS_ERR_UNSUPPORTED;

@@ -48,7 +48,11 @@ namespace mss {
 // precise, which lets loads issued several tiles ahead stay in flight).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every descriptor used here
+// An offset at or past the end of every descriptor used here: the host checks
+// keep each descriptor at most 2^32 - 256 bytes long (a 64-channel block of
+// fp32 scan rows reaches exactly that at seqlen 2^24 - 1), and the largest
+// access (16 bytes) from this offset does not wrap 32 bits.
+constexpr uint32_t kOffNone = 0xFFFFFF00u;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);

@@ -229,6 +229,34 @@ def scan_fused_inputs(cfg: ScanConfig, with_h0: bool = False) -> dict:
     }
 
 
+def scan_inputs_device(cfg: ScanConfig, device="cuda:0") -> dict:
+    """The scan_inputs distributions (S4D-real A) drawn on the device with
+    torch's seeded generator, for sizes whose host draw would be too slow;
+    fp32 I/O.  The values differ from scan_inputs' (another generator) but are
+    as reproducible: same cfg, same tensors."""
+    import torch
+    b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    dt = torch.exp(torch.empty(d, device=device, dtype=torch.float64).uniform_(np.log(1e-3), np.log(1e-1), generator=g))
+    bias = (dt + torch.log(-torch.expm1(-dt))).view(1, d, 1)  # inverse softplus
+    delta = torch.empty((b, d, L), device=device, dtype=torch.float32)
+    for i in range(b):  # softplus(0.5 eps + bias) per batch row, in fp64
+        eps = torch.randn((d, L), **kw).double()
+        delta[i] = torch.nn.functional.softplus(0.5 * eps + bias[0], threshold=40.0).float()
+        del eps
+    return {
+        "u": torch.randn((b, d, L), **kw),
+        "delta": delta,
+        "A": -(torch.arange(n, device=device, dtype=torch.float32) + 1.0).repeat(d, 1),
+        "B": torch.randn((b, n, L), **kw),
+        "C": torch.randn((b, n, L), **kw),
+        "D": torch.randn((d,), **kw),
+        "z": torch.randn((b, d, L), **kw),
+    }
+
+
 def scan_grad_output(cfg: ScanConfig) -> np.ndarray:
     """dy = dloss/dy [b, d, l] ~ N(0, 1) in the I/O dtype, for the backward."""
     return _io(_normal(cfg.seed, TID_DY, (cfg.batch, cfg.dim, cfg.seqlen)), cfg.io)

@@ -70,6 +70,8 @@ def test_scan_validation_errors():
     assert scan_call(shape=(2, -1, 16, 128)) == SHAPE
     assert scan_call(shape=(2, 64, 16, 0)) == SHAPE
     assert scan_call(shape=(2, 1 << 20, 16, 1 << 12)) == SHAPE
+    assert scan_call(shape=(1, 64, 16, 1 << 24)) == SHAPE         # seqlen at 2^24
+    assert scan_call(shape=(1, 256, 16, 1 << 23)) == SHAPE        # dim*seqlen = 2^31, seqlen < 2^24
     assert scan_call(io=7) == DTYPE
     assert scan_call(shape=(2, 64, 129, 128)) == UNSUP
     assert scan_call(flags=0x80) == UNSUP
@@ -205,6 +207,11 @@ def test_ssd_validation_errors():
     assert ssd_call(shape=(2, 1024, 8, 64, 1, 64, 256)) == UNSUP      # dstate
     assert ssd_call(shape=(2, 1024, 8, 64, 1, 128, 100)) == UNSUP     # chunk
     assert ssd_call(shape=(2, 1024, 6, 64, 4, 128, 256)) == UNSUP     # nheads % ngroups
+    # y's rows of one batch entry stay within 2^32 - 256 bytes: L*H*P <= 2^30 - 64.
+    ws = lambda L, H: mss.lib().mss_ssd_workspace_size(1, L, H, 64, 1, 128, 256, BF16)
+    assert ws((1 << 16) - 1, 256) > 0
+    assert ws(1 << 16, 256) == 0
+    assert ws((1 << 24) - 1, 64) == 0 and ws(1 << 22, 64) == 0
     assert ssd_call(flags=2) == UNSUP
     assert ssd_call(B=P(3, 4)) == ALIGN
     assert ssd_call(ws=None) == WS

@@ -289,3 +289,24 @@ def test_scan_causality_and_nan_propagation():
     others = torch.cat([y3[0, :9], y3[0, 10:]])
     assert not torch.isnan(others).any()
     assert torch.isnan(h3[0, 9]).all()
+
+
+def test_scan_maximum_sizes_sampled():
+    """At the documented limits: seqlen just under 2^24 and dim*seqlen just
+    under 2^31, fp32 I/O (where a 64-channel block's rows come closest to the
+    32-bit byte offsets), ragged L, two blocks for the whole chip (split
+    passes).  Inputs drawn on the device (seeded); sampled channels over the
+    whole sequence against the oracle."""
+    L = (1 << 24) - 5
+    cfg = I.small_scan_config(1, 128, 16, L, "fp32", seed=I.SEED_BASE + 900)
+    g = I.scan_inputs_device(cfg)
+    y, hl = mss.selective_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                   return_last_state=True)
+    torch.cuda.synchronize()
+    chans = [0, 77, 127]
+    h = lambda t: t.detach().cpu().numpy().astype(np.float64)
+    ry, rh = oracle.selective_scan(h(g["u"][:, chans]), h(g["delta"][:, chans]), h(g["A"][chans]), h(g["B"]),
+                                   h(g["C"]), h(g["D"][chans]), h(g["z"][:, chans]))
+    e1 = assert_close(h(y[:, chans]), ry, "fp32", "y")
+    e2 = assert_close(h(hl[:, chans]), rh, "fp32", "h_last")
+    print(f"maximum sizes: y {e1:.2e} h_last {e2:.2e}")
