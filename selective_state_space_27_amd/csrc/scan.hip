@@ -308,7 +308,13 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       // term 0, and the update leaves h unchanged.
       constexpr int kAhead = SPW <= 4 ? kBlk : 1;
       const int sp_slot = wc == 0 ? 1 : 2 + wc;  // start power r^(wc*SPW+1): r itself for wave 0
-      auto core_tile = [&](int buf, int k, const f32x4* bc_cur) {
+      // W0: 1 = wave 0, whose readout starts from D*u, 0 = another wave (a
+      // separate copy of the loop, so the other waves keep a plain multiply
+      // for their first term); 2 = either, wave 0 adding D*u to its block's
+      // partials afterwards (SPW >= 4, whose registers do not allow two
+      // copies of the loop).
+      auto core_tile = [&](auto w0_tag, int buf, int k, const f32x4* bc_cur) {
+        constexpr int W0 = decltype(w0_tag)::value;
         const float* q = qbuf[buf];
         float* pp = pbuf[buf];
         f32x4 xvs[kAhead], rvs[kAhead], svs[kAhead];
@@ -337,10 +343,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           if constexpr (kAhead == 1) read_blk(blk, 0);
           const int i = kAhead == kBlk ? blk : 0;
           const f32x4 xv = xvs[i], rv = rvs[i], sv = svs[i];
-          f32x4 duv = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (!STATE) {
-            if (wc == 0) duv = *reinterpret_cast<const f32x4*>(&q[q_off(kQDu, blk, lane)]);
-          }
+          f32x4 duv;
+          if constexpr (W0 == 1 && !STATE) duv = *reinterpret_cast<const f32x4*>(&q[q_off(kQDu, blk, lane)]);
           f32x4 part;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
@@ -366,13 +370,17 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
               // values than registers; an empty asm per step keeps each h.
               if constexpr (STATE) asm volatile("" : "+v"(h[j]));
               if constexpr (!STATE) {  // the state-only passes need no readout
-                if (j == 0)
-                  p = fmac_row_bcast_rt(duv[kk], bcv(ic), h[j], ic % 16);
-                else
+                if (j == 0) {
+                  if constexpr (W0 == 1) p = fmac_row_bcast_rt(duv[kk], bcv(ic), h[j], ic % 16);
+                  else p = row_bcast_rt(bcv(ic), ic % 16) * h[j];
+                } else
                   p = fmac_row_bcast_rt(p, bcv(ic), h[j], ic % 16);
               }
             }
             part[kk] = p;
+          }
+          if constexpr (W0 == 2 && !STATE) {
+            if (wc == 0) part += *reinterpret_cast<const f32x4*>(&q[q_off(kQDu, blk, lane)]);
           }
           if constexpr (!STATE) *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
         }
@@ -392,7 +400,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       if constexpr (kBlkBC) {
         for (int k = tb; k < te; ++k) {
           checkpoint(k);
-          core_tile(k & 1, k, nullptr);
+          core_tile(std::integral_constant<int, 2>{}, k & 1, k, nullptr);
           __syncthreads();
         }
       } else {
@@ -401,7 +409,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           constexpr int S2 = (Sl + 2) % kPrefetch;
           load_bc(k + 2, bct[S2]);  // past the last tile: reads zeros, unused
           checkpoint(k);
-          core_tile(k & 1, k, bct[Sl]);
+          if constexpr (SPW > 2) core_tile(std::integral_constant<int, 2>{}, k & 1, k, bct[Sl]);
+          else if (wc == 0) core_tile(std::integral_constant<int, 1>{}, k & 1, k, bct[Sl]);
+          else core_tile(std::integral_constant<int, 0>{}, k & 1, k, bct[Sl]);
           __syncthreads();
         };
         int k = tb;
