@@ -315,6 +315,30 @@ def ssd_inputs(cfg: SSDConfig, with_h0: bool = False) -> dict:
     }
 
 
+def ssd_inputs_device(cfg: SSDConfig, device="cuda:0") -> dict:
+    """The ssd_inputs distributions drawn on the device with torch's seeded
+    generator (sizes whose host draw would be too slow): x, B, C bf16, delta
+    and A fp32.  Reproducible per cfg; the values differ from ssd_inputs'."""
+    import torch
+    b, L, H, P, G, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    dt = torch.exp(torch.empty(H, device=device, dtype=torch.float64).uniform_(np.log(1e-3), np.log(1e-1), generator=g))
+    bias = dt + torch.log(-torch.expm1(-dt))  # inverse softplus
+    eps = torch.randn((b, L, H), **kw).double()
+    delta = torch.nn.functional.softplus(0.5 * eps + bias, threshold=40.0).float()
+    del eps
+    A = -torch.exp(torch.empty(H, device=device, dtype=torch.float32).uniform_(0.0, float(np.log(16.0)), generator=g))
+    return {
+        "x": torch.randn((b, L, H, P), **kw).to(torch.bfloat16),
+        "delta": delta,
+        "A": A,
+        "B": torch.randn((b, L, G, N), **kw).to(torch.bfloat16),
+        "C": torch.randn((b, L, G, N), **kw).to(torch.bfloat16),
+    }
+
+
 def small_scan_config(batch, dim, dstate, seqlen, io="fp32", seed=SEED_BASE + 100, a_form="s4d",
                       head=64) -> ScanConfig:
     return ScanConfig(f"scan_b{batch}_d{dim}_n{dstate}_l{seqlen}_{io}_{a_form}", batch, dim, dstate, seqlen, io, seed,

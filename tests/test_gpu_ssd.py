@@ -148,3 +148,25 @@ def test_ssd_sequence_cut_into_pieces(case):
     e3 = assert_close(host64(hl)[:, sel], rhl, "bf16", "h_last")
     print(f"{case}: y {e1:.2e} chunk_states {e2:.2e} h_last {e3:.2e}")
     assert e1 < 5e-3 and e2 < 5e-3
+
+
+def test_ssd_maximum_sizes_sampled():
+    """At the documented limit: L*H*P just under 2^30 (y's fp32 rows of one
+    batch entry just under 4 GB), ragged L, 64 pieces in the state pass;
+    inputs drawn on the device (seeded); two heads against the oracle over
+    the whole sequence."""
+    L, H, Q = (1 << 20) - 1, 16, 256
+    cfg = I.small_ssd_config(1, L, H, 64, 1, 128, Q, seed=I.SEED_BASE + 901)
+    g = I.ssd_inputs_device(cfg)
+    y, cs, hl = mss.ssd_chunk_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], chunk=Q, return_chunk_states=True,
+                                  return_last_state=True)
+    torch.cuda.synchronize()
+    heads = np.array([0, 15])
+    x64 = host64(g["x"][:, :, heads])
+    ry, rcs, rhl = oracle.ssd(x64, host64(g["delta"][:, :, heads]), host64(g["A"][heads]), host64(g["B"]),
+                              host64(g["C"]), None, None, None, chunk=Q)
+    e1 = assert_close(host64(y[:, :, heads]), ry, "bf16", "y")
+    e2 = assert_close(host64(cs[:, :, heads]), rcs, "bf16", "chunk_states")
+    e3 = assert_close(host64(hl[:, heads]), rhl, "bf16", "h_last")
+    print(f"ssd maximum sizes: y {e1:.2e} chunk_states {e2:.2e} h_last {e3:.2e}")
+    assert e1 < 5e-3 and e2 < 5e-3
