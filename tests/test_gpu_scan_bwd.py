@@ -160,3 +160,28 @@ def test_scan_bwd_2p8b_workload():
     errs.update(check({"dA": got["dA"][chans], "dD": got["dD"][chans]}, refc, "bf16", keys=("dA", "dD")))
     print("scan_2p8b bwd:", {k: f"{v:.1e}" for k, v in errs.items()})
     assert rel_err(got["dh0"][:1], ref["dh0"]) < 1e-2
+
+
+def test_scan_bwd_maximum_sizes_sampled():
+    """At the documented limits (fp32, L = 2^24 - 5, dim*L just under 2^31,
+    split passes): du, ddelta, dz, dA, dD of sampled channels against the
+    oracle over the whole sequence (dB, dC sum over every channel and are
+    left to the smaller cases).  Inputs drawn on the device (seeded)."""
+    L = (1 << 24) - 5
+    cfg = I.small_scan_config(1, 128, 16, L, "fp32", seed=I.SEED_BASE + 902)
+    g = I.scan_inputs_device(cfg)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(cfg.seed + 1)
+    dy = torch.randn((1, 128, L), generator=gen, device="cuda:0", dtype=torch.float32)
+    r = mss.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], dy=dy)
+    torch.cuda.synchronize()
+    chans = [0, 77, 127]
+    h = lambda t: t.detach().cpu().numpy().astype(np.float64)
+    ref = oracle.selective_scan_bwd(h(g["u"][:, chans]), h(g["delta"][:, chans]), h(g["A"][chans]), h(g["B"]),
+                                    h(g["C"]), h(g["D"][chans]), h(g["z"][:, chans]), None, h(dy[:, chans]), None)
+    errs = {}
+    for k in ("du", "ddelta", "dz"):
+        errs[k] = assert_close(h(r[k][:, chans]), ref[k], "fp32", k)
+    for k in ("dA", "dD"):
+        errs[k] = assert_close(h(r[k][chans]), ref[k], "fp32", k)
+    print("bwd maximum sizes:", {k: f"{v:.1e}" for k, v in errs.items()})
