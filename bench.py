@@ -13,7 +13,7 @@ the dominant kernel (algorithmic bytes / event-timed launch duration against
 8 TB/s HBM3E) and the fp64 CPU oracle's throughput on a bounded sample of the
 same workload, timed on this host's cores.
 
-Other workloads (for the record in the design doc, not the headline):
+Other workloads (measured for the record, not the headline):
   scan_130m    b8 x d1536 x N16 x L2048, fp32 I/O
   decode_2p8b  b256 x d5120 x N16 one-token steps, bf16 I/O; one step = 1000 tokens
   ssd_2p8b     b2 x L16384 x H80 x P64 x N128, chunk 256 (Mamba-2 SSD)
@@ -21,6 +21,8 @@ Other workloads (for the record in the design doc, not the headline):
                64 channels) x N128 x L16384, A and delta shared within a head
   scan_2p8b_bwd  the backward (gradients of u, delta, A, B, C, D, z) of the
                headline scan, one mss_selective_scan_bwd call per step
+  scan_2p8b_fused  the headline scan fed by its prologue (u from the silu of
+               the causal 4-tap convolution of x, delta = softplus(raw + bias))
   copy         a plain 1 GiB device copy (calibrates the HBM byte counters)
 
 --seqlen L and --batch B (scan and SSD workloads) time the same workload at
@@ -400,7 +402,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
-              "the hot path shards over batch and channels with no communication, see DESIGN.md", file=sys.stderr)
+              "the hot path shards over batch and channels with no communication", file=sys.stderr)
         sys.exit(2)
     if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and
                                              args.workload in ("decode_2p8b", "copy", "scan_2p8b_fused")):

@@ -83,7 +83,8 @@ SSD_2P8B = SSDConfig("ssd_2p8b", 2, 16384, 80, 64, 1, 128, 256, SEED_BASE + 4)
 SCAN_M2 = ScanConfig("scan_m2shape", 2, 5120, 128, 16384, "bf16", SEED_BASE + 5, a_form="head")
 
 # Distinct per-step input sets drawn for the 1000-step decode workload; step s
-# uses set s % DECODE_POOL (input recipe).
+# uses set s % DECODE_POOL (the kernel's work does not depend on the values, and
+# this keeps input generation and host memory bounded).
 DECODE_POOL = 16
 
 
