@@ -95,6 +95,18 @@ def test_fused_decay_modes(mode):
     check(run_gpu(x, force_general=mode == "general"), run_oracle(x), "fp32", mode)
 
 
+@pytest.mark.parametrize("shape", [(1, 192, 128, 70, "bf16"), (2, 130, 64, 101, "fp32"), (1, 64, 32, 48, "fp32")],
+                         ids=["n128", "n64_ragged", "n32"])
+def test_fused_wide_states(shape):
+    """d_state 128, 64 and 32 (16, 8 and 4 states per core wave): the other
+    instantiations of the fused prologue, with the general decay path too."""
+    b, d, n, L, io = shape
+    x = I.scan_fused_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    ref = run_oracle(x, True, True)
+    check(run_gpu(x, True, True), ref, io, str(shape))
+    check(run_gpu(x, True, True, force_general=True), ref, io, f"{shape} general")
+
+
 @pytest.mark.parametrize("shape", [(2, 12800, 16, 45, "bf16"), (1, 128, 16, 16384, "fp32"),
                                    (1, 5120, 16, 4096, "bf16"), (2, 100, 16, 20001, "fp32")],
                          ids=["carry_handoff", "split_passes", "split_b1_layer", "split_ragged"])
