@@ -202,7 +202,7 @@ size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t
 /*                                                                          */
 /* Layouts: h [batch, dim, dstate] fp32;  u, delta, z, y [batch, dim];       */
 /*          B, C [batch, dstate];  A [dim, dstate] fp32;  D [dim] fp32.      */
-/* D and z may be NULL.  Supported: 1 <= dstate <= 64.  `flags` must be 0.  */
+/* D and z may be NULL.  Supported: 1 <= dstate <= 128.  `flags` must be 0. */
 /* y must not overlap h or any input; h must not overlap any input.          */
 /* ------------------------------------------------------------------------ */
 mss_status mss_state_update(float* h, const void* u, const void* delta, const float* A,

@@ -270,7 +270,7 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
   if (!dtype_ok(io_dtype)) return MSS_ERR_DTYPE;
   if (batch <= 0 || dim <= 0 || dstate <= 0) return MSS_ERR_SHAPE;
   if (batch * dim * dstate > kMaxIndex * 4LL || batch * dim * 4 > kMaxIndex * 64LL) return MSS_ERR_SHAPE;
-  if (dstate > 64) return MSS_ERR_UNSUPPORTED;
+  if (dstate > 128) return MSS_ERR_UNSUPPORTED;
   if (flags != 0) return MSS_ERR_UNSUPPORTED;
   const void* all[] = {h, u, delta, A, B, C, D, z, y};
   for (const void* p : all)

@@ -7,9 +7,10 @@
 //   h[n] <- exp(delta*A[d,n]) * h[n] + delta*B[b,n]*u ;  y = (C.h + D*u) * silu(z)
 //
 // The step is a pure stream over the fp32 state (read once, written once), so
-// the kernel is laid out for HBM: 4 consecutive lanes own one channel's state
-// row, each lane a contiguous slice of SPL states, so one wave instruction
-// touches one contiguous span of the state (1 KB for N = 16).  Each thread
+// the kernel is laid out for HBM: LPC consecutive lanes (4, or 8 for N > 64)
+// own one channel's state row, each lane a contiguous slice of SPL states, so
+// one wave instruction touches one contiguous span of the state (1 KB for
+// N = 16).  Each thread
 // handles kRows channel rows 16 channels apart and issues every load of all
 // of them before any arithmetic, so a wave keeps kRows such spans in flight
 // (the step is bound by how many state bytes are in flight, not by
@@ -22,7 +23,6 @@
 namespace mss {
 namespace {
 
-constexpr int kLanesPerChannel = 4;
 constexpr int kRows = 2;
 constexpr int kThreadsSU = 256;
 
@@ -51,7 +51,7 @@ __device__ __forceinline__ void load_vec(const void* p, size_t off, int n0, int 
   for (int j = 0; j < SPL; ++j) v[j] = (n0 + j < N) ? load_io<BF16>(p, off + j) : 0.f;
 }
 
-template <bool BF16, int SPL>
+template <bool BF16, int SPL, int LPC>
 __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restrict__ h, const void* __restrict__ u,
                                                                  const void* __restrict__ delta,
                                                                  const float* __restrict__ A,
@@ -62,13 +62,14 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
                                                                  int batch, int dim, int N) {
   const size_t gid = (size_t)blockIdx.x * kThreadsSU + threadIdx.x;
   const int lane = threadIdx.x & 63;
-  const int q = lane % kLanesPerChannel;  // slice of the state row
+  constexpr int kCh = 64 / LPC;  // channels per row set of a wave
+  const int q = lane % LPC;       // slice of the state row
   const int n0 = q * SPL;
-  // A wave covers 16 consecutive channels per row set and kRows row sets.
-  const size_t row0 = (gid >> 6) * (16 * kRows) + (size_t)(lane / kLanesPerChannel);
+  // A wave covers kCh consecutive channels per row set and kRows row sets.
+  const size_t row0 = (gid >> 6) * (kCh * kRows) + (size_t)(lane / LPC);
   const size_t nrows = (size_t)batch * dim;
-  // Vector loads need whole aligned slices: N a multiple of 4 lanes * SPL.
-  const bool full = (N == kLanesPerChannel * SPL) && (SPL % 4 == 0);
+  // Vector loads need whole aligned slices: N equal to LPC lanes * SPL.
+  const bool full = (N == LPC * SPL) && (SPL % 4 == 0);
   const bool bc_fast = full && ((N * (BF16 ? 2 : 4)) % 8 == 0);
 
   float hv[kRows][SPL], av[kRows][SPL], bv[kRows][SPL], cv[kRows][SPL];
@@ -76,7 +77,7 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
   bool act[kRows];
 #pragma unroll
   for (int k = 0; k < kRows; ++k) {
-    const size_t bd = row0 + (size_t)k * 16;
+    const size_t bd = row0 + (size_t)k * kCh;
     act[k] = bd < nrows;
     const size_t bds = act[k] ? bd : 0;
     const int b = (int)(bds / dim);
@@ -117,11 +118,11 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
       hv[k][j] = __builtin_fmaf(dec, hv[k][j], du * bv[k][j]);
       p = __builtin_fmaf(cv[k][j], hv[k][j], p);
     }
-    // Fixed-order butterfly over the 4 lanes of the channel.
-    p += __shfl_xor(p, 1, kLanesPerChannel);
-    p += __shfl_xor(p, 2, kLanesPerChannel);
+    // Fixed-order butterfly over the LPC lanes of the channel.
+#pragma unroll
+    for (int m = 1; m < LPC; m <<= 1) p += __shfl_xor(p, m, LPC);
     if (!act[k]) continue;
-    const size_t bd = row0 + (size_t)k * 16;
+    const size_t bd = row0 + (size_t)k * kCh;
     float* hrow = h + bd * N;
     if (full) {
 #pragma unroll
@@ -142,12 +143,13 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
   }
 }
 
-template <bool BF16, int SPL>
+template <bool BF16, int SPL, int LPC = 4>
 hipError_t launch_typed(const UpdateParams& p, hipStream_t stream) {
+  constexpr int kCh = 64 / LPC;
   const size_t rows = (size_t)p.batch * p.dim;
-  const size_t waves = (rows + 16 * kRows - 1) / (16 * kRows);
+  const size_t waves = (rows + kCh * kRows - 1) / (kCh * kRows);
   const unsigned grid = (unsigned)((waves * 64 + kThreadsSU - 1) / kThreadsSU);
-  hipLaunchKernelGGL((state_update_kernel<BF16, SPL>), dim3(grid), dim3(kThreadsSU), 0, stream, p.h, p.u, p.delta,
+  hipLaunchKernelGGL((state_update_kernel<BF16, SPL, LPC>), dim3(grid), dim3(kThreadsSU), 0, stream, p.h, p.u, p.delta,
                      p.A, p.B, p.C, p.D, p.z, p.y, (int)p.batch, (int)p.dim, (int)p.dstate);
   return hipGetLastError();
 }
@@ -159,7 +161,8 @@ hipError_t launch_dtype(const UpdateParams& p, hipStream_t stream) {
   if (n <= 8) return launch_typed<BF16, 2>(p, stream);
   if (n <= 16) return launch_typed<BF16, 4>(p, stream);
   if (n <= 32) return launch_typed<BF16, 8>(p, stream);
-  return launch_typed<BF16, 16>(p, stream);
+  if (n <= 64) return launch_typed<BF16, 16>(p, stream);
+  return launch_typed<BF16, 16, 8>(p, stream);  // up to 128 states: 8 lanes of 16
 }
 
 }  // namespace

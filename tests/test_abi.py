@@ -177,7 +177,7 @@ def test_state_update_validation_errors():
     assert update_call(B=None) == NULL
     assert update_call(shape=(4, 0, 16)) == SHAPE
     assert update_call(io=5) == DTYPE
-    assert update_call(shape=(4, 64, 80)) == UNSUP
+    assert update_call(shape=(4, 64, 129)) == UNSUP
     assert update_call(flags=1) == UNSUP
     assert update_call(u=P(1, 8)) == ALIGN
     assert update_call(y=P(1, 16)) == ALIAS          # y overlaps u

@@ -25,7 +25,7 @@ def small(b, d, n, io, seed=5):
 
 
 @pytest.mark.parametrize("io", ["fp32", "bf16"])
-@pytest.mark.parametrize("n", [1, 4, 5, 16, 24, 64])
+@pytest.mark.parametrize("n", [1, 4, 5, 16, 24, 64, 65, 100, 128])
 def test_state_update_shapes(io, n):
     s = small(3, 50, n, io)
     h = dev(s["h"])
