@@ -10,20 +10,24 @@
 // the kernel is laid out for HBM: LPC consecutive lanes (4, or 8 for N > 64)
 // own one channel's state row, each lane a contiguous slice of SPL states, so
 // one wave instruction touches one contiguous span of the state (1 KB for
-// N = 16).  Each thread
-// handles kRows channel rows 16 channels apart and issues every load of all
-// of them before any arithmetic, so a wave keeps kRows such spans in flight
-// (the step is bound by how many state bytes are in flight, not by
-// arithmetic; two rows measured best, more rows cost occupancy).  The new
-// state is written with non-temporal stores.  The partial readouts of the 4 lanes are combined with a fixed
-// butterfly (bitwise deterministic).  Decays use one hardware exp per state.
+// N = 16).  Each thread handles kRows channel rows (two for N <= 64, one
+// above) 64/LPC channels apart and issues every load of all of them before
+// any arithmetic, so a wave keeps kRows such spans in flight (the step is
+// bound by how many state bytes are in flight, not by arithmetic; two rows
+// measured best at N = 16, more rows cost occupancy).  The new state is
+// written with non-temporal stores.  The partial readouts of a channel's
+// lanes are combined with a fixed butterfly (bitwise deterministic).  Decays
+// use one hardware exp per state.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mss {
 namespace {
 
-constexpr int kRows = 2;
+// Channel rows per thread: two for N <= 64 (measured best there); one for the
+// 8-lane rows above 64, whose 16 states per lane already fill the registers.
+template <int LPC>
+constexpr int rows_per_thread() { return LPC == 4 ? 2 : 1; }
 constexpr int kThreadsSU = 256;
 
 template <bool BF16>
@@ -32,17 +36,21 @@ __device__ __forceinline__ float load_io(const void* p, size_t i) {
   else return static_cast<const float*>(p)[i];
 }
 
-// SPL consecutive B (or C) values from n0 of batch row b.
+// SPL consecutive B (or C) values from n0 of batch row b: 4 at a time when
+// the slices are whole and aligned (`fast`), else one by one with a bound.
 template <bool BF16, int SPL>
 __device__ __forceinline__ void load_vec(const void* p, size_t off, int n0, int N, bool fast, float* v) {
-  if constexpr (SPL == 4) {
+  if constexpr (SPL % 4 == 0) {
     if (fast) {
-      if constexpr (BF16) {
-        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + off);
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-      } else {
-        const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + off);
-        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+#pragma unroll
+      for (int j = 0; j < SPL; j += 4) {
+        if constexpr (BF16) {
+          const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + off + j);
+          v[j] = bf16_lo(w.x); v[j + 1] = bf16_hi(w.x); v[j + 2] = bf16_lo(w.y); v[j + 3] = bf16_hi(w.y);
+        } else {
+          const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + off + j);
+          v[j] = w.x; v[j + 1] = w.y; v[j + 2] = w.z; v[j + 3] = w.w;
+        }
       }
       return;
     }
@@ -63,6 +71,7 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
   const size_t gid = (size_t)blockIdx.x * kThreadsSU + threadIdx.x;
   const int lane = threadIdx.x & 63;
   constexpr int kCh = 64 / LPC;  // channels per row set of a wave
+  constexpr int kRows = rows_per_thread<LPC>();
   const int q = lane % LPC;       // slice of the state row
   const int n0 = q * SPL;
   // A wave covers kCh consecutive channels per row set and kRows row sets.
@@ -146,6 +155,7 @@ __global__ void __launch_bounds__(kThreadsSU) state_update_kernel(float* __restr
 template <bool BF16, int SPL, int LPC = 4>
 hipError_t launch_typed(const UpdateParams& p, hipStream_t stream) {
   constexpr int kCh = 64 / LPC;
+  constexpr int kRows = rows_per_thread<LPC>();
   const size_t rows = (size_t)p.batch * p.dim;
   const size_t waves = (rows + kCh * kRows - 1) / (kCh * kRows);
   const unsigned grid = (unsigned)((waves * 64 + kThreadsSU - 1) / kThreadsSU);
