@@ -171,9 +171,11 @@ mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, cons
 /* D = 0); dz [batch, dim, seqlen] io_dtype, given exactly when z is (else    */
 /* MSS_ERR_NULL); dh0 [batch, dim, dstate] fp32 (NULL = not computed; the     */
 /* gradient of the initial state, h0 or zero).                              */
-/* Supported: 1 <= dstate <= 16 (else MSS_ERR_UNSUPPORTED), the scan's other */
-/* limits.  flags: 0 or MSS_FLAG_DECAY_GENERAL (as in the forward).  Outputs */
-/* must not overlap any input or each other.  The workspace (size from       */
+/* Supported: 1 <= dstate <= 32 (else MSS_ERR_UNSUPPORTED), the scan's other */
+/* limits, and 2*batch*dstate*seqlen + dim*(dstate+1) at most 2^39 - 256     */
+/* (else MSS_ERR_SHAPE).  flags: 0 or MSS_FLAG_DECAY_GENERAL (as in the      */
+/* forward).  Outputs must not overlap any input or each other.  The         */
+/* workspace (size from                                                      */
 /* mss_selective_scan_bwd_workspace_size) need not be zeroed.                */
 /* ------------------------------------------------------------------------ */
 mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B,

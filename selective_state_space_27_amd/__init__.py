@@ -248,7 +248,7 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
     dy = dloss/dy [b, d, L] and optionally dh_last = dloss/dh_last [b, d, N]
     float32.  Returns a dict: du, ddelta, dz (None without z) [b, d, L] and dB,
     dC [b, N, L] in the I/O dtype; dA [d, N], dD [d] (None unless want_dD) and
-    dh0 [b, d, N] (None unless want_dh0) in float32.  d_state <= 16.  ``out``:
+    dh0 [b, d, N] (None unless want_dh0) in float32.  d_state <= 32.  ``out``:
     a dict from an earlier call with the same shapes whose tensors are
     written again (nothing is allocated for them)."""
     dev = _device_of(u)

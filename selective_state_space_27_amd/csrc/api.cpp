@@ -190,10 +190,21 @@ mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, cons
 }
 
 // --------------------------------------------------- selective scan backward
+// The forward's limits, d_state <= 32 (up to 4 states per wave), and one
+// reduction thread per dB, dC, dA, dD element within a one-dimensional grid.
+static mss_status scan_bwd_check_shape(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype t) {
+  const mss_status st = scan_check_shape(batch, dim, dstate, seqlen, t);
+  if (st != MSS_OK) return st;
+  if (dstate > 32) return MSS_ERR_UNSUPPORTED;
+  const int64_t reduce_threads = 2 * batch * dstate * seqlen + dim * dstate + dim;
+  if ((reduce_threads + 255) / 256 > kMaxIndex) return MSS_ERR_SHAPE;
+  return MSS_OK;
+}
+
 size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                              mss_dtype io_dtype, uint32_t flags) {
   (void)flags;
-  if (scan_check_shape(batch, dim, dstate, seqlen, io_dtype) != MSS_OK || dstate > 16) return 0;
+  if (scan_bwd_check_shape(batch, dim, dstate, seqlen, io_dtype) != MSS_OK) return 0;
   return mss::scan_bwd_workspace_bytes(batch, dim, dstate, seqlen);
 }
 
@@ -205,9 +216,8 @@ mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float*
                                   size_t workspace_bytes, void* hip_stream) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return MSS_ERR_NULL;
   if ((z == nullptr) != (dz == nullptr)) return MSS_ERR_NULL;
-  mss_status st = scan_check_shape(batch, dim, dstate, seqlen, io_dtype);
+  mss_status st = scan_bwd_check_shape(batch, dim, dstate, seqlen, io_dtype);
   if (st != MSS_OK) return st;
-  if (dstate > 16) return MSS_ERR_UNSUPPORTED;
   if (flags & ~MSS_FLAG_DECAY_GENERAL) return MSS_ERR_UNSUPPORTED;
   const void* all[] = {u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
   for (const void* p : all)

@@ -239,22 +239,58 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---- states of the 16 steps, from the checkpoint ----
-    float h[kTile][SPW];
+    // Up to 2 states per wave all 16 steps are held in registers.  With 4 or
+    // 8, only the state entering each 4-step block is (hb), and the gradient
+    // loop recomputes the block's 4 steps from it: 8 x SPW registers instead
+    // of 16 x SPW, which keeps the kernel within 256 VGPRs without spilling.
+    constexpr bool kReBlk = SPW >= 4;
+    constexpr int kHeld = kReBlk ? 4 : kTile;
+    auto fwd = [&](int t, int j, float hp) __attribute__((always_inline)) {
+      const int blk = t / 4, kk = t % 4, ib = kk * 2 * SPW + j;
+      return __builtin_fmaf(exp2_fast(s_in[1][t][lane] * A2[j]), hp,
+                            row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * s_in[0][t][lane]);
+    };
+    float h[kHeld][SPW];
+    float hb[kReBlk ? kBlk : 1][SPW];
+    if constexpr (!kReBlk) {
 #pragma unroll
-    for (int t = 0; t < kTile; ++t) {
-      const int blk = t / 4, kk = t % 4;
-      const float x = s_in[0][t][lane], dl = s_in[1][t][lane];
+      for (int t = 0; t < kTile; ++t) {
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int ib = kk * 2 * SPW + j;
-        const float hp = t > 0 ? h[t - 1][j] : hs[j];
-        h[t][j] = __builtin_fmaf(exp2_fast(dl * A2[j]), hp, row_bcast_rt(bc_cur[ib / 16][blk], ib % 16) * x);
+        for (int j = 0; j < SPW; ++j) h[t][j] = fwd(t, j, t > 0 ? h[t - 1][j] : hs[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) hb[0][j] = hs[j];
+#pragma unroll
+      for (int t = 0; t < kTile - 4; ++t) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          const float hn = fwd(t, j, t % 4 > 0 ? h[t % 4 - 1][j] : hb[t / 4][j]);
+          if (t % 4 == 3) hb[t / 4 + 1][j] = hn;
+          else h[t % 4][j] = hn;
+        }
       }
     }
+    // state after step blk*4 + kk, and the one before it
+    auto h_at = [&](int blk, int kk, int j) __attribute__((always_inline)) {
+      if constexpr (kReBlk) return h[kk][j];
+      else return h[blk * 4 + kk][j];
+    };
+    auto h_before = [&](int blk, int kk, int j) __attribute__((always_inline)) {
+      if constexpr (kReBlk) return kk > 0 ? h[kk - 1][j] : hb[blk][j];
+      else return blk * 4 + kk > 0 ? h[blk * 4 + kk - 1][j] : hs[j];
+    };
 
     // ---- gradient, 4-step blocks in reverse ----
 #pragma unroll
     for (int blk = kBlk - 1; blk >= 0; --blk) {
+      if constexpr (kReBlk) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) h[kk][j] = fwd(blk * 4 + kk, j, kk > 0 ? h[kk - 1][j] : hb[blk][j]);
+        }
+      }
 #pragma unroll
       for (int kk = 3; kk >= 0; --kk) {
         const int t = blk * 4 + kk;
@@ -265,15 +301,15 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
           const int ib = kk * 2 * SPW + j;  // B of state j at step kk
           const int ic = ib + SPW;          // C of state j at step kk
           dh[j] = fmac_row_bcast_rt(dh[j], bc_cur[ic / 16][blk], dout, ic % 16);
-          const float hp = t > 0 ? h[t - 1][j] : hs[j];
+          const float hp = h_before(blk, kk, j), ht = h_at(blk, kk, j);
           const float dec = exp2_fast(dl * A2[j]);
           const float ga = dh[j] * hp * dec;
           dA[j] = __builtin_fmaf(ga, dl, dA[j]);
           sg = __builtin_fmaf(ga, Aj[j], sg);
           s1 = fmac_row_bcast_rt(s1, bc_cur[ib / 16][blk], dh[j], ib % 16);
-          outp = fmac_row_bcast_rt(outp, bc_cur[ic / 16][blk], h[t][j], ic % 16);
+          outp = fmac_row_bcast_rt(outp, bc_cur[ic / 16][blk], ht, ic % 16);
           s_dbc[w][j][kk][0][lane] = dh[j] * x;
-          s_dbc[w][j][kk][1][lane] = dout * h[t][j];
+          s_dbc[w][j][kk][1][lane] = dout * ht;
           dh[j] *= dec;
         }
         s_part[w][kk][0][lane] = sg;
@@ -286,13 +322,13 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
       // by kTpc consecutive threads (a fixed order).
       {
         constexpr int kCols = 2 * Np * 4;
-        constexpr int kTpc = kBwdThreads / kCols;  // 4 (SPW 2) or 8 (SPW 1)
+        constexpr int kTpc = kBwdThreads / kCols;  // 8, 4, 2, 1 for SPW 1, 2, 4, 8
         constexpr int kLpt = kLanes / kTpc;
         const int col = threadIdx.x / kTpc, part = threadIdx.x % kTpc;
         const int kk = col % 4, n = (col / 4) % Np, q = col / (4 * Np);
         const float* src = &s_dbc[n / SPW][n % SPW][kk][q][part * kLpt];
         float acc = 0.f;
-#pragma unroll
+#pragma unroll 4
         for (int i = 0; i < kLpt; i += 4) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
           acc += (v[0] + v[1]) + (v[2] + v[3]);
@@ -736,9 +772,16 @@ size_t scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int6
 }
 
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t stream) {
-  const int spw = states_per_wave(p.fwd.dstate);
-  if (p.fwd.bf16) return spw == 1 ? launch_bwd_typed<true, 1>(p, stream) : launch_bwd_typed<true, 2>(p, stream);
-  return spw == 1 ? launch_bwd_typed<false, 1>(p, stream) : launch_bwd_typed<false, 2>(p, stream);
+  // d_state <= 32 (up to 4 states per wave).
+  auto typed = [&](auto bf16_tag) {
+    constexpr bool BF16 = decltype(bf16_tag)::value;
+    switch (states_per_wave(p.fwd.dstate)) {
+      case 1: return launch_bwd_typed<BF16, 1>(p, stream);
+      case 2: return launch_bwd_typed<BF16, 2>(p, stream);
+      default: return launch_bwd_typed<BF16, 4>(p, stream);
+    }
+  };
+  return p.fwd.bf16 ? typed(std::true_type{}) : typed(std::false_type{});
 }
 
 }  // namespace mss

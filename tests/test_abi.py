@@ -139,7 +139,8 @@ def test_scan_bwd_validation_enqueues_nothing():
     assert bwd_call(dB=None) == NULL
     assert bwd_call(dz=None) == NULL                  # z given without dz
     assert bwd_call(z=None) == NULL                   # dz given without z
-    assert bwd_call(shape=(2, 64, 17, 128)) == UNSUP  # d_state above 16
+    assert bwd_call(shape=(2, 64, 33, 128)) == UNSUP  # d_state above 32
+    assert bwd_call(shape=(65535, 1, 32, (1 << 24) - 1)) == SHAPE  # reduction grid beyond 2^31 blocks
     assert bwd_call(shape=(2, 64, 16, 0)) == SHAPE
     assert bwd_call(io=7) == DTYPE
     assert bwd_call(flags=0x80) == UNSUP
@@ -152,7 +153,9 @@ def test_scan_bwd_validation_enqueues_nothing():
     lib = mss.lib()
     assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 16, 8192, BF16, 0) > \
         lib.mss_selective_scan_workspace_size(4, 5120, 16, 8192, BF16, 0)
-    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 32, 8192, BF16, 0) == 0
+    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 32, 8192, BF16, 0) > \
+        lib.mss_selective_scan_bwd_workspace_size(4, 5120, 16, 8192, BF16, 0)
+    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 33, 8192, BF16, 0) == 0
 
 
 def test_scan_workspace_query():

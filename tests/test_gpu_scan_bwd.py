@@ -82,6 +82,9 @@ SHAPES = [
     (1, 192, 16, 1, "fp32"),       # single step
     (2, 64, 16, 15, "bf16"),       # shorter than one tile
     (2, 64, 16, 300, "bf16"),      # several tiles and a ragged tail
+    (2, 100, 32, 77, "fp32"),      # 4 states per wave, ragged channels and L
+    (2, 64, 24, 300, "bf16"),      # 4 states per wave, states padded
+    (1, 128, 17, 40, "fp32"),      # one state above 16
 ]
 
 
@@ -108,21 +111,23 @@ def test_scan_bwd_optional_inputs(drop):
     check(got, ref, "fp32")
 
 
+@pytest.mark.parametrize("n", [16, 32])
 @pytest.mark.parametrize("force_general", [False, True])
-def test_scan_bwd_general_a(force_general):
-    x = I.scan_inputs(I.small_scan_config(2, 128, 16, 90, "fp32"), with_h0=True)
+def test_scan_bwd_general_a(force_general, n):
+    x = I.scan_inputs(I.small_scan_config(2, 128, n, 90, "fp32"), with_h0=True)
     g = np.random.default_rng(3)
     x["A"] = (-np.exp(g.uniform(-1, 2, size=x["A"].shape))).astype(np.float32)
-    x["A"][:64] = -(np.arange(16, dtype=np.float32) + 1)
+    x["A"][:64] = -(np.arange(n, dtype=np.float32) + 1)
     dy, dhl = grads_inputs(x)
     check(run_gpu_bwd(x, dy, dhl, force_general=force_general), run_oracle_bwd(x, dy, dhl), "fp32")
 
 
 @pytest.mark.parametrize("shape", [(2, 12800, 16, 45, "bf16"), (1, 128, 16, 16384, "fp32"),
                                    (1, 5120, 16, 4096, "bf16"), (2, 100, 16, 20001, "fp32"),
-                                   (1, 64, 4, 9000, "fp32"), (2, 10240, 16, 257, "bf16")],
+                                   (1, 64, 4, 9000, "fp32"), (2, 10240, 16, 257, "bf16"),
+                                   (2, 12800, 32, 45, "bf16"), (1, 128, 32, 9000, "fp32")],
                          ids=["carry_handoff", "split_passes", "split_b1_layer", "split_ragged", "split_spw1",
-                              "split_two_pieces_per_range"])
+                              "split_two_pieces_per_range", "carry_handoff_n32", "split_passes_n32"])
 def test_scan_bwd_checkpoint_paths(shape):
     """More streams than CUs (the backward's gradient and the forward's state
     handed between workgroups), and few long sequences (both cut over all CUs:
