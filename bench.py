@@ -29,11 +29,14 @@ Other workloads (measured for the record, not the headline):
 another sequence length or batch: the preset's inputs are drawn as usual and
 repeated (or cut) along L or the batch on the device.  Such lines carry no
 traffic figure (the counters were taken at the preset shape) and no CPU
-baseline.
+baseline.  --dstate N (scan_2p8b, scan_130m, scan_2p8b_bwd, scan_2p8b_fused)
+draws the preset's inputs at d_state N instead; such lines carry no traffic
+figure either, but keep the CPU baseline (the oracle at the same shape).
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -48,6 +51,9 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "state updates/s (B*L*D*N) + % HBM roofline, Mamba-2.8b-shaped scan"
 
 
+SCAN_WORKLOADS = ("scan_2p8b", "scan_130m", "scan_2p8b_bwd", "scan_2p8b_fused")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +66,9 @@ def parse():
                     help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
     ap.add_argument("--batch", type=int, default=0,
                     help="scan/SSD workloads: batch (inputs repeated along the batch); 0 = the preset's")
+    ap.add_argument("--dstate", type=int, default=0,
+                    help="selective scan workloads (forward, fused, backward): d_state in place of the preset's, "
+                         "inputs drawn for that shape; 0 = the preset's")
     ap.add_argument("--force-general-decay", action="store_true",
                     help="scan: per-state exp decay even where A has the S4D-real structure")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -409,6 +418,9 @@ def main():
         print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
               file=sys.stderr)
         sys.exit(2)
+    if args.dstate < 0 or (args.dstate and args.workload not in SCAN_WORKLOADS):
+        print("bench.py: --dstate takes a positive size and applies to " + ", ".join(SCAN_WORKLOADS), file=sys.stderr)
+        sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -417,10 +429,15 @@ def main():
     import selective_state_space_27_amd as mss
     from selective_state_space_27_amd import inputs as I
 
+    def scan_cfg(cfg):
+        if not args.dstate:
+            return cfg
+        return dataclasses.replace(cfg, name=f"{cfg.name}_n{args.dstate}", dstate=args.dstate)
+
     if args.workload == "scan_2p8b":
-        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_2P8B)
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
     elif args.workload == "scan_130m":
-        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_130M)
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, scan_cfg(I.SCAN_130M))
     elif args.workload == "decode_2p8b":
         res, nbytes, launch_ms, kernel, files, cpu = bench_decode(args, torch, mss, I)
     elif args.workload == "ssd_2p8b":
@@ -428,14 +445,16 @@ def main():
     elif args.workload == "scan_m2shape":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_M2)
     elif args.workload == "scan_2p8b_bwd":
-        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_bwd(args, torch, mss, I, I.SCAN_2P8B)
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_bwd(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
     elif args.workload == "scan_2p8b_fused":
-        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_fused(args, torch, mss, I, I.SCAN_2P8B)
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_fused(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
     else:
         res, nbytes, launch_ms, kernel, files, cpu = bench_copy(args, torch)
 
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.workload, files) if files and not (args.seqlen or args.batch) else None
+    # (counters were taken at the presets' shapes only)
+    traffic = recorded_traffic(args.workload, files) if files and not (args.seqlen or args.batch or args.dstate) \
+        else None
     line = {
         "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
