@@ -207,6 +207,8 @@ def test_ssd_validation_errors():
     assert ssd_call(io=9) == DTYPE
     assert ssd_call(io=FP32) == UNSUP
     assert ssd_call(shape=(2, 1024, 8, 32, 1, 128, 256)) == UNSUP     # headdim
+    assert ssd_call(shape=(2, 1024, 8, 128, 1, 128, 256)) == UNSUP    # headdim 128 (64 only)
+    assert ssd_call(shape=(2, 1024, 8, 64, 1, 256, 256)) == UNSUP     # dstate 256 (128 only)
     assert ssd_call(shape=(2, 1024, 8, 64, 1, 64, 256)) == UNSUP      # dstate
     assert ssd_call(shape=(2, 1024, 8, 64, 1, 128, 100)) == UNSUP     # chunk
     assert ssd_call(shape=(2, 1024, 6, 64, 4, 128, 256)) == UNSUP     # nheads % ngroups
