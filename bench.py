@@ -165,12 +165,45 @@ def repeat_timed(fn, min_s=CPU_MIN_S, max_reps=100000):
             return reps, dt
 
 
-def cpu_threads():
+def host_cpus():
+    """The host's CPUs as this process sees them: (threads the oracle uses,
+    description).  Threads = the CPUs in this process's affinity mask, capped
+    by a cgroup CPU quota when one is set (more threads than the quota would
+    only time-slice)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        nproc = len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        nproc = os.cpu_count() or 1
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = max(1, -(-int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = min(nproc, quota) if quota else nproc
+    return threads, {"nproc": nproc, "cgroup_cpu_quota": quota, "cpu_model": model}
+
+
+def cpu_leg(all_fn, all_units, one_fn, one_units, unit, threads, info, sample_all, sample_one):
+    """Times the oracle on all host threads (all_fn, at least CPU_MIN_S) and
+    on one thread (one_fn on a smaller sample, at least CPU_MIN_S / 2)."""
+    reps, dt = repeat_timed(all_fn)
+    reps1, dt1 = repeat_timed(one_fn, CPU_MIN_S / 2)
+    res = {"value": reps * all_units / dt, "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": f"{sample_all} {reps} times on {threads} threads; {dt:.2f} s wall, fp64 C oracle",
+           "value_1thread": reps1 * one_units / dt1,
+           "sample_1thread": f"{sample_one} {reps1} times on 1 thread; {dt1:.2f} s wall"}
+    res.update(info)
+    return res
 
 
 def along_l(torch, t, L, dim):
@@ -223,11 +256,13 @@ def bench_scan(args, torch, mss, I, cfg):
         f64 = lambda k: I.to_f64(x[k], cfg.io)  # the whole workload, repeated for at least CPU_MIN_S
         args64 = (f64("u"), f64("delta"), x["A"].astype(np.float64), f64("B"), f64("C"), x["D"].astype(np.float64),
                   f64("z"))
-        th = cpu_threads()
-        reps, dt = repeat_timed(lambda: oracle.selective_scan(*args64, threads=th))
-        cpu = {"value": reps * b * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"the whole workload (b={b}, d={d}, N={n}, L={L}) {reps} times; {dt:.2f} s wall, "
-                         "fp64 C oracle"}
+        th, info = host_cpus()
+        d1 = max(1, d // 32)  # one thread: batch row 0, the first d/32 channels
+        one = tuple(a[:1, :d1] if a.ndim == 3 and a.shape[1] == d else a[:1] if a.ndim == 3 else a[:d1]
+                    for a in args64)
+        cpu = cpu_leg(lambda: oracle.selective_scan(*args64, threads=th), b * d * n * L,
+                      lambda: oracle.selective_scan(*one, threads=1), d1 * n * L, "state updates/s", th, info,
+                      f"the whole workload (b={b}, d={d}, N={n}, L={L})", f"batch row 0, channels 0..{d1 - 1}")
     return res, nbytes, ms, kernel, files, cpu
 
 
@@ -259,14 +294,18 @@ def bench_scan_fused(args, torch, mss, I, cfg):
     if not args.no_cpu_baseline:
         import oracle
         f64 = lambda k: I.to_f64(x[k], cfg.io)
-        th = cpu_threads()
-        call = lambda: oracle.selective_scan_fused(f64("x"), x["conv_w"], x["conv_b"], f64("delta_raw"),
-                                                   x["delta_bias"], x["A"], f64("B"), f64("C"), x["D"], f64("z"),
-                                                   conv_silu=True, softplus=True, threads=th)
-        reps, dt = repeat_timed(call)
-        cpu = {"value": reps * b * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"the whole workload (b={b}, d={d}, N={n}, L={L}) {reps} times; {dt:.2f} s wall, "
-                         "fp64 C oracle (prologue single-threaded, scan on the threads)"}
+        th, info = host_cpus()
+        xs, dr, Bs, Cs, zs = f64("x"), f64("delta_raw"), f64("B"), f64("C"), f64("z")
+        d1 = max(1, d // 32)  # one thread: batch row 0, the first d/32 channels
+
+        def call(bsl, dsl, t):
+            return oracle.selective_scan_fused(xs[bsl, dsl], x["conv_w"][dsl], x["conv_b"][dsl], dr[bsl, dsl],
+                                               x["delta_bias"][dsl], x["A"][dsl], Bs[bsl], Cs[bsl], x["D"][dsl],
+                                               zs[bsl, dsl], conv_silu=True, softplus=True, threads=t)
+        cpu = cpu_leg(lambda: call(slice(None), slice(None), th), b * d * n * L,
+                      lambda: call(slice(0, 1), slice(0, d1), 1), d1 * n * L, "state updates/s", th, info,
+                      f"the whole workload (b={b}, d={d}, N={n}, L={L}; prologue on one thread, scan on all)",
+                      f"batch row 0, channels 0..{d1 - 1}")
     return res, scan_fused_bytes(b, d, n, L, es), ms, kernel, files, cpu
 
 
@@ -306,11 +345,14 @@ def bench_scan_bwd(args, torch, mss, I, cfg):
         f64 = lambda k: I.to_f64(x[k][:1], cfg.io)  # bounded sample: batch row 0, every channel, full L
         args64 = (f64("u"), f64("delta"), x["A"].astype(np.float64), f64("B"), f64("C"), x["D"].astype(np.float64),
                   f64("z"), None, I.to_f64(dy_host[:1], cfg.io))
-        th = cpu_threads()
-        reps, dt = repeat_timed(lambda: oracle.selective_scan_bwd(*args64, threads=th))
-        cpu = {"value": reps * d * n * L / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"batch row 0 of {b} (all {d} channels, full L={L}) {reps} times; {dt:.2f} s wall, "
-                         "fp64 C oracle backward"}
+        th, info = host_cpus()
+        d1 = max(1, d // 64)
+        one = tuple(None if a is None else a[:, :d1] if a.ndim == 3 and a.shape[1] == d else
+                    a[:d1] if a.ndim in (1, 2) else a for a in args64)
+        cpu = cpu_leg(lambda: oracle.selective_scan_bwd(*args64, threads=th), d * n * L,
+                      lambda: oracle.selective_scan_bwd(*one, threads=1), d1 * n * L, "state updates/s", th, info,
+                      f"batch row 0 of {b} (all {d} channels, full L={L}), backward",
+                      f"batch row 0, channels 0..{d1 - 1}, backward")
     files = ["scan.hip", "scan_bwd.hip", "scan_layout.hpp", "common.hpp"]
     kernel = "scan_bwd_kernel (+ checkpoint forward and bwd_reduce_kernel in the same timed call)"
     return res, scan_bwd_bytes(b, d, n, L, es), ms, kernel, files, cpu
@@ -345,17 +387,19 @@ def bench_decode(args, torch, mss, I):
         import oracle
         p64 = [{k: I.to_f64(p[k], "bf16") for k in ("u", "delta", "B", "C", "z")} for p in pool]
         state = {"h": I.decode_state0(cfg).astype(np.float64), "s": 0}
-        th = cpu_threads()
+        th, info = host_cpus()
+        b1 = max(1, b // 32)
 
-        def token_step():  # consecutive token steps over the whole batch, inputs cycling through the pool
+        def token_step(nb, t):  # consecutive token steps, inputs cycling through the pool
             p = p64[state["s"] % I.DECODE_POOL]
-            state["h"], _ = oracle.state_update(state["h"], p["u"], p["delta"], st["A"], p["B"], p["C"], st["D"],
-                                                p["z"], threads=th)
+            h, _ = oracle.state_update(state["h"][:nb], p["u"][:nb], p["delta"][:nb], st["A"], p["B"][:nb],
+                                       p["C"][:nb], st["D"], p["z"][:nb], threads=t)
+            state["h"][:nb] = h
             state["s"] += 1
 
-        reps, dt = repeat_timed(token_step)
-        cpu = {"value": b * d * n * reps / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"all {b} batch rows, {reps} consecutive token steps; {dt:.2f} s wall"}
+        cpu = cpu_leg(lambda: token_step(b, th), b * d * n, lambda: token_step(b1, 1), b1 * d * n,
+                      "state updates/s", th, info, f"all {b} batch rows, consecutive token steps",
+                      f"batch rows 0..{b1 - 1}, consecutive token steps")
     # per-launch figures: one launch = one token step
     return res, nbytes, ms / cfg.steps, "state_update_kernel", ["state_update.hip", "common.hpp"], cpu
 
@@ -388,12 +432,15 @@ def bench_ssd(args, torch, mss, I):
     cpu = None
     if not args.no_cpu_baseline and not (args.seqlen or args.batch):
         import oracle
-        th = cpu_threads()
+        th, info = host_cpus()
         args64 = (I.to_f64(x["x"], "bf16"), x["delta"].astype(np.float64), x["A"], I.to_f64(x["B"], "bf16"),
                   I.to_f64(x["C"], "bf16"))
-        reps, dt = repeat_timed(lambda: oracle.ssd(*args64, threads=th))
-        cpu = {"value": reps * b * L * H * P * N / dt, "unit": "state updates/s", "cores": th, "kind": "oracle",
-               "sample": f"the whole workload (b={b}, L={L}, all heads) {reps} times; {dt:.2f} s wall"}
+        h1 = 2  # one thread: batch row 0, heads 0..1
+        one = (np.ascontiguousarray(args64[0][:1, :, :h1]), np.ascontiguousarray(args64[1][:1, :, :h1]),
+               args64[2][:h1], args64[3][:1], args64[4][:1])
+        cpu = cpu_leg(lambda: oracle.ssd(*args64, threads=th), b * L * H * P * N,
+                      lambda: oracle.ssd(*one, threads=1), L * h1 * P * N, "state updates/s", th, info,
+                      f"the whole workload (b={b}, L={L}, all heads)", f"batch row 0, heads 0..{h1 - 1}")
     return res, ssd_bytes(b, L, H, P, G, N, 2), ms, "ssd kernels", ["ssd.hip", "common.hpp"], cpu
 
 

@@ -19,6 +19,9 @@
  *   MSS_ERR_WORKSPACE   workspace NULL or smaller than the query returned
  *   MSS_ERR_ALIAS       an output buffer overlaps an input buffer
  *   MSS_ERR_HIP         a HIP launch failed (mss_last_hip_error() has the code)
+ *   MSS_ERR_WAIT        (mss_workspace_status only) a bounded wait between
+ *                       workgroups gave up during the call: its outputs are
+ *                       not valid
  *
  * The same inputs, shapes and flags give bitwise-identical outputs: no
  * floating-point atomics are used and reduction orders are fixed.
@@ -37,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSS_ABI_VERSION 1
+#define MSS_ABI_VERSION 2
 
 typedef enum {
   MSS_OK = 0,
@@ -48,7 +51,8 @@ typedef enum {
   MSS_ERR_UNSUPPORTED = 5,
   MSS_ERR_WORKSPACE = 6,
   MSS_ERR_ALIAS = 7,
-  MSS_ERR_HIP = 8
+  MSS_ERR_HIP = 8,
+  MSS_ERR_WAIT = 9
 } mss_status;
 
 /* Storage type of the streamed tensors (u, delta, B, C, z, y; x for SSD).
@@ -171,9 +175,8 @@ mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, cons
 /* D = 0); dz [batch, dim, seqlen] io_dtype, given exactly when z is (else    */
 /* MSS_ERR_NULL); dh0 [batch, dim, dstate] fp32 (NULL = not computed; the     */
 /* gradient of the initial state, h0 or zero).                              */
-/* Supported: 1 <= dstate <= 32 (else MSS_ERR_UNSUPPORTED), the scan's other */
-/* limits, and 2*batch*dstate*seqlen + dim*(dstate+1) at most 2^39 - 256     */
-/* (else MSS_ERR_SHAPE).  flags: 0 or MSS_FLAG_DECAY_GENERAL (as in the      */
+/* Supported: 1 <= dstate <= 32 (else MSS_ERR_UNSUPPORTED) and the scan's    */
+/* other limits (else MSS_ERR_SHAPE).  flags: 0 or MSS_FLAG_DECAY_GENERAL (as in the */
 /* forward).  Outputs must not overlap any input or each other.  The         */
 /* workspace (size from                                                      */
 /* mss_selective_scan_bwd_workspace_size) need not be zeroed.                */
@@ -204,8 +207,10 @@ size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t
 /*                                                                          */
 /* Layouts: h [batch, dim, dstate] fp32;  u, delta, z, y [batch, dim];       */
 /*          B, C [batch, dstate];  A [dim, dstate] fp32;  D [dim] fp32.      */
-/* D and z may be NULL.  Supported: 1 <= dstate <= 128.  `flags` must be 0. */
-/* y must not overlap h or any input; h must not overlap any input.          */
+/* D and z may be NULL.  Supported: 1 <= dstate <= 128 (else                */
+/* MSS_ERR_UNSUPPORTED) and batch*dim <= 2^28 (else MSS_ERR_SHAPE).  `flags` */
+/* must be 0.  y must not overlap h or any input; h must not overlap any     */
+/* input.                                                                    */
 /* ------------------------------------------------------------------------ */
 mss_status mss_state_update(float* h, const void* u, const void* delta, const float* A,
                             const void* B, const void* C, const float* D, const void* z, void* y,
@@ -236,7 +241,8 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
 /* D, z, h0, chunk_states and h_last may be NULL.                           */
 /* Supported: in_dtype MSS_BF16; headdim 64; dstate 128; chunk 64, 128 or   */
 /* 256; nheads % ngroups == 0; seqlen*nheads*headdim and                  */
-/* seqlen*ngroups*dstate below 2^30 (else MSS_ERR_SHAPE).  seqlen need not  */
+/* seqlen*ngroups*dstate below 2^30 and ceil(seqlen/chunk)*nheads*batch at  */
+/* most 2^24 (else MSS_ERR_SHAPE).  seqlen need not                        */
 /* be a multiple of chunk.                                                  */
 /* `flags` must be 0.  Outputs must not overlap inputs or each other.        */
 /* ------------------------------------------------------------------------ */
@@ -250,6 +256,22 @@ mss_status mss_ssd_chunk_fwd(const void* x, const float* delta, const float* A, 
 /* Bytes of device workspace mss_ssd_chunk_fwd needs (0 when unsupported). */
 size_t mss_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                               int64_t ngroups, int64_t dstate, int64_t chunk, mss_dtype in_dtype);
+
+/* ------------------------------------------------------------------------ */
+/* Status of a call that used `workspace`.                                   */
+/*                                                                          */
+/* The selective scan (forward, fused, backward) hands states between        */
+/* workgroups through flags in its workspace; each wait for such a flag is   */
+/* bounded, and a wait that gives up (never expected) leaves the call's      */
+/* outputs invalid and sets the status word, the workspace's first 4 bytes, */
+/* which every call of the library clears in its first kernel (the SSD      */
+/* workspace has the word too and never sets it).  This waits for           */
+/* `hip_stream` (NULL = the default stream) to finish, reads the word and    */
+/* returns MSS_OK, or MSS_ERR_WAIT when the last call that used the         */
+/* workspace gave up a wait; MSS_ERR_NULL for a NULL workspace, MSS_ERR_HIP  */
+/* when the synchronisation or the read fails.                              */
+/* ------------------------------------------------------------------------ */
+mss_status mss_workspace_status(const void* workspace, void* hip_stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mss_status_string(mss_status status);

@@ -33,14 +33,16 @@ MSS_FLAG_CONV_SILU = 0x2
 MSS_FLAG_DELTA_SOFTPLUS = 0x4
 
 STATUS_NAMES = {0: "MSS_OK", 1: "MSS_ERR_NULL", 2: "MSS_ERR_SHAPE", 3: "MSS_ERR_DTYPE", 4: "MSS_ERR_ALIGN",
-                5: "MSS_ERR_UNSUPPORTED", 6: "MSS_ERR_WORKSPACE", 7: "MSS_ERR_ALIAS", 8: "MSS_ERR_HIP"}
+                5: "MSS_ERR_UNSUPPORTED", 6: "MSS_ERR_WORKSPACE", 7: "MSS_ERR_ALIAS", 8: "MSS_ERR_HIP",
+                9: "MSS_ERR_WAIT"}
+MSS_ERR_WAIT = 9
 
 # Every symbol the header declares.
 EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_selective_scan_fwd_fused",
            "mss_selective_scan_bwd",
            "mss_selective_scan_bwd_workspace_size", "mss_state_update",
-           "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_status_string", "mss_last_hip_error",
-           "mss_abi_version")
+           "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_workspace_status", "mss_status_string",
+           "mss_last_hip_error", "mss_abi_version")
 
 
 class MambaScanError(RuntimeError):
@@ -86,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.mss_ssd_chunk_fwd.restype = ctypes.c_int
     L.mss_ssd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.mss_ssd_workspace_size.restype = sz
+    L.mss_workspace_status.argtypes = [vp, vp]
+    L.mss_workspace_status.restype = ctypes.c_int
     L.mss_status_string.argtypes = [ctypes.c_int]
     L.mss_status_string.restype = ctypes.c_char_p
     L.mss_last_hip_error.argtypes = []
@@ -144,14 +148,35 @@ def _device_of(t: torch.Tensor) -> torch.device:
     return t.device
 
 
+def workspace_status(workspace, stream=None) -> int:
+    """Waits for the stream, then reads the status word of the last call that
+    used ``workspace`` (a uint8 device tensor): MSS_OK, or MSS_ERR_WAIT when a
+    bounded wait between workgroups gave up and that call's outputs are not
+    valid.  Other failures raise."""
+    st = lib().mss_workspace_status(_ptr(workspace), _stream(stream))
+    if st not in (MSS_OK, MSS_ERR_WAIT):
+        _raise(st, "mss_workspace_status")
+    return st
+
+
+def _check_waits(workspace, stream, what):
+    if workspace_status(workspace, stream) != MSS_OK:
+        raise MambaScanError(MSS_ERR_WAIT, what)
+
+
 # ------------------------------------------------------------ selective scan
 def selective_scan_workspace_size(batch, dim, dstate, seqlen, dtype=torch.bfloat16, flags=0) -> int:
     return lib().mss_selective_scan_workspace_size(batch, dim, dstate, seqlen, _io_code(dtype), flags)
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, *, return_last_state=False,
-                       force_general_decay=False, out=None, h_last=None, workspace=None, stream=None):
+                       force_general_decay=False, out=None, h_last=None, workspace=None, stream=None,
+                       check_waits=False):
     """Selective scan over the whole sequence.
+
+    ``check_waits``: wait for the call and raise MambaScanError(MSS_ERR_WAIT)
+    if a bounded wait between workgroups gave up (never expected; off by
+    default because it synchronises).
 
     u, delta, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16, all the same);
     A: [d, N] float32; D: [d] float32; h0: [b, d, N] float32.
@@ -187,12 +212,14 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, *, return_las
                                       _ptr(out), _ptr(h_last), b, d, N, L, code, flags, _ptr(workspace),
                                       workspace.numel(), _stream(stream))
     _raise(st, "mss_selective_scan_fwd")
+    if check_waits:
+        _check_waits(workspace, stream, "mss_selective_scan_fwd")
     return (out, h_last) if return_last_state else out
 
 
 def selective_scan_fwd_fused(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None, h0=None, *,
                              conv_silu=False, softplus=True, return_last_state=False, force_general_decay=False,
-                             out=None, h_last=None, workspace=None, stream=None):
+                             out=None, h_last=None, workspace=None, stream=None, check_waits=False):
     """Selective scan whose u and delta are formed inside the kernel:
     u = conv_b + causal 4-tap depthwise convolution of x with conv_w (tap 3 on
     the current step), through silu if ``conv_silu``; delta = delta_raw +
@@ -200,7 +227,8 @@ def selective_scan_fwd_fused(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, 
 
     x, delta_raw, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16, all the
     same); conv_w: [d, 4] float32; conv_b, delta_bias: [d] float32 or None;
-    A, D, h0 as in selective_scan_fwd.  Returns y (and h_last) like it."""
+    A, D, h0 as in selective_scan_fwd.  Returns y (and h_last) like it;
+    ``check_waits`` as there."""
     dev = _device_of(x)
     b, d, L = x.shape
     N = A.shape[1]
@@ -235,6 +263,8 @@ def selective_scan_fwd_fused(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, 
                                             _ptr(h_last), b, d, N, L, code, flags, _ptr(workspace), workspace.numel(),
                                             _stream(stream))
     _raise(st, "mss_selective_scan_fwd_fused")
+    if check_waits:
+        _check_waits(workspace, stream, "mss_selective_scan_fwd_fused")
     return (out, h_last) if return_last_state else out
 
 
@@ -243,14 +273,16 @@ def selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, dtype=torch.bf
 
 
 def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dD=True,
-                       want_dh0=False, force_general_decay=False, out=None, workspace=None, stream=None) -> dict:
+                       want_dh0=False, force_general_decay=False, out=None, workspace=None, stream=None,
+                       check_waits=False) -> dict:
     """Gradient of a loss through selective_scan_fwd (same inputs), given
     dy = dloss/dy [b, d, L] and optionally dh_last = dloss/dh_last [b, d, N]
     float32.  Returns a dict: du, ddelta, dz (None without z) [b, d, L] and dB,
     dC [b, N, L] in the I/O dtype; dA [d, N], dD [d] (None unless want_dD) and
     dh0 [b, d, N] (None unless want_dh0) in float32.  d_state <= 32.  ``out``:
     a dict from an earlier call with the same shapes whose tensors are
-    written again (nothing is allocated for them)."""
+    written again (nothing is allocated for them).  ``check_waits`` as in
+    selective_scan_fwd."""
     dev = _device_of(u)
     b, d, L = u.shape
     N = A.shape[1]
@@ -286,6 +318,8 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
                                       _ptr(g.get("dh0")),
                                       b, d, N, L, code, flags, _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(st, "mss_selective_scan_bwd")
+    if check_waits:
+        _check_waits(workspace, stream, "mss_selective_scan_bwd")
     return g
 
 

@@ -62,6 +62,7 @@ const char* mss_status_string(mss_status s) {
     case MSS_ERR_WORKSPACE: return "MSS_ERR_WORKSPACE: workspace missing or too small";
     case MSS_ERR_ALIAS: return "MSS_ERR_ALIAS: an output overlaps an input";
     case MSS_ERR_HIP: return "MSS_ERR_HIP: a HIP call failed";
+    case MSS_ERR_WAIT: return "MSS_ERR_WAIT: a bounded wait between workgroups gave up; the outputs are not valid";
   }
   return "unknown mss_status";
 }
@@ -69,6 +70,15 @@ const char* mss_status_string(mss_status s) {
 int mss_last_hip_error(void) { return g_last_hip_error; }
 
 int mss_abi_version(void) { return MSS_ABI_VERSION; }
+
+mss_status mss_workspace_status(const void* workspace, void* hip_stream) {
+  if (workspace == nullptr) return MSS_ERR_NULL;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(hip_stream));
+  int word = 0;
+  if (e == hipSuccess) e = hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(e);
+  return word == 0 ? MSS_OK : MSS_ERR_WAIT;
+}
 
 // ------------------------------------------------------------ selective scan
 static mss_status scan_check_shape(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype t) {
@@ -190,14 +200,11 @@ mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, cons
 }
 
 // --------------------------------------------------- selective scan backward
-// The forward's limits, d_state <= 32 (up to 4 states per wave), and one
-// reduction thread per dB, dC, dA, dD element within a one-dimensional grid.
+// The forward's limits and d_state <= 32 (up to 4 states per wave).
 static mss_status scan_bwd_check_shape(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype t) {
   const mss_status st = scan_check_shape(batch, dim, dstate, seqlen, t);
   if (st != MSS_OK) return st;
   if (dstate > 32) return MSS_ERR_UNSUPPORTED;
-  const int64_t reduce_threads = 2 * batch * dstate * seqlen + dim * dstate + dim;
-  if ((reduce_threads + 255) / 256 > kMaxIndex) return MSS_ERR_SHAPE;
   return MSS_OK;
 }
 
@@ -279,7 +286,10 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
   if (!h || !u || !delta || !A || !B || !C || !y) return MSS_ERR_NULL;
   if (!dtype_ok(io_dtype)) return MSS_ERR_DTYPE;
   if (batch <= 0 || dim <= 0 || dstate <= 0) return MSS_ERR_SHAPE;
-  if (batch * dim * dstate > kMaxIndex * 4LL || batch * dim * 4 > kMaxIndex * 64LL) return MSS_ERR_SHAPE;
+  // At most 2^28 rows: 8 threads per row above 64 states keeps the grid below
+  // 2^31 work-items, and every state offset below 2^35 elements.
+  if (batch > (int64_t{1} << 28) || dim > (int64_t{1} << 28) || batch * dim > (int64_t{1} << 28))
+    return MSS_ERR_SHAPE;
   if (dstate > 128) return MSS_ERR_UNSUPPORTED;
   if (flags != 0) return MSS_ERR_UNSUPPORTED;
   const void* all[] = {h, u, delta, A, B, C, D, z, y};
@@ -324,6 +334,9 @@ static mss_status ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads,
   if (seqlen * nheads * headdim > (int64_t{1} << 30) - 64 || seqlen * ngroups * dstate >= (int64_t{1} << 30) ||
       batch > 65535 || nheads > 65535)
     return MSS_ERR_SHAPE;
+  // One 256-thread workgroup per (chunk, head, batch entry) at most: the
+  // launch stays below 2^32 work-items.
+  if (((seqlen + chunk - 1) / chunk) * nheads * batch > (int64_t{1} << 24)) return MSS_ERR_SHAPE;
   if (t != MSS_BF16) return MSS_ERR_UNSUPPORTED;
   if (headdim != 64 || dstate != 128 || !(chunk == 64 || chunk == 128 || chunk == 256)) return MSS_ERR_UNSUPPORTED;
   if (nheads % ngroups != 0) return MSS_ERR_UNSUPPORTED;

@@ -10,12 +10,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Loads through the constant address space: with a wave-uniform address the
-// compiler emits scalar (s_load) reads, so per-timestep values shared by all
-// lanes (B and C rows) arrive in SGPRs without touching the vector memory path.
-typedef const __attribute__((address_space(4))) float* cfloat_ptr;
-__device__ __forceinline__ cfloat_ptr as_const(const float* p) { return (cfloat_ptr)(p); }
-
 // Exact widening of bf16 (stored in the low/high half of a 32-bit word).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -94,9 +88,9 @@ __device__ __forceinline__ float row_bcast(float v) {
 
 // acc + (lane P of each 16-lane row of v, broadcast) * h as one
 // v_fmac_f32_dpp, which the compiler does not form from a DPP move and a
-// multiply-add.  The broadcast operand v is only ever a register filled by a
-// buffer load, never one written by a VALU instruction just before (that
-// would need wait states the compiler does not insert around inline assembly).
+// multiply-add.  The broadcast operand v must not have been written by a VALU
+// instruction in the two wait states before (the compiler inserts none around
+// inline assembly); the build checks the disassembly of every kernel for it.
 template <int P>
 __device__ __forceinline__ float fmac_row_bcast(float acc, float v, float h) {
   asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"

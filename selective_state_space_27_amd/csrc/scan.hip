@@ -71,7 +71,8 @@ struct ScanArgs {
   float* hloc;         // same layout: zero-start end state of the piece ending at boundary g (split pass)
   float* dsum;         // [kMaxWG][64 channels][4]: partial sums of delta over that piece (split pass)
   float* ckpt;         // state-only kernels outside the local pass: [streams][ntiles][8][SPW][64] (nullable)
-  int* flags;          // [kMaxWG] carry ready; [kMaxWG] = spin-limit error; [kMaxWG + 1] = ticket
+  int* flags;          // [kMaxWG]: carry of workgroup g ready
+  int* err;            // status word of the call: set when a bounded carry wait gave up
   int* ticket;
   int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
   int force_general;
@@ -105,7 +106,7 @@ __device__ __forceinline__ float quad_prev(float v) {
 constexpr int kMaxSpins = 1 << 22;
 
 // Workgroups per launch at most (carry slots are per workgroup boundary).
-constexpr int kMaxWG = 512;
+constexpr int kMaxWG = kMaxScanWG;
 
 // Passes.  Single: one launch, each carry handed to the next workgroup through
 // a flag.  When there are too few sequences to fill the chip, sequences are
@@ -241,8 +242,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         int spins = 0;
         while (__hip_atomic_load(a.flags + wg_id - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
           __builtin_amdgcn_s_sleep(4);
-          if (++spins > kMaxSpins) {  // never expected; keeps every wait finite
-            __hip_atomic_store(a.flags + kMaxWG, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (++spins > kMaxSpins) {  // never expected; keeps every wait finite, reported through err
+            __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
         }
@@ -707,12 +708,12 @@ __global__ void __launch_bounds__(256) carry_combine_kernel(const float* __restr
 }
 
 // B, C [batch, N, L] (bf16 or fp32) -> fp32 workspace in the bc_index layout,
-// zero for n >= N, l >= L and unused row positions.  One thread per float.
-// The same launch clears the carry flags, the error word and the ticket, and
-// its first waves pick each 64-channel block's decay mode (wave blk checks
-// block blk, comparing exactly in fp32): kDecayScalar when A[d,n] == A[d,0]
-// for every channel d of the block, else kDecayS4D when A[d,n] == (n+1)*A[d,0]
-// for every channel, else kDecayGeneral.
+// zero for n >= N, l >= L and unused row positions.  Every loop strides over
+// the whole grid, so a capped grid covers any size.  The same launch clears
+// the status word, the ticket and the carry flags, and picks each 64-channel
+// block's decay mode (one wave per block, comparing exactly in fp32):
+// kDecayScalar when A[d,n] == A[d,0] for every channel d of the block, else
+// kDecayS4D when A[d,n] == (n+1)*A[d,0] for every channel, else kDecayGeneral.
 template <bool BF16, int SPW>
 __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restrict__ B, const void* __restrict__ C,
                                                            float* __restrict__ out, int batch, int N, int L,
@@ -720,11 +721,11 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
                                                            const float* __restrict__ A, int* __restrict__ mode_out,
                                                            int dim, int nblocks) {
   using S = BCShape<SPW>;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (size_t i = idx; i < (size_t)nflags; i += (size_t)gridDim.x * blockDim.x) flags[i] = 0;
-  const size_t wave = idx / kLanes;  // whole waves: the block size is a multiple of 64
-  if (wave < (size_t)nblocks) {
-    const int c = (int)wave * kLanes + (int)(idx % kLanes);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;  // a multiple of 64: whole waves
+  const size_t idx0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (size_t i = idx0; i < (size_t)nflags; i += stride) flags[i] = 0;
+  for (size_t wave = idx0 / kLanes; wave < (size_t)nblocks; wave += stride / kLanes) {
+    const int c = (int)wave * kLanes + (int)(idx0 % kLanes);
     bool s4d = true, scalar = true;
     if (c < dim) {
       const float a0 = A[(size_t)c * N];
@@ -735,48 +736,57 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
       }
     }
     const bool all_scalar = __all(scalar), all_s4d = __all(s4d);
-    if (idx % kLanes == 0) mode_out[wave] = all_scalar ? kDecayScalar : all_s4d ? kDecayS4D : kDecayGeneral;
+    if (idx0 % kLanes == 0) mode_out[wave] = all_scalar ? kDecayScalar : all_s4d ? kDecayS4D : kDecayGeneral;
   }
   const size_t total = (size_t)batch * kWaves * ntiles * S::kPerTile;
-  if (idx >= total) return;
-  int blk, p, v;
-  size_t rest;
-  if constexpr (S::kBlockLayout) {
-    p = (int)((idx / 4) % 16);
-    v = (int)((idx / 64) % (S::kNV / 4)) * 4 + (int)(idx % 4);
-    rest = idx / (64 * (S::kNV / 4));
-    blk = (int)(rest % kBlk);
-    rest /= kBlk;
-  } else {
-    blk = (int)(idx % 4);
-    p = (int)((idx / 4) % 16);
-    rest = idx / 64;
-    v = (int)(rest % S::kNV);
-    rest /= S::kNV;
-  }
-  const int tile = (int)(rest % ntiles);
-  rest /= ntiles;
-  const int g = (int)(rest % kWaves);
-  const int b = (int)(rest / kWaves);
-  const int i = v * 16 + p;
-  float val = 0.f;
-  if (i < S::kPerBlk) {
-    const int kk = i / (2 * SPW), qn = i % (2 * SPW);
-    const int l = tile * kTile + blk * 4 + kk;
-    const bool isC = qn >= SPW;
-    const int n = g * SPW + (isC ? qn - SPW : qn);
-    if (n < N && l < L) {
-      const size_t off = ((size_t)b * N + n) * L + l;
-      const void* src = isC ? C : B;
-      val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(src)[off]) : static_cast<const float*>(src)[off];
+  for (size_t idx = idx0; idx < total; idx += stride) {
+    int blk, p, v;
+    size_t rest;
+    if constexpr (S::kBlockLayout) {
+      p = (int)((idx / 4) % 16);
+      v = (int)((idx / 64) % (S::kNV / 4)) * 4 + (int)(idx % 4);
+      rest = idx / (64 * (S::kNV / 4));
+      blk = (int)(rest % kBlk);
+      rest /= kBlk;
+    } else {
+      blk = (int)(idx % 4);
+      p = (int)((idx / 4) % 16);
+      rest = idx / 64;
+      v = (int)(rest % S::kNV);
+      rest /= S::kNV;
     }
+    const int tile = (int)(rest % ntiles);
+    rest /= ntiles;
+    const int g = (int)(rest % kWaves);
+    const int b = (int)(rest / kWaves);
+    const int i = v * 16 + p;
+    float val = 0.f;
+    if (i < S::kPerBlk) {
+      const int kk = i / (2 * SPW), qn = i % (2 * SPW);
+      const int l = tile * kTile + blk * 4 + kk;
+      const bool isC = qn >= SPW;
+      const int n = g * SPW + (isC ? qn - SPW : qn);
+      if (n < N && l < L) {
+        const size_t off = ((size_t)b * N + n) * L + l;
+        const void* src = isC ? C : B;
+        val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(src)[off]) : static_cast<const float*>(src)[off];
+      }
+    }
+    out[idx] = val;
   }
-  out[idx] = val;
+}
+
+// Grid of the one-dimensional helper kernels: enough 256-thread workgroups
+// for `items`, at most kMaxHelperGrid (their loops stride over the grid), so
+// the launch stays far below the 2^32 work-items of a dispatch.
+constexpr size_t kMaxHelperGrid = 16384;
+inline unsigned helper_grid(size_t items) {
+  return (unsigned)std::max<size_t>(1, std::min<size_t>((items + 255) / 256, kMaxHelperGrid));
 }
 
 size_t carry_floats(int spw) { return (size_t)kMaxWG * kWaves * spw * kLanes; }  // also the hloc size
 size_t dsum_floats() { return (size_t)kMaxWG * kLanes * 4; }
-size_t flag_ints() { return (size_t)kMaxWG + 2; }
+size_t flag_ints() { return scan_flags_bytes() / sizeof(int); }
 
 // Sequences are cut into pieces for the split passes when there are at most
 // half as many streams as workgroups and each piece still has this many tiles.
@@ -787,9 +797,11 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   const int64_t ntiles = num_tiles(p.seqlen);
   const int nblocks = (int)((p.dim + kLanes - 1) / kLanes);
   char* ws = static_cast<char*>(p.workspace);
-  float* bc = reinterpret_cast<float*>(ws);
+  int* flags = reinterpret_cast<int*>(ws);
+  size_t off = scan_flags_bytes();
+  float* bc = reinterpret_cast<float*>(ws + off);
   const size_t nbc = bc_floats(SPW, p.batch, p.seqlen);
-  size_t off = align256(nbc * sizeof(float));
+  off += align256(nbc * sizeof(float));
   int* mode = reinterpret_cast<int*>(ws + off);
   off += align256((size_t)nblocks * sizeof(int));
   float* carry = reinterpret_cast<float*>(ws + off);
@@ -797,18 +809,13 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   float* hloc = reinterpret_cast<float*>(ws + off);
   off += align256(carry_floats(SPW) * sizeof(float));
   float* dsum = reinterpret_cast<float*>(ws + off);
-  off += align256(dsum_floats() * sizeof(float));
-  int* flags = reinterpret_cast<int*>(ws + off);
   const int64_t nstreams = p.batch * nblocks;
 
-  {
-    // Enough threads for every B/C float and one wave per channel block.
-    const size_t threads = std::max<size_t>(nbc, (size_t)nblocks * kLanes);
-    const unsigned grid = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(grid), dim3(256), 0, stream, p.B, p.C, bc,
-                       (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles, flags, (int)flag_ints(), p.A, mode,
-                       (int)p.dim, nblocks);
-  }
+  hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(helper_grid(std::max<size_t>(nbc, (size_t)nblocks * kLanes))),
+                     dim3(256), 0, stream, p.B, p.C, bc, (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles,
+                     flags, (int)flag_ints(), p.A, mode, (int)p.dim, nblocks);
+  hipError_t err = hipGetLastError();  // the scan relies on the cleared ticket and flags
+  if (err != hipSuccess) return err;
 
   ScanArgs a;
   a.u = p.u;
@@ -830,8 +837,9 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.hloc = hloc;
   a.dsum = dsum;
   a.ckpt = p.ckpt;
-  a.flags = flags;
-  a.ticket = flags + kMaxWG + 1;
+  a.err = flags;
+  a.ticket = flags + 1;
+  a.flags = flags + 2;
   a.nblocks = nblocks;
   a.force_general = p.force_general ? 1 : 0;
   a.fused = p.fused ? 1 : 0;
@@ -843,7 +851,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   // One workgroup per compute unit at most (the kernel's LDS allows one), so
   // the balanced split covers the chip in a single wave of workgroups.
   int dev = 0, cus = 0;
-  hipError_t err = hipGetDevice(&dev);
+  err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
   const int cap = std::min(std::max(cus, 1), kMaxWG);
@@ -869,10 +877,15 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   } else {
     a.pass = kPassLocal;
     run(std::true_type{});
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // nstreams <= cap / 2 here: at most 256 * 8 * 16 * 64 threads
     const int64_t threads = nstreams * kWaves * SPW * kLanes;
     hipLaunchKernelGGL((carry_combine_kernel<SPW>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        hloc, dsum, p.A, p.h0, carry, (int)p.batch, (int)p.dim, (int)p.dstate, (int)ntiles, nblocks,
                        a.nwg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
     a.pass = kPassFinal;
     if (p.ckpt != nullptr) run(std::true_type{});
     else run(std::false_type{});
@@ -896,9 +909,9 @@ hipError_t launch_dtype(const ScanParams& p, hipStream_t stream) {
 size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   const int64_t nblocks = (dim + kLanes - 1) / kLanes;
   const int spw = states_per_wave(dstate);
-  return align256(bc_floats(spw, batch, seqlen) * sizeof(float)) + align256((size_t)nblocks * sizeof(int)) +
-         2 * align256(carry_floats(spw) * sizeof(float)) + align256(dsum_floats() * sizeof(float)) +
-         align256(flag_ints() * sizeof(int));
+  return scan_flags_bytes() + align256(bc_floats(spw, batch, seqlen) * sizeof(float)) +
+         align256((size_t)nblocks * sizeof(int)) + 2 * align256(carry_floats(spw) * sizeof(float)) +
+         align256(dsum_floats() * sizeof(float));
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {

@@ -66,7 +66,8 @@ struct BwdArgs {
   float* dA_part;      // [streams][2 pieces][8*SPW][64]
   float* dD_part;      // [streams][2 pieces][64][4]
   float* carry;        // [kMaxBwdWG][8][SPW][64]: dh entering the first tile of range g
-  int* flags;          // [kMaxBwdWG] carry ready; [kMaxBwdWG] spin-limit error; [kMaxBwdWG + 1] ticket
+  int* flags;          // [kMaxBwdWG] carry ready; [kMaxBwdWG + 1] ticket
+  int* err;            // the call's status word (the forward workspace's first word): set when a wait gave up
   int* ticket;
   int batch, dim, dstate, seqlen, ntiles, nblocks, nwg;
   float* hloc;         // split passes: [kMaxBwdWG][8][SPW][64] zero-end gradient at the start of range g's first piece
@@ -175,7 +176,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) scan_bwd_kernel(BwdArgs a) {
       while (__hip_atomic_load(a.flags + g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
         __builtin_amdgcn_s_sleep(4);
         if (++spins > kBwdMaxSpins) {  // never expected; keeps every wait finite
-          __hip_atomic_store(a.flags + kMaxBwdWG, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
       }
@@ -574,7 +575,8 @@ __global__ void __launch_bounds__(256) bwd_combine_kernel(const float* __restric
   }
 }
 
-// Clears the backward's carry flags, error word and ticket.
+// Clears the backward's carry flags and ticket (the status word was cleared
+// by the forward pass of the same call).
 __global__ void __launch_bounds__(256) bwd_clear_kernel(int* flags, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) flags[i] = 0;
 }
@@ -609,8 +611,10 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
                                                          int dim, int N, int L, int nblocks, int ntiles, int nwg,
                                                          int split) {
   constexpr int Np = kWaves * SPW;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nbc = (int64_t)batch * N * L;
+  const int64_t total = 2 * nbc + (int64_t)dim * N + dim;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
   if (idx < 2 * nbc) {
     const int q = (int)(idx / nbc);
     const int64_t r = idx % nbc;
@@ -623,7 +627,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
     void* out = q == 0 ? dB : dC;
     if (BF16) static_cast<uint16_t*>(out)[r] = f32_to_bf16(acc);
     else static_cast<float*>(out)[r] = acc;
-    return;
+    continue;
   }
   int64_t r = idx - 2 * nbc;
   if (r < (int64_t)dim * N) {
@@ -635,7 +639,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
         acc += dA_part[((size_t)sl * Np + n) * kLanes + d % kLanes];
       });
     dA[r] = acc;
-    return;
+    continue;
   }
   r -= (int64_t)dim * N;
   if (dD != nullptr && r < dim) {
@@ -648,6 +652,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict
         acc += (p[0] + p[1]) + (p[2] + p[3]);
       });
     dD[d] = acc;
+  }
   }
 }
 
@@ -712,6 +717,8 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   const bool split = nstreams * 5 < (int64_t)cap * 4 && nstreams * ntiles >= (int64_t)cap * kBwdMinPieceTiles;
   const int nwg = split ? cap : (int)std::min<int64_t>(nstreams, cap);
   hipLaunchKernelGGL(bwd_clear_kernel, dim3(1), dim3(256), 0, stream, flags, kMaxBwdWG + 2);
+  err = hipGetLastError();  // the gradient kernel relies on the cleared ticket and flags
+  if (err != hipSuccess) return err;
   BwdArgs a;
   a.u = p.fwd.u;
   a.delta = p.fwd.delta;
@@ -720,7 +727,8 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
   a.z = p.fwd.z;
   a.dy = p.dy;
   a.dh_last = p.dh_last;
-  a.bc = reinterpret_cast<const float*>(ws);
+  a.bc = reinterpret_cast<const float*>(ws + scan_flags_bytes());
+  a.err = reinterpret_cast<int*>(ws);
   a.ckpt = ckpt;
   a.du = p.du;
   a.ddelta = p.ddelta;
@@ -751,15 +759,20 @@ hipError_t launch_bwd_typed(const ScanBwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_combine_kernel<SPW>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, hloc,
                        dsum, p.fwd.A, p.dh_last, carry, (int)p.fwd.batch, (int)p.fwd.dim, (int)p.fwd.dstate,
                        (int)ntiles, nblocks, nwg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
   if (p.fwd.seqlen % 4 == 0)
     hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, true>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((scan_bwd_kernel<BF16, SPW, false>), dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
 
   // 3. fixed-order sums
   const int64_t total = 2 * p.fwd.batch * p.fwd.dstate * p.fwd.seqlen + p.fwd.dim * p.fwd.dstate + p.fwd.dim;
-  hipLaunchKernelGGL((bwd_reduce_kernel<BF16, SPW>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, dbc,
+  const unsigned rgrid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 16384));
+  hipLaunchKernelGGL((bwd_reduce_kernel<BF16, SPW>), dim3(rgrid), dim3(256), 0, stream, dbc,
                      dA_part, dD_part, p.dB, p.dC, p.dA, p.dD, (int)p.fwd.batch, (int)p.fwd.dim, (int)p.fwd.dstate,
                      (int)p.fwd.seqlen, nblocks, (int)ntiles, nwg, split ? 1 : 0);
   return hipGetLastError();

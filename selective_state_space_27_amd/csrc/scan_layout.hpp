@@ -144,6 +144,14 @@ __device__ __forceinline__ void store4(rsrc_t r, uint32_t lane_off, int t, int L
   }
 }
 
+// The forward's workspace opens with its flags block: [0] the call's status
+// word (nonzero when a bounded wait between workgroups gave up), [1] the
+// ticket, [2 ..) the carry flags of up to kMaxScanWG workgroups; the fp32 B/C
+// arrangement follows.
+constexpr int kMaxScanWG = 512;
+inline size_t align256(size_t x);
+inline size_t scan_flags_bytes() { return align256((size_t)(kMaxScanWG + 2) * sizeof(int)); }
+
 inline int states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : N <= 64 ? 8 : 16; }
 inline int64_t num_tiles(int64_t L) { return (L + kTile - 1) / kTile; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -140,6 +140,7 @@ struct SSDArgs {
   float* pstart;       // workspace [b, H, npieces, P, N]: exact state entering each piece (pieces 1..)
   float* cdec;         // workspace [b, H, nchunks]: A log2(e) sum of delta from the chunk's piece's start to the chunk
   float* pdec;         // workspace [b, H, npieces]: the same over each whole piece
+  int* status;         // workspace: the call's status word (first 4 bytes)
   int batch, L, H, G, Q, nchunks, Lp;
   int npieces, cpp;    // the sequence is cut into npieces pieces of cpp chunks (the last may be shorter)
 };
@@ -174,6 +175,8 @@ __global__ void __launch_bounds__(256) ssd_cumsum_kernel(SSDArgs a) {
   __shared__ float tile[kSub][65];
   const int l0 = blockIdx.x * kSub, h0 = blockIdx.y * 64, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // The workspace's status word (no kernel here waits on another workgroup).
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.status = 0;
 #pragma unroll
   for (int i = 0; i < kSub / 4; ++i) {
     const int j = w + 4 * i, l = l0 + j, hh = h0 + lane;
@@ -862,7 +865,7 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_
   int np, cpp;
   ssd_pieces(batch, nheads, nchunks, np, cpp);
   const size_t state = (size_t)headdim * dstate * sizeof(float);
-  return align256((size_t)batch * nchunks * nheads * state) + 2 * align256((size_t)batch * nheads * lp * sizeof(float)) +
+  return 256 + align256((size_t)batch * nchunks * nheads * state) + 2 * align256((size_t)batch * nheads * lp * sizeof(float)) +
          2 * align256((size_t)batch * nheads * np * state) + align256((size_t)batch * nheads * nchunks * sizeof(float)) +
          align256((size_t)batch * nheads * np * sizeof(float));
 }
@@ -880,7 +883,8 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.y = p.y;
   a.chunk_states = p.chunk_states;
   a.h_last = p.h_last;
-  a.s_in = static_cast<float*>(p.workspace);
+  a.status = static_cast<int*>(p.workspace);
+  a.s_in = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + 256);
   a.batch = (int)p.batch;
   a.L = (int)p.seqlen;
   a.H = (int)p.nheads;
@@ -889,7 +893,7 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.nchunks = (int)((p.seqlen + p.chunk - 1) / p.chunk);
   const int nsub = (a.L + kSub - 1) / kSub;
   a.Lp = nsub * kSub;
-  char* ws = static_cast<char*>(p.workspace);
+  char* ws = static_cast<char*>(p.workspace) + 256;
   ws += align256((size_t)a.batch * a.nchunks * a.H * kP * kN * sizeof(float));
   a.dlT = reinterpret_cast<float*>(ws);
   ws += align256((size_t)a.batch * a.H * a.Lp * sizeof(float));

@@ -133,16 +133,18 @@ def test_fused_identity_taps_equal_unfused_scan_bitwise():
     assert np.array_equal(y, host64(y2)) and np.array_equal(hl, host64(hl2))
 
 
-def test_fused_2p8b_workload_sampled_channels():
-    """b=4, d_inner=5120, N=16, L=8192, bf16: the full launch, bitwise
-    repeatable, checked on sampled channels of every batch row over the whole
-    sequence."""
+@pytest.mark.timeout(900)
+def test_fused_2p8b_workload_full():
+    """b=4, d_inner=5120, N=16, L=8192, bf16, silu convolution and softplus
+    delta: the full launch, bitwise repeatable, every element of y and h_last
+    against the oracle."""
     cfg = I.SCAN_2P8B
     x = I.scan_fused_inputs(cfg)
     y, hl = run_gpu(x, True, True)
     y2, hl2 = run_gpu(x, True, True)  # the same launch again: bitwise the same
     assert np.array_equal(y, y2) and np.array_equal(hl, hl2)
     del y2, hl2
-    chans = [0, 63, 64, 777, 2500, 5119]
-    ry, rhl = run_oracle(x, True, True, chans=chans)
-    check((y[:, chans], hl[:, chans]), (ry, rhl), "bf16", "scan_2p8b fused")
+    ry, rhl = run_oracle(x, True, True)
+    e1 = assert_close(y, ry, "bf16", "scan_2p8b fused y")
+    e2 = assert_close(hl, rhl, "bf16", "scan_2p8b fused h_last")
+    print(f"scan_2p8b fused full ({y.size} outputs): y max rel err {e1:.3e}, h_last {e2:.3e}")

@@ -65,11 +65,13 @@ def test_scan_equals_repeated_state_update_on_gpu():
     assert_close(host64(h), host64(hl), "fp32", "h")
 
 
-def test_decode_2p8b_workload_1000_steps_sampled():
+@pytest.mark.timeout(900)
+def test_decode_2p8b_workload_1000_steps_full():
     """b=256, d_inner=5120, N=16 bf16 generation: 1000 consecutive steps on the
     full state (in place), inputs cycling through the seeded per-step pool.
-    y at steps 1, 10, 100, 1000 and the final state are checked on 8 batch rows
-    x 64 channels against the oracle run over the same 1000 steps."""
+    Every element of y at steps 1, 10, 100 and 1000 and of the state after
+    steps 1, 100 and 1000, against the oracle run over the same 1000 steps
+    on the whole batch."""
     cfg = I.DECODE_2P8B
     st = I.decode_static(cfg)
     pool = [I.decode_step_inputs(cfg, s, st["dt"]) for s in range(I.DECODE_POOL)]
@@ -77,27 +79,25 @@ def test_decode_2p8b_workload_1000_steps_sampled():
     h0 = I.decode_state0(cfg)
     h = dev(h0)
     A, D = dev(st["A"]), dev(st["D"])
-    g = np.random.default_rng(7)
-    bsel = np.unique(np.concatenate([[0, cfg.batch - 1], g.choice(cfg.batch, 6, replace=False)]))
-    dsel = np.unique(np.concatenate([[0, cfg.dim - 1], g.choice(cfg.dim, 62, replace=False)]))
-    keep = {}
+    ys, hs = {}, {}
     for s in range(1, cfg.steps + 1):
         p = dpool[(s - 1) % I.DECODE_POOL]
         y = mss.state_update(h, p["u"], p["delta"], A, p["B"], p["C"], D, p["z"])
         if s in (1, 10, 100, 1000):
-            keep[s] = host64(y)[np.ix_(bsel, dsel)]
+            ys[s] = y.clone()
+        if s in (1, 100, 1000):
+            hs[s] = h.clone()
     torch.cuda.synchronize()
-    hg = host64(h)[np.ix_(bsel, dsel)]
-    hr = h0[np.ix_(bsel, dsel)].astype(np.float64)
-    Ar, Dr = st["A"][dsel].astype(np.float64), st["D"][dsel].astype(np.float64)
+    p64 = [{k: I.to_f64(p[k], "bf16") for k in ("u", "delta", "B", "C", "z")} for p in pool]
+    hr = h0.astype(np.float64)
     for s in range(1, cfg.steps + 1):
-        p = pool[(s - 1) % I.DECODE_POOL]
-        sub = lambda k: I.to_f64(p[k], "bf16")[np.ix_(bsel, dsel)]
-        hr, yr = oracle.state_update(hr, sub("u"), sub("delta"), Ar, I.to_f64(p["B"], "bf16")[bsel],
-                                     I.to_f64(p["C"], "bf16")[bsel], Dr, sub("z"))
-        if s in keep:
-            print(f"step {s}: y err {assert_close(keep[s], yr, 'bf16', f'y step {s}'):.2e}")
-    e = assert_close(hg, hr, "bf16", "h after 1000 steps")
-    rms = np.sqrt(np.mean(hr ** 2))
-    print(f"h after 1000 steps: err {e:.2e}, max abs err / rms {np.max(np.abs(hg - hr)) / rms:.2e}")
-    assert np.max(np.abs(hg - hr)) / rms < 1e-4
+        p = p64[(s - 1) % I.DECODE_POOL]
+        hr, yr = oracle.state_update(hr, p["u"], p["delta"], st["A"], p["B"], p["C"], st["D"], p["z"])
+        if s in ys:
+            print(f"step {s}: y max rel err {assert_close(host64(ys[s]), yr, 'bf16', f'y step {s}'):.3e}")
+        if s in hs:
+            hg = host64(hs[s])
+            e = assert_close(hg, hr, "bf16", f"h after step {s}")
+            rms = np.sqrt(np.mean(hr ** 2))
+            print(f"h after step {s}: max rel err {e:.3e}, max abs err / rms {np.max(np.abs(hg - hr)) / rms:.3e}")
+            assert np.max(np.abs(hg - hr)) / rms < 1e-4
