@@ -27,8 +27,9 @@
  * floating-point atomics are used and reduction orders are fixed.
  *
  * Thread safety: the library holds no mutable global state other than the
- * thread-local last HIP error; concurrent calls on different streams with
- * disjoint outputs and workspaces are safe.
+ * thread-local last HIP error and, for mss_selective_scan_fwd_noalloc, one
+ * fixed scratch buffer per GPU (see there); concurrent calls on different
+ * streams with disjoint outputs and workspaces are safe.
  */
 #ifndef MAMBASCAN_H_
 #define MAMBASCAN_H_
@@ -102,6 +103,29 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
                                   int64_t dstate, int64_t seqlen, mss_dtype io_dtype,
                                   uint32_t flags, void* workspace, size_t workspace_bytes,
                                   void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* mss_selective_scan_fwd without a workspace, for callers that cannot       */
+/* allocate device memory (code under HIP graph capture, tight serving       */
+/* loops, harnesses that forbid allocation).  The same computation, limits   */
+/* and errors as mss_selective_scan_fwd; its scratch is instead a fixed      */
+/* 64 MiB buffer inside the library, one per GPU, set up on the first call   */
+/* on that GPU (the stream's device must be current) and held until the      */
+/* process ends.  The call allocates nothing.  Shapes whose                  */
+/* mss_selective_scan_workspace_size() exceeds 64 MiB return                 */
+/* MSS_ERR_WORKSPACE, with nothing enqueued.  All calls on one GPU share that */
+/* buffer: calls that overlap in time on one GPU (different streams, or      */
+/* threads) race and give wrong results; calls in one stream are ordered.    */
+/* wait_status (nullable, 4-byte aligned device int, must not overlap any    */
+/* input or output): set to 0 by the call, to nonzero if a bounded wait      */
+/* between workgroups gave up (the outputs are then not valid).              */
+/* ------------------------------------------------------------------------ */
+mss_status mss_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
+                                          const void* B, const void* C, const float* D,
+                                          const void* z, const float* h0, void* y, float* h_last,
+                                          int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                          mss_dtype io_dtype, uint32_t flags, int* wait_status,
+                                          void* hip_stream);
 
 /* Bytes of device workspace mss_selective_scan_fwd needs for this shape
  * (0 when the shape is unsupported).  The workspace need not be zeroed. */

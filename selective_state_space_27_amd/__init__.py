@@ -9,6 +9,8 @@ or a GPU is absent, the calls raise.
 
 Operations (see the header for the exact definitions and layouts):
   selective_scan_fwd  Mamba-1 selective scan over a whole sequence
+  selective_scan_fwd_noalloc  the same on the library's fixed per-GPU
+                      scratch, for callers that cannot allocate
   selective_scan_fwd_fused  the same, fed by its prologue (short causal
                       convolution for u, delta from its raw value) in one pass
   selective_scan_bwd  its gradient
@@ -38,7 +40,8 @@ STATUS_NAMES = {0: "MSS_OK", 1: "MSS_ERR_NULL", 2: "MSS_ERR_SHAPE", 3: "MSS_ERR_
 MSS_ERR_WAIT = 9
 
 # Every symbol the header declares.
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_workspace_size", "mss_selective_scan_fwd_fused",
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_noalloc", "mss_selective_scan_workspace_size",
+           "mss_selective_scan_fwd_fused",
            "mss_selective_scan_bwd",
            "mss_selective_scan_bwd_workspace_size", "mss_state_update",
            "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_workspace_status", "mss_status_string",
@@ -71,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.mss_selective_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, i64, i64, i64, i64, ctypes.c_int,
                                          u32, vp, sz, vp]
     L.mss_selective_scan_fwd.restype = ctypes.c_int
+    L.mss_selective_scan_fwd_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, i64, i64, i64, i64,
+                                                 ctypes.c_int, u32, vp, vp]
+    L.mss_selective_scan_fwd_noalloc.restype = ctypes.c_int
     L.mss_selective_scan_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
     L.mss_selective_scan_workspace_size.restype = sz
     L.mss_selective_scan_fwd_fused.argtypes = [vp, fp, fp, vp, fp, fp, vp, vp, fp, vp, fp, vp, fp, i64, i64, i64,
@@ -214,6 +220,44 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, h0=None, *, return_las
     _raise(st, "mss_selective_scan_fwd")
     if check_waits:
         _check_waits(workspace, stream, "mss_selective_scan_fwd")
+    return (out, h_last) if return_last_state else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def selective_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, h0=None, *, return_last_state=False,
+                               force_general_decay=False, out=None, h_last=None, wait_status=None, stream=None):
+    """selective_scan_fwd on the library's fixed per-GPU scratch instead of a
+    workspace (the library allocates nothing; ``out`` and ``h_last`` given
+    make the call allocation-free here too).  Shapes that need more than
+    NOALLOC_SCRATCH_BYTES of scratch raise MSS_ERR_WORKSPACE; calls that
+    overlap in time on one GPU race.  ``wait_status``: an int32 device tensor
+    of one element, set to 0, or nonzero if a bounded wait gave up."""
+    dev = _device_of(u)
+    b, d, L = u.shape
+    N = A.shape[1]
+    io = u.dtype
+    _check(u, "u", (b, d, L), io, dev)
+    _check(delta, "delta", (b, d, L), io, dev)
+    _check(A, "A", (d, N), torch.float32, dev)
+    _check(B, "B", (b, N, L), io, dev)
+    _check(C, "C", (b, N, L), io, dev)
+    _check(D, "D", (d,), torch.float32, dev)
+    _check(z, "z", (b, d, L), io, dev)
+    _check(h0, "h0", (b, d, N), torch.float32, dev)
+    _check(wait_status, "wait_status", (1,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((b, d, L), dtype=io, device=dev)
+    _check(out, "out", (b, d, L), io, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((b, d, N), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", (b, d, N), torch.float32, dev)
+    flags = MSS_FLAG_DECAY_GENERAL if force_general_decay else 0
+    st = lib().mss_selective_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                              _ptr(h0), _ptr(out), _ptr(h_last), b, d, N, L, _io_code(io), flags,
+                                              _ptr(wait_status), _stream(stream))
+    _raise(st, "mss_selective_scan_fwd_noalloc")
     return (out, h_last) if return_last_state else out
 
 

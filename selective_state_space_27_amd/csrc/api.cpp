@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mambascan.h"
 #include "launch.hpp"
 
@@ -46,6 +48,35 @@ mss_status hip_status(hipError_t e) {
 }
 
 constexpr int64_t kMaxIndex = INT32_MAX;
+
+// Scratch of mss_selective_scan_fwd_noalloc, for callers that cannot allocate:
+// one copy per GPU, held until the process ends.  In host code `scratch`
+// names a host-side stand-in; its device address, different on each GPU,
+// comes from hipGetSymbolAddress with that GPU current and is kept per device.
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on its first use there.
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -98,10 +129,12 @@ size_t mss_selective_scan_workspace_size(int64_t batch, int64_t dim, int64_t dst
   return mss::scan_workspace_bytes(batch, dim, dstate, seqlen);
 }
 
-mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                                  const float* D, const void* z, const float* h0, void* y, float* h_last,
-                                  int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype io_dtype,
-                                  uint32_t flags, void* workspace, size_t workspace_bytes, void* hip_stream) {
+// The selective scan forward's checks before the workspace's: pointers,
+// shape, flags, alignment (`extra`, a 4-byte output, only needs 4 bytes).
+static mss_status scan_fwd_check_args(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                      const float* D, const void* z, const float* h0, const void* y,
+                                      const float* h_last, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                      mss_dtype io_dtype, uint32_t flags, const void* workspace, const void* extra) {
   if (!u || !delta || !A || !B || !C || !y) return MSS_ERR_NULL;
   mss_status st = scan_check_shape(batch, dim, dstate, seqlen, io_dtype);
   if (st != MSS_OK) return st;
@@ -109,9 +142,17 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
   const void* all[] = {u, delta, A, B, C, D, z, h0, y, h_last, workspace};
   for (const void* p : all)
     if (p && !aligned16(p)) return MSS_ERR_ALIGN;
-  const size_t need = mss::scan_workspace_bytes(batch, dim, dstate, seqlen);
-  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+  if (extra && (reinterpret_cast<uintptr_t>(extra) & 3u)) return MSS_ERR_ALIGN;
+  return MSS_OK;
+}
 
+// ... and after it: no output overlaps an input (the workspace, `need` bytes,
+// counts as one) or another output (`extra`, 4 bytes, nullable).
+static mss_status scan_fwd_check_alias(const void* u, const void* delta, const float* A, const void* B,
+                                       const void* C, const float* D, const void* z, const float* h0, const void* y,
+                                       const float* h_last, int64_t batch, int64_t dim, int64_t dstate,
+                                       int64_t seqlen, mss_dtype io_dtype, const void* workspace, size_t need,
+                                       const void* extra) {
   const size_t es = elem_size(io_dtype);
   const size_t nbdl = (size_t)batch * dim * seqlen;
   const size_t nbnl = (size_t)batch * dstate * seqlen;
@@ -122,7 +163,19 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
   if (!output_clear(y, nbdl * es, ins, in_bytes, 9)) return MSS_ERR_ALIAS;
   if (!output_clear(h_last, nstate, ins, in_bytes, 9)) return MSS_ERR_ALIAS;
   if (h_last && overlaps(range_of(y, nbdl * es), range_of(h_last, nstate))) return MSS_ERR_ALIAS;
+  if (extra) {
+    const Range e = range_of(extra, sizeof(int));
+    if (!output_clear(extra, sizeof(int), ins, in_bytes, 9)) return MSS_ERR_ALIAS;
+    if (overlaps(e, range_of(y, nbdl * es))) return MSS_ERR_ALIAS;
+    if (h_last && overlaps(e, range_of(h_last, nstate))) return MSS_ERR_ALIAS;
+  }
+  return MSS_OK;
+}
 
+static mss::ScanParams scan_params(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                   const float* D, const void* z, const float* h0, void* y, float* h_last,
+                                   int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype io_dtype,
+                                   uint32_t flags, void* workspace) {
   mss::ScanParams p;
   p.u = u;
   p.delta = delta;
@@ -141,6 +194,43 @@ mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float*
   p.bf16 = io_dtype == MSS_BF16;
   p.force_general = (flags & MSS_FLAG_DECAY_GENERAL) != 0;
   p.workspace = workspace;
+  return p;
+}
+
+mss_status mss_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* h0, void* y, float* h_last,
+                                  int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype io_dtype,
+                                  uint32_t flags, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  mss_status st = scan_fwd_check_args(u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen, io_dtype,
+                                      flags, workspace, nullptr);
+  if (st != MSS_OK) return st;
+  const size_t need = mss::scan_workspace_bytes(batch, dim, dstate, seqlen);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+  st = scan_fwd_check_alias(u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen, io_dtype, workspace,
+                            need, nullptr);
+  if (st != MSS_OK) return st;
+  const mss::ScanParams p = scan_params(u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen, io_dtype,
+                                        flags, workspace);
+  return hip_status(mss::launch_scan(p, static_cast<hipStream_t>(hip_stream)));
+}
+
+mss_status mss_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* D, const void* z, const float* h0, void* y,
+                                          float* h_last, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                          mss_dtype io_dtype, uint32_t flags, int* wait_status, void* hip_stream) {
+  mss_status st = scan_fwd_check_args(u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen, io_dtype,
+                                      flags, nullptr, wait_status);
+  if (st != MSS_OK) return st;
+  st = scan_fwd_check_alias(u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen, io_dtype, nullptr, 0,
+                            wait_status);
+  if (st != MSS_OK) return st;
+  if (mss::scan_workspace_bytes(batch, dim, dstate, seqlen) > kNoAllocScratchBytes) return MSS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  mss::ScanParams p = scan_params(u, delta, A, B, C, D, z, h0, y, h_last, batch, dim, dstate, seqlen, io_dtype, flags,
+                                  ws);
+  p.status = wait_status;
   return hip_status(mss::launch_scan(p, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -23,6 +23,9 @@ struct ScanParams {
   bool bf16;
   bool force_general;
   void* workspace;
+  // Where a bounded wait that gives up is reported (cleared at the start of
+  // the call): the workspace's first word when null.
+  int* status = nullptr;
   float* ckpt = nullptr;  // backward only: states entering every tile, [b*nblocks][ntiles][8][SPW][64]
   // Fused prologue (u = x and delta = delta_raw above): u from the causal
   // 4-tap convolution of x, delta from delta_raw plus bias, optionally softplus.

@@ -710,7 +710,8 @@ __global__ void __launch_bounds__(256) carry_combine_kernel(const float* __restr
 // B, C [batch, N, L] (bf16 or fp32) -> fp32 workspace in the bc_index layout,
 // zero for n >= N, l >= L and unused row positions.  Every loop strides over
 // the whole grid, so a capped grid covers any size.  The same launch clears
-// the status word, the ticket and the carry flags, and picks each 64-channel
+// the flags block (ticket, carry flags) and the call's status word (the
+// block's first word, or the caller's), and picks each 64-channel
 // block's decay mode (one wave per block, comparing exactly in fp32):
 // kDecayScalar when A[d,n] == A[d,0] for every channel d of the block, else
 // kDecayS4D when A[d,n] == (n+1)*A[d,0] for every channel, else kDecayGeneral.
@@ -719,11 +720,12 @@ __global__ void __launch_bounds__(256) bc_transpose_kernel(const void* __restric
                                                            float* __restrict__ out, int batch, int N, int L,
                                                            int ntiles, int* __restrict__ flags, int nflags,
                                                            const float* __restrict__ A, int* __restrict__ mode_out,
-                                                           int dim, int nblocks) {
+                                                           int dim, int nblocks, int* __restrict__ status) {
   using S = BCShape<SPW>;
   const size_t stride = (size_t)gridDim.x * blockDim.x;  // a multiple of 64: whole waves
   const size_t idx0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (size_t i = idx0; i < (size_t)nflags; i += stride) flags[i] = 0;
+  if (idx0 == 0) *status = 0;
   for (size_t wave = idx0 / kLanes; wave < (size_t)nblocks; wave += stride / kLanes) {
     const int c = (int)wave * kLanes + (int)(idx0 % kLanes);
     bool s4d = true, scalar = true;
@@ -813,7 +815,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
 
   hipLaunchKernelGGL((bc_transpose_kernel<BF16, SPW>), dim3(helper_grid(std::max<size_t>(nbc, (size_t)nblocks * kLanes))),
                      dim3(256), 0, stream, p.B, p.C, bc, (int)p.batch, (int)p.dstate, (int)p.seqlen, (int)ntiles,
-                     flags, (int)flag_ints(), p.A, mode, (int)p.dim, nblocks);
+                     flags, (int)flag_ints(), p.A, mode, (int)p.dim, nblocks, p.status ? p.status : flags);
   hipError_t err = hipGetLastError();  // the scan relies on the cleared ticket and flags
   if (err != hipSuccess) return err;
 
@@ -837,7 +839,7 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   a.hloc = hloc;
   a.dsum = dsum;
   a.ckpt = p.ckpt;
-  a.err = flags;
+  a.err = p.status ? p.status : flags;
   a.ticket = flags + 1;
   a.flags = flags + 2;
   a.nblocks = nblocks;

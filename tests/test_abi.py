@@ -229,6 +229,36 @@ def test_ssd_validation_errors():
     assert ssd_call(cs=P(11)) == ALIAS                                 # chunk_states on workspace
 
 
+def noalloc_call(**kw):
+    b, d, n, L = kw.pop("shape", (2, 64, 16, 128))
+    io = kw.pop("io", BF16)
+    a = dict(u=P(0), delta=P(1), A=P(2), B=P(3), C=P(4), D=P(5), z=P(6), h0=P(7), y=P(8), h_last=P(9), st=P(10),
+             flags=0)
+    a.update(kw)
+    return mss.lib().mss_selective_scan_fwd_noalloc(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                                    a["h0"], a["y"], a["h_last"], b, d, n, L, io, a["flags"], a["st"],
+                                                    None)
+
+
+def test_noalloc_validation_errors():
+    """The no-allocation scan validates like the forward, plus its fixed
+    scratch limit (64 MiB) and its status word, all before any HIP call."""
+    lib = mss.lib()
+    assert noalloc_call(u=None) == NULL
+    assert noalloc_call(shape=(0, 64, 16, 128)) == SHAPE
+    assert noalloc_call(shape=(2, 64, 129, 128)) == UNSUP
+    assert noalloc_call(flags=0x8) == UNSUP
+    assert noalloc_call(u=P(0, 8)) == ALIGN
+    assert noalloc_call(st=P(10, 2)) == ALIGN          # the status word needs 4-byte alignment
+    assert noalloc_call(y=P(0, 64)) == ALIAS
+    assert noalloc_call(st=P(8, 64)) == ALIAS          # status word inside y
+    assert noalloc_call(st=P(1, 4)) == ALIAS           # status word inside an input
+    big = (4, 5120, 128, 8192)
+    assert lib.mss_selective_scan_workspace_size(*big, BF16, 0) > mss.NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(shape=big) == WS
+    assert lib.mss_selective_scan_workspace_size(4, 5120, 16, 8192, BF16, 0) < mss.NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_status_rejects_null():
     assert mss.lib().mss_workspace_status(None, None) == NULL
 
