@@ -263,10 +263,11 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
 /*          chunk_states [batch, nchunks, nheads, headdim, dstate] fp32, the */
 /*          state after the last step of each chunk, nchunks = ceil(L/chunk). */
 /* D, z, h0, chunk_states and h_last may be NULL.                           */
-/* Supported: in_dtype MSS_BF16; headdim 64; dstate 128; chunk 64, 128 or   */
-/* 256; nheads % ngroups == 0; seqlen*nheads*headdim and                  */
-/* seqlen*ngroups*dstate below 2^30 and ceil(seqlen/chunk)*nheads*batch at  */
-/* most 2^24 (else MSS_ERR_SHAPE).  seqlen need not                        */
+/* Supported: in_dtype MSS_BF16; headdim 64 or 128; dstate a multiple of 16 */
+/* up to 256; chunk 64, 128 or 256; nheads % ngroups == 0 (else            */
+/* MSS_ERR_UNSUPPORTED); seqlen*nheads*headdim below 2^30 - 64,             */
+/* seqlen*ngroups*dstate below 2^30 and ceil(seqlen/chunk) * nheads *       */
+/* (headdim/64) * batch below 2^22 (else MSS_ERR_SHAPE).  seqlen need not   */
 /* be a multiple of chunk.                                                  */
 /* `flags` must be 0.  Outputs must not overlap inputs or each other.        */
 /* ------------------------------------------------------------------------ */

@@ -424,11 +424,13 @@ static mss_status ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads,
   if (seqlen * nheads * headdim > (int64_t{1} << 30) - 64 || seqlen * ngroups * dstate >= (int64_t{1} << 30) ||
       batch > 65535 || nheads > 65535)
     return MSS_ERR_SHAPE;
-  // One 256-thread workgroup per (chunk, head, batch entry) at most: the
-  // launch stays below 2^32 work-items.
-  if (((seqlen + chunk - 1) / chunk) * nheads * batch > (int64_t{1} << 24)) return MSS_ERR_SHAPE;
   if (t != MSS_BF16) return MSS_ERR_UNSUPPORTED;
-  if (headdim != 64 || dstate != 128 || !(chunk == 64 || chunk == 128 || chunk == 256)) return MSS_ERR_UNSUPPORTED;
+  if (!(headdim == 64 || headdim == 128) || dstate % 16 != 0 || dstate > 256 ||
+      !(chunk == 64 || chunk == 128 || chunk == 256))
+    return MSS_ERR_UNSUPPORTED;
+  // Grids: at most 2 * (chunks x 64-row head slices x batch) workgroups of
+  // 512 threads, below 2^32 work-items.
+  if (((seqlen + chunk - 1) / chunk) * nheads * (headdim / 64) * batch >= (int64_t{1} << 22)) return MSS_ERR_SHAPE;
   if (nheads % ngroups != 0) return MSS_ERR_UNSUPPORTED;
   return MSS_OK;
 }

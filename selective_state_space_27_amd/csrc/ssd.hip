@@ -133,18 +133,33 @@ struct SSDArgs {
   float* y;            // [b, L, H, P]
   float* chunk_states; // [b, nchunks, H, P, N] or null
   float* h_last;       // [b, H, P, N] or null
-  float* s_in;         // workspace [b, nchunks, H, P, N]: state entering each chunk, from its piece's start
   float* dlT;          // workspace [b, H, Lp]: delta, head-major (0 past L)
   float* lsT;          // workspace [b, H, Lp]: A log2(e) times the prefix sum of delta inside each 64-step block
-  float* pend;         // workspace [b, H, npieces, P, N]: state at the end of each piece, from the piece's start
-  float* pstart;       // workspace [b, H, npieces, P, N]: exact state entering each piece (pieces 1..)
-  float* cdec;         // workspace [b, H, nchunks]: A log2(e) sum of delta from the chunk's piece's start to the chunk
-  float* pdec;         // workspace [b, H, npieces]: the same over each whole piece
+  float* pend;         // workspace [b, Hv, npieces, 64, 128]: state at the end of each piece, from the piece's start
+  float* pstart;       // workspace [b, Hv, npieces, 64, 128]: exact state entering each piece (pieces 1..)
+  float* pdec;         // workspace [b, Hv, npieces]: A log2(e) sum of delta over each piece
   int* status;         // workspace: the call's status word (first 4 bytes)
   int batch, L, H, G, Q, nchunks, Lp;
+  // Heads of headdim P run as P/64 "virtual heads" of 64 (the rows p of a
+  // head's state evolve independently under the head's delta and A): virtual
+  // head v is rows (v % ph)*64.. of head v / ph.  States wider than 128 run as
+  // 128-wide halves, one launch sequence each: states noff .. noff+127 here
+  // (columns past N read and stay zero).
+  int P, ph, Hv, N, noff;
+  int accumulate;      // y += this half's part (second half of N > 128)
   int npieces, cpp;    // the sequence is cut into npieces pieces of cpp chunks (the last may be shorter)
 };
 
+__device__ __forceinline__ int head_of(const SSDArgs& a, int vh) { return vh / a.ph; }
+// Element offset of (virtual head vh, its row p) inside one step's [H, P] row.
+__device__ __forceinline__ size_t row_el(const SSDArgs& a, int vh, int p) {
+  return (size_t)(vh / a.ph) * a.P + (size_t)(vh % a.ph) * kP + p;
+}
+// Element offset of state row p, column noff of virtual head vh in a
+// [b, H, P, N] tensor (state_el(a, b, vh) + p*N + n, n < N - noff).
+__device__ __forceinline__ size_t state_el(const SSDArgs& a, int b, int vh) {
+  return (((size_t)b * a.H + vh / a.ph) * a.P + (size_t)(vh % a.ph) * kP) * a.N + a.noff;
+}
 
 // x plus lane (lane - S) of its 16-lane row (0 for the first S lanes of a row).
 template <int S>
@@ -194,21 +209,24 @@ __global__ void __launch_bounds__(256) ssd_cumsum_kernel(SSDArgs a) {
   }
 }
 
-// B or C rows of group g for steps (l0 + j, l0 + j + 1), 8 states from ng*8:
-// two 16-byte loads per unit, 2 units per thread.  Steps past L read zero.
+// B or C rows of group g for steps (l0 + j, l0 + j + 1), 8 states from
+// noff + ng*8: two 16-byte loads per unit, 2 units per thread.  Steps past L
+// and states past N read zero.
 struct BCRegs {
   u32x4 r[2][2];
 };
 __device__ __forceinline__ void load_bc_rows(const SSDArgs& a, const uint16_t* src, int b, int g, int l0, BCRegs& o) {
-  const rsrc_t rs = make_rsrc(src + (size_t)b * a.L * a.G * kN, (uint32_t)((size_t)a.L * a.G * kN * 2));
+  const rsrc_t rs = make_rsrc(src + (size_t)b * a.L * a.G * a.N, (uint32_t)((size_t)a.L * a.G * a.N * 2));
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int u = threadIdx.x + kT * it;  // 512 units: 32 step pairs x 16 groups of 8 states
     const int ng = u & 15, j = 2 * (u >> 4);
+    const bool nok = a.noff + ng * 8 < a.N;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int l = l0 + j + e;
-      const uint32_t off = (l < a.L) ? (uint32_t)((((size_t)l * a.G + g) * kN + ng * 8) * 2) : kOffNone;
+      const uint32_t off =
+          (l < a.L && nok) ? (uint32_t)((((size_t)l * a.G + g) * a.N + a.noff + ng * 8) * 2) : kOffNone;
       o.r[it][e] = buf_load_u32x4(rs, off);
     }
   }
@@ -237,43 +255,49 @@ __device__ __forceinline__ void store_bc_rows(const BCRegs& o, uint16_t (*rm)[kN
 }
 
 // One 32x32 tile of S^T (rows n = nt*32.., columns p = pt*32..) from a
-// [P][N] fp32 state: each lane moves 4 consecutive n of its column at a time.
-__device__ __forceinline__ void load_stateT(f32x16& acc, const float* S, int nt, int pt) {
+// state whose row p starts at S + p*ld (columns n < nmax valid, the rest
+// zero; nmax a multiple of 16): each lane moves 4 consecutive n of its column.
+__device__ __forceinline__ void load_stateT(f32x16& acc, const float* S, int nt, int pt, int ld = kN,
+                                            int nmax = kN) {
   const int lane = threadIdx.x & 63;
   const int p = pt * 32 + (lane & 31);
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
     const int n = nt * 32 + 8 * g4 + 4 * (lane >> 5);
-    const f32x4 v = S ? *reinterpret_cast<const f32x4*>(&S[(size_t)p * kN + n]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 v = (S && n < nmax) ? *reinterpret_cast<const f32x4*>(&S[(size_t)p * ld + n])
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[4 * g4 + q] = v[q];
   }
 }
 
-// The inverse: a 32x32 tile of S^T written back to a [P][N] fp32 state.
-__device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt, int pt) {
+// The inverse: a 32x32 tile of S^T written back (columns n < nmax only).
+__device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt, int pt, int ld = kN,
+                                             int nmax = kN) {
   const int lane = threadIdx.x & 63;
   const int p = pt * 32 + (lane & 31);
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
     const int n = nt * 32 + 8 * g4 + 4 * (lane >> 5);
-    *reinterpret_cast<f32x4*>(&S[(size_t)p * kN + n]) =
-        f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+    if (n < nmax)
+      *reinterpret_cast<f32x4*>(&S[(size_t)p * ld + n]) =
+          f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
   }
 }
 
 // ---------------------------------------------------------------------------
-// Chunk states.  grid (2H, batch, npieces), 512 threads: workgroup (b, h, pt,
-// piece) owns headdim tile pt over the chunks of one piece of the sequence and
-// runs them from a zero state (piece 0 from h0); ssd_chain_kernel then makes
-// the exact state entering each piece, which the scan kernel adds, decayed,
-// to the state entering each of its chunks.  Cutting the sequence keeps every
-// CU equally busy (2H x batch streams alone would leave some CUs with two).  Wave w owns S^T rows (w&3)*32.. over half of every block's
-// steps (k-half w>>2): the state is the sum of the two halves' partial states,
-// which decay alike, so they are only added where a state is written out.
-// Each thread forms the decay weights of its own steps from the head-major
-// delta rows; the weighted x (w_j x_j) is staged once per block as bf16 hi/lo
-// pairs.  Stagings are double-buffered: one barrier per block.
+// Piece states.  grid (2 Hv, batch, npieces), 512 threads: workgroup (b, vh,
+// pt, piece) owns headdim tile pt of virtual head vh over the chunks of one
+// piece of the sequence and runs them from a zero state (piece 0 from h0),
+// writing only the piece's end state and its decay; ssd_chain_kernel then
+// makes the exact state entering each piece, from which the scan kernel walks
+// the piece's chunks.  Cutting the sequence keeps every CU equally busy.
+// Wave w owns S^T rows (w&3)*32.. over half of every block's steps (k-half
+// w>>2): the state is the sum of the two halves' partial states, which decay
+// alike, so they are only added where the state is written out.  Each thread
+// forms the decay weights of its own steps from the head-major delta rows;
+// the weighted x (w_j x_j) is staged once per block as bf16 hi/lo pairs.
+// Stagings are double-buffered: one barrier per block.
 constexpr int kTS = 512;
 
 __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
@@ -286,12 +310,13 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   constexpr int kSRow = kN + 4;
   __shared__ __attribute__((aligned(16))) float sout[32 * kSRow];
 
-  // Both headdim tiles of a head on one XCD (workgroups are dealt to the XCDs
-  // round-robin), so that each x row is fetched from HBM once.
+  // Both headdim tiles of a virtual head on one XCD (workgroups are dealt to
+  // the XCDs round-robin), so that each x row is fetched from HBM once.
   const int i = blockIdx.x;
-  const bool pair = (a.H & 7) == 0;
+  const bool pair = (a.Hv & 7) == 0;
   const int pt = pair ? (i >> 3) & 1 : i & 1;
-  const int h = pair ? ((i >> 4) << 3) | (i & 7) : i >> 1;
+  const int vh = pair ? ((i >> 4) << 3) | (i & 7) : i >> 1;
+  const int h = head_of(a, vh);
   const int b = blockIdx.y;
   const int piece = blockIdx.z;
   const int g = h / (a.H / a.G);
@@ -300,7 +325,7 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const int nt = w & 3, kh = w >> 2;
   const size_t state_stride = (size_t)kP * kN;
   const Dot2Masks dm = dot2_masks();
-  // This piece's chunks [c0, c1) and 64-step blocks [sb0, sb1).
+  // This piece's 64-step blocks [sb0, sb1).
   const int sub_per_chunk = a.Q / kSub;
   const int nsub = (a.L + kSub - 1) / kSub;
   const int c0 = piece * a.cpp;
@@ -308,15 +333,19 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const int sb1 = min(nsub, min(a.nchunks, c0 + a.cpp) * sub_per_chunk);
 
   // Staging map: thread -> step pair (jx, jx+1); headdim values pq*2, pq*2+1
-  // of x, states ng*8 .. ng*8+7 of B.
+  // of x, states noff + ng*8 .. +7 of B.
   const int pq = threadIdx.x & 15, ng = pq, jx = 2 * (threadIdx.x >> 4);
   // Each block's loads go through descriptors based at the block's first
   // step, so the per-lane offsets are fixed; rows past L (or past the padded
-  // delta rows) lie beyond the descriptor and read 0.  Byte offsets inside
-  // one batch entry fit 32 bits (checked by the caller).
-  const uint32_t x_row = (uint32_t)(a.H * kP * 2), b_row = (uint32_t)(a.G * kN * 2);
-  const uint32_t xo0 = (uint32_t)jx * x_row + (uint32_t)((h * kP + pt * 32 + pq * 2) * 2), xo1 = xo0 + x_row;
-  const uint32_t bo0 = (uint32_t)jx * b_row + (uint32_t)((g * kN + ng * 8) * 2), bo1 = bo0 + b_row;
+  // delta rows) lie beyond the descriptor and read 0, and so do the B columns
+  // past N.  Byte offsets inside one batch entry fit 32 bits (checked by the
+  // caller).
+  const uint32_t x_row = (uint32_t)(a.H * a.P * 2), b_row = (uint32_t)(a.G * a.N * 2);
+  const uint32_t xo0 = (uint32_t)jx * x_row + (uint32_t)(row_el(a, vh, pt * 32 + pq * 2) * 2), xo1 = xo0 + x_row;
+  const bool bok = a.noff + ng * 8 < a.N;
+  const uint32_t bcol = (uint32_t)((g * a.N + a.noff + ng * 8) * 2);
+  const uint32_t bo0 = bok ? (uint32_t)jx * b_row + bcol : kOffNone;
+  const uint32_t bo1 = bok ? (uint32_t)(jx + 1) * b_row + bcol : kOffNone;
   const uint32_t dlo = (uint32_t)jx * 4u;
   const size_t row_bh = ((size_t)b * a.H + h) * a.Lp;
 
@@ -336,7 +365,7 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   auto load_x = [&](int blk, XSlot& sl) {
     const int l0 = blk * kSub;
     const uint32_t left = (uint32_t)max(a.L - l0, 0), left_p = (uint32_t)max(a.Lp - l0, 0);
-    const rsrc_t rx = make_rsrc(a.x + ((size_t)b * a.L + l0) * a.H * kP, left * x_row);
+    const rsrc_t rx = make_rsrc(a.x + ((size_t)b * a.L + l0) * a.H * a.P, left * x_row);
     const rsrc_t rd = make_rsrc(a.dlT + row_bh + l0, left_p * 4u);
     const rsrc_t rl = make_rsrc(a.lsT + row_bh + l0, left_p * 4u);
     sl.xr[0] = buf_load_u32(rx, xo0);
@@ -351,7 +380,7 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   auto load_b = [&](int blk, BSlot& sl) {
     const int l0 = blk * kSub;
     const uint32_t left = (uint32_t)max(a.L - l0, 0);
-    const rsrc_t rb = make_rsrc(a.B + ((size_t)b * a.L + l0) * a.G * kN, left * b_row);
+    const rsrc_t rb = make_rsrc(a.B + ((size_t)b * a.L + l0) * a.G * a.N, left * b_row);
     sl.br[0] = buf_load_u32x4(rb, bo0);
     sl.br[1] = buf_load_u32x4(rb, bo1);
   };
@@ -378,10 +407,11 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   // The state is the sum of both k-halves' partials: k-half 0 of piece 0
   // starts from h0, everything else from zero.
   f32x16 st;
-  load_stateT(st, (a.h0 && kh == 0 && piece == 0) ? a.h0 + ((size_t)b * a.H + h) * state_stride : nullptr, nt, pt);
-  // Writes the full state slice (rows pt*32.., all n) of a [P][N] state: k-half
-  // 1 puts its partial in LDS, k-half 0 adds its own, then the workgroup
-  // copies the 16 KB slice out with whole-row stores.
+  load_stateT(st, (a.h0 && kh == 0 && piece == 0) ? a.h0 + state_el(a, b, vh) : nullptr, nt, pt, a.N,
+              a.N - a.noff);
+  // Writes the full state slice (rows pt*32.., all 128 n) of a [64][128]
+  // state: k-half 1 puts its partial in LDS, k-half 0 adds its own, then the
+  // workgroup copies the 16 KB slice out with whole-row stores.
   auto write_state = [&](float* S) {
     const int sp = lc;  // headdim row of this lane's accumulator column
     if (kh == 1) {
@@ -409,7 +439,6 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
       const int row = e / kN, col = e % kN;
       *reinterpret_cast<f32x4*>(&dst[e]) = *reinterpret_cast<const f32x4*>(&sout[row * kSRow + col]);
     }
-    __syncthreads();
   };
 
   // Software pipeline: iteration rel runs block sb0+rel's products from
@@ -428,10 +457,6 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   stage(xring[0], bring[0], 0);
   float lcur = xring[0].last;  // s_last (log2 units) of the block being multiplied
   float lsum = 0.f;            // the same summed over the piece's earlier blocks
-  // Chunk and piece decays for the scan and chain kernels (uniform values;
-  // one thread of one headdim tile writes them).
-  const bool dec_writer = threadIdx.x == 0 && pt == 0;
-  float* const cdec_row = a.cdec + ((size_t)b * a.H + h) * a.nchunks;
   load_b(sb0 + 2, bring[0]);
   load_x(sb0 + 4, xring[0]);
   __syncthreads();
@@ -440,14 +465,7 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
     constexpr int SX = decltype(x_tag)::value;  // (rel + 1) % 4
     constexpr int SB = decltype(b_tag)::value;  // (rel + 1) % 2
     const int sb = sb0 + rel;
-    const int c = sb / sub_per_chunk;
     const int buf = rel & 1;
-    // State entering chunk c (a later piece's first chunk enters with zero,
-    // which the scan kernel knows without reading it).
-    if (rel % sub_per_chunk == 0) {
-      if (rel > 0 || piece == 0) write_state(a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride);
-      if (dec_writer) cdec_row[c] = lsum;
-    }
     st *= exp2_fast(lcur);
     lsum += lcur;
 #pragma unroll
@@ -486,24 +504,25 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   if (rel < nrel) step(I1{}, I1{}, rel);
   if (rel + 1 < nrel) step(I2{}, I0{}, rel + 1);
   if (rel + 2 < nrel) step(I3{}, I1{}, rel + 2);
-  // The piece's end state (from its start) for the chain; the last piece's is
-  // not needed (the scan kernel of the last chunk writes the final state).
-  if (piece < a.npieces - 1)
-    write_state(a.pend + (((size_t)b * a.H + h) * a.npieces + piece) * state_stride);
-  if (dec_writer) a.pdec[((size_t)b * a.H + h) * a.npieces + piece] = lsum;
+  // The piece's end state (from its start) and decay for the chain; the last
+  // piece's are not needed (the scan kernel walks that piece to the end).
+  if (piece < a.npieces - 1) {
+    write_state(a.pend + (((size_t)b * a.Hv + vh) * a.npieces + piece) * state_stride);
+    if (threadIdx.x == 0 && pt == 0) a.pdec[((size_t)b * a.Hv + vh) * a.npieces + piece] = lsum;
+  }
 }
 
 // The exact state entering every piece after the first:
 // S(k+1) = exp(A sum of delta over piece k) S(k) + pend(k), S(1) = pend(0)
-// (piece 0 ran from h0).  grid (8 slices of the state, H, batch), 256
+// (piece 0 ran from h0).  grid (8 slices of the state, Hv, batch), 256
 // threads, 4 state elements per thread.
 constexpr int kMaxPieces = 64;
 __global__ void __launch_bounds__(256) ssd_chain_kernel(SSDArgs a) {
   const int h = blockIdx.y, b = blockIdx.z;
   const size_t state_stride = (size_t)kP * kN;
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
-  const size_t base = ((size_t)b * a.H + h) * a.npieces * state_stride + e;
-  const float* pdec = a.pdec + ((size_t)b * a.H + h) * a.npieces;
+  const size_t base = ((size_t)b * a.Hv + h) * a.npieces * state_stride + e;
+  const float* pdec = a.pdec + ((size_t)b * a.Hv + h) * a.npieces;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   for (int k = 1; k < a.npieces; ++k) {
     const f32x4 pe = *reinterpret_cast<const f32x4*>(&a.pend[base + (size_t)(k - 1) * state_stride]);
@@ -513,15 +532,20 @@ __global__ void __launch_bounds__(256) ssd_chain_kernel(SSDArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk outputs.  grid (nchunks, H, batch), 256 threads.  Wave w = (rt, pt)
-// with rt = w>>1, pt = w&1 owns output tile (row tile rt, headdim tile pt) and
-// the two S^T tiles (state rows 64*rt .. +64, headdim tile pt).  C S^T is
-// split by state rows: each wave forms it over its own two state tiles for
-// both row tiles and hands the other row tile's partial sum to its partner
-// wave (1-rt, pt) through LDS, already scaled by exp(s_i).  Of the masked
-// decay block's three 32x32 tiles (0,0), (1,0), (1,1), the full tile (1,0) is
-// split by k-slice between the two row tiles, so that every wave forms three
-// slices; the rows-0 wave hands its slice's product over with the C S^T part.
+// Outputs.  grid (npieces x Hv x batch), 256 threads: one workgroup per
+// (batch, virtual head, piece) starts from the exact state entering its piece
+// and walks the piece's chunks in 64-step blocks, the running state staying
+// in the matrix cores' accumulators; the state after each chunk is written
+// when requested (it is exact), and the final state by the last piece.  Wave
+// w = (rt, pt) with rt = w>>1, pt = w&1 owns output tile (row tile rt,
+// headdim tile pt) and the two S^T tiles (state rows 64*rt .. +64, headdim
+// tile pt).  C S^T is split by state rows: each wave forms it over its own
+// two state tiles for both row tiles and hands the other row tile's partial
+// sum to its partner wave (1-rt, pt) through LDS, already scaled by exp(s_i).
+// Of the masked decay block's three 32x32 tiles (0,0), (1,0), (1,1), the full
+// tile (1,0) is split by k-slice between the two row tiles, so that every wave
+// forms three slices; the rows-0 wave hands its slice's product over with the
+// C S^T part.
 // Part of the masked decay block: the G^T tile (rows j of tile JT, columns i
 // of tile RT) = B C^T on the matrix cores, then k-slices [S0, S1) of
 // M = mask o G o exp(s_i - s_j) delta_j as the A operand (rows i, k = j),
@@ -585,7 +609,7 @@ __device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN 
   if constexpr (S0 <= 1 && S1 > 1) slice(std::integral_constant<int, 1>{});
 }
 
-template <bool HAS_Z, bool HAS_D>
+template <bool HAS_Z, bool HAS_D, bool ACCUM>
 __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xT[kP * kTRow];  // tsw layout, headdim rows
   __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];  // tsw layout, state rows
@@ -602,18 +626,20 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ int s_factored;
 
   // Workgroups are dealt to the 8 XCDs round-robin; XCD x takes a contiguous
-  // run of (chunk, batch, head) items in chunk-major order, so the B and C
-  // rows of a chunk and the entering state of a piece are read into one L2.
-  int c, h, b;
+  // run of (piece, batch, virtual head) items in piece-major order, so the B
+  // and C rows of a piece, shared by all heads of its group, are read into one
+  // L2.
+  int piece, vh, b;
   {
-    const int nwg = a.nchunks * a.batch * a.H;
+    const int nwg = a.npieces * a.batch * a.Hv;
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int q = nwg >> 3, r = nwg & 7;
     const int t = x * q + min(x, r) + j;
-    c = t / (a.batch * a.H);
-    b = (t / a.H) % a.batch;
-    h = t % a.H;
+    piece = t / (a.batch * a.Hv);
+    b = (t / a.Hv) % a.batch;
+    vh = t % a.Hv;
   }
+  const int h = head_of(a, vh);
   const int g = h / (a.H / a.G);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lc = lane & 31, hf = lane >> 5;
@@ -622,16 +648,18 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const int partner = w ^ 2;
   const float dh = a.D ? a.D[h] : 0.f;
   const size_t state_stride = (size_t)kP * kN;
-  const int p = pt * 32 + lc;  // headdim of this lane's output column
+  const int p = pt * 32 + lc;  // headdim row (within the virtual head) of this lane's output column
+  const int nvalid = a.N - a.noff;  // state columns of this half that exist (the rest stay zero)
 
   // x staging: thread -> (step pair j, 8 headdim values pg*8..).
   const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
-  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * kP, (uint32_t)((size_t)a.L * a.H * kP * 2));
+  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * a.P, (uint32_t)((size_t)a.L * a.H * a.P * 2));
+  const size_t xcol = row_el(a, vh, pg * 8);
   auto load_x = [&](int l0, u32x4* xr) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int l = l0 + jx + e;
-      const uint32_t off = (l < a.L) ? (uint32_t)((((size_t)l * a.H + h) * kP + pg * 8) * 2) : kOffNone;
+      const uint32_t off = (l < a.L) ? (uint32_t)(((size_t)l * a.H * a.P + xcol) * 2) : kOffNone;
       xr[e] = buf_load_u32x4(rx, off);
     }
   };
@@ -644,55 +672,51 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     }
   };
 
-  // This wave's two S^T tiles: state rows (2*rt + t)*32.., headdim tile pt.
-  // The state entering the chunk is the one from its piece's start plus the
-  // exact state entering the piece decayed over the chunks between (the first
-  // chunk of a later piece enters with zero from its piece's start).
+  // This wave's two S^T tiles: state rows (2*rt + t)*32.., headdim tile pt,
+  // from the exact state entering the piece (piece 0: h0 or zero).
   f32x16 st[2];
-  const int piece = c / a.cpp;
-  const bool piece_head = piece > 0 && c % a.cpp == 0;
-  const float* sin = a.s_in + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride;
+  if (piece == 0) {
+    const float* s0 = a.h0 ? a.h0 + state_el(a, b, vh) : nullptr;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) load_stateT(st[t], piece_head ? nullptr : sin, 2 * rt + t, pt);
-  if (piece > 0) {
-    const float e = exp2_fast(a.cdec[((size_t)b * a.H + h) * a.nchunks + c]);
-    const float* ps = a.pstart + (((size_t)b * a.H + h) * a.npieces + piece) * state_stride;
+    for (int t = 0; t < 2; ++t) load_stateT(st[t], s0, 2 * rt + t, pt, a.N, nvalid);
+  } else {
+    const float* ps = a.pstart + (((size_t)b * a.Hv + vh) * a.npieces + piece) * state_stride;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 v;
-      load_stateT(v, ps, 2 * rt + t, pt);
-      st[t] += e * v;
-    }
+    for (int t = 0; t < 2; ++t) load_stateT(st[t], ps, 2 * rt + t, pt);
   }
 
   // Output of the previous block, finished at the start of the next one (the
   // partner's part is in xbuf then): accumulator and x of this lane's 16 rows.
-  const int lbeg = c * a.Q;
-  const int lend = min(a.L, lbeg + a.Q);
+  const int lbeg = piece * a.cpp * a.Q;
+  const int lend = min(a.L, lbeg + a.cpp * a.Q);
   f32x16 yprev = {};
   float xprev[16];
   int lprev = -1;  // first step of the block yprev belongs to
-  // y and z rows of this batch entry and head: element (step l, headdim p) at
-  // l*H*P + p; steps outside the chunk are dropped (store) or read as 0 (z).
-  const uint32_t row = (uint32_t)(a.H * kP);
-  const size_t bh_el = (size_t)b * a.L * a.H * kP + (size_t)h * kP;
-  const rsrc_t ry = make_rsrc(a.y + bh_el, (uint32_t)(((size_t)a.L * a.H - h) * kP * 4));
-  const rsrc_t rz = make_rsrc(a.z ? a.z + bh_el : nullptr, a.z ? (uint32_t)(((size_t)a.L * a.H - h) * kP * 2) : 0u);
+  // y and z rows of this batch entry and virtual head: element (step l,
+  // headdim p) at l*H*P + p; steps outside the piece are dropped (store) or
+  // read as 0 (z, and y when accumulating).
+  const uint32_t row = (uint32_t)(a.H * a.P);
+  const size_t hoff = row_el(a, vh, 0);
+  const size_t bh_el = (size_t)b * a.L * a.H * a.P + hoff;
+  const uint32_t ybytes = (uint32_t)(((size_t)a.L * a.H * a.P - hoff) * 4);
+  const rsrc_t ry = make_rsrc(a.y + bh_el, ybytes);
+  const rsrc_t rz = make_rsrc(a.z ? a.z + bh_el : nullptr, a.z ? ybytes / 2 : 0u);
   auto finish = [&]() {
     if (lprev < 0) return;
-    float zv[16];
-    if constexpr (HAS_Z) {
+    float zv[16], yv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int l = lprev + rt * 32 + acc_row(r, lane);
-        const uint32_t zo = (l < lend) ? ((uint32_t)l * row + (uint32_t)p) * 2u : kOffNone;
-        zv[r] = bf16_to_f32(buf_load_u16(rz, zo));
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int l = lprev + rt * 32 + acc_row(r, lane);
+      const bool in = l < lend;
+      if constexpr (HAS_Z) zv[r] = bf16_to_f32(buf_load_u16(rz, in ? ((uint32_t)l * row + (uint32_t)p) * 2u : kOffNone));
+      if constexpr (ACCUM)
+        yv[r] = __uint_as_float(buf_load_u32(ry, in ? ((uint32_t)l * row + (uint32_t)p) * 4u : kOffNone));
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int l = lprev + rt * 32 + acc_row(r, lane);
       float v = xbuf[partner][r][lane] + yprev[r];
+      if constexpr (ACCUM) v += yv[r];
       if constexpr (HAS_D) v = __builtin_fmaf(dh, xprev[r], v);
       if constexpr (HAS_Z) v *= silu(zv[r]);
       const uint32_t yo = (l < lend) ? ((uint32_t)l * row + (uint32_t)p) * 4u : kOffNone;
@@ -785,7 +809,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) xbuf[w][r][lane] = yoth[r];
     // The next block's loads, issued once the products that need the most
-    // registers are done (the block after the chunk's last is read and
+    // registers are done (the block after the piece's last is read and
     // ignored; past L reads zero).
     load_x(l0 + kSub, xr);
     load_bc_rows(a, a.B, b, g, l0 + kSub, br);
@@ -826,48 +850,69 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
         st[t] = mfma(av, bl, st[t]);
       }
     }
+    // The state after a chunk (exact: the piece started from the exact
+    // state).  A chunk ends with a block (chunks hold whole 64-step blocks);
+    // the last chunk may stop at L, where the block's later steps (delta 0)
+    // left the state unchanged.
+    if (a.chunk_states && ((l0 + kSub) % a.Q == 0 || l0 + kSub >= lend)) {
+      const int c = l0 / a.Q;
+      float* cs = a.chunk_states + ((size_t)b * a.nchunks + c) * a.H * a.P * a.N +
+                  (state_el(a, b, vh) - (size_t)b * a.H * a.P * a.N);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) store_stateT(st[t], cs, 2 * rt + t, pt, a.N, nvalid);
+    }
     __syncthreads();
   }
   finish();
-  // The state after the chunk (exact: the chunk started from the exact state).
-  if (a.chunk_states) {
-    float* cs = a.chunk_states + (((size_t)b * a.nchunks + c) * a.H + h) * state_stride;
+  if (a.h_last && piece == a.npieces - 1) {
+    float* hl = a.h_last + state_el(a, b, vh);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) store_stateT(st[t], cs, 2 * rt + t, pt);
-  }
-  if (a.h_last && c == a.nchunks - 1) {
-    float* hl = a.h_last + ((size_t)b * a.H + h) * state_stride;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) store_stateT(st[t], hl, 2 * rt + t, pt);
+    for (int t = 0; t < 2; ++t) store_stateT(st[t], hl, 2 * rt + t, pt, a.N, nvalid);
   }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-}  // namespace
-
-// Pieces per sequence: about ten state-kernel workgroups per CU over all
-// pieces (2H x batch streams), at most kMaxPieces and one per chunk; pieces
-// hold whole chunks, cpp each.
-void ssd_pieces(int64_t batch, int64_t nheads, int64_t nchunks, int& npieces, int& cpp) {
-  const int64_t streams = 2 * nheads * batch;
+// Pieces per sequence: the scan kernel runs one workgroup per (batch, virtual
+// head, piece), two per CU, so about ten of them per CU over all pieces (and
+// twice as many state-kernel workgroups), at most kMaxPieces and one per
+// chunk; pieces hold whole chunks, cpp each.
+void ssd_pieces(int64_t batch, int64_t vheads, int64_t nchunks, int& npieces, int& cpp) {
+  const int64_t streams = vheads * batch;
   int64_t np = (2560 + streams - 1) / streams;
   np = std::max<int64_t>(1, std::min<int64_t>({np, (int64_t)kMaxPieces, nchunks}));
   cpp = (int)((nchunks + np - 1) / np);
   npieces = (int)((nchunks + cpp - 1) / cpp);
 }
 
+struct SSDLayout {
+  size_t dlT, lsT, pend, pstart, pdec, total;
+};
+
+SSDLayout ssd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t chunk) {
+  const int64_t nchunks = (seqlen + chunk - 1) / chunk;
+  const int64_t lp = (seqlen + kSub - 1) / kSub * kSub;
+  const int64_t vheads = nheads * (headdim / kP);
+  int np, cpp;
+  ssd_pieces(batch, vheads, nchunks, np, cpp);
+  const size_t state = (size_t)kP * kN * sizeof(float);
+  SSDLayout l;
+  l.dlT = 256;  // after the status word
+  l.lsT = l.dlT + align256((size_t)batch * nheads * lp * sizeof(float));
+  l.pend = l.lsT + align256((size_t)batch * nheads * lp * sizeof(float));
+  l.pstart = l.pend + align256((size_t)batch * vheads * np * state);
+  l.pdec = l.pstart + align256((size_t)batch * vheads * np * state);
+  l.total = l.pdec + align256((size_t)batch * vheads * np * sizeof(float));
+  return l;
+}
+
+}  // namespace
+
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                            int64_t dstate, int64_t chunk) {
   (void)ngroups;
-  const int64_t nchunks = (seqlen + chunk - 1) / chunk;
-  const int64_t lp = (seqlen + kSub - 1) / kSub * kSub;
-  int np, cpp;
-  ssd_pieces(batch, nheads, nchunks, np, cpp);
-  const size_t state = (size_t)headdim * dstate * sizeof(float);
-  return 256 + align256((size_t)batch * nchunks * nheads * state) + 2 * align256((size_t)batch * nheads * lp * sizeof(float)) +
-         2 * align256((size_t)batch * nheads * np * state) + align256((size_t)batch * nheads * nchunks * sizeof(float)) +
-         align256((size_t)batch * nheads * np * sizeof(float));
+  (void)dstate;
+  return ssd_layout(batch, seqlen, nheads, headdim, chunk).total;
 }
 
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
@@ -883,48 +928,58 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
   a.y = p.y;
   a.chunk_states = p.chunk_states;
   a.h_last = p.h_last;
-  a.status = static_cast<int*>(p.workspace);
-  a.s_in = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + 256);
   a.batch = (int)p.batch;
   a.L = (int)p.seqlen;
   a.H = (int)p.nheads;
   a.G = (int)p.ngroups;
   a.Q = (int)p.chunk;
+  a.P = (int)p.headdim;
+  a.ph = (int)(p.headdim / kP);
+  a.Hv = a.H * a.ph;
+  a.N = (int)p.dstate;
   a.nchunks = (int)((p.seqlen + p.chunk - 1) / p.chunk);
   const int nsub = (a.L + kSub - 1) / kSub;
   a.Lp = nsub * kSub;
-  char* ws = static_cast<char*>(p.workspace) + 256;
-  ws += align256((size_t)a.batch * a.nchunks * a.H * kP * kN * sizeof(float));
-  a.dlT = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)a.batch * a.H * a.Lp * sizeof(float));
-  a.lsT = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)a.batch * a.H * a.Lp * sizeof(float));
-  ssd_pieces(a.batch, a.H, a.nchunks, a.npieces, a.cpp);
-  const size_t piece_states = (size_t)a.batch * a.H * a.npieces * kP * kN * sizeof(float);
-  a.pend = reinterpret_cast<float*>(ws);
-  ws += align256(piece_states);
-  a.pstart = reinterpret_cast<float*>(ws);
-  ws += align256(piece_states);
-  a.cdec = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)a.batch * a.H * a.nchunks * sizeof(float));
-  a.pdec = reinterpret_cast<float*>(ws);
+  const SSDLayout l = ssd_layout(p.batch, p.seqlen, p.nheads, p.headdim, p.chunk);
+  char* ws = static_cast<char*>(p.workspace);
+  a.status = reinterpret_cast<int*>(ws);
+  a.dlT = reinterpret_cast<float*>(ws + l.dlT);
+  a.lsT = reinterpret_cast<float*>(ws + l.lsT);
+  a.pend = reinterpret_cast<float*>(ws + l.pend);
+  a.pstart = reinterpret_cast<float*>(ws + l.pstart);
+  a.pdec = reinterpret_cast<float*>(ws + l.pdec);
+  ssd_pieces(a.batch, a.Hv, a.nchunks, a.npieces, a.cpp);
   hipLaunchKernelGGL(ssd_cumsum_kernel, dim3((unsigned)nsub, (unsigned)((a.H + 63) / 64), (unsigned)a.batch), dim3(256),
                      0, stream, a);
-  hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.H), (unsigned)a.batch, (unsigned)a.npieces), dim3(kTS), 0,
-                     stream, a);
-  if (a.npieces > 1)
-    hipLaunchKernelGGL(ssd_chain_kernel, dim3((unsigned)(kP * kN / 1024), (unsigned)a.H, (unsigned)a.batch), dim3(256),
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // States wider than 128 run as two 128-wide halves; the second adds its
+  // part of y to the first's and applies D and the gate.
+  const int halves = (a.N + kN - 1) / kN;
+  for (int hv = 0; hv < halves; ++hv) {
+    a.noff = hv * kN;
+    a.accumulate = hv > 0 ? 1 : 0;
+    const bool last = hv == halves - 1;
+    hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.Hv), (unsigned)a.batch, (unsigned)a.npieces), dim3(kTS),
                        0, stream, a);
-  const dim3 grid((unsigned)a.nchunks * (unsigned)a.H * (unsigned)a.batch);
-  if (a.z && a.D)
-    hipLaunchKernelGGL((ssd_scan_kernel<true, true>), grid, dim3(kT), 0, stream, a);
-  else if (a.z)
-    hipLaunchKernelGGL((ssd_scan_kernel<true, false>), grid, dim3(kT), 0, stream, a);
-  else if (a.D)
-    hipLaunchKernelGGL((ssd_scan_kernel<false, true>), grid, dim3(kT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((ssd_scan_kernel<false, false>), grid, dim3(kT), 0, stream, a);
-  return hipGetLastError();
+    if (a.npieces > 1)
+      hipLaunchKernelGGL(ssd_chain_kernel, dim3((unsigned)(kP * kN / 1024), (unsigned)a.Hv, (unsigned)a.batch),
+                         dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)a.npieces * (unsigned)a.Hv * (unsigned)a.batch);
+    const bool hz = last && a.z != nullptr, hd = last && a.D != nullptr;
+    auto go = [&](auto accum_tag) {
+      constexpr bool ACC = decltype(accum_tag)::value;
+      if (hz && hd) hipLaunchKernelGGL((ssd_scan_kernel<true, true, ACC>), grid, dim3(kT), 0, stream, a);
+      else if (hz) hipLaunchKernelGGL((ssd_scan_kernel<true, false, ACC>), grid, dim3(kT), 0, stream, a);
+      else if (hd) hipLaunchKernelGGL((ssd_scan_kernel<false, true, ACC>), grid, dim3(kT), 0, stream, a);
+      else hipLaunchKernelGGL((ssd_scan_kernel<false, false, ACC>), grid, dim3(kT), 0, stream, a);
+    };
+    if (a.accumulate) go(std::true_type{});
+    else go(std::false_type{});
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mss

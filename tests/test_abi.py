@@ -209,17 +209,27 @@ def test_ssd_validation_errors():
     assert ssd_call(shape=(2, 0, 8, 64, 1, 128, 256)) == SHAPE
     assert ssd_call(io=9) == DTYPE
     assert ssd_call(io=FP32) == UNSUP
-    assert ssd_call(shape=(2, 1024, 8, 32, 1, 128, 256)) == UNSUP     # headdim
-    assert ssd_call(shape=(2, 1024, 8, 128, 1, 128, 256)) == UNSUP    # headdim 128 (64 only)
-    assert ssd_call(shape=(2, 1024, 8, 64, 1, 256, 256)) == UNSUP     # dstate 256 (128 only)
-    assert ssd_call(shape=(2, 1024, 8, 64, 1, 64, 256)) == UNSUP      # dstate
+    assert ssd_call(shape=(2, 1024, 8, 32, 1, 128, 256)) == UNSUP     # headdim 32
+    assert ssd_call(shape=(2, 1024, 8, 96, 1, 128, 256)) == UNSUP     # headdim 96
+    assert ssd_call(shape=(2, 1024, 8, 64, 1, 40, 256)) == UNSUP      # dstate not a multiple of 16
+    assert ssd_call(shape=(2, 1024, 8, 64, 1, 272, 256)) == UNSUP     # dstate above 256
+    lib = mss.lib()
+    for Pd, N in ((64, 16), (64, 48), (64, 64), (64, 128), (128, 128), (128, 64), (64, 192), (64, 256), (128, 256)):
+        assert lib.mss_ssd_workspace_size(2, 1024, 8, Pd, 1, N, 256, BF16) > 0, (Pd, N)
+    # headdim 128 runs as two 64-wide halves: twice the piece-state workspace.
+    assert lib.mss_ssd_workspace_size(2, 1024, 8, 128, 1, 128, 256, BF16) > \
+        lib.mss_ssd_workspace_size(2, 1024, 8, 64, 1, 128, 256, BF16)
     assert ssd_call(shape=(2, 1024, 8, 64, 1, 128, 100)) == UNSUP     # chunk
     assert ssd_call(shape=(2, 1024, 6, 64, 4, 128, 256)) == UNSUP     # nheads % ngroups
     # y's rows of one batch entry stay within 2^32 - 256 bytes: L*H*P <= 2^30 - 64.
-    ws = lambda L, H: mss.lib().mss_ssd_workspace_size(1, L, H, 64, 1, 128, 256, BF16)
+    ws = lambda L, H, Pd=64: mss.lib().mss_ssd_workspace_size(1, L, H, Pd, 1, 128, 256, BF16)
     assert ws((1 << 16) - 1, 256) > 0
     assert ws(1 << 16, 256) == 0
+    assert ws((1 << 15) - 1, 256, 128) > 0 and ws(1 << 15, 256, 128) == 0
     assert ws((1 << 24) - 1, 64) == 0 and ws(1 << 22, 64) == 0
+    # Grids: chunks x 64-row head slices x batch below 2^22.
+    assert mss.lib().mss_ssd_workspace_size(1024, 1024, 1024, 64, 1, 16, 64, BF16) == 0
+    assert mss.lib().mss_ssd_workspace_size(1024, 1024, 255, 64, 1, 16, 64, BF16) > 0
     assert ssd_call(flags=2) == UNSUP
     assert ssd_call(B=P(3, 4)) == ALIGN
     assert ssd_call(ws=None) == WS

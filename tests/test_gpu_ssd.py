@@ -16,12 +16,12 @@ from gpu_util import assert_close, dev, host64, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def gen(b, L, H, G, chunk, seed=3, with_d=False, with_z=False, with_h0=False):
-    cfg = I.small_ssd_config(b, L, H, 64, G, 128, chunk, seed=seed)
+def gen(b, L, H, G, chunk, seed=3, with_d=False, with_z=False, with_h0=False, P=64, N=128):
+    cfg = I.small_ssd_config(b, L, H, P, G, N, chunk, seed=seed)
     x = I.ssd_inputs(cfg, with_h0=with_h0)
     g = np.random.default_rng(seed + 1)
     x["D"] = g.standard_normal(H).astype(np.float32) if with_d else None
-    x["z"] = I.f32_to_bf16_bits(g.standard_normal((b, L, H, 64)).astype(np.float32)) if with_z else None
+    x["z"] = I.f32_to_bf16_bits(g.standard_normal((b, L, H, P)).astype(np.float32)) if with_z else None
     return cfg, x
 
 
@@ -61,6 +61,36 @@ CASES = [
 def test_ssd_small(case):
     b, L, H, G, Q, d, z, h0 = case
     cfg, x = gen(b, L, H, G, Q, with_d=d, with_z=z, with_h0=h0)
+    y, cs, hl = run_gpu(x, Q)
+    ry, rcs, rhl = run_oracle(x, Q)
+    e1 = assert_close(host64(y), ry, "bf16", "y")
+    e2 = assert_close(host64(cs), rcs, "bf16", "chunk_states")
+    e3 = assert_close(host64(hl), rhl, "bf16", "h_last")
+    print(f"{case}: y {e1:.2e} chunk_states {e2:.2e} h_last {e3:.2e}")
+    assert e1 < 5e-3 and e2 < 5e-3
+
+
+WIDE = [
+    # P, N, b, L, H, G, chunk, D, z, h0
+    (128, 128, 1, 300, 4, 2, 64, True, True, True),     # headdim 128: two 64-row halves per head
+    (128, 128, 2, 1000, 3, 1, 256, False, False, True),
+    (64, 64, 2, 517, 4, 2, 64, True, False, True),      # narrower states: columns past N stay zero
+    (64, 16, 1, 333, 4, 1, 256, False, True, True),
+    (64, 48, 2, 130, 6, 2, 128, True, True, False),
+    (128, 48, 1, 257, 2, 1, 64, True, False, True),
+    (64, 256, 1, 300, 4, 2, 128, True, True, True),     # two 128-state halves, y accumulated, then D and z
+    (64, 192, 2, 200, 2, 1, 64, False, True, True),
+    (128, 256, 1, 129, 2, 1, 256, True, False, True),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "p{}n{}b{}l{}h{}g{}q{}".format(*c[:7]))
+def test_ssd_headdim_and_dstate(case):
+    """headdim 64 or 128 and d_state any multiple of 16 up to 256 against the
+    oracle, every output element: ragged L, one and two groups, chunk 64 to
+    256, with and without D, z and h0."""
+    P, N, b, L, H, G, Q, d, z, h0 = case
+    cfg, x = gen(b, L, H, G, Q, seed=31, with_d=d, with_z=z, with_h0=h0, P=P, N=N)
     y, cs, hl = run_gpu(x, Q)
     ry, rcs, rhl = run_oracle(x, Q)
     e1 = assert_close(host64(y), ry, "bf16", "y")
@@ -138,18 +168,19 @@ def test_ssd_2p8b_workload_full():
 
 
 @pytest.mark.parametrize("case", [
-    # b, L, H, chunk, D, z, h0, heads checked (None: all)
-    (1, 5000, 80, 64, True, True, True, [0, 5, 41, 79]),   # 16 pieces of 5 chunks, ragged L
-    (2, 3000, 40, 128, False, False, True, [0, 13, 39]),   # 12 pieces of 2 chunks, ragged last chunk
-    (1, 16384, 2, 64, False, False, True, None),           # 64 pieces of 4 chunks
+    # b, L, H, chunk, D, z, h0, heads checked (None: all), headdim
+    (1, 5000, 80, 64, True, True, True, [0, 5, 41, 79], 64),   # 27 pieces of 3 chunks, ragged L
+    (2, 3000, 40, 128, False, False, True, [0, 13, 39], 64),   # 24 pieces of 1 chunk, ragged last chunk
+    (1, 16384, 2, 64, False, False, True, None, 64),           # 64 pieces of 4 chunks
+    (1, 4100, 40, 256, True, True, True, [0, 17, 39], 128),    # headdim 128 (80 half heads): 17 pieces
 ])
 def test_ssd_sequence_cut_into_pieces(case):
-    """With many heads the state pass cuts every sequence into pieces of
-    whole chunks that run from zero; the exact state entering each piece is
-    chained afterwards and added, decayed, to every chunk's entering state.
-    Checked where pieces hold several chunks and L is ragged."""
-    b, L, H, Q, d, z, h0, heads = case
-    cfg, x = gen(b, L, H, 1, Q, seed=21, with_d=d, with_z=z, with_h0=h0)
+    """With many heads the sequence is cut into pieces of whole chunks: the
+    state pass runs every piece from zero, the chain makes the exact state
+    entering each piece, and the output pass walks each piece's chunks from
+    it.  Checked where pieces hold several chunks and L is ragged."""
+    b, L, H, Q, d, z, h0, heads, P = case
+    cfg, x = gen(b, L, H, 1, Q, seed=21, with_d=d, with_z=z, with_h0=h0, P=P)
     y, cs, hl = run_gpu(x, Q)
     sel = slice(None) if heads is None else np.array(heads)
     ry, rcs, rhl = run_oracle(x, Q, None if heads is None else sel)
