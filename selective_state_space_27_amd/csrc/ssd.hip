@@ -210,26 +210,37 @@ __global__ void __launch_bounds__(256) ssd_cumsum_kernel(SSDArgs a) {
 }
 
 // B or C rows of group g for steps (l0 + j, l0 + j + 1), 8 states from
-// noff + ng*8: two 16-byte loads per unit, 2 units per thread.  Steps past L
-// and states past N read zero.
+// noff + ng*8: two 16-byte loads per unit, 2 units per thread.  The
+// descriptor starts at step l0, so each thread's offsets are fixed; steps past
+// L lie beyond it and read zero, and so do states past N.
 struct BCRegs {
   u32x4 r[2][2];
 };
-__device__ __forceinline__ void load_bc_rows(const SSDArgs& a, const uint16_t* src, int b, int g, int l0, BCRegs& o) {
-  const rsrc_t rs = make_rsrc(src + (size_t)b * a.L * a.G * a.N, (uint32_t)((size_t)a.L * a.G * a.N * 2));
+struct BCOffsets {
+  uint32_t o[2][2];
+};
+__device__ __forceinline__ BCOffsets bc_offsets(const SSDArgs& a, int g) {
+  BCOffsets r;
+  const uint32_t row = (uint32_t)(a.G * a.N * 2);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int u = threadIdx.x + kT * it;  // 512 units: 32 step pairs x 16 groups of 8 states
     const int ng = u & 15, j = 2 * (u >> 4);
     const bool nok = a.noff + ng * 8 < a.N;
+    const uint32_t col = (uint32_t)((g * a.N + a.noff + ng * 8) * 2);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int l = l0 + j + e;
-      const uint32_t off =
-          (l < a.L && nok) ? (uint32_t)((((size_t)l * a.G + g) * a.N + a.noff + ng * 8) * 2) : kOffNone;
-      o.r[it][e] = buf_load_u32x4(rs, off);
-    }
+    for (int e = 0; e < 2; ++e) r.o[it][e] = nok ? (uint32_t)(j + e) * row + col : kOffNone;
   }
+  return r;
+}
+__device__ __forceinline__ void load_bc_rows(const SSDArgs& a, const uint16_t* src, int b, int l0,
+                                             const BCOffsets& off, BCRegs& o) {
+  const uint32_t left = (uint32_t)max(a.L - l0, 0);
+  const rsrc_t rs = make_rsrc(src + ((size_t)b * a.L + l0) * a.G * a.N, left * (uint32_t)(a.G * a.N * 2));
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) o.r[it][e] = buf_load_u32x4(rs, off.o[it][e]);
 }
 // Row-major copy rm[step][N + pad] and/or time-contiguous copy tr (tsw layout, N rows).
 template <bool ROWMAJOR, bool TRANSPOSED>
@@ -320,7 +331,8 @@ __global__ void __launch_bounds__(kTS, 4) ssd_state_kernel(SSDArgs a) {
   const int b = blockIdx.y;
   const int piece = blockIdx.z;
   const int g = h / (a.H / a.G);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave id, uniform
   const int lc = lane & 31, hf = lane >> 5;
   const int nt = w & 3, kh = w >> 2;
   const size_t state_stride = (size_t)kP * kN;
@@ -641,7 +653,8 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   }
   const int h = head_of(a, vh);
   const int g = h / (a.H / a.G);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave id, uniform: branches on it are scalar
   const int lc = lane & 31, hf = lane >> 5;
   const int rt = w >> 1, pt = w & 1;
   const Dot2Masks dm = dot2_masks();
@@ -651,18 +664,19 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const int p = pt * 32 + lc;  // headdim row (within the virtual head) of this lane's output column
   const int nvalid = a.N - a.noff;  // state columns of this half that exist (the rest stay zero)
 
-  // x staging: thread -> (step pair j, 8 headdim values pg*8..).
+  // x staging: thread -> (step pair j, 8 headdim values pg*8..), through a
+  // descriptor starting at the block's first step (fixed per-thread offsets;
+  // steps past L read zero).
   const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
-  const rsrc_t rx = make_rsrc(a.x + (size_t)b * a.L * a.H * a.P, (uint32_t)((size_t)a.L * a.H * a.P * 2));
-  const size_t xcol = row_el(a, vh, pg * 8);
+  const uint32_t x_row = (uint32_t)(a.H * a.P * 2);
+  const uint32_t xo0 = (uint32_t)jx * x_row + (uint32_t)(row_el(a, vh, pg * 8) * 2);
   auto load_x = [&](int l0, u32x4* xr) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int l = l0 + jx + e;
-      const uint32_t off = (l < a.L) ? (uint32_t)(((size_t)l * a.H * a.P + xcol) * 2) : kOffNone;
-      xr[e] = buf_load_u32x4(rx, off);
-    }
+    const uint32_t left = (uint32_t)max(a.L - l0, 0);
+    const rsrc_t rx = make_rsrc(a.x + ((size_t)b * a.L + l0) * a.H * a.P, left * x_row);
+    xr[0] = buf_load_u32x4(rx, xo0);
+    xr[1] = buf_load_u32x4(rx, xo0 + x_row);
   };
+  const BCOffsets bco = bc_offsets(a, g);
   auto store_x = [&](const u32x4* xr) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -701,25 +715,29 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const uint32_t ybytes = (uint32_t)(((size_t)a.L * a.H * a.P - hoff) * 4);
   const rsrc_t ry = make_rsrc(a.y + bh_el, ybytes);
   const rsrc_t rz = make_rsrc(a.z ? a.z + bh_el : nullptr, a.z ? ybytes / 2 : 0u);
+  // Row r of this lane's accumulator tile is step lprev + rt*32 + 4*hf +
+  // 8*(r>>2) + (r&3): a per-lane base plus a compile-time multiple of the row.
   auto finish = [&]() {
     if (lprev < 0) return;
+    const int l_lane = lprev + rt * 32 + 4 * hf;
+    const uint32_t o_lane = (uint32_t)l_lane * row + (uint32_t)p;
     float zv[16], yv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int l = lprev + rt * 32 + acc_row(r, lane);
-      const bool in = l < lend;
-      if constexpr (HAS_Z) zv[r] = bf16_to_f32(buf_load_u16(rz, in ? ((uint32_t)l * row + (uint32_t)p) * 2u : kOffNone));
-      if constexpr (ACCUM)
-        yv[r] = __uint_as_float(buf_load_u32(ry, in ? ((uint32_t)l * row + (uint32_t)p) * 4u : kOffNone));
+      const int dr = 8 * (r >> 2) + (r & 3);
+      const bool in = l_lane + dr < lend;
+      const uint32_t o = o_lane + (uint32_t)dr * row;
+      if constexpr (HAS_Z) zv[r] = bf16_to_f32(buf_load_u16(rz, in ? o * 2u : kOffNone));
+      if constexpr (ACCUM) yv[r] = __uint_as_float(buf_load_u32(ry, in ? o * 4u : kOffNone));
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int l = lprev + rt * 32 + acc_row(r, lane);
+      const int dr = 8 * (r >> 2) + (r & 3);
       float v = xbuf[partner][r][lane] + yprev[r];
       if constexpr (ACCUM) v += yv[r];
       if constexpr (HAS_D) v = __builtin_fmaf(dh, xprev[r], v);
       if constexpr (HAS_Z) v *= silu(zv[r]);
-      const uint32_t yo = (l < lend) ? ((uint32_t)l * row + (uint32_t)p) * 4u : kOffNone;
+      const uint32_t yo = (l_lane + dr < lend) ? (o_lane + (uint32_t)dr * row) * 4u : kOffNone;
       buf_store_u32(ry, yo, __float_as_uint(v));
     }
   };
@@ -737,8 +755,8 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   BCRegs br, cr;
   float d, ls;
   load_x(lbeg, xr);
-  load_bc_rows(a, a.B, b, g, lbeg, br);
-  load_bc_rows(a, a.C, b, g, lbeg, cr);
+  load_bc_rows(a, a.B, b, lbeg, bco, br);
+  load_bc_rows(a, a.C, b, lbeg, bco, cr);
   load_dls(lbeg, d, ls);  // every wave loads them (no branch around loads); wave 0 uses them
   for (int l0 = lbeg; l0 < lend; l0 += kSub) {
     finish();  // the previous block (its xbuf entries were written before the last barrier)
@@ -786,11 +804,17 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       slice(std::integral_constant<int, 1>{});
     }
 
-    // exp(s_i) on both row tiles' C S^T parts, then the masked decay block.
+    // exp(s_i) on both row tiles' C S^T parts (registers 4k..4k+3 hold four
+    // consecutive rows: one 16-byte read each), then the masked decay block.
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      yown[r] *= s_e[rt * 32 + acc_row(r, lane)];
-      yoth[r] *= s_e[(1 - rt) * 32 + acc_row(r, lane)];
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 eo = *reinterpret_cast<const f32x4*>(&s_e[rt * 32 + 8 * k + 4 * hf]);
+      const f32x4 et = *reinterpret_cast<const f32x4*>(&s_e[(1 - rt) * 32 + 8 * k + 4 * hf]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        yown[4 * k + q] *= eo[q];
+        yoth[4 * k + q] *= et[q];
+      }
     }
     auto diag = [&](auto factored_tag) {
       constexpr bool F = decltype(factored_tag)::value;
@@ -812,8 +836,8 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     // registers are done (the block after the piece's last is read and
     // ignored; past L reads zero).
     load_x(l0 + kSub, xr);
-    load_bc_rows(a, a.B, b, g, l0 + kSub, br);
-    load_bc_rows(a, a.C, b, g, l0 + kSub, cr);
+    load_bc_rows(a, a.B, b, l0 + kSub, bco, br);
+    load_bc_rows(a, a.C, b, l0 + kSub, bco, cr);
     yprev = yown;
     if constexpr (HAS_D) {
 #pragma unroll
