@@ -18,7 +18,11 @@ SSD equals the Mamba-1 scan with scalar-per-head A and its matrix form, special
 cases of D and the gate, linearity, causality; the scan prologue against a
 library convolution and softplus's closed forms).
 The backward is pinned by central finite differences of the forward, a
-different computation.
+different computation.  The Mamba-3 step is pinned by its reduction to the
+SSD recurrence (rank 1, real, Euler input), MIMO superposition over SSD runs,
+the closed form of a rotating decaying state, the trapezoid rule's second-order
+convergence on an ODE with a known solution, and the closed-form fixed point of
+a constant input (real and complex).
 """
 from __future__ import annotations
 
@@ -58,6 +62,8 @@ def _load():
         lib.oracle_selective_scan_bwd.restype = None
         lib.oracle_scan_prologue.argtypes = [_dp] * 7 + [L, L, L, ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_prologue.restype = None
+        lib.oracle_mamba3_step.argtypes = [_dp] * 12 + [L] * 6 + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_mamba3_step.restype = None
         _lib = lib
     return _lib
 
@@ -213,3 +219,39 @@ def ssd(x, delta, A, B, C, D=None, z=None, h0=None, chunk=None, threads=None):
                        _ptr(y), _ptr(cs), _ptr(h_last), b, L, H, P, G, N, q,
                        threads or default_threads())
     return y, cs, h_last
+
+
+def mamba3_step(h, x, delta, A, B, C, D=None, z=None, x_prev=None, B_prev=None, theta=None, complex_state=False,
+                threads=None):
+    """One Mamba-3 generation step in fp64 (see ``oracle_mamba3_step`` in
+    mss_oracle.c for the passages and the readings).  h: [b, H, P, N], or
+    [b, H, P, N, 2] (re, im) when ``complex_state`` (not modified; a new array
+    is returned); x, z, x_prev: [b, H, R, P]; B, C, B_prev: [b, G, R, N];
+    delta: [b, H]; A, D: [H]; theta: [H, N].  x_prev and B_prev given = the
+    trapezoid input rule.  Returns (h_new, y [b, H, R, P])."""
+    h = np.array(h, dtype=np.float64, order="C", copy=True)
+    x = _f64(x)
+    b, H, R, P = x.shape
+    N = np.shape(B)[3]
+    G = np.shape(B)[1]
+    if complex_state:
+        if h.shape != (b, H, P, N, 2) or theta is None:
+            raise ValueError("complex state: h is [b, H, P, N, 2] and theta [H, N] is required")
+    elif h.shape != (b, H, P, N):
+        raise ValueError("h must be [b, H, P, N]")
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev go together (the trapezoid rule)")
+    delta = _f64(delta, (b, H))
+    A = _f64(A, (H,))
+    B = _f64(B, (b, G, R, N))
+    C = _f64(C, (b, G, R, N))
+    D = _f64(D, (H,))
+    z = _f64(z, (b, H, R, P))
+    x_prev = _f64(x_prev, (b, H, R, P))
+    B_prev = _f64(B_prev, (b, G, R, N))
+    theta = _f64(theta, (H, N)) if complex_state else None
+    y = np.empty((b, H, R, P), dtype=np.float64)
+    _load().oracle_mamba3_step(_ptr(h), _ptr(x), _ptr(x_prev), _ptr(delta), _ptr(A), _ptr(theta), _ptr(B),
+                               _ptr(B_prev), _ptr(C), _ptr(D), _ptr(z), _ptr(y), b, H, P, G, N, R,
+                               int(bool(complex_state)), threads or default_threads())
+    return h, y

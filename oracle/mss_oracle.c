@@ -402,3 +402,122 @@ void oracle_scan_prologue(const double* x, const double* conv_w, const double* c
     }
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Mamba-3 state update (one generation step), with its three changes to    */
+/* the recurrence as options.                                                */
+/*                                                                           */
+/* Source: "Mamba-1/2/3 visual guide" (blog.yecov.com), section 4: Mamba-3  */
+/* updates the state with an exponential-trapezoidal discretisation (an     */
+/* exponential transition and an input approximation that uses both ends of */
+/* the step), a complex-valued state that decays while it rotates, and MIMO */
+/* (several inputs and outputs per state update, as a small matrix product */
+/* that raises decode's arithmetic intensity); the section 4 table keeps    */
+/* the Mamba-2 head structure (scalar decay per head, heads of a group      */
+/* sharing B and C).  The page gives no formulas; the readings taken:       */
+/*  - trapezoid: the input integral over the step,                           */
+/*    int_0^delta exp(A (delta - s)) b(s) ds with b = B x, by the trapezoid  */
+/*    rule: (delta/2) (alpha b_prev + b_cur), alpha the step's transition;   */
+/*    without it the Euler-style term delta * b_cur of the other calls.      */
+/*  - complex state: per head and state n the transition is                  */
+/*    alpha_n = exp(delta A_h) (cos(delta theta_n) + i sin(delta theta_n)),  */
+/*    the rotation angle growing with delta (data dependent); B, C, x are   */
+/*    real; the readout takes the real part of C . h.                       */
+/*  - MIMO rank R: per head, R input vectors x_r (headdim P) and R pairs of  */
+/*    B_r, C_r (dstate N): H <- alpha H + w sum_r x_r B_r^T and R outputs    */
+/*    y_r = Re(H) C_r (+ D x_r, times silu(z_r)); R = 1 is the SISO update. */
+/* Per (b, head h), g = h / (H/G), state row p and state n:                 */
+/*   alpha = exp(delta A_h) [* (cos, sin)(delta theta[h, n])]                */
+/*   u_cur = sum_r x[b,h,r,p] B[b,g,r,n];  u_prev likewise from x_prev, B_prev */
+/*   h[p,n] <- alpha h[p,n] + (delta/2)(alpha u_prev + u_cur)   (trapezoid)  */
+/*   h[p,n] <- alpha h[p,n] + delta u_cur                       (otherwise)  */
+/*   y[b,h,r,p] = (sum_n C[b,g,r,n] Re h[p,n] + D_h x[b,h,r,p]) * silu(z)    */
+/* Layouts: h [batch, nheads, headdim, dstate] (x2 re/im last when complex); */
+/* x, x_prev, z, y [batch, nheads, rank, headdim]; B, C, B_prev [batch,      */
+/* ngroups, rank, dstate]; delta [batch, nheads]; A, D [nheads]; theta       */
+/* [nheads, dstate].  x_prev and B_prev NULL = no trapezoid.                  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  double* h;
+  const double *x, *x_prev, *delta, *A, *theta, *B, *B_prev, *C, *D, *z;
+  double* y;
+  long batch, nheads, headdim, ngroups, dstate, rank;
+  int complex_state;
+  long unit_begin, unit_end;
+} m3_job;
+
+static void m3_unit(const m3_job* j, long b, long hd) {
+  const long H = j->nheads, P = j->headdim, G = j->ngroups, N = j->dstate, R = j->rank;
+  const long g = hd / (H / G);
+  const double dlt = j->delta[b * H + hd];
+  const double a = exp(dlt * j->A[hd]);
+  const int trap = j->x_prev != NULL;
+  const double* xs = j->x + (b * H + hd) * R * P;
+  const double* xp = trap ? j->x_prev + (b * H + hd) * R * P : NULL;
+  const double* Bs = j->B + (b * G + g) * R * N;
+  const double* Bp = trap ? j->B_prev + (b * G + g) * R * N : NULL;
+  const double* Cs = j->C + (b * G + g) * R * N;
+  const long stride = j->complex_state ? 2 : 1;
+  double* hs = j->h + (b * H + hd) * P * N * stride;
+  for (long p = 0; p < P; ++p) {
+    for (long n = 0; n < N; ++n) {
+      double ucur = 0.0, uprev = 0.0;
+      for (long r = 0; r < R; ++r) {
+        ucur += xs[r * P + p] * Bs[r * N + n];
+        if (trap) uprev += xp[r * P + p] * Bp[r * N + n];
+      }
+      double ar = a, ai = 0.0; /* the transition alpha = ar + i ai */
+      if (j->complex_state) {
+        const double ang = dlt * j->theta[hd * N + n];
+        ar = a * cos(ang);
+        ai = a * sin(ang);
+      }
+      double* e = hs + (p * N + n) * stride;
+      const double re = e[0], im = j->complex_state ? e[1] : 0.0;
+      double nre = ar * re - ai * im, nim = ar * im + ai * re; /* alpha * h */
+      if (trap) {
+        nre += 0.5 * dlt * (ar * uprev + ucur);
+        nim += 0.5 * dlt * (ai * uprev);
+      } else {
+        nre += dlt * ucur;
+      }
+      e[0] = nre;
+      if (j->complex_state) e[1] = nim;
+    }
+  }
+  for (long r = 0; r < R; ++r) {
+    for (long p = 0; p < P; ++p) {
+      double acc = 0.0;
+      for (long n = 0; n < N; ++n) acc += Cs[r * N + n] * hs[(p * N + n) * stride];
+      double out = acc + (j->D ? j->D[hd] : 0.0) * xs[r * P + p];
+      const long o = ((b * H + hd) * R + r) * P + p;
+      j->y[o] = j->z ? out * silu(j->z[o]) : out;
+    }
+  }
+}
+
+static void* m3_worker(void* arg) {
+  const m3_job* j = (const m3_job*)arg;
+  for (long k = j->unit_begin; k < j->unit_end; ++k) m3_unit(j, k / j->nheads, k % j->nheads);
+  return NULL;
+}
+
+void oracle_mamba3_step(double* h, const double* x, const double* x_prev, const double* delta, const double* A,
+                        const double* theta, const double* B, const double* B_prev, const double* C, const double* D,
+                        const double* z, double* y, long batch, long nheads, long headdim, long ngroups,
+                        long dstate, long rank, int complex_state, int nthreads) {
+  long units = batch * nheads;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  m3_job* jobs = (m3_job*)calloc((size_t)nthreads, sizeof(m3_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    m3_job j = {h, x, x_prev, delta, A, theta, B, B_prev, C, D, z, y, batch, nheads, headdim, ngroups, dstate,
+                rank, complex_state, units * i / nthreads, units * (i + 1) / nthreads};
+    jobs[i] = j;
+    pthread_create(&th[i], NULL, m3_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+}

@@ -525,3 +525,133 @@ def test_fused_scan_equals_scan_of_prologue_by_library_routes():
     y, h = oracle.selective_scan_fused(x, w, cb, dr, db, A, B, C, D, z, h0, conv_silu=True, softplus=True)
     np.testing.assert_allclose(y, y_ref, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(h, h_ref, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- Mamba-3 ---
+# The Mamba-3 step ("Mamba-1/2/3 visual guide", section 4) is pinned by
+# reductions to the SSD oracle (itself pinned above), closed forms and the
+# trapezoid rule's convergence order, never by its own formula retyped.
+
+def _m3_inputs(b, H, P, N, R, G=1, seed=0):
+    g = np.random.default_rng(seed)
+    return dict(x=g.standard_normal((b, H, R, P)), B=g.standard_normal((b, G, R, N)),
+                C=g.standard_normal((b, G, R, N)), delta=0.01 + 0.2 * g.random((b, H)),
+                A=-np.exp(g.uniform(0, np.log(16), H)), D=g.standard_normal(H), z=g.standard_normal((b, H, R, P)))
+
+
+def test_mamba3_rank1_real_euler_is_the_ssd_recurrence():
+    """Rank 1, real state, Euler input: L steps equal the SSD layer over L."""
+    b, H, P, N, G, L = 2, 4, 5, 6, 2, 9
+    g = np.random.default_rng(3)
+    x = g.standard_normal((b, L, H, P))
+    Bv, Cv = g.standard_normal((b, L, G, N)), g.standard_normal((b, L, G, N))
+    dl = 0.01 + 0.3 * g.random((b, L, H))
+    A, D, z = -np.exp(g.uniform(0, 2, H)), g.standard_normal(H), g.standard_normal((b, L, H, P))
+    h0 = 0.1 * g.standard_normal((b, H, P, N))
+    ry, _, rh = oracle.ssd(x, dl, A, Bv, Cv, D, z, h0)
+    h = h0.copy()
+    for t in range(L):
+        h, y = oracle.mamba3_step(h, x[:, t, :, None, :], dl[:, t], A, Bv[:, t, :, None, :], Cv[:, t, :, None, :], D,
+                                  z[:, t, :, None, :])
+        np.testing.assert_allclose(y[:, :, 0], ry[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(h, rh, rtol=1e-12, atol=1e-12)
+
+
+def test_mamba3_mimo_is_superposition_of_ssd_runs():
+    """Rank R: the state is the sum of R SISO (SSD) states driven by (x_r,
+    B_r), and output r reads that sum with C_r, i.e. sum_r' SSD(x_r', B_r',
+    C_r) (state linear in the inputs), over several steps."""
+    b, H, P, N, R, L = 1, 3, 4, 5, 3, 6
+    g = np.random.default_rng(4)
+    x = g.standard_normal((b, L, H, R, P))
+    Bv, Cv = g.standard_normal((b, L, 1, R, N)), g.standard_normal((b, L, 1, R, N))
+    dl, A = 0.05 + 0.2 * g.random((b, L, H)), -np.exp(g.uniform(0, 2, H))
+    h = np.zeros((b, H, P, N))
+    ys = []
+    for t in range(L):
+        h, y = oracle.mamba3_step(h, x[:, t], dl[:, t], A, Bv[:, t], Cv[:, t])
+        ys.append(y)
+    ys = np.stack(ys, axis=1)  # [b, L, H, R, P]
+    state = np.zeros((b, H, P, N))
+    for r in range(R):
+        yr = np.zeros((b, L, H, P))
+        for r2 in range(R):
+            yy, _, hl = oracle.ssd(x[:, :, :, r2], dl, A, Bv[:, :, :, r2], Cv[:, :, :, r])
+            yr += yy
+            if r == 0:
+                state += hl
+        np.testing.assert_allclose(ys[:, :, :, r], yr, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(h, state, rtol=1e-11, atol=1e-12)
+
+
+def test_mamba3_complex_state_rotates_and_decays_in_closed_form():
+    """No input (B = 0): each complex state is multiplied by
+    exp(A sum delta) e^{i theta sum delta}; its modulus decays exactly as the
+    real decay, and theta = 0 leaves a real state real."""
+    b, H, P, N, L = 1, 2, 3, 4, 7
+    g = np.random.default_rng(5)
+    h0 = g.standard_normal((b, H, P, N, 2))
+    theta = g.uniform(-3, 3, (H, N))
+    A = -np.exp(g.uniform(0, 1, H))
+    dls = 0.05 + 0.3 * g.random((L, b, H))
+    h = h0.copy()
+    x = g.standard_normal((b, H, 1, P))
+    Bz, C = np.zeros((b, 1, 1, N)), g.standard_normal((b, 1, 1, N))
+    for t in range(L):
+        h, _ = oracle.mamba3_step(h, x, dls[t], A, Bz, C, theta=theta, complex_state=True)
+    sd = dls.sum(axis=0)[0]                                   # [H]
+    z0 = h0[..., 0] + 1j * h0[..., 1]
+    want = z0 * (np.exp(A * sd)[None, :, None, None] * np.exp(1j * theta[None, :, None, :] * sd[None, :, None, None]))
+    np.testing.assert_allclose(h[..., 0] + 1j * h[..., 1], want, rtol=1e-12, atol=1e-14)
+    # theta = 0: the imaginary part of a real start stays exactly zero
+    hr = np.concatenate([h0[..., :1], np.zeros_like(h0[..., :1])], axis=-1)
+    for t in range(L):
+        hr, _ = oracle.mamba3_step(hr, x, dls[t], A, g.standard_normal((b, 1, 1, N)), C, theta=0 * theta,
+                                   complex_state=True)
+    assert np.all(hr[..., 1] == 0.0)
+
+
+@pytest.mark.parametrize("trapezoid", [True, False])
+def test_mamba3_trapezoid_is_second_order(trapezoid):
+    """dh/dt = A h + sin(w t), h(0) = 0, has the closed form
+    h(T) = (w e^{AT} - A sin(wT) - w cos(wT)) / (A^2 + w^2).  Stepping it
+    with the exponential-trapezoidal update (input at both ends of each step)
+    halves the step and quarters the error (second order); the Euler-style
+    input term only halves it (first order)."""
+    A, w, T = -1.3, 2.0, 2.0
+    exact = (w * np.exp(A * T) - A * np.sin(w * T) - w * np.cos(w * T)) / (A * A + w * w)
+    errs = []
+    for K in (100, 200, 400):
+        dlt = T / K
+        h = np.zeros((1, 1, 1, 1))
+        one = np.ones((1, 1, 1, 1))
+        for k in range(1, K + 1):
+            xc = np.full((1, 1, 1, 1), np.sin(w * k * dlt))
+            xp = np.full((1, 1, 1, 1), np.sin(w * (k - 1) * dlt)) if trapezoid else None
+            h, _ = oracle.mamba3_step(h, xc, np.full((1, 1), dlt), np.array([A]), one, one, x_prev=xp,
+                                      B_prev=one if trapezoid else None)
+        errs.append(abs(h[0, 0, 0, 0] - exact))
+    r1, r2 = errs[0] / errs[1], errs[1] / errs[2]
+    if trapezoid:
+        assert 3.8 < r1 < 4.2 and 3.8 < r2 < 4.2, errs
+    else:
+        assert 1.8 < r1 < 2.2 and 1.8 < r2 < 2.2, errs
+
+
+@pytest.mark.parametrize("complex_state", [False, True])
+def test_mamba3_trapezoid_fixed_point(complex_state):
+    """A constant input u (x_prev = x, B_prev = B) drives the trapezoid
+    recurrence h <- alpha h + (delta/2)(alpha + 1) u to its fixed point
+    h* = (delta/2)(1 + alpha) u / (1 - alpha), alpha complex with rotation."""
+    A, dlt, th = -0.7, 0.4, 1.1
+    u = 0.8
+    alpha = np.exp(dlt * A) * (np.exp(1j * dlt * th) if complex_state else 1.0)
+    want = 0.5 * dlt * (1 + alpha) * u / (1 - alpha)
+    one = np.ones((1, 1, 1, 1))
+    x = np.full((1, 1, 1, 1), u)
+    h = np.zeros((1, 1, 1, 1, 2)) if complex_state else np.zeros((1, 1, 1, 1))
+    for _ in range(400):
+        h, _ = oracle.mamba3_step(h, x, np.full((1, 1), dlt), np.array([A]), one, one, x_prev=x, B_prev=one,
+                                  theta=np.array([[th]]), complex_state=complex_state)
+    got = h[..., 0] + 1j * h[..., 1] if complex_state else h
+    np.testing.assert_allclose(np.ravel(got)[0], want, rtol=1e-12)
