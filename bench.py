@@ -23,6 +23,9 @@ Other workloads (measured for the record, not the headline):
                headline scan, one mss_selective_scan_bwd call per step
   scan_2p8b_fused  the headline scan fed by its prologue (u from the silu of
                the causal 4-tap convolution of x, delta = softplus(raw + bias))
+  decode_m3    Mamba-3 generation: b128 x 80 heads x P64 x N128, MIMO rank 4,
+               complex (rotating) fp32 state, trapezoid input, bf16 I/O; one
+               step = 100 consecutive tokens
   copy         a plain 1 GiB device copy (calibrates the HBM byte counters)
 
 --seqlen L and --batch B (scan and SSD workloads) time the same workload at
@@ -61,7 +64,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scan_2p8b",
                     choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "scan_m2shape", "scan_2p8b_bwd",
-                             "scan_2p8b_fused", "copy"])
+                             "scan_2p8b_fused", "decode_m3", "copy"])
     ap.add_argument("--seqlen", type=int, default=0,
                     help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
     ap.add_argument("--batch", type=int, default=0,
@@ -98,6 +101,16 @@ def scan_bwd_bytes(b, d, n, L, es):
 def decode_step_bytes(b, d, n, es):
     """Per token step: state read + written (fp32), u/delta/z/y, B/C, A, D."""
     return 2 * b * d * n * 4 + 4 * b * d * es + 2 * b * n * es + d * n * 4 + d * 4
+
+
+def mamba3_step_bytes(cfg, es):
+    """Per token step: the state read and written (fp32, re and im when
+    complex); x, z, y and x_prev [b,H,R,P]; B, C and B_prev [b,G,R,N]; delta
+    [b,H]; A, D [H] and theta [H,N] fp32."""
+    b, H, P, G, N, R = cfg.batch, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.rank
+    state = b * H * P * N * 4 * (2 if cfg.complex_state else 1)
+    return (2 * state + (4 if cfg.trapezoid else 3) * b * H * R * P * es + (3 if cfg.trapezoid else 2) * b * G * R * N * es
+            + b * H * 4 + 2 * H * 4 + (H * N * 4 if cfg.complex_state else 0))
 
 
 def ssd_bytes(b, L, H, P, G, N, es):
@@ -404,6 +417,53 @@ def bench_decode(args, torch, mss, I):
     return res, nbytes, ms / cfg.steps, "state_update_kernel", ["state_update.hip", "common.hpp"], cpu
 
 
+def bench_decode_m3(args, torch, mss, I):
+    cfg = I.DECODE_M3
+    st = I.mamba3_static(cfg)
+    pool = [I.mamba3_step_inputs(cfg, s, st["dt"]) for s in range(I.DECODE_POOL)]
+    dpool = [{k: to_dev(torch, p[k]) for k in ("x", "B", "C", "z", "delta")} for p in pool]
+    h = to_dev(torch, st["h0"])
+    A, D, th = to_dev(torch, st["A"]), to_dev(torch, st["D"]), to_dev(torch, st["theta"])
+    y = torch.empty_like(dpool[0]["x"])
+
+    def step():  # consecutive generation steps; x_prev, B_prev are the previous step's
+        for s in range(cfg.steps):
+            p, q = dpool[s % I.DECODE_POOL], dpool[(s - 1) % I.DECODE_POOL]
+            mss.mamba3_state_update(h, p["x"], p["delta"], A, p["B"], p["C"], D, p["z"], x_prev=q["x"], B_prev=q["B"],
+                                    theta=th, out=y)
+
+    steps = max(1, args.steps // 10)
+    ms = time_region(torch, step, steps, max(1, args.warmup // 5))
+    b, H, P, N, R = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.rank
+    updates = b * H * P * N * cfg.steps
+    res = {"metric": "state updates/s (B*H*P*N per token step), Mamba-3 generation", "value": updates / (ms * 1e-3),
+           "unit": "state updates/s", "ms_per_step": ms, "dtype": "f32",
+           "config": {"workload": f"{cfg.name}: Mamba-3 state update b={b} heads={H} headdim={P} d_state={N} "
+                                  f"MIMO rank {R}, complex state, trapezoid input, {cfg.steps} consecutive tokens, "
+                                  "bf16 x/B/C/z/y, fp32 state in place", "batch": b, "nheads": H, "headdim": P,
+                      "d_state": N, "rank": R, "tokens_per_step": cfg.steps}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th_n, info = host_cpus()
+        p64 = [{k: I.to_f64(p[k], "bf16") for k in ("x", "B", "C", "z")} | {"delta": p["delta"]} for p in pool]
+        state = {"h": st["h0"].astype(np.float64), "s": 0}
+        b1 = max(1, b // 32)
+
+        def token_step(nb, t):
+            p, q = p64[state["s"] % I.DECODE_POOL], p64[(state["s"] - 1) % I.DECODE_POOL]
+            hn, _ = oracle.mamba3_step(state["h"][:nb], p["x"][:nb], p["delta"][:nb], st["A"], p["B"][:nb],
+                                       p["C"][:nb], st["D"], p["z"][:nb], x_prev=q["x"][:nb], B_prev=q["B"][:nb],
+                                       theta=st["theta"], complex_state=True, threads=t)
+            state["h"][:nb] = hn
+            state["s"] += 1
+
+        cpu = cpu_leg(lambda: token_step(b, th_n), b * H * P * N, lambda: token_step(b1, 1), b1 * H * P * N,
+                      "state updates/s", th_n, info, f"all {b} batch rows, consecutive token steps",
+                      f"batch rows 0..{b1 - 1}, consecutive token steps")
+    return res, mamba3_step_bytes(cfg, 2), ms / cfg.steps, "mamba3_step_kernel", ["mamba3.hip", "common.hpp"], cpu
+
+
 def bench_ssd(args, torch, mss, I):
     cfg = I.SSD_2P8B
     x = I.ssd_inputs(cfg)
@@ -495,6 +555,8 @@ def main():
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan_bwd(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
     elif args.workload == "scan_2p8b_fused":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan_fused(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
+    elif args.workload == "decode_m3":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_decode_m3(args, torch, mss, I)
     else:
         res, nbytes, launch_ms, kernel, files, cpu = bench_copy(args, torch)
 

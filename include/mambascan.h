@@ -242,6 +242,49 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
                             uint32_t flags, void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* Mamba-3 state update (one generation step).                               */
+/*                                                                          */
+/* "Mamba-1/2/3 visual guide", section 4, gives Mamba-3's recurrence three   */
+/* changes over Mamba-2's: an exponential-trapezoidal discretisation (the   */
+/* step's input taken at both its ends, with an exponential transition), a  */
+/* complex state that decays while it rotates, and MIMO (several inputs and */
+/* outputs per state update as a small matrix product, raising the work per */
+/* byte of the state that decode streams).  The page gives no formulas; the */
+/* readings implemented (each an option):                                    */
+/*   alpha = exp(delta A_h), times e^{i delta theta[h,n]} with               */
+/*           MSS_FLAG_COMPLEX_STATE (the rotation angle grows with delta);   */
+/*   u = sum_r x[b,h,r,p] B[b,g,r,n],  u' likewise from x_prev and B_prev    */
+/*   h[p,n] <- alpha h[p,n] + (delta/2)(alpha u' + u)  (x_prev, B_prev given: */
+/*           the trapezoid rule on the step's input integral)                */
+/*   h[p,n] <- alpha h[p,n] + delta u                  (otherwise)           */
+/*   y[b,h,r,p] = (sum_n C[b,g,r,n] Re h[p,n] + D_h x[b,h,r,p]) * silu(z)    */
+/* per batch b, head h (group g = h / (nheads/ngroups)), state row p and     */
+/* state n; R = rank inputs and outputs per head (R = 1: the SISO update of  */
+/* the Mamba-2 head).  For a sequence of steps, x_prev and B_prev are the    */
+/* previous step's x and B (zero before the first step).                     */
+/*                                                                          */
+/* Layouts: h [batch, nheads, headdim, dstate] fp32, in place, or with       */
+/*   MSS_FLAG_COMPLEX_STATE [batch, nheads, headdim, dstate, 2] (re, im);    */
+/*   x, x_prev, z, y [batch, nheads, rank, headdim] io_dtype;                */
+/*   B, B_prev, C [batch, ngroups, rank, dstate] io_dtype; delta [batch,     */
+/*   nheads] fp32; A, D [nheads] fp32; theta [nheads, dstate] fp32.          */
+/* x_prev and B_prev are both given or both NULL; theta is required with    */
+/* MSS_FLAG_COMPLEX_STATE (else ignored); D and z may be NULL.               */
+/* Supported: headdim a multiple of 16 up to 4096, dstate 64, 128 or 256,    */
+/* rank 1..8, nheads % ngroups == 0 (else MSS_ERR_UNSUPPORTED); batch and    */
+/* nheads at most 65535 and batch*nheads*headdim at most 2^28 (else          */
+/* MSS_ERR_SHAPE).  h, delta, A, theta and D 16-byte aligned.  y and h must  */
+/* not overlap any input or each other.                                      */
+/* ------------------------------------------------------------------------ */
+#define MSS_FLAG_COMPLEX_STATE 0x10u
+mss_status mss_mamba3_state_update(float* h, const void* x, const void* x_prev, const float* delta,
+                                   const float* A, const float* theta, const void* B,
+                                   const void* B_prev, const void* C, const float* D, const void* z,
+                                   void* y, int64_t batch, int64_t nheads, int64_t headdim,
+                                   int64_t ngroups, int64_t dstate, int64_t rank, mss_dtype io_dtype,
+                                   uint32_t flags, void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Mamba-2 SSD layer, chunked.                                               */
 /*                                                                          */
 /* The same recurrence with A restricted to a scalar per head ("Mamba-1/2/3 */

@@ -15,6 +15,8 @@ Operations (see the header for the exact definitions and layouts):
                       convolution for u, delta from its raw value) in one pass
   selective_scan_bwd  its gradient
   state_update        one recurrent generation step, state updated in place
+  mamba3_state_update one Mamba-3 generation step (trapezoid input, complex
+                      state, MIMO rank R as options), state updated in place
   ssd_chunk_fwd       Mamba-2 SSD layer, chunked, dense products on MFMA
 """
 from __future__ import annotations
@@ -33,6 +35,7 @@ MSS_BF16 = 1
 MSS_FLAG_DECAY_GENERAL = 0x1
 MSS_FLAG_CONV_SILU = 0x2
 MSS_FLAG_DELTA_SOFTPLUS = 0x4
+MSS_FLAG_COMPLEX_STATE = 0x10
 
 STATUS_NAMES = {0: "MSS_OK", 1: "MSS_ERR_NULL", 2: "MSS_ERR_SHAPE", 3: "MSS_ERR_DTYPE", 4: "MSS_ERR_ALIGN",
                 5: "MSS_ERR_UNSUPPORTED", 6: "MSS_ERR_WORKSPACE", 7: "MSS_ERR_ALIAS", 8: "MSS_ERR_HIP",
@@ -44,6 +47,7 @@ EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_noalloc", "mss_sele
            "mss_selective_scan_fwd_fused",
            "mss_selective_scan_bwd",
            "mss_selective_scan_bwd_workspace_size", "mss_state_update",
+           "mss_mamba3_state_update",
            "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_workspace_status", "mss_status_string",
            "mss_last_hip_error", "mss_abi_version")
 
@@ -89,6 +93,9 @@ def lib() -> ctypes.CDLL:
     L.mss_selective_scan_bwd_workspace_size.restype = sz
     L.mss_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ctypes.c_int, u32, vp]
     L.mss_state_update.restype = ctypes.c_int
+    L.mss_mamba3_state_update.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, vp, fp, vp, vp, i64, i64, i64, i64, i64,
+                                          i64, ctypes.c_int, u32, vp]
+    L.mss_mamba3_state_update.restype = ctypes.c_int
     L.mss_ssd_chunk_fwd.argtypes = [vp, fp, fp, vp, vp, fp, vp, fp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_int, u32, vp, sz, vp]
     L.mss_ssd_chunk_fwd.restype = ctypes.c_int
@@ -390,6 +397,45 @@ def state_update(h, u, delta, A, B, C, D=None, z=None, *, out=None, stream=None)
     st = lib().mss_state_update(_ptr(h), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                 _ptr(out), b, d, N, _io_code(io), 0, _stream(stream))
     _raise(st, "mss_state_update")
+    return out
+
+
+# --------------------------------------------------------- Mamba-3 update
+def mamba3_state_update(h, x, delta, A, B, C, D=None, z=None, *, x_prev=None, B_prev=None, theta=None, out=None,
+                        stream=None):
+    """One Mamba-3 generation step; ``h`` is updated in place.
+
+    h: [b, H, P, N] float32, or [b, H, P, N, 2] (re, im) for the complex
+    state, which needs theta [H, N] float32; x, z, x_prev: [b, H, R, P] and
+    B, C, B_prev: [b, G, R, N] (float32 or bfloat16, all the same); delta:
+    [b, H]; A, D: [H] float32.  x_prev and B_prev (the previous step's x and
+    B) select the trapezoid input rule.  Returns y [b, H, R, P]."""
+    dev = _device_of(h)
+    b, H, R, P = x.shape
+    G, N = B.shape[1], B.shape[3]
+    io = x.dtype
+    cplx = h.dim() == 5
+    _check(h, "h", (b, H, P, N, 2) if cplx else (b, H, P, N), torch.float32, dev)
+    if cplx and theta is None:
+        raise ValueError("the complex state needs theta [H, N]")
+    _check(x, "x", (b, H, R, P), io, dev)
+    _check(x_prev, "x_prev", (b, H, R, P), io, dev)
+    _check(delta, "delta", (b, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(theta, "theta", (H, N), torch.float32, dev)
+    _check(B, "B", (b, G, R, N), io, dev)
+    _check(B_prev, "B_prev", (b, G, R, N), io, dev)
+    _check(C, "C", (b, G, R, N), io, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(z, "z", (b, H, R, P), io, dev)
+    if out is None:
+        out = torch.empty((b, H, R, P), dtype=io, device=dev)
+    _check(out, "out", (b, H, R, P), io, dev)
+    st = lib().mss_mamba3_state_update(_ptr(h), _ptr(x), _ptr(x_prev), _ptr(delta), _ptr(A),
+                                       _ptr(theta if cplx else None), _ptr(B), _ptr(B_prev), _ptr(C), _ptr(D), _ptr(z),
+                                       _ptr(out), b, H, P, G, N, R, _io_code(io),
+                                       MSS_FLAG_COMPLEX_STATE if cplx else 0, _stream(stream))
+    _raise(st, "mss_mamba3_state_update")
     return out
 
 

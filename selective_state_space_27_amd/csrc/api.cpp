@@ -412,6 +412,61 @@ mss_status mss_state_update(float* h, const void* u, const void* delta, const fl
   return hip_status(mss::launch_state_update(p, static_cast<hipStream_t>(hip_stream)));
 }
 
+// ---------------------------------------------------------- Mamba-3 update
+mss_status mss_mamba3_state_update(float* h, const void* x, const void* x_prev, const float* delta, const float* A,
+                                   const float* theta, const void* B, const void* B_prev, const void* C,
+                                   const float* D, const void* z, void* y, int64_t batch, int64_t nheads,
+                                   int64_t headdim, int64_t ngroups, int64_t dstate, int64_t rank,
+                                   mss_dtype io_dtype, uint32_t flags, void* hip_stream) {
+  if (!h || !x || !delta || !A || !B || !C || !y) return MSS_ERR_NULL;
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return MSS_ERR_NULL;
+  const bool cplx = (flags & MSS_FLAG_COMPLEX_STATE) != 0;
+  if (cplx && !theta) return MSS_ERR_NULL;
+  if (!dtype_ok(io_dtype)) return MSS_ERR_DTYPE;
+  if (batch <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 || rank <= 0) return MSS_ERR_SHAPE;
+  // Grid (headdim/16, nheads, batch); state offsets within 2^40 floats.
+  if (batch > 65535 || nheads > 65535 || batch * nheads * headdim > (int64_t{1} << 28)) return MSS_ERR_SHAPE;
+  if (flags & ~MSS_FLAG_COMPLEX_STATE) return MSS_ERR_UNSUPPORTED;
+  if (headdim % 16 != 0 || headdim > 4096 || !(dstate == 64 || dstate == 128 || dstate == 256) || rank > 8 ||
+      nheads % ngroups != 0)
+    return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {h, delta, A, theta, D};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t es = elem_size(io_dtype);
+  const size_t nx = (size_t)batch * nheads * rank * headdim * es;
+  const size_t nbc = (size_t)batch * ngroups * rank * dstate * es;
+  const size_t nstate = (size_t)batch * nheads * headdim * dstate * sizeof(float) * (cplx ? 2 : 1);
+  const void* ins[] = {x, x_prev, delta, A, theta, B, B_prev, C, D, z};
+  const size_t in_bytes[] = {nx, nx, (size_t)batch * nheads * 4, (size_t)nheads * 4,
+                             (size_t)nheads * dstate * 4, nbc, nbc, nbc, (size_t)nheads * 4, nx};
+  if (!output_clear(h, nstate, ins, in_bytes, 10)) return MSS_ERR_ALIAS;
+  if (!output_clear(y, nx, ins, in_bytes, 10)) return MSS_ERR_ALIAS;
+  if (overlaps(range_of(y, nx), range_of(h, nstate))) return MSS_ERR_ALIAS;
+
+  mss::Mamba3Params p;
+  p.h = h;
+  p.x = x;
+  p.x_prev = x_prev;
+  p.delta = delta;
+  p.A = A;
+  p.theta = cplx ? theta : nullptr;
+  p.B = B;
+  p.B_prev = B_prev;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.y = y;
+  p.batch = batch;
+  p.nheads = nheads;
+  p.headdim = headdim;
+  p.ngroups = ngroups;
+  p.dstate = dstate;
+  p.rank = rank;
+  p.bf16 = io_dtype == MSS_BF16;
+  return hip_status(mss::launch_mamba3_step(p, static_cast<hipStream_t>(hip_stream)));
+}
+
 // ----------------------------------------------------------------------- SSD
 static mss_status ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                   int64_t ngroups, int64_t dstate, int64_t chunk, mss_dtype t) {

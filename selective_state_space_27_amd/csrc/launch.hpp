@@ -91,6 +91,27 @@ struct SSDParams {
   void* workspace;
 };
 
+// Mamba-3 state update: trapezoid input when x_prev (and B_prev) are given,
+// complex state when theta is.
+struct Mamba3Params {
+  float* h;               // [b, H, P, N] or [b, H, P, N, 2]
+  const void* x;          // [b, H, R, P]
+  const void* x_prev;     // nullable
+  const float* delta;     // [b, H]
+  const float* A;         // [H]
+  const float* theta;     // [H, N], nullable
+  const void* B;          // [b, G, R, N]
+  const void* B_prev;     // nullable
+  const void* C;          // [b, G, R, N]
+  const float* D;         // [H], nullable
+  const void* z;          // [b, H, R, P], nullable
+  void* y;                // [b, H, R, P]
+  int64_t batch, nheads, headdim, ngroups, dstate, rank;
+  bool bf16;
+};
+
+hipError_t launch_mamba3_step(const Mamba3Params& p, hipStream_t stream);
+
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t ngroups, int64_t dstate, int64_t chunk);
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);

@@ -16,6 +16,10 @@ library's benchmark presets):
   ssd_2p8b      b=2  H=80 P=64 N=128 L=16384 chunk 256
   scan_m2shape  b=2  d_inner=5120 (80 heads of 64) N=128 L=16384, bf16 I/O,
                 A and delta shared within a head (the Mamba-2 form)
+  decode_m3     b=128 H=80 P=64 N=128 rank 4, one token per step: Mamba-3
+                generation step with the trapezoid input rule and a complex
+                (rotating) fp32 state, bf16 I/O (the Mamba-3 block example's
+                d_state 128, headdim 64 and MIMO rank 4 at the 2.8b d_inner)
 
 Every tensor comes from its own numpy PCG64 stream seeded by
 SeedSequence([seed, tensor_id(, step)]), so the order in which tensors are
@@ -28,6 +32,7 @@ import numpy as np
 
 # Tensor ids for the per-tensor child streams.
 TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X, TID_DY, TID_CONVW, TID_CONVB = range(1, 14)
+TID_THETA = 14
 
 SEED_BASE = 27000
 
@@ -78,6 +83,25 @@ SCAN_130M = ScanConfig("scan_130m", 8, 1536, 16, 2048, "fp32", SEED_BASE + 1)
 SCAN_2P8B = ScanConfig("scan_2p8b", 4, 5120, 16, 8192, "bf16", SEED_BASE + 2)
 DECODE_2P8B = DecodeConfig("decode_2p8b", 256, 5120, 16, 1000, "bf16", SEED_BASE + 3)
 SSD_2P8B = SSDConfig("ssd_2p8b", 2, 16384, 80, 64, 1, 128, 256, SEED_BASE + 4)
+@dataclasses.dataclass(frozen=True)
+class Mamba3Config:
+    name: str
+    batch: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    rank: int
+    steps: int
+    io: str          # x, B, C, z, y; the state and delta, A, theta, D are fp32
+    complex_state: bool
+    trapezoid: bool
+    seed: int
+
+
+DECODE_M3 = Mamba3Config("decode_m3", 128, 80, 64, 1, 128, 4, 100, "bf16", True, True, SEED_BASE + 6)
+
+
 # The Mamba-1 scan on the SSD workload's shape (d_inner = 80 heads x 64, N=128,
 # the same b and L): the two kernels compared on one layer shape.
 SCAN_M2 = ScanConfig("scan_m2shape", 2, 5120, 128, 16384, "bf16", SEED_BASE + 5, a_form="head")
@@ -338,6 +362,45 @@ def ssd_inputs_device(cfg: SSDConfig, device="cuda:0") -> dict:
         "B": torch.randn((b, L, G, N), **kw).to(torch.bfloat16),
         "C": torch.randn((b, L, G, N), **kw).to(torch.bfloat16),
     }
+
+
+# -------------------------------------------------------- Mamba-3 inputs ---
+def mamba3_static(cfg: Mamba3Config) -> dict:
+    """Per-layer parameters of a Mamba-3 decode workload: A [H] =
+    -exp(U(0, ln 16)) and dt [H] (log-uniform on [1e-3, 1e-1]) as for SSD, D
+    [H] ~ N(0, 1), theta [H, N] ~ U(-pi, pi) (rotation rate per state; the
+    pages give no distribution), and the initial state 0.1 N(0, 1), [b, H, P,
+    N] or [b, H, P, N, 2]."""
+    b, H, P, N, s = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.seed
+    shape = (b, H, P, N, 2) if cfg.complex_state else (b, H, P, N)
+    return {
+        "A": (-np.exp(rng(s, TID_A).uniform(0.0, np.log(16.0), size=H))).astype(np.float32),
+        "dt": draw_dt(s, H),
+        "D": _normal(s, TID_D, (H,)),
+        "theta": rng(s, TID_THETA).uniform(-np.pi, np.pi, size=(H, N)).astype(np.float32),
+        "h0": (0.1 * _normal(s, TID_H0, shape)).astype(np.float32),
+    }
+
+
+def mamba3_step_inputs(cfg: Mamba3Config, step: int, dt: np.ndarray) -> dict:
+    """Fresh token inputs of one Mamba-3 step: x, z [b, H, R, P] and B, C
+    [b, G, R, N] ~ N(0, 1) in the I/O dtype; delta [b, H] fp32 from dt and
+    per-element noise as in the other workloads."""
+    b, H, P, G, N, R, s = cfg.batch, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.rank, cfg.seed
+    noise = _normal(s, TID_DNOISE, (b, H), step)
+    return {
+        "x": _io(_normal(s, TID_X, (b, H, R, P), step), cfg.io),
+        "B": _io(_normal(s, TID_B, (b, G, R, N), step), cfg.io),
+        "C": _io(_normal(s, TID_C, (b, G, R, N), step), cfg.io),
+        "z": _io(_normal(s, TID_Z, (b, H, R, P), step), cfg.io),
+        "delta": make_delta(dt, noise, (1, H)).astype(np.float32),
+    }
+
+
+def small_mamba3_config(batch, nheads, headdim, ngroups, dstate, rank, steps, io="fp32", complex_state=True,
+                        trapezoid=True, seed=SEED_BASE + 300) -> Mamba3Config:
+    return Mamba3Config(f"m3_b{batch}_h{nheads}_p{headdim}_g{ngroups}_n{dstate}_r{rank}_{io}", batch, nheads, headdim,
+                        ngroups, dstate, rank, steps, io, complex_state, trapezoid, seed)
 
 
 def small_scan_config(batch, dim, dstate, seqlen, io="fp32", seed=SEED_BASE + 100, a_form="s4d",

@@ -291,3 +291,34 @@ def test_python_binding_rejects_cpu_tensors():
     u = torch.zeros(1, 16, 8)
     with pytest.raises(ValueError, match="GPU tensors only"):
         mss.selective_scan_fwd(u, u, torch.zeros(16, 4), torch.zeros(1, 4, 8), torch.zeros(1, 4, 8))
+
+
+def m3_call(**kw):
+    b, H, Pd, G, N, R = kw.pop("shape", (2, 4, 64, 2, 128, 4))
+    io = kw.pop("io", BF16)
+    a = dict(h=P(0), x=P(1), xp=P(2), delta=P(3), A=P(4), theta=P(5), B=P(6), Bp=P(7), C=P(8), D=P(9), z=P(10),
+             y=P(11), flags=0x10)
+    a.update(kw)
+    return mss.lib().mss_mamba3_state_update(a["h"], a["x"], a["xp"], a["delta"], a["A"], a["theta"], a["B"],
+                                             a["Bp"], a["C"], a["D"], a["z"], a["y"], b, H, Pd, G, N, R, io,
+                                             a["flags"], None)
+
+
+def test_mamba3_validation_errors():
+    """Every error of the Mamba-3 step is found on the host (fake pointers);
+    a call that passes every check is never made here."""
+    assert m3_call(h=None) == NULL
+    assert m3_call(xp=None) == NULL                   # x_prev without B_prev
+    assert m3_call(Bp=None) == NULL
+    assert m3_call(theta=None) == NULL                # complex state without theta
+    assert m3_call(io=4) == DTYPE
+    assert m3_call(shape=(2, 4, 0, 2, 128, 4)) == SHAPE
+    assert m3_call(shape=(70000, 4, 64, 2, 128, 4)) == SHAPE
+    assert m3_call(shape=(2, 4, 24, 2, 128, 4)) == UNSUP   # headdim not a multiple of 16
+    assert m3_call(shape=(2, 4, 64, 2, 96, 4)) == UNSUP    # dstate not 64/128/256
+    assert m3_call(shape=(2, 4, 64, 2, 128, 9)) == UNSUP   # rank above 8
+    assert m3_call(shape=(2, 6, 64, 4, 128, 4)) == UNSUP   # nheads % ngroups
+    assert m3_call(flags=0x11) == UNSUP
+    assert m3_call(h=P(0, 8)) == ALIGN
+    assert m3_call(y=P(1, 32)) == ALIAS                     # y on x
+    assert m3_call(h=P(8, 64)) == ALIAS                     # state on C
