@@ -22,7 +22,9 @@ different computation.  The Mamba-3 step is pinned by its reduction to the
 SSD recurrence (rank 1, real, Euler input), MIMO superposition over SSD runs,
 the closed form of a rotating decaying state, the trapezoid rule's second-order
 convergence on an ODE with a known solution, and the closed-form fixed point of
-a constant input (real and complex).
+a constant input (real and complex).  The SSD backward is pinned by central
+finite differences of the SSD forward and by its equality with the selective
+scan's backward on the SSD's Mamba-1 form.
 """
 from __future__ import annotations
 
@@ -62,6 +64,8 @@ def _load():
         lib.oracle_selective_scan_bwd.restype = None
         lib.oracle_scan_prologue.argtypes = [_dp] * 7 + [L, L, L, ctypes.c_int, ctypes.c_int]
         lib.oracle_scan_prologue.restype = None
+        lib.oracle_ssd_bwd.argtypes = [_dp] * 18 + [L] * 6 + [ctypes.c_int]
+        lib.oracle_ssd_bwd.restype = None
         lib.oracle_mamba3_step.argtypes = [_dp] * 12 + [L] * 6 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_mamba3_step.restype = None
         _lib = lib
@@ -219,6 +223,34 @@ def ssd(x, delta, A, B, C, D=None, z=None, h0=None, chunk=None, threads=None):
                        _ptr(y), _ptr(cs), _ptr(h_last), b, L, H, P, G, N, q,
                        threads or default_threads())
     return y, cs, h_last
+
+
+def ssd_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, threads=None):
+    """Gradient of a loss through the SSD layer, in fp64 (mss_oracle.c,
+    oracle_ssd_bwd): given dy = dloss/dy [b, L, H, P] and optionally dh_last
+    [b, H, P, N], returns a dict with dx, dz (None without z) [b, L, H, P],
+    ddelta [b, L, H], dA [H], dB, dC [b, L, G, N], dD [H] (None without D) and
+    dh0 [b, H, P, N]."""
+    x = _f64(x)
+    b, L, H, P = x.shape
+    G, N = np.shape(B)[2], np.shape(B)[3]
+    delta = _f64(delta, (b, L, H))
+    A = _f64(A, (H,))
+    B = _f64(B, (b, L, G, N))
+    C = _f64(C, (b, L, G, N))
+    D = _f64(D, (H,))
+    z = _f64(z, (b, L, H, P))
+    h0 = _f64(h0, (b, H, P, N))
+    dy = _f64(dy, (b, L, H, P))
+    dh_last = _f64(dh_last, (b, H, P, N))
+    g = {"dx": np.empty((b, L, H, P)), "ddelta": np.empty((b, L, H)), "dA": np.empty(H),
+         "dB": np.empty((b, L, G, N)), "dC": np.empty((b, L, G, N)), "dD": np.empty(H) if D is not None else None,
+         "dz": np.empty((b, L, H, P)) if z is not None else None, "dh0": np.empty((b, H, P, N))}
+    _load().oracle_ssd_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
+                           _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                           _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), b, L, H, P, G, N,
+                           threads or default_threads())
+    return g
 
 
 def mamba3_step(h, x, delta, A, B, C, D=None, z=None, x_prev=None, B_prev=None, theta=None, complex_state=False,

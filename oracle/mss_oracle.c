@@ -521,3 +521,163 @@ void oracle_mamba3_step(double* h, const double* x, const double* x_prev, const 
   free(th);
   free(jobs);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Mamba-2 (SSD) layer, backward: the gradient of a scalar loss through      */
+/* oracle_ssd, given dy = dloss/dy and optionally dh_last = dloss/dh_last.   */
+/* Training runs the layer over whole sequences ("Mamba (deep learning)",   */
+/* paragraph on training and generation; "Mamba-1/2/3 visual guide",        */
+/* section 3 table: Mamba-2 trains with the chunked algorithm); its gradient */
+/* is the chain rule through the recurrence, here in reverse time, one step */
+/* at a time.  Per (b, head h, group g), with G the gradient of the state   */
+/* after step t and a_t = exp(delta_t A_h):                                  */
+/*   dout = dy * silu(z);  dz = dy * out * silu'(z)    (out = C.S + D x)     */
+/*   G += dout C_t^T;  dC_t += S_t^T dout;  dD += dout . x_t                 */
+/*   dx_t = delta_t G B_t + D dout;  dB_t += delta_t G^T x_t                 */
+/*   ddelta_t = x_t^T G B_t + A_h a_t <G, S_{t-1}>;  dA_h += delta_t a_t <G, S_{t-1}> */
+/*   G *= a_t   (the gradient of S_{t-1});  dh0 = G at the end               */
+/* dB and dC are summed over the heads of a group.  Layouts as oracle_ssd;  */
+/* dx, dz [batch, seqlen, nheads, headdim]; ddelta [batch, seqlen, nheads]; */
+/* dA, dD [nheads]; dB, dC [batch, seqlen, ngroups, dstate]; dh0 [batch,    */
+/* nheads, headdim, dstate].  The forward states are kept (seqlen x P x N   */
+/* per unit).  Units are (b, group) so that the sums over a group's heads   */
+/* stay in one thread.                                                      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const double *x, *delta, *A, *B, *C, *D, *z, *h0, *dy, *dh_last;
+  double *dx, *ddelta, *dA_part, *dB, *dC, *dD_part, *dz, *dh0;
+  long batch, seqlen, nheads, headdim, ngroups, dstate;
+  long unit_begin, unit_end;
+} ssd_bwd_job;
+
+static double dsilu(double z) { /* d/dz of z sigma(z) */
+  const double sg = 1.0 / (1.0 + exp(-z));
+  return sg * (1.0 + z * (1.0 - sg));
+}
+
+static void ssd_bwd_head(const ssd_bwd_job* j, long b, long hd) {
+  const long L = j->seqlen, H = j->nheads, P = j->headdim, G = j->ngroups, N = j->dstate;
+  const long g = hd / (H / G);
+  const double A = j->A[hd], D = j->D ? j->D[hd] : 0.0;
+  /* forward, keeping every state: Ss[t+1] is the state after step t, Ss[0] the initial one */
+  double* Ss = (double*)malloc(sizeof(double) * (size_t)((L + 1) * P * N));
+  for (long i = 0; i < P * N; ++i) Ss[i] = j->h0 ? j->h0[(b * H + hd) * P * N + i] : 0.0;
+  for (long t = 0; t < L; ++t) {
+    const double dlt = j->delta[(b * L + t) * H + hd], a = exp(dlt * A);
+    const double* Bt = j->B + ((b * L + t) * G + g) * N;
+    const double* xt = j->x + ((b * L + t) * H + hd) * P;
+    const double* prev = Ss + t * P * N;
+    double* cur = Ss + (t + 1) * P * N;
+    for (long p = 0; p < P; ++p)
+      for (long n = 0; n < N; ++n) cur[p * N + n] = a * prev[p * N + n] + dlt * Bt[n] * xt[p];
+  }
+  /* reverse */
+  double* Gs = (double*)malloc(sizeof(double) * (size_t)(P * N));
+  double* dout = (double*)malloc(sizeof(double) * (size_t)P);
+  for (long i = 0; i < P * N; ++i) Gs[i] = j->dh_last ? j->dh_last[(b * H + hd) * P * N + i] : 0.0;
+  double dA = 0.0, dD = 0.0;
+  for (long t = L - 1; t >= 0; --t) {
+    const double dlt = j->delta[(b * L + t) * H + hd], a = exp(dlt * A);
+    const double* Bt = j->B + ((b * L + t) * G + g) * N;
+    const double* Ct = j->C + ((b * L + t) * G + g) * N;
+    const long xo = ((b * L + t) * H + hd) * P;
+    const double* xt = j->x + xo;
+    const double* St = Ss + (t + 1) * P * N;
+    const double* Sp = Ss + t * P * N;
+    for (long p = 0; p < P; ++p) {
+      double out = D * xt[p];
+      for (long n = 0; n < N; ++n) out += Ct[n] * St[p * N + n];
+      const double dyv = j->dy[xo + p];
+      if (j->z) {
+        const double zv = j->z[xo + p];
+        dout[p] = dyv * (zv / (1.0 + exp(-zv)));
+        j->dz[xo + p] = dyv * out * dsilu(zv);
+      } else {
+        dout[p] = dyv;
+      }
+      dD += dout[p] * xt[p];
+    }
+    double* dCt = j->dC + ((b * L + t) * G + g) * N;
+    double* dBt = j->dB + ((b * L + t) * G + g) * N;
+    for (long n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (long p = 0; p < P; ++p) {
+        Gs[p * N + n] += dout[p] * Ct[n];
+        acc += St[p * N + n] * dout[p];
+      }
+      dCt[n] += acc;
+    }
+    double gsp = 0.0, xgb = 0.0;
+    for (long p = 0; p < P; ++p) {
+      double gb = 0.0;
+      for (long n = 0; n < N; ++n) {
+        gb += Gs[p * N + n] * Bt[n];
+        gsp += Gs[p * N + n] * Sp[p * N + n];
+      }
+      j->dx[xo + p] = dlt * gb + D * dout[p];
+      xgb += xt[p] * gb;
+    }
+    for (long n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (long p = 0; p < P; ++p) acc += Gs[p * N + n] * xt[p];
+      dBt[n] += dlt * acc;
+    }
+    j->ddelta[(b * L + t) * H + hd] = xgb + A * a * gsp;
+    dA += dlt * a * gsp;
+    for (long i = 0; i < P * N; ++i) Gs[i] *= a;
+  }
+  if (j->dh0) memcpy(j->dh0 + (b * H + hd) * P * N, Gs, sizeof(double) * (size_t)(P * N));
+  j->dA_part[b * H + hd] = dA;
+  j->dD_part[b * H + hd] = dD;
+  free(dout);
+  free(Gs);
+  free(Ss);
+}
+
+static void* ssd_bwd_worker(void* arg) {
+  const ssd_bwd_job* j = (const ssd_bwd_job*)arg;
+  const long hpg = j->nheads / j->ngroups;
+  for (long k = j->unit_begin; k < j->unit_end; ++k) {
+    const long b = k / j->ngroups, g = k % j->ngroups;
+    for (long hd = g * hpg; hd < (g + 1) * hpg; ++hd) ssd_bwd_head(j, b, hd);
+  }
+  return NULL;
+}
+
+void oracle_ssd_bwd(const double* x, const double* delta, const double* A, const double* B, const double* C,
+                    const double* D, const double* z, const double* h0, const double* dy, const double* dh_last,
+                    double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dz,
+                    double* dh0, long batch, long seqlen, long nheads, long headdim, long ngroups, long dstate,
+                    int nthreads) {
+  const long H = nheads;
+  memset(dB, 0, sizeof(double) * (size_t)(batch * seqlen * ngroups * dstate));
+  memset(dC, 0, sizeof(double) * (size_t)(batch * seqlen * ngroups * dstate));
+  double* dA_part = (double*)calloc((size_t)(batch * H), sizeof(double));
+  double* dD_part = (double*)calloc((size_t)(batch * H), sizeof(double));
+  long units = batch * ngroups;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  ssd_bwd_job* jobs = (ssd_bwd_job*)calloc((size_t)nthreads, sizeof(ssd_bwd_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    ssd_bwd_job jb = {x, delta, A, B, C, D, z, h0, dy, dh_last, dx, ddelta, dA_part, dB, dC, dD_part, dz, dh0,
+                      batch, seqlen, nheads, headdim, ngroups, dstate, units * i / nthreads,
+                      units * (i + 1) / nthreads};
+    jobs[i] = jb;
+    pthread_create(&th[i], NULL, ssd_bwd_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  for (long hd = 0; hd < H; ++hd) {
+    double sa = 0.0, sd = 0.0;
+    for (long b = 0; b < batch; ++b) {
+      sa += dA_part[b * H + hd];
+      sd += dD_part[b * H + hd];
+    }
+    dA[hd] = sa;
+    if (dD) dD[hd] = sd;
+  }
+  free(th);
+  free(jobs);
+  free(dD_part);
+  free(dA_part);
+}

@@ -655,3 +655,74 @@ def test_mamba3_trapezoid_fixed_point(complex_state):
                                   theta=np.array([[th]]), complex_state=complex_state)
     got = h[..., 0] + 1j * h[..., 1] if complex_state else h
     np.testing.assert_allclose(np.ravel(got)[0], want, rtol=1e-12)
+
+
+# ----------------------------------------------------------- SSD backward ---
+def _ssd_small(b=1, L=6, H=2, P=3, N=4, G=1, seed=0, D=True, z=True, h0=True):
+    g = np.random.default_rng(seed)
+    return dict(x=g.standard_normal((b, L, H, P)), delta=0.05 + 0.4 * g.random((b, L, H)),
+                A=-np.exp(g.uniform(-0.5, 1.0, H)), B=g.standard_normal((b, L, G, N)),
+                C=g.standard_normal((b, L, G, N)), D=g.standard_normal(H) if D else None,
+                z=g.standard_normal((b, L, H, P)) if z else None,
+                h0=0.3 * g.standard_normal((b, H, P, N)) if h0 else None)
+
+
+@pytest.mark.parametrize("G, opts", [(1, (True, True, True)), (2, (True, True, True)), (1, (False, False, False))])
+def test_ssd_backward_equals_finite_differences(G, opts):
+    """Every element of every gradient against central differences of the
+    forward oracle, for the loss sum(dy * y) + sum(dh_last * h_last)."""
+    inp = _ssd_small(b=2, L=5, H=4, P=3, N=4, G=G, seed=7 + G, D=opts[0], z=opts[1], h0=opts[2])
+    g = np.random.default_rng(99)
+    dy = g.standard_normal(inp["x"].shape)
+    dhl = g.standard_normal((2, 4, 3, 4))
+
+    def loss(d):
+        y, _, hl = oracle.ssd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"])
+        return float(np.sum(dy * y) + np.sum(dhl * hl))
+
+    got = oracle.ssd_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"], dy=dy,
+                         dh_last=dhl)
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    eps = 1e-6
+    for k, gk in names.items():
+        if inp[k] is None:
+            continue
+        num = np.zeros_like(inp[k])
+        for idx in np.ndindex(inp[k].shape):
+            plus, minus = dict(inp), dict(inp)
+            plus[k], minus[k] = inp[k].copy(), inp[k].copy()
+            plus[k][idx] += eps
+            minus[k][idx] -= eps
+            num[idx] = (loss(plus) - loss(minus)) / (2 * eps)
+        np.testing.assert_allclose(got[gk], num, rtol=1e-6, atol=1e-7, err_msg=k)
+
+
+def test_ssd_backward_equals_scan_backward_on_mamba1_form():
+    """The SSD with one group is the selective scan with channels (h, p),
+    A[d, n] = A_h, delta[b, d, l] = delta[b, l, h] and B, C shared by all
+    channels: its gradients are the scan backward's, summed over the channels
+    of a head where the SSD shares a parameter (delta, A, D)."""
+    b, L, H, P, N = 2, 7, 3, 4, 5
+    inp = _ssd_small(b=b, L=L, H=H, P=P, N=N, G=1, seed=21)
+    g = np.random.default_rng(22)
+    dy = g.standard_normal(inp["x"].shape)
+    dhl = g.standard_normal((b, H, P, N))
+    s = oracle.ssd_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"], dy=dy,
+                       dh_last=dhl)
+    tr = lambda a: np.ascontiguousarray(a.reshape(b, L, H * P).transpose(0, 2, 1))   # [b, L, H, P] -> [b, d, L]
+    u, zz, dyy = tr(inp["x"]), tr(inp["z"]), tr(dy)
+    dl = np.ascontiguousarray(np.repeat(inp["delta"], P, axis=2).transpose(0, 2, 1))
+    A1 = np.repeat(np.repeat(inp["A"], P)[:, None], N, axis=1)
+    B1 = np.ascontiguousarray(inp["B"][:, :, 0].transpose(0, 2, 1))
+    C1 = np.ascontiguousarray(inp["C"][:, :, 0].transpose(0, 2, 1))
+    m = oracle.selective_scan_bwd(u, dl, A1, B1, C1, np.repeat(inp["D"], P), zz, inp["h0"].reshape(b, H * P, N),
+                                  dy=dyy, dh_last=dhl.reshape(b, H * P, N))
+    back = lambda a: a.transpose(0, 2, 1).reshape(b, L, H, P)
+    np.testing.assert_allclose(s["dx"], back(m["du"]), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["dz"], back(m["dz"]), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["ddelta"], back(m["ddelta"]).sum(axis=3), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["dA"], m["dA"].reshape(H, P, N).sum(axis=(1, 2)), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["dD"], m["dD"].reshape(H, P).sum(axis=1), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["dB"][:, :, 0], m["dB"].transpose(0, 2, 1), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["dC"][:, :, 0], m["dC"].transpose(0, 2, 1), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s["dh0"], m["dh0"].reshape(b, H, P, N), rtol=1e-10, atol=1e-12)
