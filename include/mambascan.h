@@ -326,6 +326,55 @@ size_t mss_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int
                               int64_t ngroups, int64_t dstate, int64_t chunk, mss_dtype in_dtype);
 
 /* ------------------------------------------------------------------------ */
+/* Mamba-2 SSD layer, backward (training).                                   */
+/*                                                                          */
+/* The gradient of a scalar loss through mss_ssd_chunk_fwd, given dy =       */
+/* dloss/dy and optionally dh_last = dloss/dh_last.  Training runs the SSD   */
+/* over whole sequences with the chunked algorithm ("Mamba-1/2/3 visual      */
+/* guide", section 3 comparison table, training row); the gradient is the    */
+/* chain rule through the forward recurrence in reverse time.  Per (b, h),   */
+/* with dout = dy*silu(z) (dy without z), G the gradient of the state after  */
+/* step t (G = dout_t C_t^T + exp(delta_{t+1} A) G_{t+1}, G after the last   */
+/* step = dout C^T + dh_last) and S the state:                               */
+/*   dx_t = delta_t G B_t + D dout_t;   dz_t = dy_t y_t silu'(z_t)           */
+/*          (y_t = C_t S_t + D x_t, the output before the gate)              */
+/*   ddelta_t = x_t^T G B_t + A <G, exp(delta_t A) S_{t-1}>                  */
+/*   dB_t, dC_t = sums over the heads of the group of delta_t G^T x_t and    */
+/*          S_t^T dout_t;  dA, dD = sums over batch and time of              */
+/*          delta_t <G, exp(delta_t A) S_{t-1}> and dout_t . x_t;            */
+/*   dh0 = exp(delta_0 A) G_0.                                               */
+/* The states are recomputed (a forward pass with 64-step chunks keeps the   */
+/* state after every 64 steps in the workspace), not taken from the caller. */
+/* Sums run in a fixed order: the results are bitwise repeatable.           */
+/*                                                                          */
+/* Inputs: as mss_ssd_chunk_fwd (x, delta, A, B, C, D, z, h0; same layouts  */
+/* and dtypes), dy [batch, seqlen, nheads, headdim] fp32 (the forward's y    */
+/* dtype), dh_last [batch, nheads, headdim, dstate] fp32 (NULL = zero).      */
+/* Outputs (fp32, written, not accumulated): dx, dz [batch, seqlen, nheads,  */
+/* headdim]; ddelta [batch, seqlen, nheads]; dA [nheads]; dB, dC [batch,     */
+/* seqlen, ngroups, dstate]; dD [nheads] (NULL = not computed; with D NULL   */
+/* it is the gradient at D = 0); dz given exactly when z is (else            */
+/* MSS_ERR_NULL); dh0 [batch, nheads, headdim, dstate] (NULL = not computed; */
+/* the gradient of h0, or of a zero initial state).                          */
+/* Supported: in_dtype MSS_BF16; headdim 64 or 128; dstate a multiple of 16 */
+/* up to 128; nheads % ngroups == 0 (else MSS_ERR_UNSUPPORTED); the         */
+/* forward's size limits with chunk 64 (else MSS_ERR_SHAPE).  `flags` must   */
+/* be 0.  Outputs must not overlap any input or each other.  The workspace  */
+/* (size from mss_ssd_bwd_workspace_size) need not be zeroed.               */
+/* ------------------------------------------------------------------------ */
+mss_status mss_ssd_chunk_bwd(const void* x, const float* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z, const float* h0,
+                             const float* dy, const float* dh_last, float* dx, float* ddelta,
+                             float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
+                             int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t ngroups, int64_t dstate, mss_dtype in_dtype, uint32_t flags,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace mss_ssd_chunk_bwd needs (0 when unsupported). */
+size_t mss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                  int64_t ngroups, int64_t dstate, mss_dtype in_dtype);
+
+/* ------------------------------------------------------------------------ */
 /* Status of a call that used `workspace`.                                   */
 /*                                                                          */
 /* The selective scan (forward, fused, backward) hands states between        */

@@ -48,7 +48,8 @@ EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_noalloc", "mss_sele
            "mss_selective_scan_bwd",
            "mss_selective_scan_bwd_workspace_size", "mss_state_update",
            "mss_mamba3_state_update",
-           "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_workspace_status", "mss_status_string",
+           "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_ssd_chunk_bwd", "mss_ssd_bwd_workspace_size",
+           "mss_workspace_status", "mss_status_string",
            "mss_last_hip_error", "mss_abi_version")
 
 
@@ -101,6 +102,11 @@ def lib() -> ctypes.CDLL:
     L.mss_ssd_chunk_fwd.restype = ctypes.c_int
     L.mss_ssd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.mss_ssd_workspace_size.restype = sz
+    L.mss_ssd_chunk_bwd.argtypes = [vp, fp, fp, vp, vp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, i64, i64,
+                                    i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.mss_ssd_chunk_bwd.restype = ctypes.c_int
+    L.mss_ssd_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    L.mss_ssd_bwd_workspace_size.restype = sz
     L.mss_workspace_status.argtypes = [vp, vp]
     L.mss_workspace_status.restype = ctypes.c_int
     L.mss_status_string.argtypes = [ctypes.c_int]
@@ -486,3 +492,50 @@ def ssd_chunk_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk=256, retu
     if return_last_state:
         res.append(hl)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def ssd_bwd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, dtype=torch.bfloat16) -> int:
+    return lib().mss_ssd_bwd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, _io_code(dtype))
+
+
+def ssd_chunk_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dD=True, want_dh0=True,
+                  out=None, workspace=None, stream=None) -> dict:
+    """Gradient of a loss through ssd_chunk_fwd (same inputs), given dy =
+    dloss/dy [b, L, H, P] and optionally dh_last = dloss/dh_last [b, H, P, N],
+    both float32.  Returns a dict of float32 tensors: dx, dz (None without z)
+    [b, L, H, P], ddelta [b, L, H], dA [H], dB, dC [b, L, G, N], dD [H] (None
+    unless want_dD) and dh0 [b, H, P, N] (None unless want_dh0).  d_state <=
+    128.  ``out``: a dict from an earlier call with the same shapes whose
+    tensors are written again."""
+    dev = _device_of(x)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = x.dtype
+    f32 = torch.float32
+    for t, name, shape, dt in ((x, "x", (b, L, H, P), io), (delta, "delta", (b, L, H), f32), (A, "A", (H,), f32),
+                               (B, "B", (b, L, G, N), io), (C, "C", (b, L, G, N), io), (D, "D", (H,), f32),
+                               (z, "z", (b, L, H, P), io), (h0, "h0", (b, H, P, N), f32),
+                               (dy, "dy", (b, L, H, P), f32), (dh_last, "dh_last", (b, H, P, N), f32)):
+        _check(t, name, shape, dt, dev)
+    code = _io_code(io)
+    shapes = {"dx": (b, L, H, P), "ddelta": (b, L, H), "dA": (H,), "dB": (b, L, G, N), "dC": (b, L, G, N),
+              "dD": (H,), "dz": (b, L, H, P), "dh0": (b, H, P, N)}
+    want = {"dD": want_dD, "dz": z is not None, "dh0": want_dh0}
+    g = out if out is not None else {
+        k: (torch.empty(shp, dtype=f32, device=dev) if want.get(k, True) else None) for k, shp in shapes.items()}
+    for k, shp in shapes.items():
+        _check(g.get(k), k, shp, f32, dev)
+    if (z is None) != (g.get("dz") is None):
+        raise ValueError("dz is returned exactly when z is given")
+    need = lib().mss_ssd_bwd_workspace_size(b, L, H, P, G, N, code)
+    if need == 0:
+        _raise(5, "ssd_chunk_bwd")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().mss_ssd_chunk_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                 _ptr(dy), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                 _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+                                 _ptr(g.get("dh0")), b, L, H, P, G, N, code, 0, _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _raise(st, "mss_ssd_chunk_bwd")
+    return g

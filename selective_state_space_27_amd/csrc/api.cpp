@@ -551,4 +551,82 @@ mss_status mss_ssd_chunk_fwd(const void* x, const float* delta, const float* A, 
   return hip_status(mss::launch_ssd(p, static_cast<hipStream_t>(hip_stream)));
 }
 
+
+static mss_status ssd_bwd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                      int64_t ngroups, int64_t dstate, mss_dtype t) {
+  const mss_status st = ssd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, 64, t);
+  if (st != MSS_OK) return st;
+  if (dstate > 128) return MSS_ERR_UNSUPPORTED;
+  return MSS_OK;
+}
+
+size_t mss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                  int64_t ngroups, int64_t dstate, mss_dtype in_dtype) {
+  if (ssd_bwd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype) != MSS_OK) return 0;
+  return mss::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
+}
+
+mss_status mss_ssd_chunk_bwd(const void* x, const float* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* h0, const float* dy, const float* dh_last,
+                             float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz,
+                             float* dh0, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t ngroups, int64_t dstate, mss_dtype in_dtype, uint32_t flags, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return MSS_ERR_NULL;
+  if ((z == nullptr) != (dz == nullptr)) return MSS_ERR_NULL;
+  mss_status st = ssd_bwd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype);
+  if (st != MSS_OK) return st;
+  if (flags != 0) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {x, delta, A, B, C, D, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t need = mss::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+
+  const size_t es = elem_size(in_dtype);
+  const size_t nx = (size_t)batch * seqlen * nheads * headdim;
+  const size_t nbc = (size_t)batch * seqlen * ngroups * dstate;
+  const size_t nstate = (size_t)batch * nheads * headdim * dstate * sizeof(float);
+  const size_t ndl = (size_t)batch * seqlen * nheads * 4;
+  const void* ins[] = {x, delta, A, B, C, D, z, h0, dy, dh_last, workspace};
+  const size_t in_bytes[] = {nx * es, ndl, (size_t)nheads * 4, nbc * es, nbc * es, (size_t)nheads * 4, nx * es,
+                             nstate, nx * 4, nstate, need};
+  const void* outs[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0};
+  const size_t out_bytes[] = {nx * 4, ndl, (size_t)nheads * 4, nbc * 4, nbc * 4, (size_t)nheads * 4, nx * 4, nstate};
+  for (int i = 0; i < 8; ++i) {
+    if (!output_clear(outs[i], out_bytes[i], ins, in_bytes, 11)) return MSS_ERR_ALIAS;
+    for (int j = i + 1; j < 8; ++j)
+      if (outs[i] && outs[j] && overlaps(range_of(outs[i], out_bytes[i]), range_of(outs[j], out_bytes[j])))
+        return MSS_ERR_ALIAS;
+  }
+
+  mss::SSDBwdParams p;
+  p.x = x;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.h0 = h0;
+  p.dy = dy;
+  p.dh_last = dh_last;
+  p.dx = dx;
+  p.ddelta = ddelta;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = dD;
+  p.dz = dz;
+  p.dh0 = dh0;
+  p.batch = batch;
+  p.seqlen = seqlen;
+  p.nheads = nheads;
+  p.headdim = headdim;
+  p.ngroups = ngroups;
+  p.dstate = dstate;
+  p.workspace = workspace;
+  return hip_status(mss::launch_ssd_bwd(p, static_cast<hipStream_t>(hip_stream)));
+}
+
 }  // extern "C"

@@ -75,6 +75,9 @@ __device__ __forceinline__ void buf_store_u16(rsrc_t r, uint32_t off, uint16_t v
 __device__ __forceinline__ void buf_store_u32x2(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store_u32x4(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 
 // Broadcast lane P of each row of 16 lanes to the whole row (DPP row_newbcast).
 // Used as the first operand of a multiply, the move folds into v_mul_f32_dpp.

@@ -115,5 +115,40 @@ hipError_t launch_mamba3_step(const Mamba3Params& p, hipStream_t stream);
 size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t ngroups, int64_t dstate, int64_t chunk);
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
+// Byte offsets, inside the SSD forward's workspace, of its head-major delta
+// rows and their prefix sums inside every 64-step block scaled by A log2(e)
+// ([b, H, Lp] fp32 each, Lp = seqlen rounded up to 64).
+void ssd_delta_rows(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t chunk, size_t& dlT,
+                    size_t& lsT);
+
+// Backward of the SSD layer (dstate <= 128): the forward's inputs, dy and
+// dh_last (nullable), and the gradients (dD exactly when D, dz exactly when
+// z; dh0 nullable).
+struct SSDBwdParams {
+  const void* x;
+  const float* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* h0;       // nullable
+  const float* dy;
+  const float* dh_last;  // nullable
+  float* dx;
+  float* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;             // nullable
+  float* dz;             // nullable
+  float* dh0;            // nullable
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+  void* workspace;
+};
+
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                               int64_t dstate);
+hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream);
 
 }  // namespace mss

@@ -1,0 +1,892 @@
+// Backward of the Mamba-2 SSD layer on the CDNA4 matrix cores (gfx950).
+//
+// What is computed (see include/mambascan.h): the gradient of a loss through
+// the SSD recurrence ("Mamba-1/2/3 visual guide", section 3: scalar decay per
+// head, B and C shared by the heads of a group; the training row of its
+// comparison table: the chunked algorithm), given dy = dloss/dy and
+// optionally dh_last = dloss/dh_last.  With dyy = dy * silu(z) the gradient
+// with respect to the ungated output, G_t the adjoint of the state after
+// step t (G_t = dyy_t C_t^T + exp(delta_{t+1} A) G_{t+1}) and h_t the state:
+//   dx_t    = delta_t G_t B_t + D dyy_t
+//   dB_t    = sum over the group's heads of delta_t G_t^T x_t
+//   dC_t    = sum over the group's heads of h_t^T dyy_t
+//   ddelta_t = x_t^T G_t B_t + A <G_t, exp(delta_t A) h_{t-1}>
+//   dA = sum delta_t <G_t, exp(delta_t A) h_{t-1}>,  dD = sum dyy . x
+//   dz = dy * y_ungated * silu'(z),  dh0 = exp(delta_0 A) G_0.
+// Blocked the way the page's chunk figures block the forward: 64-step
+// blocks, inside a block dense products on the matrix cores, between blocks
+// the forward state S and the adjoint E handed along the sequence.  Per block,
+// with s_i = A sum_{k<=i} delta_k (prefix sums inside the block), the entering
+// state S_in and the adjoint E arriving from the later blocks:
+//   G_t = sum_{i>=t} exp(s_i - s_t) dyy_i C_i^T + exp(s_63 - s_t) E
+//   h_t = exp(s_t) S_in + sum_{j<=t} exp(s_t - s_j) delta_j x_j B_j^T
+// so that, with K = C B^T, W = dyy x^T (64 x 64) and M_ij = exp(s_i - s_j)
+// for j <= i (else 0):
+//   (G B)^T = E B^T diag(f) + dyy^T (M o K)         f_t = exp(s_63 - s_t)
+//   (x^T G)^T = E^T x^T diag(f) + C^T (M o W)
+//   (h^T dyy)^T = S_in^T dyy^T diag(e) + B^T (M o W^T o delta)   e_i = exp(s_i)
+// and <G_t, exp(delta_t A) h_{t-1}> splits into four sums over the block
+// (the i >= t, j < t corner of M o K o W o delta, a suffix sum of
+// e_i C_i . (S_in^T dyy_i), a prefix sum of f_j delta_j B_j . (E^T x_j), and
+// exp(s_63) <E, S_in>), formed from row and column sums and wave-wide scans.
+//
+// Passes:
+//   1. the forward kernels with 64-step chunks: the state after every block
+//      and the ungated output (for dz);
+//   2. ssd_bwd_local_kernel: per (block, virtual head) the block's own part of
+//      the adjoint handed to the block before, F = sum_i exp(s_i) dyy_i C_i^T,
+//      and dz;
+//   3. ssd_bwd_chain_kernel: E along the sequence, from the last block to the
+//      first: E_{k-1} = exp(s_63 of block k) E_k + F_k (dh0 at the end);
+//   4. ssd_bwd_grad_kernel: per (block, virtual head) every gradient above on
+//      the matrix cores; dB, dC, ddelta, dA and dD as per-virtual-head parts;
+//   5. fixed-order sums of those parts (the results are bitwise repeatable).
+// Operands that are not exact bf16 inputs enter the matrix cores as bf16
+// hi/lo pairs (two products, three when both operands are split).
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "ssd_common.hpp"
+
+namespace mss {
+namespace {
+
+using namespace ssd;
+
+constexpr int kRowP = kP + kPadH;  // row length of the step-major dyy stagings (bf16)
+
+struct BwdArgs {
+  const uint16_t* x;      // [b, L, H, P] bf16
+  const float* A;         // [H]
+  const uint16_t* B;      // [b, L, G, N] bf16
+  const uint16_t* C;      // [b, L, G, N] bf16
+  const float* D;         // [H] or null
+  const uint16_t* z;      // [b, L, H, P] bf16 or null
+  const float* h0;        // [b, H, P, N] or null
+  const float* dy;        // [b, L, H, P]
+  const float* dh_last;   // [b, H, P, N] or null
+  float* dx;              // [b, L, H, P]
+  float* dz;              // [b, L, H, P], exactly when z is given
+  float* ddelta;          // [b, L, H]
+  float* dA;              // [H]
+  float* dB;              // [b, L, G, N]
+  float* dC;              // [b, L, G, N]
+  float* dD;              // [H], exactly when D is given
+  float* dh0;             // [b, H, P, N] or null
+  // Workspace.
+  const float* dlT;       // [b, H, Lp]: delta, head-major (0 past L)
+  const float* lsT;       // [b, H, Lp]: A log2(e) times the prefix sum of delta inside each 64-step block
+  const float* yf;        // [b, L, H, P]: the forward output before the gate
+  const float* Sblk;      // [b, nblk, H, P, N]: the state after every block
+  float* Eblk;            // [b, nblk, H, P, N]: F of every block, then the adjoint E arriving at it
+  float* dBp;             // [b, L, Hv, N]: per-virtual-head parts of dB
+  float* dCp;             // [b, L, Hv, N]: of dC
+  float* ddp;             // [b, L, Hv]: of ddelta
+  float* dAp;             // [b, nblk, Hv]: of dA
+  float* dDp;             // [b, nblk, Hv]: of dD
+  int batch, L, H, G, P, ph, Hv, N, nblk, Lp;
+};
+
+// Element offset, inside one step's [H, P] row, of row 0 of virtual head vh
+// (rows (vh % ph)*64 .. of head vh / ph).
+__device__ __forceinline__ size_t vrow(const BwdArgs& a, int vh) {
+  return (size_t)(vh / a.ph) * a.P + (size_t)(vh % a.ph) * kP;
+}
+// Element offset of virtual head vh's 64 x N state slice in a [lead, H, P, N]
+// tensor (rows p at p*N).
+__device__ __forceinline__ size_t sbase(const BwdArgs& a, size_t lead, int vh) {
+  return (lead * a.H * a.P + vrow(a, vh)) * a.N;
+}
+
+__device__ __forceinline__ float sigmoid(float z) { return rcp_fast(1.0f + exp2_fast(-z * kLog2e)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ f32x4 as_f32x4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
+__device__ __forceinline__ u32x4 as_u32x4(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+
+// B or C (group g) transposed into a time-contiguous staging T (tsw layout,
+// 128 state rows): 512 units of (step pair, 8 states), two per thread; steps
+// past L and states past N are staged as zeros.
+__device__ __forceinline__ void stage_bc_transposed(const BwdArgs& a, const uint16_t* src, int b, int g, int l0,
+                                                    uint16_t* T) {
+  const uint32_t row = (uint32_t)(a.G * a.N * 2);
+  const uint32_t left = (uint32_t)max(a.L - l0, 0);
+  const rsrc_t r = make_rsrc(src + ((size_t)b * a.L + l0) * a.G * a.N, left * row);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int u = threadIdx.x + 256 * it;
+    const int ng = u & 15, j = 2 * (u >> 4);
+    const bool nok = ng * 8 < a.N;
+    const uint32_t col = (uint32_t)((g * a.N + ng * 8) * 2);
+    const u32x4 r0 = buf_load_u32x4(r, nok ? (uint32_t)j * row + col : kOffNone);
+    const u32x4 r1 = buf_load_u32x4(r, nok ? (uint32_t)(j + 1) * row + col : kOffNone);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      *reinterpret_cast<uint32_t*>(&T[tsw(ng * 8 + 2 * k, j)]) = (r0[k] & 0xffffu) | (r1[k] << 16);
+      *reinterpret_cast<uint32_t*>(&T[tsw(ng * 8 + 2 * k + 1, j)]) = (r0[k] >> 16) | (r1[k] & 0xffff0000u);
+    }
+  }
+}
+
+// dyy = dy * silu(z) (dy without z) for steps (jx, jx+1) of the block, 8
+// headdim rows pg*8.. of virtual head vh; when `dz_out`, also writes dz.
+// Steps past L read 0 and their stores are dropped.
+__device__ __forceinline__ void load_dyy(const BwdArgs& a, int b, int vh, int l0, int jx, int pg, float (&v)[2][8],
+                                         bool dz_out) {
+  const uint32_t row = (uint32_t)(a.H * a.P);
+  const uint32_t left = (uint32_t)max(a.L - l0, 0);
+  const size_t base = ((size_t)b * a.L + l0) * row + vrow(a, vh);
+  const rsrc_t rdy = make_rsrc(a.dy + base, left * row * 4);
+  const rsrc_t rz = make_rsrc(a.z ? a.z + base : nullptr, a.z ? left * row * 2 : 0u);
+  const rsrc_t ryf = make_rsrc(a.z ? a.yf + base : nullptr, a.z ? left * row * 4 : 0u);
+  const rsrc_t rdz = make_rsrc(a.z ? a.dz + base : nullptr, a.z ? left * row * 4 : 0u);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t o = (uint32_t)(jx + s) * row + (uint32_t)pg * 8;
+    const f32x4 d0 = as_f32x4(buf_load_u32x4(rdy, o * 4)), d1 = as_f32x4(buf_load_u32x4(rdy, o * 4 + 16));
+    const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    if (a.z) {
+      const u32x4 zz = buf_load_u32x4(rz, o * 2);
+      float zv[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        zv[2 * k] = bf16_lo(zz[k]);
+        zv[2 * k + 1] = bf16_hi(zz[k]);
+      }
+      if (dz_out) {
+        const f32x4 y0 = as_f32x4(buf_load_u32x4(ryf, o * 4)), y1 = as_f32x4(buf_load_u32x4(ryf, o * 4 + 16));
+        const float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+        float dzv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float sg = sigmoid(zv[k]);
+          v[s][k] = dv[k] * (zv[k] * sg);
+          dzv[k] = dv[k] * yv[k] * (sg * (1.0f + zv[k] * (1.0f - sg)));
+        }
+        buf_store_u32x4(rdz, o * 4, as_u32x4(f32x4{dzv[0], dzv[1], dzv[2], dzv[3]}));
+        buf_store_u32x4(rdz, o * 4 + 16, as_u32x4(f32x4{dzv[4], dzv[5], dzv[6], dzv[7]}));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[s][k] = dv[k] * silu(zv[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[s][k] = dv[k];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2.  grid (nblk * Hv, batch), 256 threads: F^T = C^T (e o dyy) for one
+// (block, virtual head), e_i = exp(s_i), written over the workspace slot of
+// the block; wave w forms state rows w*32.. for both 32-row headdim tiles.
+__global__ void __launch_bounds__(256) ssd_bwd_local_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t gh[kP * kTRow];  // e o dyy, headdim rows (tsw): hi
+  __shared__ __attribute__((aligned(16))) uint16_t gl[kP * kTRow];  // lo
+  __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];  // C, state rows (tsw)
+  const int vh = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, b = blockIdx.y;
+  const int h = vh / a.ph, g = h / (a.H / a.G);
+  const int l0 = blk * kSub;
+  const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Dot2Masks dm = dot2_masks();
+  {
+    const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
+    float v[2][8];
+    load_dyy(a, b, vh, l0, jx, pg, v, true);
+    const float* ls = a.lsT + ((size_t)b * a.H + h) * a.Lp + l0 + jx;
+    const float e0 = exp2_fast(ls[0]), e1 = exp2_fast(ls[1]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t hi, lo;
+      split2(v[0][k] * e0, v[1][k] * e1, hi, lo, dm);
+      *reinterpret_cast<uint32_t*>(&gh[tsw(pg * 8 + k, jx)]) = hi;
+      *reinterpret_cast<uint32_t*>(&gl[tsw(pg * 8 + k, jx)]) = lo;
+    }
+  }
+  stage_bc_transposed(a, a.C, b, g, l0, CT);
+  __syncthreads();
+  const int nt = w;
+  if (nt * 32 >= a.N) return;
+  f32x16 acc[2] = {};
+#pragma unroll
+  for (int kk = 0; kk < kSub / 16; ++kk) {
+    const int j0 = kk * 16 + 8 * hf;
+    const u32x4 av = *reinterpret_cast<const u32x4*>(&CT[tsw(nt * 32 + lc, j0)]);
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      acc[pt] = mfma(av, *reinterpret_cast<const u32x4*>(&gh[tsw(pt * 32 + lc, j0)]), acc[pt]);
+      acc[pt] = mfma(av, *reinterpret_cast<const u32x4*>(&gl[tsw(pt * 32 + lc, j0)]), acc[pt]);
+    }
+  }
+  float* dst = a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh);
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt) store_stateT(acc[pt], dst, nt, pt, a.N, a.N);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3.  grid (ceil(16 N / 256) * Hv, batch), 256 threads, 4 state elements
+// per thread: from the last block to the first, the slot of block k receives
+// E_k (dh_last, or 0, for the last block) and E_{k-1} = exp2(ls_63(k)) E_k +
+// F_k; what arrives before block 0 is dh0.  Four blocks are loaded ahead.
+__global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
+  const int xb = (16 * a.N + 255) / 256;
+  const int vh = blockIdx.x / xb, b = blockIdx.y, h = vh / a.ph;
+  const int e = ((blockIdx.x % xb) * 256 + threadIdx.x) * 4;
+  if (e >= kP * a.N) return;
+  const size_t stride = (size_t)a.H * a.P * a.N;  // from one block's slot to the next
+  float* E0 = a.Eblk + sbase(a, (size_t)b * a.nblk, vh) + e;
+  const float* last = a.lsT + ((size_t)b * a.H + h) * a.Lp + (kSub - 1);  // + k*64: block k's decay (log2)
+  f32x4 E = a.dh_last ? *reinterpret_cast<const f32x4*>(a.dh_last + sbase(a, b, vh) + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 F[4];
+  float dq[4];
+  auto fetch = [&](int k, int s) {
+    if (k >= 0) {
+      F[s] = *reinterpret_cast<const f32x4*>(E0 + (size_t)k * stride);
+      dq[s] = last[(size_t)k * kSub];
+    }
+  };
+  int k = a.nblk - 1;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) fetch(k - s, s);
+  for (; k >= 0; k -= 4) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = k - s;
+      if (kk < 0) break;
+      const f32x4 f = F[s];
+      const float d = dq[s];
+      fetch(kk - 4, s);
+      *reinterpret_cast<f32x4*>(E0 + (size_t)kk * stride) = E;
+      E = E * exp2_fast(d) + f;
+    }
+  }
+  if (a.dh0) *reinterpret_cast<f32x4*>(a.dh0 + sbase(a, b, vh) + e) = E;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 4.  grid (nblk * Hv, batch), 256 threads: every gradient of one
+// (64-step block, virtual head).  Wave w = (q, sub), q = w >> 1 the half of
+// the block whose steps it owns as output columns, sub = w & 1.
+//   products 1: K(i, j) = C_i . B_j and W(i, j) = dyy_i . x_j for j in half q,
+//     i in halves >= q; their column sums of Z = M o K o W o delta (strictly
+//     below the diagonal); then M o K and M o W as bf16 hi/lo operands;
+//   products 2: (G B)^T for headdim half sub -> dx, x . (G B), dyy . x;
+//   products 3: (x^T G)^T for state tiles 2 sub, 2 sub + 1 -> dB part and
+//     B . (E^T x);
+//   products 4: W^T(j, i) and K^T(j, i) for i in half q, j in halves <= q (row
+//     sums of Z), then (h^T dyy)^T for the same state tiles -> dC part and
+//     C . (S_in^T dyy);
+//   then wave 0 (lane = step) assembles ddelta and the dA and dD parts.
+__global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t dyRh[kSub][kRowP];  // dyy, step rows: hi
+  __shared__ __attribute__((aligned(16))) uint16_t dyRl[kSub][kRowP];  // lo
+  __shared__ __attribute__((aligned(16))) uint16_t dyTh[kP * kTRow];   // dyy, headdim rows (tsw): hi
+  __shared__ __attribute__((aligned(16))) uint16_t dyTl[kP * kTRow];   // lo
+  __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];     // B, state rows (tsw)
+  __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];     // C, state rows (tsw)
+  __shared__ __attribute__((aligned(16))) float s_dl[kSub], s_ls[kSub], s_e[kSub], s_f[kSub];
+  __shared__ float s_col[kSub], s_row[kSub], s_T[2][kSub], s_U[2][kSub], s_c[2][kSub];
+  __shared__ float s_es[4], s_dd[4];
+
+  const int vh = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, b = blockIdx.y;
+  const int h = vh / a.ph, g = h / (a.H / a.G);
+  const int l0 = blk * kSub;
+  const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = w >> 1, sub = w & 1;
+  const Dot2Masks dm = dot2_masks();
+  const int nk = a.N / 16;  // 16-state k-steps
+  const uint32_t left = (uint32_t)max(a.L - l0, 0);
+  const uint32_t xrow = (uint32_t)(a.H * a.P), brow = (uint32_t)(a.G * a.N);
+  const size_t xbase = ((size_t)b * a.L + l0) * xrow + vrow(a, vh);
+  const size_t bbase = ((size_t)b * a.L + l0) * brow + (size_t)g * a.N;
+  const rsrc_t rx = make_rsrc(a.x + xbase, left * xrow * 2);
+  const rsrc_t rdy = make_rsrc(a.dy + xbase, left * xrow * 4);
+  const rsrc_t rz = make_rsrc(a.z ? a.z + xbase : nullptr, a.z ? left * xrow * 2 : 0u);
+  const rsrc_t rdx = make_rsrc(a.dx + xbase, left * xrow * 4);
+  const rsrc_t rb = make_rsrc(a.B + bbase, left * brow * 2);
+  const rsrc_t rc = make_rsrc(a.C + bbase, left * brow * 2);
+  const float* Ep = a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh);
+  const float* Sp = blk > 0 ? a.Sblk + sbase(a, (size_t)b * a.nblk + blk - 1, vh)
+                            : (a.h0 ? a.h0 + sbase(a, b, vh) : nullptr);
+  const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
+
+  // ---- stagings, <E, S_in>
+  if (w == 0) {
+    const size_t o = ((size_t)b * a.H + h) * a.Lp + l0 + lane;
+    const float d = a.dlT[o], ls = a.lsT[o];
+    const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
+    s_dl[lane] = d;
+    s_ls[lane] = ls;
+    s_e[lane] = exp2_fast(ls);
+    s_f[lane] = exp2_fast(ls63 - ls);
+  }
+  {
+    const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
+    float v[2][8];
+    load_dyy(a, b, vh, l0, jx, pg, v, false);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 hi, lo;
+      split8(v[s], hi, lo, dm);
+      *reinterpret_cast<u32x4*>(&dyRh[jx + s][pg * 8]) = hi;
+      *reinterpret_cast<u32x4*>(&dyRl[jx + s][pg * 8]) = lo;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t hi, lo;
+      split2(v[0][k], v[1][k], hi, lo, dm);
+      *reinterpret_cast<uint32_t*>(&dyTh[tsw(pg * 8 + k, jx)]) = hi;
+      *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
+    }
+  }
+  stage_bc_transposed(a, a.B, b, g, l0, BT);
+  stage_bc_transposed(a, a.C, b, g, l0, CT);
+  {
+    float es = 0.f;
+    if (Sp) {
+      for (int e4 = threadIdx.x; e4 < 16 * a.N; e4 += 256) {
+        const f32x4 ev = *reinterpret_cast<const f32x4*>(Ep + 4 * e4);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(Sp + 4 * e4);
+        es += ev[0] * sv[0] + ev[1] * sv[1] + ev[2] * sv[2] + ev[3] * sv[3];
+      }
+    }
+    es = wave_sum(es);
+    if (lane == 0) s_es[w] = es;
+  }
+  __syncthreads();
+
+  // ---- operand fragments
+  // B or C rows of step T*32 + lc, states kk*16 + 8hf .. +8 (A rows or B columns).
+  auto frag_bc = [&](rsrc_t r, int T, int kk) -> u32x4 {
+    return buf_load_u32x4(r, ((uint32_t)(T * 32 + lc) * brow + (uint32_t)(kk * 16 + 8 * hf)) * 2);
+  };
+  // x of step T*32 + lc, headdim rows kp*16 + 8hf .. +8.
+  auto frag_x = [&](int T, int kp) -> u32x4 {
+    return buf_load_u32x4(rx, ((uint32_t)(T * 32 + lc) * xrow + (uint32_t)(kp * 16 + 8 * hf)) * 2);
+  };
+  // State slice S [64][N]: rows p = PT*32 + lc, states kk*16 + 8hf .. +8, as hi/lo.
+  auto frag_srow = [&](const float* S, int PT, int kk, u32x4& hi, u32x4& lo) {
+    const float* s = S + (size_t)(PT * 32 + lc) * a.N + kk * 16 + 8 * hf;
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(s), v1 = *reinterpret_cast<const f32x4*>(s + 4);
+    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    split8(v, hi, lo, dm);
+  };
+  // State slice S [64][N]: state n = NT*32 + lc (0 past N), rows kp*16 + 8hf + t, as hi/lo.
+  auto frag_scol = [&](const float* S, int NT, int kp, u32x4& hi, u32x4& lo) {
+    const int n = NT * 32 + lc;
+    const bool ok = n < a.N;
+    const float* s = S + (size_t)(kp * 16 + 8 * hf) * a.N + (ok ? n : 0);
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = ok ? s[(size_t)t * a.N] : 0.f;
+    split8(v, hi, lo, dm);
+  };
+  auto lds4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
+
+  const int col = q * 32 + lc;  // this lane's output column: step (of the block) of every tile below
+  const float ls_c = s_ls[col], dl_c = s_dl[col];
+
+  auto body = [&](auto qtag) {
+    constexpr int Q = decltype(qtag)::value;
+    constexpr int NI = 2 - Q;  // row halves Q..1 (products 1)
+    constexpr int NJ = Q + 1;  // row halves 0..Q (products 4)
+
+    // ---- products 1: K and W, rows i in halves >= Q, columns j = col
+    u32x4 mkh[NI][2], mkl[NI][2], mwh[NI][2], mwl[NI][2];
+    {
+      f32x16 kacc[NI] = {}, wacc[NI] = {};
+      for (int kk = 0; kk < nk; ++kk) {
+        const u32x4 bop = frag_bc(rb, Q, kk);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) kacc[u] = mfma(frag_bc(rc, Q + u, kk), bop, kacc[u]);
+      }
+#pragma unroll
+      for (int kp = 0; kp < kP / 16; ++kp) {
+        const u32x4 xop = frag_x(Q, kp);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          wacc[u] = mfma(*reinterpret_cast<const u32x4*>(&dyRh[(Q + u) * 32 + lc][kp * 16 + 8 * hf]), xop, wacc[u]);
+          wacc[u] = mfma(*reinterpret_cast<const u32x4*>(&dyRl[(Q + u) * 32 + lc][kp * 16 + 8 * hf]), xop, wacc[u]);
+        }
+      }
+      // Column sums of Z below the diagonal (i > j).
+      float cs = 0.f;
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int i0 = (Q + u) * 32 + 8 * k4 + 4 * hf;
+          const f32x4 lsi = lds4(&s_ls[i0]);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const float m = (i0 + qq > col) ? exp2_fast(lsi[qq] - ls_c) : 0.f;
+            cs += m * kacc[u][4 * k4 + qq] * wacc[u][4 * k4 + qq];
+          }
+        }
+      }
+      cs = (cs + __shfl_xor(cs, 32)) * dl_c;
+      if (sub == 0 && hf == 0) s_col[col] = cs;
+      // M o K and M o W (i >= j) as operands: k = i, column j.
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        auto slice = [&](auto stag) {
+          constexpr int S = decltype(stag)::value;
+          float kv[8], wv[8];
+          acc_kslice<S>(kacc[u], kv);
+          acc_kslice<S>(wacc[u], wv);
+          const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
+          const f32x4 l0v = lds4(&s_ls[i0]), l1v = lds4(&s_ls[i0 + 4]);
+          const float lsi[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float m = (i0 + t >= col) ? exp2_fast(lsi[t] - ls_c) : 0.f;
+            kv[t] *= m;
+            wv[t] *= m;
+          }
+          split8(kv, mkh[u][S], mkl[u][S], dm);
+          split8(wv, mwh[u][S], mwl[u][S], dm);
+        };
+        slice(std::integral_constant<int, 0>{});
+        slice(std::integral_constant<int, 1>{});
+      }
+    }
+
+    // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
+    {
+      f32x16 gacc = {};
+      for (int kk = 0; kk < nk; ++kk) {
+        u32x4 eh, el;
+        frag_srow(Ep, sub, kk, eh, el);
+        const u32x4 bop = frag_bc(rb, Q, kk);
+        gacc = mfma(eh, bop, gacc);
+        gacc = mfma(el, bop, gacc);
+      }
+      gacc *= s_f[col];
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+#pragma unroll
+        for (int S = 0; S < 2; ++S) {
+          const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
+          const u32x4 ah = *reinterpret_cast<const u32x4*>(&dyTh[tsw(sub * 32 + lc, i0)]);
+          const u32x4 al = *reinterpret_cast<const u32x4*>(&dyTl[tsw(sub * 32 + lc, i0)]);
+          gacc = mfma(ah, mkh[u][S], gacc);
+          gacc = mfma(al, mkh[u][S], gacc);
+          gacc = mfma(ah, mkl[u][S], gacc);
+        }
+      }
+      // dx, x . (G B) and dyy . x for (step col, rows p).
+      float cp = 0.f, dd = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const uint32_t o = (uint32_t)col * xrow + (uint32_t)(sub * 32 + 8 * k4 + 4 * hf);
+        const f32x4 dyv = as_f32x4(buf_load_u32x4(rdy, o * 4));
+        const u32x2 xx = buf_load_u32x2(rx, o * 2);
+        const float xv[4] = {bf16_lo(xx[0]), bf16_hi(xx[0]), bf16_lo(xx[1]), bf16_hi(xx[1])};
+        float sz[4] = {1.f, 1.f, 1.f, 1.f};
+        if (a.z) {
+          const u32x2 zz = buf_load_u32x2(rz, o * 2);
+          sz[0] = silu(bf16_lo(zz[0]));
+          sz[1] = silu(bf16_hi(zz[0]));
+          sz[2] = silu(bf16_lo(zz[1]));
+          sz[3] = silu(bf16_hi(zz[1]));
+        }
+        f32x4 dxv;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float gb = gacc[4 * k4 + qq], dyy = dyv[qq] * sz[qq];
+          cp += xv[qq] * gb;
+          dd += dyy * xv[qq];
+          dxv[qq] = dl_c * gb + Dh * dyy;
+        }
+        buf_store_u32x4(rdx, o * 4, as_u32x4(dxv));
+      }
+      cp += __shfl_xor(cp, 32);
+      if (hf == 0) s_c[sub][col] = cp;
+      dd = wave_sum(dd);
+      if (lane == 0) s_dd[w] = dd;
+    }
+
+    // ---- products 3: (x^T G)^T, state tiles 2 sub + v, columns col
+    {
+      float up = 0.f;
+      const size_t prow = ((size_t)b * a.L + l0 + col) * a.Hv + vh;  // this column's row of the parts
+      const bool in = l0 + col < a.L;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int NT = 2 * sub + v;
+        if (NT * 32 >= a.N) continue;
+        f32x16 xacc = {};
+#pragma unroll
+        for (int kp = 0; kp < kP / 16; ++kp) {
+          u32x4 eh, el;
+          frag_scol(Ep, NT, kp, eh, el);
+          const u32x4 xop = frag_x(Q, kp);
+          xacc = mfma(eh, xop, xacc);
+          xacc = mfma(el, xop, xacc);
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int n0 = NT * 32 + 8 * k4 + 4 * hf;
+          const u32x2 bb = buf_load_u32x2(rb, n0 < a.N ? ((uint32_t)col * brow + (uint32_t)n0) * 2 : kOffNone);
+          up += xacc[4 * k4] * bf16_lo(bb[0]) + xacc[4 * k4 + 1] * bf16_hi(bb[0]) +
+                xacc[4 * k4 + 2] * bf16_lo(bb[1]) + xacc[4 * k4 + 3] * bf16_hi(bb[1]);
+        }
+        xacc *= s_f[col];
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+#pragma unroll
+          for (int S = 0; S < 2; ++S) {
+            const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
+            const u32x4 av = *reinterpret_cast<const u32x4*>(&CT[tsw(NT * 32 + lc, i0)]);
+            xacc = mfma(av, mwh[u][S], xacc);
+            xacc = mfma(av, mwl[u][S], xacc);
+          }
+        }
+        if (in) {
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int n0 = NT * 32 + 8 * k4 + 4 * hf;
+            if (n0 < a.N)
+              *reinterpret_cast<f32x4*>(a.dBp + prow * a.N + n0) =
+                  dl_c * f32x4{xacc[4 * k4], xacc[4 * k4 + 1], xacc[4 * k4 + 2], xacc[4 * k4 + 3]};
+          }
+        }
+      }
+      up += __shfl_xor(up, 32);
+      if (hf == 0) s_U[sub][col] = up;
+    }
+
+    // ---- products 4: W^T and K^T (rows j in halves <= Q, columns i = col),
+    // then (h^T dyy)^T for state tiles 2 sub + v.
+    {
+      u32x4 mth[NJ][2], mtl[NJ][2];
+      {
+        f32x16 wt[NJ] = {}, kt[NJ] = {};
+#pragma unroll
+        for (int kp = 0; kp < kP / 16; ++kp) {
+          const u32x4 dh = *reinterpret_cast<const u32x4*>(&dyRh[col][kp * 16 + 8 * hf]);
+          const u32x4 dl = *reinterpret_cast<const u32x4*>(&dyRl[col][kp * 16 + 8 * hf]);
+#pragma unroll
+          for (int u = 0; u < NJ; ++u) {
+            const u32x4 xa = frag_x(u, kp);
+            wt[u] = mfma(xa, dh, wt[u]);
+            wt[u] = mfma(xa, dl, wt[u]);
+          }
+        }
+        for (int kk = 0; kk < nk; ++kk) {
+          const u32x4 cop = frag_bc(rc, Q, kk);
+#pragma unroll
+          for (int u = 0; u < NJ; ++u) kt[u] = mfma(frag_bc(rb, u, kk), cop, kt[u]);
+        }
+        // Row sums of Z left of the diagonal (j < i).
+        float rs = 0.f;
+#pragma unroll
+        for (int u = 0; u < NJ; ++u) {
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int j0 = u * 32 + 8 * k4 + 4 * hf;
+            const f32x4 lsj = lds4(&s_ls[j0]), dlj = lds4(&s_dl[j0]);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const float m = (j0 + qq < col) ? exp2_fast(ls_c - lsj[qq]) * dlj[qq] : 0.f;
+              rs += m * wt[u][4 * k4 + qq] * kt[u][4 * k4 + qq];
+            }
+          }
+        }
+        rs += __shfl_xor(rs, 32);
+        if (sub == 0 && hf == 0) s_row[col] = rs;
+        // M o W^T o delta_j (j <= i) as operands: k = j, column i.
+#pragma unroll
+        for (int u = 0; u < NJ; ++u) {
+          auto slice = [&](auto stag) {
+            constexpr int S = decltype(stag)::value;
+            float v[8];
+            acc_kslice<S>(wt[u], v);
+            const int j0 = u * 32 + 16 * S + 8 * hf;
+            const f32x4 l0v = lds4(&s_ls[j0]), l1v = lds4(&s_ls[j0 + 4]);
+            const f32x4 d0v = lds4(&s_dl[j0]), d1v = lds4(&s_dl[j0 + 4]);
+            const float lsj[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
+            const float dlj[8] = {d0v[0], d0v[1], d0v[2], d0v[3], d1v[0], d1v[1], d1v[2], d1v[3]};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] *= (j0 + t <= col) ? exp2_fast(ls_c - lsj[t]) * dlj[t] : 0.f;
+            split8(v, mth[u][S], mtl[u][S], dm);
+          };
+          slice(std::integral_constant<int, 0>{});
+          slice(std::integral_constant<int, 1>{});
+        }
+      }
+      float tp = 0.f;
+      const size_t prow = ((size_t)b * a.L + l0 + col) * a.Hv + vh;
+      const bool in = l0 + col < a.L;
+      const float ec = s_e[col];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int NT = 2 * sub + v;
+        if (NT * 32 >= a.N) continue;
+        f32x16 cacc = {};
+        if (Sp) {
+#pragma unroll
+          for (int kp = 0; kp < kP / 16; ++kp) {
+            u32x4 sh, sl;
+            frag_scol(Sp, NT, kp, sh, sl);
+            const u32x4 bh = *reinterpret_cast<const u32x4*>(&dyRh[col][kp * 16 + 8 * hf]);
+            const u32x4 bl = *reinterpret_cast<const u32x4*>(&dyRl[col][kp * 16 + 8 * hf]);
+            cacc = mfma(sh, bh, cacc);
+            cacc = mfma(sh, bl, cacc);
+            cacc = mfma(sl, bh, cacc);
+          }
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int n0 = NT * 32 + 8 * k4 + 4 * hf;
+            const u32x2 cc = buf_load_u32x2(rc, n0 < a.N ? ((uint32_t)col * brow + (uint32_t)n0) * 2 : kOffNone);
+            tp += cacc[4 * k4] * bf16_lo(cc[0]) + cacc[4 * k4 + 1] * bf16_hi(cc[0]) +
+                  cacc[4 * k4 + 2] * bf16_lo(cc[1]) + cacc[4 * k4 + 3] * bf16_hi(cc[1]);
+          }
+          cacc *= ec;
+        }
+#pragma unroll
+        for (int u = 0; u < NJ; ++u) {
+#pragma unroll
+          for (int S = 0; S < 2; ++S) {
+            const int j0 = u * 32 + 16 * S + 8 * hf;
+            const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[tsw(NT * 32 + lc, j0)]);
+            cacc = mfma(av, mth[u][S], cacc);
+            cacc = mfma(av, mtl[u][S], cacc);
+          }
+        }
+        if (in) {
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int n0 = NT * 32 + 8 * k4 + 4 * hf;
+            if (n0 < a.N)
+              *reinterpret_cast<f32x4*>(a.dCp + prow * a.N + n0) =
+                  f32x4{cacc[4 * k4], cacc[4 * k4 + 1], cacc[4 * k4 + 2], cacc[4 * k4 + 3]};
+          }
+        }
+      }
+      tp += __shfl_xor(tp, 32);
+      if (hf == 0) s_T[sub][col] = tp;
+    }
+  };
+  if (q == 0)
+    body(std::integral_constant<int, 0>{});
+  else
+    body(std::integral_constant<int, 1>{});
+  __syncthreads();
+
+  // ---- ddelta and the dA, dD parts (lane = step of the block)
+  if (w == 0) {
+    const int t = lane;
+    const float dl = s_dl[t], e = s_e[t], f = s_f[t];
+    const float cprime = s_c[0][t] + s_c[1][t];
+    const float cr = s_col[t] - s_row[t];
+    const float corner = wave_prefix_sum(cr) - cr;  // R_t: sum over u < t
+    const float et = e * (s_T[0][t] + s_T[1][t]);
+    const float pt = wave_prefix_sum(et);
+    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pt), 63));
+    const float suffix = tot - (pt - et);  // sum over i >= t
+    const float fu = f * dl * (s_U[0][t] + s_U[1][t]);
+    const float prefix = wave_prefix_sum(fu) - fu;  // sum over j < t
+    const float dq63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), 63));
+    const float es = (s_es[0] + s_es[1]) + (s_es[2] + s_es[3]);
+    const float gh = corner + suffix + prefix + dq63 * es;  // <G_t, exp(delta_t A) h_{t-1}>
+    if (l0 + t < a.L) a.ddp[((size_t)b * a.L + l0 + t) * a.Hv + vh] = cprime + Ah * gh;
+    const float da = wave_sum(dl * gh);
+    if (lane == 0) {
+      const size_t o = ((size_t)b * a.nblk + blk) * a.Hv + vh;
+      a.dAp[o] = da;
+      a.dDp[o] = (s_dd[0] + s_dd[1]) + (s_dd[2] + s_dd[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 5: fixed-order sums of the per-virtual-head parts.
+// dB and dC: grid-stride over (b, l, g, 4 states), the group's virtual heads
+// summed in order.
+__global__ void __launch_bounds__(256) ssd_bwd_reduce_bc_kernel(BwdArgs a) {
+  const int n4s = a.N / 4;
+  const int hvg = a.Hv / a.G;
+  const size_t total = (size_t)a.batch * a.L * a.G * n4s;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (size_t)gridDim.x * 256) {
+    const int n4 = (int)(idx % n4s);
+    const size_t rest = idx / n4s;
+    const int g = (int)(rest % a.G);
+    const size_t bl = rest / a.G;  // b*L + l
+    const size_t src = (bl * a.Hv + (size_t)g * hvg) * a.N + 4 * n4;
+    f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < hvg; ++v) {
+      sb += *reinterpret_cast<const f32x4*>(a.dBp + src + (size_t)v * a.N);
+      sc += *reinterpret_cast<const f32x4*>(a.dCp + src + (size_t)v * a.N);
+    }
+    const size_t dst = (bl * a.G + g) * a.N + 4 * n4;
+    *reinterpret_cast<f32x4*>(a.dB + dst) = sb;
+    *reinterpret_cast<f32x4*>(a.dC + dst) = sc;
+  }
+}
+
+// ddelta: grid-stride over (b, l, h), the head's ph virtual heads in order.
+__global__ void __launch_bounds__(256) ssd_bwd_reduce_dd_kernel(BwdArgs a) {
+  const size_t total = (size_t)a.batch * a.L * a.H;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (size_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int r = 0; r < a.ph; ++r) s += a.ddp[idx * a.ph + r];
+    a.ddelta[idx] = s;
+  }
+}
+
+// dA and dD: one workgroup per head; thread k sums parts k, k+256, ... in
+// order, then a fixed tree over the threads.
+__global__ void __launch_bounds__(256) ssd_bwd_reduce_head_kernel(BwdArgs a) {
+  __shared__ float sa[256], sd[256];
+  const int h = blockIdx.x;
+  const int items = a.batch * a.nblk * a.ph;
+  float va = 0.f, vd = 0.f;
+  for (int i = threadIdx.x; i < items; i += 256) {
+    const size_t o = (size_t)(i / a.ph) * a.Hv + (size_t)h * a.ph + i % a.ph;
+    va += a.dAp[o];
+    vd += a.dDp[o];
+  }
+  sa[threadIdx.x] = va;
+  sd[threadIdx.x] = vd;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      sa[threadIdx.x] += sa[threadIdx.x + s];
+      sd[threadIdx.x] += sd[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.dA[h] = sa[0];
+    if (a.dD) a.dD[h] = sd[0];
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t fwd, yf, Sblk, Eblk, dBp, dCp, ddp, dAp, dDp, total;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                     int64_t dstate) {
+  const int64_t nblk = (seqlen + kSub - 1) / kSub;
+  const int64_t vheads = nheads * (headdim / kP);
+  const size_t f4 = sizeof(float);
+  BwdLayout l;
+  l.fwd = 0;  // the forward's workspace (its status word first)
+  l.yf = align256(ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, kSub));
+  l.Sblk = l.yf + align256((size_t)batch * seqlen * nheads * headdim * f4);
+  l.Eblk = l.Sblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
+  l.dBp = l.Eblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
+  l.dCp = l.dBp + align256((size_t)batch * seqlen * vheads * dstate * f4);
+  l.ddp = l.dCp + align256((size_t)batch * seqlen * vheads * dstate * f4);
+  l.dAp = l.ddp + align256((size_t)batch * seqlen * vheads * f4);
+  l.dDp = l.dAp + align256((size_t)batch * nblk * vheads * f4);
+  l.total = l.dDp + align256((size_t)batch * nblk * vheads * f4);
+  return l;
+}
+
+unsigned stride_grid(size_t total) {
+  return (unsigned)std::max<size_t>(1, std::min<size_t>((total + 255) / 256, 16384));
+}
+
+}  // namespace
+
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                               int64_t dstate) {
+  return bwd_layout(batch, seqlen, nheads, headdim, ngroups, dstate).total;
+}
+
+hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream) {
+  const BwdLayout l = bwd_layout(p.batch, p.seqlen, p.nheads, p.headdim, p.ngroups, p.dstate);
+  char* ws = static_cast<char*>(p.workspace);
+  // Pass 1: the forward with 64-step chunks, ungated, keeping every block's state.
+  SSDParams f;
+  f.x = p.x;
+  f.delta = p.delta;
+  f.A = p.A;
+  f.B = p.B;
+  f.C = p.C;
+  f.D = p.D;
+  f.z = nullptr;
+  f.h0 = p.h0;
+  f.y = reinterpret_cast<float*>(ws + l.yf);
+  f.chunk_states = reinterpret_cast<float*>(ws + l.Sblk);
+  f.h_last = nullptr;
+  f.batch = p.batch;
+  f.seqlen = p.seqlen;
+  f.nheads = p.nheads;
+  f.headdim = p.headdim;
+  f.ngroups = p.ngroups;
+  f.dstate = p.dstate;
+  f.chunk = kSub;
+  f.workspace = ws + l.fwd;
+  hipError_t err = launch_ssd(f, stream);
+  if (err != hipSuccess) return err;
+
+  BwdArgs a;
+  a.x = static_cast<const uint16_t*>(p.x);
+  a.A = p.A;
+  a.B = static_cast<const uint16_t*>(p.B);
+  a.C = static_cast<const uint16_t*>(p.C);
+  a.D = p.D;
+  a.z = static_cast<const uint16_t*>(p.z);
+  a.h0 = p.h0;
+  a.dy = p.dy;
+  a.dh_last = p.dh_last;
+  a.dx = p.dx;
+  a.dz = p.dz;
+  a.ddelta = p.ddelta;
+  a.dA = p.dA;
+  a.dB = p.dB;
+  a.dC = p.dC;
+  a.dD = p.dD;
+  a.dh0 = p.dh0;
+  size_t dl_off, ls_off;
+  ssd_delta_rows(p.batch, p.seqlen, p.nheads, p.headdim, kSub, dl_off, ls_off);
+  a.dlT = reinterpret_cast<const float*>(ws + l.fwd + dl_off);
+  a.lsT = reinterpret_cast<const float*>(ws + l.fwd + ls_off);
+  a.yf = reinterpret_cast<const float*>(ws + l.yf);
+  a.Sblk = reinterpret_cast<const float*>(ws + l.Sblk);
+  a.Eblk = reinterpret_cast<float*>(ws + l.Eblk);
+  a.dBp = reinterpret_cast<float*>(ws + l.dBp);
+  a.dCp = reinterpret_cast<float*>(ws + l.dCp);
+  a.ddp = reinterpret_cast<float*>(ws + l.ddp);
+  a.dAp = reinterpret_cast<float*>(ws + l.dAp);
+  a.dDp = reinterpret_cast<float*>(ws + l.dDp);
+  a.batch = (int)p.batch;
+  a.L = (int)p.seqlen;
+  a.H = (int)p.nheads;
+  a.G = (int)p.ngroups;
+  a.P = (int)p.headdim;
+  a.ph = (int)(p.headdim / kP);
+  a.Hv = a.H * a.ph;
+  a.N = (int)p.dstate;
+  a.nblk = (int)((p.seqlen + kSub - 1) / kSub);
+  a.Lp = a.nblk * kSub;
+
+  const dim3 blocks((unsigned)a.nblk * (unsigned)a.Hv, (unsigned)a.batch);
+  hipLaunchKernelGGL(ssd_bwd_local_kernel, blocks, dim3(256), 0, stream, a);
+  const unsigned xb = (unsigned)((16 * a.N + 255) / 256);
+  hipLaunchKernelGGL(ssd_bwd_chain_kernel, dim3(xb * (unsigned)a.Hv, (unsigned)a.batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_grad_kernel, blocks, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.G * (a.N / 4))), dim3(256),
+                     0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_reduce_dd_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.H)), dim3(256), 0, stream,
+                     a);
+  hipLaunchKernelGGL(ssd_bwd_reduce_head_kernel, dim3((unsigned)a.H), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mss

@@ -33,6 +33,7 @@ import numpy as np
 # Tensor ids for the per-tensor child streams.
 TID_U, TID_DNOISE, TID_DT, TID_B, TID_C, TID_Z, TID_D, TID_H0, TID_A, TID_X, TID_DY, TID_CONVW, TID_CONVB = range(1, 14)
 TID_THETA = 14
+TID_DHL = 15
 
 SEED_BASE = 27000
 
@@ -337,6 +338,17 @@ def ssd_inputs(cfg: SSDConfig, with_h0: bool = False) -> dict:
         "B": f32_to_bf16_bits(_normal(s, TID_B, (b, L, G, N))),
         "C": f32_to_bf16_bits(_normal(s, TID_C, (b, L, G, N))),
         "h0": (0.1 * _normal(s, TID_H0, (b, H, P, N))).astype(np.float32) if with_h0 else None,
+    }
+
+
+def ssd_grad_output(cfg: SSDConfig, with_dh_last: bool = False) -> dict:
+    """Loss gradients for the SSD backward: dy = dloss/dy [b, l, h, p] ~ N(0, 1)
+    fp32 (the forward's output dtype) and dh_last = dloss/dh_last [b, h, p, n]
+    ~ 0.1 N(0, 1) fp32 (optional)."""
+    b, L, H, P, N, s = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.seed
+    return {
+        "dy": _normal(s, TID_DY, (b, L, H, P)),
+        "dh_last": (0.1 * _normal(s, TID_DHL, (b, H, P, N))).astype(np.float32) if with_dh_last else None,
     }
 
 

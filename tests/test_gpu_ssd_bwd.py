@@ -1,0 +1,212 @@
+"""GPU parity of mss_ssd_chunk_bwd (gradient through the Mamba-2 SSD layer)
+against the fp64 oracle (oracle.ssd_bwd: the reverse-time adjoint of the
+plain per-step recurrence, no blocking).  Inputs x, B, C, z are bf16 (widened
+exactly for the oracle); delta, A, D, h0, dy, dh_last and every gradient are
+fp32.
+
+Tolerance: max |g - r| / max(|r|, rms(r)) <= 2e-3 per gradient tensor.  The
+arithmetic is fp32 with matrix-core operands split into bf16 hi/lo pairs
+(each product carries ~2^-16 relative error); the gradients are sums of up
+to L (dA, dD: batch x L) such products of either sign, so errors of a few
+1e-5 of the tensor's scale are expected, and the sums over time (ddelta's
+decay term, dA) lose a further digit to cancellation.  The measured errors
+are printed."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_27_amd as mss
+from selective_state_space_27_amd import inputs as I
+from gpu_util import dev, host64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+NAMES = ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0")
+
+
+def gen(b, L, H, G, P=64, N=128, seed=11, with_d=False, with_z=False, with_h0=False, with_dhl=False):
+    cfg = I.small_ssd_config(b, L, H, P, G, N, 64, seed=I.SEED_BASE + 300 + seed)
+    x = I.ssd_inputs(cfg, with_h0=with_h0)
+    g = np.random.default_rng(cfg.seed + 1)
+    x["D"] = g.standard_normal(H).astype(np.float32) if with_d else None
+    x["z"] = I.f32_to_bf16_bits(g.standard_normal((b, L, H, P)).astype(np.float32)) if with_z else None
+    x.update(I.ssd_grad_output(cfg, with_dh_last=with_dhl))
+    return cfg, x
+
+
+def run_gpu(x, **kw):
+    g = mss.ssd_chunk_bwd(dev(x["x"]), dev(x["delta"]), dev(x["A"]), dev(x["B"]), dev(x["C"]), dev(x["D"]),
+                          dev(x["z"]), dev(x["h0"]), dy=dev(x["dy"]), dh_last=dev(x["dh_last"]), **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def run_oracle(x, heads=None, dy=None):
+    sel = slice(None) if heads is None else heads
+    f64 = lambda a: None if a is None else I.to_f64(a, "bf16")
+    return oracle.ssd_bwd(f64(x["x"])[:, :, sel], x["delta"][:, :, sel], x["A"][sel], f64(x["B"]), f64(x["C"]),
+                          None if x["D"] is None else x["D"][sel], None if x["z"] is None else f64(x["z"])[:, :, sel],
+                          None if x["h0"] is None else x["h0"][:, sel], (x["dy"] if dy is None else dy)[:, :, sel],
+                          None if x["dh_last"] is None else x["dh_last"][:, sel])
+
+
+def compare(g, r, what, names=NAMES):
+    errs = {}
+    for k in names:
+        if r.get(k) is None:
+            assert g.get(k) is None, f"{what}: {k} returned without its input"
+            continue
+        errs[k] = rel_err(host64(g[k]), r[k])
+    print(f"{what}: " + " ".join(f"{k} {e:.2e}" for k, e in errs.items()))
+    bad = {k: e for k, e in errs.items() if not e <= TOL}
+    assert not bad, f"{what}: max rel err above {TOL:.0e}: {bad}"
+    return errs
+
+
+CASES = [
+    # b, L, H, G, P, N, D, z, h0, dh_last
+    (1, 64, 2, 1, 64, 128, False, False, False, False),   # exactly one block
+    (1, 128, 2, 1, 64, 128, True, True, True, True),      # two blocks, everything optional given
+    (2, 300, 4, 2, 64, 128, True, False, True, False),    # ragged L, two groups
+    (1, 77, 3, 1, 64, 128, False, True, False, True),     # ragged, shorter than two blocks
+    (1, 1, 2, 1, 64, 128, True, True, True, True),        # a single step
+    (2, 65, 8, 4, 64, 128, True, False, False, False),    # one step past a block, four groups
+    (1, 200, 4, 4, 64, 128, False, True, True, False),    # one head per group
+    (1, 300, 3, 1, 128, 128, True, True, True, True),     # headdim 128: two 64-row halves per head
+    (2, 517, 4, 2, 64, 64, True, False, True, True),      # narrower states
+    (1, 333, 4, 1, 64, 16, False, True, True, False),
+    (2, 130, 6, 2, 64, 48, True, True, False, True),
+    (1, 257, 2, 1, 128, 48, True, False, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}l{}h{}g{}p{}n{}".format(*c[:6]))
+def test_ssd_bwd_small(case):
+    """Every element of every gradient against the oracle."""
+    b, L, H, G, P, N, d, z, h0, dhl = case
+    cfg, x = gen(b, L, H, G, P, N, with_d=d, with_z=z, with_h0=h0, with_dhl=dhl)
+    g = run_gpu(x)
+    r = run_oracle(x)
+    if x["D"] is None:
+        r["dD"] = None
+        g["dD"] = None  # computed at D = 0 (checked below)
+    compare(g, r, str(case))
+
+
+def test_ssd_bwd_dD_at_zero_and_optional_outputs():
+    """Without D, dD is the gradient at D = 0 (sum of dout . x); dD and dh0
+    may be skipped; a second call through `out` writes the same values."""
+    cfg, x = gen(1, 200, 4, 1, with_z=True, with_h0=True)
+    g = run_gpu(x)
+    r = run_oracle(x)
+    x0 = dict(x, D=np.zeros(4, np.float32))
+    r0 = run_oracle(x0)
+    assert rel_err(host64(g["dD"]), r0["dD"]) <= TOL
+    g2 = run_gpu(x, want_dD=False, want_dh0=False)
+    assert g2["dD"] is None and g2["dh0"] is None
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dz"):
+        assert torch.equal(g[k], g2[k]), k
+    g3 = run_gpu(x, out=g2)
+    assert g3 is g2
+    compare(g3, r, "through out", names=("dx", "ddelta", "dA", "dB", "dC", "dz"))
+
+
+def test_ssd_bwd_decay_regimes():
+    """Fast decay (A = -16, delta ~ 0.5: whole blocks decay to nothing) and a
+    growing state (A > 0) on one tensor, with h0 and dh_last."""
+    cfg, x = gen(1, 256, 4, 1, with_h0=True, with_dhl=True, with_d=True)
+    x["A"] = np.array([-16.0, -1.0, 0.05, -0.001], np.float32)
+    x["delta"] = x["delta"].copy()
+    x["delta"][:, :, 0] = 0.5
+    g = run_gpu(x)
+    r = run_oracle(x)
+    compare(g, r, "decay regimes")
+
+
+def test_ssd_bwd_deterministic():
+    """Every sum runs in a fixed order: repeated calls are bitwise equal."""
+    cfg, x = gen(2, 700, 8, 2, with_d=True, with_z=True, with_h0=True, with_dhl=True)
+    g1 = run_gpu(x)
+    g2 = run_gpu(x)
+    for k in NAMES:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_ssd_bwd_many_heads_per_group():
+    """2048 steps, 16 heads in one group: dB and dC sum 16 heads' parts."""
+    cfg, x = gen(2, 2048, 16, 1, with_d=True, with_z=True, with_h0=True, with_dhl=True)
+    g = run_gpu(x)
+    r = run_oracle(x)
+    compare(g, r, "b2 l2048 h16 g1")
+
+
+def _full_inputs():
+    cfg = I.SSD_2P8B
+    x = I.ssd_inputs(cfg)
+    x["D"] = x["z"] = None
+    x.update(I.ssd_grad_output(cfg))
+    return cfg, x
+
+
+def test_ssd_bwd_2p8b_one_head_full():
+    """b=2, L=16384, H=80, P=64, N=128 (the backward bench workload, same
+    launch): dy nonzero on one head only, so dB and dC are that head's
+    contribution alone.  Every element of dx, ddelta, dh0 (that head; the
+    other heads' are exactly 0), dA, dD, dB and dC against the oracle run on
+    that head."""
+    cfg, x = _full_inputs()
+    h = 37
+    dy = np.zeros_like(x["dy"])
+    dy[:, :, h] = x["dy"][:, :, h]
+    x["dy"] = dy
+    g = run_gpu(x)
+    r = run_oracle(x, heads=np.array([h]))
+    for k in ("dx", "ddelta", "dh0"):
+        full = g[k]
+        g[k] = full[:, :, h:h + 1] if k != "dh0" else full[:, h:h + 1]
+        rest = torch.cat([full[:, :, :h], full[:, :, h + 1:]], 2) if k != "dh0" else \
+            torch.cat([full[:, :h], full[:, h + 1:]], 1)
+        assert not bool(rest.any()), f"{k} nonzero outside the head"
+    g["dA"] = g["dA"][h:h + 1]
+    g["dD"] = None
+    r["dD"] = None
+    compare(g, r, "ssd_2p8b, one head")
+
+
+def test_ssd_bwd_2p8b_all_heads_linear_functionals():
+    """The same workload with dy on every head.  y and h_last are linear in
+    each of x, B, C and h0 separately, so for a direction V the gradient's
+    inner product with V equals <dy, y(V)> (+ <dh_last, h_last(V)>) with V in
+    that input's place and the other linear terms dropped: four exact
+    identities at full size, evaluated with the fp64 oracle forward.  The
+    bound is TOL * sum_i max(|g_i|, rms(g)) |V_i| (the error rel_err allows,
+    summed)."""
+    cfg, x = _full_inputs()
+    x["dh_last"] = (0.1 * np.random.default_rng(5).standard_normal((2, 80, 64, 128))).astype(np.float32)
+    g = run_gpu(x)
+    rng = np.random.default_rng(7)
+    f64 = lambda a: I.to_f64(a, "bf16")
+    X, Bm, Cm = f64(x["x"]), f64(x["B"]), f64(x["C"])
+    dy, dhl = x["dy"].astype(np.float64), x["dh_last"].astype(np.float64)
+
+    def fwd(xx, B, C, h0):
+        y, _, hl = oracle.ssd(xx, x["delta"], x["A"], B, C, None, None, h0)
+        return float(np.sum(dy * y) + np.sum(dhl * hl))
+
+    checks = {
+        "dx": lambda V: fwd(V, Bm, Cm, None),
+        "dB": lambda V: fwd(X, V, Cm, None),
+        "dC": lambda V: fwd(X, Bm, V, None) - fwd(X, Bm, np.zeros_like(Cm), None),
+        "dh0": lambda V: fwd(np.zeros_like(X), Bm, Cm, V),
+    }
+    shapes = {"dx": X.shape, "dB": Bm.shape, "dC": Cm.shape, "dh0": (2, 80, 64, 128)}
+    for k, f in checks.items():
+        V = rng.standard_normal(shapes[k])
+        gk = host64(g[k])
+        got = float(np.sum(gk * V))
+        ref = f(V)
+        scale = float(np.sum(np.maximum(np.abs(gk), np.sqrt(np.mean(gk * gk))) * np.abs(V)))
+        print(f"<{k}, V>: {got:.9e} vs {ref:.9e}, |diff| / scale {abs(got - ref) / scale:.2e}")
+        assert abs(got - ref) <= TOL * scale, k
