@@ -21,6 +21,8 @@ Other workloads (measured for the record, not the headline):
                64 channels) x N128 x L16384, A and delta shared within a head
   scan_2p8b_bwd  the backward (gradients of u, delta, A, B, C, D, z) of the
                headline scan, one mss_selective_scan_bwd call per step
+  ssd_2p8b_bwd the backward of ssd_2p8b (gradients of x, delta, A, B, C), one
+               mss_ssd_chunk_bwd call per step
   scan_2p8b_fused  the headline scan fed by its prologue (u from the silu of
                the causal 4-tap convolution of x, delta = softplus(raw + bias))
   decode_m3    Mamba-3 generation: b128 x 80 heads x P64 x N128, MIMO rank 4,
@@ -69,8 +71,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scan_2p8b",
-                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "scan_m2shape", "scan_2p8b_bwd",
-                             "scan_2p8b_fused", "decode_m3", "copy"])
+                    choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "ssd_2p8b_bwd", "scan_m2shape",
+                             "scan_2p8b_bwd", "scan_2p8b_fused", "decode_m3", "copy"])
     ap.add_argument("--seqlen", type=int, default=0,
                     help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
     ap.add_argument("--batch", type=int, default=0,
@@ -142,6 +144,26 @@ def mamba3_step_bytes(cfg, es):
     state = b * H * P * N * 4 * (2 if cfg.complex_state else 1)
     return (2 * state + (4 if cfg.trapezoid else 3) * b * H * R * P * es + (3 if cfg.trapezoid else 2) * b * G * R * N * es
             + b * H * 4 + 2 * H * 4 + (H * N * 4 if cfg.complex_state else 0))
+
+
+def ssd_bwd_mfma_flops(b, L, H, P, N):
+    """Dense-tile matrix flops of the SSD backward: the forward pass with
+    64-step chunks (ssd_mfma_flops), then per 64-step block and head the
+    block's adjoint part C^T (e dy) (N x P over 64), W = dy x^T (64x64 over
+    P), (G B)^T = E B^T + dy^T (M o K) (P x 64 over N and over 64),
+    (x^T G)^T = E^T x^T + C^T (M o W) (N x 64 over P and over 64) and
+    (h^T dy)^T = S^T dy^T + B^T (M o W^T) (N x 64 over P and over 64), plus
+    K = C B^T per block and group (64x64 over N)."""
+    blocks = b * (-(-L // 64))
+    per_head = 4 * (2 * N * P * 64) + 2 * (2 * 64 * 64 * P) + 2 * (2 * N * 64 * 64)
+    return ssd_mfma_flops(b, L, H, P, N, 64) + blocks * (H * per_head + 2 * 64 * 64 * N)
+
+
+def ssd_bwd_bytes(b, L, H, P, G, N, es):
+    """Algorithmic bytes of the SSD backward: x, B, C read once (bf16), delta,
+    dy read once (fp32), A read once; dx, ddelta, dB, dC, dA written once
+    (fp32)."""
+    return (b * L * H * P * (es + 4 + 4) + b * L * H * 8 + b * L * G * N * (2 * es + 2 * 4) + 2 * H * 4)
 
 
 def ssd_bytes(b, L, H, P, G, N, es):
@@ -535,7 +557,49 @@ def bench_ssd(args, torch, mss, I):
                       lambda: oracle.ssd(*one, threads=1), L * h1 * P * N, "state updates/s", th, info,
                       f"the whole workload (b={b}, L={L}, all heads)", f"batch row 0, heads 0..{h1 - 1}")
     res["mfma_flops"] = ssd_mfma_flops(b, L, H, P, N, Q)
-    return res, ssd_bytes(b, L, H, P, G, N, 2), ms, "ssd kernels", ["ssd.hip", "common.hpp"], cpu
+    return res, ssd_bytes(b, L, H, P, G, N, 2), ms, "ssd kernels", ["ssd.hip", "ssd_common.hpp", "common.hpp"], cpu
+
+
+def bench_ssd_bwd(args, torch, mss, I):
+    cfg = I.SSD_2P8B
+    x = I.ssd_inputs(cfg)
+    x.update(I.ssd_grad_output(cfg))
+    g = {k: to_dev(torch, x[k]) for k in ("x", "delta", "A", "B", "C", "dy")}
+    b, L, H, P, G, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+    ws = torch.empty(mss.ssd_bwd_workspace_size(b, L, H, P, G, N), dtype=torch.uint8, device="cuda:0")
+    out = mss.ssd_chunk_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy=g["dy"], want_dD=False, want_dh0=False,
+                            workspace=ws)
+
+    def step():
+        mss.ssd_chunk_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy=g["dy"], want_dD=False, want_dh0=False,
+                          out=out, workspace=ws)
+
+    ms = time_region(torch, step, args.steps, args.warmup)
+    updates = b * L * H * P * N
+    res = {"metric": "state updates/s (B*L*H*P*N), Mamba-2 SSD layer backward", "value": updates / (ms * 1e-3),
+           "unit": "state updates/s", "ms_per_step": ms, "dtype": "bf16 MFMA operands (hi/lo pairs), f32 accumulate",
+           "config": {"workload": f"{cfg.name}_bwd: SSD backward b={b} L={L} H={H} P={P} G={G} N={N}, gradients "
+                                  "of x, delta, A, B, C from dy (fp32); bf16 x/B/C, fp32 delta/dy/gradients; the "
+                                  "states recomputed by a forward pass inside the call", "batch": b, "seqlen": L,
+                      "nheads": H, "headdim": P, "d_state": N}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th, info = host_cpus()
+        f64 = lambda k: I.to_f64(x[k], "bf16")
+        X, Bm, Cm, dl, dy = f64("x"), f64("B"), f64("C"), x["delta"].astype(np.float64), x["dy"].astype(np.float64)
+        hs = 8  # all threads: both batch rows, heads 0..7 (the oracle runs one thread per (batch, group))
+        units = min(th, b * G)
+
+        def call(nb, nh, t):
+            return oracle.ssd_bwd(np.ascontiguousarray(X[:nb, :, :nh]), np.ascontiguousarray(dl[:nb, :, :nh]),
+                                  x["A"][:nh], Bm[:nb], Cm[:nb], dy=np.ascontiguousarray(dy[:nb, :, :nh]), threads=t)
+        cpu = cpu_leg(lambda: call(b, hs, units), b * L * hs * P * N, lambda: call(1, 2, 1), L * 2 * P * N,
+                      "state updates/s", units, info, f"batch rows 0..{b - 1}, heads 0..{hs - 1}, full L={L}",
+                      "batch row 0, heads 0..1, full L")
+    res["mfma_flops"] = ssd_bwd_mfma_flops(b, L, H, P, N)
+    files = ["ssd.hip", "ssd_bwd.hip", "ssd_common.hpp", "common.hpp"]
+    return res, ssd_bwd_bytes(b, L, H, P, G, N, 2), ms, "ssd backward kernels (forward pass included)", files, cpu
 
 
 def bench_copy(args, torch):
@@ -555,7 +619,8 @@ def main():
               "the hot path shards over batch and channels with no communication", file=sys.stderr)
         sys.exit(2)
     if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and
-                                             args.workload in ("decode_2p8b", "copy", "scan_2p8b_fused")):
+                                             args.workload in ("decode_2p8b", "copy", "scan_2p8b_fused",
+                                                               "ssd_2p8b_bwd", "decode_m3")):
         print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
               file=sys.stderr)
         sys.exit(2)
@@ -583,6 +648,8 @@ def main():
         res, nbytes, launch_ms, kernel, files, cpu = bench_decode(args, torch, mss, I)
     elif args.workload == "ssd_2p8b":
         res, nbytes, launch_ms, kernel, files, cpu = bench_ssd(args, torch, mss, I)
+    elif args.workload == "ssd_2p8b_bwd":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_ssd_bwd(args, torch, mss, I)
     elif args.workload == "scan_m2shape":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_M2)
     elif args.workload == "scan_2p8b_bwd":

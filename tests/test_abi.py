@@ -239,6 +239,50 @@ def test_ssd_validation_errors():
     assert ssd_call(cs=P(11)) == ALIAS                                 # chunk_states on workspace
 
 
+def ssd_bwd_call(**kw):
+    b, L, H, Pd, G, N = kw.pop("shape", (2, 1024, 8, 64, 1, 128))
+    io = kw.pop("io", BF16)
+    ws_bytes = kw.pop("ws_bytes", mss.lib().mss_ssd_bwd_workspace_size(b, L, H, Pd, G, N, io) or 1 << 20)
+    a = dict(x=P(0), delta=P(1), A=P(2), B=P(3), C=P(4), D=P(5), z=P(6), h0=P(7), dy=P(8), dhl=P(9), dx=P(10),
+             ddelta=P(11), dA=P(12), dB=P(13), dC=P(14), dD=P(15), dz=P(16), dh0=P(17), ws=P(18), flags=0)
+    a.update(kw)
+    return mss.lib().mss_ssd_chunk_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["dy"],
+                                       a["dhl"], a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                                       a["dh0"], b, L, H, Pd, G, N, io, a["flags"], a["ws"], ws_bytes, None)
+
+
+def test_ssd_bwd_validation_errors():
+    """Everything rejected on the host before any HIP call (fake pointers)."""
+    for k in ("x", "delta", "A", "B", "C", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        assert ssd_bwd_call(**{k: None}) == NULL, k
+    assert ssd_bwd_call(dz=None) == NULL                                 # z given without dz
+    assert ssd_bwd_call(z=None) == NULL                                  # dz given without z
+    assert ssd_bwd_call(shape=(2, 0, 8, 64, 1, 128)) == SHAPE
+    assert ssd_bwd_call(io=9) == DTYPE
+    assert ssd_bwd_call(io=FP32) == UNSUP
+    assert ssd_bwd_call(shape=(2, 1024, 8, 96, 1, 128)) == UNSUP         # headdim 96
+    assert ssd_bwd_call(shape=(2, 1024, 8, 64, 1, 40)) == UNSUP          # dstate not a multiple of 16
+    assert ssd_bwd_call(shape=(2, 1024, 8, 64, 1, 144)) == UNSUP         # dstate above 128
+    assert ssd_bwd_call(shape=(2, 1024, 6, 64, 4, 128)) == UNSUP         # nheads % ngroups
+    lib = mss.lib()
+    for Pd, N in ((64, 16), (64, 48), (64, 64), (64, 128), (128, 128), (128, 48)):
+        assert lib.mss_ssd_bwd_workspace_size(2, 1024, 8, Pd, 1, N, BF16) > 0, (Pd, N)
+    assert lib.mss_ssd_bwd_workspace_size(2, 1024, 8, 64, 1, 256, BF16) == 0
+    # The forward's limits with 64-step chunks: L*H*P below 2^30 - 64 and
+    # ceil(L/64) * H * P/64 * batch below 2^22.
+    assert lib.mss_ssd_bwd_workspace_size(1, (1 << 16) - 1, 256, 64, 1, 128, BF16) > 0
+    assert lib.mss_ssd_bwd_workspace_size(1, 1 << 16, 256, 64, 1, 128, BF16) == 0
+    assert lib.mss_ssd_bwd_workspace_size(64, 1 << 15, 128, 64, 1, 16, BF16) == 0
+    assert ssd_bwd_call(flags=1) == UNSUP
+    assert ssd_bwd_call(dy=P(8, 4)) == ALIGN
+    assert ssd_bwd_call(ws=None) == WS
+    assert ssd_bwd_call(ws_bytes=1) == WS
+    assert ssd_bwd_call(dx=P(0, 512)) == ALIAS                           # dx over x
+    assert ssd_bwd_call(dB=P(8)) == ALIAS                                # dB over dy
+    assert ssd_bwd_call(dh0=P(10)) == ALIAS                              # dh0 over dx
+    assert ssd_bwd_call(dC=P(18)) == ALIAS                               # dC over the workspace
+
+
 def noalloc_call(**kw):
     b, d, n, L = kw.pop("shape", (2, 64, 16, 128))
     io = kw.pop("io", BF16)
