@@ -350,45 +350,38 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
   }
   stage_bc_transposed(a, a.B, b, g, l0, BT);
   stage_bc_transposed(a, a.C, b, g, l0, CT);
-  {
-    float es = 0.f;
-    if (Sp) {
-      for (int e4 = threadIdx.x; e4 < 16 * a.N; e4 += 256) {
-        const f32x4 ev = *reinterpret_cast<const f32x4*>(Ep + 4 * e4);
-        const f32x4 sv = *reinterpret_cast<const f32x4*>(Sp + 4 * e4);
-        es += ev[0] * sv[0] + ev[1] * sv[1] + ev[2] * sv[2] + ev[3] * sv[3];
-      }
-    }
-    es = wave_sum(es);
-    if (lane == 0) s_es[w] = es;
-  }
   __syncthreads();
 
-  // ---- operand fragments
+  // ---- operand fragments.  Every k loop runs over all 128 states (8 steps of
+  // 16) so that it unrolls and its loads issue together; states past N read 0.
+  constexpr int kNK = kN / 16;
   // B or C rows of step T*32 + lc, states kk*16 + 8hf .. +8 (A rows or B columns).
   auto frag_bc = [&](rsrc_t r, int T, int kk) -> u32x4 {
-    return buf_load_u32x4(r, ((uint32_t)(T * 32 + lc) * brow + (uint32_t)(kk * 16 + 8 * hf)) * 2);
+    return buf_load_u32x4(r, kk < nk ? ((uint32_t)(T * 32 + lc) * brow + (uint32_t)(kk * 16 + 8 * hf)) * 2
+                                     : kOffNone);
   };
   // x of step T*32 + lc, headdim rows kp*16 + 8hf .. +8.
   auto frag_x = [&](int T, int kp) -> u32x4 {
     return buf_load_u32x4(rx, ((uint32_t)(T * 32 + lc) * xrow + (uint32_t)(kp * 16 + 8 * hf)) * 2);
   };
-  // State slice S [64][N]: rows p = PT*32 + lc, states kk*16 + 8hf .. +8, as hi/lo.
-  auto frag_srow = [&](const float* S, int PT, int kk, u32x4& hi, u32x4& lo) {
-    const float* s = S + (size_t)(PT * 32 + lc) * a.N + kk * 16 + 8 * hf;
-    const f32x4 v0 = *reinterpret_cast<const f32x4*>(s), v1 = *reinterpret_cast<const f32x4*>(s + 4);
-    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    split8(v, hi, lo, dm);
+  // The 64 x N state slices E and S_in (S_in absent: reads 0).
+  const rsrc_t rE = make_rsrc(Ep, (uint32_t)(kP * a.N * 4));
+  const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
+  // Rows p = PT*32 + lc, states kk*16 + 8hf .. +8 (raw fp32).
+  auto ld_srow = [&](rsrc_t r, int PT, int kk, float* v) {
+    const uint32_t o = kk < nk ? ((uint32_t)(PT * 32 + lc) * a.N + (uint32_t)(kk * 16 + 8 * hf)) * 4 : kOffNone;
+    const f32x4 v0 = as_f32x4(buf_load_u32x4(r, o)), v1 = as_f32x4(buf_load_u32x4(r, o + 16));
+    v[0] = v0[0], v[1] = v0[1], v[2] = v0[2], v[3] = v0[3], v[4] = v1[0], v[5] = v1[1], v[6] = v1[2], v[7] = v1[3];
   };
-  // State slice S [64][N]: state n = NT*32 + lc (0 past N), rows kp*16 + 8hf + t, as hi/lo.
-  auto frag_scol = [&](const float* S, int NT, int kp, u32x4& hi, u32x4& lo) {
+  // State n = NT*32 + lc (0 past N), rows kp*16 + 8hf + t (raw fp32).  The
+  // "no element" offset is chosen per load: added to it, the row offset
+  // would wrap back into the slice.
+  auto ld_scol = [&](rsrc_t r, int NT, int kp, float* v) {
     const int n = NT * 32 + lc;
     const bool ok = n < a.N;
-    const float* s = S + (size_t)(kp * 16 + 8 * hf) * a.N + (ok ? n : 0);
-    float v[8];
+    const uint32_t o = ((uint32_t)(kp * 16 + 8 * hf) * a.N + (uint32_t)n) * 4;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = ok ? s[(size_t)t * a.N] : 0.f;
-    split8(v, hi, lo, dm);
+    for (int t = 0; t < 8; ++t) v[t] = __uint_as_float(buf_load_u32(r, ok ? o + (uint32_t)(t * a.N * 4) : kOffNone));
   };
   auto lds4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
 
@@ -404,7 +397,8 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
     u32x4 mkh[NI][2], mkl[NI][2], mwh[NI][2], mwl[NI][2];
     {
       f32x16 kacc[NI] = {}, wacc[NI] = {};
-      for (int kk = 0; kk < nk; ++kk) {
+#pragma unroll
+      for (int kk = 0; kk < kNK; ++kk) {
         const u32x4 bop = frag_bc(rb, Q, kk);
 #pragma unroll
         for (int u = 0; u < NI; ++u) kacc[u] = mfma(frag_bc(rc, Q + u, kk), bop, kacc[u]);
@@ -463,9 +457,12 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
     {
       f32x16 gacc = {};
-      for (int kk = 0; kk < nk; ++kk) {
+#pragma unroll
+      for (int kk = 0; kk < kNK; ++kk) {
+        float ev[8];
+        ld_srow(rE, sub, kk, ev);
         u32x4 eh, el;
-        frag_srow(Ep, sub, kk, eh, el);
+        split8(ev, eh, el, dm);
         const u32x4 bop = frag_bc(rb, Q, kk);
         gacc = mfma(eh, bop, gacc);
         gacc = mfma(el, bop, gacc);
@@ -527,8 +524,10 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
         f32x16 xacc = {};
 #pragma unroll
         for (int kp = 0; kp < kP / 16; ++kp) {
+          float ev[8];
+          ld_scol(rE, NT, kp, ev);
           u32x4 eh, el;
-          frag_scol(Ep, NT, kp, eh, el);
+          split8(ev, eh, el, dm);
           const u32x4 xop = frag_x(Q, kp);
           xacc = mfma(eh, xop, xacc);
           xacc = mfma(el, xop, xacc);
@@ -582,7 +581,8 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
             wt[u] = mfma(xa, dl, wt[u]);
           }
         }
-        for (int kk = 0; kk < nk; ++kk) {
+#pragma unroll
+        for (int kk = 0; kk < kNK; ++kk) {
           const u32x4 cop = frag_bc(rc, Q, kk);
 #pragma unroll
           for (int u = 0; u < NJ; ++u) kt[u] = mfma(frag_bc(rb, u, kk), cop, kt[u]);
@@ -624,7 +624,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
           slice(std::integral_constant<int, 1>{});
         }
       }
-      float tp = 0.f;
+      float tp = 0.f, es = 0.f;
       const size_t prow = ((size_t)b * a.L + l0 + col) * a.Hv + vh;
       const bool in = l0 + col < a.L;
       const float ec = s_e[col];
@@ -636,8 +636,16 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
         if (Sp) {
 #pragma unroll
           for (int kp = 0; kp < kP / 16; ++kp) {
+            float sv[8];
+            ld_scol(rS, NT, kp, sv);
+            if (Q == 0) {  // <E, S_in>: each element once, over the two Q = 0 waves
+              float ev[8];
+              ld_scol(rE, NT, kp, ev);
+#pragma unroll
+              for (int t = 0; t < 8; ++t) es += ev[t] * sv[t];
+            }
             u32x4 sh, sl;
-            frag_scol(Sp, NT, kp, sh, sl);
+            split8(sv, sh, sl, dm);
             const u32x4 bh = *reinterpret_cast<const u32x4*>(&dyRh[col][kp * 16 + 8 * hf]);
             const u32x4 bl = *reinterpret_cast<const u32x4*>(&dyRl[col][kp * 16 + 8 * hf]);
             cacc = mfma(sh, bh, cacc);
@@ -675,6 +683,8 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       }
       tp += __shfl_xor(tp, 32);
       if (hf == 0) s_T[sub][col] = tp;
+      es = wave_sum(es);
+      if (lane == 0) s_es[w] = es;
     }
   };
   if (q == 0)
