@@ -202,19 +202,27 @@ def to_dev(torch, a):
     return torch.from_numpy(a).to("cuda:0")
 
 
+STEP_TIMES = {}  # per-step event times of the last timed region (median, p10, p90)
+
+
 def time_region(torch, fn, steps, warmup):
-    """Event-timed region on the current stream (the library launches there)."""
+    """Event-timed region on the current stream (the library launches there):
+    ms per step over the whole region; an event between consecutive steps
+    also gives each step's own time (STEP_TIMES)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms per step
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    STEP_TIMES.update({"ms_per_step_median": float(np.median(per)), "ms_per_step_p10": float(np.percentile(per, 10)),
+                       "ms_per_step_p90": float(np.percentile(per, 90))})
+    return ev[0].elapsed_time(ev[-1]) / steps  # ms per step
 
 
 CPU_MIN_S = 10.0  # the oracle leg repeats its sample until at least this much wall time has passed
@@ -686,9 +694,10 @@ def main():
         roofline[r["bound"]] = {k: r[k] for k in ("achieved", "peak", "unit", "frac")}
     line = {
         "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic (seeded generator, workload shapes)",
-        "config": res["config"], "roofline": roofline, "cpu_baseline": cpu,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], **STEP_TIMES, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"],
+        "data": "synthetic (seeded generator, workload shapes)", "config": res["config"], "roofline": roofline,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

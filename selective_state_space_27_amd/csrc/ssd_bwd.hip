@@ -454,6 +454,9 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       }
     }
 
+    // The two waves reading the same state fragments (same sub, q = 0 and 1)
+    // start each phase together, so the second read finds the lines in L2.
+    __syncthreads();
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
     {
       f32x16 gacc = {};
@@ -512,6 +515,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       if (lane == 0) s_dd[w] = dd;
     }
 
+    __syncthreads();
     // ---- products 3: (x^T G)^T, state tiles 2 sub + v, columns col
     {
       float up = 0.f;
@@ -564,6 +568,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       if (hf == 0) s_U[sub][col] = up;
     }
 
+    __syncthreads();
     // ---- products 4: W^T and K^T (rows j in halves <= Q, columns i = col),
     // then (h^T dyy)^T for state tiles 2 sub + v.
     {
