@@ -212,12 +212,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       cbias = a.conv_b != nullptr ? a.conv_b[c_io] : 0.f;
       dbias = a.delta_bias != nullptr ? a.delta_bias[c_io] : 0.f;
     }
-    float A2[SPW];
+    // The core channel's A row for this wave's states (general decay only),
+    // loaded inside that mode's loop so the other modes do not keep it live.
+    auto load_a2 = [&](float* A2) {
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int n = wc * SPW + j;
-      A2[j] = (is_core && cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
-    }
+      for (int j = 0; j < SPW; ++j) {
+        const int n = wc * SPW + j;
+        A2[j] = (is_core && cok && n < N) ? a.A[(size_t)c * N + n] * kLog2e : 0.f;
+      }
+    };
 
     // Initial state: zero in the local pass; for a piece that continues a
     // sequence, the carry at the end of the previous workgroup's range
@@ -274,6 +277,8 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       // component (i / 16) % 4 of bcb[blk][i / 64].
       constexpr bool kBlkBC = S::kBlockLayout;
       constexpr int kRing = kBlkBC ? 1 : kPrefetch;
+      float A2[M == kDecayGeneral ? SPW : 1];
+      if constexpr (M == kDecayGeneral) load_a2(A2);
       f32x4 bct[kRing][NV];
       f32x4 bcb[kBlk][kBlkBC ? NV / 4 : 1];
       auto load_bc = [&](int tile, f32x4* dst) {
