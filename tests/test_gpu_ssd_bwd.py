@@ -210,3 +210,43 @@ def test_ssd_bwd_2p8b_all_heads_linear_functionals():
         scale = float(np.sum(np.maximum(np.abs(gk), np.sqrt(np.mean(gk * gk))) * np.abs(V)))
         print(f"<{k}, V>: {got:.9e} vs {ref:.9e}, |diff| / scale {abs(got - ref) / scale:.2e}")
         assert abs(got - ref) <= TOL * scale, k
+
+
+def test_ssd_bwd_maximum_sizes_linear_functionals():
+    """At the documented limit: L*H*P just under 2^30 (dy's and dx's fp32 rows
+    of one batch entry just under 4 GB), ragged L, 16384 blocks; inputs drawn
+    on the device (seeded).  The oracle's backward would keep ~69 GB of states
+    per head here, so the gradients are checked through the same exact linear
+    identities as at the workload size (fp64 oracle forward, which streams)."""
+    L, H = (1 << 20) - 1, 16
+    cfg = I.small_ssd_config(1, L, H, 64, 1, 128, 64, seed=I.SEED_BASE + 902)
+    g = I.ssd_inputs_device(cfg)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(cfg.seed + 1)
+    dy = torch.randn((1, L, H, 64), generator=gen, device="cuda:0", dtype=torch.float32)
+    out = mss.ssd_chunk_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy=dy)
+    torch.cuda.synchronize()
+    X, Bm, Cm = host64(g["x"]), host64(g["B"]), host64(g["C"])
+    dl, A, dyh = host64(g["delta"]), host64(g["A"]), host64(dy)
+    del dy
+    rng = np.random.default_rng(11)
+
+    def fwd(xx, B, C, h0):
+        y, _, _ = oracle.ssd(xx, dl, A, B, C, None, None, h0)
+        return float(np.sum(dyh * y))
+
+    checks = {
+        "dB": (lambda V: fwd(X, V, Cm, None), Bm.shape),
+        "dC": (lambda V: fwd(X, Bm, V, None), Cm.shape),
+        "dx": (lambda V: fwd(V, Bm, Cm, None), X.shape),
+        "dh0": (lambda V: fwd(np.zeros_like(X), Bm, Cm, V), (1, H, 64, 128)),
+    }
+    for k, (f, shape) in checks.items():
+        V = rng.standard_normal(shape)
+        gk = host64(out[k])
+        got = float(np.sum(gk * V))
+        ref = f(V)
+        scale = float(np.sum(np.maximum(np.abs(gk), np.sqrt(np.mean(gk * gk))) * np.abs(V)))
+        print(f"max sizes <{k}, V>: {got:.9e} vs {ref:.9e}, |diff| / scale {abs(got - ref) / scale:.2e}")
+        assert abs(got - ref) <= TOL * scale, k
+        del V, gk
