@@ -590,7 +590,9 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const size_t hoff = row_el(a, vh, 0);
   const size_t bh_el = (size_t)b * a.L * a.H * a.P + hoff;
   const uint32_t ybytes = (uint32_t)(((size_t)a.L * a.H * a.P - hoff) * 4);
-  const rsrc_t ry = make_rsrc(a.y + bh_el, ybytes);
+  // y may be null inside the library (the backward's state pass without a
+  // gate needs no output): a zero-size descriptor then drops every store.
+  const rsrc_t ry = make_rsrc(a.y ? a.y + bh_el : nullptr, a.y ? ybytes : 0u);
   const rsrc_t rz = make_rsrc(a.z ? a.z + bh_el : nullptr, a.z ? ybytes / 2 : 0u);
   // Row r of this lane's accumulator tile is step lprev + rt*32 + 4*hf +
   // 8*(r>>2) + (r&3): a per-lane base plus a compile-time multiple of the row.

@@ -32,7 +32,7 @@
 //
 // Passes:
 //   1. the forward kernels with 64-step chunks: the state after every block
-//      and the ungated output (for dz);
+//      and, with a gate, the ungated output (for dz);
 //   2. ssd_bwd_local_kernel: per (block, virtual head) the block's own part of
 //      the adjoint handed to the block before, F = sum_i exp(s_i) dyy_i C_i^T,
 //      and dz;
@@ -836,7 +836,7 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream) {
   f.D = p.D;
   f.z = nullptr;
   f.h0 = p.h0;
-  f.y = reinterpret_cast<float*>(ws + l.yf);
+  f.y = p.z ? reinterpret_cast<float*>(ws + l.yf) : nullptr;  // the ungated y serves dz only
   f.chunk_states = reinterpret_cast<float*>(ws + l.Sblk);
   f.h_last = nullptr;
   f.batch = p.batch;
