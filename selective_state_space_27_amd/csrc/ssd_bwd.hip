@@ -115,13 +115,13 @@ __device__ __forceinline__ u32x4 as_u32x4(f32x4 v) { return __builtin_bit_cast(u
 // 128 state rows): 512 units of (step pair, 8 states), two per thread; steps
 // past L and states past N are staged as zeros.
 __device__ __forceinline__ void stage_bc_transposed(const BwdArgs& a, const uint16_t* src, int b, int g, int l0,
-                                                    uint16_t* T) {
+                                                    uint16_t* T, int tid) {
   const uint32_t row = (uint32_t)(a.G * a.N * 2);
   const uint32_t left = (uint32_t)max(a.L - l0, 0);
   const rsrc_t r = make_rsrc(src + ((size_t)b * a.L + l0) * a.G * a.N, left * row);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int u = threadIdx.x + 256 * it;
+    const int u = tid + 256 * it;
     const int ng = u & 15, j = 2 * (u >> 4);
     const bool nok = ng * 8 < a.N;
     const uint32_t col = (uint32_t)((g * a.N + ng * 8) * 2);
@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(256) ssd_bwd_local_kernel(BwdArgs a) {
       *reinterpret_cast<uint32_t*>(&gl[tsw(pg * 8 + k, jx)]) = lo;
     }
   }
-  stage_bc_transposed(a, a.C, b, g, l0, CT);
+  stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
   __syncthreads();
   const int nt = w;
   if (nt * 32 >= a.N) return;
@@ -272,9 +272,16 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 4.  grid (nblk * Hv, batch), 256 threads: every gradient of one
-// (64-step block, virtual head).  Wave w = (q, sub), q = w >> 1 the half of
-// the block whose steps it owns as output columns, sub = w & 1.
+// Pass 4.  grid (nblk * Hv, batch), 512 threads, one workgroup per CU: every
+// gradient of one (64-step block, virtual head).  All threads first stage the
+// block's operands in LDS (x, dyy as hi/lo in two layouts, B and C
+// time-contiguous, E and S_in as fp32 rows; 150 KB), read from memory once
+// with whole-row loads; the products then read LDS, and only the step-major
+// B/C fragments (shared by the group's heads, L2-resident) and the row
+// segments of the outputs touch memory.  Two teams of four waves run
+// concurrently: team 0 does products 1-3, team 1 products 4.  Wave
+// (team, q, sub): q the half of the block whose steps it owns as output
+// columns, sub = w & 1.
 //   products 1: K(i, j) = C_i . B_j and W(i, j) = dyy_i . x_j for j in half q,
 //     i in halves >= q; their column sums of Z = M o K o W o delta (strictly
 //     below the diagonal); then M o K and M o W as bf16 hi/lo operands;
@@ -285,13 +292,18 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 //     sums of Z), then (h^T dyy)^T for the same state tiles -> dC part and
 //     C . (S_in^T dyy);
 //   then wave 0 (lane = step) assembles ddelta and the dA and dD parts.
-__global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
+constexpr int kERow = kN + 4;  // row length (floats) of the E and S_in stagings
+
+__global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t dyRh[kSub][kRowP];  // dyy, step rows: hi
   __shared__ __attribute__((aligned(16))) uint16_t dyRl[kSub][kRowP];  // lo
   __shared__ __attribute__((aligned(16))) uint16_t dyTh[kP * kTRow];   // dyy, headdim rows (tsw): hi
   __shared__ __attribute__((aligned(16))) uint16_t dyTl[kP * kTRow];   // lo
   __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];     // B, state rows (tsw)
   __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];     // C, state rows (tsw)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kSub][kRowP];    // x, step rows
+  __shared__ __attribute__((aligned(16))) float Es[kP * kERow];        // E [p][n] (0 past N)
+  __shared__ __attribute__((aligned(16))) float Ss[kP * kERow];        // S_in [p][n] (0 past N or absent)
   __shared__ __attribute__((aligned(16))) float s_dl[kSub], s_ls[kSub], s_e[kSub], s_f[kSub];
   __shared__ float s_col[kSub], s_row[kSub], s_T[2][kSub], s_U[2][kSub], s_c[2][kSub];
   __shared__ float s_es[4], s_dd[4];
@@ -301,7 +313,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
   const int l0 = blk * kSub;
   const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int q = w >> 1, sub = w & 1;
+  const int team = w >> 2, q = (w >> 1) & 1, sub = w & 1;
   const Dot2Masks dm = dot2_masks();
   const int nk = a.N / 16;  // 16-state k-steps
   const uint32_t left = (uint32_t)max(a.L - l0, 0);
@@ -329,7 +341,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
     s_e[lane] = exp2_fast(ls);
     s_f[lane] = exp2_fast(ls63 - ls);
   }
-  {
+  if (threadIdx.x < 256) {
     const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
     float v[2][8];
     load_dyy(a, b, vh, l0, jx, pg, v, false);
@@ -348,8 +360,25 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
     }
   }
-  stage_bc_transposed(a, a.B, b, g, l0, BT);
-  stage_bc_transposed(a, a.C, b, g, l0, CT);
+  if (threadIdx.x < 256)
+    stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
+  else
+    stage_bc_transposed(a, a.B, b, g, l0, BT, threadIdx.x - 256);
+  {  // x: step threadIdx.x / 8, headdim rows (threadIdx.x % 8) * 8 .. +8 (steps past L read 0)
+    const int st = threadIdx.x >> 3, pc = (threadIdx.x & 7) * 8;
+    *reinterpret_cast<u32x4*>(&xs[st][pc]) = buf_load_u32x4(rx, ((uint32_t)st * xrow + (uint32_t)pc) * 2);
+  }
+  {  // E and S_in: whole 16-byte groups of their 64 x N slices; states past N (and an absent S_in) read 0
+    const rsrc_t rE = make_rsrc(Ep, (uint32_t)(kP * a.N * 4));
+    const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
+#pragma unroll
+    for (int it = 0; it < kP * kN / 4 / 512; ++it) {
+      const int e4 = threadIdx.x + 512 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
+      const uint32_t o = n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone;
+      *reinterpret_cast<u32x4*>(&Es[pr * kERow + n]) = buf_load_u32x4(rE, o);
+      *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = buf_load_u32x4(rS, o);
+    }
+  }
   __syncthreads();
 
   // ---- operand fragments.  Every k loop runs over all 128 states (8 steps of
@@ -362,37 +391,32 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
   };
   // x of step T*32 + lc, headdim rows kp*16 + 8hf .. +8.
   auto frag_x = [&](int T, int kp) -> u32x4 {
-    return buf_load_u32x4(rx, ((uint32_t)(T * 32 + lc) * xrow + (uint32_t)(kp * 16 + 8 * hf)) * 2);
+    return *reinterpret_cast<const u32x4*>(&xs[T * 32 + lc][kp * 16 + 8 * hf]);
   };
-  // The 64 x N state slices E and S_in (S_in absent: reads 0).
-  const rsrc_t rE = make_rsrc(Ep, (uint32_t)(kP * a.N * 4));
-  const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
-  // Rows p = PT*32 + lc, states kk*16 + 8hf .. +8 (raw fp32).
-  auto ld_srow = [&](rsrc_t r, int PT, int kk, float* v) {
-    const uint32_t o = kk < nk ? ((uint32_t)(PT * 32 + lc) * a.N + (uint32_t)(kk * 16 + 8 * hf)) * 4 : kOffNone;
-    const f32x4 v0 = as_f32x4(buf_load_u32x4(r, o)), v1 = as_f32x4(buf_load_u32x4(r, o + 16));
+  // Staged state slice (Es or Ss): rows p = PT*32 + lc, states kk*16 + 8hf .. +8.
+  auto ld_srow = [&](const float* S, int PT, int kk, float* v) {
+    const float* r = S + (PT * 32 + lc) * kERow + kk * 16 + 8 * hf;
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(r), v1 = *reinterpret_cast<const f32x4*>(r + 4);
     v[0] = v0[0], v[1] = v0[1], v[2] = v0[2], v[3] = v0[3], v[4] = v1[0], v[5] = v1[1], v[6] = v1[2], v[7] = v1[3];
   };
-  // State n = NT*32 + lc (0 past N), rows kp*16 + 8hf + t (raw fp32).  The
-  // "no element" offset is chosen per load: added to it, the row offset
-  // would wrap back into the slice.
-  auto ld_scol = [&](rsrc_t r, int NT, int kp, float* v) {
-    const int n = NT * 32 + lc;
-    const bool ok = n < a.N;
-    const uint32_t o = ((uint32_t)(kp * 16 + 8 * hf) * a.N + (uint32_t)n) * 4;
+  // Staged state slice: state n = NT*32 + lc, rows kp*16 + 8hf + t.
+  auto ld_scol = [&](const float* S, int NT, int kp, float* v) {
+    const float* r = S + (kp * 16 + 8 * hf) * kERow + NT * 32 + lc;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = __uint_as_float(buf_load_u32(r, ok ? o + (uint32_t)(t * a.N * 4) : kOffNone));
+    for (int t = 0; t < 8; ++t) v[t] = r[t * kERow];
   };
   auto lds4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
 
   const int col = q * 32 + lc;  // this lane's output column: step (of the block) of every tile below
   const float ls_c = s_ls[col], dl_c = s_dl[col];
 
-  auto body = [&](auto qtag) {
+  auto body = [&](auto qtag, auto team_tag) {
     constexpr int Q = decltype(qtag)::value;
     constexpr int NI = 2 - Q;  // row halves Q..1 (products 1)
     constexpr int NJ = Q + 1;  // row halves 0..Q (products 4)
+    constexpr int TEAM = decltype(team_tag)::value;
 
+    if constexpr (TEAM == 0) {
     // ---- products 1: K and W, rows i in halves >= Q, columns j = col
     u32x4 mkh[NI][2], mkl[NI][2], mwh[NI][2], mwl[NI][2];
     {
@@ -454,16 +478,14 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       }
     }
 
-    // The two waves reading the same state fragments (same sub, q = 0 and 1)
-    // start each phase together, so the second read finds the lines in L2.
-    __syncthreads();
+
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
     {
       f32x16 gacc = {};
 #pragma unroll
       for (int kk = 0; kk < kNK; ++kk) {
         float ev[8];
-        ld_srow(rE, sub, kk, ev);
+        ld_srow(Es, sub, kk, ev);
         u32x4 eh, el;
         split8(ev, eh, el, dm);
         const u32x4 bop = frag_bc(rb, Q, kk);
@@ -489,7 +511,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       for (int k4 = 0; k4 < 4; ++k4) {
         const uint32_t o = (uint32_t)col * xrow + (uint32_t)(sub * 32 + 8 * k4 + 4 * hf);
         const f32x4 dyv = as_f32x4(buf_load_u32x4(rdy, o * 4));
-        const u32x2 xx = buf_load_u32x2(rx, o * 2);
+        const u32x2 xx = *reinterpret_cast<const u32x2*>(&xs[col][sub * 32 + 8 * k4 + 4 * hf]);
         const float xv[4] = {bf16_lo(xx[0]), bf16_hi(xx[0]), bf16_lo(xx[1]), bf16_hi(xx[1])};
         float sz[4] = {1.f, 1.f, 1.f, 1.f};
         if (a.z) {
@@ -515,7 +537,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       if (lane == 0) s_dd[w] = dd;
     }
 
-    __syncthreads();
+
     // ---- products 3: (x^T G)^T, state tiles 2 sub + v, columns col
     {
       float up = 0.f;
@@ -529,7 +551,7 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int kp = 0; kp < kP / 16; ++kp) {
           float ev[8];
-          ld_scol(rE, NT, kp, ev);
+          ld_scol(Es, NT, kp, ev);
           u32x4 eh, el;
           split8(ev, eh, el, dm);
           const u32x4 xop = frag_x(Q, kp);
@@ -568,7 +590,8 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       if (hf == 0) s_U[sub][col] = up;
     }
 
-    __syncthreads();
+    }  // team 0
+    if constexpr (TEAM == 1) {
     // ---- products 4: W^T and K^T (rows j in halves <= Q, columns i = col),
     // then (h^T dyy)^T for state tiles 2 sub + v.
     {
@@ -642,10 +665,10 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int kp = 0; kp < kP / 16; ++kp) {
             float sv[8];
-            ld_scol(rS, NT, kp, sv);
+            ld_scol(Ss, NT, kp, sv);
             if (Q == 0) {  // <E, S_in>: each element once, over the two Q = 0 waves
               float ev[8];
-              ld_scol(rE, NT, kp, ev);
+              ld_scol(Es, NT, kp, ev);
 #pragma unroll
               for (int t = 0; t < 8; ++t) es += ev[t] * sv[t];
             }
@@ -689,13 +712,17 @@ __global__ void __launch_bounds__(256, 2) ssd_bwd_grad_kernel(BwdArgs a) {
       tp += __shfl_xor(tp, 32);
       if (hf == 0) s_T[sub][col] = tp;
       es = wave_sum(es);
-      if (lane == 0) s_es[w] = es;
+      if (lane == 0) s_es[w & 3] = es;
+    }
     }
   };
-  if (q == 0)
-    body(std::integral_constant<int, 0>{});
-  else
-    body(std::integral_constant<int, 1>{});
+  if (team == 0) {
+    if (q == 0) body(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    else body(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  } else {
+    if (q == 0) body(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    else body(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+  }
   __syncthreads();
 
   // ---- ddelta and the dA, dD parts (lane = step of the block)
@@ -895,7 +922,7 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(ssd_bwd_local_kernel, blocks, dim3(256), 0, stream, a);
   const unsigned xb = (unsigned)((16 * a.N + 255) / 256);
   hipLaunchKernelGGL(ssd_bwd_chain_kernel, dim3(xb * (unsigned)a.Hv, (unsigned)a.batch), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(ssd_bwd_grad_kernel, blocks, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_grad_kernel, blocks, dim3(512), 0, stream, a);
   hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.G * (a.N / 4))), dim3(256),
                      0, stream, a);
   hipLaunchKernelGGL(ssd_bwd_reduce_dd_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.H)), dim3(256), 0, stream,
