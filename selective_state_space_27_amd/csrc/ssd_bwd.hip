@@ -330,6 +330,12 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   const float* Sp = blk > 0 ? a.Sblk + sbase(a, (size_t)b * a.nblk + blk - 1, vh)
                             : (a.h0 ? a.h0 + sbase(a, b, vh) : nullptr);
   const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
+  constexpr int kNK = kN / 16;
+  // B or C rows of step T*32 + lc, states kk*16 + 8hf .. +8 (A rows or B columns).
+  auto frag_bc = [&](rsrc_t r, int T, int kk) -> u32x4 {
+    return buf_load_u32x4(r, kk < nk ? ((uint32_t)(T * 32 + lc) * brow + (uint32_t)(kk * 16 + 8 * hf)) * 2
+                                     : kOffNone);
+  };
 
   // ---- stagings, <E, S_in>
   if (w == 0) {
@@ -379,16 +385,28 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = buf_load_u32x4(rS, o);
     }
   }
+  // The step-major B and C fragments of the first products (read from memory:
+  // shared by the group's heads, they are L2-resident), issued before the
+  // barrier so that their latency hides behind the staging.  Team 0 (K = C
+  // B^T, columns in half q): f1 = B rows q, f2[u] = C rows q + u; team 1
+  // (K^T = B C^T, columns in half q): f1 = C rows q, f2[u] = B rows u <= q.
+  u32x4 f1[kNK], f2[2][kNK];
+  {
+    const rsrc_t r1 = team == 0 ? rb : rc, r2 = team == 0 ? rc : rb;
+#pragma unroll
+    for (int kk = 0; kk < kNK; ++kk) f1[kk] = frag_bc(r1, q, kk);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bool use = team == 0 ? q + u <= 1 : u <= q;
+      const int rows = team == 0 ? q + u : u;
+#pragma unroll
+      for (int kk = 0; kk < kNK; ++kk) f2[u][kk] = use ? frag_bc(r2, rows, kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   __syncthreads();
 
   // ---- operand fragments.  Every k loop runs over all 128 states (8 steps of
-  // 16) so that it unrolls and its loads issue together; states past N read 0.
-  constexpr int kNK = kN / 16;
-  // B or C rows of step T*32 + lc, states kk*16 + 8hf .. +8 (A rows or B columns).
-  auto frag_bc = [&](rsrc_t r, int T, int kk) -> u32x4 {
-    return buf_load_u32x4(r, kk < nk ? ((uint32_t)(T * 32 + lc) * brow + (uint32_t)(kk * 16 + 8 * hf)) * 2
-                                     : kOffNone);
-  };
+  // 16) so that it unrolls; states past N read 0.
   // x of step T*32 + lc, headdim rows kp*16 + 8hf .. +8.
   auto frag_x = [&](int T, int kp) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(&xs[T * 32 + lc][kp * 16 + 8 * hf]);
@@ -423,9 +441,8 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       f32x16 kacc[NI] = {}, wacc[NI] = {};
 #pragma unroll
       for (int kk = 0; kk < kNK; ++kk) {
-        const u32x4 bop = frag_bc(rb, Q, kk);
 #pragma unroll
-        for (int u = 0; u < NI; ++u) kacc[u] = mfma(frag_bc(rc, Q + u, kk), bop, kacc[u]);
+        for (int u = 0; u < NI; ++u) kacc[u] = mfma(f2[u][kk], f1[kk], kacc[u]);
       }
 #pragma unroll
       for (int kp = 0; kp < kP / 16; ++kp) {
@@ -488,9 +505,8 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         ld_srow(Es, sub, kk, ev);
         u32x4 eh, el;
         split8(ev, eh, el, dm);
-        const u32x4 bop = frag_bc(rb, Q, kk);
-        gacc = mfma(eh, bop, gacc);
-        gacc = mfma(el, bop, gacc);
+        gacc = mfma(eh, f1[kk], gacc);
+        gacc = mfma(el, f1[kk], gacc);
       }
       gacc *= s_f[col];
 #pragma unroll
@@ -611,9 +627,8 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int kk = 0; kk < kNK; ++kk) {
-          const u32x4 cop = frag_bc(rc, Q, kk);
 #pragma unroll
-          for (int u = 0; u < NJ; ++u) kt[u] = mfma(frag_bc(rb, u, kk), cop, kt[u]);
+          for (int u = 0; u < NJ; ++u) kt[u] = mfma(f2[u][kk], f1[kk], kt[u]);
         }
         // Row sums of Z left of the diagonal (j < i).
         float rs = 0.f;
