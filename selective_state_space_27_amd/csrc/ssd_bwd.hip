@@ -38,12 +38,14 @@
 //      and dz;
 //   3. ssd_bwd_chain_kernel: E along the sequence, from the last block to the
 //      first: E_{k-1} = exp(s_63 of block k) E_k + F_k (dh0 at the end);
-//   4. ssd_bwd_grad_kernel: per (block, virtual head) every gradient above on
-//      the matrix cores; dB, dC, ddelta, dA and dD as per-virtual-head parts;
+//   4. ssd_bwd_grad_kernel: per (block, chunk of a group's virtual heads)
+//      every gradient above on the matrix cores; dB and dC as per-chunk
+//      parts, ddelta, dA and dD as per-virtual-head parts;
 //   5. fixed-order sums of those parts (the results are bitwise repeatable).
 // Operands that are not exact bf16 inputs enter the matrix cores as bf16
 // hi/lo pairs (two products, three when both operands are split).
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.hpp"
@@ -81,12 +83,13 @@ struct BwdArgs {
   const float* yf;        // [b, L, H, P]: the forward output before the gate
   const float* Sblk;      // [b, nblk, H, P, N]: the state after every block
   float* Eblk;            // [b, nblk, H, P, N]: F of every block, then the adjoint E arriving at it
-  float* dBp;             // [b, L, Hv, N]: per-virtual-head parts of dB
-  float* dCp;             // [b, L, Hv, N]: of dC
+  float* dBp;             // [b, L, G * cpg, N]: per-chunk parts of dB (hpw virtual heads each)
+  float* dCp;             // [b, L, G * cpg, N]: of dC
   float* ddp;             // [b, L, Hv]: of ddelta
   float* dAp;             // [b, nblk, Hv]: of dA
   float* dDp;             // [b, nblk, Hv]: of dD
   int batch, L, H, G, P, ph, Hv, N, nblk, Lp;
+  int hpw, cpg, Gc;       // virtual heads per gradient workgroup, chunks per group, G * cpg
 };
 
 // Element offset, inside one step's [H, P] row, of row 0 of virtual head vh
@@ -272,24 +275,28 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 4.  grid (nblk * Hv, batch), 512 threads, one workgroup per CU: every
-// gradient of one (64-step block, virtual head).  All threads first stage the
-// block's operands in LDS (x, dyy as hi/lo in two layouts, B and C
-// time-contiguous, E and S_in as fp32 rows; 150 KB), read from memory once
-// with whole-row loads; the products then read LDS, and only the step-major
-// B/C fragments (shared by the group's heads, L2-resident) and the row
-// segments of the outputs touch memory.  Two teams of four waves run
-// concurrently: team 0 does products 1-3, team 1 products 4.  Wave
+// Pass 4.  grid (nblk * G * cpg, batch), 512 threads, one workgroup per CU:
+// every gradient of one 64-step block for hpw consecutive virtual heads of
+// one group (cpg = the group's virtual heads / hpw chunks).  B and C are the
+// same for all of them: they are staged once, and K = C B^T (the only product
+// that does not involve the head) is formed once and kept in registers; the
+// dB and dC parts of the heads are summed in registers, in head order, and
+// written once per chunk.  Per head, all threads first stage the head's
+// operands in LDS (x, dyy as hi/lo in two layouts, E and S_in as fp32 rows),
+// read from memory once with whole-row loads; the products then read LDS,
+// and only the step-major B fragments of (G B)^T (L2-resident) and the row
+// segments of the outputs touch memory.  Two teams of four waves
+// run concurrently: team 0 does products 1-3, team 1 products 4.  Wave
 // (team, q, sub): q the half of the block whose steps it owns as output
 // columns, sub = w & 1.
-//   products 1: K(i, j) = C_i . B_j and W(i, j) = dyy_i . x_j for j in half q,
-//     i in halves >= q; their column sums of Z = M o K o W o delta (strictly
+//   products 1: W(i, j) = dyy_i . x_j for j in half q, i in halves >= q; with
+//     K(i, j) = C_i . B_j the column sums of Z = M o K o W o delta (strictly
 //     below the diagonal); then M o K and M o W as bf16 hi/lo operands;
 //   products 2: (G B)^T for headdim half sub -> dx, x . (G B), dyy . x;
 //   products 3: (x^T G)^T for state tiles 2 sub, 2 sub + 1 -> dB part and
 //     B . (E^T x);
-//   products 4: W^T(j, i) and K^T(j, i) for i in half q, j in halves <= q (row
-//     sums of Z), then (h^T dyy)^T for the same state tiles -> dC part and
+//   products 4: W^T(j, i) for i in half q, j in halves <= q, with K^T the row
+//     sums of Z, then (h^T dyy)^T for the same state tiles -> dC part and
 //     C . (S_in^T dyy);
 //   then wave 0 (lane = step) assembles ddelta and the dA and dD parts.
 constexpr int kERow = kN + 4;  // row length (floats) of the E and S_in stagings
@@ -308,90 +315,99 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   __shared__ float s_col[kSub], s_row[kSub], s_T[2][kSub], s_U[2][kSub], s_c[2][kSub];
   __shared__ float s_es[4], s_dd[4];
 
-  const int vh = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, b = blockIdx.y;
-  const int h = vh / a.ph, g = h / (a.H / a.G);
+  const int gc = blockIdx.x % a.Gc, blk = blockIdx.x / a.Gc, b = blockIdx.y;
+  const int g = gc / a.cpg;
+  const int vh0 = g * (a.Hv / a.G) + (gc % a.cpg) * a.hpw;  // the chunk's first virtual head
   const int l0 = blk * kSub;
-  const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
+  // Lane indexes (re-derived opaquely for every head: see the head loop).
+  int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int team = w >> 2, q = (w >> 1) & 1, sub = w & 1;
   const Dot2Masks dm = dot2_masks();
   const int nk = a.N / 16;  // 16-state k-steps
   const uint32_t left = (uint32_t)max(a.L - l0, 0);
   const uint32_t xrow = (uint32_t)(a.H * a.P), brow = (uint32_t)(a.G * a.N);
-  const size_t xbase = ((size_t)b * a.L + l0) * xrow + vrow(a, vh);
   const size_t bbase = ((size_t)b * a.L + l0) * brow + (size_t)g * a.N;
-  const rsrc_t rx = make_rsrc(a.x + xbase, left * xrow * 2);
-  const rsrc_t rdy = make_rsrc(a.dy + xbase, left * xrow * 4);
-  const rsrc_t rz = make_rsrc(a.z ? a.z + xbase : nullptr, a.z ? left * xrow * 2 : 0u);
-  const rsrc_t rdx = make_rsrc(a.dx + xbase, left * xrow * 4);
   const rsrc_t rb = make_rsrc(a.B + bbase, left * brow * 2);
   const rsrc_t rc = make_rsrc(a.C + bbase, left * brow * 2);
-  const float* Ep = a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh);
-  const float* Sp = blk > 0 ? a.Sblk + sbase(a, (size_t)b * a.nblk + blk - 1, vh)
-                            : (a.h0 ? a.h0 + sbase(a, b, vh) : nullptr);
-  const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.f;
+  // Every k loop runs over all 128 states (8 steps of 16) so that it unrolls;
+  // states past N read 0.
   constexpr int kNK = kN / 16;
   // B or C rows of step T*32 + lc, states kk*16 + 8hf .. +8 (A rows or B columns).
   auto frag_bc = [&](rsrc_t r, int T, int kk) -> u32x4 {
     return buf_load_u32x4(r, kk < nk ? ((uint32_t)(T * 32 + lc) * brow + (uint32_t)(kk * 16 + 8 * hf)) * 2
                                      : kOffNone);
   };
+  auto xbase = [&](int vh) { return ((size_t)b * a.L + l0) * xrow + vrow(a, vh); };
+  // The state entering the block (S_in) of virtual head vh, or null.
+  auto sin_ptr = [&](int vh) -> const float* {
+    return blk > 0 ? a.Sblk + sbase(a, (size_t)b * a.nblk + blk - 1, vh) : (a.h0 ? a.h0 + sbase(a, b, vh) : nullptr);
+  };
 
-  // ---- stagings, <E, S_in>
-  if (w == 0) {
-    const size_t o = ((size_t)b * a.H + h) * a.Lp + l0 + lane;
-    const float d = a.dlT[o], ls = a.lsT[o];
-    const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
-    s_dl[lane] = d;
-    s_ls[lane] = ls;
-    s_e[lane] = exp2_fast(ls);
-    s_f[lane] = exp2_fast(ls63 - ls);
-  }
-  if (threadIdx.x < 256) {
-    const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
-    float v[2][8];
-    load_dyy(a, b, vh, l0, jx, pg, v, false);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 hi, lo;
-      split8(v[s], hi, lo, dm);
-      *reinterpret_cast<u32x4*>(&dyRh[jx + s][pg * 8]) = hi;
-      *reinterpret_cast<u32x4*>(&dyRl[jx + s][pg * 8]) = lo;
+  // ---- the per-head stagings
+  auto stage_head = [&](int vh) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // keep the staging addresses from being held over the head loop
+    if (w == 0) {
+      const size_t o = ((size_t)b * a.H + vh / a.ph) * a.Lp + l0 + lane;
+      const float d = a.dlT[o], ls = a.lsT[o];
+      const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
+      s_dl[lane] = d;
+      s_ls[lane] = ls;
+      s_e[lane] = exp2_fast(ls);
+      s_f[lane] = exp2_fast(ls63 - ls);
     }
+    if (tid < 256) {
+      const int pg = tid & 7, jx = 2 * (tid >> 3);
+      float v[2][8];
+      load_dyy(a, b, vh, l0, jx, pg, v, false);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t hi, lo;
-      split2(v[0][k], v[1][k], hi, lo, dm);
-      *reinterpret_cast<uint32_t*>(&dyTh[tsw(pg * 8 + k, jx)]) = hi;
-      *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
+      for (int s = 0; s < 2; ++s) {
+        u32x4 hi, lo;
+        split8(v[s], hi, lo, dm);
+        *reinterpret_cast<u32x4*>(&dyRh[jx + s][pg * 8]) = hi;
+        *reinterpret_cast<u32x4*>(&dyRl[jx + s][pg * 8]) = lo;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t hi, lo;
+        split2(v[0][k], v[1][k], hi, lo, dm);
+        *reinterpret_cast<uint32_t*>(&dyTh[tsw(pg * 8 + k, jx)]) = hi;
+        *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
+      }
     }
-  }
+    {  // x: step tid / 8, headdim rows (tid % 8) * 8 .. +8 (steps past L read 0)
+      const rsrc_t rx = make_rsrc(a.x + xbase(vh), left * xrow * 2);
+      const int st = tid >> 3, pc = (tid & 7) * 8;
+      *reinterpret_cast<u32x4*>(&xs[st][pc]) = buf_load_u32x4(rx, ((uint32_t)st * xrow + (uint32_t)pc) * 2);
+    }
+    {  // E and S_in: whole 16-byte groups of their 64 x N slices; states past N (and an absent S_in) read 0
+      const float* Sp = sin_ptr(vh);
+      const rsrc_t rE = make_rsrc(a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh), (uint32_t)(kP * a.N * 4));
+      const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
+#pragma unroll
+      for (int it = 0; it < kP * kN / 4 / 512; ++it) {
+        const int e4 = tid + 512 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
+        const uint32_t o = n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone;
+        *reinterpret_cast<u32x4*>(&Es[pr * kERow + n]) = buf_load_u32x4(rE, o);
+        *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = buf_load_u32x4(rS, o);
+      }
+    }
+  };
+
   if (threadIdx.x < 256)
     stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
   else
     stage_bc_transposed(a, a.B, b, g, l0, BT, threadIdx.x - 256);
-  {  // x: step threadIdx.x / 8, headdim rows (threadIdx.x % 8) * 8 .. +8 (steps past L read 0)
-    const int st = threadIdx.x >> 3, pc = (threadIdx.x & 7) * 8;
-    *reinterpret_cast<u32x4*>(&xs[st][pc]) = buf_load_u32x4(rx, ((uint32_t)st * xrow + (uint32_t)pc) * 2);
-  }
-  {  // E and S_in: whole 16-byte groups of their 64 x N slices; states past N (and an absent S_in) read 0
-    const rsrc_t rE = make_rsrc(Ep, (uint32_t)(kP * a.N * 4));
-    const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
-#pragma unroll
-    for (int it = 0; it < kP * kN / 4 / 512; ++it) {
-      const int e4 = threadIdx.x + 512 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
-      const uint32_t o = n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone;
-      *reinterpret_cast<u32x4*>(&Es[pr * kERow + n]) = buf_load_u32x4(rE, o);
-      *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = buf_load_u32x4(rS, o);
-    }
-  }
-  // The step-major B and C fragments of the first products (read from memory:
-  // shared by the group's heads, they are L2-resident), issued before the
-  // barrier so that their latency hides behind the staging.  Team 0 (K = C
-  // B^T, columns in half q): f1 = B rows q, f2[u] = C rows q + u; team 1
-  // (K^T = B C^T, columns in half q): f1 = C rows q, f2[u] = B rows u <= q.
-  u32x4 f1[kNK], f2[2][kNK];
+  stage_head(vh0);
+  // K (team 0: K = C B^T, columns in half q, row halves q + u) or K^T (team 1:
+  // K^T = B C^T, columns in half q, row halves u <= q), from step-major B and C
+  // fragments read from memory (L2-resident: the group's other chunks read
+  // them too), issued before the barrier so that their latency hides behind
+  // the staging.
+  f32x16 kk2[2] = {};
   {
+    u32x4 f1[kNK], f2[2][kNK];
     const rsrc_t r1 = team == 0 ? rb : rc, r2 = team == 0 ? rc : rb;
 #pragma unroll
     for (int kk = 0; kk < kNK; ++kk) f1[kk] = frag_bc(r1, q, kk);
@@ -402,11 +418,15 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < kNK; ++kk) f2[u][kk] = use ? frag_bc(r2, rows, kk) : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int kk = 0; kk < kNK; ++kk) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) kk2[u] = mfma(f2[u][kk], f1[kk], kk2[u]);
+    }
   }
   __syncthreads();
 
-  // ---- operand fragments.  Every k loop runs over all 128 states (8 steps of
-  // 16) so that it unrolls; states past N read 0.
+  // ---- operand fragments
   // x of step T*32 + lc, headdim rows kp*16 + 8hf .. +8.
   auto frag_x = [&](int T, int kp) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(&xs[T * 32 + lc][kp * 16 + 8 * hf]);
@@ -425,25 +445,22 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   };
   auto lds4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
 
-  const int col = q * 32 + lc;  // this lane's output column: step (of the block) of every tile below
-  const float ls_c = s_ls[col], dl_c = s_dl[col];
+  int col = q * 32 + lc;  // this lane's output column: step (of the block) of every tile below
+  // The chunk's dB (team 0) or dC (team 1) part for state tiles 2 sub + v, column col.
+  f32x16 dacc[2] = {};
 
-  auto body = [&](auto qtag, auto team_tag) {
+  auto body = [&](auto qtag, auto team_tag, int vh) {
     constexpr int Q = decltype(qtag)::value;
     constexpr int NI = 2 - Q;  // row halves Q..1 (products 1)
     constexpr int NJ = Q + 1;  // row halves 0..Q (products 4)
     constexpr int TEAM = decltype(team_tag)::value;
+    const float ls_c = s_ls[col], dl_c = s_dl[col];
 
     if constexpr (TEAM == 0) {
-    // ---- products 1: K and W, rows i in halves >= Q, columns j = col
+    // ---- products 1: W, rows i in halves >= Q, columns j = col
     u32x4 mkh[NI][2], mkl[NI][2], mwh[NI][2], mwl[NI][2];
     {
-      f32x16 kacc[NI] = {}, wacc[NI] = {};
-#pragma unroll
-      for (int kk = 0; kk < kNK; ++kk) {
-#pragma unroll
-        for (int u = 0; u < NI; ++u) kacc[u] = mfma(f2[u][kk], f1[kk], kacc[u]);
-      }
+      f32x16 wacc[NI] = {};
 #pragma unroll
       for (int kp = 0; kp < kP / 16; ++kp) {
         const u32x4 xop = frag_x(Q, kp);
@@ -464,7 +481,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             const float m = (i0 + qq > col) ? exp2_fast(lsi[qq] - ls_c) : 0.f;
-            cs += m * kacc[u][4 * k4 + qq] * wacc[u][4 * k4 + qq];
+            cs += m * kk2[u][4 * k4 + qq] * wacc[u][4 * k4 + qq];
           }
         }
       }
@@ -476,7 +493,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         auto slice = [&](auto stag) {
           constexpr int S = decltype(stag)::value;
           float kv[8], wv[8];
-          acc_kslice<S>(kacc[u], kv);
+          acc_kslice<S>(kk2[u], kv);
           acc_kslice<S>(wacc[u], wv);
           const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
           const f32x4 l0v = lds4(&s_ls[i0]), l1v = lds4(&s_ls[i0 + 4]);
@@ -495,7 +512,6 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       }
     }
 
-
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
     {
       f32x16 gacc = {};
@@ -505,8 +521,9 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         ld_srow(Es, sub, kk, ev);
         u32x4 eh, el;
         split8(ev, eh, el, dm);
-        gacc = mfma(eh, f1[kk], gacc);
-        gacc = mfma(el, f1[kk], gacc);
+        const u32x4 bop = frag_bc(rb, Q, kk);
+        gacc = mfma(eh, bop, gacc);
+        gacc = mfma(el, bop, gacc);
       }
       gacc *= s_f[col];
 #pragma unroll
@@ -522,6 +539,11 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         }
       }
       // dx, x . (G B) and dyy . x for (step col, rows p).
+      const size_t xb = xbase(vh);
+      const rsrc_t rdy = make_rsrc(a.dy + xb, left * xrow * 4);
+      const rsrc_t rz = make_rsrc(a.z ? a.z + xb : nullptr, a.z ? left * xrow * 2 : 0u);
+      const rsrc_t rdx = make_rsrc(a.dx + xb, left * xrow * 4);
+      const float Dh = a.D ? a.D[vh / a.ph] : 0.f;
       float cp = 0.f, dd = 0.f;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
@@ -553,12 +575,9 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       if (lane == 0) s_dd[w] = dd;
     }
 
-
     // ---- products 3: (x^T G)^T, state tiles 2 sub + v, columns col
     {
       float up = 0.f;
-      const size_t prow = ((size_t)b * a.L + l0 + col) * a.Hv + vh;  // this column's row of the parts
-      const bool in = l0 + col < a.L;
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         const int NT = 2 * sub + v;
@@ -592,15 +611,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
             xacc = mfma(av, mwl[u][S], xacc);
           }
         }
-        if (in) {
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const int n0 = NT * 32 + 8 * k4 + 4 * hf;
-            if (n0 < a.N)
-              *reinterpret_cast<f32x4*>(a.dBp + prow * a.N + n0) =
-                  dl_c * f32x4{xacc[4 * k4], xacc[4 * k4 + 1], xacc[4 * k4 + 2], xacc[4 * k4 + 3]};
-          }
-        }
+        dacc[v] += dl_c * xacc;
       }
       up += __shfl_xor(up, 32);
       if (hf == 0) s_U[sub][col] = up;
@@ -608,12 +619,12 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 
     }  // team 0
     if constexpr (TEAM == 1) {
-    // ---- products 4: W^T and K^T (rows j in halves <= Q, columns i = col),
-    // then (h^T dyy)^T for state tiles 2 sub + v.
+    // ---- products 4: W^T (rows j in halves <= Q, columns i = col), with K^T
+    // the row sums of Z, then (h^T dyy)^T for state tiles 2 sub + v.
     {
       u32x4 mth[NJ][2], mtl[NJ][2];
       {
-        f32x16 wt[NJ] = {}, kt[NJ] = {};
+        f32x16 wt[NJ] = {};
 #pragma unroll
         for (int kp = 0; kp < kP / 16; ++kp) {
           const u32x4 dh = *reinterpret_cast<const u32x4*>(&dyRh[col][kp * 16 + 8 * hf]);
@@ -624,11 +635,6 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
             wt[u] = mfma(xa, dh, wt[u]);
             wt[u] = mfma(xa, dl, wt[u]);
           }
-        }
-#pragma unroll
-        for (int kk = 0; kk < kNK; ++kk) {
-#pragma unroll
-          for (int u = 0; u < NJ; ++u) kt[u] = mfma(f2[u][kk], f1[kk], kt[u]);
         }
         // Row sums of Z left of the diagonal (j < i).
         float rs = 0.f;
@@ -641,7 +647,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const float m = (j0 + qq < col) ? exp2_fast(ls_c - lsj[qq]) * dlj[qq] : 0.f;
-              rs += m * wt[u][4 * k4 + qq] * kt[u][4 * k4 + qq];
+              rs += m * wt[u][4 * k4 + qq] * kk2[u][4 * k4 + qq];
             }
           }
         }
@@ -667,16 +673,15 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
           slice(std::integral_constant<int, 1>{});
         }
       }
+      const bool has_sin = sin_ptr(vh) != nullptr;
       float tp = 0.f, es = 0.f;
-      const size_t prow = ((size_t)b * a.L + l0 + col) * a.Hv + vh;
-      const bool in = l0 + col < a.L;
       const float ec = s_e[col];
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         const int NT = 2 * sub + v;
         if (NT * 32 >= a.N) continue;
         f32x16 cacc = {};
-        if (Sp) {
+        if (has_sin) {
 #pragma unroll
           for (int kp = 0; kp < kP / 16; ++kp) {
             float sv[8];
@@ -714,15 +719,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
             cacc = mfma(av, mtl[u][S], cacc);
           }
         }
-        if (in) {
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const int n0 = NT * 32 + 8 * k4 + 4 * hf;
-            if (n0 < a.N)
-              *reinterpret_cast<f32x4*>(a.dCp + prow * a.N + n0) =
-                  f32x4{cacc[4 * k4], cacc[4 * k4 + 1], cacc[4 * k4 + 2], cacc[4 * k4 + 3]};
-          }
-        }
+        dacc[v] += cacc;
       }
       tp += __shfl_xor(tp, 32);
       if (hf == 0) s_T[sub][col] = tp;
@@ -731,57 +728,91 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     }
     }
   };
-  if (team == 0) {
-    if (q == 0) body(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    else body(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
-  } else {
-    if (q == 0) body(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    else body(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-  }
-  __syncthreads();
 
-  // ---- ddelta and the dA, dD parts (lane = step of the block)
-  if (w == 0) {
-    const int t = lane;
-    const float dl = s_dl[t], e = s_e[t], f = s_f[t];
-    const float cprime = s_c[0][t] + s_c[1][t];
-    const float cr = s_col[t] - s_row[t];
-    const float corner = wave_prefix_sum(cr) - cr;  // R_t: sum over u < t
-    const float et = e * (s_T[0][t] + s_T[1][t]);
-    const float pt = wave_prefix_sum(et);
-    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pt), 63));
-    const float suffix = tot - (pt - et);  // sum over i >= t
-    const float fu = f * dl * (s_U[0][t] + s_U[1][t]);
-    const float prefix = wave_prefix_sum(fu) - fu;  // sum over j < t
-    const float dq63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), 63));
-    const float es = (s_es[0] + s_es[1]) + (s_es[2] + s_es[3]);
-    const float gh = corner + suffix + prefix + dq63 * es;  // <G_t, exp(delta_t A) h_{t-1}>
-    if (l0 + t < a.L) a.ddp[((size_t)b * a.L + l0 + t) * a.Hv + vh] = cprime + Ah * gh;
-    const float da = wave_sum(dl * gh);
-    if (lane == 0) {
-      const size_t o = ((size_t)b * a.nblk + blk) * a.Hv + vh;
-      a.dAp[o] = da;
-      a.dDp[o] = (s_dd[0] + s_dd[1]) + (s_dd[2] + s_dd[3]);
+  // The head loop, inside each wave kind's own copy of the code (its values
+  // that do not change over the heads then stay its own).
+  auto run = [&](auto qtag, auto team_tag) {
+    for (int i = 0; i < a.hpw; ++i) {
+      const int vh = vh0 + i;
+      // Opaque copies of the lane indexes: the addresses formed from them are
+      // then formed again for every head instead of being held (in registers
+      // that the products need) over the whole loop.
+      asm volatile("" : "+v"(lane), "+v"(lc), "+v"(hf));
+      col = q * 32 + lc;
+      if (i > 0) {
+        stage_head(vh);
+        __syncthreads();
+      }
+      body(qtag, team_tag, vh);
+      __syncthreads();
+
+      // ---- ddelta and the dA, dD parts (lane = step of the block).  The next
+      // head's stagings (after this) rewrite only the LDS that this wave alone
+      // reads here after it.
+      if (w == 0) {
+        const int t = lane;
+        const float dl = s_dl[t], e = s_e[t], f = s_f[t];
+        const float cprime = s_c[0][t] + s_c[1][t];
+        const float cr = s_col[t] - s_row[t];
+        const float corner = wave_prefix_sum(cr) - cr;  // R_t: sum over u < t
+        const float et = e * (s_T[0][t] + s_T[1][t]);
+        const float pt = wave_prefix_sum(et);
+        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pt), 63));
+        const float suffix = tot - (pt - et);  // sum over i >= t
+        const float fu = f * dl * (s_U[0][t] + s_U[1][t]);
+        const float prefix = wave_prefix_sum(fu) - fu;  // sum over j < t
+        const float dq63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), 63));
+        const float es = (s_es[0] + s_es[1]) + (s_es[2] + s_es[3]);
+        const float gh = corner + suffix + prefix + dq63 * es;  // <G_t, exp(delta_t A) h_{t-1}>
+        if (l0 + t < a.L) a.ddp[((size_t)b * a.L + l0 + t) * a.Hv + vh] = cprime + a.A[vh / a.ph] * gh;
+        const float da = wave_sum(dl * gh);
+        if (lane == 0) {
+          const size_t o = ((size_t)b * a.nblk + blk) * a.Hv + vh;
+          a.dAp[o] = da;
+          a.dDp[o] = (s_dd[0] + s_dd[1]) + (s_dd[2] + s_dd[3]);
+        }
+      }
+    }
+  };
+  if (team == 0) {
+    if (q == 0) run(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  } else {
+    if (q == 0) run(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+  }
+
+  // ---- the chunk's dB (team 0) and dC (team 1) parts, row (b, l0 + col, g, chunk)
+  if (l0 + col < a.L) {
+    float* dst = (team == 0 ? a.dBp : a.dCp) + (((size_t)b * a.L + l0 + col) * a.Gc + gc) * a.N;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int n0 = (2 * sub + v) * 32 + 8 * k4 + 4 * hf;
+        if (n0 < a.N)
+          *reinterpret_cast<f32x4*>(dst + n0) =
+              f32x4{dacc[v][4 * k4], dacc[v][4 * k4 + 1], dacc[v][4 * k4 + 2], dacc[v][4 * k4 + 3]};
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 5: fixed-order sums of the per-virtual-head parts.
-// dB and dC: grid-stride over (b, l, g, 4 states), the group's virtual heads
-// summed in order.
+// Pass 5: fixed-order sums of the parts.
+// dB and dC: grid-stride over (b, l, g, 4 states), the group's chunks summed
+// in order.
 __global__ void __launch_bounds__(256) ssd_bwd_reduce_bc_kernel(BwdArgs a) {
   const int n4s = a.N / 4;
-  const int hvg = a.Hv / a.G;
   const size_t total = (size_t)a.batch * a.L * a.G * n4s;
   for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (size_t)gridDim.x * 256) {
     const int n4 = (int)(idx % n4s);
     const size_t rest = idx / n4s;
     const int g = (int)(rest % a.G);
     const size_t bl = rest / a.G;  // b*L + l
-    const size_t src = (bl * a.Hv + (size_t)g * hvg) * a.N + 4 * n4;
+    const size_t src = (bl * a.Gc + (size_t)g * a.cpg) * a.N + 4 * n4;
     f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
-    for (int v = 0; v < hvg; ++v) {
+    for (int v = 0; v < a.cpg; ++v) {
       sb += *reinterpret_cast<const f32x4*>(a.dBp + src + (size_t)v * a.N);
       sc += *reinterpret_cast<const f32x4*>(a.dCp + src + (size_t)v * a.N);
     }
@@ -835,10 +866,28 @@ struct BwdLayout {
   size_t fwd, yf, Sblk, Eblk, dBp, dCp, ddp, dAp, dDp, total;
 };
 
+// Virtual heads per gradient workgroup: the largest divisor of a group's
+// virtual heads that still leaves 8 workgroups per CU (2048 for 256 CUs), or 1.
+// More heads per workgroup mean fewer dB/dC parts to write and sum and fewer
+// loads of B and C; the workgroups run one at a time per CU.  The environment
+// variable MSS_SSD_BWD_HEADS_PER_WG, when it holds a divisor of the group's
+// virtual heads, overrides the choice (tuning and tests).
+int grad_heads_per_wg(int64_t batch, int64_t nblk, int64_t vheads, int64_t ngroups) {
+  const int64_t hvg = vheads / ngroups;
+  if (const char* e = std::getenv("MSS_SSD_BWD_HEADS_PER_WG")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v <= hvg && hvg % v == 0) return (int)v;
+  }
+  for (int64_t d = hvg; d > 1; --d)
+    if (hvg % d == 0 && batch * nblk * ngroups * (hvg / d) >= 2048) return (int)d;
+  return 1;
+}
+
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                      int64_t dstate) {
   const int64_t nblk = (seqlen + kSub - 1) / kSub;
   const int64_t vheads = nheads * (headdim / kP);
+  const int64_t chunks = vheads / grad_heads_per_wg(batch, nblk, vheads, ngroups);  // G * cpg
   const size_t f4 = sizeof(float);
   BwdLayout l;
   l.fwd = 0;  // the forward's workspace (its status word first)
@@ -846,8 +895,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
   l.Sblk = l.yf + align256((size_t)batch * seqlen * nheads * headdim * f4);
   l.Eblk = l.Sblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
   l.dBp = l.Eblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
-  l.dCp = l.dBp + align256((size_t)batch * seqlen * vheads * dstate * f4);
-  l.ddp = l.dCp + align256((size_t)batch * seqlen * vheads * dstate * f4);
+  l.dCp = l.dBp + align256((size_t)batch * seqlen * chunks * dstate * f4);
+  l.ddp = l.dCp + align256((size_t)batch * seqlen * chunks * dstate * f4);
   l.dAp = l.ddp + align256((size_t)batch * seqlen * vheads * f4);
   l.dDp = l.dAp + align256((size_t)batch * nblk * vheads * f4);
   l.total = l.dDp + align256((size_t)batch * nblk * vheads * f4);
@@ -932,12 +981,16 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream) {
   a.N = (int)p.dstate;
   a.nblk = (int)((p.seqlen + kSub - 1) / kSub);
   a.Lp = a.nblk * kSub;
+  a.hpw = grad_heads_per_wg(a.batch, a.nblk, a.Hv, a.G);
+  a.cpg = a.Hv / a.G / a.hpw;
+  a.Gc = a.G * a.cpg;
 
   const dim3 blocks((unsigned)a.nblk * (unsigned)a.Hv, (unsigned)a.batch);
   hipLaunchKernelGGL(ssd_bwd_local_kernel, blocks, dim3(256), 0, stream, a);
   const unsigned xb = (unsigned)((16 * a.N + 255) / 256);
   hipLaunchKernelGGL(ssd_bwd_chain_kernel, dim3(xb * (unsigned)a.Hv, (unsigned)a.batch), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(ssd_bwd_grad_kernel, blocks, dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_grad_kernel, dim3((unsigned)a.nblk * (unsigned)a.Gc, (unsigned)a.batch), dim3(512), 0,
+                     stream, a);
   hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.G * (a.N / 4))), dim3(256),
                      0, stream, a);
   hipLaunchKernelGGL(ssd_bwd_reduce_dd_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.H)), dim3(256), 0, stream,

@@ -142,6 +142,38 @@ def test_ssd_bwd_many_heads_per_group():
     compare(g, r, "b2 l2048 h16 g1")
 
 
+HPW_CASES = [
+    # b, L, H, G, P, N, D, z, h0, dh_last, heads per gradient workgroup
+    (2, 300, 8, 2, 64, 128, True, True, True, True, 4),    # a whole group per workgroup
+    (1, 200, 8, 1, 64, 128, True, False, True, False, 2),  # four chunks of two heads
+    (1, 130, 3, 1, 128, 48, False, True, False, True, 3),  # headdim 128: 6 slices, chunks of 3
+    (2, 77, 6, 3, 128, 16, True, True, True, True, 4),     # one group's 4 slices at once
+]
+
+
+@pytest.mark.parametrize("case", HPW_CASES, ids=lambda c: "b{}l{}h{}g{}p{}n{}hpw{}".format(*c[:6], c[10]))
+def test_ssd_bwd_heads_per_workgroup(case, monkeypatch):
+    """Several virtual heads in one gradient workgroup (the full-size
+    workloads' launch; small sizes otherwise take one): every element of
+    every gradient against the oracle, and the same values as with one head
+    per workgroup up to the order of the dB and dC sums."""
+    b, L, H, G, P, N, d, z, h0, dhl, hpw = case
+    cfg, x = gen(b, L, H, G, P, N, seed=40, with_d=d, with_z=z, with_h0=h0, with_dhl=dhl)
+    monkeypatch.setenv("MSS_SSD_BWD_HEADS_PER_WG", str(hpw))
+    g = run_gpu(x)
+    monkeypatch.setenv("MSS_SSD_BWD_HEADS_PER_WG", "1")
+    g1 = run_gpu(x)
+    r = run_oracle(x)
+    if x["D"] is None:
+        r["dD"] = g["dD"] = g1["dD"] = None
+    compare(g, r, f"{case} heads per workgroup {hpw}")
+    for k in ("dx", "ddelta", "dA", "dD", "dz", "dh0"):
+        if g[k] is not None:
+            assert torch.equal(g[k], g1[k]), k
+    for k in ("dB", "dC"):
+        assert rel_err(host64(g[k]), host64(g1[k])) <= 1e-5, k
+
+
 def _full_inputs():
     cfg = I.SSD_2P8B
     x = I.ssd_inputs(cfg)
