@@ -281,11 +281,14 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 // same for all of them: they are staged once, and K = C B^T (the only product
 // that does not involve the head) is formed once and kept in registers; the
 // dB and dC parts of the heads are summed in registers, in head order, and
-// written once per chunk.  Per head, all threads first stage the head's
-// operands in LDS (x, dyy as hi/lo in two layouts, E and S_in as fp32 rows),
-// read from memory once with whole-row loads; the products then read LDS,
-// and only the step-major B fragments of (G B)^T (L2-resident) and the row
-// segments of the outputs touch memory.  Two teams of four waves
+// written once per chunk.  A head's operands (x, dyy, E, S_in) are read from
+// memory once, with whole-row loads into registers issued while the head
+// before is computed (team 0 loads dyy and x after its first products, team
+// 1 E and S_in before its products), and written to LDS (x, dyy as hi/lo in
+// two layouts, E and S_in as fp32 rows) between the two heads; the products
+// read LDS, and only the step-major B fragments of (G B)^T (L2-resident) and
+// the row segments of the outputs touch memory.  Wave 4 assembles each
+// head's ddelta and dA, dD parts between the heads.  Two teams of four waves
 // run concurrently: team 0 does products 1-3, team 1 products 4.  Wave
 // (team, q, sub): q the half of the block whose steps it owns as output
 // columns, sub = w & 1.
@@ -298,7 +301,7 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 //   products 4: W^T(j, i) for i in half q, j in halves <= q, with K^T the row
 //     sums of Z, then (h^T dyy)^T for the same state tiles -> dC part and
 //     C . (S_in^T dyy);
-//   then wave 0 (lane = step) assembles ddelta and the dA and dD parts.
+//   then wave 4 (lane = step) assembles ddelta and the dA and dD parts.
 constexpr int kERow = kN + 4;  // row length (floats) of the E and S_in stagings
 
 __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
@@ -344,67 +347,124 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     return blk > 0 ? a.Sblk + sbase(a, (size_t)b * a.nblk + blk - 1, vh) : (a.h0 ? a.h0 + sbase(a, b, vh) : nullptr);
   };
 
-  // ---- the per-head stagings
-  auto stage_head = [&](int vh) {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));  // keep the staging addresses from being held over the head loop
-    if (w == 0) {
+  // ---- the per-head stagings, in two halves: loads into registers, issued
+  // for the next head while the current one is computed, and their writes
+  // to LDS after the barrier that ends the current head.  Team 0 moves dyy
+  // and x, team 1 E, S_in and (wave 4) the step values delta and s.
+  struct T0Regs {
+    u32x4 dy[2][2], z[2], x[2];
+  };
+  struct T1Regs {
+    u32x4 e[kP * kN / 4 / 256], s[kP * kN / 4 / 256];
+    float dl, ls;
+  };
+  // The staging addresses are formed from an opaque copy of the thread index
+  // so that they are formed again for every head instead of being held (in
+  // registers that the products need) over the head loop.
+  auto opaque_tid = [] {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+  };
+  auto issue_t0 = [&](int vh, T0Regs& r) {
+    const int t = opaque_tid(), pg = t & 7, jx = 2 * (t >> 3);
+    const size_t xb = xbase(vh);
+    const rsrc_t rdy = make_rsrc(a.dy + xb, left * xrow * 4);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t o = (uint32_t)(jx + s) * xrow + (uint32_t)pg * 8;  // dyy: steps jx, jx + 1, rows pg*8 .. +8
+      r.dy[s][0] = buf_load_u32x4(rdy, o * 4);
+      r.dy[s][1] = buf_load_u32x4(rdy, o * 4 + 16);
+    }
+    if (a.z) {
+      const rsrc_t rz = make_rsrc(a.z + xb, left * xrow * 2);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) r.z[s] = buf_load_u32x4(rz, ((uint32_t)(jx + s) * xrow + (uint32_t)pg * 8) * 2);
+    }
+    const rsrc_t rx = make_rsrc(a.x + xb, left * xrow * 2);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {  // x: step u / 8, headdim rows (u % 8) * 8 .. +8
+      const int u = t + 256 * k, st = u >> 3, pc = (u & 7) * 8;
+      r.x[k] = buf_load_u32x4(rx, ((uint32_t)st * xrow + (uint32_t)pc) * 2);
+    }
+  };
+  auto commit_t0 = [&](const T0Regs& r) {
+    const int t = opaque_tid(), pg = t & 7, jx = 2 * (t >> 3);
+    float v[2][8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 d0 = as_f32x4(r.dy[s][0]), d1 = as_f32x4(r.dy[s][1]);
+      const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[s][k] = dv[k];
+      if (a.z) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[s][2 * k] *= silu(bf16_lo(r.z[s][k]));
+          v[s][2 * k + 1] *= silu(bf16_hi(r.z[s][k]));
+        }
+      }
+      u32x4 hi, lo;
+      split8(v[s], hi, lo, dm);
+      *reinterpret_cast<u32x4*>(&dyRh[jx + s][pg * 8]) = hi;
+      *reinterpret_cast<u32x4*>(&dyRl[jx + s][pg * 8]) = lo;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t hi, lo;
+      split2(v[0][k], v[1][k], hi, lo, dm);
+      *reinterpret_cast<uint32_t*>(&dyTh[tsw(pg * 8 + k, jx)]) = hi;
+      *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int u = t + 256 * k, st = u >> 3, pc = (u & 7) * 8;
+      *reinterpret_cast<u32x4*>(&xs[st][pc]) = r.x[k];
+    }
+  };
+  // E and S_in: whole 16-byte groups of their 64 x N slices; states past N
+  // (and an absent S_in) read 0.
+  auto issue_t1 = [&](int vh, T1Regs& r) {
+    const int t = opaque_tid() - 256;
+    if (w == 4) {
       const size_t o = ((size_t)b * a.H + vh / a.ph) * a.Lp + l0 + lane;
-      const float d = a.dlT[o], ls = a.lsT[o];
-      const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
-      s_dl[lane] = d;
-      s_ls[lane] = ls;
-      s_e[lane] = exp2_fast(ls);
-      s_f[lane] = exp2_fast(ls63 - ls);
+      r.dl = a.dlT[o];
+      r.ls = a.lsT[o];
     }
-    if (tid < 256) {
-      const int pg = tid & 7, jx = 2 * (tid >> 3);
-      float v[2][8];
-      load_dyy(a, b, vh, l0, jx, pg, v, false);
+    const float* Sp = sin_ptr(vh);
+    const rsrc_t rE = make_rsrc(a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh), (uint32_t)(kP * a.N * 4));
+    const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 hi, lo;
-        split8(v[s], hi, lo, dm);
-        *reinterpret_cast<u32x4*>(&dyRh[jx + s][pg * 8]) = hi;
-        *reinterpret_cast<u32x4*>(&dyRl[jx + s][pg * 8]) = lo;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        uint32_t hi, lo;
-        split2(v[0][k], v[1][k], hi, lo, dm);
-        *reinterpret_cast<uint32_t*>(&dyTh[tsw(pg * 8 + k, jx)]) = hi;
-        *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
-      }
+    for (int it = 0; it < kP * kN / 4 / 256; ++it) {
+      const int e4 = t + 256 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
+      const uint32_t o = n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone;
+      r.e[it] = buf_load_u32x4(rE, o);
+      r.s[it] = buf_load_u32x4(rS, o);
     }
-    {  // x: step tid / 8, headdim rows (tid % 8) * 8 .. +8 (steps past L read 0)
-      const rsrc_t rx = make_rsrc(a.x + xbase(vh), left * xrow * 2);
-      const int st = tid >> 3, pc = (tid & 7) * 8;
-      *reinterpret_cast<u32x4*>(&xs[st][pc]) = buf_load_u32x4(rx, ((uint32_t)st * xrow + (uint32_t)pc) * 2);
+  };
+  auto commit_t1 = [&](const T1Regs& r) {
+    const int t = opaque_tid() - 256;
+    if (w == 4) {
+      const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.ls), 63));
+      s_dl[lane] = r.dl;
+      s_ls[lane] = r.ls;
+      s_e[lane] = exp2_fast(r.ls);
+      s_f[lane] = exp2_fast(ls63 - r.ls);
     }
-    {  // E and S_in: whole 16-byte groups of their 64 x N slices; states past N (and an absent S_in) read 0
-      const float* Sp = sin_ptr(vh);
-      const rsrc_t rE = make_rsrc(a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh), (uint32_t)(kP * a.N * 4));
-      const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
 #pragma unroll
-      for (int it = 0; it < kP * kN / 4 / 512; ++it) {
-        const int e4 = tid + 512 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
-        const uint32_t o = n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone;
-        *reinterpret_cast<u32x4*>(&Es[pr * kERow + n]) = buf_load_u32x4(rE, o);
-        *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = buf_load_u32x4(rS, o);
-      }
+    for (int it = 0; it < kP * kN / 4 / 256; ++it) {
+      const int e4 = t + 256 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
+      *reinterpret_cast<u32x4*>(&Es[pr * kERow + n]) = r.e[it];
+      *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = r.s[it];
     }
   };
 
-  if (threadIdx.x < 256)
-    stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
-  else
-    stage_bc_transposed(a, a.B, b, g, l0, BT, threadIdx.x - 256);
-  stage_head(vh0);
-  // K (team 0: K = C B^T, columns in half q, row halves q + u) or K^T (team 1:
-  // K^T = B C^T, columns in half q, row halves u <= q), from step-major B and C
-  // fragments read from memory (L2-resident: the group's other chunks read
-  // them too), issued before the barrier so that their latency hides behind
-  // the staging.
+  // The first head's stagings and B, C (time-contiguous), with K (team 0:
+  // K = C B^T, columns in half q, row halves q + u) or K^T (team 1: K^T =
+  // B C^T, columns in half q, row halves u <= q) formed from step-major B and
+  // C fragments read from memory (L2-resident: the group's other chunks read
+  // them too) and issued first, so that their latency hides behind the
+  // stagings.
   f32x16 kk2[2] = {};
   {
     u32x4 f1[kNK], f2[2][kNK];
@@ -417,6 +477,17 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       const int rows = team == 0 ? q + u : u;
 #pragma unroll
       for (int kk = 0; kk < kNK; ++kk) f2[u][kk] = use ? frag_bc(r2, rows, kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (team == 0) {
+      T0Regs r;
+      issue_t0(vh0, r);
+      stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
+      commit_t0(r);
+    } else {
+      T1Regs r;
+      issue_t1(vh0, r);
+      stage_bc_transposed(a, a.B, b, g, l0, BT, threadIdx.x - 256);
+      commit_t1(r);
     }
 #pragma unroll
     for (int kk = 0; kk < kNK; ++kk) {
@@ -449,7 +520,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   // The chunk's dB (team 0) or dC (team 1) part for state tiles 2 sub + v, column col.
   f32x16 dacc[2] = {};
 
-  auto body = [&](auto qtag, auto team_tag, int vh) {
+  auto body = [&](auto qtag, auto team_tag, int vh, bool next, T0Regs& p0, T1Regs& p1) {
     constexpr int Q = decltype(qtag)::value;
     constexpr int NI = 2 - Q;  // row halves Q..1 (products 1)
     constexpr int NJ = Q + 1;  // row halves 0..Q (products 4)
@@ -511,6 +582,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         slice(std::integral_constant<int, 1>{});
       }
     }
+    if (next) issue_t0(vh + 1, p0);  // the next head's dyy and x, in flight until the stagings
 
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
     {
@@ -619,6 +691,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 
     }  // team 0
     if constexpr (TEAM == 1) {
+    if (next) issue_t1(vh + 1, p1);  // the next head's E, S_in and step values, in flight until the stagings
     // ---- products 4: W^T (rows j in halves <= Q, columns i = col), with K^T
     // the row sums of Z, then (h^T dyy)^T for state tiles 2 sub + v.
     {
@@ -732,24 +805,23 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   // The head loop, inside each wave kind's own copy of the code (its values
   // that do not change over the heads then stay its own).
   auto run = [&](auto qtag, auto team_tag) {
+    constexpr int TEAM = decltype(team_tag)::value;
+    T0Regs p0;
+    T1Regs p1;
     for (int i = 0; i < a.hpw; ++i) {
       const int vh = vh0 + i;
+      const bool next = i + 1 < a.hpw;
       // Opaque copies of the lane indexes: the addresses formed from them are
-      // then formed again for every head instead of being held (in registers
-      // that the products need) over the whole loop.
+      // then formed again for every head instead of being held over the loop.
       asm volatile("" : "+v"(lane), "+v"(lc), "+v"(hf));
       col = q * 32 + lc;
-      if (i > 0) {
-        stage_head(vh);
-        __syncthreads();
-      }
-      body(qtag, team_tag, vh);
+      body(qtag, team_tag, vh, next, p0, p1);
       __syncthreads();
 
       // ---- ddelta and the dA, dD parts (lane = step of the block).  The next
       // head's stagings (after this) rewrite only the LDS that this wave alone
       // reads here after it.
-      if (w == 0) {
+      if (w == 4) {
         const int t = lane;
         const float dl = s_dl[t], e = s_e[t], f = s_f[t];
         const float cprime = s_c[0][t] + s_c[1][t];
@@ -771,6 +843,13 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
           a.dAp[o] = da;
           a.dDp[o] = (s_dd[0] + s_dd[1]) + (s_dd[2] + s_dd[3]);
         }
+      }
+      if (next) {
+        if constexpr (TEAM == 0)
+          commit_t0(p0);
+        else
+          commit_t1(p1);
+        __syncthreads();
       }
     }
   };
