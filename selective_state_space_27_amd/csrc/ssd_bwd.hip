@@ -347,10 +347,11 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     return blk > 0 ? a.Sblk + sbase(a, (size_t)b * a.nblk + blk - 1, vh) : (a.h0 ? a.h0 + sbase(a, b, vh) : nullptr);
   };
 
-  // ---- the per-head stagings, in two halves: loads into registers, issued
-  // for the next head while the current one is computed, and their writes
-  // to LDS after the barrier that ends the current head.  Team 0 moves dyy
-  // and x, team 1 E, S_in and (wave 4) the step values delta and s.
+  // ---- the per-head stagings, in two halves: loads into registers and their
+  // writes to LDS.  Of the first head, team 0 moves dyy and x, team 1 E, S_in
+  // and (wave 4) the step values delta and s; of every later head, team 1
+  // moves all of them: it issues the loads as it starts the head before (its
+  // registers allow it) and writes LDS after the barrier that ends that head.
   struct T0Regs {
     u32x4 dy[2][2], z[2], x[2];
   };
@@ -359,6 +360,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     float dl, ls;
   };
   // The staging addresses are formed from an opaque copy of the thread index
+  // (taken mod 256: the thread's index in its team)
   // so that they are formed again for every head instead of being held (in
   // registers that the products need) over the head loop.
   auto opaque_tid = [] {
@@ -367,7 +369,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     return t;
   };
   auto issue_t0 = [&](int vh, T0Regs& r) {
-    const int t = opaque_tid(), pg = t & 7, jx = 2 * (t >> 3);
+    const int t = opaque_tid() & 255, pg = t & 7, jx = 2 * (t >> 3);
     const size_t xb = xbase(vh);
     const rsrc_t rdy = make_rsrc(a.dy + xb, left * xrow * 4);
 #pragma unroll
@@ -389,7 +391,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     }
   };
   auto commit_t0 = [&](const T0Regs& r) {
-    const int t = opaque_tid(), pg = t & 7, jx = 2 * (t >> 3);
+    const int t = opaque_tid() & 255, pg = t & 7, jx = 2 * (t >> 3);
     float v[2][8];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -425,7 +427,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   // E and S_in: whole 16-byte groups of their 64 x N slices; states past N
   // (and an absent S_in) read 0.
   auto issue_t1 = [&](int vh, T1Regs& r) {
-    const int t = opaque_tid() - 256;
+    const int t = opaque_tid() & 255;
     if (w == 4) {
       const size_t o = ((size_t)b * a.H + vh / a.ph) * a.Lp + l0 + lane;
       r.dl = a.dlT[o];
@@ -443,7 +445,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     }
   };
   auto commit_t1 = [&](const T1Regs& r) {
-    const int t = opaque_tid() - 256;
+    const int t = opaque_tid() & 255;
     if (w == 4) {
       const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.ls), 63));
       s_dl[lane] = r.dl;
@@ -582,7 +584,6 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         slice(std::integral_constant<int, 1>{});
       }
     }
-    if (next) issue_t0(vh + 1, p0);  // the next head's dyy and x, in flight until the stagings
 
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
     {
@@ -668,9 +669,10 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
           const int n0 = NT * 32 + 8 * k4 + 4 * hf;
-          const u32x2 bb = buf_load_u32x2(rb, n0 < a.N ? ((uint32_t)col * brow + (uint32_t)n0) * 2 : kOffNone);
-          up += xacc[4 * k4] * bf16_lo(bb[0]) + xacc[4 * k4 + 1] * bf16_hi(bb[0]) +
-                xacc[4 * k4 + 2] * bf16_lo(bb[1]) + xacc[4 * k4 + 3] * bf16_hi(bb[1]);
+          // B of step col, states n0 .. n0 + 3 (the staged rows past N are 0)
+          up += xacc[4 * k4] * bf16_to_f32(BT[tsw(n0, col)]) + xacc[4 * k4 + 1] * bf16_to_f32(BT[tsw(n0 + 1, col)]) +
+                xacc[4 * k4 + 2] * bf16_to_f32(BT[tsw(n0 + 2, col)]) +
+                xacc[4 * k4 + 3] * bf16_to_f32(BT[tsw(n0 + 3, col)]);
         }
         xacc *= s_f[col];
 #pragma unroll
@@ -691,7 +693,13 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 
     }  // team 0
     if constexpr (TEAM == 1) {
-    if (next) issue_t1(vh + 1, p1);  // the next head's E, S_in and step values, in flight until the stagings
+    // The next head's operands, in flight until the stagings (the products
+    // below read only LDS: a load's result would wait for every load issued
+    // before it).
+    if (next) {
+      issue_t1(vh + 1, p1);
+      issue_t0(vh + 1, p0);
+    }
     // ---- products 4: W^T (rows j in halves <= Q, columns i = col), with K^T
     // the row sums of Z, then (h^T dyy)^T for state tiles 2 sub + v.
     {
@@ -776,9 +784,10 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4) {
             const int n0 = NT * 32 + 8 * k4 + 4 * hf;
-            const u32x2 cc = buf_load_u32x2(rc, n0 < a.N ? ((uint32_t)col * brow + (uint32_t)n0) * 2 : kOffNone);
-            tp += cacc[4 * k4] * bf16_lo(cc[0]) + cacc[4 * k4 + 1] * bf16_hi(cc[0]) +
-                  cacc[4 * k4 + 2] * bf16_lo(cc[1]) + cacc[4 * k4 + 3] * bf16_hi(cc[1]);
+            // C of step col, states n0 .. n0 + 3 (the staged rows past N are 0)
+            tp += cacc[4 * k4] * bf16_to_f32(CT[tsw(n0, col)]) + cacc[4 * k4 + 1] * bf16_to_f32(CT[tsw(n0 + 1, col)]) +
+                  cacc[4 * k4 + 2] * bf16_to_f32(CT[tsw(n0 + 2, col)]) +
+                  cacc[4 * k4 + 3] * bf16_to_f32(CT[tsw(n0 + 3, col)]);
           }
           cacc *= ec;
         }
@@ -845,10 +854,10 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         }
       }
       if (next) {
-        if constexpr (TEAM == 0)
-          commit_t0(p0);
-        else
+        if constexpr (TEAM == 1) {
           commit_t1(p1);
+          commit_t0(p0);
+        }
         __syncthreads();
       }
     }
