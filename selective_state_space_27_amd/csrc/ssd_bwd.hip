@@ -287,7 +287,7 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 // 1 E and S_in before its products), and written to LDS (x, dyy as hi/lo in
 // two layouts, E and S_in as fp32 rows) between the two heads; the products
 // read LDS, and only the step-major B fragments of (G B)^T (L2-resident) and
-// the row segments of the outputs touch memory.  Wave 4 assembles each
+// the row segments of the outputs touch memory.  Wave 0 assembles each
 // head's ddelta and dA, dD parts between the heads.  Two teams of four waves
 // run concurrently: team 0 does products 1-3, team 1 products 4.  Wave
 // (team, q, sub): q the half of the block whose steps it owns as output
@@ -301,8 +301,23 @@ __global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
 //   products 4: W^T(j, i) for i in half q, j in halves <= q, with K^T the row
 //     sums of Z, then (h^T dyy)^T for the same state tiles -> dC part and
 //     C . (S_in^T dyy);
-//   then wave 4 (lane = step) assembles ddelta and the dA and dD parts.
-constexpr int kERow = kN + 4;  // row length (floats) of the E and S_in stagings
+//   then wave 0 (lane = step) assembles ddelta and the dA and dD parts.
+constexpr int kERow = kN + 4;  // row length (floats) of the E staging
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not first wait for this wave's direct-to-LDS loads (whose data only
+// the wave that issued them reads, after waiting for them itself).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Position of S_in element (row p, state n) in its staging: the two 64-state
+// halves one after the other, each as 64 rows of 64 states in 4-state groups;
+// in rows p with bit 3 set, bit 3 of the group index is flipped, so that a
+// column read of rows p and p + 8 by one wave touches every bank once.  A
+// direct-to-LDS load writes 64 consecutive groups (4 rows): the swizzle is
+// applied to the addresses it reads.
+__device__ __forceinline__ int ss_index(int p, int n) {
+  return (n >> 6) * (kP * 64) + p * 64 + (((((n & 63) >> 2) ^ (((p >> 3) & 1) << 3))) << 2) + (n & 3);
+}
 
 __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t dyRh[kSub][kRowP];  // dyy, step rows: hi
@@ -313,8 +328,11 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];     // C, state rows (tsw)
   __shared__ __attribute__((aligned(16))) uint16_t xs[kSub][kRowP];    // x, step rows
   __shared__ __attribute__((aligned(16))) float Es[kP * kERow];        // E [p][n] (0 past N)
-  __shared__ __attribute__((aligned(16))) float Ss[kP * kERow];        // S_in [p][n] (0 past N or absent)
-  __shared__ __attribute__((aligned(16))) float s_dl[kSub], s_ls[kSub], s_e[kSub], s_f[kSub];
+  __shared__ __attribute__((aligned(16))) float Ss[kP * kN];           // S_in (layout: ss_index; 0 past N)
+  // Step values of the block (delta, s, exp(s), exp(s_63 - s)), double-buffered
+  // over the heads: the next head's are written while this head's assembly
+  // still reads them.
+  __shared__ __attribute__((aligned(16))) float s_dl[2][kSub], s_ls[2][kSub], s_e[2][kSub], s_f[2][kSub];
   __shared__ float s_col[kSub], s_row[kSub], s_T[2][kSub], s_U[2][kSub], s_c[2][kSub];
   __shared__ float s_es[4], s_dd[4];
 
@@ -356,7 +374,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     u32x4 dy[2][2], z[2], x[2];
   };
   struct T1Regs {
-    u32x4 e[kP * kN / 4 / 256], s[kP * kN / 4 / 256];
+    u32x4 e[kP * kN / 4 / 256];
     float dl, ls;
   };
   // The staging addresses are formed from an opaque copy of the thread index
@@ -424,8 +442,10 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(&xs[st][pc]) = r.x[k];
     }
   };
-  // E and S_in: whole 16-byte groups of their 64 x N slices; states past N
-  // (and an absent S_in) read 0.
+  // The fewest loads from memory a team-1 wave issues for the next head's
+  // operands (E 8, dyy 4, x 2; z and the step values add to them).
+  constexpr int kOperandLoadsMin = kP * kN / 4 / 256 + 4 + 2;
+  // E: whole 16-byte groups of its 64 x N slice; states past N read 0.
   auto issue_t1 = [&](int vh, T1Regs& r) {
     const int t = opaque_tid() & 255;
     if (w == 4) {
@@ -433,31 +453,44 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       r.dl = a.dlT[o];
       r.ls = a.lsT[o];
     }
-    const float* Sp = sin_ptr(vh);
     const rsrc_t rE = make_rsrc(a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh), (uint32_t)(kP * a.N * 4));
-    const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
 #pragma unroll
     for (int it = 0; it < kP * kN / 4 / 256; ++it) {
       const int e4 = t + 256 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
-      const uint32_t o = n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone;
-      r.e[it] = buf_load_u32x4(rE, o);
-      r.s[it] = buf_load_u32x4(rS, o);
+      r.e[it] = buf_load_u32x4(rE, n < a.N ? ((uint32_t)pr * a.N + (uint32_t)n) * 4 : kOffNone);
     }
   };
-  auto commit_t1 = [&](const T1Regs& r) {
+  // S_in straight from memory into its staging (direct-to-LDS loads: no
+  // registers), by team 1, whose products alone read it: wave (q, sub) loads
+  // the half of the states it reads, 16 loads of 4 rows each (the two waves of
+  // a half write the same values).  States past N and an absent S_in are
+  // written as 0.  A wave's reads of the staging wait for its own loads.
+  auto dma_s = [&](int vh) {
+    const int t = opaque_tid() & 63;
+    const float* Sp = sin_ptr(vh);
+    const rsrc_t rS = make_rsrc(Sp, Sp ? (uint32_t)(kP * a.N * 4) : 0u);
+    const int pl = t >> 4, gs = t & 15;  // row in the load's 4, swizzled group
+#pragma unroll
+    for (int j = 0; j < kP / 4; ++j) {
+      const int p = 4 * j + pl, n = sub * 64 + ((gs ^ (((p >> 3) & 1) << 3)) << 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rS, (__attribute__((address_space(3))) void*)(Ss + sub * (kP * 64) + j * 256), 16,
+          n < a.N ? ((uint32_t)p * a.N + (uint32_t)n) * 4 : kOffNone, 0, 0, 0);
+    }
+  };
+  auto commit_t1 = [&](const T1Regs& r, int pw) {
     const int t = opaque_tid() & 255;
     if (w == 4) {
       const float ls63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.ls), 63));
-      s_dl[lane] = r.dl;
-      s_ls[lane] = r.ls;
-      s_e[lane] = exp2_fast(r.ls);
-      s_f[lane] = exp2_fast(ls63 - r.ls);
+      s_dl[pw][lane] = r.dl;
+      s_ls[pw][lane] = r.ls;
+      s_e[pw][lane] = exp2_fast(r.ls);
+      s_f[pw][lane] = exp2_fast(ls63 - r.ls);
     }
 #pragma unroll
     for (int it = 0; it < kP * kN / 4 / 256; ++it) {
       const int e4 = t + 256 * it, pr = e4 >> 5, n = (e4 & 31) * 4;
       *reinterpret_cast<u32x4*>(&Es[pr * kERow + n]) = r.e[it];
-      *reinterpret_cast<u32x4*>(&Ss[pr * kERow + n]) = r.s[it];
     }
   };
 
@@ -487,9 +520,10 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       commit_t0(r);
     } else {
       T1Regs r;
+      dma_s(vh0);
       issue_t1(vh0, r);
       stage_bc_transposed(a, a.B, b, g, l0, BT, threadIdx.x - 256);
-      commit_t1(r);
+      commit_t1(r, 0);
     }
 #pragma unroll
     for (int kk = 0; kk < kNK; ++kk) {
@@ -504,17 +538,23 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   auto frag_x = [&](int T, int kp) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(&xs[T * 32 + lc][kp * 16 + 8 * hf]);
   };
-  // Staged state slice (Es or Ss): rows p = PT*32 + lc, states kk*16 + 8hf .. +8.
+  // E staging: rows p = PT*32 + lc, states kk*16 + 8hf .. +8.
   auto ld_srow = [&](const float* S, int PT, int kk, float* v) {
     const float* r = S + (PT * 32 + lc) * kERow + kk * 16 + 8 * hf;
     const f32x4 v0 = *reinterpret_cast<const f32x4*>(r), v1 = *reinterpret_cast<const f32x4*>(r + 4);
     v[0] = v0[0], v[1] = v0[1], v[2] = v0[2], v[3] = v0[3], v[4] = v1[0], v[5] = v1[1], v[6] = v1[2], v[7] = v1[3];
   };
-  // Staged state slice: state n = NT*32 + lc, rows kp*16 + 8hf + t.
+  // E staging: state n = NT*32 + lc, rows kp*16 + 8hf + t.
   auto ld_scol = [&](const float* S, int NT, int kp, float* v) {
     const float* r = S + (kp * 16 + 8 * hf) * kERow + NT * 32 + lc;
 #pragma unroll
     for (int t = 0; t < 8; ++t) v[t] = r[t * kERow];
+  };
+  // S_in staging: state n = NT*32 + lc, rows kp*16 + 8hf + t.
+  auto ld_scol_s = [&](int NT, int kp, float* v) {
+    const float* r = Ss + ss_index(kp * 16 + 8 * hf, NT * 32 + lc);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = r[t * 64];
   };
   auto lds4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
 
@@ -522,12 +562,13 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   // The chunk's dB (team 0) or dC (team 1) part for state tiles 2 sub + v, column col.
   f32x16 dacc[2] = {};
 
-  auto body = [&](auto qtag, auto team_tag, int vh, bool next, T0Regs& p0, T1Regs& p1) {
+  int par = 0;  // the current head's buffer of the step values
+  auto body = [&](auto qtag, auto team_tag, int vh, bool next, T0Regs& p0, T1Regs& p1, const u32x4* fb1) {
     constexpr int Q = decltype(qtag)::value;
     constexpr int NI = 2 - Q;  // row halves Q..1 (products 1)
     constexpr int NJ = Q + 1;  // row halves 0..Q (products 4)
     constexpr int TEAM = decltype(team_tag)::value;
-    const float ls_c = s_ls[col], dl_c = s_dl[col];
+    const float ls_c = s_ls[par][col], dl_c = s_dl[par][col];
 
     if constexpr (TEAM == 0) {
     // ---- products 1: W, rows i in halves >= Q, columns j = col
@@ -550,7 +591,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
           const int i0 = (Q + u) * 32 + 8 * k4 + 4 * hf;
-          const f32x4 lsi = lds4(&s_ls[i0]);
+          const f32x4 lsi = lds4(&s_ls[par][i0]);
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             const float m = (i0 + qq > col) ? exp2_fast(lsi[qq] - ls_c) : 0.f;
@@ -569,7 +610,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
           acc_kslice<S>(kk2[u], kv);
           acc_kslice<S>(wacc[u], wv);
           const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
-          const f32x4 l0v = lds4(&s_ls[i0]), l1v = lds4(&s_ls[i0 + 4]);
+          const f32x4 l0v = lds4(&s_ls[par][i0]), l1v = lds4(&s_ls[par][i0 + 4]);
           const float lsi[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
@@ -594,11 +635,11 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         ld_srow(Es, sub, kk, ev);
         u32x4 eh, el;
         split8(ev, eh, el, dm);
-        const u32x4 bop = frag_bc(rb, Q, kk);
+        const u32x4 bop = Q == 1 ? fb1[kk] : frag_bc(rb, Q, kk);
         gacc = mfma(eh, bop, gacc);
         gacc = mfma(el, bop, gacc);
       }
-      gacc *= s_f[col];
+      gacc *= s_f[par][col];
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
 #pragma unroll
@@ -611,31 +652,25 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
           gacc = mfma(ah, mkl[u][S], gacc);
         }
       }
-      // dx, x . (G B) and dyy . x for (step col, rows p).
-      const size_t xb = xbase(vh);
-      const rsrc_t rdy = make_rsrc(a.dy + xb, left * xrow * 4);
-      const rsrc_t rz = make_rsrc(a.z ? a.z + xb : nullptr, a.z ? left * xrow * 2 : 0u);
-      const rsrc_t rdx = make_rsrc(a.dx + xb, left * xrow * 4);
+      // dx, x . (G B) and dyy . x for (step col, rows p); dyy as its staged
+      // hi + lo pair (within 2^-17 of the fp32 value).
+      const rsrc_t rdx = make_rsrc(a.dx + xbase(vh), left * xrow * 4);
       const float Dh = a.D ? a.D[vh / a.ph] : 0.f;
       float cp = 0.f, dd = 0.f;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        const uint32_t o = (uint32_t)col * xrow + (uint32_t)(sub * 32 + 8 * k4 + 4 * hf);
-        const f32x4 dyv = as_f32x4(buf_load_u32x4(rdy, o * 4));
-        const u32x2 xx = *reinterpret_cast<const u32x2*>(&xs[col][sub * 32 + 8 * k4 + 4 * hf]);
+        const int p0 = sub * 32 + 8 * k4 + 4 * hf;
+        const uint32_t o = (uint32_t)col * xrow + (uint32_t)p0;
+        const u32x2 xx = *reinterpret_cast<const u32x2*>(&xs[col][p0]);
+        const u32x2 yh = *reinterpret_cast<const u32x2*>(&dyRh[col][p0]);
+        const u32x2 yl = *reinterpret_cast<const u32x2*>(&dyRl[col][p0]);
         const float xv[4] = {bf16_lo(xx[0]), bf16_hi(xx[0]), bf16_lo(xx[1]), bf16_hi(xx[1])};
-        float sz[4] = {1.f, 1.f, 1.f, 1.f};
-        if (a.z) {
-          const u32x2 zz = buf_load_u32x2(rz, o * 2);
-          sz[0] = silu(bf16_lo(zz[0]));
-          sz[1] = silu(bf16_hi(zz[0]));
-          sz[2] = silu(bf16_lo(zz[1]));
-          sz[3] = silu(bf16_hi(zz[1]));
-        }
+        const float yv[4] = {bf16_lo(yh[0]) + bf16_lo(yl[0]), bf16_hi(yh[0]) + bf16_hi(yl[0]),
+                             bf16_lo(yh[1]) + bf16_lo(yl[1]), bf16_hi(yh[1]) + bf16_hi(yl[1])};
         f32x4 dxv;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const float gb = gacc[4 * k4 + qq], dyy = dyv[qq] * sz[qq];
+          const float gb = gacc[4 * k4 + qq], dyy = yv[qq];
           cp += xv[qq] * gb;
           dd += dyy * xv[qq];
           dxv[qq] = dl_c * gb + Dh * dyy;
@@ -674,7 +709,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
                 xacc[4 * k4 + 2] * bf16_to_f32(BT[tsw(n0 + 2, col)]) +
                 xacc[4 * k4 + 3] * bf16_to_f32(BT[tsw(n0 + 3, col)]);
         }
-        xacc *= s_f[col];
+        xacc *= s_f[par][col];
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
 #pragma unroll
@@ -724,7 +759,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4) {
             const int j0 = u * 32 + 8 * k4 + 4 * hf;
-            const f32x4 lsj = lds4(&s_ls[j0]), dlj = lds4(&s_dl[j0]);
+            const f32x4 lsj = lds4(&s_ls[par][j0]), dlj = lds4(&s_dl[par][j0]);
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const float m = (j0 + qq < col) ? exp2_fast(ls_c - lsj[qq]) * dlj[qq] : 0.f;
@@ -742,8 +777,8 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
             float v[8];
             acc_kslice<S>(wt[u], v);
             const int j0 = u * 32 + 16 * S + 8 * hf;
-            const f32x4 l0v = lds4(&s_ls[j0]), l1v = lds4(&s_ls[j0 + 4]);
-            const f32x4 d0v = lds4(&s_dl[j0]), d1v = lds4(&s_dl[j0 + 4]);
+            const f32x4 l0v = lds4(&s_ls[par][j0]), l1v = lds4(&s_ls[par][j0 + 4]);
+            const f32x4 d0v = lds4(&s_dl[par][j0]), d1v = lds4(&s_dl[par][j0 + 4]);
             const float lsj[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
             const float dlj[8] = {d0v[0], d0v[1], d0v[2], d0v[3], d1v[0], d1v[1], d1v[2], d1v[3]};
 #pragma unroll
@@ -755,8 +790,16 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         }
       }
       const bool has_sin = sin_ptr(vh) != nullptr;
+      // This wave's direct-to-LDS loads of S_in (issued before this head
+      // began) must have landed; the compiler does not track them over the
+      // head loop.  Only the next head's operand loads, issued after them, may
+      // still be in flight.
+      if (next)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOperandLoadsMin) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       float tp = 0.f, es = 0.f;
-      const float ec = s_e[col];
+      const float ec = s_e[par][col];
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         const int NT = 2 * sub + v;
@@ -766,7 +809,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
           for (int kp = 0; kp < kP / 16; ++kp) {
             float sv[8];
-            ld_scol(Ss, NT, kp, sv);
+            ld_scol_s(NT, kp, sv);
             if (Q == 0) {  // <E, S_in>: each element once, over the two Q = 0 waves
               float ev[8];
               ld_scol(Es, NT, kp, ev);
@@ -815,8 +858,16 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   // that do not change over the heads then stay its own).
   auto run = [&](auto qtag, auto team_tag) {
     constexpr int TEAM = decltype(team_tag)::value;
+    constexpr int Q = decltype(qtag)::value;
     T0Regs p0;
     T1Regs p1;
+    // The half-1 waves of team 0 (registers to spare) keep the B fragments of
+    // (G B)^T over the heads; the half-0 waves load them for every head.
+    u32x4 fb1[TEAM == 0 && Q == 1 ? kNK : 1];
+    if constexpr (TEAM == 0 && Q == 1) {
+#pragma unroll
+      for (int kk = 0; kk < kNK; ++kk) fb1[kk] = frag_bc(rb, 1, kk);
+    }
     for (int i = 0; i < a.hpw; ++i) {
       const int vh = vh0 + i;
       const bool next = i + 1 < a.hpw;
@@ -824,15 +875,16 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       // then formed again for every head instead of being held over the loop.
       asm volatile("" : "+v"(lane), "+v"(lc), "+v"(hf));
       col = q * 32 + lc;
-      body(qtag, team_tag, vh, next, p0, p1);
+      par = i & 1;
+      body(qtag, team_tag, vh, next, p0, p1, fb1);
       __syncthreads();
 
-      // ---- ddelta and the dA, dD parts (lane = step of the block).  The next
-      // head's stagings (after this) rewrite only the LDS that this wave alone
-      // reads here after it.
-      if (w == 4) {
+      // ---- ddelta and the dA, dD parts (lane = step of the block), by wave 0
+      // while team 1 writes the next head's stagings (no LDS that this reads:
+      // the step values are double-buffered).
+      if (w == 0) {
         const int t = lane;
-        const float dl = s_dl[t], e = s_e[t], f = s_f[t];
+        const float dl = s_dl[par][t], e = s_e[par][t], f = s_f[par][t];
         const float cprime = s_c[0][t] + s_c[1][t];
         const float cr = s_col[t] - s_row[t];
         const float corner = wave_prefix_sum(cr) - cr;  // R_t: sum over u < t
@@ -855,10 +907,13 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       }
       if (next) {
         if constexpr (TEAM == 1) {
-          commit_t1(p1);
+          commit_t1(p1, par ^ 1);
           commit_t0(p0);
+          // After the writes above: a write to LDS waits for the direct-to-LDS
+          // loads issued before it.
+          dma_s(vh + 1);
         }
-        __syncthreads();
+        barrier_lds();
       }
     }
   };
