@@ -498,7 +498,9 @@ __device__ __forceinline__ void diag_part(f32x16& yacc, const uint16_t (*Cs)[kN 
   if constexpr (S0 <= 1 && S1 > 1) slice(std::integral_constant<int, 1>{});
 }
 
-template <bool HAS_Z, bool HAS_D, bool ACCUM>
+// Y = false: the states only (chunk_states, h_last), no output: the block
+// products that form y are skipped, and C is not read.
+template <bool HAS_Z, bool HAS_D, bool ACCUM, bool Y = true>
 __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xT[kP * kTRow];  // tsw layout, headdim rows
   __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];  // tsw layout, state rows
@@ -590,8 +592,8 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   const size_t hoff = row_el(a, vh, 0);
   const size_t bh_el = (size_t)b * a.L * a.H * a.P + hoff;
   const uint32_t ybytes = (uint32_t)(((size_t)a.L * a.H * a.P - hoff) * 4);
-  // y may be null inside the library (the backward's state pass without a
-  // gate needs no output): a zero-size descriptor then drops every store.
+  // y is null only in the states-only instantiation (the backward's state
+  // pass without a gate needs no output), which stores none.
   const rsrc_t ry = make_rsrc(a.y ? a.y + bh_el : nullptr, a.y ? ybytes : 0u);
   const rsrc_t rz = make_rsrc(a.z ? a.z + bh_el : nullptr, a.z ? ybytes / 2 : 0u);
   // Row r of this lane's accumulator tile is step lprev + rt*32 + 4*hf +
@@ -635,13 +637,17 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   float d, ls;
   load_x(lbeg, xr);
   load_bc_rows(a, a.B, b, lbeg, bco, br);
-  load_bc_rows(a, a.C, b, lbeg, bco, cr);
+  if constexpr (Y) load_bc_rows(a, a.C, b, lbeg, bco, cr);
   load_dls(lbeg, d, ls);  // every wave loads them (no branch around loads); wave 0 uses them
   for (int l0 = lbeg; l0 < lend; l0 += kSub) {
-    finish();  // the previous block (its xbuf entries were written before the last barrier)
+    if constexpr (Y) finish();  // the previous block (its xbuf entries were written before the last barrier)
     store_x(xr);
-    store_bc_rows<true, true>(br, Bs, BT);
-    store_bc_rows<true, false>(cr, Cs, nullptr);
+    if constexpr (Y) {
+      store_bc_rows<true, true>(br, Bs, BT);
+      store_bc_rows<true, false>(cr, Cs, nullptr);
+    } else {
+      store_bc_rows<false, true>(br, nullptr, BT);
+    }
     if (w == 0) {
       // e_i = exp(s_i), w_j = delta_j exp(s_last - s_j), decay = exp(s_last).
       const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 63));
@@ -661,6 +667,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     load_dls(l0 + kSub, d, ls);
     __syncthreads();
 
+    if constexpr (Y) {
     // C S^T over this wave's state rows for both row tiles, the state as hi + lo.
     f32x16 yown = {}, yoth = {};
 #pragma unroll
@@ -730,6 +737,10 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       }
     }
     lprev = l0;
+    } else {  // the next block's loads
+      load_x(l0 + kSub, xr);
+      load_bc_rows(a, a.B, b, l0 + kSub, bco, br);
+    }
 
     // State after the block: S^T <- decay S^T + B^T (w o x).
     const float decay = s_decay;
@@ -766,7 +777,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     }
     __syncthreads();
   }
-  finish();
+  if constexpr (Y) finish();
   if (a.h_last && piece == a.npieces - 1) {
     float* hl = a.h_last + state_el(a, b, vh);
 #pragma unroll
@@ -884,8 +895,12 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
       else if (hd) hipLaunchKernelGGL((ssd_scan_kernel<false, true, ACC>), grid, dim3(kT), 0, stream, a);
       else hipLaunchKernelGGL((ssd_scan_kernel<false, false, ACC>), grid, dim3(kT), 0, stream, a);
     };
-    if (a.accumulate) go(std::true_type{});
-    else go(std::false_type{});
+    if (a.y == nullptr)
+      hipLaunchKernelGGL((ssd_scan_kernel<false, false, false, false>), grid, dim3(kT), 0, stream, a);
+    else if (a.accumulate)
+      go(std::true_type{});
+    else
+      go(std::false_type{});
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
