@@ -33,15 +33,15 @@
 // Passes:
 //   1. the forward kernels with 64-step chunks: the state after every block
 //      and, with a gate, the ungated output (for dz);
-//   2. ssd_bwd_local_kernel: per (block, virtual head) the block's own part of
-//      the adjoint handed to the block before, F = sum_i exp(s_i) dyy_i C_i^T,
-//      and dz;
-//   3. ssd_bwd_chain_kernel: E along the sequence, from the last block to the
-//      first: E_{k-1} = exp(s_63 of block k) E_k + F_k (dh0 at the end);
-//   4. ssd_bwd_grad_kernel: per (block, chunk of a group's virtual heads)
+//   2. E along the sequence, from the last block to the first: E_{k-1} =
+//      exp(s_63 of block k) E_k + F_k with F_k = sum_i exp(s_i) dyy_i C_i^T
+//      (the block's own part of the adjoint handed to the block before), cut
+//      into pieces of blocks: each piece's sum from zero, a chain over the
+//      pieces, then every block's E from its piece's (dh0 and dz on the way);
+//   3. ssd_bwd_grad_kernel: per (block, chunk of a group's virtual heads)
 //      every gradient above on the matrix cores; dB and dC as per-chunk
 //      parts, ddelta, dA and dD as per-virtual-head parts;
-//   5. fixed-order sums of those parts (the results are bitwise repeatable).
+//   4. fixed-order sums of those parts (the results are bitwise repeatable).
 // Operands that are not exact bf16 inputs enter the matrix cores as bf16
 // hi/lo pairs (two products, three when both operands are split).
 #include <algorithm>
@@ -82,7 +82,9 @@ struct BwdArgs {
   const float* lsT;       // [b, H, Lp]: A log2(e) times the prefix sum of delta inside each 64-step block
   const float* yf;        // [b, L, H, P]: the forward output before the gate
   const float* Sblk;      // [b, nblk, H, P, N]: the state after every block
-  float* Eblk;            // [b, nblk, H, P, N]: F of every block, then the adjoint E arriving at it
+  float* Eblk;            // [b, nblk, H, P, N]: the adjoint E arriving at every block
+  float* Ep;              // [b, npc, H, P, N]: each piece's sum from zero, then the E arriving at its last block
+  float* Dp;              // [b, npc, Hv]: each piece's decay (log2)
   float* dBp;             // [b, L, G * cpg, N]: per-chunk parts of dB (hpw virtual heads each)
   float* dCp;             // [b, L, G * cpg, N]: of dC
   float* ddp;             // [b, L, Hv]: of ddelta
@@ -90,6 +92,7 @@ struct BwdArgs {
   float* dDp;             // [b, nblk, Hv]: of dD
   int batch, L, H, G, P, ph, Hv, N, nblk, Lp;
   int hpw, cpg, Gc;       // virtual heads per gradient workgroup, chunks per group, G * cpg
+  int npc, bpp;           // pieces per sequence for E, blocks per piece
 };
 
 // Element offset, inside one step's [H, P] row, of row 0 of virtual head vh
@@ -187,95 +190,153 @@ __device__ __forceinline__ void load_dyy(const BwdArgs& a, int b, int vh, int l0
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2.  grid (nblk * Hv, batch), 256 threads: F^T = C^T (e o dyy) for one
-// (block, virtual head), e_i = exp(s_i), written over the workspace slot of
-// the block; wave w forms state rows w*32.. for both 32-row headdim tiles.
-__global__ void __launch_bounds__(256) ssd_bwd_local_kernel(BwdArgs a) {
+// Pass 2: the adjoint E arriving at every block.  Along the sequence
+// E_{k-1} = exp2(ls_63(k)) E_k + F_k, with block k's own part F_k =
+// sum_i exp(s_i) dyy_i C_i^T; the blocks are cut into pieces of bpp, and F
+// is formed where it is needed (twice) instead of being stored.
+//   ssd_bwd_piece_kernel<false>: per (piece, virtual head) the recurrence
+//     from zero over the piece's blocks, last to first: its result P into the
+//     piece's slot of Ep and the piece's decay (log2) into Dp; dz.
+//   ssd_bwd_piece_chain_kernel: along the pieces, last to first, the E
+//     arriving at each piece's last block, E_top(j-1) = exp2(Dp_j) E_top(j) +
+//     P_j, written over P_j; what arrives before the first block is dh0.
+//   ssd_bwd_piece_kernel<true>: per (piece, virtual head) from E_top down
+//     the piece, the E arriving at every block into its slot of Eblk.
+// grid (npc * Hv, batch), 256 threads.  Wave w forms the states w*32.. (its
+// lanes) of F for both 32-row headdim tiles (its registers) and keeps the
+// same elements of E: a register of the tile is one row segment of 32
+// states, so E is read and written in whole 128-byte lines (waves with
+// w*32 >= N only stage).
+template <bool WRITE_E>
+__global__ void __launch_bounds__(256) ssd_bwd_piece_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t gh[kP * kTRow];  // e o dyy, headdim rows (tsw): hi
   __shared__ __attribute__((aligned(16))) uint16_t gl[kP * kTRow];  // lo
   __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];  // C, state rows (tsw)
-  const int vh = blockIdx.x % a.Hv, blk = blockIdx.x / a.Hv, b = blockIdx.y;
+  const int vh = blockIdx.x % a.Hv, pc = blockIdx.x / a.Hv, b = blockIdx.y;
   const int h = vh / a.ph, g = h / (a.H / a.G);
-  const int l0 = blk * kSub;
-  const int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
+  const int k0 = pc * a.bpp, k1 = min(a.nblk, k0 + a.bpp) - 1;
+  int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Dot2Masks dm = dot2_masks();
-  {
-    const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
-    float v[2][8];
-    load_dyy(a, b, vh, l0, jx, pg, v, true);
-    const float* ls = a.lsT + ((size_t)b * a.H + h) * a.Lp + l0 + jx;
-    const float e0 = exp2_fast(ls[0]), e1 = exp2_fast(ls[1]);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t hi, lo;
-      split2(v[0][k] * e0, v[1][k] * e1, hi, lo, dm);
-      *reinterpret_cast<uint32_t*>(&gh[tsw(pg * 8 + k, jx)]) = hi;
-      *reinterpret_cast<uint32_t*>(&gl[tsw(pg * 8 + k, jx)]) = lo;
-    }
-  }
-  stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
-  __syncthreads();
   const int nt = w;
-  if (nt * 32 >= a.N) return;
-  f32x16 acc[2] = {};
+  const bool act = nt * 32 < a.N;
+  const float* ls_row = a.lsT + ((size_t)b * a.H + h) * a.Lp;  // + l: s of step l, log2
+  float* top = a.Ep + sbase(a, (size_t)b * a.npc + pc, vh);
+  // Element (row p, state n) of a 64 x N slice held as register r of tile pt:
+  // p = pt*32 + 8(r >> 2) + 4hf + (r & 3), n = nt*32 + lc.
+  int n_l = nt * 32 + lc;
+  const bool n_ok = n_l < a.N;
+  auto tile_off = [&](int pt, int r) { return (size_t)(pt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)) * a.N + n_l; };
+  f32x16 E[2];
 #pragma unroll
-  for (int kk = 0; kk < kSub / 16; ++kk) {
-    const int j0 = kk * 16 + 8 * hf;
-    const u32x4 av = *reinterpret_cast<const u32x4*>(&CT[tsw(nt * 32 + lc, j0)]);
+  for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      acc[pt] = mfma(av, *reinterpret_cast<const u32x4*>(&gh[tsw(pt * 32 + lc, j0)]), acc[pt]);
-      acc[pt] = mfma(av, *reinterpret_cast<const u32x4*>(&gl[tsw(pt * 32 + lc, j0)]), acc[pt]);
-    }
+    for (int r = 0; r < 16; ++r) E[pt][r] = (WRITE_E && n_ok) ? top[tile_off(pt, r)] : 0.f;
   }
-  float* dst = a.Eblk + sbase(a, (size_t)b * a.nblk + blk, vh);
+  float dsum = 0.f;  // log2 of the piece's decay
+  for (int k = k1; k >= k0; --k) {
+    if constexpr (WRITE_E) {
+      // Opaque copies of the lane indexes: the 32 store addresses are formed
+      // again for every block instead of being held over the loop.
+      asm volatile("" : "+v"(hf), "+v"(n_l));
+      if (n_ok) {
+        float* dst = a.Eblk + sbase(a, (size_t)b * a.nblk + k, vh);
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt) store_stateT(acc[pt], dst, nt, pt, a.N, a.N);
+        for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[tile_off(pt, r)] = E[pt][r];
+        }
+      }
+      if (k == k0) break;
+    }
+    const int l0 = k * kSub;
+    {
+      const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
+      float v[2][8];
+      load_dyy(a, b, vh, l0, jx, pg, v, !WRITE_E);
+      const float e0 = exp2_fast(ls_row[l0 + jx]), e1 = exp2_fast(ls_row[l0 + jx + 1]);
+#pragma unroll
+      for (int kq = 0; kq < 8; ++kq) {
+        uint32_t hi, lo;
+        split2(v[0][kq] * e0, v[1][kq] * e1, hi, lo, dm);
+        *reinterpret_cast<uint32_t*>(&gh[tsw(pg * 8 + kq, jx)]) = hi;
+        *reinterpret_cast<uint32_t*>(&gl[tsw(pg * 8 + kq, jx)]) = lo;
+      }
+    }
+    stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
+    const float ls63 = ls_row[l0 + kSub - 1];
+    dsum += ls63;
+    __syncthreads();
+    if (act) {
+      f32x16 acc[2] = {};
+#pragma unroll
+      for (int kk = 0; kk < kSub / 16; ++kk) {
+        const int j0 = kk * 16 + 8 * hf;
+        const u32x4 cv = *reinterpret_cast<const u32x4*>(&CT[tsw(nt * 32 + lc, j0)]);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          acc[pt] = mfma(*reinterpret_cast<const u32x4*>(&gh[tsw(pt * 32 + lc, j0)]), cv, acc[pt]);
+          acc[pt] = mfma(*reinterpret_cast<const u32x4*>(&gl[tsw(pt * 32 + lc, j0)]), cv, acc[pt]);
+        }
+      }
+      const float dq = exp2_fast(ls63);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) E[pt] = E[pt] * dq + acc[pt];
+    }
+    __syncthreads();  // the stagings are rewritten for the next block
+  }
+  if constexpr (!WRITE_E) {
+    if (n_ok) {
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) top[tile_off(pt, r)] = E[pt][r];
+      }
+    }
+    if (threadIdx.x == 0) a.Dp[((size_t)b * a.npc + pc) * a.Hv + vh] = dsum;
+  }
 }
 
-// ---------------------------------------------------------------------------
-// Pass 3.  grid (ceil(16 N / 256) * Hv, batch), 256 threads, 4 state elements
-// per thread: from the last block to the first, the slot of block k receives
-// E_k (dh_last, or 0, for the last block) and E_{k-1} = exp2(ls_63(k)) E_k +
-// F_k; what arrives before block 0 is dh0.  Four blocks are loaded ahead.
-__global__ void __launch_bounds__(256) ssd_bwd_chain_kernel(BwdArgs a) {
+// grid (ceil(16 N / 256) * Hv, batch), 256 threads, 4 state elements per
+// thread: from the last piece to the first (the slots hold P_j, loaded four
+// pieces ahead).
+__global__ void __launch_bounds__(256) ssd_bwd_piece_chain_kernel(BwdArgs a) {
   const int xb = (16 * a.N + 255) / 256;
-  const int vh = blockIdx.x / xb, b = blockIdx.y, h = vh / a.ph;
+  const int vh = blockIdx.x / xb, b = blockIdx.y;
   const int e = ((blockIdx.x % xb) * 256 + threadIdx.x) * 4;
   if (e >= kP * a.N) return;
-  const size_t stride = (size_t)a.H * a.P * a.N;  // from one block's slot to the next
-  float* E0 = a.Eblk + sbase(a, (size_t)b * a.nblk, vh) + e;
-  const float* last = a.lsT + ((size_t)b * a.H + h) * a.Lp + (kSub - 1);  // + k*64: block k's decay (log2)
+  const size_t stride = (size_t)a.H * a.P * a.N;  // from one piece's slot to the next
+  float* E0 = a.Ep + sbase(a, (size_t)b * a.npc, vh) + e;
+  const float* dp = a.Dp + (size_t)b * a.npc * a.Hv + vh;  // + j*Hv: piece j's decay (log2)
   f32x4 E = a.dh_last ? *reinterpret_cast<const f32x4*>(a.dh_last + sbase(a, b, vh) + e) : f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 F[4];
+  f32x4 P[4];
   float dq[4];
-  auto fetch = [&](int k, int s) {
-    if (k >= 0) {
-      F[s] = *reinterpret_cast<const f32x4*>(E0 + (size_t)k * stride);
-      dq[s] = last[(size_t)k * kSub];
+  auto fetch = [&](int j, int s) {
+    if (j >= 0) {
+      P[s] = *reinterpret_cast<const f32x4*>(E0 + (size_t)j * stride);
+      dq[s] = dp[(size_t)j * a.Hv];
     }
   };
-  int k = a.nblk - 1;
+  int j = a.npc - 1;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) fetch(k - s, s);
-  for (; k >= 0; k -= 4) {
+  for (int s = 0; s < 4; ++s) fetch(j - s, s);
+  for (; j >= 0; j -= 4) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int kk = k - s;
-      if (kk < 0) break;
-      const f32x4 f = F[s];
+      const int jj = j - s;
+      if (jj < 0) break;
+      const f32x4 p = P[s];
       const float d = dq[s];
-      fetch(kk - 4, s);
-      *reinterpret_cast<f32x4*>(E0 + (size_t)kk * stride) = E;
-      E = E * exp2_fast(d) + f;
+      fetch(jj - 4, s);
+      *reinterpret_cast<f32x4*>(E0 + (size_t)jj * stride) = E;
+      E = E * exp2_fast(d) + p;
     }
   }
   if (a.dh0) *reinterpret_cast<f32x4*>(a.dh0 + sbase(a, b, vh) + e) = E;
 }
 
 // ---------------------------------------------------------------------------
-// Pass 4.  grid (nblk * G * cpg, batch), 512 threads, one workgroup per CU:
+// Pass 3.  grid (nblk * G * cpg, batch), 512 threads, one workgroup per CU:
 // every gradient of one 64-step block for hpw consecutive virtual heads of
 // one group (cpg = the group's virtual heads / hpw chunks).  B and C are the
 // same for all of them: they are staged once, and K = C B^T (the only product
@@ -942,7 +1003,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 5: fixed-order sums of the parts.
+// Pass 4: fixed-order sums of the parts.
 // dB and dC: grid-stride over (b, l, g, 4 states), the group's chunks summed
 // in order.
 __global__ void __launch_bounds__(256) ssd_bwd_reduce_bc_kernel(BwdArgs a) {
@@ -1006,8 +1067,17 @@ __global__ void __launch_bounds__(256) ssd_bwd_reduce_head_kernel(BwdArgs a) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t fwd, yf, Sblk, Eblk, dBp, dCp, ddp, dAp, dDp, total;
+  size_t fwd, yf, Sblk, Eblk, Ep, Dp, dBp, dCp, ddp, dAp, dDp, total;
 };
+
+// Pieces of blocks for the adjoint passes: about 2560 (piece, virtual head,
+// batch) workgroups (ten per CU), whole blocks each.
+void e_pieces(int64_t batch, int64_t vheads, int64_t nblk, int& npc, int& bpp) {
+  const int64_t streams = batch * vheads;
+  const int64_t np = std::max<int64_t>(1, std::min<int64_t>((2560 + streams - 1) / streams, nblk));
+  bpp = (int)((nblk + np - 1) / np);
+  npc = (int)((nblk + bpp - 1) / bpp);
+}
 
 // Virtual heads per gradient workgroup: the largest divisor of a group's
 // virtual heads that still leaves 8 workgroups per CU (2048 for 256 CUs), or 1.
@@ -1037,7 +1107,11 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
   l.yf = align256(ssd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, kSub));
   l.Sblk = l.yf + align256((size_t)batch * seqlen * nheads * headdim * f4);
   l.Eblk = l.Sblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
-  l.dBp = l.Eblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
+  int npc, bpp;
+  e_pieces(batch, vheads, nblk, npc, bpp);
+  l.Ep = l.Eblk + align256((size_t)batch * nblk * nheads * headdim * dstate * f4);
+  l.Dp = l.Ep + align256((size_t)batch * npc * nheads * headdim * dstate * f4);
+  l.dBp = l.Dp + align256((size_t)batch * npc * vheads * f4);
   l.dCp = l.dBp + align256((size_t)batch * seqlen * chunks * dstate * f4);
   l.ddp = l.dCp + align256((size_t)batch * seqlen * chunks * dstate * f4);
   l.dAp = l.ddp + align256((size_t)batch * seqlen * vheads * f4);
@@ -1109,6 +1183,8 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream) {
   a.yf = reinterpret_cast<const float*>(ws + l.yf);
   a.Sblk = reinterpret_cast<const float*>(ws + l.Sblk);
   a.Eblk = reinterpret_cast<float*>(ws + l.Eblk);
+  a.Ep = reinterpret_cast<float*>(ws + l.Ep);
+  a.Dp = reinterpret_cast<float*>(ws + l.Dp);
   a.dBp = reinterpret_cast<float*>(ws + l.dBp);
   a.dCp = reinterpret_cast<float*>(ws + l.dCp);
   a.ddp = reinterpret_cast<float*>(ws + l.ddp);
@@ -1127,11 +1203,14 @@ hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream) {
   a.hpw = grad_heads_per_wg(a.batch, a.nblk, a.Hv, a.G);
   a.cpg = a.Hv / a.G / a.hpw;
   a.Gc = a.G * a.cpg;
+  e_pieces(a.batch, a.Hv, a.nblk, a.npc, a.bpp);
 
-  const dim3 blocks((unsigned)a.nblk * (unsigned)a.Hv, (unsigned)a.batch);
-  hipLaunchKernelGGL(ssd_bwd_local_kernel, blocks, dim3(256), 0, stream, a);
+  const dim3 pieces((unsigned)a.npc * (unsigned)a.Hv, (unsigned)a.batch);
+  hipLaunchKernelGGL(ssd_bwd_piece_kernel<false>, pieces, dim3(256), 0, stream, a);
   const unsigned xb = (unsigned)((16 * a.N + 255) / 256);
-  hipLaunchKernelGGL(ssd_bwd_chain_kernel, dim3(xb * (unsigned)a.Hv, (unsigned)a.batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_bwd_piece_chain_kernel, dim3(xb * (unsigned)a.Hv, (unsigned)a.batch), dim3(256), 0, stream,
+                     a);
+  hipLaunchKernelGGL(ssd_bwd_piece_kernel<true>, pieces, dim3(256), 0, stream, a);
   hipLaunchKernelGGL(ssd_bwd_grad_kernel, dim3((unsigned)a.nblk * (unsigned)a.Gc, (unsigned)a.batch), dim3(512), 0,
                      stream, a);
   hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(stride_grid((size_t)a.batch * a.L * a.G * (a.N / 4))), dim3(256),
