@@ -565,17 +565,31 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
     }
   };
 
-  // This wave's two S^T tiles: state rows (2*rt + t)*32.., headdim tile pt,
-  // from the exact state entering the piece (piece 0: h0 or zero).
+  // This wave's two state tiles: state rows (2*rt + t)*32.., headdim tile pt,
+  // from the exact state entering the piece (piece 0: h0 or zero); as S^T
+  // tiles (the operand of C S^T), or with no output as S tiles (stored in
+  // whole lines).
   f32x16 st[2];
+  auto load_st = [&](f32x16& acc, const float* S, int nt, int ld, int nmax) {
+    if constexpr (Y)
+      load_stateT(acc, S, nt, pt, ld, nmax);
+    else
+      load_stateS(acc, S, nt, pt, ld, nmax);
+  };
+  auto store_st = [&](const f32x16& acc, float* S, int nt) {
+    if constexpr (Y)
+      store_stateT(acc, S, nt, pt, a.N, nvalid);
+    else
+      store_stateS(acc, S, nt, pt, a.N, nvalid);
+  };
   if (piece == 0) {
     const float* s0 = a.h0 ? a.h0 + state_el(a, b, vh) : nullptr;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) load_stateT(st[t], s0, 2 * rt + t, pt, a.N, nvalid);
+    for (int t = 0; t < 2; ++t) load_st(st[t], s0, 2 * rt + t, a.N, nvalid);
   } else {
     const float* ps = a.pstart + (((size_t)b * a.Hv + vh) * a.npieces + piece) * state_stride;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) load_stateT(st[t], ps, 2 * rt + t, pt);
+    for (int t = 0; t < 2; ++t) load_st(st[t], ps, 2 * rt + t, kN, kN);
   }
 
   // Output of the previous block, finished at the start of the next one (the
@@ -760,8 +774,13 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const u32x4 av = *reinterpret_cast<const u32x4*>(&BT[tsw((2 * rt + t) * 32 + lc, j0)]);
-        st[t] = mfma(av, bh, st[t]);
-        st[t] = mfma(av, bl, st[t]);
+        if constexpr (Y) {
+          st[t] = mfma(av, bh, st[t]);
+          st[t] = mfma(av, bl, st[t]);
+        } else {  // S <- S + (w o x)^T B
+          st[t] = mfma(bh, av, st[t]);
+          st[t] = mfma(bl, av, st[t]);
+        }
       }
     }
     // The state after a chunk (exact: the piece started from the exact
@@ -773,7 +792,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
       float* cs = a.chunk_states + ((size_t)b * a.nchunks + c) * a.H * a.P * a.N +
                   (state_el(a, b, vh) - (size_t)b * a.H * a.P * a.N);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) store_stateT(st[t], cs, 2 * rt + t, pt, a.N, nvalid);
+      for (int t = 0; t < 2; ++t) store_st(st[t], cs, 2 * rt + t);
     }
     __syncthreads();
   }
@@ -781,7 +800,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
   if (a.h_last && piece == a.npieces - 1) {
     float* hl = a.h_last + state_el(a, b, vh);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) store_stateT(st[t], hl, 2 * rt + t, pt, a.N, nvalid);
+    for (int t = 0; t < 2; ++t) store_st(st[t], hl, 2 * rt + t);
   }
 }
 

@@ -137,5 +137,28 @@ __device__ __forceinline__ void store_stateT(const f32x16& acc, float* S, int nt
   }
 }
 
+// The same state as an S tile: headdim rows p = pt*32 + 8(r >> 2) + 4hf +
+// (r & 3) in register r, states n = nt*32 + lane % 32 in the lanes (the
+// accumulator layout of a product with the headdim rows as its A operand).
+// A register is one row segment of 32 states: whole 128-byte lines.
+__device__ __forceinline__ void load_stateS(f32x16& acc, const float* S, int nt, int pt, int ld = kN,
+                                            int nmax = kN) {
+  const int lane = threadIdx.x & 63;
+  const int n = nt * 32 + (lane & 31), p0 = pt * 32 + 4 * (lane >> 5);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    acc[r] = (S && n < nmax) ? S[(size_t)(p0 + 8 * (r >> 2) + (r & 3)) * ld + n] : 0.f;
+}
+
+__device__ __forceinline__ void store_stateS(const f32x16& acc, float* S, int nt, int pt, int ld = kN,
+                                             int nmax = kN) {
+  const int lane = threadIdx.x & 63;
+  const int n = nt * 32 + (lane & 31), p0 = pt * 32 + 4 * (lane >> 5);
+  if (n < nmax) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[(size_t)(p0 + 8 * (r >> 2) + (r & 3)) * ld + n] = acc[r];
+  }
+}
+
 }  // namespace ssd
 }  // namespace mss
