@@ -388,6 +388,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];     // B, state rows (tsw)
   __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];     // C, state rows (tsw)
   __shared__ __attribute__((aligned(16))) uint16_t xs[kSub][kRowP];    // x, step rows
+  __shared__ __attribute__((aligned(16))) uint16_t Bq0[32][kN + kPadH];  // B, steps 0..31 (0 past N)
   __shared__ __attribute__((aligned(16))) float Es[kP * kERow];        // E [p][n] (0 past N)
   __shared__ __attribute__((aligned(16))) float Ss[kP * kN];           // S_in (layout: ss_index; 0 past N)
   // Step values of the block (delta, s, exp(s), exp(s_63 - s)), double-buffered
@@ -578,6 +579,12 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       T0Regs r;
       issue_t0(vh0, r);
       stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {  // B rows of the first half, step-major
+        const int u = threadIdx.x + 256 * it, row = u >> 4, n = (u & 15) * 8;
+        *reinterpret_cast<u32x4*>(&Bq0[row][n]) =
+            buf_load_u32x4(rb, n < a.N ? ((uint32_t)row * brow + (uint32_t)n) * 2 : kOffNone);
+      }
       commit_t0(r);
     } else {
       T1Regs r;
@@ -696,7 +703,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
         ld_srow(Es, sub, kk, ev);
         u32x4 eh, el;
         split8(ev, eh, el, dm);
-        const u32x4 bop = Q == 1 ? fb1[kk] : frag_bc(rb, Q, kk);
+        const u32x4 bop = Q == 1 ? fb1[kk] : *reinterpret_cast<const u32x4*>(&Bq0[lc][kk * 16 + 8 * hf]);
         gacc = mfma(eh, bop, gacc);
         gacc = mfma(el, bop, gacc);
       }
@@ -922,8 +929,9 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
     constexpr int Q = decltype(qtag)::value;
     T0Regs p0;
     T1Regs p1;
-    // The half-1 waves of team 0 (registers to spare) keep the B fragments of
-    // (G B)^T over the heads; the half-0 waves load them for every head.
+    // The B fragments of (G B)^T: the half-1 waves of team 0 (registers to
+    // spare) keep theirs over the heads, the half-0 waves read theirs from
+    // the step-major staging of the first half.
     u32x4 fb1[TEAM == 0 && Q == 1 ? kNK : 1];
     if constexpr (TEAM == 0 && Q == 1) {
 #pragma unroll
