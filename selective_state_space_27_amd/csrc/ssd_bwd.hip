@@ -141,54 +141,6 @@ __device__ __forceinline__ void stage_bc_transposed(const BwdArgs& a, const uint
   }
 }
 
-// dyy = dy * silu(z) (dy without z) for steps (jx, jx+1) of the block, 8
-// headdim rows pg*8.. of virtual head vh; when `dz_out`, also writes dz.
-// Steps past L read 0 and their stores are dropped.
-__device__ __forceinline__ void load_dyy(const BwdArgs& a, int b, int vh, int l0, int jx, int pg, float (&v)[2][8],
-                                         bool dz_out) {
-  const uint32_t row = (uint32_t)(a.H * a.P);
-  const uint32_t left = (uint32_t)max(a.L - l0, 0);
-  const size_t base = ((size_t)b * a.L + l0) * row + vrow(a, vh);
-  const rsrc_t rdy = make_rsrc(a.dy + base, left * row * 4);
-  const rsrc_t rz = make_rsrc(a.z ? a.z + base : nullptr, a.z ? left * row * 2 : 0u);
-  const rsrc_t ryf = make_rsrc(a.z ? a.yf + base : nullptr, a.z ? left * row * 4 : 0u);
-  const rsrc_t rdz = make_rsrc(a.z ? a.dz + base : nullptr, a.z ? left * row * 4 : 0u);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const uint32_t o = (uint32_t)(jx + s) * row + (uint32_t)pg * 8;
-    const f32x4 d0 = as_f32x4(buf_load_u32x4(rdy, o * 4)), d1 = as_f32x4(buf_load_u32x4(rdy, o * 4 + 16));
-    const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-    if (a.z) {
-      const u32x4 zz = buf_load_u32x4(rz, o * 2);
-      float zv[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        zv[2 * k] = bf16_lo(zz[k]);
-        zv[2 * k + 1] = bf16_hi(zz[k]);
-      }
-      if (dz_out) {
-        const f32x4 y0 = as_f32x4(buf_load_u32x4(ryf, o * 4)), y1 = as_f32x4(buf_load_u32x4(ryf, o * 4 + 16));
-        const float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-        float dzv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float sg = sigmoid(zv[k]);
-          v[s][k] = dv[k] * (zv[k] * sg);
-          dzv[k] = dv[k] * yv[k] * (sg * (1.0f + zv[k] * (1.0f - sg)));
-        }
-        buf_store_u32x4(rdz, o * 4, as_u32x4(f32x4{dzv[0], dzv[1], dzv[2], dzv[3]}));
-        buf_store_u32x4(rdz, o * 4 + 16, as_u32x4(f32x4{dzv[4], dzv[5], dzv[6], dzv[7]}));
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[s][k] = dv[k] * silu(zv[k]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[s][k] = dv[k];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Pass 2: the adjoint E arriving at every block.  Along the sequence
 // E_{k-1} = exp2(ls_63(k)) E_k + F_k, with block k's own part F_k =
@@ -233,7 +185,108 @@ __global__ void __launch_bounds__(256) ssd_bwd_piece_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) E[pt][r] = (WRITE_E && n_ok) ? top[tile_off(pt, r)] : 0.f;
   }
+  // A block's loads from memory (dy, and in the first pass z and the ungated
+  // y for dz; C; the prefix sums), issued one block ahead of their staging.
+  struct Raw {
+    u32x4 dy[2][2], z[2], yf[2][2], c[2][2];
+    float ls0, ls1, ls63;
+  };
+  const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);  // dyy: steps jx, jx + 1, rows pg*8 .. +8
+  const uint32_t row = (uint32_t)(a.H * a.P), crow = (uint32_t)(a.G * a.N * 2);
+  auto issue = [&](int k, Raw& r) {
+    const int l0 = k * kSub;
+    const uint32_t left = (uint32_t)max(a.L - l0, 0);
+    const size_t base = ((size_t)b * a.L + l0) * row + vrow(a, vh);
+    const rsrc_t rdy = make_rsrc(a.dy + base, left * row * 4);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint32_t o = (uint32_t)(jx + s2) * row + (uint32_t)pg * 8;
+      r.dy[s2][0] = buf_load_u32x4(rdy, o * 4);
+      r.dy[s2][1] = buf_load_u32x4(rdy, o * 4 + 16);
+      if (a.z) {
+        const rsrc_t rz = make_rsrc(a.z + base, left * row * 2);
+        r.z[s2] = buf_load_u32x4(rz, o * 2);
+        if constexpr (!WRITE_E) {
+          const rsrc_t ryf = make_rsrc(a.yf + base, left * row * 4);
+          r.yf[s2][0] = buf_load_u32x4(ryf, o * 4);
+          r.yf[s2][1] = buf_load_u32x4(ryf, o * 4 + 16);
+        }
+      }
+    }
+    const rsrc_t rc = make_rsrc(a.C + ((size_t)b * a.L + l0) * a.G * a.N, left * crow);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // C: (step pair, 8 states) units, two per thread
+      const int u = threadIdx.x + 256 * it, ng = u & 15, j = 2 * (u >> 4);
+      const uint32_t col = (uint32_t)((g * a.N + ng * 8) * 2);
+      r.c[it][0] = buf_load_u32x4(rc, ng * 8 < a.N ? (uint32_t)j * crow + col : kOffNone);
+      r.c[it][1] = buf_load_u32x4(rc, ng * 8 < a.N ? (uint32_t)(j + 1) * crow + col : kOffNone);
+    }
+    r.ls0 = ls_row[l0 + jx];
+    r.ls1 = ls_row[l0 + jx + 1];
+    r.ls63 = ls_row[l0 + kSub - 1];
+  };
+  // e o dyy as hi/lo pairs and C transposed into LDS; the first pass writes dz.
+  auto stage = [&](const Raw& r, int k) {
+    const int l0 = k * kSub;
+    const float e[2] = {exp2_fast(r.ls0), exp2_fast(r.ls1)};
+    float v[2][8];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const f32x4 d0 = as_f32x4(r.dy[s2][0]), d1 = as_f32x4(r.dy[s2][1]);
+      const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      if (a.z) {
+        float zv[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          zv[2 * q] = bf16_lo(r.z[s2][q]);
+          zv[2 * q + 1] = bf16_hi(r.z[s2][q]);
+        }
+        if constexpr (!WRITE_E) {
+          const f32x4 y0 = as_f32x4(r.yf[s2][0]), y1 = as_f32x4(r.yf[s2][1]);
+          const float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+          float dzv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float sg = sigmoid(zv[q]);
+            v[s2][q] = dv[q] * (zv[q] * sg);
+            dzv[q] = dv[q] * yv[q] * (sg * (1.0f + zv[q] * (1.0f - sg)));
+          }
+          const uint32_t left = (uint32_t)max(a.L - l0, 0);
+          const rsrc_t rdz = make_rsrc(a.dz + ((size_t)b * a.L + l0) * row + vrow(a, vh), left * row * 4);
+          const uint32_t o = (uint32_t)(jx + s2) * row + (uint32_t)pg * 8;
+          buf_store_u32x4(rdz, o * 4, as_u32x4(f32x4{dzv[0], dzv[1], dzv[2], dzv[3]}));
+          buf_store_u32x4(rdz, o * 4 + 16, as_u32x4(f32x4{dzv[4], dzv[5], dzv[6], dzv[7]}));
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[s2][q] = dv[q] * silu(zv[q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[s2][q] = dv[q];
+      }
+    }
+#pragma unroll
+    for (int kq = 0; kq < 8; ++kq) {
+      uint32_t hi, lo;
+      split2(v[0][kq] * e[0], v[1][kq] * e[1], hi, lo, dm);
+      *reinterpret_cast<uint32_t*>(&gh[tsw(pg * 8 + kq, jx)]) = hi;
+      *reinterpret_cast<uint32_t*>(&gl[tsw(pg * 8 + kq, jx)]) = lo;
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int u = threadIdx.x + 256 * it, ng = u & 15, j = 2 * (u >> 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w0 = r.c[it][0][q], w1 = r.c[it][1][q];
+        *reinterpret_cast<uint32_t*>(&CT[tsw(ng * 8 + 2 * q, j)]) = (w0 & 0xffffu) | (w1 << 16);
+        *reinterpret_cast<uint32_t*>(&CT[tsw(ng * 8 + 2 * q + 1, j)]) = (w0 >> 16) | (w1 & 0xffff0000u);
+      }
+    }
+  };
+
   float dsum = 0.f;  // log2 of the piece's decay
+  Raw raw;
+  if (!WRITE_E || k1 > k0) issue(k1, raw);
   for (int k = k1; k >= k0; --k) {
     if constexpr (WRITE_E) {
       // Opaque copies of the lane indexes: the 32 store addresses are formed
@@ -249,23 +302,12 @@ __global__ void __launch_bounds__(256) ssd_bwd_piece_kernel(BwdArgs a) {
       }
       if (k == k0) break;
     }
-    const int l0 = k * kSub;
-    {
-      const int pg = threadIdx.x & 7, jx = 2 * (threadIdx.x >> 3);
-      float v[2][8];
-      load_dyy(a, b, vh, l0, jx, pg, v, !WRITE_E);
-      const float e0 = exp2_fast(ls_row[l0 + jx]), e1 = exp2_fast(ls_row[l0 + jx + 1]);
-#pragma unroll
-      for (int kq = 0; kq < 8; ++kq) {
-        uint32_t hi, lo;
-        split2(v[0][kq] * e0, v[1][kq] * e1, hi, lo, dm);
-        *reinterpret_cast<uint32_t*>(&gh[tsw(pg * 8 + kq, jx)]) = hi;
-        *reinterpret_cast<uint32_t*>(&gl[tsw(pg * 8 + kq, jx)]) = lo;
-      }
-    }
-    stage_bc_transposed(a, a.C, b, g, l0, CT, threadIdx.x);
-    const float ls63 = ls_row[l0 + kSub - 1];
+    stage(raw, k);
+    const float ls63 = raw.ls63;
     dsum += ls63;
+    // The next block's loads (the second pass needs none for the piece's
+    // first block).
+    if (k - 1 >= k0 && !(WRITE_E && k - 1 == k0)) issue(k - 1, raw);
     __syncthreads();
     if (act) {
       f32x16 acc[2] = {};
