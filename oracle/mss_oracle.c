@@ -540,8 +540,8 @@ void oracle_mamba3_step(double* h, const double* x, const double* x_prev, const 
 /* dx, dz [batch, seqlen, nheads, headdim]; ddelta [batch, seqlen, nheads]; */
 /* dA, dD [nheads]; dB, dC [batch, seqlen, ngroups, dstate]; dh0 [batch,    */
 /* nheads, headdim, dstate].  The forward states are kept (seqlen x P x N   */
-/* per unit).  Units are (b, group) so that the sums over a group's heads   */
-/* stay in one thread.                                                      */
+/* per unit).  Units are (b, head); each thread sums its units' dB and dC   */
+/* parts in arrays of its own, added in thread order at the end.            */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   const double *x, *delta, *A, *B, *C, *D, *z, *h0, *dy, *dh_last;
@@ -636,11 +636,7 @@ static void ssd_bwd_head(const ssd_bwd_job* j, long b, long hd) {
 
 static void* ssd_bwd_worker(void* arg) {
   const ssd_bwd_job* j = (const ssd_bwd_job*)arg;
-  const long hpg = j->nheads / j->ngroups;
-  for (long k = j->unit_begin; k < j->unit_end; ++k) {
-    const long b = k / j->ngroups, g = k % j->ngroups;
-    for (long hd = g * hpg; hd < (g + 1) * hpg; ++hd) ssd_bwd_head(j, b, hd);
-  }
+  for (long k = j->unit_begin; k < j->unit_end; ++k) ssd_bwd_head(j, k / j->nheads, k % j->nheads);
   return NULL;
 }
 
@@ -654,19 +650,31 @@ void oracle_ssd_bwd(const double* x, const double* delta, const double* A, const
   memset(dC, 0, sizeof(double) * (size_t)(batch * seqlen * ngroups * dstate));
   double* dA_part = (double*)calloc((size_t)(batch * H), sizeof(double));
   double* dD_part = (double*)calloc((size_t)(batch * H), sizeof(double));
-  long units = batch * ngroups;
+  long units = batch * H;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  const size_t nbc = (size_t)(batch * seqlen * ngroups * dstate);
   ssd_bwd_job* jobs = (ssd_bwd_job*)calloc((size_t)nthreads, sizeof(ssd_bwd_job));
   pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
   for (int i = 0; i < nthreads; ++i) {
-    ssd_bwd_job jb = {x, delta, A, B, C, D, z, h0, dy, dh_last, dx, ddelta, dA_part, dB, dC, dD_part, dz, dh0,
+    /* thread 0 sums into the outputs, the others into arrays of their own */
+    double* pB = i == 0 ? dB : (double*)calloc(nbc, sizeof(double));
+    double* pC = i == 0 ? dC : (double*)calloc(nbc, sizeof(double));
+    ssd_bwd_job jb = {x, delta, A, B, C, D, z, h0, dy, dh_last, dx, ddelta, dA_part, pB, pC, dD_part, dz, dh0,
                       batch, seqlen, nheads, headdim, ngroups, dstate, units * i / nthreads,
                       units * (i + 1) / nthreads};
     jobs[i] = jb;
     pthread_create(&th[i], NULL, ssd_bwd_worker, &jobs[i]);
   }
   for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  for (int i = 1; i < nthreads; ++i) {
+    for (size_t e = 0; e < nbc; ++e) {
+      dB[e] += jobs[i].dB[e];
+      dC[e] += jobs[i].dC[e];
+    }
+    free(jobs[i].dB);
+    free(jobs[i].dC);
+  }
   for (long hd = 0; hd < H; ++hd) {
     double sa = 0.0, sd = 0.0;
     for (long b = 0; b < batch; ++b) {

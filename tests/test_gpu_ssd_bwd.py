@@ -207,6 +207,19 @@ def test_ssd_bwd_2p8b_one_head_full():
     compare(g, r, "ssd_2p8b, one head")
 
 
+def test_ssd_bwd_2p8b_all_heads_full():
+    """b=2, L=16384, H=80, P=64, N=128 with dy on every head, in the bench's
+    launch (20 heads per gradient workgroup, 16-block pieces): every element
+    of dx, ddelta, dA, dB, dC and dh0 against the oracle (160 head-sequences
+    of fp64 work over the host's threads).  dD (at D = 0 here) is checked at
+    small sizes."""
+    cfg, x = _full_inputs()
+    g = run_gpu(x)
+    r = run_oracle(x)
+    g["dD"] = r["dD"] = None
+    compare(g, r, "ssd_2p8b, all heads")
+
+
 def test_ssd_bwd_2p8b_all_heads_linear_functionals():
     """The same workload with dy on every head.  y and h_last are linear in
     each of x, B, C and h0 separately, so for a direction V the gradient's
