@@ -694,46 +694,39 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
           wacc[u] = mfma(*reinterpret_cast<const u32x4*>(&dyRl[(Q + u) * 32 + lc][kp * 16 + 8 * hf]), xop, wacc[u]);
         }
       }
-      // Column sums of Z below the diagonal (i > j).
+      // M o K and M o W (i >= j) in the accumulator layout (each M_ij formed
+      // once), the column sums of Z below the diagonal (i > j) from them, then
+      // both as operands: k = i, column j.
       float cs = 0.f;
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
+        f32x16 mk;
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
           const int i0 = (Q + u) * 32 + 8 * k4 + 4 * hf;
           const f32x4 lsi = lds4(&s_ls[par][i0]);
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            const float m = (i0 + qq > col) ? exp2_fast(lsi[qq] - ls_c) : 0.f;
-            cs += m * kk2[u][4 * k4 + qq] * wacc[u][4 * k4 + qq];
+            const int r = 4 * k4 + qq;
+            const float m = (i0 + qq >= col) ? exp2_fast(lsi[qq] - ls_c) : 0.f;
+            mk[r] = m * kk2[u][r];
+            cs += (i0 + qq > col ? mk[r] : 0.f) * wacc[u][r];
+            wacc[u][r] *= m;
           }
         }
-      }
-      cs = (cs + __shfl_xor(cs, 32)) * dl_c;
-      if (sub == 0 && hf == 0) s_col[col] = cs;
-      // M o K and M o W (i >= j) as operands: k = i, column j.
-#pragma unroll
-      for (int u = 0; u < NI; ++u) {
         auto slice = [&](auto stag) {
           constexpr int S = decltype(stag)::value;
           float kv[8], wv[8];
-          acc_kslice<S>(kk2[u], kv);
+          acc_kslice<S>(mk, kv);
           acc_kslice<S>(wacc[u], wv);
-          const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
-          const f32x4 l0v = lds4(&s_ls[par][i0]), l1v = lds4(&s_ls[par][i0 + 4]);
-          const float lsi[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float m = (i0 + t >= col) ? exp2_fast(lsi[t] - ls_c) : 0.f;
-            kv[t] *= m;
-            wv[t] *= m;
-          }
           split8(kv, mkh[u][S], mkl[u][S], dm);
           split8(wv, mwh[u][S], mwl[u][S], dm);
         };
         slice(std::integral_constant<int, 0>{});
         slice(std::integral_constant<int, 1>{});
       }
+      cs = (cs + __shfl_xor(cs, 32)) * dl_c;
+      if (sub == 0 && hf == 0) s_col[col] = cs;
     }
 
     // ---- products 2: (G B)^T, headdim rows sub*32.., columns col
@@ -862,7 +855,9 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
             wt[u] = mfma(xa, dl, wt[u]);
           }
         }
-        // Row sums of Z left of the diagonal (j < i).
+        // M o W^T o delta_j (j <= i) in the accumulator layout (each weight
+        // formed once), the row sums of Z left of the diagonal (j < i) from it,
+        // then as operands: k = j, column i.
         float rs = 0.f;
 #pragma unroll
         for (int u = 0; u < NJ; ++u) {
@@ -872,27 +867,21 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
             const f32x4 lsj = lds4(&s_ls[par][j0]), dlj = lds4(&s_dl[par][j0]);
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-              const float m = (j0 + qq < col) ? exp2_fast(ls_c - lsj[qq]) * dlj[qq] : 0.f;
-              rs += m * wt[u][4 * k4 + qq] * kk2[u][4 * k4 + qq];
+              const int r = 4 * k4 + qq;
+              const float m = (j0 + qq <= col) ? exp2_fast(ls_c - lsj[qq]) * dlj[qq] : 0.f;
+              wt[u][r] = m * wt[u][r];
+              rs += (j0 + qq < col ? wt[u][r] : 0.f) * kk2[u][r];
             }
           }
         }
         rs += __shfl_xor(rs, 32);
         if (sub == 0 && hf == 0) s_row[col] = rs;
-        // M o W^T o delta_j (j <= i) as operands: k = j, column i.
 #pragma unroll
         for (int u = 0; u < NJ; ++u) {
           auto slice = [&](auto stag) {
             constexpr int S = decltype(stag)::value;
             float v[8];
             acc_kslice<S>(wt[u], v);
-            const int j0 = u * 32 + 16 * S + 8 * hf;
-            const f32x4 l0v = lds4(&s_ls[par][j0]), l1v = lds4(&s_ls[par][j0 + 4]);
-            const f32x4 d0v = lds4(&s_dl[par][j0]), d1v = lds4(&s_dl[par][j0 + 4]);
-            const float lsj[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
-            const float dlj[8] = {d0v[0], d0v[1], d0v[2], d0v[3], d1v[0], d1v[1], d1v[2], d1v[3]};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] *= (j0 + t <= col) ? exp2_fast(ls_c - lsj[t]) * dlj[t] : 0.f;
             split8(v, mth[u][S], mtl[u][S], dm);
           };
           slice(std::integral_constant<int, 0>{});
