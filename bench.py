@@ -596,8 +596,8 @@ def bench_ssd_bwd(args, torch, mss, I):
         th, info = host_cpus()
         f64 = lambda k: I.to_f64(x[k], "bf16")
         X, Bm, Cm, dl, dy = f64("x"), f64("B"), f64("C"), x["delta"].astype(np.float64), x["dy"].astype(np.float64)
-        hs = 8  # all threads: both batch rows, heads 0..7 (the oracle runs one thread per (batch, group))
-        units = min(th, b * G)
+        hs = 16  # all threads: both batch rows, heads 0..15 (the oracle runs one thread per (batch, head))
+        units = min(th, b * hs)
 
         def call(nb, nh, t):
             return oracle.ssd_bwd(np.ascontiguousarray(X[:nb, :, :nh]), np.ascontiguousarray(dl[:nb, :, :nh]),
