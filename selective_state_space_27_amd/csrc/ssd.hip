@@ -174,7 +174,7 @@ __device__ __forceinline__ void store_bc_rows(const BCRegs& o, uint16_t (*rm)[kN
 }
 
 // ---------------------------------------------------------------------------
-// Piece states.  grid (2 Hv, batch, npieces), 512 threads: workgroup (b, vh,
+// Piece states.  grid (2 Hv, batch, npieces - 1), 512 threads: workgroup (b, vh,
 // pt, piece) owns headdim tile pt of virtual head vh over the chunks of one
 // piece of the sequence and runs them from a zero state (piece 0 from h0),
 // writing only the piece's end state and its decay; ssd_chain_kernel then
@@ -900,8 +900,11 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
     a.noff = hv * kN;
     a.accumulate = hv > 0 ? 1 : 0;
     const bool last = hv == halves - 1;
-    hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.Hv), (unsigned)a.batch, (unsigned)a.npieces), dim3(kTS),
-                       0, stream, a);
+    // The last piece's end state is not needed (the scan kernel walks that
+    // piece to the end), nor is any with a single piece.
+    if (a.npieces > 1)
+      hipLaunchKernelGGL(ssd_state_kernel, dim3((unsigned)(2 * a.Hv), (unsigned)a.batch, (unsigned)(a.npieces - 1)),
+                         dim3(kTS), 0, stream, a);
     if (a.npieces > 1)
       hipLaunchKernelGGL(ssd_chain_kernel, dim3((unsigned)(kP * kN / 1024), (unsigned)a.Hv, (unsigned)a.batch),
                          dim3(256), 0, stream, a);

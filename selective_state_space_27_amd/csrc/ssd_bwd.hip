@@ -167,6 +167,9 @@ __global__ void __launch_bounds__(256) ssd_bwd_piece_kernel(BwdArgs a) {
   const int vh = blockIdx.x % a.Hv, pc = blockIdx.x / a.Hv, b = blockIdx.y;
   const int h = vh / a.ph, g = h / (a.H / a.G);
   const int k0 = pc * a.bpp, k1 = min(a.nblk, k0 + a.bpp) - 1;
+  // The first piece's sum only feeds dh0: without dh0 (and with no dz to
+  // write) the first pass skips it.
+  if (!WRITE_E && pc == 0 && !a.dh0 && !a.z) return;
   int lane = threadIdx.x & 63, lc = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Dot2Masks dm = dot2_masks();
@@ -341,7 +344,8 @@ __global__ void __launch_bounds__(256) ssd_bwd_piece_kernel(BwdArgs a) {
 
 // grid (ceil(16 N / 256) * Hv, batch), 256 threads, 4 state elements per
 // thread: from the last piece to the first (the slots hold P_j, loaded four
-// pieces ahead).
+// pieces ahead; P_0 and its decay, left unwritten without dh0, only reach the
+// final E, which is then not stored).
 __global__ void __launch_bounds__(256) ssd_bwd_piece_chain_kernel(BwdArgs a) {
   const int xb = (16 * a.N + 255) / 256;
   const int vh = blockIdx.x / xb, b = blockIdx.y;
