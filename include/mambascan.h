@@ -363,8 +363,10 @@ size_t mss_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int
 /* (size from mss_ssd_bwd_workspace_size) need not be zeroed.               */
 /* Tuning: the environment variable MSS_SSD_BWD_HEADS_PER_WG, when it holds */
 /* a divisor of a group's nheads/ngroups * headdim/64 64-row head slices,   */
-/* sets how many of them one gradient workgroup takes (else chosen from the */
-/* sizes); both functions read it, so it must not change between them.     */
+/* sets how many of them one gradient workgroup takes, and                  */
+/* MSS_SSD_BWD_BLOCKS_PER_PIECE (a positive count) how many 64-step blocks  */
+/* one piece of the adjoint passes takes (else both are chosen from the     */
+/* sizes); both functions read them, so they must not change between them.  */
 /* ------------------------------------------------------------------------ */
 mss_status mss_ssd_chunk_bwd(const void* x, const float* delta, const float* A, const void* B,
                              const void* C, const float* D, const void* z, const float* h0,

@@ -1114,11 +1114,17 @@ struct BwdLayout {
 };
 
 // Pieces of blocks for the adjoint passes: about 2560 (piece, virtual head,
-// batch) workgroups (ten per CU), whole blocks each.
+// batch) workgroups (ten per CU), whole blocks each.  The environment
+// variable MSS_SSD_BWD_BLOCKS_PER_PIECE, when it holds a positive count,
+// overrides the piece length (tuning and tests).
 void e_pieces(int64_t batch, int64_t vheads, int64_t nblk, int& npc, int& bpp) {
   const int64_t streams = batch * vheads;
   const int64_t np = std::max<int64_t>(1, std::min<int64_t>((2560 + streams - 1) / streams, nblk));
   bpp = (int)((nblk + np - 1) / np);
+  if (const char* e = std::getenv("MSS_SSD_BWD_BLOCKS_PER_PIECE")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1) bpp = (int)std::min<int64_t>(v, nblk);
+  }
   npc = (int)((nblk + bpp - 1) / bpp);
 }
 

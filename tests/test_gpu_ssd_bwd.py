@@ -174,6 +174,36 @@ def test_ssd_bwd_heads_per_workgroup(case, monkeypatch):
         assert rel_err(host64(g[k]), host64(g1[k])) <= 1e-5, k
 
 
+PIECE_CASES = [
+    # b, L, H, G, P, N, D, z, h0, dh_last, blocks per piece of the adjoint passes
+    (2, 300, 4, 2, 64, 128, True, True, True, True, 2),    # 5 blocks: pieces of 2, 2, 1
+    (1, 700, 3, 1, 128, 48, True, False, True, True, 4),   # 11 blocks: 4, 4, 3
+    (1, 1000, 2, 1, 64, 64, False, True, False, False, 3),  # 16 blocks: 3 x 5 + 1; no dh0 wanted below
+]
+
+
+@pytest.mark.parametrize("case", PIECE_CASES, ids=lambda c: "b{}l{}h{}g{}p{}n{}bpp{}".format(*c[:6], c[10]))
+def test_ssd_bwd_adjoint_pieces(case, monkeypatch):
+    """The adjoint passes over pieces of several blocks (the full-size
+    workloads' launch; small sizes otherwise take one block per piece), the
+    last piece shorter: every element of every gradient against the oracle,
+    and with dh0 not wanted (the first piece's sum is then skipped) the same
+    values."""
+    b, L, H, G, P, N, d, z, h0, dhl, bpp = case
+    cfg, x = gen(b, L, H, G, P, N, seed=60, with_d=d, with_z=z, with_h0=h0, with_dhl=dhl)
+    monkeypatch.setenv("MSS_SSD_BWD_BLOCKS_PER_PIECE", str(bpp))
+    g = run_gpu(x)
+    g2 = run_gpu(x, want_dh0=False, want_dD=False)
+    r = run_oracle(x)
+    if x["D"] is None:
+        r["dD"] = g["dD"] = None
+    compare(g, r, f"{case} blocks per piece {bpp}")
+    assert g2["dh0"] is None
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dz"):
+        if g[k] is not None:
+            assert torch.equal(g[k], g2[k]), k
+
+
 def _full_inputs():
     cfg = I.SSD_2P8B
     x = I.ssd_inputs(cfg)
