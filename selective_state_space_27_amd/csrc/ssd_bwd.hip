@@ -429,8 +429,6 @@ __device__ __forceinline__ int ss_index(int p, int n) {
 __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t dyRh[kSub][kRowP];  // dyy, step rows: hi
   __shared__ __attribute__((aligned(16))) uint16_t dyRl[kSub][kRowP];  // lo
-  __shared__ __attribute__((aligned(16))) uint16_t dyTh[kP * kTRow];   // dyy, headdim rows (tsw): hi
-  __shared__ __attribute__((aligned(16))) uint16_t dyTl[kP * kTRow];   // lo
   __shared__ __attribute__((aligned(16))) uint16_t BT[kN * kTRow];     // B, state rows (tsw)
   __shared__ __attribute__((aligned(16))) uint16_t CT[kN * kTRow];     // C, state rows (tsw)
   __shared__ __attribute__((aligned(16))) uint16_t xs[kSub][kRowP];    // x, step rows
@@ -536,13 +534,6 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
       split8(v[s], hi, lo, dm);
       *reinterpret_cast<u32x4*>(&dyRh[jx + s][pg * 8]) = hi;
       *reinterpret_cast<u32x4*>(&dyRl[jx + s][pg * 8]) = lo;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t hi, lo;
-      split2(v[0][k], v[1][k], hi, lo, dm);
-      *reinterpret_cast<uint32_t*>(&dyTh[tsw(pg * 8 + k, jx)]) = hi;
-      *reinterpret_cast<uint32_t*>(&dyTl[tsw(pg * 8 + k, jx)]) = lo;
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -652,6 +643,21 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
   auto frag_x = [&](int T, int kp) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(&xs[T * 32 + lc][kp * 16 + 8 * hf]);
   };
+  // dyy (hi or lo) as the headdim-row operand: row p = sub*32 + lc, steps
+  // i0 .. i0 + 7 (i0 includes 8hf), read from the step-major staging with two
+  // transposing LDS reads.  ds_read_b64_tr_b16 gives lane i of each 16-lane
+  // group, as value q, 16-bit element i % 4 of the 8 bytes addressed by lane
+  // 4q + i / 4 of the group; so lane i addresses steps i0 + i / 4 (+ 4),
+  // headdim rows sub*32 + 16 (group & 1) + 4 (i % 4) .. +4.
+  auto frag_tr = [&](const uint16_t (*R)[kRowP], int i0) -> u32x4 {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int i = lane & 15;
+    const uint16_t* p0 = &R[i0 + (i >> 2)][sub * 32 + 16 * ((lane >> 4) & 1) + 4 * (i & 3)];
+    const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0));
+    const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * kRowP));
+    const u32x2 a2 = __builtin_bit_cast(u32x2, lo4), b2 = __builtin_bit_cast(u32x2, hi4);
+    return u32x4{a2[0], a2[1], b2[0], b2[1]};
+  };
   // E staging: rows p = PT*32 + lc, states kk*16 + 8hf .. +8.
   auto ld_srow = [&](const float* S, int PT, int kk, float* v) {
     const float* r = S + (PT * 32 + lc) * kERow + kk * 16 + 8 * hf;
@@ -752,8 +758,7 @@ __global__ void __launch_bounds__(512, 1) ssd_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int S = 0; S < 2; ++S) {
           const int i0 = (Q + u) * 32 + 16 * S + 8 * hf;
-          const u32x4 ah = *reinterpret_cast<const u32x4*>(&dyTh[tsw(sub * 32 + lc, i0)]);
-          const u32x4 al = *reinterpret_cast<const u32x4*>(&dyTl[tsw(sub * 32 + lc, i0)]);
+          const u32x4 ah = frag_tr(dyRh, i0), al = frag_tr(dyRl, i0);
           gacc = mfma(ah, mkh[u][S], gacc);
           gacc = mfma(al, mkh[u][S], gacc);
           gacc = mfma(ah, mkl[u][S], gacc);
