@@ -129,16 +129,31 @@ constexpr int kDecayScalar = 2;   // A[d,n] == A[d,0]: one r per (d,l) for every
 
 
 // LDS: per buffer, kQMax quantities x kBlk x channels x float4 (4 steps), and
-// 8 waves x kBlk x channels x float4 of partial readouts.  The channel
-// dimension is padded to kRowPad slots: the core accesses (lane = channel,
-// one 4-step block) stay contiguous, and the prologue/epilogue accesses (four
-// lanes per channel, one per block; the block stride is 64 bytes modulo 256)
-// fall on 16 distinct 16-byte bank groups per 16 lanes.
-constexpr int kRowPad = kLanes + 4;
+// 8 waves x kBlk x channels x float4 of partial readouts, each (quantity,
+// block) row of channels padded to kRowPad 16-byte slots.  The core accesses
+// (lane = channel, one 4-step block) are contiguous.  The prologue/epilogue
+// accesses have four lanes per channel, one per block (a block row lies 2
+// slots further modulo 32 slots), and io_channel() gives every 8, 16 or 32
+// consecutive lanes channels whose slots do not meet modulo 128, 256 or 512
+// bytes: {c, c+1}, then {c, c+1, c+8, c+9}, then those and +16.
+constexpr int kRowPad = kLanes + 2;
 constexpr int kQFloats = kQMax * kBlk * kRowPad * 4;
 constexpr int kPFloats = kWaves * kBlk * kRowPad * 4;
 
-__device__ __forceinline__ int q_off(int q, int blk, int ch) { return ((q * kBlk + blk) * kRowPad + ch) * 4; }
+// Float offset of (quantity q, block blk, channel ch) in a buffer:
+// q_lane(blk, ch) + q * q_step.  The part fixed per thread and the constant
+// per quantity stay separate, so the constant folds into the LDS
+// instruction's offset field.
+__device__ __forceinline__ constexpr int q_lane(int blk, int ch) { return (blk * kRowPad + ch) * 4; }
+constexpr int q_step = kBlk * kRowPad * 4;
+
+// Channel (0..63 within the block) of prologue/epilogue wave io (0..3), lane
+// `lane`; the lane's 4-step block is lane & 3.  Lane bits 2, 5, 3, 4 and the
+// wave bits 0, 1 give channel bits 0, 1, 3, 4 and 2, 5.
+__device__ __forceinline__ int io_channel(int io, int lane) {
+  return ((lane >> 2) & 1) | (((lane >> 5) & 1) << 1) | ((io & 1) << 2) | (((lane >> 3) & 1) << 3) |
+         (((lane >> 4) & 1) << 4) | ((io >> 1) << 5);
+}
 
 template <bool BF16, int SPW, bool VEC, bool STATE, bool FUSED>
 __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
@@ -161,11 +176,12 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
   // channel's 16 steps and each global access instruction moves 16 whole row
   // segments.
   const int io = is_core ? 0 : (w - kWaves) % kIoWaves;
-  const int io_ch = io * 16 + (lane >> 2);
+  const int io_ch = io_channel(io, lane);
   const int io_blk = lane & 3;
   const int p16 = lane & 15;
   const int ntiles = a.ntiles;
   const uint32_t io_off = (uint32_t)io_ch * (uint32_t)L * es;
+  const int io_lds = q_lane(io_blk, io_ch);  // this I/O thread's LDS slot within a quantity's rows
   float h[SPW];
 
   // Logical workgroup id in start order (a ticket), so the workgroup a carry
@@ -325,9 +341,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         float* pp = pbuf[buf];
         f32x4 xvs[kAhead], rvs[kAhead], svs[kAhead];
         auto read_blk = [&](int blk, int i) {
-          xvs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(0, blk, lane)]);
-          rvs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(1, blk, lane)]);
-          if constexpr (S4D) svs[i] = *reinterpret_cast<const f32x4*>(&q[q_off(sp_slot, blk, lane)]);
+          const float* qb = q + q_lane(blk, lane);
+          xvs[i] = *reinterpret_cast<const f32x4*>(&qb[0]);
+          rvs[i] = *reinterpret_cast<const f32x4*>(&qb[q_step]);
+          if constexpr (S4D) svs[i] = *reinterpret_cast<const f32x4*>(&qb[sp_slot * q_step]);
           else svs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         };
         if constexpr (kAhead == kBlk) {
@@ -350,7 +367,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
           const int i = kAhead == kBlk ? blk : 0;
           const f32x4 xv = xvs[i], rv = rvs[i], sv = svs[i];
           f32x4 duv;
-          if constexpr (W0 == 1 && !STATE) duv = *reinterpret_cast<const f32x4*>(&q[q_off(kQDu, blk, lane)]);
+          if constexpr (W0 == 1 && !STATE) duv = *reinterpret_cast<const f32x4*>(&q[q_lane(blk, lane) + kQDu * q_step]);
           f32x4 part;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
@@ -386,9 +403,9 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
             part[kk] = p;
           }
           if constexpr (W0 == 2 && !STATE) {
-            if (wc == 0) part += *reinterpret_cast<const f32x4*>(&q[q_off(kQDu, blk, lane)]);
+            if (wc == 0) part += *reinterpret_cast<const f32x4*>(&q[q_lane(blk, lane) + kQDu * q_step]);
           }
-          if constexpr (!STATE) *reinterpret_cast<f32x4*>(&pp[q_off(wc, blk, lane)]) = part;
+          if constexpr (!STATE) *reinterpret_cast<f32x4*>(&pp[q_lane(blk, lane) + wc * q_step]) = part;
         }
       };
 
@@ -433,9 +450,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 
     // ---- prologue waves prepare tile k+1 and epilogue waves finish tile k-1
     // while the core runs tile k ----
-    auto io_run = [&](auto mode_tag, auto pro_tag) __attribute__((always_inline)) {
+    auto io_run = [&](auto mode_tag, auto pro_tag, auto gate_tag) __attribute__((always_inline)) {
       constexpr int M = decltype(mode_tag)::value;
       constexpr bool PRO = decltype(pro_tag)::value;
+      constexpr bool GATE = decltype(gate_tag)::value;  // epilogue: z given (a copy of the loop per case)
       if constexpr (STATE && !PRO) {  // no outputs in the state-only passes: keep the barrier count only
         for (int k = tb; k <= te; ++k) __syncthreads();
         return;
@@ -455,6 +473,7 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         pd[slot] = load_raw4<BF16, VEC>(rd_d, io_off, t, L, ok);
       };
       auto load_epi = [&](int tile, int slot) {
+        if constexpr (!GATE) return;
         const int t = tile * kTile + io_blk * 4;
         const bool ok = iok && tile >= tb && tile < te;
         ez[slot] = load_raw4<BF16, VEC>(rz_d, io_off, t, L, ok);
@@ -511,19 +530,19 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
         if constexpr (FUSED) fuse(uu, dd, tile);
         if constexpr (STATE) dacc += (dd[0] + dd[1]) + (dd[2] + dd[3]);  // zero past the piece and past L
         refill();  // the slot's registers are free: issue its next load now
-        float* q = qbuf[buf];
-        *reinterpret_cast<f32x4*>(&q[q_off(0, io_blk, io_ch)]) = dd * uu;
-        if constexpr (!STATE) *reinterpret_cast<f32x4*>(&q[q_off(kQDu, io_blk, io_ch)]) = dskip * uu;
+        float* q = qbuf[buf] + io_lds;  // quantity k of this thread's (channel, block) at q[k * q_step]
+        *reinterpret_cast<f32x4*>(&q[0]) = dd * uu;
+        if constexpr (!STATE) *reinterpret_cast<f32x4*>(&q[kQDu * q_step]) = dskip * uu;
         if constexpr (M == kDecayScalar) {
           f32x4 r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
-          *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = r;
+          *reinterpret_cast<f32x4*>(&q[q_step]) = r;
         } else if constexpr (M == kDecayS4D) {
           f32x4 r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) r[i] = exp2_fast(dd[i] * a20);
-          *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = r;
+          *reinterpret_cast<f32x4*>(&q[q_step]) = r;
           f32x4 stp = r;  // r^SPW
 #pragma unroll
           for (int j = 1; j < SPW; ++j) stp = stp * r;
@@ -531,10 +550,10 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
 #pragma unroll
           for (int wv = 1; wv < kWaves; ++wv) {
             sp = sp * stp;
-            *reinterpret_cast<f32x4*>(&q[q_off(2 + wv, io_blk, io_ch)]) = sp;
+            *reinterpret_cast<f32x4*>(&q[(2 + wv) * q_step]) = sp;
           }
         } else {
-          *reinterpret_cast<f32x4*>(&q[q_off(1, io_blk, io_ch)]) = dd;
+          *reinterpret_cast<f32x4*>(&q[q_step]) = dd;
         }
       };
 
@@ -542,18 +561,15 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       // is in wave 0's) summed in a fixed order, gated by silu(z); stores only
       // inside the piece.
       auto epilogue = [&](int buf, int slot, int tile, auto&& refill) {
-        const f32x4 zz = decode4(ez[slot]);
+        const f32x4 zz = GATE ? decode4(ez[slot]) : f32x4{0.f, 0.f, 0.f, 0.f};
         refill();  // the slot's registers are free: issue its next load now
-        const float* pp = pbuf[buf];
-        f32x4 acc = *reinterpret_cast<const f32x4*>(&pp[q_off(0, io_blk, io_ch)]);
+        const float* pp = pbuf[buf] + io_lds;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(&pp[0]);
 #pragma unroll
-        for (int wv = 1; wv < kWaves; ++wv) acc += *reinterpret_cast<const f32x4*>(&pp[q_off(wv, io_blk, io_ch)]);
+        for (int wv = 1; wv < kWaves; ++wv) acc += *reinterpret_cast<const f32x4*>(&pp[wv * q_step]);
         f32x4 out;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float g = silu(zz[i]);  // z reads as 0 when absent; the select drops it
-          out[i] = acc[i] * (has_z ? g : 1.0f);
-        }
+        for (int i = 0; i < 4; ++i) out[i] = GATE ? acc[i] * silu(zz[i]) : acc[i];
         const bool ok = iok && tile >= tb && tile < te;
         store4<BF16, VEC>(ry_d, io_off, tile * kTile + io_blk * 4, L, ok, out);
       };
@@ -610,11 +626,13 @@ __global__ void __launch_bounds__(kThreads, 1) scan_kernel(ScanArgs a) {
       else if (mode == kDecayScalar) core_run(SC{});
       else core_run(G{});
     } else if (is_pro) {
-      if (mode == kDecayS4D) io_run(S4{}, std::true_type{});
-      else if (mode == kDecayScalar) io_run(SC{}, std::true_type{});
-      else io_run(G{}, std::true_type{});
+      if (mode == kDecayS4D) io_run(S4{}, std::true_type{}, std::false_type{});
+      else if (mode == kDecayScalar) io_run(SC{}, std::true_type{}, std::false_type{});
+      else io_run(G{}, std::true_type{}, std::false_type{});
     } else {
-      io_run(G{}, std::false_type{});  // the epilogue is the same for every decay
+      // the epilogue is the same for every decay
+      if (has_z) io_run(G{}, std::false_type{}, std::true_type{});
+      else io_run(G{}, std::false_type{}, std::false_type{});
     }
 
     if (STATE && a.pass == kPassLocal) {  // the zero-start end state, for carry_combine_kernel (a later launch)
