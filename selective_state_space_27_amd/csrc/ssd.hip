@@ -37,6 +37,7 @@
 // bf16 hi/lo pair (two products), keeping ~16 bits of mantissa.  Operands the
 // matrix cores read along time (x and B) are staged transposed in LDS.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.hpp"
@@ -807,14 +808,25 @@ __global__ void __launch_bounds__(kT, 2) ssd_scan_kernel(SSDArgs a) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Pieces per sequence: the scan kernel runs one workgroup per (batch, virtual
-// head, piece), two per CU, so about ten of them per CU over all pieces (and
+// head, piece), two per CU, so about five of them per CU over all pieces (and
 // twice as many state-kernel workgroups), at most kMaxPieces and one per
-// chunk; pieces hold whole chunks, cpp each.
+// chunk; pieces hold whole chunks, cpp each.  Fewer, longer pieces leave the
+// state kernel less to do (it runs every piece but the last) and each scan
+// workgroup fewer pipeline fills; ten per CU measured 5% slower on a
+// 160-stream, 64-chunk layer.  The environment variable
+// MSS_SSD_CHUNKS_PER_PIECE, when it holds a positive count, overrides the
+// piece length within the same limits (tuning and tests); the workspace
+// query and the call must see the same value.
 void ssd_pieces(int64_t batch, int64_t vheads, int64_t nchunks, int& npieces, int& cpp) {
   const int64_t streams = vheads * batch;
-  int64_t np = (2560 + streams - 1) / streams;
+  int64_t np = (1280 + streams - 1) / streams;
   np = std::max<int64_t>(1, std::min<int64_t>({np, (int64_t)kMaxPieces, nchunks}));
   cpp = (int)((nchunks + np - 1) / np);
+  if (const char* e = std::getenv("MSS_SSD_CHUNKS_PER_PIECE")) {
+    const long v = std::strtol(e, nullptr, 10);
+    const int64_t min_cpp = (nchunks + kMaxPieces - 1) / kMaxPieces;  // at most kMaxPieces pieces
+    if (v >= 1) cpp = (int)std::max<int64_t>(min_cpp, std::min<int64_t>(v, nchunks));
+  }
   npieces = (int)((nchunks + cpp - 1) / cpp);
 }
 

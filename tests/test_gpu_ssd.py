@@ -168,18 +168,24 @@ def test_ssd_2p8b_workload_full():
 
 
 @pytest.mark.parametrize("case", [
-    # b, L, H, chunk, D, z, h0, heads checked (None: all), headdim
-    (1, 5000, 80, 64, True, True, True, [0, 5, 41, 79], 64),   # 27 pieces of 3 chunks, ragged L
-    (2, 3000, 40, 128, False, False, True, [0, 13, 39], 64),   # 24 pieces of 1 chunk, ragged last chunk
-    (1, 16384, 2, 64, False, False, True, None, 64),           # 64 pieces of 4 chunks
-    (1, 4100, 40, 256, True, True, True, [0, 17, 39], 128),    # headdim 128 (80 half heads): 17 pieces
+    # b, L, H, chunk, D, z, h0, heads checked (None: all), headdim, chunks per piece (None: the library's choice)
+    (1, 5000, 80, 64, True, True, True, [0, 5, 41, 79], 64, None),   # 16 pieces of 5 chunks, ragged L
+    (2, 3000, 40, 128, False, False, True, [0, 13, 39], 64, None),   # 12 pieces of 2 chunks, ragged last chunk
+    (2, 3000, 40, 128, False, False, True, [0, 13, 39], 64, 1),      # 24 pieces of 1 chunk
+    (1, 16384, 2, 64, False, False, True, None, 64, None),           # 64 pieces of 4 chunks
+    (1, 4100, 40, 256, True, True, True, [0, 17, 39], 128, None),    # headdim 128 (80 half heads): 9 pieces
+    (1, 4100, 40, 256, True, True, True, [0, 17, 39], 128, 3),       # 6 pieces, the last of 2 chunks
 ])
-def test_ssd_sequence_cut_into_pieces(case):
+def test_ssd_sequence_cut_into_pieces(case, monkeypatch):
     """With many heads the sequence is cut into pieces of whole chunks: the
     state pass runs every piece from zero, the chain makes the exact state
     entering each piece, and the output pass walks each piece's chunks from
-    it.  Checked where pieces hold several chunks and L is ragged."""
-    b, L, H, Q, d, z, h0, heads, P = case
+    it.  Checked where pieces hold one or several chunks and L is ragged
+    (piece lengths other than the library's choice through
+    MSS_SSD_CHUNKS_PER_PIECE)."""
+    b, L, H, Q, d, z, h0, heads, P, cpp = case
+    if cpp is not None:
+        monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", str(cpp))
     cfg, x = gen(b, L, H, 1, Q, seed=21, with_d=d, with_z=z, with_h0=h0, P=P)
     y, cs, hl = run_gpu(x, Q)
     sel = slice(None) if heads is None else np.array(heads)
