@@ -313,6 +313,12 @@ mss_status mss_mamba3_state_update(float* h, const void* x, const void* x_prev, 
 /* (headdim/64) * batch below 2^22 (else MSS_ERR_SHAPE).  seqlen need not   */
 /* be a multiple of chunk.                                                  */
 /* `flags` must be 0.  Outputs must not overlap inputs or each other.        */
+/* Tuning: the environment variable MSS_SSD_CHUNKS_PER_PIECE, when it holds */
+/* a positive count, sets how many chunks one piece of the sequence takes   */
+/* (else chosen from the sizes; at most 64 pieces either way).  The         */
+/* workspace query and the call read it; a value that needs more workspace  */
+/* than was queried gives MSS_ERR_WORKSPACE.  mss_ssd_chunk_bwd's forward  */
+/* pass (chunk 64) reads it too.                                            */
 /* ------------------------------------------------------------------------ */
 mss_status mss_ssd_chunk_fwd(const void* x, const float* delta, const float* A, const void* B,
                              const void* C, const float* D, const void* z, const float* h0,
