@@ -54,7 +54,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 # fp32 vector arithmetic: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
-# = 78.6 TFLOP/s without packed fp32 (kept out of this build's code), 157.3
+# = 78.6 TFLOP/s without packed fp32 (kept out of the library's code), 157.3
 # with it; bf16 dense MFMA 2.5 PFLOP/s.
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 ALU_PEAK_PACKED_TFLOPS = 2 * ALU_PEAK_TFLOPS
@@ -623,7 +623,7 @@ def bench_copy(args, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); "
               "the hot path shards over batch and channels with no communication", file=sys.stderr)
         sys.exit(2)
     if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and

@@ -15,7 +15,7 @@
  *                       in-kernel indexing of one row/plane
  *   MSS_ERR_DTYPE       unknown dtype code
  *   MSS_ERR_ALIGN       a pointer is not 16-byte aligned
- *   MSS_ERR_UNSUPPORTED a shape this build does not implement (see each call)
+ *   MSS_ERR_UNSUPPORTED a shape the library does not implement (see each call)
  *   MSS_ERR_WORKSPACE   workspace NULL or smaller than the query returned
  *   MSS_ERR_ALIAS       an output buffer overlaps an input buffer
  *   MSS_ERR_HIP         a HIP launch failed (mss_last_hip_error() has the code)
