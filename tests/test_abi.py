@@ -366,3 +366,29 @@ def test_mamba3_validation_errors():
     assert m3_call(h=P(0, 8)) == ALIGN
     assert m3_call(y=P(1, 32)) == ALIAS                     # y on x
     assert m3_call(h=P(8, 64)) == ALIAS                     # state on C
+
+
+def test_ssd_chunks_per_piece_override_and_workspace(monkeypatch):
+    """MSS_SSD_CHUNKS_PER_PIECE sets the piece length of the SSD forward: more
+    pieces need more piece-state workspace, the count stays at most 64, and
+    a call whose workspace was sized under another setting that needs less
+    is refused on the host (fake pointers; nothing is enqueued)."""
+    shape = (2, 16384, 80, 64, 1, 128, 256)  # 64 chunks per sequence
+    lib = mss.lib()
+    monkeypatch.delenv("MSS_SSD_CHUNKS_PER_PIECE", raising=False)
+    default = lib.mss_ssd_workspace_size(*shape, BF16)
+    monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "64")  # one piece: no piece states beyond the first
+    one = lib.mss_ssd_workspace_size(*shape, BF16)
+    monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "1")   # 64 pieces, the most allowed
+    many = lib.mss_ssd_workspace_size(*shape, BF16)
+    assert one < default < many
+    monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "0")   # not a positive count: the library's choice
+    assert lib.mss_ssd_workspace_size(*shape, BF16) == default
+    monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "1")
+    assert ssd_call(shape=shape, ws_bytes=default) == WS  # sized for fewer pieces than the call now takes
+    # At most 64 pieces: a shorter piece than 1/64 of the sequence is lengthened.
+    long_shape = (1, 65536, 8, 64, 1, 128, 256)  # 256 chunks
+    monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "4")
+    cap = lib.mss_ssd_workspace_size(*long_shape, BF16)
+    monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "1")
+    assert lib.mss_ssd_workspace_size(*long_shape, BF16) == cap
