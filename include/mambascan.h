@@ -199,10 +199,14 @@ mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, cons
 /* D = 0); dz [batch, dim, seqlen] io_dtype, given exactly when z is (else    */
 /* MSS_ERR_NULL); dh0 [batch, dim, dstate] fp32 (NULL = not computed; the     */
 /* gradient of the initial state, h0 or zero).                              */
-/* Supported: 1 <= dstate <= 32 (else MSS_ERR_UNSUPPORTED) and the scan's    */
-/* other limits (else MSS_ERR_SHAPE).  flags: 0 or MSS_FLAG_DECAY_GENERAL (as in the */
-/* forward).  Outputs must not overlap any input or each other.  The         */
-/* workspace (size from                                                      */
+/* Supported: 1 <= dstate <= 128 (else MSS_ERR_UNSUPPORTED) and the scan's   */
+/* other limits (else MSS_ERR_SHAPE).  Above 32 states the gradient is taken */
+/* by slices of 32 states (each state's recurrence is independent; du,       */
+/* ddelta and dz are sums over the slices, the skip term taken once), in     */
+/* fp32, rounded to io_dtype once at the end; the workspace then also holds */
+/* fp32 copies of the [batch, dim, seqlen] tensors.  flags: 0 or             */
+/* MSS_FLAG_DECAY_GENERAL (as in the forward).  Outputs must not overlap any  */
+/* input or each other.  The workspace (size from                            */
 /* mss_selective_scan_bwd_workspace_size) need not be zeroed.                */
 /* ------------------------------------------------------------------------ */
 mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B,

@@ -290,19 +290,23 @@ mss_status mss_selective_scan_fwd_fused(const void* x, const float* conv_w, cons
 }
 
 // --------------------------------------------------- selective scan backward
-// The forward's limits and d_state <= 32 (up to 4 states per wave).
+// The forward's limits (d_state <= 128).  Up to 32 states the gradient
+// kernels take them all (up to 4 states per wave); above, slices of 32 run
+// one after the other.
 static mss_status scan_bwd_check_shape(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, mss_dtype t) {
-  const mss_status st = scan_check_shape(batch, dim, dstate, seqlen, t);
-  if (st != MSS_OK) return st;
-  if (dstate > 32) return MSS_ERR_UNSUPPORTED;
-  return MSS_OK;
+  return scan_check_shape(batch, dim, dstate, seqlen, t);
+}
+
+static size_t scan_bwd_need(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  return dstate > 32 ? mss::scan_bwd_wide_workspace_bytes(batch, dim, seqlen)
+                     : mss::scan_bwd_workspace_bytes(batch, dim, dstate, seqlen);
 }
 
 size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                              mss_dtype io_dtype, uint32_t flags) {
   (void)flags;
   if (scan_bwd_check_shape(batch, dim, dstate, seqlen, io_dtype) != MSS_OK) return 0;
-  return mss::scan_bwd_workspace_bytes(batch, dim, dstate, seqlen);
+  return scan_bwd_need(batch, dim, dstate, seqlen);
 }
 
 mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -319,7 +323,7 @@ mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float*
   const void* all[] = {u, delta, A, B, C, D, z, h0, dy, dh_last, du, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
   for (const void* p : all)
     if (p && !aligned16(p)) return MSS_ERR_ALIGN;
-  const size_t need = mss::scan_bwd_workspace_bytes(batch, dim, dstate, seqlen);
+  const size_t need = scan_bwd_need(batch, dim, dstate, seqlen);
   if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
 
   const size_t es = elem_size(io_dtype);
@@ -366,6 +370,7 @@ mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float*
   p.dD = dD;
   p.dz = dz;
   p.dh0 = dh0;
+  if (dstate > 32) return hip_status(mss::launch_scan_bwd_wide(p, static_cast<hipStream_t>(hip_stream)));
   return hip_status(mss::launch_scan_bwd(p, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -41,7 +41,7 @@ size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
 
 // Backward of the selective scan: fwd holds the forward's inputs, shape and
-// workspace (y, h_last and ckpt unused); dstate <= 16.
+// workspace (y, h_last and ckpt unused); dstate <= 32 for launch_scan_bwd.
 struct ScanBwdParams {
   ScanParams fwd;
   const void* dy;
@@ -58,6 +58,9 @@ struct ScanBwdParams {
 
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t stream);
+// d_state 33..128: the same gradient by slices of 32 states, in fp32.
+size_t scan_bwd_wide_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
+hipError_t launch_scan_bwd_wide(const ScanBwdParams& p, hipStream_t stream);
 
 struct UpdateParams {
   float* h;

@@ -139,7 +139,7 @@ def test_scan_bwd_validation_enqueues_nothing():
     assert bwd_call(dB=None) == NULL
     assert bwd_call(dz=None) == NULL                  # z given without dz
     assert bwd_call(z=None) == NULL                   # dz given without z
-    assert bwd_call(shape=(2, 64, 33, 128)) == UNSUP  # d_state above 32
+    assert bwd_call(shape=(2, 64, 129, 128)) == UNSUP  # d_state above 128
     assert bwd_call(shape=(2, 64, 16, 0)) == SHAPE
     assert bwd_call(io=7) == DTYPE
     assert bwd_call(flags=0x80) == UNSUP
@@ -154,7 +154,13 @@ def test_scan_bwd_validation_enqueues_nothing():
         lib.mss_selective_scan_workspace_size(4, 5120, 16, 8192, BF16, 0)
     assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 32, 8192, BF16, 0) > \
         lib.mss_selective_scan_bwd_workspace_size(4, 5120, 16, 8192, BF16, 0)
-    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 33, 8192, BF16, 0) == 0
+    # Above 32 states: a 32-state backward's workspace reused by every slice,
+    # plus fp32 copies of the [batch, dim, seqlen] tensors; the same for any
+    # d_state from 33 to 128, none above.
+    wide = lib.mss_selective_scan_bwd_workspace_size(4, 5120, 33, 8192, BF16, 0)
+    assert wide > lib.mss_selective_scan_bwd_workspace_size(4, 5120, 32, 8192, BF16, 0) + 10 * 4 * 5120 * 8192 * 4
+    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 128, 8192, BF16, 0) == wide
+    assert lib.mss_selective_scan_bwd_workspace_size(4, 5120, 129, 8192, BF16, 0) == 0
 
 
 def test_scan_workspace_query():
@@ -327,7 +333,7 @@ def test_helper_grids_beyond_2p32_items_are_accepted():
     assert ws > 4 * (1 << 32)
     assert lib.mss_selective_scan_workspace_size(4, 64, 128, (1 << 23) + 7, BF16, 0) > 0
     assert lib.mss_selective_scan_bwd_workspace_size(65535, 64, 32, 1 << 12, BF16, 0) > 0
-    assert lib.mss_selective_scan_bwd_workspace_size(1, 64, 33, 1 << 12, BF16, 0) == 0  # d_state > 32
+    assert lib.mss_selective_scan_bwd_workspace_size(1, 64, 129, 1 << 12, BF16, 0) == 0  # d_state > 128
 
 
 def test_python_binding_rejects_cpu_tensors():

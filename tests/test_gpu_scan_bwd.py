@@ -140,6 +140,78 @@ def test_scan_bwd_checkpoint_paths(shape):
     print(shape, {k: f"{v:.1e}" for k, v in errs.items()})
 
 
+WIDE_SHAPES = [
+    # b, d, N, L, io: d_state above 32, taken by slices of 32 states
+    (2, 100, 40, 77, "fp32"),      # slices of 32 and 8, ragged channels and L
+    (1, 64, 64, 150, "fp32"),      # two full slices
+    (2, 80, 128, 60, "bf16"),      # four slices, bf16 I/O (fp32 inside, rounded once)
+    (1, 130, 33, 40, "fp32"),      # a one-state last slice
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: "b{}d{}n{}l{}{}".format(*s))
+def test_scan_bwd_wide_dstate(shape):
+    """d_state 33..128: every element of every gradient against the oracle
+    (the slices' du, ddelta, dz summed, dA, dB, dC, dh0 placed per state,
+    the skip term's dD from the first slice)."""
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    dy, dhl = grads_inputs(x)
+    errs = check(run_gpu_bwd(x, dy, dhl), run_oracle_bwd(x, dy, dhl), io)
+    print(shape, {k: f"{v:.1e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("drop", [("D",), ("z",), ("D", "z")])
+def test_scan_bwd_wide_optional_inputs(drop):
+    x = I.scan_inputs(I.small_scan_config(2, 96, 64, 70, "fp32"))
+    dy, _ = grads_inputs(x, with_dh_last=False)
+    got = run_gpu_bwd(x, dy, None, drop=drop, with_h0=False)
+    ref = run_oracle_bwd(x, dy, None, drop=drop, with_h0=False)
+    if "D" in drop:
+        ref_d = run_oracle_bwd(dict(x, D=np.zeros_like(x["D"])), dy, None, drop=tuple(k for k in drop if k != "D"),
+                               with_h0=False)
+        ref["dD"] = ref_d["dD"]
+    check(got, ref, "fp32")
+
+
+@pytest.mark.parametrize("force_general", [False, True])
+def test_scan_bwd_wide_general_a(force_general):
+    """A general in half the channels (per-state decay in every slice) and
+    S4D-real in the rest (slices past the first see A[d, n0 + j], which the
+    decay detection then treats as general)."""
+    x = I.scan_inputs(I.small_scan_config(2, 128, 72, 90, "fp32"), with_h0=True)
+    g = np.random.default_rng(5)
+    x["A"] = (-np.exp(g.uniform(-1, 2, size=x["A"].shape))).astype(np.float32)
+    x["A"][:64] = -(np.arange(72, dtype=np.float32) + 1)
+    dy, dhl = grads_inputs(x)
+    check(run_gpu_bwd(x, dy, dhl, force_general=force_general), run_oracle_bwd(x, dy, dhl), "fp32")
+
+
+@pytest.mark.parametrize("shape", [(2, 12800, 64, 45, "bf16"), (1, 128, 48, 9000, "fp32")],
+                         ids=["carry_handoff_n64", "split_passes_n48"])
+def test_scan_bwd_wide_checkpoint_paths(shape):
+    """The slices through the multi-workgroup paths: more streams than CUs
+    (hand-offs) and few long sequences (split passes)."""
+    b, d, n, L, io = shape
+    x = I.scan_inputs(I.small_scan_config(b, d, n, L, io), with_h0=True)
+    dy, dhl = grads_inputs(x)
+    errs = check(run_gpu_bwd(x, dy, dhl), run_oracle_bwd(x, dy, dhl), io)
+    print(shape, {k: f"{v:.1e}" for k, v in errs.items()})
+
+
+def test_scan_bwd_wide_status_word():
+    """The call's status word (first word of the workspace) is clear after a
+    sliced backward with hand-offs between workgroups in every slice."""
+    x = I.scan_inputs(I.small_scan_config(2, 12800, 40, 45, "bf16"), with_h0=True)
+    dy, dhl = grads_inputs(x)
+    g = {k: dev(x[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")}
+    ws = torch.full((mss.selective_scan_bwd_workspace_size(2, 12800, 40, 45, torch.bfloat16),), 255,
+                    dtype=torch.uint8, device="cuda:0")
+    mss.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["h0"], dy=dev(dy),
+                           dh_last=dev(dhl), workspace=ws)
+    assert mss.workspace_status(ws) == mss.MSS_OK
+
+
 def test_scan_bwd_deterministic():
     x = I.scan_inputs(I.small_scan_config(2, 256, 16, 200, "bf16"), with_h0=True)
     dy, dhl = grads_inputs(x)
