@@ -367,8 +367,12 @@ size_t mss_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int
 /* MSS_ERR_NULL); dh0 [batch, nheads, headdim, dstate] (NULL = not computed; */
 /* the gradient of h0, or of a zero initial state).                          */
 /* Supported: in_dtype MSS_BF16; headdim 64 or 128; dstate a multiple of 16 */
-/* up to 128; nheads % ngroups == 0 (else MSS_ERR_UNSUPPORTED); the         */
-/* forward's size limits with chunk 64 (else MSS_ERR_SHAPE).  `flags` must   */
+/* up to 256; nheads % ngroups == 0 (else MSS_ERR_UNSUPPORTED); the         */
+/* forward's size limits with chunk 64 (else MSS_ERR_SHAPE).  Above 128     */
+/* states the gradient is taken by two halves of the states (each state     */
+/* column evolves on its own; dx, ddelta, dA and dz are sums over the       */
+/* halves, the skip term taken once); the workspace then also holds the     */
+/* halves' B/C and state columns and the second half's sums.  `flags` must  */
 /* be 0.  Outputs must not overlap any input or each other.  The workspace  */
 /* (size from mss_ssd_bwd_workspace_size) need not be zeroed.               */
 /* Tuning: the environment variable MSS_SSD_BWD_HEADS_PER_WG, when it holds */

@@ -505,7 +505,7 @@ def ssd_chunk_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=Non
     both float32.  Returns a dict of float32 tensors: dx, dz (None without z)
     [b, L, H, P], ddelta [b, L, H], dA [H], dB, dC [b, L, G, N], dD [H] (None
     unless want_dD) and dh0 [b, H, P, N] (None unless want_dh0).  d_state <=
-    128.  ``out``: a dict from an earlier call with the same shapes whose
+    256.  ``out``: a dict from an earlier call with the same shapes whose
     tensors are written again."""
     dev = _device_of(x)
     b, L, H, P = x.shape

@@ -557,18 +557,23 @@ mss_status mss_ssd_chunk_fwd(const void* x, const float* delta, const float* A, 
 }
 
 
+// The forward's limits with chunk 64 (d_state up to 256).  Up to 128 states
+// one pass takes them all; above, two halves run one after the other.
 static mss_status ssd_bwd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                       int64_t ngroups, int64_t dstate, mss_dtype t) {
-  const mss_status st = ssd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, 64, t);
-  if (st != MSS_OK) return st;
-  if (dstate > 128) return MSS_ERR_UNSUPPORTED;
-  return MSS_OK;
+  return ssd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, 64, t);
+}
+
+static size_t ssd_bwd_need(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                           int64_t dstate) {
+  return dstate > 128 ? mss::ssd_bwd_halves_workspace_bytes(batch, seqlen, nheads, headdim, ngroups)
+                      : mss::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
 }
 
 size_t mss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                   int64_t ngroups, int64_t dstate, mss_dtype in_dtype) {
   if (ssd_bwd_check_shape(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype) != MSS_OK) return 0;
-  return mss::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
+  return ssd_bwd_need(batch, seqlen, nheads, headdim, ngroups, dstate);
 }
 
 mss_status mss_ssd_chunk_bwd(const void* x, const float* delta, const float* A, const void* B, const void* C,
@@ -585,7 +590,7 @@ mss_status mss_ssd_chunk_bwd(const void* x, const float* delta, const float* A, 
   const void* all[] = {x, delta, A, B, C, D, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
   for (const void* p : all)
     if (p && !aligned16(p)) return MSS_ERR_ALIGN;
-  const size_t need = mss::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
+  const size_t need = ssd_bwd_need(batch, seqlen, nheads, headdim, ngroups, dstate);
   if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
 
   const size_t es = elem_size(in_dtype);
@@ -631,6 +636,7 @@ mss_status mss_ssd_chunk_bwd(const void* x, const float* delta, const float* A, 
   p.ngroups = ngroups;
   p.dstate = dstate;
   p.workspace = workspace;
+  if (dstate > 128) return hip_status(mss::launch_ssd_bwd_halves(p, static_cast<hipStream_t>(hip_stream)));
   return hip_status(mss::launch_ssd_bwd(p, static_cast<hipStream_t>(hip_stream)));
 }
 

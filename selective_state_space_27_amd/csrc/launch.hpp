@@ -153,5 +153,9 @@ struct SSDBwdParams {
 size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                                int64_t dstate);
 hipError_t launch_ssd_bwd(const SSDBwdParams& p, hipStream_t stream);
+// d_state 129..256: the same gradient by two halves of the states.
+size_t ssd_bwd_halves_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                      int64_t ngroups);
+hipError_t launch_ssd_bwd_halves(const SSDBwdParams& p, hipStream_t stream);
 
 }  // namespace mss

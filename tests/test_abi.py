@@ -268,12 +268,17 @@ def test_ssd_bwd_validation_errors():
     assert ssd_bwd_call(io=FP32) == UNSUP
     assert ssd_bwd_call(shape=(2, 1024, 8, 96, 1, 128)) == UNSUP         # headdim 96
     assert ssd_bwd_call(shape=(2, 1024, 8, 64, 1, 40)) == UNSUP          # dstate not a multiple of 16
-    assert ssd_bwd_call(shape=(2, 1024, 8, 64, 1, 144)) == UNSUP         # dstate above 128
+    assert ssd_bwd_call(shape=(2, 1024, 8, 64, 1, 272)) == UNSUP         # dstate above 256
     assert ssd_bwd_call(shape=(2, 1024, 6, 64, 4, 128)) == UNSUP         # nheads % ngroups
     lib = mss.lib()
     for Pd, N in ((64, 16), (64, 48), (64, 64), (64, 128), (128, 128), (128, 48)):
         assert lib.mss_ssd_bwd_workspace_size(2, 1024, 8, Pd, 1, N, BF16) > 0, (Pd, N)
-    assert lib.mss_ssd_bwd_workspace_size(2, 1024, 8, 64, 1, 256, BF16) == 0
+    # Above 128 states: two halves, one d_state-128 workspace reused, plus
+    # the half's B/C and state columns and the second half's sums.
+    halves = lib.mss_ssd_bwd_workspace_size(2, 1024, 8, 64, 1, 256, BF16)
+    assert halves > lib.mss_ssd_bwd_workspace_size(2, 1024, 8, 64, 1, 128, BF16)
+    assert lib.mss_ssd_bwd_workspace_size(2, 1024, 8, 64, 1, 144, BF16) == halves
+    assert lib.mss_ssd_bwd_workspace_size(2, 1024, 8, 64, 1, 272, BF16) == 0
     # The forward's limits with 64-step chunks: L*H*P below 2^30 - 64 and
     # ceil(L/64) * H * P/64 * batch below 2^22.
     assert lib.mss_ssd_bwd_workspace_size(1, (1 << 16) - 1, 256, 64, 1, 128, BF16) > 0

@@ -79,6 +79,10 @@ CASES = [
     (1, 333, 4, 1, 64, 16, False, True, True, False),
     (2, 130, 6, 2, 64, 48, True, True, False, True),
     (1, 257, 2, 1, 128, 48, True, False, True, False),
+    # above 128 states: two halves of the states
+    (1, 150, 4, 2, 64, 256, True, True, True, True),
+    (2, 130, 3, 1, 128, 144, True, False, True, False),
+    (1, 200, 4, 1, 64, 160, False, True, False, True),
 ]
 
 
@@ -93,6 +97,17 @@ def test_ssd_bwd_small(case):
         r["dD"] = None
         g["dD"] = None  # computed at D = 0 (checked below)
     compare(g, r, str(case))
+
+
+def test_ssd_bwd_halves_status_word():
+    """d_state 256 (two halves): the call's status word, set beforehand,
+    is clear after the call, and dD and dh0 may be skipped."""
+    cfg, x = gen(1, 100, 4, 1, 64, 256, with_d=True, with_z=True, with_h0=True, with_dhl=True)
+    ws = torch.full((mss.ssd_bwd_workspace_size(1, 100, 4, 64, 1, 256),), 255, dtype=torch.uint8, device="cuda:0")
+    g = run_gpu(x, workspace=ws, want_dD=False, want_dh0=False)
+    assert mss.workspace_status(ws) == mss.MSS_OK
+    assert g["dD"] is None and g["dh0"] is None
+    compare(g, run_oracle(x), "halves, no dD or dh0", names=("dx", "ddelta", "dA", "dB", "dC", "dz"))
 
 
 def test_ssd_bwd_dD_at_zero_and_optional_outputs():
