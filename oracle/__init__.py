@@ -24,7 +24,9 @@ the closed form of a rotating decaying state, the trapezoid rule's second-order
 convergence on an ODE with a known solution, and the closed-form fixed point of
 a constant input (real and complex).  The SSD backward is pinned by central
 finite differences of the SSD forward and by its equality with the selective
-scan's backward on the SSD's Mamba-1 form.
+scan's backward on the SSD's Mamba-1 form.  The fused scan's backward (numpy
+here: the prologue's chain rule around the scan's backward) is pinned by
+central finite differences of the fused forward.
 """
 from __future__ import annotations
 
@@ -172,6 +174,46 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_l
                                       _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
                                       b, d, N, L, threads or default_threads())
     return g
+
+
+def selective_scan_fused_bwd(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None, h0=None, dy=None,
+                             dh_last=None, conv_silu=False, softplus=True, threads=None):
+    """Gradient of a loss through selective_scan_fused, in fp64: the scan's
+    gradient (selective_scan_bwd at u, delta = scan_prologue(...)) taken back
+    through the prologue by the chain rule.  With c = conv_b + sum_k w_k
+    x[t-3+k] (zeros before step 0) and v = delta_raw + delta_bias:
+      dc = du * silu'(c) (du without silu),  silu'(c) = s (1 + c (1 - s)),
+      s = 1 / (1 + exp(-c));  dv = ddelta * sigmoid(v) (ddelta without softplus);
+      dx[s] = sum_k w_k dc[s + 3 - k] (terms past L dropped);
+      dconv_w[:, k] = sum over batch and t of dc[t] x[t - 3 + k];
+      dconv_b = sum of dc;  ddelta_raw = dv;  ddelta_bias = sum of dv.
+    Returns the scan's dict (dA, dB, dC, dD, dz, dh0) with du and ddelta
+    replaced by dx, ddelta_raw, dconv_w, dconv_b, ddelta_bias."""
+    x = _f64(x)
+    b, d, L = x.shape
+    w = _f64(conv_w, (d, 4))
+    cb = np.zeros(d) if conv_b is None else _f64(conv_b, (d,))
+    dr = _f64(delta_raw, (b, d, L))
+    dbias = np.zeros(d) if delta_bias is None else _f64(delta_bias, (d,))
+    u, dl = scan_prologue(x, conv_w, conv_b, delta_raw, delta_bias, conv_silu, softplus)
+    g = selective_scan_bwd(u, dl, A, B, C, D, z, h0, dy, dh_last, threads=threads)
+    xp = np.concatenate([np.zeros((b, d, 3)), x], axis=2)  # xp[..., t + 3] = x[..., t]
+    c = cb[None, :, None] + sum(w[None, :, k, None] * xp[:, :, k:k + L] for k in range(4))
+    if conv_silu:
+        s = 1.0 / (1.0 + np.exp(-c))
+        dc = g["du"] * s * (1.0 + c * (1.0 - s))
+    else:
+        dc = g["du"]
+    v = dr + dbias[None, :, None]
+    dv = g["ddelta"] / (1.0 + np.exp(-v)) if softplus else g["ddelta"]
+    dcp = np.concatenate([dc, np.zeros((b, d, 3))], axis=2)  # dcp[..., t] = dc[..., t], zero past L
+    dx = sum(w[None, :, k, None] * dcp[:, :, 3 - k:3 - k + L] for k in range(4))
+    dw = np.stack([np.sum(dc * xp[:, :, k:k + L], axis=(0, 2)) for k in range(4)], axis=1)
+    out = dict(g)
+    del out["du"], out["ddelta"]
+    out.update({"dx": dx, "ddelta_raw": dv, "dconv_w": dw, "dconv_b": dc.sum(axis=(0, 2)),
+                "ddelta_bias": dv.sum(axis=(0, 2))})
+    return out
 
 
 def state_update(h, u, delta, A, B, C, D=None, z=None, threads=None):

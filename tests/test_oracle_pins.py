@@ -726,3 +726,45 @@ def test_ssd_backward_equals_scan_backward_on_mamba1_form():
     np.testing.assert_allclose(s["dB"][:, :, 0], m["dB"].transpose(0, 2, 1), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(s["dC"][:, :, 0], m["dC"].transpose(0, 2, 1), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(s["dh0"], m["dh0"].reshape(b, H, P, N), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("silu,softplus", [(True, True), (False, False), (True, False)],
+                         ids=["silu_softplus", "plain", "silu_only"])
+def test_fused_backward_equals_finite_differences(silu, softplus):
+    """The fused scan's backward (the prologue's chain rule around the scan's
+    backward) against central differences of the fused forward oracle, for
+    every element of x, delta_raw, the taps and both biases and of the scan's
+    own inputs (a wrong tap index, a missing activation derivative or a
+    dropped bias sum fails this)."""
+    g = np.random.default_rng(23 + silu + 2 * softplus)
+    b, d, N, L = 2, 3, 4, 7
+    args = {"x": g.normal(size=(b, d, L)), "conv_w": 0.5 * g.normal(size=(d, 4)), "conv_b": 0.1 * g.normal(size=d),
+            "delta_raw": 0.5 * g.normal(size=(b, d, L)),
+            "delta_bias": (np.log(np.expm1(0.05)) if softplus else 0.3) + 0.1 * g.normal(size=d),
+            "A": -np.exp(g.uniform(-1, 1, size=(d, N))), "B": g.normal(size=(b, N, L)),
+            "C": g.normal(size=(b, N, L)), "D": g.normal(size=d), "z": g.normal(size=(b, d, L)),
+            "h0": g.normal(size=(b, d, N))}
+    dy = g.normal(size=(b, d, L))
+    dh_last = g.normal(size=(b, d, N))
+
+    def loss(a):
+        y, hl = oracle.selective_scan_fused(a["x"], a["conv_w"], a["conv_b"], a["delta_raw"], a["delta_bias"],
+                                            a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], conv_silu=silu,
+                                            softplus=softplus, threads=1)
+        return float((y * dy).sum() + (hl * dh_last).sum())
+
+    gr = oracle.selective_scan_fused_bwd(args["x"], args["conv_w"], args["conv_b"], args["delta_raw"],
+                                         args["delta_bias"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                                         args["h0"], dy, dh_last, conv_silu=silu, softplus=softplus, threads=2)
+    names = {"x": "dx", "conv_w": "dconv_w", "conv_b": "dconv_b", "delta_raw": "ddelta_raw",
+             "delta_bias": "ddelta_bias", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    eps = 1e-6
+    for k, v in args.items():
+        fd = np.zeros_like(v)
+        for i in np.ndindex(v.shape):
+            vp, vm = v.copy(), v.copy()
+            vp[i] += eps
+            vm[i] -= eps
+            fd[i] = (loss(dict(args, **{k: vp})) - loss(dict(args, **{k: vm}))) / (2 * eps)
+        err = np.max(np.abs(gr[names[k]] - fd)) / np.max(np.abs(fd))
+        assert err < 1e-7, (k, err)
