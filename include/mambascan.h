@@ -223,6 +223,48 @@ size_t mss_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t
                                              int64_t seqlen, mss_dtype io_dtype, uint32_t flags);
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the scan fed by its prologue (mss_selective_scan_fwd_fused). */
+/*                                                                          */
+/* The gradient of a scalar loss through the fused forward exactly as      */
+/* defined there ("Mamba (deep learning)", paragraph on the block: the      */
+/* convolution in front of the SSM; "Mamba State-Space Models", usage       */
+/* example, kernel size 4): the scan's gradient (as mss_selective_scan_bwd) */
+/* at u and delta formed in fp32 from x and delta_raw, taken back through   */
+/* the prologue.  With c = conv_b + sum_k conv_w[d,k] x[t-3+k] and          */
+/* v = delta_raw + delta_bias:                                              */
+/*   dc = du * silu'(c) (MSS_FLAG_CONV_SILU; else du),                       */
+/*   ddelta_raw = ddelta * sigmoid(v) (MSS_FLAG_DELTA_SOFTPLUS; else ddelta),*/
+/*   dx[s] = sum_k conv_w[d,k] dc[s+3-k],  dconv_w[d,k] = sum dc[t] x[t-3+k],*/
+/*   dconv_b = sum dc,  ddelta_bias = sum ddelta_raw (sums over batch, time).*/
+/* Inputs: as mss_selective_scan_fwd_fused, plus dy [batch, dim, seqlen]    */
+/* io_dtype and dh_last [batch, dim, dstate] fp32 (NULL = zero).            */
+/* Outputs (written): dx, ddelta_raw [batch, dim, seqlen] io_dtype;         */
+/* dconv_w [dim, 4] fp32; dconv_b, ddelta_bias [dim] fp32 (NULL = not       */
+/* computed); dA, dB, dC, dD, dz, dh0 as mss_selective_scan_bwd.  Internally */
+/* fp32 throughout (the workspace holds fp32 copies of the [batch, dim,      */
+/* seqlen] and [batch, dstate, seqlen] tensors); gradients in io_dtype are  */
+/* rounded once.  Supported shapes as mss_selective_scan_bwd; flags: any of */
+/* MSS_FLAG_DECAY_GENERAL, MSS_FLAG_CONV_SILU, MSS_FLAG_DELTA_SOFTPLUS (the */
+/* forward's).  Outputs must not overlap any input or each other; the       */
+/* workspace (size from mss_selective_scan_fused_bwd_workspace_size) need    */
+/* not be zeroed; its first word is the call's status word.                 */
+/* ------------------------------------------------------------------------ */
+mss_status mss_selective_scan_fused_bwd(const void* x, const float* conv_w, const float* conv_b,
+                                        const void* delta_raw, const float* delta_bias, const float* A,
+                                        const void* B, const void* C, const float* D, const void* z,
+                                        const float* h0, const void* dy, const float* dh_last, void* dx,
+                                        void* ddelta_raw, float* dconv_w, float* dconv_b, float* ddelta_bias,
+                                        float* dA, void* dB, void* dC, float* dD, void* dz, float* dh0,
+                                        int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                        mss_dtype io_dtype, uint32_t flags, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace mss_selective_scan_fused_bwd needs (0 when the */
+/* shape is unsupported).                                                    */
+size_t mss_selective_scan_fused_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                                   int64_t seqlen, mss_dtype io_dtype, uint32_t flags);
+
+/* ------------------------------------------------------------------------ */
 /* Single-token state update (generation step).                             */
 /*                                                                          */
 /* One step of the same recurrence, with the state carried between calls     */

@@ -46,7 +46,8 @@ MSS_ERR_WAIT = 9
 EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_noalloc", "mss_selective_scan_workspace_size",
            "mss_selective_scan_fwd_fused",
            "mss_selective_scan_bwd",
-           "mss_selective_scan_bwd_workspace_size", "mss_state_update",
+           "mss_selective_scan_bwd_workspace_size", "mss_selective_scan_fused_bwd",
+           "mss_selective_scan_fused_bwd_workspace_size", "mss_state_update",
            "mss_mamba3_state_update",
            "mss_ssd_chunk_fwd", "mss_ssd_workspace_size", "mss_ssd_chunk_bwd", "mss_ssd_bwd_workspace_size",
            "mss_workspace_status", "mss_status_string",
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
                                          i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
     L.mss_selective_scan_bwd.restype = ctypes.c_int
     L.mss_selective_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
+    L.mss_selective_scan_fused_bwd.argtypes = [vp] * 24 + [i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.mss_selective_scan_fused_bwd.restype = ctypes.c_int
+    L.mss_selective_scan_fused_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, u32]
+    L.mss_selective_scan_fused_bwd_workspace_size.restype = sz
     L.mss_selective_scan_bwd_workspace_size.restype = sz
     L.mss_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, i64, i64, i64, ctypes.c_int, u32, vp]
     L.mss_state_update.restype = ctypes.c_int
@@ -377,6 +382,49 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
     _raise(st, "mss_selective_scan_bwd")
     if check_waits:
         _check_waits(workspace, stream, "mss_selective_scan_bwd")
+    return g
+
+
+def selective_scan_fused_bwd(x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D=None, z=None, h0=None, *, dy,
+                             dh_last=None, conv_silu=False, softplus=True, want_dD=True, want_dh0=False,
+                             force_general_decay=False, workspace=None, stream=None) -> dict:
+    """Gradient of a loss through selective_scan_fwd_fused (same inputs and
+    options), given dy [b, d, L] (I/O dtype) and optionally dh_last [b, d, N]
+    float32.  Returns a dict: dx, ddelta_raw, dz (None without z) [b, d, L]
+    and dB, dC [b, N, L] in the I/O dtype; dconv_w [d, 4], dconv_b and
+    ddelta_bias [d] (None when the bias was None), dA [d, N], dD [d] (None
+    unless want_dD) and dh0 [b, d, N] (None unless want_dh0) in float32."""
+    dev = _device_of(x)
+    b, d, L = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    f32 = torch.float32
+    for t, name, shape, dt in ((x, "x", (b, d, L), io), (conv_w, "conv_w", (d, 4), f32), (conv_b, "conv_b", (d,), f32),
+                               (delta_raw, "delta_raw", (b, d, L), io), (delta_bias, "delta_bias", (d,), f32),
+                               (A, "A", (d, N), f32), (B, "B", (b, N, L), io), (C, "C", (b, N, L), io),
+                               (D, "D", (d,), f32), (z, "z", (b, d, L), io), (h0, "h0", (b, d, N), f32),
+                               (dy, "dy", (b, d, L), io), (dh_last, "dh_last", (b, d, N), f32)):
+        _check(t, name, shape, dt, dev)
+    flags = ((MSS_FLAG_DECAY_GENERAL if force_general_decay else 0) | (MSS_FLAG_CONV_SILU if conv_silu else 0) |
+             (MSS_FLAG_DELTA_SOFTPLUS if softplus else 0))
+    code = _io_code(io)
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+    g = {"dx": e((b, d, L), io), "ddelta_raw": e((b, d, L), io), "dconv_w": e((d, 4), f32),
+         "dconv_b": e((d,), f32) if conv_b is not None else None,
+         "ddelta_bias": e((d,), f32) if delta_bias is not None else None, "dA": e((d, N), f32),
+         "dB": e((b, N, L), io), "dC": e((b, N, L), io), "dD": e((d,), f32) if want_dD else None,
+         "dz": e((b, d, L), io) if z is not None else None, "dh0": e((b, d, N), f32) if want_dh0 else None}
+    need = lib().mss_selective_scan_fused_bwd_workspace_size(b, d, N, L, code, flags)
+    if need == 0:
+        _raise(5, "selective_scan_fused_bwd")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().mss_selective_scan_fused_bwd(
+        _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(delta_raw), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta_raw"]), _ptr(g["dconv_w"]),
+        _ptr(g["dconv_b"]), _ptr(g["ddelta_bias"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+        _ptr(g["dz"]), _ptr(g["dh0"]), b, d, N, L, code, flags, _ptr(workspace), workspace.numel(), _stream(stream))
+    _raise(st, "mss_selective_scan_fused_bwd")
     return g
 
 

@@ -24,8 +24,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmambascan.so")
-SOURCES = ["scan.hip", "scan_bwd.hip", "scan_bwd_wide.hip", "state_update.hip", "ssd.hip", "ssd_bwd.hip",
-           "ssd_bwd_halves.hip", "mamba3.hip", "api.cpp"]
+SOURCES = ["scan.hip", "scan_bwd.hip", "scan_bwd_wide.hip", "scan_fused_bwd.hip", "state_update.hip", "ssd.hip",
+           "ssd_bwd.hip", "ssd_bwd_halves.hip", "mamba3.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -374,6 +374,89 @@ mss_status mss_selective_scan_bwd(const void* u, const void* delta, const float*
   return hip_status(mss::launch_scan_bwd(p, static_cast<hipStream_t>(hip_stream)));
 }
 
+// ------------------------------------------ fused scan (prologue) backward
+size_t mss_selective_scan_fused_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                                   mss_dtype io_dtype, uint32_t flags) {
+  (void)flags;
+  if (scan_bwd_check_shape(batch, dim, dstate, seqlen, io_dtype) != MSS_OK) return 0;
+  return mss::scan_fused_bwd_workspace_bytes(batch, dim, dstate, seqlen);
+}
+
+mss_status mss_selective_scan_fused_bwd(const void* x, const float* conv_w, const float* conv_b,
+                                        const void* delta_raw, const float* delta_bias, const float* A,
+                                        const void* B, const void* C, const float* D, const void* z,
+                                        const float* h0, const void* dy, const float* dh_last, void* dx,
+                                        void* ddelta_raw, float* dconv_w, float* dconv_b, float* ddelta_bias,
+                                        float* dA, void* dB, void* dC, float* dD, void* dz, float* dh0,
+                                        int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                        mss_dtype io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream) {
+  if (!x || !conv_w || !delta_raw || !A || !B || !C || !dy || !dx || !ddelta_raw || !dconv_w || !dA || !dB || !dC)
+    return MSS_ERR_NULL;
+  if ((z == nullptr) != (dz == nullptr)) return MSS_ERR_NULL;
+  mss_status st = scan_bwd_check_shape(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MSS_OK) return st;
+  if (flags & ~(MSS_FLAG_DECAY_GENERAL | MSS_FLAG_CONV_SILU | MSS_FLAG_DELTA_SOFTPLUS)) return MSS_ERR_UNSUPPORTED;
+  const void* all[] = {x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D, z, h0, dy, dh_last, dx, ddelta_raw,
+                       dconv_w, dconv_b, ddelta_bias, dA, dB, dC, dD, dz, dh0, workspace};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return MSS_ERR_ALIGN;
+  const size_t need = mss::scan_fused_bwd_workspace_bytes(batch, dim, dstate, seqlen);
+  if (!workspace || workspace_bytes < need) return MSS_ERR_WORKSPACE;
+
+  const size_t es = elem_size(io_dtype);
+  const size_t nbdl = (size_t)batch * dim * seqlen * es;
+  const size_t nbnl = (size_t)batch * dstate * seqlen * es;
+  const size_t nA = (size_t)dim * dstate * 4, nD = (size_t)dim * 4;
+  const size_t nstate = (size_t)batch * dim * dstate * sizeof(float);
+  const void* ins[] = {x, conv_w, conv_b, delta_raw, delta_bias, A, B, C, D, z, h0, dy, dh_last, workspace};
+  const size_t in_bytes[] = {nbdl, nD * 4, nD, nbdl, nD, nA, nbnl, nbnl, nD, nbdl, nstate, nbdl, nstate, need};
+  void* outs[] = {dx, ddelta_raw, dconv_w, dconv_b, ddelta_bias, dA, dB, dC, dD, dz, dh0};
+  const size_t out_bytes[] = {nbdl, nbdl, nD * 4, nD, nD, nA, nbnl, nbnl, nD, nbdl, nstate};
+  for (int i = 0; i < 11; ++i) {
+    if (!output_clear(outs[i], out_bytes[i], ins, in_bytes, 14)) return MSS_ERR_ALIAS;
+    for (int j = i + 1; j < 11; ++j)
+      if (outs[i] && outs[j] && overlaps(range_of(outs[i], out_bytes[i]), range_of(outs[j], out_bytes[j])))
+        return MSS_ERR_ALIAS;
+  }
+
+  mss::ScanFusedBwdParams p;
+  p.x = x;
+  p.delta_raw = delta_raw;
+  p.conv_w = conv_w;
+  p.conv_b = conv_b;
+  p.delta_bias = delta_bias;
+  p.conv_silu = (flags & MSS_FLAG_CONV_SILU) != 0;
+  p.softplus = (flags & MSS_FLAG_DELTA_SOFTPLUS) != 0;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.h0 = h0;
+  p.dy = dy;
+  p.dh_last = dh_last;
+  p.dx = dx;
+  p.ddelta_raw = ddelta_raw;
+  p.dconv_w = dconv_w;
+  p.dconv_b = dconv_b;
+  p.ddelta_bias = ddelta_bias;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = dD;
+  p.dz = dz;
+  p.dh0 = dh0;
+  p.batch = batch;
+  p.dim = dim;
+  p.dstate = dstate;
+  p.seqlen = seqlen;
+  p.bf16 = io_dtype == MSS_BF16;
+  p.force_general = (flags & MSS_FLAG_DECAY_GENERAL) != 0;
+  p.workspace = workspace;
+  return hip_status(mss::launch_scan_fused_bwd(p, static_cast<hipStream_t>(hip_stream)));
+}
+
 // -------------------------------------------------------------- state update
 mss_status mss_state_update(float* h, const void* u, const void* delta, const float* A, const void* B,
                             const void* C, const float* D, const void* z, void* y, int64_t batch, int64_t dim,

@@ -58,6 +58,43 @@ struct ScanBwdParams {
 
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t stream);
+// Backward of the scan fed by its prologue (x, delta_raw and the taps and
+// biases in place of u and delta); any d_state the scan backward takes.
+struct ScanFusedBwdParams {
+  const void* x;
+  const void* delta_raw;
+  const float* conv_w;      // [dim][4]
+  const float* conv_b;      // nullable
+  const float* delta_bias;  // nullable
+  bool conv_silu, softplus;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;           // nullable
+  const void* z;            // nullable
+  const float* h0;          // nullable
+  const void* dy;
+  const float* dh_last;     // nullable
+  void* dx;
+  void* ddelta_raw;
+  float* dconv_w;
+  float* dconv_b;           // nullable
+  float* ddelta_bias;       // nullable
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;                // nullable
+  void* dz;                 // non-null exactly when z is
+  float* dh0;               // nullable
+  int64_t batch, dim, dstate, seqlen;
+  bool bf16;
+  bool force_general;
+  void* workspace;
+};
+
+size_t scan_fused_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
+hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream);
+
 // d_state 33..128: the same gradient by slices of 32 states, in fp32.
 size_t scan_bwd_wide_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
 hipError_t launch_scan_bwd_wide(const ScanBwdParams& p, hipStream_t stream);

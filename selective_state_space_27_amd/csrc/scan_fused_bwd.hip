@@ -1,0 +1,292 @@
+// Backward of the selective scan fed by its prologue (the short causal
+// convolution forming u, softplus forming delta; see scan.hip's fused form).
+//
+// "Mamba (deep learning)" (paragraph on the block: a convolution in front of
+// the SSM on the input branch) and "Mamba State-Space Models" (usage example,
+// kernel size 4) give the prologue; the gradient is the chain rule through it
+// around the scan's own gradient:
+//   c = conv_b + sum_k w_k x[t-3+k] (zeros before step 0),  u = c or silu(c),
+//   v = delta_raw + delta_bias,  delta = v or softplus(v);
+//   dc = du silu'(c) (du without silu),  silu'(c) = s (1 + c (1 - s)),
+//   s = sigmoid(c);  dv = ddelta sigmoid(v) (ddelta without softplus);
+//   dx[s] = sum_k w_k dc[s+3-k] (terms past L dropped);
+//   dconv_w[d,k] = sum_{b,t} dc[t] x[t-3+k];  dconv_b = sum dc;
+//   ddelta_raw = dv;  ddelta_bias = sum dv.
+// Passes: u and delta formed once in fp32 (they never exist outside the
+// forward kernel, so the scan's gradient is taken at their fp32 values), the
+// other [b, d, L] and [b, N, L] inputs widened to fp32, the scan's backward in
+// fp32 (by slices of 32 states above 32), then the prologue's chain rule:
+// an elementwise pass (dc, dv, ddelta_raw), a pass for dx, and one workgroup
+// per channel for the tap and bias sums (a fixed order: bitwise repeatable).
+// Gradients in the I/O type are rounded once, at the end.
+//
+// Workspace: a 256-byte head (word 0: the call's status), the scan backward's
+// workspace, then the fp32 buffers of the layout below.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mss {
+namespace {
+
+constexpr size_t kMaxFbGrid = 16384;
+inline unsigned fb_grid(size_t items) {
+  return (unsigned)std::max<size_t>(1, std::min<size_t>((items + 255) / 256, kMaxFbGrid));
+}
+inline size_t al256f(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__device__ __forceinline__ float ld_io(const void* p, size_t i, int bf16) {
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+__device__ __forceinline__ void st_io(void* p, size_t i, float v, int bf16) {
+  if (bf16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  else static_cast<float*>(p)[i] = v;
+}
+__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
+
+// The convolution's pre-activation at step t of row r (a [b, d] row of x).
+__device__ __forceinline__ float conv_at(const void* x, size_t row_base, int t, const float* w, float cb, int bf16) {
+  float c = cb;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = t - 3 + k;
+    if (s >= 0) c = __builtin_fmaf(w[k], ld_io(x, row_base + s, bf16), c);
+  }
+  return c;
+}
+
+// u, delta in fp32 from x, delta_raw (one element per thread).
+__global__ void __launch_bounds__(256) fb_prologue(const void* __restrict__ x, const void* __restrict__ delta_raw,
+                                                   const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+                                                   const float* __restrict__ delta_bias, float* __restrict__ u,
+                                                   float* __restrict__ delta, size_t rows, int dim, int L, int silu_on,
+                                                   int softplus_on, int bf16) {
+  const size_t total = rows * (size_t)L;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t r = i / (size_t)L;
+    const int t = (int)(i % (size_t)L), d = (int)(r % (size_t)dim);
+    const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
+    const float c = conv_at(x, r * (size_t)L, t, w, conv_b ? conv_b[d] : 0.f, bf16);
+    u[i] = silu_on ? c * sigmoid_f(c) : c;
+    const float v = ld_io(delta_raw, i, bf16) + (delta_bias ? delta_bias[d] : 0.f);
+    // softplus(v) = max(v, 0) + log1p(exp(-|v|))
+    delta[i] = softplus_on ? fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))) : v;
+  }
+}
+
+__global__ void __launch_bounds__(256) fb_to_f32(const void* __restrict__ src, float* __restrict__ dst, size_t n,
+                                                 int bf16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = ld_io(src, i, bf16);
+}
+
+__global__ void __launch_bounds__(256) fb_from_f32(const float* __restrict__ src, void* __restrict__ dst, size_t n,
+                                                   int bf16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) st_io(dst, i, src[i], bf16);
+}
+
+// dc = du silu'(c) in place of du; dv = ddelta sigmoid(v) in place of
+// ddelta, and ddelta_raw = dv in the I/O type.
+__global__ void __launch_bounds__(256) fb_chain(const void* __restrict__ x, const void* __restrict__ delta_raw,
+                                                const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+                                                const float* __restrict__ delta_bias, float* __restrict__ du_dc,
+                                                float* __restrict__ dd_dv, void* __restrict__ ddelta_raw, size_t rows,
+                                                int dim, int L, int silu_on, int softplus_on, int bf16) {
+  const size_t total = rows * (size_t)L;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t r = i / (size_t)L;
+    const int t = (int)(i % (size_t)L), d = (int)(r % (size_t)dim);
+    if (silu_on) {
+      const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
+      const float c = conv_at(x, r * (size_t)L, t, w, conv_b ? conv_b[d] : 0.f, bf16);
+      const float s = sigmoid_f(c);
+      du_dc[i] *= s * (1.0f + c * (1.0f - s));
+    }
+    float dv = dd_dv[i];
+    if (softplus_on) {
+      const float v = ld_io(delta_raw, i, bf16) + (delta_bias ? delta_bias[d] : 0.f);
+      dv *= sigmoid_f(v);
+      dd_dv[i] = dv;
+    }
+    st_io(ddelta_raw, i, dv, bf16);
+  }
+}
+
+// dx[s] = sum_k w_k dc[s+3-k] (terms past L dropped).
+__global__ void __launch_bounds__(256) fb_dx(const float* __restrict__ dc, const float* __restrict__ conv_w,
+                                             void* __restrict__ dx, size_t rows, int dim, int L, int bf16) {
+  const size_t total = rows * (size_t)L;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t r = i / (size_t)L;
+    const int s = (int)(i % (size_t)L), d = (int)(r % (size_t)dim);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = s + 3 - k;
+      if (t < L) acc = __builtin_fmaf(conv_w[4 * d + k], dc[r * (size_t)L + t], acc);
+    }
+    st_io(dx, i, acc, bf16);
+  }
+}
+
+// One workgroup per channel d: dconv_w[d, k] = sum_{b,t} dc x[t-3+k],
+// dconv_b[d] = sum dc, ddelta_bias[d] = sum dv; each thread sums a fixed
+// stride of the (b, t) pairs, then a fixed tree over the threads.
+__global__ void __launch_bounds__(256) fb_channel_sums(const void* __restrict__ x, const float* __restrict__ dc,
+                                                       const float* __restrict__ dv, float* __restrict__ dconv_w,
+                                                       float* __restrict__ dconv_b, float* __restrict__ ddelta_bias,
+                                                       int batch, int dim, int L, int bf16) {
+  __shared__ float red[6][256];
+  const int d = blockIdx.x;
+  float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const size_t n = (size_t)batch * L;
+  for (size_t j = threadIdx.x; j < n; j += blockDim.x) {
+    const int b = (int)(j / (size_t)L), t = (int)(j % (size_t)L);
+    const size_t base = ((size_t)b * dim + d) * (size_t)L;
+    const float g = dc[base + t];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = t - 3 + k;
+      if (s >= 0) acc[k] = __builtin_fmaf(g, ld_io(x, base + s, bf16), acc[k]);
+    }
+    acc[4] += g;
+    acc[5] += dv[base + t];
+  }
+#pragma unroll
+  for (int q = 0; q < 6; ++q) red[q][threadIdx.x] = acc[q];
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+#pragma unroll
+      for (int q = 0; q < 6; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + h];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dconv_w[4 * d + k] = red[k][0];
+    if (dconv_b) dconv_b[d] = red[4][0];
+    if (ddelta_bias) ddelta_bias[d] = red[5][0];
+  }
+}
+
+// Status: mode 0 clears the call's word, 1 copies the scan backward's into it.
+__global__ void fb_status(int* __restrict__ head, const int* __restrict__ inner, int mode) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  head[0] = mode == 0 ? 0 : *inner;
+}
+
+struct FbLayout {
+  size_t head, inner, u, delta, z, dy, B, C, du, dd, dz, dB, dC, total;
+};
+
+FbLayout fb_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  const size_t bdl = (size_t)batch * dim * seqlen * 4;
+  const size_t bnl = (size_t)batch * dstate * seqlen * 4;
+  FbLayout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += al256f(bytes);
+    return at;
+  };
+  l.head = take(256);
+  l.inner = take(dstate > 32 ? scan_bwd_wide_workspace_bytes(batch, dim, seqlen)
+                             : scan_bwd_workspace_bytes(batch, dim, dstate, seqlen));
+  l.u = take(bdl);
+  l.delta = take(bdl);
+  l.z = take(bdl);
+  l.dy = take(bdl);
+  l.B = take(bnl);
+  l.C = take(bnl);
+  l.du = take(bdl);
+  l.dd = take(bdl);
+  l.dz = take(bdl);
+  l.dB = take(bnl);
+  l.dC = take(bnl);
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+size_t scan_fused_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  return fb_layout(batch, dim, dstate, seqlen).total;
+}
+
+hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream) {
+  const FbLayout l = fb_layout(p.batch, p.dim, p.dstate, p.seqlen);
+  char* ws = static_cast<char*>(p.workspace);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const int bf16 = p.bf16 ? 1 : 0;
+  const size_t rows = (size_t)p.batch * p.dim;
+  const size_t bdl = rows * (size_t)p.seqlen;
+  const size_t bnl = (size_t)p.batch * p.dstate * p.seqlen;
+  const int dim = (int)p.dim, L = (int)p.seqlen;
+  hipError_t err = hipSuccess;
+  auto check = [&]() {
+    err = hipGetLastError();
+    return err == hipSuccess;
+  };
+
+  int* head = reinterpret_cast<int*>(ws + l.head);
+  hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, head, 0);
+  hipLaunchKernelGGL(fb_prologue, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
+                     p.delta_bias, fp(l.u), fp(l.delta), rows, dim, L, p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
+  if (p.z) hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.z, fp(l.z), bdl, bf16);
+  hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.dy, fp(l.dy), bdl, bf16);
+  hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, p.B, fp(l.B), bnl, bf16);
+  hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, p.C, fp(l.C), bnl, bf16);
+  if (!check()) return err;
+
+  ScanBwdParams q;
+  q.fwd.u = fp(l.u);
+  q.fwd.delta = fp(l.delta);
+  q.fwd.A = p.A;
+  q.fwd.B = fp(l.B);
+  q.fwd.C = fp(l.C);
+  q.fwd.D = p.D;
+  q.fwd.z = p.z ? fp(l.z) : nullptr;
+  q.fwd.h0 = p.h0;
+  q.fwd.y = nullptr;
+  q.fwd.h_last = nullptr;
+  q.fwd.batch = p.batch;
+  q.fwd.dim = p.dim;
+  q.fwd.dstate = p.dstate;
+  q.fwd.seqlen = p.seqlen;
+  q.fwd.bf16 = false;
+  q.fwd.force_general = p.force_general;
+  q.fwd.workspace = ws + l.inner;
+  q.dy = fp(l.dy);
+  q.dh_last = p.dh_last;
+  q.du = fp(l.du);
+  q.ddelta = fp(l.dd);
+  q.dA = p.dA;
+  q.dB = fp(l.dB);
+  q.dC = fp(l.dC);
+  q.dD = p.dD;
+  q.dz = p.z ? fp(l.dz) : nullptr;
+  q.dh0 = p.dh0;
+  err = p.dstate > 32 ? launch_scan_bwd_wide(q, stream) : launch_scan_bwd(q, stream);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, reinterpret_cast<const int*>(ws + l.inner), 1);
+
+  hipLaunchKernelGGL(fb_chain, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
+                     p.delta_bias, fp(l.du), fp(l.dd), p.ddelta_raw, rows, dim, L, p.conv_silu ? 1 : 0,
+                     p.softplus ? 1 : 0, bf16);
+  hipLaunchKernelGGL(fb_dx, dim3(fb_grid(bdl)), dim3(256), 0, stream, fp(l.du), p.conv_w, p.dx, rows, dim, L, bf16);
+  hipLaunchKernelGGL(fb_channel_sums, dim3((unsigned)p.dim), dim3(256), 0, stream, p.x, fp(l.du), fp(l.dd),
+                     p.dconv_w, p.dconv_b, p.ddelta_bias, (int)p.batch, dim, L, bf16);
+  hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dB), p.dB, bnl, bf16);
+  hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dC), p.dC, bnl, bf16);
+  if (p.z) hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, fp(l.dz), p.dz, bdl, bf16);
+  check();
+  return err;
+}
+
+}  // namespace mss

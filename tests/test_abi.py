@@ -403,3 +403,41 @@ def test_ssd_chunks_per_piece_override_and_workspace(monkeypatch):
     cap = lib.mss_ssd_workspace_size(*long_shape, BF16)
     monkeypatch.setenv("MSS_SSD_CHUNKS_PER_PIECE", "1")
     assert lib.mss_ssd_workspace_size(*long_shape, BF16) == cap
+
+
+def fused_bwd_call(**kw):
+    b, d, n, L = kw.pop("shape", (2, 64, 16, 128))
+    io = kw.pop("io", BF16)
+    ws_bytes = kw.pop("ws_bytes", mss.lib().mss_selective_scan_fused_bwd_workspace_size(b, d, n, L, io, 0) or 1 << 20)
+    names = ("x", "conv_w", "conv_b", "delta_raw", "delta_bias", "A", "B", "C", "D", "z", "h0", "dy", "dh_last", "dx",
+             "ddelta_raw", "dconv_w", "dconv_b", "ddelta_bias", "dA", "dB", "dC", "dD", "dz", "dh0")
+    args = {k: P(i) for i, k in enumerate(names)}
+    args.update(ws=P(len(names)), flags=0)
+    args.update(kw)
+    return mss.lib().mss_selective_scan_fused_bwd(*(args[k] for k in names), b, d, n, L, io, args["flags"],
+                                                  args["ws"], ws_bytes, None)
+
+
+def test_fused_scan_bwd_validation_errors():
+    """The fused backward's errors come back from the host checks (fake
+    pointers; nothing is enqueued); its workspace covers the scan's backward
+    and the fp32 copies, at any d_state the scan's backward takes."""
+    for k in ("x", "conv_w", "delta_raw", "A", "B", "C", "dy", "dx", "ddelta_raw", "dconv_w", "dA", "dB", "dC"):
+        assert fused_bwd_call(**{k: None}) == NULL, k
+    assert fused_bwd_call(dz=None) == NULL              # z given without dz
+    assert fused_bwd_call(z=None) == NULL               # dz given without z
+    assert fused_bwd_call(shape=(2, 64, 16, 0)) == SHAPE
+    assert fused_bwd_call(io=7) == DTYPE
+    assert fused_bwd_call(shape=(2, 64, 129, 128)) == UNSUP
+    assert fused_bwd_call(flags=0x80) == UNSUP
+    assert fused_bwd_call(dconv_w=P(15, 4)) == ALIGN
+    assert fused_bwd_call(ws=None) == WS
+    assert fused_bwd_call(ws_bytes=16) == WS
+    assert fused_bwd_call(dx=P(0, 256)) == ALIAS        # dx inside x
+    assert fused_bwd_call(dconv_b=P(1)) == ALIAS        # dconv_b on the taps
+    assert fused_bwd_call(ddelta_raw=P(13)) == ALIAS    # two outputs
+    lib = mss.lib()
+    for n in (16, 32, 64, 128):
+        assert lib.mss_selective_scan_fused_bwd_workspace_size(4, 512, n, 1024, BF16, 0) > \
+            lib.mss_selective_scan_bwd_workspace_size(4, 512, n, 1024, BF16, 0)
+    assert lib.mss_selective_scan_fused_bwd_workspace_size(4, 512, 129, 1024, BF16, 0) == 0
