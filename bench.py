@@ -62,7 +62,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "state updates/s (B*L*D*N) + % HBM roofline, Mamba-2.8b-shaped scan"
 
 
-SCAN_WORKLOADS = ("scan_2p8b", "scan_130m", "scan_2p8b_bwd", "scan_2p8b_fused")
+SCAN_WORKLOADS = ("scan_2p8b", "scan_130m", "scan_2p8b_bwd", "scan_2p8b_fused", "scan_2p8b_fused_bwd")
 
 
 def parse():
@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scan_2p8b",
                     choices=["scan_2p8b", "scan_130m", "decode_2p8b", "ssd_2p8b", "ssd_2p8b_bwd", "scan_m2shape",
-                             "scan_2p8b_bwd", "scan_2p8b_fused", "decode_m3", "copy"])
+                             "scan_2p8b_bwd", "scan_2p8b_fused", "scan_2p8b_fused_bwd", "decode_m3", "copy"])
     ap.add_argument("--seqlen", type=int, default=0,
                     help="scan/SSD workloads: sequence length (inputs repeated along L); 0 = the preset's")
     ap.add_argument("--batch", type=int, default=0,
@@ -434,6 +434,53 @@ def bench_scan_bwd(args, torch, mss, I, cfg):
     return res, scan_bwd_bytes(b, d, n, L, es), ms, kernel, files, cpu
 
 
+def bench_scan_fused_bwd(args, torch, mss, I, cfg):
+    x = I.scan_fused_inputs(cfg)
+    keys = ("x", "conv_w", "conv_b", "delta_raw", "delta_bias", "A", "B", "C", "D", "z")
+    g = {k: to_dev(torch, x[k]) for k in keys}
+    dy_host = I.scan_grad_output(cfg)
+    dy = to_dev(torch, dy_host)
+    io_dt = g["x"].dtype
+    b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    flags = mss.MSS_FLAG_CONV_SILU | mss.MSS_FLAG_DELTA_SOFTPLUS
+    ws = torch.empty(mss.lib().mss_selective_scan_fused_bwd_workspace_size(b, d, n, L, mss._io_code(io_dt), flags),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        mss.selective_scan_fused_bwd(*(g[k] for k in keys), dy=dy, conv_silu=True, softplus=True, workspace=ws)
+
+    ms = time_region(torch, step, args.steps, args.warmup)
+    es = 2 if cfg.io == "bf16" else 4
+    res = {"metric": "state updates/s (B*L*D*N), selective scan backward through its prologue",
+           "value": b * d * n * L / (ms * 1e-3), "unit": "state updates/s", "ms_per_step": ms, "dtype": "f32",
+           "config": {"workload": f"{cfg.name}_fused_bwd: backward of the scan fed by its prologue (silu "
+                                  f"convolution, softplus delta) b={b} d_inner={d} d_state={n} L={L}, {cfg.io} "
+                                  f"x/delta_raw/B/C/z/dy and gradients, fp32 taps, biases, A/D and their gradients",
+                      "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io_dtype": cfg.io,
+                      "gradients": "dx, ddelta_raw, dconv_w, dconv_b, ddelta_bias, dA, dB, dC, dD, dz"}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        f64 = lambda k: I.to_f64(x[k][:1], cfg.io)  # bounded sample: batch row 0, every channel, full L
+        args64 = (f64("x"), x["conv_w"], x["conv_b"], f64("delta_raw"), x["delta_bias"], x["A"].astype(np.float64),
+                  f64("B"), f64("C"), x["D"].astype(np.float64), f64("z"), None)
+        dy64 = I.to_f64(dy_host[:1], cfg.io)
+        th, info = host_cpus()
+        d1 = max(1, d // 64)
+        one = tuple(None if a is None else a[:, :d1] if a.ndim == 3 and a.shape[1] == d else
+                    a[:d1] if a.ndim in (1, 2) else a for a in args64)
+        cpu = cpu_leg(lambda: oracle.selective_scan_fused_bwd(*args64, dy=dy64, conv_silu=True, softplus=True,
+                                                              threads=th), d * n * L,
+                      lambda: oracle.selective_scan_fused_bwd(*one, dy=dy64[:, :d1], conv_silu=True, softplus=True,
+                                                              threads=1), d1 * n * L, "state updates/s", th, info,
+                      f"batch row 0 of {b} (all {d} channels, full L={L}), fused backward",
+                      f"batch row 0, channels 0..{d1 - 1}, fused backward")
+    files = ["scan.hip", "scan_bwd.hip", "scan_fused_bwd.hip", "scan_layout.hpp", "common.hpp"]
+    kernel = "scan_bwd_kernel (+ prologue, fp32 copies, checkpoint forward, reductions and the prologue's chain rule)"
+    # The scan backward's bytes with x, delta_raw for u, delta and dx, ddelta_raw for du, ddelta, plus the taps.
+    return res, scan_bwd_bytes(b, d, n, L, es) + 2 * d * 16 + 4 * d * 4, ms, kernel, files, cpu
+
+
 def bench_decode(args, torch, mss, I):
     cfg = I.DECODE_2P8B
     st = I.decode_static(cfg)
@@ -628,7 +675,7 @@ def main():
         sys.exit(2)
     if args.seqlen < 0 or args.batch < 0 or ((args.seqlen or args.batch) and
                                              args.workload in ("decode_2p8b", "copy", "scan_2p8b_fused",
-                                                               "ssd_2p8b_bwd", "decode_m3")):
+                                                               "scan_2p8b_fused_bwd", "ssd_2p8b_bwd", "decode_m3")):
         print("bench.py: --seqlen and --batch take positive sizes and apply to the scan and SSD workloads",
               file=sys.stderr)
         sys.exit(2)
@@ -662,6 +709,8 @@ def main():
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan(args, torch, mss, I, I.SCAN_M2)
     elif args.workload == "scan_2p8b_bwd":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan_bwd(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
+    elif args.workload == "scan_2p8b_fused_bwd":
+        res, nbytes, launch_ms, kernel, files, cpu = bench_scan_fused_bwd(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
     elif args.workload == "scan_2p8b_fused":
         res, nbytes, launch_ms, kernel, files, cpu = bench_scan_fused(args, torch, mss, I, scan_cfg(I.SCAN_2P8B))
     elif args.workload == "decode_m3":

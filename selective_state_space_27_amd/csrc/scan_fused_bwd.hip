@@ -56,23 +56,32 @@ __device__ __forceinline__ float conv_at(const void* x, size_t row_base, int t, 
   return c;
 }
 
-// u, delta in fp32 from x, delta_raw (one element per thread).
+// Grid of the per-element passes: steps of a row along x, rows along y (each
+// loop strides over its grid dimension, so any size fits).
+inline dim3 fb_grid2(size_t rows, int L) {
+  const unsigned gx = (unsigned)std::min<int64_t>(((int64_t)L + 255) / 256, 16);
+  const unsigned gy = (unsigned)std::max<size_t>(1, std::min<size_t>(rows, (size_t)(8192 / gx)));
+  return dim3(gx, gy);
+}
+
+// u, delta in fp32 from x, delta_raw (one step of one row per thread).
 __global__ void __launch_bounds__(256) fb_prologue(const void* __restrict__ x, const void* __restrict__ delta_raw,
                                                    const float* __restrict__ conv_w, const float* __restrict__ conv_b,
                                                    const float* __restrict__ delta_bias, float* __restrict__ u,
                                                    float* __restrict__ delta, size_t rows, int dim, int L, int silu_on,
                                                    int softplus_on, int bf16) {
-  const size_t total = rows * (size_t)L;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const size_t r = i / (size_t)L;
-    const int t = (int)(i % (size_t)L), d = (int)(r % (size_t)dim);
+  for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const int d = (int)(r % (size_t)dim);
     const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
-    const float c = conv_at(x, r * (size_t)L, t, w, conv_b ? conv_b[d] : 0.f, bf16);
-    u[i] = silu_on ? c * sigmoid_f(c) : c;
-    const float v = ld_io(delta_raw, i, bf16) + (delta_bias ? delta_bias[d] : 0.f);
-    // softplus(v) = max(v, 0) + log1p(exp(-|v|))
-    delta[i] = softplus_on ? fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))) : v;
+    const float cb = conv_b ? conv_b[d] : 0.f, db = delta_bias ? delta_bias[d] : 0.f;
+    const size_t base = r * (size_t)L;
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < L; t += gridDim.x * blockDim.x) {
+      const float c = conv_at(x, base, t, w, cb, bf16);
+      u[base + t] = silu_on ? c * sigmoid_f(c) : c;
+      const float v = ld_io(delta_raw, base + t, bf16) + db;
+      // softplus(v) = max(v, 0) + log1p(exp(-|v|))
+      delta[base + t] = softplus_on ? fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))) : v;
+    }
   }
 }
 
@@ -95,48 +104,50 @@ __global__ void __launch_bounds__(256) fb_chain(const void* __restrict__ x, cons
                                                 const float* __restrict__ delta_bias, float* __restrict__ du_dc,
                                                 float* __restrict__ dd_dv, void* __restrict__ ddelta_raw, size_t rows,
                                                 int dim, int L, int silu_on, int softplus_on, int bf16) {
-  const size_t total = rows * (size_t)L;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const size_t r = i / (size_t)L;
-    const int t = (int)(i % (size_t)L), d = (int)(r % (size_t)dim);
-    if (silu_on) {
-      const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
-      const float c = conv_at(x, r * (size_t)L, t, w, conv_b ? conv_b[d] : 0.f, bf16);
-      const float s = sigmoid_f(c);
-      du_dc[i] *= s * (1.0f + c * (1.0f - s));
+  for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const int d = (int)(r % (size_t)dim);
+    const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
+    const float cb = conv_b ? conv_b[d] : 0.f, db = delta_bias ? delta_bias[d] : 0.f;
+    const size_t base = r * (size_t)L;
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < L; t += gridDim.x * blockDim.x) {
+      const size_t i = base + t;
+      if (silu_on) {
+        const float c = conv_at(x, base, t, w, cb, bf16);
+        const float s = sigmoid_f(c);
+        du_dc[i] *= s * (1.0f + c * (1.0f - s));
+      }
+      float dv = dd_dv[i];
+      if (softplus_on) {
+        dv *= sigmoid_f(ld_io(delta_raw, i, bf16) + db);
+        dd_dv[i] = dv;
+      }
+      st_io(ddelta_raw, i, dv, bf16);
     }
-    float dv = dd_dv[i];
-    if (softplus_on) {
-      const float v = ld_io(delta_raw, i, bf16) + (delta_bias ? delta_bias[d] : 0.f);
-      dv *= sigmoid_f(v);
-      dd_dv[i] = dv;
-    }
-    st_io(ddelta_raw, i, dv, bf16);
   }
 }
 
 // dx[s] = sum_k w_k dc[s+3-k] (terms past L dropped).
 __global__ void __launch_bounds__(256) fb_dx(const float* __restrict__ dc, const float* __restrict__ conv_w,
                                              void* __restrict__ dx, size_t rows, int dim, int L, int bf16) {
-  const size_t total = rows * (size_t)L;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const size_t r = i / (size_t)L;
-    const int s = (int)(i % (size_t)L), d = (int)(r % (size_t)dim);
-    float acc = 0.f;
+  for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const int d = (int)(r % (size_t)dim);
+    const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
+    const size_t base = r * (size_t)L;
+    for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < L; s += gridDim.x * blockDim.x) {
+      float acc = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = s + 3 - k;
-      if (t < L) acc = __builtin_fmaf(conv_w[4 * d + k], dc[r * (size_t)L + t], acc);
+      for (int k = 0; k < 4; ++k) {
+        const int t = s + 3 - k;
+        if (t < L) acc = __builtin_fmaf(w[k], dc[base + t], acc);
+      }
+      st_io(dx, base + s, acc, bf16);
     }
-    st_io(dx, i, acc, bf16);
   }
 }
 
 // One workgroup per channel d: dconv_w[d, k] = sum_{b,t} dc x[t-3+k],
 // dconv_b[d] = sum dc, ddelta_bias[d] = sum dv; each thread sums a fixed
-// stride of the (b, t) pairs, then a fixed tree over the threads.
+// stride of the steps of every batch row, then a fixed tree over the threads.
 __global__ void __launch_bounds__(256) fb_channel_sums(const void* __restrict__ x, const float* __restrict__ dc,
                                                        const float* __restrict__ dv, float* __restrict__ dconv_w,
                                                        float* __restrict__ dconv_b, float* __restrict__ ddelta_bias,
@@ -144,18 +155,18 @@ __global__ void __launch_bounds__(256) fb_channel_sums(const void* __restrict__ 
   __shared__ float red[6][256];
   const int d = blockIdx.x;
   float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const size_t n = (size_t)batch * L;
-  for (size_t j = threadIdx.x; j < n; j += blockDim.x) {
-    const int b = (int)(j / (size_t)L), t = (int)(j % (size_t)L);
+  for (int b = 0; b < batch; ++b) {
     const size_t base = ((size_t)b * dim + d) * (size_t)L;
-    const float g = dc[base + t];
+    for (int t = threadIdx.x; t < L; t += blockDim.x) {
+      const float g = dc[base + t];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = t - 3 + k;
-      if (s >= 0) acc[k] = __builtin_fmaf(g, ld_io(x, base + s, bf16), acc[k]);
+      for (int k = 0; k < 4; ++k) {
+        const int s = t - 3 + k;
+        if (s >= 0) acc[k] = __builtin_fmaf(g, ld_io(x, base + s, bf16), acc[k]);
+      }
+      acc[4] += g;
+      acc[5] += dv[base + t];
     }
-    acc[4] += g;
-    acc[5] += dv[base + t];
   }
 #pragma unroll
   for (int q = 0; q < 6; ++q) red[q][threadIdx.x] = acc[q];
@@ -236,7 +247,7 @@ hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream
 
   int* head = reinterpret_cast<int*>(ws + l.head);
   hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, head, 0);
-  hipLaunchKernelGGL(fb_prologue, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
+  hipLaunchKernelGGL(fb_prologue, fb_grid2(rows, L), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
                      p.delta_bias, fp(l.u), fp(l.delta), rows, dim, L, p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
   if (p.z) hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.z, fp(l.z), bdl, bf16);
   hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.dy, fp(l.dy), bdl, bf16);
@@ -276,10 +287,10 @@ hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, reinterpret_cast<const int*>(ws + l.inner), 1);
 
-  hipLaunchKernelGGL(fb_chain, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
+  hipLaunchKernelGGL(fb_chain, fb_grid2(rows, L), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
                      p.delta_bias, fp(l.du), fp(l.dd), p.ddelta_raw, rows, dim, L, p.conv_silu ? 1 : 0,
                      p.softplus ? 1 : 0, bf16);
-  hipLaunchKernelGGL(fb_dx, dim3(fb_grid(bdl)), dim3(256), 0, stream, fp(l.du), p.conv_w, p.dx, rows, dim, L, bf16);
+  hipLaunchKernelGGL(fb_dx, fb_grid2(rows, L), dim3(256), 0, stream, fp(l.du), p.conv_w, p.dx, rows, dim, L, bf16);
   hipLaunchKernelGGL(fb_channel_sums, dim3((unsigned)p.dim), dim3(256), 0, stream, p.x, fp(l.du), fp(l.dd),
                      p.dconv_w, p.dconv_b, p.ddelta_bias, (int)p.batch, dim, L, bf16);
   hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dB), p.dB, bnl, bf16);
