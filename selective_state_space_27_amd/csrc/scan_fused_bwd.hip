@@ -32,7 +32,7 @@ namespace {
 
 constexpr size_t kMaxFbGrid = 16384;
 inline unsigned fb_grid(size_t items) {
-  return (unsigned)std::max<size_t>(1, std::min<size_t>((items + 255) / 256, kMaxFbGrid));
+  return (unsigned)std::max<size_t>(1, std::min<size_t>((items + 1023) / 1024, kMaxFbGrid));
 }
 inline size_t al256f(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -45,127 +45,265 @@ __device__ __forceinline__ void st_io(void* p, size_t i, float v, int bf16) {
 }
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
-// The convolution's pre-activation at step t of row r (a [b, d] row of x).
-__device__ __forceinline__ float conv_at(const void* x, size_t row_base, int t, const float* w, float cb, int bf16) {
-  float c = cb;
+// Groups of four consecutive elements: the per-element passes move 8 (bf16)
+// or 16 (fp32) bytes per lane and access, where one element per lane left
+// them far below the HBM rate.  V: the group is whole and starts at a
+// multiple of 4 elements from a 16-byte-aligned base (one vector access);
+// otherwise elements k < n are accessed one by one and the rest read as 0.
+template <bool V>
+__device__ __forceinline__ void ld4(const void* p, size_t i, int n, int bf16, float (&v)[4]) {
+  if (V) {
+    if (bf16) {
+      const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+      v[0] = __uint_as_float(q.x << 16);
+      v[1] = __uint_as_float(q.x & 0xffff0000u);
+      v[2] = __uint_as_float(q.y << 16);
+      v[3] = __uint_as_float(q.y & 0xffff0000u);
+    } else {
+      const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+      v[0] = q.x;
+      v[1] = q.y;
+      v[2] = q.z;
+      v[3] = q.w;
+    }
+  } else {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int s = t - 3 + k;
-    if (s >= 0) c = __builtin_fmaf(w[k], ld_io(x, row_base + s, bf16), c);
+    for (int k = 0; k < 4; ++k) v[k] = k < n ? ld_io(p, i + k, bf16) : 0.f;
   }
-  return c;
+}
+template <bool V>
+__device__ __forceinline__ void ld4f(const float* p, size_t i, int n, float (&v)[4]) {
+  ld4<V>(p, i, n, 0, v);
+}
+template <bool V>
+__device__ __forceinline__ void st4(void* p, size_t i, int n, int bf16, const float (&v)[4]) {
+  if (V) {
+    if (bf16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(pack_bf16x2(v[0], v[1]),
+                                                                            pack_bf16x2(v[2], v[3]));
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < n) st_io(p, i + k, v[k], bf16);
+  }
 }
 
-// Grid of the per-element passes: steps of a row along x, rows along y (each
-// loop strides over its grid dimension, so any size fits).
+// The convolution's pre-activations at steps t0..t0+3 of a row from the
+// window win[m] = x[t0-4+m] (m = 0..7; steps before 0 are skipped, as the
+// filter sees zeros there).
+__device__ __forceinline__ void conv4(const float (&win)[8], int t0, const float* w, float cb, float (&c)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float a = cb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (t0 + k - 3 + q >= 0) a = __builtin_fmaf(w[q], win[k + 1 + q], a);
+    c[k] = a;
+  }
+}
+
+// x over steps t0-4..t0+3 of the row at base (t0 a multiple of 4, so the
+// group before a non-first group is whole).
+template <bool V>
+__device__ __forceinline__ void x_window(const void* x, size_t base, int t0, int n, int bf16, float (&win)[8]) {
+  float prev[4] = {0.f, 0.f, 0.f, 0.f}, cur[4];
+  if (t0 > 0) ld4<V>(x, base + t0 - 4, 4, bf16, prev);
+  ld4<V>(x, base + t0, n, bf16, cur);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    win[k] = prev[k];
+    win[4 + k] = cur[k];
+  }
+}
+
+// Grid of the per-row passes: groups of 4 steps of a row along x, rows along
+// y (each loop strides over its grid dimension, so any size fits).
 inline dim3 fb_grid2(size_t rows, int L) {
-  const unsigned gx = (unsigned)std::min<int64_t>(((int64_t)L + 255) / 256, 16);
+  const int groups = (L + 3) / 4;
+  const unsigned gx = (unsigned)std::min<int64_t>(((int64_t)groups + 255) / 256, 16);
   const unsigned gy = (unsigned)std::max<size_t>(1, std::min<size_t>(rows, (size_t)(8192 / gx)));
   return dim3(gx, gy);
 }
 
-// u, delta in fp32 from x, delta_raw (one step of one row per thread).
+// u, delta in fp32 from x, delta_raw (four steps of one row per thread).
+template <bool V>
 __global__ void __launch_bounds__(256) fb_prologue(const void* __restrict__ x, const void* __restrict__ delta_raw,
                                                    const float* __restrict__ conv_w, const float* __restrict__ conv_b,
                                                    const float* __restrict__ delta_bias, float* __restrict__ u,
                                                    float* __restrict__ delta, size_t rows, int dim, int L, int silu_on,
                                                    int softplus_on, int bf16) {
+  const int groups = (L + 3) / 4;
   for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
     const int d = (int)(r % (size_t)dim);
     const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
     const float cb = conv_b ? conv_b[d] : 0.f, db = delta_bias ? delta_bias[d] : 0.f;
     const size_t base = r * (size_t)L;
-    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < L; t += gridDim.x * blockDim.x) {
-      const float c = conv_at(x, base, t, w, cb, bf16);
-      u[base + t] = silu_on ? c * sigmoid_f(c) : c;
-      const float v = ld_io(delta_raw, base + t, bf16) + db;
-      // softplus(v) = max(v, 0) + log1p(exp(-|v|))
-      delta[base + t] = softplus_on ? fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))) : v;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < groups; j += gridDim.x * blockDim.x) {
+      const int t0 = 4 * j, n = std::min(4, L - t0);
+      float win[8], c[4], v[4], uo[4], dl[4];
+      x_window<V>(x, base, t0, n, bf16, win);
+      conv4(win, t0, w, cb, c);
+      ld4<V>(delta_raw, base + t0, n, bf16, v);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uo[k] = silu_on ? c[k] * sigmoid_f(c[k]) : c[k];
+        const float vv = v[k] + db;
+        // softplus(v) = max(v, 0) + log1p(exp(-|v|))
+        dl[k] = softplus_on ? fmaxf(vv, 0.f) + log1pf(__expf(-fabsf(vv))) : vv;
+      }
+      st4<V>(u, base + t0, n, 0, uo);
+      st4<V>(delta, base + t0, n, 0, dl);
     }
   }
 }
 
+// Flat widening and narrowing, four elements per thread and step (the bases
+// are 16-byte aligned; a partial last group goes element by element).
 __global__ void __launch_bounds__(256) fb_to_f32(const void* __restrict__ src, float* __restrict__ dst, size_t n,
                                                  int bf16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = ld_io(src, i, bf16);
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    float v[4];
+    if (i + 4 <= n) {
+      ld4<true>(src, i, 4, bf16, v);
+      st4<true>(dst, i, 4, 0, v);
+    } else {
+      const int m = (int)(n - i);
+      ld4<false>(src, i, m, bf16, v);
+      st4<false>(dst, i, m, 0, v);
+    }
+  }
 }
 
 __global__ void __launch_bounds__(256) fb_from_f32(const float* __restrict__ src, void* __restrict__ dst, size_t n,
                                                    int bf16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) st_io(dst, i, src[i], bf16);
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    float v[4];
+    if (i + 4 <= n) {
+      ld4f<true>(src, i, 4, v);
+      st4<true>(dst, i, 4, bf16, v);
+    } else {
+      const int m = (int)(n - i);
+      ld4f<false>(src, i, m, v);
+      st4<false>(dst, i, m, bf16, v);
+    }
+  }
 }
 
 // dc = du silu'(c) in place of du; dv = ddelta sigmoid(v) in place of
 // ddelta, and ddelta_raw = dv in the I/O type.
+template <bool V>
 __global__ void __launch_bounds__(256) fb_chain(const void* __restrict__ x, const void* __restrict__ delta_raw,
                                                 const float* __restrict__ conv_w, const float* __restrict__ conv_b,
                                                 const float* __restrict__ delta_bias, float* __restrict__ du_dc,
                                                 float* __restrict__ dd_dv, void* __restrict__ ddelta_raw, size_t rows,
                                                 int dim, int L, int silu_on, int softplus_on, int bf16) {
+  const int groups = (L + 3) / 4;
   for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
     const int d = (int)(r % (size_t)dim);
     const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
     const float cb = conv_b ? conv_b[d] : 0.f, db = delta_bias ? delta_bias[d] : 0.f;
     const size_t base = r * (size_t)L;
-    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < L; t += gridDim.x * blockDim.x) {
-      const size_t i = base + t;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < groups; j += gridDim.x * blockDim.x) {
+      const int t0 = 4 * j, n = std::min(4, L - t0);
+      const size_t i = base + t0;
       if (silu_on) {
-        const float c = conv_at(x, base, t, w, cb, bf16);
-        const float s = sigmoid_f(c);
-        du_dc[i] *= s * (1.0f + c * (1.0f - s));
+        float win[8], c[4], g[4];
+        x_window<V>(x, base, t0, n, bf16, win);
+        conv4(win, t0, w, cb, c);
+        ld4f<V>(du_dc, i, n, g);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float s = sigmoid_f(c[k]);
+          g[k] *= s * (1.0f + c[k] * (1.0f - s));
+        }
+        st4<V>(du_dc, i, n, 0, g);
       }
-      float dv = dd_dv[i];
+      float dv[4];
+      ld4f<V>(dd_dv, i, n, dv);
       if (softplus_on) {
-        dv *= sigmoid_f(ld_io(delta_raw, i, bf16) + db);
-        dd_dv[i] = dv;
+        float v[4];
+        ld4<V>(delta_raw, i, n, bf16, v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dv[k] *= sigmoid_f(v[k] + db);
+        st4<V>(dd_dv, i, n, 0, dv);
       }
-      st_io(ddelta_raw, i, dv, bf16);
+      st4<V>(ddelta_raw, i, n, bf16, dv);
     }
   }
 }
 
 // dx[s] = sum_k w_k dc[s+3-k] (terms past L dropped).
+template <bool V>
 __global__ void __launch_bounds__(256) fb_dx(const float* __restrict__ dc, const float* __restrict__ conv_w,
                                              void* __restrict__ dx, size_t rows, int dim, int L, int bf16) {
+  const int groups = (L + 3) / 4;
   for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
     const int d = (int)(r % (size_t)dim);
     const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
     const size_t base = r * (size_t)L;
-    for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < L; s += gridDim.x * blockDim.x) {
-      float acc = 0.f;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < groups; j += gridDim.x * blockDim.x) {
+      const int t0 = 4 * j, n = std::min(4, L - t0);
+      // win[m] = dc[t0+m], m = 0..7 (the next group may be partial or absent)
+      float cur[4], next[4] = {0.f, 0.f, 0.f, 0.f}, win[8], out[4];
+      ld4f<V>(dc, base + t0, n, cur);
+      if (t0 + 4 < L) {
+        if (V) ld4f<true>(dc, base + t0 + 4, 4, next);
+        else ld4f<false>(dc, base + t0 + 4, std::min(4, L - t0 - 4), next);
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int t = s + 3 - k;
-        if (t < L) acc = __builtin_fmaf(w[k], dc[base + t], acc);
+        win[k] = cur[k];
+        win[4 + k] = next[k];
       }
-      st_io(dx, base + s, acc, bf16);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (t0 + m + 3 - k < L) acc = __builtin_fmaf(w[k], win[m + 3 - k], acc);
+        out[m] = acc;
+      }
+      st4<V>(dx, base + t0, n, bf16, out);
     }
   }
 }
 
 // One workgroup per channel d: dconv_w[d, k] = sum_{b,t} dc x[t-3+k],
-// dconv_b[d] = sum dc, ddelta_bias[d] = sum dv; each thread sums a fixed
-// stride of the steps of every batch row, then a fixed tree over the threads.
+// dconv_b[d] = sum dc, ddelta_bias[d] = sum dv; each thread sums fixed
+// groups of four steps of every batch row, then a fixed tree over the
+// threads.
+template <bool V>
 __global__ void __launch_bounds__(256) fb_channel_sums(const void* __restrict__ x, const float* __restrict__ dc,
                                                        const float* __restrict__ dv, float* __restrict__ dconv_w,
                                                        float* __restrict__ dconv_b, float* __restrict__ ddelta_bias,
                                                        int batch, int dim, int L, int bf16) {
   __shared__ float red[6][256];
   const int d = blockIdx.x;
+  const int groups = (L + 3) / 4;
   float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < batch; ++b) {
     const size_t base = ((size_t)b * dim + d) * (size_t)L;
-    for (int t = threadIdx.x; t < L; t += blockDim.x) {
-      const float g = dc[base + t];
+    for (int j = threadIdx.x; j < groups; j += blockDim.x) {
+      const int t0 = 4 * j, n = std::min(4, L - t0);
+      float win[8], g[4], h[4];
+      x_window<V>(x, base, t0, n, bf16, win);
+      ld4f<V>(dc, base + t0, n, g);
+      ld4f<V>(dv, base + t0, n, h);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int s = t - 3 + k;
-        if (s >= 0) acc[k] = __builtin_fmaf(g, ld_io(x, base + s, bf16), acc[k]);
+      for (int m = 0; m < 4; ++m) {
+        if (m < n) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (t0 + m - 3 + k >= 0) acc[k] = __builtin_fmaf(g[m], win[m + 1 + k], acc[k]);
+          acc[4] += g[m];
+          acc[5] += h[m];
+        }
       }
-      acc[4] += g;
-      acc[5] += dv[base + t];
     }
   }
 #pragma unroll
@@ -247,8 +385,12 @@ hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream
 
   int* head = reinterpret_cast<int*>(ws + l.head);
   hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, head, 0);
-  hipLaunchKernelGGL(fb_prologue, fb_grid2(rows, L), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
-                     p.delta_bias, fp(l.u), fp(l.delta), rows, dim, L, p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
+  // Whole groups of four steps start at 16-byte-aligned addresses when L is a
+  // multiple of 4 (every buffer base is 16-byte aligned).
+  const bool vec = L % 4 == 0;
+  hipLaunchKernelGGL(vec ? fb_prologue<true> : fb_prologue<false>, fb_grid2(rows, L), dim3(256), 0, stream, p.x,
+                     p.delta_raw, p.conv_w, p.conv_b, p.delta_bias, fp(l.u), fp(l.delta), rows, dim, L,
+                     p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
   if (p.z) hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.z, fp(l.z), bdl, bf16);
   hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, p.dy, fp(l.dy), bdl, bf16);
   hipLaunchKernelGGL(fb_to_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, p.B, fp(l.B), bnl, bf16);
@@ -287,12 +429,14 @@ hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, reinterpret_cast<const int*>(ws + l.inner), 1);
 
-  hipLaunchKernelGGL(fb_chain, fb_grid2(rows, L), dim3(256), 0, stream, p.x, p.delta_raw, p.conv_w, p.conv_b,
-                     p.delta_bias, fp(l.du), fp(l.dd), p.ddelta_raw, rows, dim, L, p.conv_silu ? 1 : 0,
-                     p.softplus ? 1 : 0, bf16);
-  hipLaunchKernelGGL(fb_dx, fb_grid2(rows, L), dim3(256), 0, stream, fp(l.du), p.conv_w, p.dx, rows, dim, L, bf16);
-  hipLaunchKernelGGL(fb_channel_sums, dim3((unsigned)p.dim), dim3(256), 0, stream, p.x, fp(l.du), fp(l.dd),
-                     p.dconv_w, p.dconv_b, p.ddelta_bias, (int)p.batch, dim, L, bf16);
+  hipLaunchKernelGGL(vec ? fb_chain<true> : fb_chain<false>, fb_grid2(rows, L), dim3(256), 0, stream, p.x,
+                     p.delta_raw, p.conv_w, p.conv_b, p.delta_bias, fp(l.du), fp(l.dd), p.ddelta_raw, rows, dim, L,
+                     p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
+  hipLaunchKernelGGL(vec ? fb_dx<true> : fb_dx<false>, fb_grid2(rows, L), dim3(256), 0, stream, fp(l.du), p.conv_w,
+                     p.dx, rows, dim, L, bf16);
+  hipLaunchKernelGGL(vec ? fb_channel_sums<true> : fb_channel_sums<false>, dim3((unsigned)p.dim), dim3(256), 0,
+                     stream, p.x, fp(l.du), fp(l.dd), p.dconv_w, p.dconv_b, p.ddelta_bias, (int)p.batch, dim, L,
+                     bf16);
   hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dB), p.dB, bnl, bf16);
   hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dC), p.dC, bnl, bf16);
   if (p.z) hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bdl)), dim3(256), 0, stream, fp(l.dz), p.dz, bdl, bf16);
