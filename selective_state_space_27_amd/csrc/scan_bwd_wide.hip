@@ -34,17 +34,63 @@ constexpr size_t kMaxWideGrid = 16384;
 inline unsigned wide_grid(size_t items) {
   return (unsigned)std::max<size_t>(1, std::min<size_t>((items + 255) / 256, kMaxWideGrid));
 }
+// The flat passes over [b, d, L] take four elements per thread and step.
+inline unsigned wide_grid4(size_t items) { return wide_grid((items + 3) / 4); }
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __device__ __forceinline__ float ld_any(const void* p, size_t i, bool bf16) {
   return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
 }
 
+// Four consecutive elements i..i+3 (k < n of them; n = 4 is one 8-byte bf16
+// or 16-byte fp32 access, i being a multiple of 4 from a 16-byte-aligned
+// base), read as fp32 or written narrowed to the output type (bf16 round to
+// nearest even).  One element per thread and access left these passes far
+// below the HBM rate.
+__device__ __forceinline__ void wide_ld4(const void* p, size_t i, int n, bool bf16, float (&v)[4]) {
+  if (n == 4 && bf16) {
+    const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xffff0000u);
+  } else if (n == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = k < n ? ld_any(p, i + k, bf16) : 0.f;
+  }
+}
+__device__ __forceinline__ void wide_st4(void* p, size_t i, int n, bool bf16, const float (&v)[4]) {
+  if (n == 4 && bf16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(pack_bf16x2(v[0], v[1]),
+                                                                          pack_bf16x2(v[2], v[3]));
+  } else if (n == 4) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k >= n) break;
+      if (bf16) static_cast<uint16_t*>(p)[i + k] = f32_to_bf16(v[k]);
+      else static_cast<float*>(p)[i + k] = v[k];
+    }
+  }
+}
+
 // dst[i] = src[i] widened to fp32.
 __global__ void __launch_bounds__(256) wide_to_f32(const void* __restrict__ src, float* __restrict__ dst, size_t n,
                                                    int bf16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = ld_any(src, i, bf16);
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    const int m = (int)std::min<size_t>(4, n - i);
+    float v[4];
+    wide_ld4(src, i, m, bf16 != 0, v);
+    wide_st4(dst, i, m, false, v);
+  }
 }
 
 // Columns [n0, n0+ns) of rows of length N: dst[r*ns + j] = src[r*N + n0 + j]
@@ -83,21 +129,36 @@ __global__ void __launch_bounds__(256) wide_accumulate(const float* __restrict__
                                                        const float* __restrict__ s1, float* __restrict__ a1,
                                                        const float* __restrict__ s2, float* __restrict__ a2, size_t n,
                                                        int first) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    a0[i] = first ? s0[i] : a0[i] + s0[i];
-    a1[i] = first ? s1[i] : a1[i] + s1[i];
-    if (s2 != nullptr) a2[i] = first ? s2[i] : a2[i] + s2[i];
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+  const float* src[3] = {s0, s1, s2};
+  float* acc[3] = {a0, a1, a2};
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    const int m = (int)std::min<size_t>(4, n - i);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (src[q] == nullptr) continue;
+      float v[4];
+      wide_ld4(src[q], i, m, false, v);
+      if (!first) {
+        float a[4];
+        wide_ld4(acc[q], i, m, false, a);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = a[k] + v[k];
+      }
+      wide_st4(acc[q], i, m, false, v);
+    }
   }
 }
 
 // dst[i] = src[i] narrowed to the output type.
 __global__ void __launch_bounds__(256) wide_from_f32(const float* __restrict__ src, void* __restrict__ dst, size_t n,
                                                      int bf16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    if (bf16) static_cast<uint16_t*>(dst)[i] = f32_to_bf16(src[i]);
-    else static_cast<float*>(dst)[i] = src[i];
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    const int m = (int)std::min<size_t>(4, n - i);
+    float v[4];
+    wide_ld4(src, i, m, false, v);
+    wide_st4(dst, i, m, bf16 != 0, v);
   }
 }
 
@@ -190,7 +251,7 @@ hipError_t launch_scan_bwd_wide(const ScanBwdParams& p, hipStream_t stream) {
     float* dst[4] = {fp(l.u), fp(l.delta), fp(l.dy), fp(l.z)};
     for (int i = 0; i < 4; ++i) {
       if (src[i] == nullptr) continue;
-      hipLaunchKernelGGL(wide_to_f32, dim3(wide_grid(bdl)), dim3(256), 0, stream, src[i], dst[i], bdl, 1);
+      hipLaunchKernelGGL(wide_to_f32, dim3(wide_grid4(bdl)), dim3(256), 0, stream, src[i], dst[i], bdl, 1);
     }
     u32 = dst[0], d32 = dst[1], dy32 = dst[2], z32 = f.z ? dst[3] : nullptr;
   }
@@ -243,7 +304,7 @@ hipError_t launch_scan_bwd_wide(const ScanBwdParams& p, hipStream_t stream) {
 
     hipLaunchKernelGGL(wide_status, dim3(1), dim3(64), 0, stream, head, reinterpret_cast<const int*>(ws + l.slice_ws),
                        1);
-    hipLaunchKernelGGL(wide_accumulate, dim3(wide_grid(bdl)), dim3(256), 0, stream, fp(l.du), fp(l.acc_du),
+    hipLaunchKernelGGL(wide_accumulate, dim3(wide_grid4(bdl)), dim3(256), 0, stream, fp(l.du), fp(l.acc_du),
                        fp(l.ddelta), fp(l.acc_dd), z32 ? fp(l.dz) : nullptr, fp(l.acc_dz), bdl, s == 0 ? 1 : 0);
     hipLaunchKernelGGL(wide_scatter, dim3(wide_grid((size_t)f.dim * ns)), dim3(256), 0, stream, fp(l.dA),
                        static_cast<void*>(p.dA), (size_t)f.dim, N, n0, ns, (size_t)1, 0);
@@ -257,9 +318,9 @@ hipError_t launch_scan_bwd_wide(const ScanBwdParams& p, hipStream_t stream) {
     if (!check()) return err;
   }
 
-  hipLaunchKernelGGL(wide_from_f32, dim3(wide_grid(bdl)), dim3(256), 0, stream, fp(l.acc_du), p.du, bdl, bf16);
-  hipLaunchKernelGGL(wide_from_f32, dim3(wide_grid(bdl)), dim3(256), 0, stream, fp(l.acc_dd), p.ddelta, bdl, bf16);
-  if (z32) hipLaunchKernelGGL(wide_from_f32, dim3(wide_grid(bdl)), dim3(256), 0, stream, fp(l.acc_dz), p.dz, bdl, bf16);
+  hipLaunchKernelGGL(wide_from_f32, dim3(wide_grid4(bdl)), dim3(256), 0, stream, fp(l.acc_du), p.du, bdl, bf16);
+  hipLaunchKernelGGL(wide_from_f32, dim3(wide_grid4(bdl)), dim3(256), 0, stream, fp(l.acc_dd), p.ddelta, bdl, bf16);
+  if (z32) hipLaunchKernelGGL(wide_from_f32, dim3(wide_grid4(bdl)), dim3(256), 0, stream, fp(l.acc_dz), p.dz, bdl, bf16);
   hipLaunchKernelGGL(wide_status, dim3(1), dim3(64), 0, stream, head, head, 2);
   check();
   return err;

@@ -56,10 +56,18 @@ __global__ void __launch_bounds__(256) half_scatter(const float* __restrict__ sr
   }
 }
 
-// dst[i] += src[i].
+// dst[i] += src[i], four elements per thread and step (one 16-byte access
+// each when whole: the bases are 16-byte aligned and i a multiple of 4).
 __global__ void __launch_bounds__(256) half_add(const float* __restrict__ src, float* __restrict__ dst, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] += src[i];
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      const float4 a = *reinterpret_cast<const float4*>(dst + i), b = *reinterpret_cast<const float4*>(src + i);
+      *reinterpret_cast<float4*>(dst + i) = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    } else {
+      for (size_t k = i; k < n; ++k) dst[k] += src[k];
+    }
+  }
 }
 
 // Status words: mode 0 clears the head, 1 ors a half's word into word 1,
@@ -180,10 +188,10 @@ hipError_t launch_ssd_bwd_halves(const SSDBwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL(half_scatter, dim3(halves_grid(st_rows * nh)), dim3(256), 0, stream, fp(l.dh0), p.dh0,
                          st_rows, N, n0, nh);
     if (h == 1) {
-      hipLaunchKernelGGL(half_add, dim3(halves_grid(nx)), dim3(256), 0, stream, fp(l.dx), p.dx, nx);
-      hipLaunchKernelGGL(half_add, dim3(halves_grid(ndl)), dim3(256), 0, stream, fp(l.ddelta), p.ddelta, ndl);
+      hipLaunchKernelGGL(half_add, dim3(halves_grid((nx + 3) / 4)), dim3(256), 0, stream, fp(l.dx), p.dx, nx);
+      hipLaunchKernelGGL(half_add, dim3(halves_grid((ndl + 3) / 4)), dim3(256), 0, stream, fp(l.ddelta), p.ddelta, ndl);
       hipLaunchKernelGGL(half_add, dim3(1), dim3(256), 0, stream, fp(l.dA), p.dA, (size_t)p.nheads);
-      if (p.dz) hipLaunchKernelGGL(half_add, dim3(halves_grid(nx)), dim3(256), 0, stream, fp(l.dz), p.dz, nx);
+      if (p.dz) hipLaunchKernelGGL(half_add, dim3(halves_grid((nx + 3) / 4)), dim3(256), 0, stream, fp(l.dz), p.dz, nx);
     }
     if (!check()) return err;
   }
