@@ -146,6 +146,8 @@ WIDE_SHAPES = [
     (1, 64, 64, 150, "fp32"),      # two full slices
     (2, 80, 128, 60, "bf16"),      # four slices, bf16 I/O (fp32 inside, rounded once)
     (1, 130, 33, 40, "fp32"),      # a one-state last slice
+    (1, 33, 40, 31, "bf16"),       # b*d*L not a multiple of 4 (partial last group of the flat passes)
+    (1, 35, 48, 29, "fp32"),
 ]
 
 

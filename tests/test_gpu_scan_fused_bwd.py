@@ -76,6 +76,9 @@ SHAPES = [
     (2, 64, 4, 40, "fp32"),       # one state per wave pair
     (2, 80, 40, 60, "fp32"),      # d_state above 32 (slices of states)
     (1, 72, 64, 50, "bf16"),
+    (1, 64, 16, 1030, "bf16"),    # L not a multiple of 4 over several workgroups per row
+    (1, 33, 5, 31, "bf16"),       # b*d*L and b*N*L not multiples of 4
+    (1, 35, 40, 29, "fp32"),
 ]
 
 

@@ -84,6 +84,7 @@ CASES = [
     (2, 130, 3, 1, 128, 144, True, False, True, False),
     (1, 200, 4, 1, 64, 160, False, True, False, True),
     (1, 2048, 16, 2, 64, 256, True, True, True, True),    # halves over many blocks and pieces
+    (1, 151, 3, 1, 64, 256, True, True, True, True),      # b*L*H not a multiple of 4 (partial last group of the adds)
 ]
 
 
