@@ -43,7 +43,18 @@ __device__ __forceinline__ void st_io(void* p, size_t i, float v, int bf16) {
   if (bf16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
   else static_cast<float*>(p)[i] = v;
 }
-__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
+// The forward kernel's forms: sigmoid by the hardware exp2 and reciprocal,
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)) with log1p(e) taken as
+// log(w) e / (w - 1), w = 1 + e rounded (e itself when w rounds to 1), so
+// that u and delta here are bitwise those the forward formed.
+__device__ __forceinline__ float sigmoid_f(float v) { return rcp_fast(1.0f + exp2_fast(-v * kLog2e)); }
+__device__ __forceinline__ float softplus_fwd(float v) {
+  constexpr float kLn2f = 0.6931471805599453f;
+  const float e = exp2_fast(-fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float l = (w == 1.0f) ? e : __builtin_amdgcn_logf(w) * kLn2f * (e * rcp_fast(w - 1.0f));
+  return fmaxf(v, 0.f) + l;
+}
 
 // Groups of four consecutive elements: the per-element passes move 8 (bf16)
 // or 16 (fp32) bytes per lane and access, where one element per lane left
@@ -149,10 +160,9 @@ __global__ void __launch_bounds__(256) fb_prologue(const void* __restrict__ x, c
       ld4<V>(delta_raw, base + t0, n, bf16, v);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uo[k] = silu_on ? c[k] * sigmoid_f(c[k]) : c[k];
+        uo[k] = silu_on ? silu(c[k]) : c[k];
         const float vv = v[k] + db;
-        // softplus(v) = max(v, 0) + log1p(exp(-|v|))
-        dl[k] = softplus_on ? fmaxf(vv, 0.f) + log1pf(__expf(-fabsf(vv))) : vv;
+        dl[k] = softplus_on ? softplus_fwd(vv) : vv;
       }
       st4<V>(u, base + t0, n, 0, uo);
       st4<V>(delta, base + t0, n, 0, dl);
