@@ -16,9 +16,9 @@
 // forward kernel, so the scan's gradient is taken at their fp32 values), the
 // other [b, d, L] and [b, N, L] inputs widened to fp32, the scan's backward in
 // fp32 (by slices of 32 states above 32), then the prologue's chain rule:
-// an elementwise pass (dc, dv, ddelta_raw), a pass for dx, and one workgroup
-// per channel for the tap and bias sums (a fixed order: bitwise repeatable).
-// Gradients in the I/O type are rounded once, at the end.
+// one pass over the steps (dc, dx, dv, ddelta_raw) and one workgroup per
+// channel for the tap and bias sums (a fixed order: bitwise repeatable).
+// Gradients in the I/O type are rounded once.
 //
 // Workspace: a 256-byte head (word 0: the call's status), the scan backward's
 // workspace, then the fp32 buffers of the layout below.
@@ -204,13 +204,17 @@ __global__ void __launch_bounds__(256) fb_from_f32(const float* __restrict__ src
   }
 }
 
-// dc = du silu'(c) in place of du; dv = ddelta sigmoid(v) in place of
-// ddelta, and ddelta_raw = dv in the I/O type.
+// dc = du silu'(c) (du itself without silu) into dc_out, dx[s] = sum_k w_k
+// dc[s+3-k] (terms past L dropped), dv = ddelta sigmoid(v) in place of
+// ddelta, and ddelta_raw = dv in the I/O type.  A thread's dx needs dc three
+// steps into the next group: it forms those from du and x as that group's
+// thread does (the same operations, so the same values).
 template <bool V>
 __global__ void __launch_bounds__(256) fb_chain(const void* __restrict__ x, const void* __restrict__ delta_raw,
                                                 const float* __restrict__ conv_w, const float* __restrict__ conv_b,
-                                                const float* __restrict__ delta_bias, float* __restrict__ du_dc,
-                                                float* __restrict__ dd_dv, void* __restrict__ ddelta_raw, size_t rows,
+                                                const float* __restrict__ delta_bias, const float* __restrict__ du,
+                                                float* __restrict__ dc_out, float* __restrict__ dd_dv,
+                                                void* __restrict__ ddelta_raw, void* __restrict__ dx, size_t rows,
                                                 int dim, int L, int silu_on, int softplus_on, int bf16) {
   const int groups = (L + 3) / 4;
   for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
@@ -220,19 +224,57 @@ __global__ void __launch_bounds__(256) fb_chain(const void* __restrict__ x, cons
     const size_t base = r * (size_t)L;
     for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < groups; j += gridDim.x * blockDim.x) {
       const int t0 = 4 * j, n = std::min(4, L - t0);
+      const int nn = t0 + 4 < L ? std::min(4, L - t0 - 4) : 0;  // steps of the next group
       const size_t i = base + t0;
+      // g[m] = dc at step t0+m, m = 0..7 (0 past L)
+      float g[8], a4[4], b4[4] = {0.f, 0.f, 0.f, 0.f};
+      ld4f<V>(du, i, n, a4);
+      if (nn > 0) {
+        if (V) ld4f<true>(du, i + 4, 4, b4);
+        else ld4f<false>(du, i + 4, nn, b4);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        g[k] = a4[k];
+        g[4 + k] = b4[k];
+      }
       if (silu_on) {
-        float win[8], c[4], g[4];
-        x_window<V>(x, base, t0, n, bf16, win);
-        conv4(win, t0, w, cb, c);
-        ld4f<V>(du_dc, i, n, g);
+        // xw[m] = x at step t0-4+m, m = 0..11 (zeros outside the row)
+        float xw[12], p4[4] = {0.f, 0.f, 0.f, 0.f}, c4[4], n4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t0 > 0) ld4<V>(x, base + t0 - 4, 4, bf16, p4);
+        ld4<V>(x, i, n, bf16, c4);
+        if (nn > 0) {
+          if (V) ld4<true>(x, i + 4, 4, bf16, n4);
+          else ld4<false>(x, i + 4, nn, bf16, n4);
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float s = sigmoid_f(c[k]);
-          g[k] *= s * (1.0f + c[k] * (1.0f - s));
+          xw[k] = p4[k];
+          xw[4 + k] = c4[k];
+          xw[8 + k] = n4[k];
         }
-        st4<V>(du_dc, i, n, 0, g);
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+          float c = cb;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (t0 + m - 3 + q >= 0) c = __builtin_fmaf(w[q], xw[m + 1 + q], c);
+          const float s = sigmoid_f(c);
+          g[m] *= s * (1.0f + c * (1.0f - s));
+        }
       }
+      const float dcv[4] = {g[0], g[1], g[2], g[3]};
+      st4<V>(dc_out, i, n, 0, dcv);
+      float out[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (t0 + m + 3 - k < L) acc = __builtin_fmaf(w[k], g[m + 3 - k], acc);
+        out[m] = acc;
+      }
+      st4<V>(dx, i, n, bf16, out);
       float dv[4];
       ld4f<V>(dd_dv, i, n, dv);
       if (softplus_on) {
@@ -243,42 +285,6 @@ __global__ void __launch_bounds__(256) fb_chain(const void* __restrict__ x, cons
         st4<V>(dd_dv, i, n, 0, dv);
       }
       st4<V>(ddelta_raw, i, n, bf16, dv);
-    }
-  }
-}
-
-// dx[s] = sum_k w_k dc[s+3-k] (terms past L dropped).
-template <bool V>
-__global__ void __launch_bounds__(256) fb_dx(const float* __restrict__ dc, const float* __restrict__ conv_w,
-                                             void* __restrict__ dx, size_t rows, int dim, int L, int bf16) {
-  const int groups = (L + 3) / 4;
-  for (size_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    const int d = (int)(r % (size_t)dim);
-    const float w[4] = {conv_w[4 * d], conv_w[4 * d + 1], conv_w[4 * d + 2], conv_w[4 * d + 3]};
-    const size_t base = r * (size_t)L;
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < groups; j += gridDim.x * blockDim.x) {
-      const int t0 = 4 * j, n = std::min(4, L - t0);
-      // win[m] = dc[t0+m], m = 0..7 (the next group may be partial or absent)
-      float cur[4], next[4] = {0.f, 0.f, 0.f, 0.f}, win[8], out[4];
-      ld4f<V>(dc, base + t0, n, cur);
-      if (t0 + 4 < L) {
-        if (V) ld4f<true>(dc, base + t0 + 4, 4, next);
-        else ld4f<false>(dc, base + t0 + 4, std::min(4, L - t0 - 4), next);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        win[k] = cur[k];
-        win[4 + k] = next[k];
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (t0 + m + 3 - k < L) acc = __builtin_fmaf(w[k], win[m + 3 - k], acc);
-        out[m] = acc;
-      }
-      st4<V>(dx, base + t0, n, bf16, out);
     }
   }
 }
@@ -439,13 +445,12 @@ hipError_t launch_scan_fused_bwd(const ScanFusedBwdParams& p, hipStream_t stream
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fb_status, dim3(1), dim3(64), 0, stream, head, reinterpret_cast<const int*>(ws + l.inner), 1);
 
+  // dc goes where u was: u is read only by the scan's backward, done by now.
   hipLaunchKernelGGL(vec ? fb_chain<true> : fb_chain<false>, fb_grid2(rows, L), dim3(256), 0, stream, p.x,
-                     p.delta_raw, p.conv_w, p.conv_b, p.delta_bias, fp(l.du), fp(l.dd), p.ddelta_raw, rows, dim, L,
-                     p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
-  hipLaunchKernelGGL(vec ? fb_dx<true> : fb_dx<false>, fb_grid2(rows, L), dim3(256), 0, stream, fp(l.du), p.conv_w,
-                     p.dx, rows, dim, L, bf16);
+                     p.delta_raw, p.conv_w, p.conv_b, p.delta_bias, fp(l.du), fp(l.u), fp(l.dd), p.ddelta_raw, p.dx,
+                     rows, dim, L, p.conv_silu ? 1 : 0, p.softplus ? 1 : 0, bf16);
   hipLaunchKernelGGL(vec ? fb_channel_sums<true> : fb_channel_sums<false>, dim3((unsigned)p.dim), dim3(256), 0,
-                     stream, p.x, fp(l.du), fp(l.dd), p.dconv_w, p.dconv_b, p.ddelta_bias, (int)p.batch, dim, L,
+                     stream, p.x, fp(l.u), fp(l.dd), p.dconv_w, p.dconv_b, p.ddelta_bias, (int)p.batch, dim, L,
                      bf16);
   hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dB), p.dB, bnl, bf16);
   hipLaunchKernelGGL(fb_from_f32, dim3(fb_grid(bnl)), dim3(256), 0, stream, fp(l.dC), p.dC, bnl, bf16);
